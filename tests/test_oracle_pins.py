@@ -1,0 +1,555 @@
+"""Pins of the CPU oracle against things other than itself: closed forms,
+invariants, library special cases (torch float64 CPU routines and autograd),
+brute force on tiny inputs, and central finite differences.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a
+wrong sign or index, a transposed operand) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import ops
+from oracle.block import block_forward, block_backward, PARAM_NAMES, positions
+from bwd_rmsnorm_qkv_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def fd_directional(f, x, direction, h):
+    return (f(x + h * direction) - f(x - h * direction)) / (2.0 * h)
+
+
+# ------------------------------------------------------------------ RMSNorm
+
+def test_rmsnorm_mean_square_identity(rng):
+    x = rng.standard_normal((7, 33))
+    g = rng.uniform(0.5, 2.0, 33)
+    eps = 1e-3
+    y, rho = ops.rmsnorm_fwd(x, g, eps)
+    ms = np.mean(x * x, axis=-1)
+    np.testing.assert_allclose(np.mean((y / g) ** 2, axis=-1), ms / (ms + eps), rtol=1e-13)
+    np.testing.assert_allclose(rho, 1.0 / np.sqrt(ms + eps), rtol=1e-14)
+
+
+def test_rmsnorm_scale_invariance_and_orthogonality(rng):
+    x = rng.standard_normal((5, 40))
+    g = rng.uniform(0.5, 2.0, 40)
+    y1, _ = ops.rmsnorm_fwd(x, g, 0.0)
+    y2, _ = ops.rmsnorm_fwd(3.7 * x, g, 0.0)
+    np.testing.assert_allclose(y1, y2, rtol=1e-13, atol=1e-14)
+    dx, _ = ops.rmsnorm_bwd(x, g, rng.standard_normal(x.shape), 0.0)
+    np.testing.assert_allclose(np.sum(dx * x, axis=-1), 0.0, atol=1e-12)
+
+
+def test_rmsnorm_matches_torch(rng):
+    x = rng.standard_normal((6, 24))
+    g = rng.uniform(0.5, 2.0, 24)
+    y, _ = ops.rmsnorm_fwd(x, g, 1e-6)
+    ref = F.rms_norm(torch.tensor(x), (24,), torch.tensor(g), eps=1e-6).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-12)
+
+
+def test_rmsnorm_bwd_finite_difference(rng):
+    x = rng.standard_normal((4, 16))
+    g = rng.uniform(0.5, 2.0, 16)
+    w = rng.standard_normal((4, 16))
+    dx, dg = ops.rmsnorm_bwd(x, g, w, 1e-6)
+    vx, vg = rng.standard_normal(x.shape), rng.standard_normal(g.shape)
+    fx = fd_directional(lambda t: np.sum(ops.rmsnorm_fwd(t, g, 1e-6)[0] * w), x, vx, 1e-6)
+    fg = fd_directional(lambda t: np.sum(ops.rmsnorm_fwd(x, t, 1e-6)[0] * w), g, vg, 1e-6)
+    assert abs(fx - np.sum(dx * vx)) < 1e-7 * max(1.0, abs(fx))
+    assert abs(fg - np.sum(dg * vg)) < 1e-7 * max(1.0, abs(fg))
+
+
+def test_head_rmsnorm_is_per_head(rng):
+    x = rng.standard_normal((3, 4 * 8))
+    g = rng.uniform(0.5, 2.0, 8)
+    y, rho = ops.head_rmsnorm_fwd(x, g, 4, 1e-6)
+    for h in range(4):
+        yh, rh = ops.rmsnorm_fwd(x[:, h * 8:(h + 1) * 8], g, 1e-6)
+        np.testing.assert_array_equal(y[:, h * 8:(h + 1) * 8], yh)
+        np.testing.assert_array_equal(rho[:, h], rh)
+    dy = rng.standard_normal(x.shape)
+    dx, dg = ops.head_rmsnorm_bwd(x, g, dy, 4, 1e-6)
+    v = rng.standard_normal(g.shape)
+    f = fd_directional(lambda t: np.sum(ops.head_rmsnorm_fwd(x, t, 4, 1e-6)[0] * dy), g, v, 1e-6)
+    assert abs(f - np.sum(dg * v)) < 1e-7 * max(1.0, abs(f))
+
+
+# ------------------------------------------------------------------- Linear
+
+def test_linear_exact_on_small_integers(rng):
+    x = rng.integers(-3, 4, (5, 7)).astype(np.float64)
+    w = rng.integers(-3, 4, (6, 7)).astype(np.float64)
+    dy = rng.integers(-3, 4, (5, 6)).astype(np.float64)
+    y = ops.linear_fwd(x, w)
+    brute = np.array([[sum(x[t, i] * w[o, i] for i in range(7)) for o in range(6)] for t in range(5)])
+    np.testing.assert_array_equal(y, brute)
+    dx, dw = ops.linear_bwd(x, w, dy)
+    np.testing.assert_array_equal(dx, np.array([[sum(dy[t, o] * w[o, i] for o in range(6))
+                                                 for i in range(7)] for t in range(5)]))
+    np.testing.assert_array_equal(dw, np.array([[sum(dy[t, o] * x[t, i] for t in range(5))
+                                                 for i in range(7)] for o in range(6)]))
+    np.testing.assert_array_equal(ops.linear_fwd(x, np.eye(7)), x)
+
+
+# --------------------------------------------------------------------- RoPE
+
+def test_rope_against_complex_rotation(rng):
+    t, nh, d, theta = 6, 3, 8, 1e4
+    x = rng.standard_normal((t, nh * d))
+    pos = np.arange(t) * 5 + 1
+    y = ops.rope_fwd(x, pos, nh, theta)
+    for ti in range(t):
+        for h in range(nh):
+            seg = x[ti, h * d:(h + 1) * d]
+            z = seg[: d // 2] + 1j * seg[d // 2:]
+            freqs = np.array([theta ** (-2.0 * i / d) for i in range(d // 2)])
+            zr = z * np.exp(1j * pos[ti] * freqs)
+            np.testing.assert_allclose(y[ti, h * d:(h + 1) * d],
+                                       np.concatenate([zr.real, zr.imag]), rtol=1e-12, atol=1e-13)
+
+
+def test_rope_invariants(rng):
+    t, nh, d, theta = 9, 2, 16, 1e6
+    x = rng.standard_normal((t, nh * d))
+    pos = np.arange(t)
+    y = ops.rope_fwd(x, pos, nh, theta)
+    xh, yh = x.reshape(t, nh, d), y.reshape(t, nh, d)
+    pair = lambda a: a[..., : d // 2] ** 2 + a[..., d // 2:] ** 2
+    np.testing.assert_allclose(pair(yh), pair(xh), rtol=1e-12)
+    np.testing.assert_array_equal(y[0], x[0])  # position 0 is the identity
+    np.testing.assert_allclose(ops.rope_bwd(y, pos, nh, theta), x, rtol=1e-12, atol=1e-13)
+    # frequency 0 is 1: the first pair turns by exactly pos radians
+    a0 = np.arctan2(yh[:, 0, d // 2], yh[:, 0, 0]) - np.arctan2(xh[:, 0, d // 2], xh[:, 0, 0])
+    np.testing.assert_allclose(np.cos(a0), np.cos(pos), atol=1e-12)
+    # <R_m q, R_n k> depends only on m - n
+    q, k = rng.standard_normal((1, d)), rng.standard_normal((1, d))
+    dots = []
+    for m, n in ((3, 1), (7, 5), (12, 10)):
+        qm = ops.rope_fwd(q, np.array([m]), 1, theta)
+        kn = ops.rope_fwd(k, np.array([n]), 1, theta)
+        dots.append(float((qm @ kn.T)[0, 0]))
+    np.testing.assert_allclose(dots, dots[0], rtol=1e-12)
+
+
+def test_rope_bwd_is_transpose(rng):
+    t, nh, d = 5, 2, 8
+    x, g = rng.standard_normal((t, nh * d)), rng.standard_normal((t, nh * d))
+    pos = np.arange(t) + 3
+    lhs = np.sum(ops.rope_fwd(x, pos, nh, 1e4) * g)
+    rhs = np.sum(x * ops.rope_bwd(g, pos, nh, 1e4))
+    assert abs(lhs - rhs) < 1e-12 * max(1.0, abs(lhs))
+
+
+# ---------------------------------------------------------------- Attention
+
+def _sdpa_reference(q, k, v, batch, seq, heads, kv, d):
+    """torch float64 scaled_dot_product_attention(is_causal) with K/V heads
+    replicated for GQA."""
+    qt = torch.tensor(q).reshape(batch, seq, heads, d).transpose(1, 2)
+    kt = torch.tensor(k).reshape(batch, seq, kv, d).transpose(1, 2)
+    vt = torch.tensor(v).reshape(batch, seq, kv, d).transpose(1, 2)
+    kt = kt.repeat_interleave(heads // kv, dim=1)
+    vt = vt.repeat_interleave(heads // kv, dim=1)
+    o = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    return o.transpose(1, 2).reshape(batch * seq, heads * d).numpy()
+
+
+def test_attention_matches_torch_sdpa_gqa(rng):
+    batch, seq, heads, kv, d = 2, 11, 4, 2, 8
+    q = rng.standard_normal((batch * seq, heads * d))
+    k = rng.standard_normal((batch * seq, kv * d))
+    v = rng.standard_normal((batch * seq, kv * d))
+    o = ops.attention_fwd(q, k, v, batch, seq, heads, kv, d)
+    np.testing.assert_allclose(o, _sdpa_reference(q, k, v, batch, seq, heads, kv, d),
+                               rtol=1e-11, atol=1e-12)
+
+
+def test_attention_probabilities_and_closed_forms(rng):
+    batch, seq, heads, kv, d = 1, 9, 2, 1, 4
+    q = rng.standard_normal((seq, heads * d))
+    k = rng.standard_normal((seq, kv * d))
+    v = rng.standard_normal((seq, kv * d))
+    o, p = ops.attention_fwd(q, k, v, batch, seq, heads, kv, d, return_probs=True)
+    np.testing.assert_allclose(p.sum(axis=-1), 1.0, rtol=1e-14)
+    assert np.all(p[..., np.triu_indices(seq, 1)[0], np.triu_indices(seq, 1)[1]] == 0.0)
+    np.testing.assert_allclose(o[0, :d], v[0, :d], rtol=1e-14)   # row 0 sees only key 0
+    np.testing.assert_allclose(o[0, d:], v[0, :d], rtol=1e-14)
+    # q = 0: uniform weights over the causal prefix -> running mean of v
+    o0 = ops.attention_fwd(np.zeros_like(q), k, v, batch, seq, heads, kv, d)
+    running = np.cumsum(v, axis=0) / np.arange(1, seq + 1)[:, None]
+    np.testing.assert_allclose(o0[:, :d], running, rtol=1e-13)
+    np.testing.assert_allclose(o0[:, d:], running, rtol=1e-13)
+
+
+def test_attention_gqa_equals_replicated_mha(rng):
+    seq, heads, kv, d = 7, 6, 2, 4
+    q = rng.standard_normal((seq, heads * d))
+    k = rng.standard_normal((seq, kv * d))
+    v = rng.standard_normal((seq, kv * d))
+    rep = lambda a: np.concatenate([a[:, (h // 3) * d:(h // 3 + 1) * d] for h in range(heads)], 1)
+    o_gqa = ops.attention_fwd(q, k, v, 1, seq, heads, kv, d)
+    o_mha = ops.attention_fwd(q, rep(k), rep(v), 1, seq, heads, heads, d)
+    np.testing.assert_allclose(o_gqa, o_mha, rtol=1e-14)
+    do = rng.standard_normal(q.shape)
+    dq, dk, dv = ops.attention_bwd(q, k, v, do, 1, seq, heads, kv, d)
+    dq2, dk2, dv2 = ops.attention_bwd(q, rep(k), rep(v), do, 1, seq, heads, heads, d)
+    np.testing.assert_allclose(dq, dq2, rtol=1e-12)
+    fold = lambda a: sum(a[:, j * d:(j + 1) * d] for j in range(3))
+    np.testing.assert_allclose(dk[:, :d], fold(dk2[:, :3 * d]), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dv[:, d:], fold(dv2[:, 3 * d:]), rtol=1e-12, atol=1e-14)
+
+
+def test_attention_bwd_matches_autograd(rng):
+    batch, seq, heads, kv, d = 2, 6, 4, 2, 4
+    q = rng.standard_normal((batch * seq, heads * d))
+    k = rng.standard_normal((batch * seq, kv * d))
+    v = rng.standard_normal((batch * seq, kv * d))
+    do = rng.standard_normal(q.shape)
+    dq, dk, dv = ops.attention_bwd(q, k, v, do, batch, seq, heads, kv, d)
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    qt = tq.reshape(batch, seq, heads, d).transpose(1, 2)
+    kt = tk.reshape(batch, seq, kv, d).transpose(1, 2).repeat_interleave(heads // kv, 1)
+    vt = tv.reshape(batch, seq, kv, d).transpose(1, 2).repeat_interleave(heads // kv, 1)
+    o = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    o = o.transpose(1, 2).reshape(batch * seq, heads * d)
+    (o * torch.tensor(do)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------------------------- SwiGLU
+
+def test_swiglu_closed_forms_and_fd(rng):
+    assert ops.swiglu_fwd(np.array([0.0]), np.array([3.0]))[0] == 0.0
+    dg, du = ops.swiglu_bwd(np.array([0.0]), np.array([1.0]), np.array([1.0]))
+    assert dg[0] == 0.5 and du[0] == 0.0
+    g, u = rng.standard_normal(50) * 3, rng.standard_normal(50)
+    np.testing.assert_allclose(ops.swiglu_fwd(g, u), F.silu(torch.tensor(g)).numpy() * u,
+                               rtol=1e-13)
+    ds = rng.standard_normal(50)
+    dg, du = ops.swiglu_bwd(g, u, ds)
+    h = 1e-6
+    np.testing.assert_allclose(dg, ds * (ops.swiglu_fwd(g + h, u) - ops.swiglu_fwd(g - h, u)) / (2 * h),
+                               rtol=1e-7, atol=1e-9)
+    np.testing.assert_allclose(du, ds * (ops.swiglu_fwd(g, u + h) - ops.swiglu_fwd(g, u - h)) / (2 * h),
+                               rtol=1e-7, atol=1e-9)
+
+
+# -------------------------------------------------------------------- Block
+
+def _torch_block_loss(c, p, x, dy):
+    """The block written with torch library routines (rms_norm, linear, SDPA,
+    silu) in float64; autograd supplies the derivatives independently of the
+    oracle's hand-written backward."""
+    t = lambda a: torch.tensor(np.asarray(a, np.float64), requires_grad=True)
+    tp = {n: t(p[n]) for n in PARAM_NAMES}
+    tx = t(x)
+    T, H, KV, d = c.tokens, c.heads, c.kv_heads, c.head_dim
+    pos = torch.tensor(positions(c.seq, c.batch), dtype=torch.float64)
+    inv = c.rope_theta ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
+    ang = pos[:, None] * inv[None, :]
+    cos, sin = torch.cos(ang)[:, None, :], torch.sin(ang)[:, None, :]
+
+    def rope(a, nh):
+        a = a.reshape(T, nh, d)
+        a0, a1 = a[..., : d // 2], a[..., d // 2:]
+        return torch.cat([a0 * cos - a1 * sin, a1 * cos + a0 * sin], -1)
+
+    n1 = F.rms_norm(tx, (c.hidden,), tp["g_in"], eps=c.eps)
+    q = F.linear(n1, tp["w_q"]).reshape(T, H, d)
+    k = F.linear(n1, tp["w_k"]).reshape(T, KV, d)
+    v = F.linear(n1, tp["w_v"]).reshape(T, KV, d)
+    q = F.rms_norm(q, (d,), tp["g_q"], eps=c.eps)
+    k = F.rms_norm(k, (d,), tp["g_k"], eps=c.eps)
+    q, k = rope(q, H), rope(k, KV)
+    qb = q.reshape(c.batch, c.seq, H, d).transpose(1, 2)
+    kb = k.reshape(c.batch, c.seq, KV, d).transpose(1, 2).repeat_interleave(H // KV, 1)
+    vb = v.reshape(c.batch, c.seq, KV, d).transpose(1, 2).repeat_interleave(H // KV, 1)
+    o = F.scaled_dot_product_attention(qb, kb, vb, is_causal=True)
+    o = o.transpose(1, 2).reshape(T, H * d)
+    r1 = tx + F.linear(o, tp["w_o"])
+    n2 = F.rms_norm(r1, (c.hidden,), tp["g_post"], eps=c.eps)
+    s = F.silu(F.linear(n2, tp["w_gate"])) * F.linear(n2, tp["w_up"])
+    y = r1 + F.linear(s, tp["w_down"])
+    (y * torch.tensor(dy, dtype=torch.float64)).sum().backward()
+    return y.detach().numpy(), tx.grad.numpy(), {n: tp[n].grad.numpy() for n in PARAM_NAMES}
+
+
+def _perturbed_gammas(p, rng):
+    p = dict(p)
+    for n in ("g_in", "g_post", "g_q", "g_k"):
+        p[n] = (1.0 + 0.3 * rng.standard_normal(p[n].shape)).astype(np.float32)
+    return p
+
+
+@pytest.mark.parametrize("shape", [synth.TINY_BLOCK, synth.TINY_BLOCK.with_tokens(seq=13, batch=3)])
+def test_block_matches_torch_autograd(shape, rng):
+    inp = synth.block_inputs(shape)
+    p = _perturbed_gammas(inp["params"], rng)
+    y, cache = block_forward(shape, p, inp["x"])
+    dx, grads = block_backward(shape, p, cache, inp["dy"])
+    ty, tdx, tgrads = _torch_block_loss(shape, p, inp["x"], inp["dy"])
+    np.testing.assert_allclose(y, ty, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dx, tdx, rtol=1e-9, atol=1e-12)
+    for n in PARAM_NAMES:
+        np.testing.assert_allclose(grads[n], tgrads[n], rtol=1e-9, atol=1e-12, err_msg=n)
+
+
+def test_block_finite_differences_tiny(rng):
+    """Central differences of L = sum(y * dy) along random directions, for x
+    and each of the 11 parameters, plus element-wise checks on a subset."""
+    c = synth.TINY_BLOCK
+    inp = synth.block_inputs(c)
+    p = {k: v.astype(np.float64) for k, v in _perturbed_gammas(inp["params"], rng).items()}
+    x, dy = inp["x"].astype(np.float64), inp["dy"].astype(np.float64)
+    _, cache = block_forward(c, p, x)
+    dx, grads = block_backward(c, p, cache, dy)
+
+    def loss_x(xx):
+        return float(np.sum(block_forward(c, p, xx)[0] * dy))
+
+    def loss_p(name):
+        def f(w):
+            q = dict(p)
+            q[name] = w
+            return float(np.sum(block_forward(c, q, x)[0] * dy))
+        return f
+
+    checks = [(loss_x, x, dx)] + [(loss_p(n), p[n], grads[n]) for n in PARAM_NAMES]
+    for f, theta, g in checks:
+        direction = rng.standard_normal(theta.shape)
+        h = 1e-6 * max(1.0, float(np.max(np.abs(theta))))
+        num = fd_directional(f, theta, direction, h)
+        ana = float(np.sum(g * direction))
+        assert abs(num - ana) <= 1e-6 * max(1e-3, abs(ana)), (num, ana)
+    for f, theta, g in checks[:3]:
+        flat = theta.reshape(-1)
+        for idx in rng.choice(flat.size, 4, replace=False):
+            e = np.zeros_like(flat)
+            e[idx] = 1.0
+            num = fd_directional(f, theta, e.reshape(theta.shape), 1e-5)
+            assert abs(num - g.reshape(-1)[idx]) <= 1e-6 * max(1e-2, abs(num))
+
+
+# ------------------------------------------------------------ LM head + CE
+
+def test_cross_entropy_closed_forms(rng):
+    T, h, V = 5, 8, 13
+    y = rng.standard_normal((T, h))
+    tgt = rng.integers(0, V, T)
+    out = oracle.lm_head_cross_entropy(y, None, np.zeros((V, h)), tgt, 1e-6)
+    np.testing.assert_allclose(out["loss"], math.log(V), rtol=1e-14)
+    expect = np.full((T, V), 1.0 / V)
+    expect[np.arange(T), tgt] -= 1.0
+    expect /= T
+    np.testing.assert_allclose(out["dy_last"], 0.0, atol=1e-15)
+    np.testing.assert_allclose(out["dw_lm"], expect.T @ y, rtol=1e-13, atol=1e-16)
+    w = rng.standard_normal((V, h))
+    out = oracle.lm_head_cross_entropy(y, rng.uniform(0.5, 2, h), w, tgt, 1e-6)
+    z = out["logits"]
+    dz = np.exp(z - z.max(1, keepdims=True))
+    dz /= dz.sum(1, keepdims=True)
+    dz[np.arange(T), tgt] -= 1
+    np.testing.assert_allclose((dz / T).sum(axis=1), 0.0, atol=1e-15)
+    brute = np.array([min(range(V), key=lambda j: (-z[t, j], j)) for t in range(T)])
+    np.testing.assert_array_equal(out["argmax"], brute)
+
+
+def test_cross_entropy_matches_torch(rng):
+    T, h, V = 6, 10, 17
+    y = rng.standard_normal((T, h))
+    gf = rng.uniform(0.5, 2.0, h)
+    w = rng.standard_normal((V, h)) * 0.5
+    tgt = rng.integers(0, V, T)
+    out = oracle.lm_head_cross_entropy(y, gf, w, tgt, 1e-6)
+    ty, tg, tw = (torch.tensor(a, requires_grad=True) for a in (y, gf, w))
+    z = F.linear(F.rms_norm(ty, (h,), tg, eps=1e-6), tw)
+    loss = F.cross_entropy(z, torch.tensor(tgt), reduction="mean")
+    loss.backward()
+    np.testing.assert_allclose(out["loss"], loss.item(), rtol=1e-13)
+    np.testing.assert_allclose(out["loss_partials"],
+                               F.cross_entropy(z.detach(), torch.tensor(tgt), reduction="none").numpy(),
+                               rtol=1e-12)
+    np.testing.assert_allclose(out["dy_last"], ty.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(out["dg_final"], tg.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(out["dw_lm"], tw.grad.numpy(), rtol=1e-10, atol=1e-14)
+
+
+# ----------------------------------------------------------- Clip + AdamW
+
+def test_global_clip(rng):
+    grads = [rng.standard_normal(s) for s in ((3, 4), (7,), (2, 2, 2))]
+    norm, scale, clipped = oracle.global_clip(grads, 1.0)
+    assert norm > 1.0
+    total = math.sqrt(sum(float(np.sum(g * g)) for g in clipped))
+    assert abs(total - 1.0) < 1e-14
+    tg = [torch.tensor(g) for g in grads]
+    params = [torch.nn.Parameter(torch.zeros_like(g)) for g in tg]
+    for prm, g in zip(params, tg):
+        prm.grad = g.clone()
+    tnorm = torch.nn.utils.clip_grad_norm_(params, 1.0)
+    np.testing.assert_allclose(norm, tnorm.item(), rtol=1e-14)
+    for c, prm in zip(clipped, params):
+        np.testing.assert_allclose(c, prm.grad.numpy(), rtol=1e-5)  # torch adds 1e-6 to the norm
+    n2, s2, c2 = oracle.global_clip([g * 1e-3 for g in grads], 1.0)
+    assert s2 == 1.0 and n2 < 1.0
+
+
+def test_adamw_closed_forms_and_torch(rng):
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    w, g = rng.standard_normal(100), rng.standard_normal(100)
+    z = np.zeros(100)
+    w1, m1, v1 = oracle.adamw_update(w, g, z, z, step=1, **hp)
+    np.testing.assert_allclose(w1 - w, -hp["lr"] * (g / (np.abs(g) + hp["eps"]) + hp["weight_decay"] * w),
+                               rtol=0, atol=1e-15)
+    w0, _, _ = oracle.adamw_update(w, z, z, z, step=1, **hp)
+    np.testing.assert_allclose(w0 - w, -hp["lr"] * hp["weight_decay"] * w, rtol=0, atol=1e-15)
+    # three steps against torch.optim.AdamW in float64
+    prm = torch.nn.Parameter(torch.tensor(w))
+    opt = torch.optim.AdamW([prm], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["weight_decay"])
+    ww, mm, vv = w, z, z
+    for step in range(1, 4):
+        gs = rng.standard_normal(100)
+        prm.grad = torch.tensor(gs)
+        opt.step()
+        ww, mm, vv = oracle.adamw_update(ww, gs, mm, vv, step=step, **hp)
+    np.testing.assert_allclose(ww, prm.detach().numpy(), rtol=1e-13)
+    st = opt.state[prm]
+    np.testing.assert_allclose(mm, st["exp_avg"].numpy(), rtol=1e-13)
+    np.testing.assert_allclose(vv, st["exp_avg_sq"].numpy(), rtol=1e-13)
+
+
+def test_toy_lm_head_converges():
+    spec = json.load(open(os.path.join(GOLDEN, "toy_lm_head_convergence.json")))
+    h, V = spec["hidden"], spec["vocab"]
+    hid = np.array([((i * 7 + 3) % 100) / 100.0 - 0.5 for i in range(4 * h)]).reshape(4, h)
+    w = np.array([((i * 13 + 7) % 100) / 100.0 - 0.5 for i in range(V * h)]).reshape(V, h)
+    m = np.zeros_like(w)
+    v = np.zeros_like(w)
+    losses = []
+    for step in range(1, spec["steps"] + 1):
+        out = oracle.lm_head_cross_entropy(hid, None, w, spec["targets"], 1e-6)
+        losses.append(out["loss"])
+        w, m, v = oracle.adamw_update(w, out["dw_lm"], m, v, lr=spec["lr"], beta1=0.9, beta2=0.999,
+                                      eps=1e-8, weight_decay=0.01, step=step)
+    assert min(losses) < spec["required_ratio_best_over_first"] * losses[0]
+
+
+# --------------------------------------------------------------------- NF4
+
+def _normal_quantile(p):
+    """Inverse of the standard normal CDF by bisection on math.erf (an
+    independent route to the quantiles the codebook is built from)."""
+    lo, hi = -10.0, 10.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if 0.5 * (1.0 + math.erf(mid / math.sqrt(2.0))) < p:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def test_nf4_codebook_invariants():
+    L = oracle.nf4_codebook()
+    assert L.dtype == np.float32 and L.size == 16
+    assert np.all(np.diff(L) > 0)
+    assert L[0] == -1.0 and L[7] == 0.0 and L[15] == 1.0
+    assert np.sum(L < 0) == 7 and np.sum(L > 0) == 8
+    delta = 0.5 * ((1 - 1 / 30) + (1 - 1 / 32))
+    pos = [_normal_quantile(delta + (0.5 - delta) * i / 8) for i in range(8)]
+    neg = [-_normal_quantile(delta + (0.5 - delta) * i / 7) for i in range(7)]
+    ref = np.sort(np.array(pos + neg + [0.0])) / max(pos)
+    np.testing.assert_allclose(L, ref.astype(np.float32), rtol=0, atol=2e-7)
+
+
+def test_nf4_quantize_properties(rng):
+    w = (rng.standard_normal((8, 64 * 3)) * 0.02).astype(np.float32)
+    w[3, :64] = 0.0  # a zero block
+    packed, scales, codes = oracle.nf4_quantize(w)
+    L = oracle.nf4_codebook()
+    blocks = w.reshape(-1, 64)
+    np.testing.assert_array_equal(scales, np.abs(blocks).max(1))
+    # the absmax element maps to the +-1 level exactly
+    for b in range(blocks.shape[0]):
+        if scales[b] > 0:
+            j = int(np.argmax(np.abs(blocks[b])))
+            assert codes[b * 64 + j] == (15 if blocks[b, j] > 0 else 0)
+        else:
+            assert np.all(codes[b * 64:(b + 1) * 64] == 7)
+    # nibble order: element 2i in the low nibble of byte i
+    np.testing.assert_array_equal(packed & 0xF, codes[0::2])
+    np.testing.assert_array_equal(packed >> 4, codes[1::2])
+    # brute force nearest level on the float32 ratio (ties: lower code)
+    x = (blocks / np.where(scales > 0, scales, 1)[:, None]).astype(np.float32).astype(np.float64)
+    dist = np.abs(x.reshape(-1)[:, None] - L.astype(np.float64)[None, :])
+    brute = np.argmin(dist, axis=1)
+    brute[np.repeat(scales == 0, 64)] = 7
+    np.testing.assert_array_equal(codes, brute)
+    # error bound: half the largest gap between neighbouring levels
+    deq = oracle.nf4_dequantize(packed, scales, w.shape)
+    bound = np.repeat(scales, 64).reshape(w.shape) * (np.max(np.diff(L.astype(np.float64))) / 2)
+    assert np.all(np.abs(deq - w) <= bound + 1e-12)
+    # round trip: a tensor built from levels quantizes back to its codes
+    c2 = rng.integers(0, 16, w.size).astype(np.uint8)
+    c2[0::64] = 15  # every block holds +1 so its absmax is the scale
+    a2 = rng.uniform(0.01, 0.05, w.size // 64).astype(np.float32)
+    w2 = (L[c2].reshape(-1, 64) * a2[:, None]).astype(np.float32)
+    _, s3, c3 = oracle.nf4_quantize(w2)
+    np.testing.assert_array_equal(s3, a2)
+    np.testing.assert_array_equal(c3, c2)
+
+
+# -------------------------------------------------------------------- LoRA
+
+def test_lora_zero_b_and_merge(rng):
+    x = rng.standard_normal((5, 12))
+    w = rng.standard_normal((9, 12))
+    a = rng.standard_normal((4, 12))
+    b0 = np.zeros((9, 4))
+    dy = rng.standard_normal((5, 9))
+    np.testing.assert_array_equal(oracle.lora_linear_fwd(x, w, a, b0, 2.0), x @ w.T)
+    dx, da, db = oracle.lora_linear_bwd(x, w, a, b0, dy, 2.0)
+    assert np.all(da == 0.0)
+    np.testing.assert_allclose(dx, dy @ w, rtol=1e-14)
+    b = rng.standard_normal((9, 4))
+    merged = x @ (w + 2.0 * b @ a).T
+    np.testing.assert_allclose(oracle.lora_linear_fwd(x, w, a, b, 2.0), merged, rtol=1e-12)
+    dx, da, db = oracle.lora_linear_bwd(x, w, a, b, dy, 2.0)
+    f = lambda aa, bb, xx: float(np.sum(oracle.lora_linear_fwd(xx, w, aa, bb, 2.0) * dy))
+    for theta, g, fn in ((a, da, lambda t: f(t, b, x)), (b, db, lambda t: f(a, t, x)),
+                         (x, dx, lambda t: f(a, b, t))):
+        v = rng.standard_normal(theta.shape)
+        num = fd_directional(fn, theta, v, 1e-6)
+        assert abs(num - np.sum(g * v)) < 1e-7 * max(1.0, abs(num))
+
+
+def test_nf4_block_reduces_to_block_when_b_is_zero(rng):
+    c = synth.TINY_BLOCK
+    inp = synth.nf4_lora_inputs(c, rank=4)
+    deq = {}
+    for n in synth.PROJ_NAMES:
+        packed, scales, _ = oracle.nf4_quantize(inp["params"][n])
+        deq[n] = oracle.nf4_dequantize(packed, scales, inp["params"][n].shape)
+    gam = {n: inp["params"][n] for n in ("g_in", "g_post", "g_q", "g_k")}
+    y, cache = oracle.nf4_block_forward(c, gam, deq, inp["lora_a"], inp["lora_b"], inp["x"], 2.0)
+    y_ref, cache_ref = block_forward(c, dict(gam, **deq), inp["x"])
+    np.testing.assert_array_equal(y, y_ref)
+    dx, da, db = oracle.nf4_block_backward(c, gam, deq, inp["lora_a"], inp["lora_b"], cache,
+                                           inp["dy"], 2.0)
+    dx_ref, _ = block_backward(c, dict(gam, **deq), cache_ref, inp["dy"])
+    np.testing.assert_allclose(dx, dx_ref, rtol=1e-13, atol=1e-15)
+    for n in synth.PROJ_NAMES:
+        assert np.all(da[n] == 0.0)
+        assert np.any(db[n] != 0.0)
