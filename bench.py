@@ -1,0 +1,224 @@
+"""Benchmark of the decoder-block training step on one MI355X.
+
+Headline: train tokens/s of one Qwen3-4B-shaped block forward + backward
+(hidden 2560, 32 heads, 8 KV heads, head_dim 128, intermediate 9728,
+seq 512, batch 1; fp32 master weights, fp16 GEMM operands with fp32
+accumulate), inputs resident in HBM, timed with HIP events over exactly
+--steps steps after --warmup untimed ones.
+
+Also reported in the same JSON line:
+  roofline      the GEMM kernels of one step (the dominant cost), replayed
+                launch by launch with HIP events on the launch stream:
+                algorithmic FLOPs / summed launch durations vs the dense
+                fp16 MFMA peak;
+  cpu_baseline  the CPU oracle (numpy float64) on a bounded sample of the
+                same workload, on this host's cores;
+  extra         the 36-layer stack training step (fused CE, global clip,
+                AdamW), the frozen-NF4 + LoRA block at seq 2048, and the
+                block step with clip + AdamW.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_F16_PEAK = 2516.6   # TFLOP/s, dense
+MFMA_F32_PEAK = 157.3    # TFLOP/s
+HBM_PEAK = 8000.0        # GB/s
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def timed(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per step
+
+
+def block_gemms(c):
+    """(layout, M, N, K, accumulate) of every GEMM launch of one block
+    forward + backward, as the block entry points issue them."""
+    T, h, q, kv, I = c.tokens, c.hidden, c.q_dim, c.kv_dim, c.intermediate
+    qkv = q + 2 * kv
+    return [
+        (0, T, qkv, h, 0), (0, T, h, q, 1), (0, T, 2 * I, h, 0), (0, T, h, I, 1),   # forward NT
+        (1, T, I, h, 0), (2, h, I, T, 0),                                         # down: dX, dW
+        (1, T, h, 2 * I, 0), (2, 2 * I, h, T, 0),                                 # gate/up
+        (1, T, q, h, 0), (2, h, q, T, 0),                                         # o
+        (1, T, h, qkv, 0), (2, qkv, h, T, 0),                                     # qkv
+    ]
+
+
+def gemm_roofline(c, torch, qblk, reps):
+    """Replay the step's GEMMs, each bracketed by HIP events on the current
+    stream; return achieved TFLOP/s over summed launch durations."""
+    specs = block_gemms(c)
+    bufs = []
+    for (lay, M, N, K, acc) in specs:
+        a_shape = (M, K) if lay in (0, 1) else (K, M)
+        b_shape = (N, K) if lay == 0 else (K, N)
+        A = torch.randn(a_shape, device="cuda") * 0.02
+        B = torch.randn(b_shape, device="cuda")
+        C = torch.zeros((M, N), device="cuda")
+        bufs.append((lay, M, N, K, acc, A, a_shape[1], B, b_shape[1], C))
+    flops = sum(2.0 * M * N * K for (_, M, N, K, _) in specs)
+    prec = c.gemm_precision
+
+    def run_all(events=None):
+        for i, (lay, M, N, K, acc, A, lda, B, ldb, C) in enumerate(bufs):
+            if events:
+                events[i][0].record()
+            qblk.gemm(lay, prec, M, N, K, A, lda, B, ldb, C, N, acc)
+            if events:
+                events[i][1].record()
+
+    for _ in range(3):
+        run_all()
+    torch.cuda.synchronize()
+    total_ms, per = 0.0, np.zeros(len(bufs))
+    for _ in range(reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in bufs]
+        run_all(ev)
+        torch.cuda.synchronize()
+        d = np.array([a.elapsed_time(b) for a, b in ev])
+        per += d
+        total_ms += d.sum()
+    step_ms = total_ms / reps
+    achieved = flops / (step_ms * 1e-3) / 1e12
+    peak = MFMA_F16_PEAK if prec else MFMA_F32_PEAK
+    return {
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4), "traffic": None,
+        "kernel": "gemm_kernel (all 12 GEMM launches of one block fwd+bwd)",
+        "flops_per_step": flops, "gemm_ms_per_step": round(step_ms, 4),
+        "avg_launch_us": round(1e3 * step_ms / len(bufs), 2),
+        "per_launch_us": [round(1e3 * x / reps, 1) for x in per],
+    }
+
+
+def cpu_baseline(c, inp, budget_s=12.0):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    n, t0 = 0, time.perf_counter()
+    while True:
+        y, cache = oracle.block_forward(c, inp["params"], inp["x"])
+        oracle.block_backward(c, inp["params"], cache, inp["dy"])
+        n += 1
+        if time.perf_counter() - t0 > budget_s or n >= 5:
+            break
+    dt = (time.perf_counter() - t0) / n
+    return {"value": round(c.tokens / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} x full Qwen3-4B-shaped block fwd+bwd (512 tokens), numpy float64, "
+                      f"{dt:.2f} s each"}
+
+
+def extra_stack(torch, qblk, synth, steps, warmup):
+    from bwd_rmsnorm_qkv_amd.stack import StackStep
+    st = StackStep(synth.STACK36_SMALL, synth.STACK_LAYERS, synth.STACK_VOCAB)
+    st.load(synth.stack_inputs())
+    ms = timed(st.step, steps, warmup, torch)
+    return {"workload": "36-layer stack (h512, 8 heads, 2 kv, d64, I1408), seq 1024, vocab 151936, fp32: "
+                        "fwd + fused CE + bwd + global clip + AdamW, loss partials to host",
+            "ms_per_step": round(ms, 3), "tokens_per_s": round(synth.STACK36_SMALL.tokens / ms * 1e3, 1)}
+
+
+def extra_nf4(torch, qblk, synth, steps, warmup):
+    from bwd_rmsnorm_qkv_amd.runtime import Nf4Block
+    c = synth.NF4_LORA_QWEN3_4B
+    blk = Nf4Block(c, synth.LORA_RANK, synth.LORA_ALPHA)
+    blk.load(synth.nf4_lora_inputs(c, b_std=1e-3))
+    ms = timed(blk.fwd_bwd, steps, warmup, torch)
+    return {"workload": "frozen NF4 + LoRA r16 Qwen3-4B block, seq 2048, fp16 operands: fwd + bwd (dx, LoRA grads)",
+            "ms_per_step": round(ms, 3), "tokens_per_s": round(c.tokens / ms * 1e3, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); nothing here shards across GPUs.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from bwd_rmsnorm_qkv_amd import qblk, synth
+    from bwd_rmsnorm_qkv_amd.runtime import Block, dev, empty
+
+    torch.cuda.set_device(0)
+    qblk.lib()
+    c = synth.QWEN3_4B_BLOCK
+    log("generating Qwen3-4B-shaped block inputs")
+    inp = synth.block_inputs(c)
+    P = {k: dev(v) for k, v in inp["params"].items()}
+    X, DY = dev(inp["x"]), dev(inp["dy"])
+    G = {k: empty(v.shape) for k, v in inp["params"].items()}
+    blk = Block(c)
+
+    def step():
+        blk.forward(P, X)
+        blk.backward(P, X, DY, G)
+
+    log("timing block fwd+bwd")
+    ms = timed(step, args.steps, args.warmup, torch)
+    value = c.tokens / (ms * 1e-3)
+    log(f"block fwd+bwd {ms:.4f} ms/step, {value:.0f} tokens/s")
+    roof = gemm_roofline(c, torch, qblk, reps=max(5, args.steps // 2))
+    log(f"GEMM roofline {roof['achieved']} TFLOP/s ({roof['frac']*100:.1f}% of peak)")
+    out = {
+        "metric": "train tokens/s per block fwd+bwd (Qwen3-4B shape); % MFMA peak, % HBM BW",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16 GEMM operands, fp32 accumulate/master",
+        "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights)",
+        "config": {"workload": "Qwen3-4B-shaped decoder block fwd+bwd", "hidden": c.hidden, "heads": c.heads,
+                   "kv_heads": c.kv_heads, "head_dim": c.head_dim, "intermediate": c.intermediate,
+                   "seq": c.seq, "batch": c.batch, "global_batch": c.batch, "seq_len": c.seq,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_extra:
+        extra = {}
+        for name, fn in (("stack36_train_step", extra_stack), ("nf4_lora_block", extra_nf4)):
+            try:
+                log(f"extra: {name}")
+                extra[name] = fn(torch, qblk, synth, max(3, args.steps // 10), 2)
+            except Exception as e:  # reported, never silently dropped
+                extra[name] = {"error": repr(e)}
+        out["extra"] = extra
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(c, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,316 @@
+// C-ABI entry points of libqblk: argument checks, workspace sizes, and the
+// calls into the kernels. Declarations and documentation: include/qblk.h
+// and include/qblk_ops.h.
+#include "../../include/qblk.h"
+#include "../../include/qblk_ops.h"
+#include "attention.h"
+#include "block.h"
+#include "gemm.h"
+#include "norms.h"
+#include "step.h"
+
+using namespace qblk;
+
+namespace {
+
+hipStream_t S(qblk_stream_t s) { return (hipStream_t)s; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+// ------------------------------------------------------------------ block
+
+int32_t qblk_block_workspace_size(const qblk_config* cfg, size_t* saved_bytes, size_t* scratch_bytes) {
+  QBLK_TRY(check_config(cfg));
+  Saved s;
+  Scratch w;
+  size_t a = 0, b = 0;
+  carve_saved(*cfg, nullptr, s, a);
+  carve_scratch(*cfg, nullptr, w, b);
+  if (saved_bytes) *saved_bytes = a;
+  if (scratch_bytes) *scratch_bytes = b;
+  return QBLK_OK;
+}
+
+static int check_params(const qblk_block_params* p) {
+  if (!p) return fail(QBLK_EINVAL, "params is NULL");
+  const void* ptrs[] = {p->w_q, p->w_k, p->w_v, p->w_o, p->w_gate, p->w_up, p->w_down,
+                        p->g_in, p->g_post, p->g_q, p->g_k};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return fail(QBLK_EINVAL, "params: null or misaligned (16 B) pointer");
+  return QBLK_OK;
+}
+
+int32_t qblk_block_forward(const qblk_config* cfg, const qblk_block_params* p, const float* x, float* y,
+                           void* saved, size_t saved_bytes, void* scratch, size_t scratch_bytes,
+                           qblk_stream_t stream) {
+  (void)scratch;
+  (void)scratch_bytes;
+  QBLK_TRY(check_config(cfg));
+  QBLK_TRY(check_params(p));
+  if (!x || !y || !saved || !aligned16(x) || !aligned16(y) || !aligned16(saved))
+    return fail(QBLK_EINVAL, "block_forward: null or misaligned buffer");
+  Saved s;
+  size_t need = 0;
+  carve_saved(*cfg, nullptr, s, need);
+  if (saved_bytes < need) return fail(QBLK_EINVAL, "block_forward: saved workspace %zu < %zu", saved_bytes, need);
+  carve_saved(*cfg, saved, s, need);
+  return dense_block_forward(*cfg, *p, x, y, s, S(stream));
+}
+
+int32_t qblk_block_backward(const qblk_config* cfg, const qblk_block_params* p, const float* x, const float* dy,
+                            const void* saved, size_t saved_bytes, float* dx, const qblk_block_grads* grads,
+                            void* scratch, size_t scratch_bytes, qblk_stream_t stream) {
+  QBLK_TRY(check_config(cfg));
+  QBLK_TRY(check_params(p));
+  if (!grads) return fail(QBLK_EINVAL, "block_backward: grads is NULL");
+  const void* gp[] = {grads->w_q, grads->w_k, grads->w_v, grads->w_o, grads->w_gate, grads->w_up,
+                      grads->w_down, grads->g_in, grads->g_post, grads->g_q, grads->g_k};
+  for (const void* q : gp)
+    if (!q || !aligned16(q)) return fail(QBLK_EINVAL, "block_backward: null or misaligned gradient pointer");
+  if (!x || !dy || !dx || !saved || !scratch || !aligned16(x) || !aligned16(dy) || !aligned16(dx) ||
+      !aligned16(saved) || !aligned16(scratch))
+    return fail(QBLK_EINVAL, "block_backward: null or misaligned buffer");
+  Saved s;
+  Scratch w;
+  size_t need_s = 0, need_w = 0;
+  carve_saved(*cfg, nullptr, s, need_s);
+  carve_scratch(*cfg, nullptr, w, need_w);
+  if (saved_bytes < need_s) return fail(QBLK_EINVAL, "block_backward: saved workspace %zu < %zu", saved_bytes, need_s);
+  if (scratch_bytes < need_w)
+    return fail(QBLK_EINVAL, "block_backward: scratch workspace %zu < %zu", scratch_bytes, need_w);
+  carve_saved(*cfg, (void*)saved, s, need_s);
+  carve_scratch(*cfg, scratch, w, need_w);
+  return dense_block_backward(*cfg, *p, *grads, x, dy, s, dx, w, S(stream));
+}
+
+// ------------------------------------------------------- cross-entropy
+
+static void ce_layout(int T, int h, int V, float** hf, float** z, float** dhf, float** red, size_t* bytes,
+                      void* base) {
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    off = (off + 255) & ~(size_t)255;
+    float* p = base ? (float*)((char*)base + off) : nullptr;
+    off += n * sizeof(float);
+    return p;
+  };
+  *hf = take((size_t)T * h);
+  *z = take((size_t)T * V);
+  *dhf = take((size_t)T * h);
+  *red = take(rmsnorm_bwd_scratch(T, h) / sizeof(float) + T);
+  *bytes = off;
+}
+
+int32_t qblk_cross_entropy_workspace_size(int32_t tokens, int32_t hidden, int32_t vocab, size_t* scratch_bytes) {
+  if (tokens <= 0 || hidden <= 0 || vocab <= 0) return fail(QBLK_EINVAL, "cross_entropy: bad sizes");
+  float *a, *b, *c, *d;
+  size_t n = 0;
+  ce_layout(tokens, hidden, vocab, &a, &b, &c, &d, &n, nullptr);
+  if (scratch_bytes) *scratch_bytes = n;
+  return QBLK_OK;
+}
+
+int32_t qblk_fused_cross_entropy(int32_t tokens, int32_t hidden, int32_t vocab, float eps, const float* y_last,
+                                 const float* g_final, const float* w_lm, const int32_t* targets,
+                                 float loss_scale, float* loss_partials, int32_t* argmax, float* dy_last,
+                                 float* dg_final, float* dw_lm, void* scratch, size_t scratch_bytes,
+                                 qblk_stream_t stream) {
+  if (tokens <= 0 || hidden <= 0 || vocab <= 0) return fail(QBLK_EINVAL, "cross_entropy: bad sizes");
+  if (hidden % 4 || vocab % 4) return fail(QBLK_EINVAL, "cross_entropy: hidden and vocab must be multiples of 4");
+  if (!y_last || !w_lm || !targets || !loss_partials || !dy_last || !dw_lm || !scratch)
+    return fail(QBLK_EINVAL, "cross_entropy: null pointer");
+  if (g_final && !dg_final) return fail(QBLK_EINVAL, "cross_entropy: dg_final is NULL");
+  if (g_final) QBLK_TRY(rmsnorm_check(tokens, hidden));
+  float *hf, *z, *dhf, *red;
+  size_t need = 0;
+  ce_layout(tokens, hidden, vocab, &hf, &z, &dhf, &red, &need, nullptr);
+  if (scratch_bytes < need) return fail(QBLK_EINVAL, "cross_entropy: scratch %zu < %zu", scratch_bytes, need);
+  ce_layout(tokens, hidden, vocab, &hf, &z, &dhf, &red, &need, scratch);
+  hipStream_t st = S(stream);
+  const float* h_in = y_last;
+  if (g_final) {
+    QBLK_TRY(rmsnorm_forward(tokens, hidden, eps, y_last, nullptr, g_final, hf, nullptr, nullptr, red, st));
+    h_in = hf;
+  }
+  GemmDesc f;  // z = hf W_lm^T
+  f.layout = Layout::NT; f.prec = Prec::F32;
+  f.M = tokens; f.N = vocab; f.K = hidden;
+  f.a = h_in; f.lda = hidden;
+  f.b = seg1(w_lm, vocab); f.ldb = hidden;
+  f.c = seg1(z, tokens); f.ldc = vocab;
+  QBLK_TRY(gemm(f, st));
+  QBLK_TRY(ce_rows(tokens, vocab, z, targets, loss_scale, loss_partials, argmax, st));
+  GemmDesc a;  // dhf = dz W_lm
+  a.layout = Layout::NN; a.prec = Prec::F32;
+  a.M = tokens; a.N = hidden; a.K = vocab;
+  a.a = z; a.lda = vocab;
+  a.b = seg1(w_lm, vocab); a.ldb = hidden;
+  a.c = seg1(g_final ? dhf : dy_last, tokens); a.ldc = hidden;
+  QBLK_TRY(gemm(a, st));
+  GemmDesc b;  // dW_lm = dz^T hf
+  b.layout = Layout::TN; b.prec = Prec::F32;
+  b.M = vocab; b.N = hidden; b.K = tokens;
+  b.a = z; b.lda = vocab;
+  b.b = seg1(h_in, tokens); b.ldb = hidden;
+  b.c = seg1(dw_lm, vocab); b.ldc = hidden;
+  QBLK_TRY(gemm(b, st));
+  if (g_final)
+    QBLK_TRY(rmsnorm_backward(tokens, hidden, eps, y_last, g_final, dhf, nullptr, dy_last, dg_final, red, st));
+  return QBLK_OK;
+}
+
+int32_t qblk_cross_entropy_rows(int32_t tokens, int32_t vocab, float* z, const int32_t* targets, float loss_scale,
+                                float* loss_partials, int32_t* argmax, qblk_stream_t stream) {
+  if (tokens <= 0 || vocab <= 0) return fail(QBLK_EINVAL, "cross_entropy_rows: bad sizes");
+  if (!z || !targets || !loss_partials) return fail(QBLK_EINVAL, "cross_entropy_rows: null pointer");
+  if (vocab % 4 == 0 && !aligned16(z)) return fail(QBLK_EINVAL, "cross_entropy_rows: z must be 16-byte aligned");
+  return ce_rows(tokens, vocab, z, targets, loss_scale, loss_partials, argmax, S(stream));
+}
+
+// ------------------------------------------------------- clip and AdamW
+
+int32_t qblk_clip_workspace_size(int32_t n, const int64_t* numel, size_t* scratch_bytes) {
+  if (n <= 0 || !numel) return fail(QBLK_EINVAL, "clip: n=%d", n);
+  if (scratch_bytes) *scratch_bytes = clip_scratch(n, numel);
+  return QBLK_OK;
+}
+
+int32_t qblk_clip_grad_norm(int32_t n, float* const* grads, const int64_t* numel, float max_norm, int32_t apply,
+                            float* norm_dev, float* scale_dev, void* scratch, size_t scratch_bytes,
+                            qblk_stream_t stream) {
+  if (n <= 0 || !grads || !numel || !norm_dev || !scale_dev || !scratch)
+    return fail(QBLK_EINVAL, "clip: null argument or n <= 0");
+  if (!(max_norm > 0.f)) return fail(QBLK_EINVAL, "clip: max_norm must be positive");
+  for (int i = 0; i < n; ++i)
+    if (!grads[i] || numel[i] < 0) return fail(QBLK_EINVAL, "clip: tensor %d", i);
+  if (scratch_bytes < clip_scratch(n, numel)) return fail(QBLK_EINVAL, "clip: scratch too small");
+  return clip_grad_norm(n, grads, numel, max_norm, apply, norm_dev, scale_dev, scratch, S(stream));
+}
+
+int32_t qblk_adamw_step(int32_t n, float* const* w, const float* const* g, float* const* m, float* const* v,
+                        const int64_t* numel, float lr, float beta1, float beta2, float eps, float weight_decay,
+                        int32_t step, const float* grad_scale_dev, qblk_stream_t stream) {
+  if (n <= 0 || !w || !g || !m || !v || !numel) return fail(QBLK_EINVAL, "adamw: null argument or n <= 0");
+  if (step < 1) return fail(QBLK_EINVAL, "adamw: step must be >= 1");
+  for (int i = 0; i < n; ++i)
+    if (!w[i] || !g[i] || !m[i] || !v[i] || numel[i] < 0) return fail(QBLK_EINVAL, "adamw: tensor %d", i);
+  return adamw(n, w, g, m, v, numel, lr, beta1, beta2, eps, weight_decay, step, grad_scale_dev, S(stream));
+}
+
+// ---------------------------------------------------------------- NF4
+
+int32_t qblk_nf4_quantize(const float* w, int64_t numel, uint8_t* codes, float* absmax, qblk_stream_t stream) {
+  if (numel <= 0 || numel % 64) return fail(QBLK_EINVAL, "nf4_quantize: numel %lld not a positive multiple of 64", (long long)numel);
+  if (!w || !codes || !absmax) return fail(QBLK_EINVAL, "nf4_quantize: null pointer");
+  return nf4_quantize(w, numel, codes, absmax, S(stream));
+}
+
+int32_t qblk_nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t numel, float* w,
+                            qblk_stream_t stream) {
+  if (!w || !codes || !absmax) return fail(QBLK_EINVAL, "nf4_dequantize: null pointer");
+  return nf4_dequantize(codes, absmax, numel, w, S(stream));
+}
+
+// ------------------------------------------------------- single steps
+
+int32_t qblk_gemm(int32_t layout, int32_t precision, int32_t M, int32_t N, int32_t K, const float* A, int64_t lda,
+                  const float* B, int64_t ldb, float* C, int64_t ldc, int32_t accumulate, qblk_stream_t stream) {
+  if (layout < 0 || layout > 2 || precision < 0 || precision > 1) return fail(QBLK_EINVAL, "gemm: layout/precision");
+  if (lda % 4 || ldb % 4) return fail(QBLK_EINVAL, "gemm: lda and ldb must be multiples of 4");
+  if (!A || !B || !C || !aligned16(A) || !aligned16(B)) return fail(QBLK_EINVAL, "gemm: null or misaligned operand");
+  GemmDesc d;
+  d.layout = (Layout)layout;
+  d.prec = (Prec)precision;
+  d.M = M; d.N = N; d.K = K;
+  d.a = A; d.lda = lda;
+  const int brows = d.layout == Layout::NT ? N : K;
+  d.b = seg1(B, brows); d.ldb = ldb;
+  d.c = seg1(C, M); d.ldc = ldc;
+  d.accumulate = accumulate;
+  return gemm(d, S(stream));
+}
+
+int32_t qblk_rmsnorm_workspace_size(int32_t rows, int32_t n, size_t* scratch_bytes) {
+  QBLK_TRY(rmsnorm_check(rows, n));
+  if (scratch_bytes) *scratch_bytes = rmsnorm_bwd_scratch(rows, n);
+  return QBLK_OK;
+}
+
+int32_t qblk_rmsnorm_forward(int32_t rows, int32_t n, float eps, const float* x, const float* res, const float* gamma,
+                             float* y, float* sum_out, float* rho, void* scratch, size_t scratch_bytes,
+                             qblk_stream_t stream) {
+  (void)scratch;
+  (void)scratch_bytes;
+  if (!x || !gamma || !y || !rho) return fail(QBLK_EINVAL, "rmsnorm_forward: null pointer");
+  if (res && !sum_out) return fail(QBLK_EINVAL, "rmsnorm_forward: sum_out needed with res");
+  return rmsnorm_forward(rows, n, eps, x, res, gamma, y, nullptr, sum_out, rho, S(stream));
+}
+
+int32_t qblk_rmsnorm_backward(int32_t rows, int32_t n, float eps, const float* x, const float* gamma,
+                              const float* dy, const float* dres, float* dx, float* dgamma, void* scratch,
+                              size_t scratch_bytes, qblk_stream_t stream) {
+  if (!x || !gamma || !dy || !dx || !dgamma || !scratch) return fail(QBLK_EINVAL, "rmsnorm_backward: null pointer");
+  QBLK_TRY(rmsnorm_check(rows, n));
+  if (scratch_bytes < rmsnorm_bwd_scratch(rows, n)) return fail(QBLK_EINVAL, "rmsnorm_backward: scratch too small");
+  return rmsnorm_backward(rows, n, eps, x, gamma, dy, dres, dx, dgamma, (float*)scratch, S(stream));
+}
+
+static int check_attn_ld(int32_t heads_or_kv, int32_t d, int64_t ld) {
+  if (ld < (int64_t)heads_or_kv * d || ld % 4) return fail(QBLK_EINVAL, "attention: leading dimension");
+  return 0;
+}
+
+int32_t qblk_attention_forward(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                               int32_t precision, const float* q, int64_t ldq, const float* k, int64_t ldk,
+                               const float* v, int64_t ldv, float* o, int64_t ldo, float* lse, qblk_stream_t stream) {
+  QBLK_TRY(attention_check(batch, seq, heads, kv_heads, head_dim));
+  if (!q || !k || !v || !o || !lse) return fail(QBLK_EINVAL, "attention_forward: null pointer");
+  QBLK_TRY(check_attn_ld(heads, head_dim, ldq));
+  QBLK_TRY(check_attn_ld(kv_heads, head_dim, ldk));
+  QBLK_TRY(check_attn_ld(kv_heads, head_dim, ldv));
+  QBLK_TRY(check_attn_ld(heads, head_dim, ldo));
+  AttnArgs a{};
+  a.batch = batch; a.seq = seq; a.heads = heads; a.kv_heads = kv_heads; a.head_dim = head_dim;
+  a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldk; a.v = v; a.ldv = ldv; a.o = o; a.ldo = ldo; a.lse = lse;
+  return attention_forward(a, precision ? Prec::F16 : Prec::F32, S(stream));
+}
+
+int32_t qblk_attention_workspace_size(int32_t batch, int32_t seq, int32_t heads, size_t* scratch_bytes) {
+  if (batch <= 0 || seq <= 0 || heads <= 0) return fail(QBLK_EINVAL, "attention: bad sizes");
+  // head_dim 128 upper bound
+  if (scratch_bytes) *scratch_bytes = attention_bwd_scratch(batch, seq, heads, 128);
+  return QBLK_OK;
+}
+
+int32_t qblk_attention_backward(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                int32_t precision, const float* q, int64_t ldq, const float* k, int64_t ldk,
+                                const float* v, int64_t ldv, const float* o, int64_t ldo, const float* lse,
+                                const float* d_o, int64_t lddo, float* dq, int64_t lddq, float* dk, int64_t lddk,
+                                float* dv, int64_t lddv, void* scratch, size_t scratch_bytes, qblk_stream_t stream) {
+  QBLK_TRY(attention_check(batch, seq, heads, kv_heads, head_dim));
+  if (precision == 0 && head_dim > 64) return fail(QBLK_EUNSUPPORTED, "attention_backward: fp32 needs head_dim <= 64");
+  if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv || !scratch)
+    return fail(QBLK_EINVAL, "attention_backward: null pointer");
+  if (scratch_bytes < attention_bwd_scratch(batch, seq, heads, head_dim))
+    return fail(QBLK_EINVAL, "attention_backward: scratch too small");
+  QBLK_TRY(check_attn_ld(heads, head_dim, ldq));
+  QBLK_TRY(check_attn_ld(kv_heads, head_dim, ldk));
+  QBLK_TRY(check_attn_ld(kv_heads, head_dim, ldv));
+  QBLK_TRY(check_attn_ld(heads, head_dim, ldo));
+  QBLK_TRY(check_attn_ld(heads, head_dim, lddo));
+  QBLK_TRY(check_attn_ld(heads, head_dim, lddq));
+  QBLK_TRY(check_attn_ld(kv_heads, head_dim, lddk));
+  QBLK_TRY(check_attn_ld(kv_heads, head_dim, lddv));
+  AttnArgs a{};
+  a.batch = batch; a.seq = seq; a.heads = heads; a.kv_heads = kv_heads; a.head_dim = head_dim;
+  a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldk; a.v = v; a.ldv = ldv;
+  a.o = const_cast<float*>(o); a.ldo = ldo; a.lse = const_cast<float*>(lse);
+  a.d_o = d_o; a.lddo = lddo; a.dq = dq; a.lddq = lddq; a.dk = dk; a.lddk = lddk; a.dv = dv; a.lddv = lddv;
+  return attention_backward(a, precision ? Prec::F16 : Prec::F32, scratch, S(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,550 @@
+// GQA causal softmax attention, forward and backward, on MFMA (gfx950).
+//
+// cuda_block.rs page: compute_attention_cuda (QK^T, 1/sqrt(d), causal mask
+// keeping key j <= query i, row softmax, times V; query head h reads KV head
+// h / (heads/kv_heads)) and backward_attention (softmax backward, the
+// matmul backward and the GQA reduction of dK and dV over the query heads of
+// a group). Here the [heads, seq, seq] score matrix is never stored: the
+// forward keeps a running max and sum per query (log-sum-exp saved for the
+// backward), and the backward recomputes the probabilities tile by tile.
+//
+// Orientation. Tiles are 32 queries x 32 keys. The forward computes
+// S^T = K Q^T so that in each 32 x 32 accumulator a lane owns ONE query
+// (column l % 32) and 16 keys (rows 8g + 4(l/32) + r): the running max, the
+// sum and the rescale of the output are per-lane scalars, and P^T, still in
+// the accumulator, is directly the B operand of O^T += V^T P^T (the key
+// order of that product is chosen to match the accumulator rows; V is staged
+// transposed in LDS so the matching A operand is two short LDS reads).
+// The dQ kernel uses the same orientation; the dK/dV kernel swaps it
+// (S = Q K^T, a lane owns one key) so that dV^T += dO^T P and dK^T += Q^T dS
+// take the accumulator directly.
+//
+// Operands are rounded to fp16 while staged (Prec::F16, v_mfma_f32_32x32x16_f16)
+// or kept fp32 (Prec::F32, v_mfma_f32_32x32x2_f32); softmax math is fp32.
+// Head dims below 32 are zero-padded to 32.
+#include "attention.h"
+
+#include "../../include/qblk.h"
+
+namespace qblk {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <Prec P, int DP>
+struct AT;
+
+template <int DP>
+struct AT<Prec::F16, DP> {
+  using T = f16;
+  using Chunk = half8;
+  static constexpr int NC = DP / 16;  // contraction chunks over head_dim
+  static constexpr int PR = DP + 8;   // pitch of [32][DP] tiles
+  static constexpr int PT = 32 + 8;   // pitch of [DP][32] tiles
+  // Chunk c of a row: elements [16c + 8kh, 16c + 8kh + 8).
+  static __device__ __forceinline__ Chunk lds_chunk(const T* row, int c, int kh) {
+    return *(const half8*)(row + 16 * c + 8 * kh);
+  }
+  static __device__ __forceinline__ Chunk glb_chunk(const float* row, int c, int kh, int D) {
+    Chunk r;
+    const int d0 = 16 * c + 8 * kh;
+    if (d0 < D) {
+      const float4 a = *(const float4*)(row + d0), b = *(const float4*)(row + d0 + 4);
+      r[0] = (f16)a.x; r[1] = (f16)a.y; r[2] = (f16)a.z; r[3] = (f16)a.w;
+      r[4] = (f16)b.x; r[5] = (f16)b.y; r[6] = (f16)b.z; r[7] = (f16)b.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = (f16)0.f;
+    }
+    return r;
+  }
+  static __device__ __forceinline__ floatx16 mma(Chunk a, Chunk b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  // out[db] += Xt^T-block times the 32x32 accumulator p (keys/queries in
+  // accumulator row order). Xt is [DP][PT] with the contraction index
+  // contiguous.
+  static __device__ __forceinline__ void acc_product(const T* Xt, const floatx16& p, int lane,
+                                                     floatx16 (&out)[DP / 32]) {
+    const int i = lane & 31, kh = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      half8 b;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[j] = (f16)p[8 * s + j];
+#pragma unroll
+      for (int db = 0; db < DP / 32; ++db) {
+        const T* row = Xt + (db * 32 + i) * PT;
+        const half4 lo = *(const half4*)(row + 16 * s + 4 * kh);
+        const half4 hi = *(const half4*)(row + 16 * s + 8 + 4 * kh);
+        half8 a;
+        a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+        a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, out[db], 0, 0, 0);
+      }
+    }
+  }
+};
+
+template <int DP>
+struct AT<Prec::F32, DP> {
+  using T = float;
+  using Chunk = float4;
+  static constexpr int NC = DP / 8;  // chunk c: elements [8c + 4kh, 8c + 4kh + 4)
+  static constexpr int PR = DP + 4;
+  static constexpr int PT = 32 + 4;
+  static __device__ __forceinline__ Chunk lds_chunk(const T* row, int c, int kh) {
+    return *(const float4*)(row + 8 * c + 4 * kh);
+  }
+  static __device__ __forceinline__ Chunk glb_chunk(const float* row, int c, int kh, int D) {
+    const int d0 = 8 * c + 4 * kh;
+    return d0 < D ? *(const float4*)(row + d0) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  static __device__ __forceinline__ floatx16 mma(Chunk a, Chunk b, floatx16 c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, c, 0, 0, 0);
+    return c;
+  }
+  static __device__ __forceinline__ void acc_product(const T* Xt, const floatx16& p, int lane,
+                                                     floatx16 (&out)[DP / 32]) {
+    const int i = lane & 31, kh = lane >> 5;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int db = 0; db < DP / 32; ++db) {
+        const float4 a = *(const float4*)(Xt + (db * 32 + i) * PT + 8 * g + 4 * kh);
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, p[4 * g + 0], out[db], 0, 0, 0);
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, p[4 * g + 1], out[db], 0, 0, 0);
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, p[4 * g + 2], out[db], 0, 0, 0);
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, p[4 * g + 3], out[db], 0, 0, 0);
+      }
+    }
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ void put4(T* p, float4 v);
+template <>
+__device__ __forceinline__ void put4<float>(float* p, float4 v) {
+  *(float4*)p = v;
+}
+template <>
+__device__ __forceinline__ void put4<f16>(f16* p, float4 v) {
+  *(half4*)p = to_half4(v);
+}
+
+// 32 rows x DP columns (columns >= D and rows >= nvalid are zero) into
+// [32][PR]; optionally also transposed into [DP][PT].
+template <typename T, int DP, int PR, int PT, bool ROWS, bool TRANS>
+__device__ __forceinline__ void stage_tile(T* s, T* st, const float* g, int64_t ld, int nvalid,
+                                           int D, int tid, int nthr) {
+  constexpr int C4 = DP / 4;
+  for (int c = tid; c < 32 * C4; c += nthr) {
+    const int r = c / C4, d4 = (c % C4) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < nvalid && d4 < D) v = *(const float4*)(g + (int64_t)r * ld + d4);
+    if (ROWS) put4<T>(s + r * PR + d4, v);
+    if (TRANS) {
+      st[(d4 + 0) * PT + r] = (T)v.x;
+      st[(d4 + 1) * PT + r] = (T)v.y;
+      st[(d4 + 2) * PT + r] = (T)v.z;
+      st[(d4 + 3) * PT + r] = (T)v.w;
+    }
+  }
+}
+
+__device__ __forceinline__ float half_max(float v) { return fmaxf(v, __shfl_xor(v, 32, kWave)); }
+__device__ __forceinline__ float half_sum(float v) { return v + __shfl_xor(v, 32, kWave); }
+
+// ------------------------------------------------------------ forward
+// grid (q tiles, kv groups, batch); one wave per query head of the group.
+template <Prec P, int DP>
+__global__ __launch_bounds__(1024) void attn_fwd_kernel(const AttnArgs a) {
+  using A = AT<P, DP>;
+  using T = typename A::T;
+  __shared__ __attribute__((aligned(16))) T sK[32 * A::PR];
+  __shared__ __attribute__((aligned(16))) T sVt[DP * A::PT];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nthr = blockDim.x;
+  const int G = a.heads / a.kv_heads, grp = blockIdx.y, b = blockIdx.z;
+  const int h = grp * G + w;
+  const int D = a.head_dim, S = a.seq;
+  const int qt = blockIdx.x, q0 = qt * 32;
+  const int64_t tok0 = (int64_t)b * S;
+  const int i = lane & 31, kh = lane >> 5;
+  const float sc = kLog2e / sqrtf((float)D);
+
+  typename A::Chunk qc[A::NC];
+  {
+    const int qi = min(q0 + i, S - 1);
+    const float* row = a.q + (tok0 + qi) * a.ldq + (int64_t)h * D;
+#pragma unroll
+    for (int c = 0; c < A::NC; ++c) qc[c] = A::glb_chunk(row, c, kh, D);
+  }
+  floatx16 o[DP / 32];
+#pragma unroll
+  for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const int qi = q0 + i;
+
+  for (int kt = 0; kt <= qt; ++kt) {
+    const int kv0 = kt * 32;
+    __syncthreads();
+    stage_tile<T, DP, A::PR, A::PT, true, false>(sK, nullptr, a.k + (tok0 + kv0) * a.ldk + (int64_t)grp * D,
+                                                 a.ldk, min(32, S - kv0), D, tid, nthr);
+    stage_tile<T, DP, A::PR, A::PT, false, true>(nullptr, sVt, a.v + (tok0 + kv0) * a.ldv + (int64_t)grp * D,
+                                                 a.ldv, min(32, S - kv0), D, tid, nthr);
+    __syncthreads();
+    floatx16 s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < A::NC; ++c) s = A::mma(A::lds_chunk(sK + i * A::PR, c, kh), qc[c], s);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kj = kv0 + 8 * g + 4 * kh + r;
+        float v = s[4 * g + r] * sc;
+        if (kj > qi || kj >= S) v = -INFINITY;
+        s[4 * g + r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = half_max(mx);
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2f(m - mn);
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = exp2f(s[e] - mn);
+      s[e] = p;
+      ps += p;
+    }
+    l = l * alpha + half_sum(ps);
+    m = mn;
+#pragma unroll
+    for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+    A::acc_product(sVt, s, lane, o);
+  }
+  if (qi < S) {
+    const float inv = 1.0f / l;
+    float* orow = a.o + (tok0 + qi) * a.ldo + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = db * 32 + 8 * g + 4 * kh + r;
+          if (d < D) orow[d] = o[db][4 * g + r] * inv;
+        }
+    if (kh == 0) a.lse[((int64_t)b * a.heads + h) * S + qi] = (m + log2f(l)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------- backward
+// delta[b, h, s] = sum_d dO * O  (the softmax-backward row term).
+__global__ __launch_bounds__(256) void attn_delta_kernel(const AttnArgs a, float* delta) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t T = (int64_t)a.batch * a.seq;
+  if (item >= T * a.heads) return;
+  const int64_t t = item / a.heads;
+  const int h = (int)(item % a.heads);
+  const int D = a.head_dim;
+  const float* o = a.o + t * a.ldo + (int64_t)h * D;
+  const float* d = a.d_o + t * a.lddo + (int64_t)h * D;
+  float s = 0.f;
+  for (int j = lane; j < D; j += 64) s += o[j] * d[j];
+  s = wave_sum(s);
+  if (lane == 0) {
+    const int b = (int)(t / a.seq), sq = (int)(t % a.seq);
+    delta[((int64_t)b * a.heads + h) * a.seq + sq] = s;
+  }
+}
+
+// dQ: grid (q tiles, kv groups, batch); one wave per query head.
+template <Prec P, int DP>
+__global__ __launch_bounds__(1024) void attn_dq_kernel(const AttnArgs a, const float* delta) {
+  using A = AT<P, DP>;
+  using T = typename A::T;
+  __shared__ __attribute__((aligned(16))) T sK[32 * A::PR];
+  __shared__ __attribute__((aligned(16))) T sV[32 * A::PR];
+  __shared__ __attribute__((aligned(16))) T sKt[DP * A::PT];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nthr = blockDim.x;
+  const int G = a.heads / a.kv_heads, grp = blockIdx.y, b = blockIdx.z;
+  const int h = grp * G + w;
+  const int D = a.head_dim, S = a.seq;
+  const int qt = blockIdx.x, q0 = qt * 32;
+  const int64_t tok0 = (int64_t)b * S;
+  const int i = lane & 31, kh = lane >> 5;
+  const float sc = kLog2e / sqrtf((float)D);
+  const int qi = q0 + i, qc_i = min(qi, S - 1);
+
+  typename A::Chunk qc[A::NC], dc[A::NC];
+  {
+    const float* qrow = a.q + (tok0 + qc_i) * a.ldq + (int64_t)h * D;
+    const float* drow = a.d_o + (tok0 + qc_i) * a.lddo + (int64_t)h * D;
+#pragma unroll
+    for (int c = 0; c < A::NC; ++c) {
+      qc[c] = A::glb_chunk(qrow, c, kh, D);
+      dc[c] = A::glb_chunk(drow, c, kh, D);
+    }
+  }
+  const int64_t rowi = ((int64_t)b * a.heads + h) * S + qc_i;
+  const float lse2 = a.lse[rowi] * kLog2e;
+  const float dl = delta[rowi];
+  floatx16 dq[DP / 32];
+#pragma unroll
+  for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[db][e] = 0.f;
+
+  for (int kt = 0; kt <= qt; ++kt) {
+    const int kv0 = kt * 32, nv = min(32, S - kv0);
+    __syncthreads();
+    stage_tile<T, DP, A::PR, A::PT, true, true>(sK, sKt, a.k + (tok0 + kv0) * a.ldk + (int64_t)grp * D,
+                                                a.ldk, nv, D, tid, nthr);
+    stage_tile<T, DP, A::PR, A::PT, true, false>(sV, nullptr, a.v + (tok0 + kv0) * a.ldv + (int64_t)grp * D,
+                                                 a.ldv, nv, D, tid, nthr);
+    __syncthreads();
+    floatx16 s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s[e] = 0.f;
+      dp[e] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < A::NC; ++c) {
+      s = A::mma(A::lds_chunk(sK + i * A::PR, c, kh), qc[c], s);
+      dp = A::mma(A::lds_chunk(sV + i * A::PR, c, kh), dc[c], dp);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = 4 * g + r;
+        const int kj = kv0 + 8 * g + 4 * kh + r;
+        const float p = (kj > qi || kj >= S) ? 0.f : exp2f(s[e] * sc - lse2);
+        s[e] = p * (dp[e] - dl);  // dS^T, unscaled
+      }
+    A::acc_product(sKt, s, lane, dq);
+  }
+  if (qi < S) {
+    const float inv = 1.0f / sqrtf((float)D);
+    float* row = a.dq + (tok0 + qi) * a.lddq + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = db * 32 + 8 * g + 4 * kh + r;
+          if (d < D) row[d] = dq[db][4 * g + r] * inv;
+        }
+  }
+}
+
+// dK, dV per query head: grid (kv tiles, heads, batch); one wave. Results
+// go to per-head partial buffers [T, heads, D], summed over each group by
+// attn_gqa_reduce_kernel in a fixed order.
+template <Prec P, int DP>
+__global__ __launch_bounds__(64) void attn_dkv_kernel(const AttnArgs a, const float* delta,
+                                                      float* dk_part, float* dv_part) {
+  using A = AT<P, DP>;
+  using T = typename A::T;
+  __shared__ __attribute__((aligned(16))) T sQ[32 * A::PR];
+  __shared__ __attribute__((aligned(16))) T sQt[DP * A::PT];
+  __shared__ __attribute__((aligned(16))) T sO[32 * A::PR];   // dO rows
+  __shared__ __attribute__((aligned(16))) T sOt[DP * A::PT];  // dO transposed
+  __shared__ float sL[32], sDl[32];
+  const int lane = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int G = a.heads / a.kv_heads, grp = h / G;
+  const int D = a.head_dim, S = a.seq;
+  const int kt = blockIdx.x, kv0 = kt * 32;
+  const int64_t tok0 = (int64_t)b * S;
+  const int i = lane & 31, kh = lane >> 5;
+  const float sc = kLog2e / sqrtf((float)D);
+  const int kj = kv0 + i;  // this lane's key (column of every accumulator)
+
+  typename A::Chunk kc[A::NC], vc[A::NC];
+  {
+    const int kr = min(kj, S - 1);
+    const float* krow = a.k + (tok0 + kr) * a.ldk + (int64_t)grp * D;
+    const float* vrow = a.v + (tok0 + kr) * a.ldv + (int64_t)grp * D;
+#pragma unroll
+    for (int c = 0; c < A::NC; ++c) {
+      kc[c] = A::glb_chunk(krow, c, kh, D);
+      vc[c] = A::glb_chunk(vrow, c, kh, D);
+    }
+  }
+  floatx16 dk[DP / 32], dv[DP / 32];
+#pragma unroll
+  for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dk[db][e] = 0.f;
+      dv[db][e] = 0.f;
+    }
+  const int nqt = (S + 31) / 32;
+  for (int qt = kt; qt < nqt; ++qt) {
+    const int q0 = qt * 32, nv = min(32, S - q0);
+    __syncthreads();
+    stage_tile<T, DP, A::PR, A::PT, true, true>(sQ, sQt, a.q + (tok0 + q0) * a.ldq + (int64_t)h * D, a.ldq,
+                                                nv, D, lane, 64);
+    stage_tile<T, DP, A::PR, A::PT, true, true>(sO, sOt, a.d_o + (tok0 + q0) * a.lddo + (int64_t)h * D,
+                                                a.lddo, nv, D, lane, 64);
+    if (lane < 32) {
+      const int64_t ri = ((int64_t)b * a.heads + h) * S + min(q0 + lane, S - 1);
+      sL[lane] = a.lse[ri] * kLog2e;
+      sDl[lane] = delta[ri];
+    }
+    __syncthreads();
+    floatx16 s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s[e] = 0.f;
+      dp[e] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < A::NC; ++c) {
+      s = A::mma(A::lds_chunk(sQ + i * A::PR, c, kh), kc[c], s);
+      dp = A::mma(A::lds_chunk(sO + i * A::PR, c, kh), vc[c], dp);
+    }
+    // accumulator rows are queries q0 + 8g + 4kh + r, column is key kj
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = 4 * g + r, ql = 8 * g + 4 * kh + r;
+        const int qq = q0 + ql;
+        const float p = (kj > qq || qq >= S || kj >= S) ? 0.f : exp2f(s[e] * sc - sL[ql]);
+        s[e] = p;
+        dp[e] = p * (dp[e] - sDl[ql]);
+      }
+    A::acc_product(sOt, s, lane, dv);   // dV^T += dO^T P
+    A::acc_product(sQt, dp, lane, dk);  // dK^T += Q^T dS
+  }
+  if (kj < S) {
+    const float inv = 1.0f / sqrtf((float)D);
+    float* krow = dk_part + ((tok0 + kj) * a.heads + h) * (int64_t)D;
+    float* vrow = dv_part + ((tok0 + kj) * a.heads + h) * (int64_t)D;
+#pragma unroll
+    for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = db * 32 + 8 * g + 4 * kh + r;
+          if (d < D) {
+            krow[d] = dk[db][4 * g + r] * inv;
+            vrow[d] = dv[db][4 * g + r];
+          }
+        }
+  }
+}
+
+__global__ void attn_gqa_reduce_kernel(int64_t T, int heads, int kv_heads, int D,
+                                       const float* dk_part, const float* dv_part, float* dk,
+                                       int64_t lddk, float* dv, int64_t lddv) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t n = T * kv_heads * D;
+  if (idx >= n) return;
+  const int64_t t = idx / ((int64_t)kv_heads * D);
+  const int rem = (int)(idx % ((int64_t)kv_heads * D));
+  const int g = rem / D, j = rem % D;
+  const int G = heads / kv_heads;
+  float sk = 0.f, sv = 0.f;
+  for (int w = 0; w < G; ++w) {
+    const int64_t o = (t * heads + g * G + w) * (int64_t)D + j;
+    sk += dk_part[o];
+    sv += dv_part[o];
+  }
+  dk[t * lddk + g * D + j] = sk;
+  dv[t * lddv + g * D + j] = sv;
+}
+
+template <Prec P, int DP>
+int fwd_launch(const AttnArgs& a, hipStream_t st) {
+  const int G = a.heads / a.kv_heads;
+  dim3 grid((unsigned)ceil_div(a.seq, 32), (unsigned)a.kv_heads, (unsigned)a.batch);
+  hipLaunchKernelGGL((attn_fwd_kernel<P, DP>), grid, dim3(64 * G), 0, st, a);
+  return check_launch("attn_fwd_kernel");
+}
+
+template <Prec P, int DP>
+int bwd_launch(const AttnArgs& a, float* delta, float* dk_part, float* dv_part, hipStream_t st) {
+  const int G = a.heads / a.kv_heads;
+  const int64_t T = (int64_t)a.batch * a.seq;
+  hipLaunchKernelGGL(attn_delta_kernel, dim3((unsigned)ceil_div(T * a.heads, 4)), dim3(256), 0, st, a,
+                     delta);
+  QBLK_TRY(check_launch("attn_delta_kernel"));
+  dim3 gq((unsigned)ceil_div(a.seq, 32), (unsigned)a.kv_heads, (unsigned)a.batch);
+  hipLaunchKernelGGL((attn_dq_kernel<P, DP>), gq, dim3(64 * G), 0, st, a, (const float*)delta);
+  QBLK_TRY(check_launch("attn_dq_kernel"));
+  dim3 gk((unsigned)ceil_div(a.seq, 32), (unsigned)a.heads, (unsigned)a.batch);
+  hipLaunchKernelGGL((attn_dkv_kernel<P, DP>), gk, dim3(64), 0, st, a, (const float*)delta, dk_part,
+                     dv_part);
+  QBLK_TRY(check_launch("attn_dkv_kernel"));
+  const int64_t n = T * a.kv_heads * a.head_dim;
+  hipLaunchKernelGGL(attn_gqa_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, T,
+                     a.heads, a.kv_heads, a.head_dim, (const float*)dk_part, (const float*)dv_part, a.dk,
+                     a.lddk, a.dv, a.lddv);
+  return check_launch("attn_gqa_reduce_kernel");
+}
+
+}  // namespace
+
+int attention_check(int batch, int seq, int heads, int kv_heads, int head_dim) {
+  if (batch <= 0 || seq <= 0 || heads <= 0 || kv_heads <= 0)
+    return fail(QBLK_EINVAL, "attention: batch=%d seq=%d heads=%d kv_heads=%d", batch, seq, heads, kv_heads);
+  if (heads % kv_heads) return fail(QBLK_EINVAL, "attention: heads %% kv_heads != 0");
+  if (heads / kv_heads > 16) return fail(QBLK_EUNSUPPORTED, "attention: more than 16 query heads per KV head");
+  if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(QBLK_EUNSUPPORTED, "attention: head_dim %d not in {16, 32, 64, 128}", head_dim);
+  return 0;
+}
+
+size_t attention_bwd_scratch(int batch, int seq, int heads, int head_dim) {
+  const size_t T = (size_t)batch * seq;
+  return (T * heads + 2 * T * heads * head_dim) * sizeof(float);
+}
+
+int attention_forward(const AttnArgs& a, Prec p, hipStream_t st) {
+  QBLK_TRY(attention_check(a.batch, a.seq, a.heads, a.kv_heads, a.head_dim));
+  const int dp = a.head_dim < 32 ? 32 : a.head_dim;
+  if (p == Prec::F16) {
+    if (dp == 32) return fwd_launch<Prec::F16, 32>(a, st);
+    if (dp == 64) return fwd_launch<Prec::F16, 64>(a, st);
+    return fwd_launch<Prec::F16, 128>(a, st);
+  }
+  if (dp == 32) return fwd_launch<Prec::F32, 32>(a, st);
+  if (dp == 64) return fwd_launch<Prec::F32, 64>(a, st);
+  return fwd_launch<Prec::F32, 128>(a, st);
+}
+
+int attention_backward(const AttnArgs& a, Prec p, void* scratch, hipStream_t st) {
+  QBLK_TRY(attention_check(a.batch, a.seq, a.heads, a.kv_heads, a.head_dim));
+  const int64_t T = (int64_t)a.batch * a.seq;
+  float* delta = (float*)scratch;
+  float* dk_part = delta + T * a.heads;
+  float* dv_part = dk_part + T * a.heads * a.head_dim;
+  const int dp = a.head_dim < 32 ? 32 : a.head_dim;
+  if (p == Prec::F16) {
+    if (dp == 32) return bwd_launch<Prec::F16, 32>(a, delta, dk_part, dv_part, st);
+    if (dp == 64) return bwd_launch<Prec::F16, 64>(a, delta, dk_part, dv_part, st);
+    return bwd_launch<Prec::F16, 128>(a, delta, dk_part, dv_part, st);
+  }
+  if (dp == 32) return bwd_launch<Prec::F32, 32>(a, delta, dk_part, dv_part, st);
+  if (dp == 64) return bwd_launch<Prec::F32, 64>(a, delta, dk_part, dv_part, st);
+  return fail(QBLK_EUNSUPPORTED, "attention backward: fp32 needs head_dim <= 64");
+}
+
+}  // namespace qblk

@@ -1,0 +1,70 @@
+// Internal interface of the block composition.
+#pragma once
+
+#include <functional>
+
+#include "common.h"
+#include "../../include/qblk.h"
+
+namespace qblk {
+
+// Forward activations kept for the backward (caller-owned `saved`).
+struct Saved {
+  float2* tab;     // RoPE cos/sin [seq, d/2]
+  float* rho1;     // [T]
+  float* n1;       // [T, h]
+  float* qkv;      // [T, (H + 2KV) d] projection outputs before QK-norm
+  float* rho_q;    // [T, H]
+  float* rho_k;    // [T, KV]
+  float* qr;       // [T, H d] attention queries (after QK-norm + RoPE)
+  float* kr;       // [T, KV d] attention keys
+  float* o;        // [T, H d] attention output
+  float* lse;      // [B, H, S]
+  float* r1;       // [T, h]
+  float* rho2;     // [T]
+  float* n2;       // [T, h]
+  float* gu;       // [T, 2I] gate | up
+  float* s;        // [T, I] SwiGLU output
+};
+
+// Backward temporaries (caller-owned `scratch`).
+struct Scratch {
+  float *ds, *dgu, *dn2, *dr1, *d_o, *dqr, *dkr, *dqkv, *dn1;
+  char* attn;
+  float* red;
+};
+
+void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes);
+void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes);
+int check_config(const qblk_config* c);
+
+// The projections of a block, forward: qkv = n1 [Wq;Wk;Wv]^T;
+// out = res + o Wo^T; gu = n2 [Wg;Wu]^T; out = res + s Wd^T.
+struct ProjFwd {
+  std::function<int(const float*, float*, hipStream_t)> qkv;
+  std::function<int(const float*, const float*, float*, hipStream_t)> o;
+  std::function<int(const float*, float*, hipStream_t)> gate_up;
+  std::function<int(const float*, const float*, float*, hipStream_t)> down;
+};
+
+// Backward: (dY, X, dX) per projection; the implementation also produces
+// whatever parameter gradients it owns.
+struct ProjBwd {
+  std::function<int(const float*, const float*, float*, hipStream_t)> qkv, o, gate_up, down;
+};
+
+int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g_in, const float* g_post,
+                       const float* g_q, const float* g_k, const float* x, float* y, const Saved& s,
+                       hipStream_t st);
+int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* g_in, const float* g_post,
+                        const float* g_q, const float* g_k, const float* x, const float* dy, const Saved& s,
+                        float* dx, float* dg_in, float* dg_post, float* dg_q, float* dg_k, const Scratch& w,
+                        hipStream_t st);
+
+int dense_block_forward(const qblk_config& c, const qblk_block_params& p, const float* x, float* y,
+                        const Saved& s, hipStream_t st);
+int dense_block_backward(const qblk_config& c, const qblk_block_params& p, const qblk_block_grads& gr,
+                         const float* x, const float* dy, const Saved& s, float* dx, const Scratch& w,
+                         hipStream_t st);
+
+}  // namespace qblk

@@ -1,0 +1,268 @@
+// Decoder block forward and backward: the launch sequence over the kernels
+// of this library, and the layout of the two caller-owned workspaces.
+//
+// cuda_block.rs page: CudaTransformerBlock::forward / compute_attention_cuda
+// and CudaTransformerBlock::backward (backward_ffn, backward_post_attn_norm,
+// the second-residual add, backward_attention, backward_residual_and_input_norm).
+// Differences from the page's launch plan: Q, K and V come out of ONE GEMM
+// over [Wq; Wk; Wv] (likewise gate and up), the residual adds ride in the
+// O-projection and down GEMM epilogues, QK-norm and RoPE are one kernel over
+// all heads, attention never materialises the [heads, seq, seq] scores, the
+// GQA reduction of dK/dV happens on device without copies, and every gamma
+// gradient is a deterministic two-stage sum instead of atomics.
+#include "block.h"
+
+#include "../../include/qblk.h"
+#include "attention.h"
+#include "gemm.h"
+#include "norms.h"
+
+namespace qblk {
+
+// ------------------------------------------------------------- layouts
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t n) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes) {
+  const size_t T = (size_t)c.seq * c.batch, h = c.hidden, d = c.head_dim;
+  const size_t qd = (size_t)c.heads * d, kvd = (size_t)c.kv_heads * d, I = c.intermediate;
+  Carver cv(base);
+  s.tab = cv.take<float2>((size_t)c.seq * (d / 2));
+  s.rho1 = cv.take<float>(T);
+  s.n1 = cv.take<float>(T * h);
+  s.qkv = cv.take<float>(T * (qd + 2 * kvd));
+  s.rho_q = cv.take<float>(T * c.heads);
+  s.rho_k = cv.take<float>(T * c.kv_heads);
+  s.qr = cv.take<float>(T * qd);
+  s.kr = cv.take<float>(T * kvd);
+  s.o = cv.take<float>(T * qd);
+  s.lse = cv.take<float>(T * c.heads);
+  s.r1 = cv.take<float>(T * h);
+  s.rho2 = cv.take<float>(T);
+  s.n2 = cv.take<float>(T * h);
+  s.gu = cv.take<float>(T * 2 * I);
+  s.s = cv.take<float>(T * I);
+  bytes = cv.off;
+}
+
+void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes) {
+  const size_t T = (size_t)c.seq * c.batch, h = c.hidden, d = c.head_dim;
+  const size_t qd = (size_t)c.heads * d, kvd = (size_t)c.kv_heads * d, I = c.intermediate;
+  Carver cv(base);
+  s.ds = cv.take<float>(T * I);
+  s.dgu = cv.take<float>(T * 2 * I);
+  s.dn2 = cv.take<float>(T * h);
+  s.dr1 = cv.take<float>(T * h);
+  s.d_o = cv.take<float>(T * qd);
+  s.dqr = cv.take<float>(T * qd);
+  s.dkr = cv.take<float>(T * kvd);
+  s.dqkv = cv.take<float>(T * (qd + 2 * kvd));
+  s.dn1 = cv.take<float>(T * h);
+  s.attn = cv.take<char>(attention_bwd_scratch(c.batch, c.seq, c.heads, c.head_dim));
+  const size_t red = std::max(rmsnorm_bwd_scratch((int)T, c.hidden),
+                              qk_norm_rope_bwd_scratch((int)T, c.heads, c.kv_heads, c.head_dim));
+  s.red = cv.take<float>(red / sizeof(float) + 1);
+  bytes = cv.off;
+}
+
+int check_config(const qblk_config* c) {
+  if (!c) return fail(QBLK_EINVAL, "config is NULL");
+  if (c->hidden <= 0 || c->heads <= 0 || c->kv_heads <= 0 || c->head_dim <= 0 || c->intermediate <= 0 ||
+      c->seq <= 0 || c->batch <= 0)
+    return fail(QBLK_EINVAL, "config: non-positive dimension");
+  if (c->heads % c->kv_heads) return fail(QBLK_EINVAL, "config: heads %% kv_heads != 0");
+  if (c->hidden % 8 || c->intermediate % 8 || (c->heads * c->head_dim) % 8)
+    return fail(QBLK_EINVAL, "config: hidden, intermediate and heads*head_dim must be multiples of 8");
+  if (c->head_dim != 16 && c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(QBLK_EUNSUPPORTED, "config: head_dim %d not in {16, 32, 64, 128}", c->head_dim);
+  if (c->gemm_precision != 0 && c->gemm_precision != 1)
+    return fail(QBLK_EINVAL, "config: gemm_precision must be 0 or 1");
+  if (c->gemm_precision == 0 && c->head_dim == 128)
+    return fail(QBLK_EUNSUPPORTED, "config: fp32 attention backward supports head_dim <= 64");
+  if (!(c->eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(QBLK_EINVAL, "config: eps/rope_theta");
+  if (c->hidden > 4096) return fail(QBLK_EUNSUPPORTED, "config: hidden above 4096");
+  return QBLK_OK;
+}
+
+Prec prec_of(const qblk_config& c) { return c.gemm_precision ? Prec::F16 : Prec::F32; }
+
+// ---------------------------------------------------------------- forward
+
+// Projection hooks: the fp32/fp16 block uses the dense fp32 weights; the
+// NF4 block substitutes dequant + LoRA GEMMs (nf4_block.hip).
+int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g_in, const float* g_post,
+                       const float* g_q, const float* g_k, const float* x, float* y, const Saved& s,
+                       hipStream_t st) {
+  const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
+  const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
+  const int ldqkv = qd + 2 * kvd;
+
+  QBLK_TRY(rope_table(c.seq, d, c.rope_theta, s.tab, st));
+  QBLK_TRY(rmsnorm_forward(T, h, c.eps, x, nullptr, g_in, s.n1, nullptr, nullptr, s.rho1, st));
+  QBLK_TRY(proj.qkv(s.n1, s.qkv, st));
+  QkRopeArgs qa{T, c.seq, c.heads, c.kv_heads, d, c.qk_norm, c.eps, s.qkv, ldqkv, g_q, g_k, s.tab,
+                s.qr, s.kr, s.rho_q, s.rho_k};
+  QBLK_TRY(qk_norm_rope_forward(qa, st));
+  AttnArgs aa{};
+  aa.batch = c.batch; aa.seq = c.seq; aa.heads = c.heads; aa.kv_heads = c.kv_heads; aa.head_dim = d;
+  aa.q = s.qr; aa.ldq = qd;
+  aa.k = s.kr; aa.ldk = kvd;
+  aa.v = s.qkv + qd + kvd; aa.ldv = ldqkv;
+  aa.o = s.o; aa.ldo = qd;
+  aa.lse = s.lse;
+  QBLK_TRY(attention_forward(aa, prec_of(c), st));
+  QBLK_TRY(proj.o(s.o, x, s.r1, st));  // r1 = x + o Wo^T
+  QBLK_TRY(rmsnorm_forward(T, h, c.eps, s.r1, nullptr, g_post, s.n2, nullptr, nullptr, s.rho2, st));
+  QBLK_TRY(proj.gate_up(s.n2, s.gu, st));
+  QBLK_TRY(swiglu_forward(T, I, s.gu, s.s, nullptr, st));
+  QBLK_TRY(proj.down(s.s, s.r1, y, st));  // y = r1 + s Wd^T
+  return QBLK_OK;
+}
+
+int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* g_in, const float* g_post,
+                        const float* g_q, const float* g_k, const float* x, const float* dy, const Saved& s,
+                        float* dx, float* dg_in, float* dg_post, float* dg_q, float* dg_k, const Scratch& w,
+                        hipStream_t st) {
+  const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
+  const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
+  const int ldqkv = qd + 2 * kvd;
+
+  // FFN: ds = dy Wd; dWd = dy^T s; SwiGLU backward; dn2 = dg Wg + du Wu; dWg, dWu.
+  QBLK_TRY(proj.down(dy, s.s, w.ds, st));
+  QBLK_TRY(swiglu_backward(T, I, s.gu, w.ds, w.dgu, st));
+  QBLK_TRY(proj.gate_up(w.dgu, s.n2, w.dn2, st));
+  // post-attention norm backward, plus the second residual's gradient dy
+  QBLK_TRY(rmsnorm_backward(T, h, c.eps, s.r1, g_post, w.dn2, dy, w.dr1, dg_post, w.red, st));
+  // O projection
+  QBLK_TRY(proj.o(w.dr1, s.o, w.d_o, st));
+  // attention backward: dq, dk at the attention inputs; dv straight into dqkv
+  AttnArgs aa{};
+  aa.batch = c.batch; aa.seq = c.seq; aa.heads = c.heads; aa.kv_heads = c.kv_heads; aa.head_dim = d;
+  aa.q = s.qr; aa.ldq = qd;
+  aa.k = s.kr; aa.ldk = kvd;
+  aa.v = s.qkv + qd + kvd; aa.ldv = ldqkv;
+  aa.o = s.o; aa.ldo = qd;
+  aa.lse = s.lse;
+  aa.d_o = w.d_o; aa.lddo = qd;
+  aa.dq = w.dqr; aa.lddq = qd;
+  aa.dk = w.dkr; aa.lddk = kvd;
+  aa.dv = w.dqkv + qd + kvd; aa.lddv = ldqkv;
+  QBLK_TRY(attention_backward(aa, prec_of(c), w.attn, st));
+  QkRopeBwdArgs qb{T, c.seq, c.heads, c.kv_heads, d, c.qk_norm, c.eps, s.qkv, ldqkv, g_q, g_k, s.tab,
+                   w.dqr, w.dkr, w.dqkv, dg_q, dg_k};
+  QBLK_TRY(qk_norm_rope_backward(qb, w.red, st));
+  QBLK_TRY(proj.qkv(w.dqkv, s.n1, w.dn1, st));
+  // input norm backward, plus the first residual's gradient dr1
+  QBLK_TRY(rmsnorm_backward(T, h, c.eps, x, g_in, w.dn1, w.dr1, dx, dg_in, w.red, st));
+  return QBLK_OK;
+}
+
+// ------------------------------------------------- dense (fp32 master) block
+
+namespace {
+
+GemmDesc nt(const qblk_config& c, int M, int N, int K, const float* a, int64_t lda, Seg b, int64_t ldb,
+            float* out, int64_t ldc) {
+  GemmDesc g;
+  g.layout = Layout::NT;
+  g.prec = prec_of(c);
+  g.M = M; g.N = N; g.K = K;
+  g.a = a; g.lda = lda;
+  g.b = b; g.ldb = ldb;
+  g.c = seg1(out, M); g.ldc = ldc;
+  return g;
+}
+
+Seg seg3(const void* a, int na, const void* b, int nb, const void* cc, int nc) {
+  Seg s;
+  s.p[0] = a; s.p[1] = b; s.p[2] = cc;
+  s.start[0] = 0; s.start[1] = na; s.start[2] = na + nb; s.start[3] = na + nb + nc;
+  s.nseg = cc ? 3 : 2;
+  return s;
+}
+
+}  // namespace
+
+int dense_block_forward(const qblk_config& c, const qblk_block_params& p, const float* x, float* y,
+                        const Saved& s, hipStream_t st) {
+  const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
+  const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
+  ProjFwd proj;
+  proj.qkv = [&](const float* n1, float* qkv, hipStream_t s_) {
+    return gemm(nt(c, T, qd + 2 * kvd, h, n1, h, seg3(p.w_q, qd, p.w_k, kvd, p.w_v, kvd), h, qkv, qd + 2 * kvd),
+                s_);
+  };
+  proj.o = [&](const float* o, const float* res, float* out, hipStream_t s_) {
+    GemmDesc g = nt(c, T, h, qd, o, qd, seg1(p.w_o, h), qd, out, h);
+    g.r = res; g.ldr = h;
+    return gemm(g, s_);
+  };
+  proj.gate_up = [&](const float* n2, float* gu, hipStream_t s_) {
+    Seg b = seg3(p.w_gate, I, p.w_up, I, nullptr, 0);
+    return gemm(nt(c, T, 2 * I, h, n2, h, b, h, gu, 2 * I), s_);
+  };
+  proj.down = [&](const float* sv, const float* res, float* out, hipStream_t s_) {
+    GemmDesc g = nt(c, T, h, I, sv, I, seg1(p.w_down, h), I, out, h);
+    g.r = res; g.ldr = h;
+    return gemm(g, s_);
+  };
+  return block_forward_impl(c, proj, p.g_in, p.g_post, p.g_q, p.g_k, x, y, s, st);
+}
+
+int dense_block_backward(const qblk_config& c, const qblk_block_params& p, const qblk_block_grads& gr,
+                         const float* x, const float* dy, const Saved& s, float* dx, const Scratch& w,
+                         hipStream_t st) {
+  const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
+  const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
+  const Prec pr = prec_of(c);
+  // dX = dY W (NN, B = W [out, in] with out the contraction) and
+  // dW = dY^T X (TN). `wseg` are the weights stacked along out; `cseg` the
+  // gradient tensors split the same way.
+  auto dxdw = [&](const float* dyv, int n_out, const float* xin, int n_in, Seg wseg, Seg cseg, float* dxo,
+                  hipStream_t s_) -> int {
+    GemmDesc a;
+    a.layout = Layout::NN; a.prec = pr;
+    a.M = T; a.N = n_in; a.K = n_out;
+    a.a = dyv; a.lda = n_out;
+    a.b = wseg; a.ldb = n_in;
+    a.c = seg1(dxo, T); a.ldc = n_in;
+    QBLK_TRY(gemm(a, s_));
+    GemmDesc b;
+    b.layout = Layout::TN; b.prec = pr;
+    b.M = n_out; b.N = n_in; b.K = T;
+    b.a = dyv; b.lda = n_out;
+    b.b = seg1(xin, T); b.ldb = n_in;
+    b.c = cseg; b.ldc = n_in;
+    return gemm(b, s_);
+  };
+  ProjBwd proj;
+  proj.down = [&](const float* dyv, const float* sv, float* ds, hipStream_t s_) {
+    return dxdw(dyv, h, sv, I, seg1(p.w_down, h), seg1(gr.w_down, h), ds, s_);
+  };
+  proj.gate_up = [&](const float* dgu, const float* n2, float* dn2, hipStream_t s_) {
+    return dxdw(dgu, 2 * I, n2, h, seg3(p.w_gate, I, p.w_up, I, nullptr, 0),
+                seg3(gr.w_gate, I, gr.w_up, I, nullptr, 0), dn2, s_);
+  };
+  proj.o = [&](const float* dr1, const float* o, float* d_o, hipStream_t s_) {
+    return dxdw(dr1, h, o, qd, seg1(p.w_o, h), seg1(gr.w_o, h), d_o, s_);
+  };
+  proj.qkv = [&](const float* dqkv, const float* n1, float* dn1, hipStream_t s_) {
+    return dxdw(dqkv, qd + 2 * kvd, n1, h, seg3(p.w_q, qd, p.w_k, kvd, p.w_v, kvd),
+                seg3(gr.w_q, qd, gr.w_k, kvd, gr.w_v, kvd), dn1, s_);
+  };
+  return block_backward_impl(c, proj, p.g_in, p.g_post, p.g_q, p.g_k, x, dy, s, dx, gr.g_in, gr.g_post,
+                             gr.g_q, gr.g_k, w, st);
+}
+
+}  // namespace qblk

@@ -1,0 +1,65 @@
+// Shared device and host helpers of libqblk (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace qblk {
+
+typedef _Float16 f16;
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------ error state
+// A thread-local message read back through qblk_last_error(). Every entry
+// point returns 0 or one of the negative codes of qblk.h.
+int fail(int code, const char* fmt, ...);
+int check_hip(hipError_t e, const char* what);
+int check_launch(const char* what);
+
+#define QBLK_TRY(expr)          \
+  do {                          \
+    int _rc = (expr);           \
+    if (_rc != 0) return _rc;   \
+  } while (0)
+
+// ------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// fp32 -> fp16 with round-to-nearest-even (v_cvt_f16_f32 under the default
+// rounding mode; the packed round-toward-zero conversion is never used).
+__device__ __forceinline__ f16 to_f16(float x) { return (f16)x; }
+
+__device__ __forceinline__ half4 to_half4(float4 v) {
+  half4 h;
+  h[0] = (f16)v.x;
+  h[1] = (f16)v.y;
+  h[2] = (f16)v.z;
+  h[3] = (f16)v.w;
+  return h;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace qblk

@@ -1,0 +1,229 @@
+// QK-norm + NeoX RoPE (forward and backward) and SwiGLU (forward and
+// backward): the memory-bound steps between the projections and attention.
+//
+// cuda_block.rs page, compute_attention_cuda: per-head RMSNorm of Q and K
+// with one gamma of size head_dim shared by the heads, applied before the
+// NeoX half rotation with positions 0..seq-1 and rope_theta; backward_attention
+// gives the inverse rotation for the backward. The page has no QK-norm
+// backward; here it is the true derivative. SwiGLU is fused_swiglu_forward;
+// its backward follows backward_ffn (and ffn_backward of the wgpu_trainer.rs
+// page): dg = ds * u * silu'(g), du = ds * silu(g).
+//
+// One wave handles one (token, head) row of head_dim <= 128 elements: lane
+// i < d/2 owns the rotation pair (i, i + d/2), so the norm's reduction and
+// the rotation stay in registers. The cos/sin table is built once per call
+// in fp64 and rounded to fp32.
+#include "norms.h"
+
+#include "../../include/qblk.h"
+
+namespace qblk {
+namespace {
+
+__global__ void rope_table_kernel(int seq, int half, int d, double log_theta, float2* tab) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= seq * half) return;
+  const int s = idx / half, i = idx % half;
+  const double f = exp(-2.0 * (double)i / (double)d * log_theta);
+  const double a = (double)s * f;
+  tab[idx] = make_float2((float)cos(a), (float)sin(a));
+}
+
+// Forward: one wave per (t, head) over the H + KV heads.
+__global__ __launch_bounds__(256) void qk_rope_fwd_kernel(QkRopeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nh = a.heads + a.kv_heads;
+  if (item >= a.T * nh) return;
+  const int t = item / nh, head = item % nh;
+  const int d = a.head_dim, half = d >> 1;
+  const bool is_q = head < a.heads;
+  const int hh = is_q ? head : head - a.heads;
+  const float* src = a.qkv + (int64_t)t * a.ld_qkv + (is_q ? 0 : a.heads * d) + hh * d;
+  float* dst = is_q ? a.qr + ((int64_t)t * a.heads + hh) * d : a.kr + ((int64_t)t * a.kv_heads + hh) * d;
+  const float* g = is_q ? a.g_q : a.g_k;
+  const bool act = lane < half;
+  float x0 = act ? src[lane] : 0.f, x1 = act ? src[lane + half] : 0.f;
+  if (a.qk_norm) {
+    const float ss = wave_sum(x0 * x0 + x1 * x1);
+    const float rho = 1.0f / sqrtf(ss / (float)d + a.eps);
+    if (lane == 0) (is_q ? a.rho_q[(int64_t)t * a.heads + hh] : a.rho_k[(int64_t)t * a.kv_heads + hh]) = rho;
+    if (act) {
+      x0 = x0 * rho * g[lane];
+      x1 = x1 * rho * g[lane + half];
+    }
+  }
+  if (act) {
+    const float2 cs = a.tab[(t % a.seq) * half + lane];
+    dst[lane] = x0 * cs.x - x1 * cs.y;
+    dst[lane + half] = x1 * cs.x + x0 * cs.y;
+  }
+}
+
+// Backward for one group of heads (the q heads or the k heads): one wave per
+// (t, head), grid-stride; dgamma partials per workgroup in scratch.
+__global__ __launch_bounds__(256) void qk_rope_bwd_kernel(int T, int seq, int nh, int d, int qk_norm,
+                                                          float eps, const float* __restrict__ qkv,
+                                                          int64_t ld, int col0,
+                                                          const float* __restrict__ g,
+                                                          const float2* __restrict__ tab,
+                                                          const float* __restrict__ dsrc,
+                                                          float* __restrict__ dqkv,
+                                                          float* __restrict__ partial) {
+  __shared__ float red[4][128];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = d >> 1;
+  const bool act = lane < half;
+  float dg0 = 0.f, dg1 = 0.f;
+  for (int item = blockIdx.x * 4 + w; item < T * nh; item += gridDim.x * 4) {
+    const int t = item / nh, hh = item % nh;
+    const float* dr = dsrc + ((int64_t)t * nh + hh) * d;
+    const float2 cs = act ? tab[(t % seq) * half + lane] : make_float2(1.f, 0.f);
+    const float y0 = act ? dr[lane] : 0.f, y1 = act ? dr[lane + half] : 0.f;
+    // transpose of the rotation
+    const float g0 = y0 * cs.x + y1 * cs.y;
+    const float g1 = y1 * cs.x - y0 * cs.y;
+    float* out = dqkv + (int64_t)t * ld + col0 + hh * d;
+    if (qk_norm) {
+      const float* xr = qkv + (int64_t)t * ld + col0 + hh * d;
+      const float x0 = act ? xr[lane] : 0.f, x1 = act ? xr[lane + half] : 0.f;
+      const float ss = wave_sum(x0 * x0 + x1 * x1);
+      const float rho = 1.0f / sqrtf(ss / (float)d + eps);
+      const float xh0 = x0 * rho, xh1 = x1 * rho;
+      const float e0 = act ? g[lane] * g0 : 0.f, e1 = act ? g[lane + half] * g1 : 0.f;
+      const float dot = wave_sum(e0 * xh0 + e1 * xh1) / (float)d;
+      if (act) {
+        out[lane] = rho * (e0 - xh0 * dot);
+        out[lane + half] = rho * (e1 - xh1 * dot);
+        dg0 += g0 * xh0;
+        dg1 += g1 * xh1;
+      }
+    } else if (act) {
+      out[lane] = g0;
+      out[lane + half] = g1;
+    }
+  }
+  if (!qk_norm) return;
+  if (act) {
+    red[w][lane] = dg0;
+    red[w][lane + half] = dg1;
+  }
+  __syncthreads();
+  if (threadIdx.x < d) {
+    const int c = threadIdx.x;
+    partial[(int64_t)blockIdx.x * d + c] = red[0][c] + red[1][c] + red[2][c] + red[3][c];
+  }
+}
+
+__global__ void fill_kernel(float* p, int n, float v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+int qk_parts(int T, int nh) { return (int)std::min<int64_t>(ceil_div((int64_t)T * nh, 4), 240); }
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+__global__ void swiglu_fwd_kernel(int T, int I, const float* __restrict__ gu, float* __restrict__ s,
+                                  f16* __restrict__ s16) {
+  const int64_t n4 = (int64_t)T * I / 4;
+  const int i4 = I / 4;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n4;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = e / i4, j = e % i4;
+    const float4 g = ((const float4*)(gu + t * 2 * I))[j];
+    const float4 u = ((const float4*)(gu + t * 2 * I + I))[j];
+    float4 o;
+    o.x = g.x * sigmoidf_(g.x) * u.x;
+    o.y = g.y * sigmoidf_(g.y) * u.y;
+    o.z = g.z * sigmoidf_(g.z) * u.z;
+    o.w = g.w * sigmoidf_(g.w) * u.w;
+    if (s) ((float4*)s)[e] = o;
+    if (s16) ((half4*)s16)[e] = to_half4(o);
+  }
+}
+
+__device__ __forceinline__ void swiglu_grad(float g, float u, float ds, float& dg, float& du) {
+  const float sg = sigmoidf_(g);
+  const float silu = g * sg;
+  dg = ds * u * (sg * (1.0f + g - silu));
+  du = ds * silu;
+}
+
+__global__ void swiglu_bwd_kernel(int T, int I, const float* __restrict__ gu,
+                                  const float* __restrict__ ds, float* __restrict__ dgu) {
+  const int64_t n4 = (int64_t)T * I / 4;
+  const int i4 = I / 4;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n4;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = e / i4, j = e % i4;
+    const float4 g = ((const float4*)(gu + t * 2 * I))[j];
+    const float4 u = ((const float4*)(gu + t * 2 * I + I))[j];
+    const float4 d = ((const float4*)ds)[e];
+    float4 dg, du;
+    swiglu_grad(g.x, u.x, d.x, dg.x, du.x);
+    swiglu_grad(g.y, u.y, d.y, dg.y, du.y);
+    swiglu_grad(g.z, u.z, d.z, dg.z, du.z);
+    swiglu_grad(g.w, u.w, d.w, dg.w, du.w);
+    ((float4*)(dgu + t * 2 * I))[j] = dg;
+    ((float4*)(dgu + t * 2 * I + I))[j] = du;
+  }
+}
+
+unsigned grid_for(int64_t n4) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(n4, 256), 4096)); }
+
+}  // namespace
+
+int rope_table(int seq, int head_dim, float theta, float2* tab, hipStream_t st) {
+  const int half = head_dim / 2;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)ceil_div((int64_t)seq * half, 256)), dim3(256), 0,
+                     st, seq, half, head_dim, log((double)theta), tab);
+  return check_launch("rope_table_kernel");
+}
+
+int qk_norm_rope_forward(const QkRopeArgs& a, hipStream_t st) {
+  const int64_t items = (int64_t)a.T * (a.heads + a.kv_heads);
+  hipLaunchKernelGGL(qk_rope_fwd_kernel, dim3((unsigned)ceil_div(items, 4)), dim3(256), 0, st, a);
+  return check_launch("qk_rope_fwd_kernel");
+}
+
+size_t qk_norm_rope_bwd_scratch(int T, int heads, int kv_heads, int head_dim) {
+  return (size_t)(qk_parts(T, heads) + qk_parts(T, kv_heads)) * head_dim * sizeof(float);
+}
+
+int qk_norm_rope_backward(const QkRopeBwdArgs& a, float* scratch, hipStream_t st) {
+  const int d = a.head_dim;
+  const int pq = qk_parts(a.T, a.heads), pk = qk_parts(a.T, a.kv_heads);
+  float* part_q = scratch;
+  float* part_k = scratch + (size_t)pq * d;
+  hipLaunchKernelGGL(qk_rope_bwd_kernel, dim3((unsigned)pq), dim3(256), 0, st, a.T, a.seq, a.heads, d,
+                     a.qk_norm, a.eps, a.qkv, a.ld_qkv, 0, a.g_q, a.tab, a.dqr, a.dqkv, part_q);
+  QBLK_TRY(check_launch("qk_rope_bwd_kernel(q)"));
+  hipLaunchKernelGGL(qk_rope_bwd_kernel, dim3((unsigned)pk), dim3(256), 0, st, a.T, a.seq, a.kv_heads,
+                     d, a.qk_norm, a.eps, a.qkv, a.ld_qkv, a.heads * d, a.g_k, a.tab, a.dkr, a.dqkv,
+                     part_k);
+  QBLK_TRY(check_launch("qk_rope_bwd_kernel(k)"));
+  if (a.qk_norm) {
+    QBLK_TRY(colsum(pq, d, part_q, a.dg_q, st));
+    QBLK_TRY(colsum(pk, d, part_k, a.dg_k, st));
+  } else {
+    if (a.dg_q) hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, a.dg_q, d, 0.f);
+    if (a.dg_k) hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, a.dg_k, d, 0.f);
+    QBLK_TRY(check_launch("fill_kernel"));
+  }
+  return 0;
+}
+
+int swiglu_forward(int T, int I, const float* gu, float* s, f16* s16, hipStream_t st) {
+  const int64_t n4 = (int64_t)T * I / 4;
+  hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(grid_for(n4)), dim3(256), 0, st, T, I, gu, s, s16);
+  return check_launch("swiglu_fwd_kernel");
+}
+
+int swiglu_backward(int T, int I, const float* gu, const float* ds, float* dgu, hipStream_t st) {
+  const int64_t n4 = (int64_t)T * I / 4;
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(grid_for(n4)), dim3(256), 0, st, T, I, gu, ds, dgu);
+  return check_launch("swiglu_bwd_kernel");
+}
+
+}  // namespace qblk

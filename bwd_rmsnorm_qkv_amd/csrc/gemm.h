@@ -1,0 +1,95 @@
+// Internal interface of the MFMA GEMM engine.
+//
+// C[M,N] (+)= alpha * op(A) op(B) (+ R), fp32 accumulate, fp32 output.
+// Three operand layouts cover every projection of the block with weights
+// stored [out, in] row-major:
+//   NT: A [M,K] K-contiguous, B [N,K] K-contiguous  (forward  y  = x W^T)
+//   NN: A [M,K] K-contiguous, B [K,N] N-contiguous  (backward dx = dy W)
+//   TN: A [K,M] M-contiguous, B [K,N] N-contiguous  (backward dW = dy^T x)
+// Contractions run on v_mfma_f32_32x32x2_f32 (Prec::F32) or, with operands
+// rounded to fp16 (nearest even) while they are staged into LDS,
+// v_mfma_f32_32x32x16_f16 (Prec::F16).
+#pragma once
+
+#include "common.h"
+
+namespace qblk {
+
+enum class Prec : int { F32 = 0, F16 = 1 };
+enum class Layout : int { NT = 0, NN = 1, TN = 2 };
+enum class Src : int { F32 = 0, F16 = 1, NF4 = 2 };
+
+// Up to three row segments stored at different addresses that together act
+// as one matrix: storage row r lives in segment s with start[s] <= r <
+// start[s+1], at p[s] + (r - start[s]) * ld. Used to treat [Wq; Wk; Wv]
+// (and [Wg; Wu]) as one operand and to split a dW output over its tensors.
+struct Seg {
+  const void* p[3] = {nullptr, nullptr, nullptr};
+  int32_t start[4] = {0, 0, 0, 0};  // start[nseg] = total rows
+  int32_t nseg = 1;
+};
+
+inline Seg seg1(const void* p, int rows) {
+  Seg s;
+  s.p[0] = p;
+  s.start[0] = 0;
+  s.start[1] = rows;
+  s.nseg = 1;
+  return s;
+}
+
+// NF4 operand: per segment packed codes (2 per byte, low nibble first) and
+// one fp32 scale per 64 consecutive elements of the row-major storage.
+struct Nf4Seg {
+  const uint8_t* codes[3] = {nullptr, nullptr, nullptr};
+  const float* scales[3] = {nullptr, nullptr, nullptr};
+  float levels[16] = {};  // the NF4 codebook (filled by nf4_codebook_host)
+};
+
+// The 16 NormalFloat4 levels, ascending, as fp32 (computed once on the host).
+const float* nf4_codebook_host();
+
+// Optional extra K columns appended to the contraction (LoRA):
+//   C += A_ext[M, kext] * B_ext^T.
+// A_ext is fp32 [M, kext] K-contiguous, times a_scale. For NT, B_ext is
+// fp32 [N, kext] K-contiguous; for NN it is fp32 [kext, N] N-contiguous.
+// When blockdiag > 0, B_ext is block diagonal over the B segments: the
+// rows (NT) or columns (NN) of B-segment s only see ext columns
+// [s*blockdiag, (s+1)*blockdiag), and b_ext holds one pointer per segment.
+struct KExt {
+  int32_t kext = 0;
+  const float* a = nullptr;
+  int64_t lda = 0;
+  float a_scale = 1.f;
+  const float* b[3] = {nullptr, nullptr, nullptr};
+  int64_t ldb = 0;
+  int32_t blockdiag = 0;
+};
+
+struct GemmDesc {
+  Layout layout = Layout::NT;
+  Prec prec = Prec::F32;
+  int32_t M = 0, N = 0, K = 0;
+  const void* a = nullptr;
+  int64_t lda = 0;
+  Src a_src = Src::F32;
+  Seg b;
+  int64_t ldb = 0;
+  Src b_src = Src::F32;
+  Nf4Seg nf4;          // when b_src == Src::NF4
+  Seg c;               // fp32 output rows (segments along M)
+  int64_t ldc = 0;
+  const float* r = nullptr;  // optional residual [M, N] added in the epilogue
+  int64_t ldr = 0;
+  int32_t accumulate = 0;    // 1: C += result
+  float alpha = 1.f;
+  KExt ext;
+  // When c_cols_blockdiag > 0 the output keeps only columns
+  // [s*c_cols_blockdiag, (s+1)*c_cols_blockdiag) of rows in C-segment s,
+  // written at column 0 of that segment (the diagonal blocks of a product).
+  int32_t c_cols_blockdiag = 0;
+};
+
+int gemm(const GemmDesc& d, hipStream_t stream);
+
+}  // namespace qblk

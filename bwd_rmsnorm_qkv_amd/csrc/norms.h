@@ -1,0 +1,63 @@
+// Internal interface of the memory-bound kernels: RMSNorm, QK-norm + RoPE,
+// SwiGLU, and the column-sum used by every deterministic gamma gradient.
+#pragma once
+
+#include "common.h"
+
+namespace qblk {
+
+int rmsnorm_check(int rows, int n);
+int rmsnorm_bwd_parts(int rows, int n);
+size_t rmsnorm_bwd_scratch(int rows, int n);
+
+// y (fp32) and/or y16 (fp16) = RMSNorm(x [+ res]) * gamma; sum_out = x + res.
+int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res,
+                    const float* gamma, float* y, f16* y16, float* sum_out, float* rho,
+                    hipStream_t st);
+// dx = RMSNorm backward (+ dres); dgamma overwritten; scratch: rmsnorm_bwd_scratch.
+int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* gamma,
+                     const float* dy, const float* dres, float* dx, float* dgamma, float* scratch,
+                     hipStream_t st);
+// out[c] = sum_p partial[p][c], fixed order.
+int colsum(int parts, int n, const float* partial, float* out, hipStream_t st);
+
+// RoPE table: tab[s][i] = (cos, sin)(s * theta^(-2i/d)), computed in fp64.
+int rope_table(int seq, int head_dim, float theta, float2* tab, hipStream_t st);
+
+// Per-head RMSNorm (optional) + NeoX RoPE of the q and k heads of a packed
+// [T, (H + 2KV) d] projection output. Writes qr [T, H d], kr [T, KV d]
+// (fp32), rho_q [T, H], rho_k [T, KV] (when qk_norm).
+struct QkRopeArgs {
+  int T, seq, heads, kv_heads, head_dim, qk_norm;
+  float eps;
+  const float* qkv;  // [T, ld_qkv]
+  int64_t ld_qkv;
+  const float *g_q, *g_k;
+  const float2* tab;
+  float *qr, *kr, *rho_q, *rho_k;
+};
+int qk_norm_rope_forward(const QkRopeArgs& a, hipStream_t st);
+
+// Backward: dqr/dkr (gradients at the attention inputs) -> dq/dk at the
+// projection outputs, written into dqkv (same packing as qkv), and
+// dg_q/dg_k (overwritten). scratch: qk_norm_rope_bwd_scratch floats.
+struct QkRopeBwdArgs {
+  int T, seq, heads, kv_heads, head_dim, qk_norm;
+  float eps;
+  const float* qkv;
+  int64_t ld_qkv;
+  const float *g_q, *g_k;
+  const float2* tab;
+  const float *dqr, *dkr;  // [T, H d], [T, KV d]
+  float* dqkv;             // [T, ld_qkv]
+  float *dg_q, *dg_k;
+};
+size_t qk_norm_rope_bwd_scratch(int T, int heads, int kv_heads, int head_dim);
+int qk_norm_rope_backward(const QkRopeBwdArgs& a, float* scratch, hipStream_t st);
+
+// s = silu(g) * u with g, u the two halves of gu [T, 2I]; s fp32 and/or fp16.
+int swiglu_forward(int T, int I, const float* gu, float* s, f16* s16, hipStream_t st);
+// dgu = [ds * u * silu'(g) | ds * silu(g)].
+int swiglu_backward(int T, int I, const float* gu, const float* ds, float* dgu, hipStream_t st);
+
+}  // namespace qblk

@@ -1,0 +1,234 @@
+// RMSNorm forward (optionally fused with the residual add) and backward.
+//
+// cuda_block.rs page: rms_norm_forward in CudaTransformerBlock::forward (the
+// pre-attention and post-attention norms), the fused residual + RMSNorm of
+// the NF4 forward, and rms_norm_backward in backward_post_attn_norm and
+// backward_residual_and_input_norm. eps sits inside the square root.
+//
+// One 64-lane wave owns a row: the row is read once with 16-byte loads into
+// registers (VPL float4 per lane, n <= 256 * VPL), reduced with cross-lane
+// shuffles, then written. The backward's dgamma uses no atomics: each
+// workgroup (a fixed function of rows and n) reduces its rows into one
+// partial row in scratch, and colsum_kernel adds the partials in a fixed
+// order, so results are bitwise reproducible.
+#include "norms.h"
+
+#include "../../include/qblk.h"
+
+namespace qblk {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+template <int VPL>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(int rows, int n, float eps,
+                                                          const float* __restrict__ x,
+                                                          const float* __restrict__ res,
+                                                          const float* __restrict__ gamma,
+                                                          float* __restrict__ y,
+                                                          f16* __restrict__ y16,
+                                                          float* __restrict__ sum_out,
+                                                          float* __restrict__ rho_out) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int n4 = n >> 2;
+  const float4* xr = (const float4*)(x + (int64_t)row * n);
+  const float4* rr = res ? (const float4*)(res + (int64_t)row * n) : nullptr;
+  float4 v[VPL];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int c = lane + j * 64;
+    if (c < n4) {
+      float4 a = xr[c];
+      if (rr) {
+        const float4 b = rr[c];
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      }
+      v[j] = a;
+      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    }
+  }
+  ss = wave_sum(ss);
+  const float rho = 1.0f / sqrtf(ss / (float)n + eps);
+  if (lane == 0 && rho_out) rho_out[row] = rho;
+  const float4* gr = (const float4*)gamma;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int c = lane + j * 64;
+    if (c < n4) {
+      if (sum_out) ((float4*)(sum_out + (int64_t)row * n))[c] = v[j];
+      const float4 g = gr[c];
+      float4 o;
+      o.x = v[j].x * rho * g.x;
+      o.y = v[j].y * rho * g.y;
+      o.z = v[j].z * rho * g.z;
+      o.w = v[j].w * rho * g.w;
+      if (y) ((float4*)(y + (int64_t)row * n))[c] = o;
+      if (y16) ((half4*)(y16 + (int64_t)row * n))[c] = to_half4(o);
+    }
+  }
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int rows, int n, float eps,
+                                                          const float* __restrict__ x,
+                                                          const float* __restrict__ gamma,
+                                                          const float* __restrict__ dy,
+                                                          const float* __restrict__ dres,
+                                                          float* __restrict__ dx,
+                                                          float* __restrict__ partial) {
+  __shared__ float4 red[kWavesPerBlock][VPL * 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n4 = n >> 2;
+  const float4* gr = (const float4*)gamma;
+  float4 dg[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) dg[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  for (int row = blockIdx.x * kWavesPerBlock + w; row < rows; row += gridDim.x * kWavesPerBlock) {
+    const float4* xr = (const float4*)(x + (int64_t)row * n);
+    const float4* dr = (const float4*)(dy + (int64_t)row * n);
+    float4 xv[VPL], e[VPL], dv[VPL];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int c = lane + j * 64;
+      if (c < n4) {
+        xv[j] = xr[c];
+        dv[j] = dr[c];
+        const float4 g = gr[c];
+        e[j] = make_float4(g.x * dv[j].x, g.y * dv[j].y, g.z * dv[j].z, g.w * dv[j].w);
+        ss += xv[j].x * xv[j].x + xv[j].y * xv[j].y + xv[j].z * xv[j].z + xv[j].w * xv[j].w;
+      }
+    }
+    ss = wave_sum(ss);
+    const float rho = 1.0f / sqrtf(ss / (float)n + eps);
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int c = lane + j * 64;
+      if (c < n4) {
+        xv[j].x *= rho; xv[j].y *= rho; xv[j].z *= rho; xv[j].w *= rho;  // xhat
+        dot += e[j].x * xv[j].x + e[j].y * xv[j].y + e[j].z * xv[j].z + e[j].w * xv[j].w;
+      }
+    }
+    dot = wave_sum(dot) / (float)n;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int c = lane + j * 64;
+      if (c < n4) {
+        float4 o;
+        o.x = rho * (e[j].x - xv[j].x * dot);
+        o.y = rho * (e[j].y - xv[j].y * dot);
+        o.z = rho * (e[j].z - xv[j].z * dot);
+        o.w = rho * (e[j].w - xv[j].w * dot);
+        if (dres) {
+          const float4 r = ((const float4*)(dres + (int64_t)row * n))[c];
+          o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
+        }
+        ((float4*)(dx + (int64_t)row * n))[c] = o;
+        dg[j].x += dv[j].x * xv[j].x;
+        dg[j].y += dv[j].y * xv[j].y;
+        dg[j].z += dv[j].z * xv[j].z;
+        dg[j].w += dv[j].w * xv[j].w;
+      }
+    }
+  }
+  // Reduce the waves' dgamma partials in a fixed order.
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) red[w][lane + j * 64] = dg[j];
+  __syncthreads();
+  for (int c = threadIdx.x; c < n4; c += blockDim.x) {
+    float4 s = red[0][c];
+#pragma unroll
+    for (int ww = 1; ww < kWavesPerBlock; ++ww) {
+      const float4 t = red[ww][c];
+      s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+    }
+    ((float4*)(partial + (int64_t)blockIdx.x * n))[c] = s;
+  }
+}
+
+__global__ void colsum_kernel(int parts, int n, const float* __restrict__ partial,
+                              float* __restrict__ out) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= n) return;
+  float s = 0.f;
+  for (int p = 0; p < parts; ++p) s += partial[(int64_t)p * n + c];
+  out[c] = s;
+}
+
+int vpl_for(int n) {
+  const int need = (int)ceil_div(n, 256);
+  if (need <= 1) return 1;
+  if (need <= 2) return 2;
+  if (need <= 4) return 4;
+  if (need <= 8) return 8;
+  if (need <= 12) return 12;
+  if (need <= 16) return 16;
+  return -1;
+}
+
+}  // namespace
+
+int rmsnorm_bwd_parts(int rows, int n) {
+  (void)n;
+  return (int)std::min<int64_t>(ceil_div(rows, kWavesPerBlock), 240);
+}
+
+size_t rmsnorm_bwd_scratch(int rows, int n) {
+  return (size_t)rmsnorm_bwd_parts(rows, n) * n * sizeof(float);
+}
+
+int rmsnorm_check(int rows, int n) {
+  if (rows <= 0 || n <= 0) return fail(QBLK_EINVAL, "rmsnorm: rows=%d n=%d", rows, n);
+  if (n % 4) return fail(QBLK_EINVAL, "rmsnorm: n=%d must be a multiple of 4", n);
+  if (vpl_for(n) < 0) return fail(QBLK_EUNSUPPORTED, "rmsnorm: n=%d above 4096", n);
+  return 0;
+}
+
+int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res,
+                    const float* gamma, float* y, f16* y16, float* sum_out, float* rho,
+                    hipStream_t st) {
+  QBLK_TRY(rmsnorm_check(rows, n));
+  const dim3 grid((unsigned)ceil_div(rows, kWavesPerBlock)), block(256);
+  switch (vpl_for(n)) {
+#define QBLK_CASE(V)                                                                          \
+  case V:                                                                                     \
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<V>, grid, block, 0, st, rows, n, eps, x, res, gamma, \
+                       y, y16, sum_out, rho);                                                 \
+    break;
+    QBLK_CASE(1) QBLK_CASE(2) QBLK_CASE(4) QBLK_CASE(8) QBLK_CASE(12) QBLK_CASE(16)
+#undef QBLK_CASE
+  }
+  return check_launch("rmsnorm_fwd_kernel");
+}
+
+int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* gamma,
+                     const float* dy, const float* dres, float* dx, float* dgamma, float* scratch,
+                     hipStream_t st) {
+  QBLK_TRY(rmsnorm_check(rows, n));
+  const int parts = rmsnorm_bwd_parts(rows, n);
+  const dim3 grid((unsigned)parts), block(256);
+  switch (vpl_for(n)) {
+#define QBLK_CASE(V)                                                                             \
+  case V:                                                                                        \
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<V>, grid, block, 0, st, rows, n, eps, x, gamma, dy,     \
+                       dres, dx, scratch);                                                       \
+    break;
+    QBLK_CASE(1) QBLK_CASE(2) QBLK_CASE(4) QBLK_CASE(8) QBLK_CASE(12) QBLK_CASE(16)
+#undef QBLK_CASE
+  }
+  QBLK_TRY(check_launch("rmsnorm_bwd_kernel"));
+  return colsum(parts, n, scratch, dgamma, st);
+}
+
+int colsum(int parts, int n, const float* partial, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, parts, n,
+                     partial, out);
+  return check_launch("colsum_kernel");
+}
+
+}  // namespace qblk

@@ -1,0 +1,91 @@
+"""One training step of a stack of decoder blocks with the LM head, on one
+GPU, as a sequence of libqblk calls (no arithmetic here).
+
+cuda_trainer.rs page, train_step_inner: gpu_forward over the blocks (each
+block's input kept for its backward), fused cross-entropy with loss scale
+1/T, gpu_backward in reverse block order. Different from the page: every
+gradient of the step is kept (one flat fp32 buffer) so that ONE global L2
+clip over all of them precedes any AdamW, and the clip scale is folded into
+the AdamW read instead of rewriting the gradients. The only device-to-host
+transfer of a step is the T loss partials.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import qblk
+from .qblk import PARAMS
+from .runtime import FlatParams, block_shapes, byte_buffer, empty
+
+
+class StackStep:
+    def __init__(self, cfg, layers, vocab, adamw=None, max_norm=1.0):
+        from .synth import ADAMW
+        self.cfg, self.L, self.V = cfg, layers, vocab
+        self.hp = dict(ADAMW if adamw is None else adamw)
+        self.max_norm = max_norm
+        self.c = qblk.make_config(cfg)
+        T, h = cfg.tokens, cfg.hidden
+        shapes = []
+        for l in range(layers):
+            shapes += block_shapes(cfg, prefix=f"{l}.")
+        shapes += [("g_final", (h,)), ("w_lm", (vocab, h))]
+        self.w = FlatParams(shapes)
+        self.g = FlatParams(shapes)  # zeroed: the padding between tensors stays 0 for the norm
+        self.m = FlatParams(shapes)
+        self.v = FlatParams(shapes)
+        self.saved_bytes, self.scratch_bytes = qblk.block_workspace_size(self.c)
+        self.saved = [byte_buffer(self.saved_bytes) for _ in range(layers)]
+        self.scratch = byte_buffer(self.scratch_bytes)
+        self.acts = empty((layers + 1, T, h))          # block inputs; acts[L] = last output
+        self.dh = [empty((T, h)), empty((T, h))]
+        self.ce_scratch = byte_buffer(qblk.cross_entropy_workspace_size(T, h, vocab))
+        self.targets = torch.zeros(T, dtype=torch.int32, device="cuda")
+        self.loss_partials = empty(T)
+        self.argmax = torch.empty(T, dtype=torch.int32, device="cuda")
+        self.loss_host = torch.empty(T, dtype=torch.float32, pin_memory=True)
+        self.norm = empty(1)
+        self.scale = empty(1)
+        self.clip_scratch = byte_buffer(qblk.clip_workspace_size([self.g.buf]))
+        self.t = 0
+
+    def load(self, inp: dict, x=None):
+        for l, p in enumerate(inp["layers"]):
+            self.w.load({f"{l}.{n}": p[n] for n in PARAMS})
+        self.w.load({"g_final": inp["g_final"], "w_lm": inp["w_lm"]})
+        self.acts[0].copy_(torch.from_numpy(inp["x"] if x is None else x))
+        self.targets.copy_(torch.from_numpy(inp["targets"]))
+        self.m.buf.zero_()
+        self.v.buf.zero_()
+        self.t = 0
+
+    def _layer(self, fp: FlatParams, l):
+        return {n: fp[f"{l}.{n}"] for n in PARAMS}
+
+    def step(self):
+        """Forward, loss, backward, global clip and AdamW; returns the loss
+        (the host sum of the partials) lazily as a callable."""
+        cfg, T, h, V = self.cfg, self.cfg.tokens, self.cfg.hidden, self.V
+        for l in range(self.L):
+            qblk.block_forward(self.c, self._layer(self.w, l), self.acts[l], self.acts[l + 1],
+                               self.saved[l], self.scratch)
+        qblk.fused_cross_entropy(T, h, V, cfg.eps, self.acts[self.L], self.w["g_final"], self.w["w_lm"],
+                                 self.targets, 1.0 / T, self.loss_partials, self.argmax, self.dh[0],
+                                 self.g["g_final"], self.g["w_lm"], self.ce_scratch)
+        self.loss_host.copy_(self.loss_partials, non_blocking=True)
+        cur = 0
+        for l in range(self.L - 1, -1, -1):
+            qblk.block_backward(self.c, self._layer(self.w, l), self.acts[l], self.dh[cur], self.saved[l],
+                                self.dh[cur ^ 1], self._layer(self.g, l), self.scratch)
+            cur ^= 1
+        self.dx = self.dh[cur]
+        qblk.clip_grad_norm([self.g.buf], self.max_norm, 0, self.norm, self.scale, self.clip_scratch)
+        self.t += 1
+        hp = self.hp
+        qblk.adamw_step([self.w.buf], [self.g.buf], [self.m.buf], [self.v.buf], hp["lr"], hp["beta1"],
+                        hp["beta2"], hp["eps"], hp["weight_decay"], self.t, grad_scale_dev=self.scale)
+
+    def loss(self):
+        torch.cuda.current_stream().synchronize()
+        return float(np.sum(self.loss_host.numpy().astype(np.float64))) / self.cfg.tokens

@@ -1,0 +1,85 @@
+/*
+ * qblk_ops.h — single-step entry points of libqblk, exported for step-level
+ * parity tests and measurement. Each runs one step of the block path with
+ * the same kernels the block entry points use. Conventions are those of
+ * qblk.h (device pointers owned by the caller, row-major, return codes).
+ */
+#ifndef QBLK_OPS_H
+#define QBLK_OPS_H
+
+#include "qblk.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Dense contraction on MFMA ([block] gemm_forward, gemm_backward_a,
+ * gemm_backward_b): layout 0 NT: C[M,N] = A[M,K] B[N,K]^T;
+ * 1 NN: C = A[M,K] B[K,N]; 2 TN: C = A[K,M]^T B[K,N]. All fp32 row-major
+ * with leading dimensions lda/ldb/ldc (elements). precision 0: fp32
+ * contraction; 1: operands rounded to fp16 (nearest even), fp32 accumulate.
+ * With accumulate = 1, C += result. The contiguous dimension of each
+ * operand must be a multiple of 4. */
+int32_t qblk_gemm(int32_t layout, int32_t precision, int32_t M, int32_t N, int32_t K,
+                  const float* A, int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                  int32_t accumulate, qblk_stream_t stream);
+
+/* RMSNorm forward over rows of x [rows, n] ([block] rms_norm_forward):
+ * y = x * rho * gamma with rho[r] = (mean x^2 + eps)^(-1/2) written to rho.
+ * When `res` is not NULL, x is first replaced by x + res and that sum is
+ * written to `sum_out` ([block] fused residual + RMSNorm). */
+int32_t qblk_rmsnorm_forward(int32_t rows, int32_t n, float eps, const float* x, const float* res,
+                             const float* gamma, float* y, float* sum_out, float* rho,
+                             void* scratch, size_t scratch_bytes, qblk_stream_t stream);
+
+/* RMSNorm backward ([block] rms_norm_backward): dx = rho (e - xhat
+ * mean(e xhat)), e = gamma dy, plus `dres` when not NULL (the residual
+ * gradient); dgamma = sum over rows of dy xhat (overwritten; deterministic
+ * two-stage reduction in scratch). */
+int32_t qblk_rmsnorm_backward(int32_t rows, int32_t n, float eps, const float* x,
+                              const float* gamma, const float* dy, const float* dres, float* dx,
+                              float* dgamma, void* scratch, size_t scratch_bytes,
+                              qblk_stream_t stream);
+
+/* Scratch bytes for the RMSNorm entry points above. */
+int32_t qblk_rmsnorm_workspace_size(int32_t rows, int32_t n, size_t* scratch_bytes);
+
+/* GQA causal softmax attention forward over q [T, heads*d], k, v
+ * [T, kv_heads*d] (rows strided by ldq/ldk/ldv elements) for `batch`
+ * independent sequences of length seq: o [T, heads*d] (ldo) and the
+ * row log-sum-exp lse [batch, heads, seq] (natural log, of the scaled
+ * scores). precision as in qblk_gemm. */
+int32_t qblk_attention_forward(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads,
+                               int32_t head_dim, int32_t precision, const float* q, int64_t ldq,
+                               const float* k, int64_t ldk, const float* v, int64_t ldv, float* o,
+                               int64_t ldo, float* lse, qblk_stream_t stream);
+
+/* Attention backward: given q, k, v, o, lse of the forward and do, writes
+ * dq [T, heads*d], dk, dv [T, kv_heads*d] (overwritten; dk and dv summed
+ * over the heads that share a KV head). scratch: qblk_attention_workspace_size. */
+int32_t qblk_attention_backward(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads,
+                                int32_t head_dim, int32_t precision, const float* q, int64_t ldq,
+                                const float* k, int64_t ldk, const float* v, int64_t ldv,
+                                const float* o, int64_t ldo, const float* lse, const float* d_o,
+                                int64_t lddo, float* dq, int64_t lddq, float* dk, int64_t lddk,
+                                float* dv, int64_t lddv, void* scratch, size_t scratch_bytes,
+                                qblk_stream_t stream);
+
+int32_t qblk_attention_workspace_size(int32_t batch, int32_t seq, int32_t heads,
+                                      size_t* scratch_bytes);
+
+/* Cross-entropy over materialised logits z [tokens, vocab] (fp32, row
+ * stride vocab), in place ([trainer] fused_cross_entropy_cuda):
+ * loss_partials[t] = logsumexp(z_t) - z_t[targets[t]]; argmax[t] = first
+ * index of the row maximum (NULL: skipped); z_t is overwritten with
+ * loss_scale * (softmax(z_t) - onehot(targets[t])). A target outside
+ * [0, vocab) yields a NaN partial and no onehot term. */
+int32_t qblk_cross_entropy_rows(int32_t tokens, int32_t vocab, float* z, const int32_t* targets,
+                                float loss_scale, float* loss_partials, int32_t* argmax,
+                                qblk_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QBLK_OPS_H */

@@ -1,0 +1,38 @@
+"""Shared helpers of the GPU parity tests."""
+import numpy as np
+import pytest
+import torch
+
+FP32_TOL = 2e-4   # max|err| / max|ref| for fp32 paths
+FP16_TOL = 2e-2   # for fp16-operand contraction paths
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def host(t):
+    return t.detach().float().cpu().double().numpy() if t.dtype != torch.float64 else t.detach().cpu().numpy()
+
+
+def rel_err(gpu, ref):
+    g = host(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    denom = np.max(np.abs(r))
+    if denom == 0.0:
+        return float(np.max(np.abs(g)))
+    return float(np.max(np.abs(g - r)) / denom)
+
+
+def check(name, gpu, ref, tol, report=None):
+    e = rel_err(gpu, ref)
+    if report is not None:
+        report[name] = e
+    assert e <= tol, f"{name}: max|err|/max|ref| = {e:.3e} > {tol:.1e}"
+    return e
+
+
+def announce(msg):
+    print(msg, flush=True)

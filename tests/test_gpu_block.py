@@ -1,0 +1,89 @@
+"""Block-level parity on the GPU: qblk_block_forward / qblk_block_backward
+against the oracle's block on the same seeded inputs, at the tiny, small
+and Qwen3-4B-shaped configurations (full sizes) and at ragged shapes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bwd_rmsnorm_qkv_amd import qblk, synth
+from bwd_rmsnorm_qkv_amd.runtime import Block, dev, empty
+from gpu_util import FP16_TOL, FP32_TOL, announce, check, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny": synth.TINY_BLOCK,
+    "tiny_ragged": synth.TINY_BLOCK.with_tokens(seq=45, batch=3),
+    "small": synth.SMALL_BLOCK,
+    "small_ragged_fp16": synth.BlockShape(hidden=512, heads=8, kv_heads=2, head_dim=64, intermediate=1408,
+                                          seq=77, batch=2, rope_theta=1e4, gemm_precision=1),
+    "qwen3_4b": synth.QWEN3_4B_BLOCK,
+}
+
+
+def _gammas_perturbed(p, seed):
+    """Non-unit gammas so every gamma path is exercised (the configs use 1)."""
+    rng = np.random.default_rng(seed)
+    p = dict(p)
+    for n in ("g_in", "g_post", "g_q", "g_k"):
+        p[n] = (1.0 + 0.25 * rng.standard_normal(p[n].shape)).astype(np.float32)
+    return p
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("unit_gammas", [True, False])
+def test_block_forward_backward(name, unit_gammas):
+    need_gpu()
+    c = CASES[name]
+    if name == "qwen3_4b" and not unit_gammas:
+        pytest.skip("one gamma variant at full Qwen3-4B size")
+    announce(f"block {name} T={c.tokens} unit_gammas={unit_gammas}")
+    inp = synth.block_inputs(c)
+    params = inp["params"] if unit_gammas else _gammas_perturbed(inp["params"], 3)
+    P = {k: dev(v) for k, v in params.items()}
+    X, DY = dev(inp["x"]), dev(inp["dy"])
+    blk = Block(c)
+    y = blk.forward(P, X)
+    grads = {k: empty(v.shape) for k, v in params.items()}
+    dx = blk.backward(P, X, DY, grads)
+    torch.cuda.synchronize()
+    y_ref, cache = oracle.block_forward(c, params, inp["x"])
+    dx_ref, g_ref = oracle.block_backward(c, params, cache, inp["dy"])
+    tol = FP16_TOL if c.gemm_precision else FP32_TOL
+    rep = {}
+    check("y", y, y_ref, tol, rep)
+    check("dx", dx, dx_ref, tol, rep)
+    for k in qblk.PARAMS:
+        check("d" + k, grads[k], g_ref[k], tol, rep)
+    announce("  " + " ".join(f"{k}={v:.1e}" for k, v in rep.items()))
+
+
+def test_block_backward_deterministic():
+    need_gpu()
+    c = synth.SMALL_BLOCK
+    announce("block determinism (small)")
+    inp = synth.block_inputs(c)
+    P = {k: dev(v) for k, v in inp["params"].items()}
+    X, DY = dev(inp["x"]), dev(inp["dy"])
+    blk = Block(c)
+    outs = []
+    for _ in range(2):
+        blk.forward(P, X)
+        grads = {k: empty(v.shape) for k, v in inp["params"].items()}
+        dx = blk.backward(P, X, DY, grads).clone()
+        torch.cuda.synchronize()
+        outs.append((dx, grads))
+    assert torch.equal(outs[0][0], outs[1][0])
+    for k in qblk.PARAMS:
+        assert torch.equal(outs[0][1][k], outs[1][1][k]), k
+
+
+def test_block_rejects_bad_config():
+    need_gpu()
+    c = synth.TINY_BLOCK
+    bad = qblk.make_config(c)
+    bad.kv_heads = 3
+    with pytest.raises(qblk.QblkError) as e:
+        qblk.block_workspace_size(bad)
+    assert e.value.code == qblk.QBLK_EINVAL

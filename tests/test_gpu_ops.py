@@ -1,0 +1,149 @@
+"""Step-level parity on the GPU: each single-step entry point of libqblk
+against the CPU oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import ops
+from bwd_rmsnorm_qkv_amd import qblk
+from bwd_rmsnorm_qkv_amd.runtime import dev, empty, byte_buffer
+from gpu_util import FP16_TOL, FP32_TOL, announce, check, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+# (M, N, K): several tiles plus ragged tails in every dimension
+GEMM_SHAPES = [(32, 64, 64), (200, 136, 104), (300, 392, 260), (37, 20, 12)]
+
+
+@pytest.mark.parametrize("precision", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1, 2])
+@pytest.mark.parametrize("shape", GEMM_SHAPES)
+def test_gemm(layout, precision, shape):
+    need_gpu()
+    M, N, K = shape
+    announce(f"gemm layout={layout} precision={precision} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    if layout == 2 and M % 4:
+        pytest.skip("TN needs M % 4 == 0")
+    a_shape = (M, K) if layout in (0, 1) else (K, M)
+    b_shape = (N, K) if layout == 0 else (K, N)
+    A = rng.standard_normal(a_shape).astype(np.float32)
+    B = rng.standard_normal(b_shape).astype(np.float32)
+    Cref = (A.astype(np.float64) if layout != 2 else A.astype(np.float64).T) @ \
+           (B.astype(np.float64).T if layout == 0 else B.astype(np.float64))
+    dA, dB = dev(A), dev(B)
+    Cg = torch.full((M, N), 7.0, device="cuda")
+    qblk.gemm(layout, precision, M, N, K, dA, a_shape[1], dB, b_shape[1], Cg, N)
+    torch.cuda.synchronize()
+    check("C", Cg, Cref, FP16_TOL if precision else FP32_TOL)
+    # accumulate mode adds to the existing C
+    qblk.gemm(layout, precision, M, N, K, dA, a_shape[1], dB, b_shape[1], Cg, N, accumulate=1)
+    torch.cuda.synchronize()
+    check("C+C", Cg, 2 * Cref, FP16_TOL if precision else FP32_TOL)
+
+
+@pytest.mark.parametrize("rows,n", [(32, 64), (77, 512), (512, 2560), (5, 4096)])
+def test_rmsnorm(rows, n):
+    need_gpu()
+    announce(f"rmsnorm rows={rows} n={n}")
+    rng = np.random.default_rng(rows + n)
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    r = rng.standard_normal((rows, n)).astype(np.float32)
+    g = (1 + 0.2 * rng.standard_normal(n)).astype(np.float32)
+    dy = rng.standard_normal((rows, n)).astype(np.float32)
+    dr = rng.standard_normal((rows, n)).astype(np.float32)
+    eps = 1e-6
+    X, R, G, DY, DR = (dev(a) for a in (x, r, g, dy, dr))
+    y, s, rho = empty((rows, n)), empty((rows, n)), empty(rows)
+    qblk.rmsnorm_forward(rows, n, eps, X, R, G, y, s, rho)
+    y_ref, rho_ref = ops.rmsnorm_fwd(x.astype(np.float64) + r, g, eps)
+    torch.cuda.synchronize()
+    check("y", y, y_ref, FP32_TOL)
+    check("sum", s, x.astype(np.float64) + r, 1e-7)
+    check("rho", rho, rho_ref, FP32_TOL)
+    dx, dg = empty((rows, n)), empty(n)
+    scratch = byte_buffer(qblk.rmsnorm_workspace_size(rows, n))
+    qblk.rmsnorm_backward(rows, n, eps, X, G, DY, DR, dx, dg, scratch)
+    dx_ref, dg_ref = ops.rmsnorm_bwd(x, g, dy, eps)
+    torch.cuda.synchronize()
+    check("dx", dx, dx_ref + dr, FP32_TOL)
+    check("dgamma", dg, dg_ref, FP32_TOL)
+    # deterministic: a second run is bitwise equal
+    dg2 = empty(n)
+    qblk.rmsnorm_backward(rows, n, eps, X, G, DY, DR, dx, dg2, scratch)
+    torch.cuda.synchronize()
+    assert torch.equal(dg, dg2)
+
+
+ATTN_SHAPES = [  # batch, seq, heads, kv_heads, head_dim, precision
+    (1, 32, 4, 2, 16, 0),
+    (2, 45, 4, 2, 16, 0),
+    (3, 100, 8, 2, 64, 0),
+    (1, 160, 8, 8, 64, 0),
+    (1, 130, 8, 2, 128, 1),
+    (2, 96, 4, 1, 64, 1),
+]
+
+
+@pytest.mark.parametrize("shape", ATTN_SHAPES)
+def test_attention(shape):
+    need_gpu()
+    B, S, H, KV, D, prec = shape
+    announce(f"attention batch={B} seq={S} heads={H} kv={KV} d={D} prec={prec}")
+    rng = np.random.default_rng(S * H + D)
+    T = B * S
+    q = rng.standard_normal((T, H * D)).astype(np.float32)
+    k = rng.standard_normal((T, KV * D)).astype(np.float32)
+    v = rng.standard_normal((T, KV * D)).astype(np.float32)
+    do = rng.standard_normal((T, H * D)).astype(np.float32)
+    Q, K_, V, DO = dev(q), dev(k), dev(v), dev(do)
+    o, lse = empty((T, H * D)), empty(B * H * S)
+    qblk.attention_forward(B, S, H, KV, D, prec, Q, H * D, K_, KV * D, V, KV * D, o, H * D, lse)
+    o_ref = ops.attention_fwd(q, k, v, B, S, H, KV, D)
+    tol = FP16_TOL if prec else FP32_TOL
+    torch.cuda.synchronize()
+    check("o", o, o_ref, tol)
+    # lse against the definition
+    lse_ref = np.zeros((B, H, S))
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // KV)
+            s = q[b * S:(b + 1) * S, h * D:(h + 1) * D].astype(np.float64) @ \
+                k[b * S:(b + 1) * S, g * D:(g + 1) * D].astype(np.float64).T / np.sqrt(D)
+            s[np.triu_indices(S, 1)] = -np.inf
+            m = s.max(1)
+            lse_ref[b, h] = m + np.log(np.exp(s - m[:, None]).sum(1))
+    assert np.max(np.abs(lse.cpu().numpy().reshape(B, H, S) - lse_ref)) < (5e-2 if prec else 1e-4)
+    dq, dk, dv = empty((T, H * D)), empty((T, KV * D)), empty((T, KV * D))
+    scratch = byte_buffer(qblk.attention_workspace_size(B, S, H))
+    qblk.attention_backward(B, S, H, KV, D, prec, Q, H * D, K_, KV * D, V, KV * D, o, H * D, lse, DO, H * D,
+                            dq, H * D, dk, KV * D, dv, KV * D, scratch)
+    dq_ref, dk_ref, dv_ref = ops.attention_bwd(q, k, v, do, B, S, H, KV, D)
+    torch.cuda.synchronize()
+    check("dq", dq, dq_ref, tol)
+    check("dk", dk, dk_ref, tol)
+    check("dv", dv, dv_ref, tol)
+
+
+def test_nf4_quantize_bit_exact():
+    need_gpu()
+    announce("nf4 quantize")
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((256, 320)) * 0.02).astype(np.float32)
+    w[7, :64] = 0.0                        # zero block
+    w[9, 64:128] = w[9, 64]                # constant block
+    w[11, 0:64] = np.float32(0.0123)       # all equal positive
+    packed, scales, _ = oracle.nf4_quantize(w)
+    W = dev(w)
+    codes = torch.empty(w.size // 2, dtype=torch.uint8, device="cuda")
+    absmax = empty(w.size // 64)
+    qblk.nf4_quantize(W, codes, absmax)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), packed)
+    assert np.array_equal(absmax.cpu().numpy().view(np.uint32), scales.view(np.uint32))
+    deq = empty(w.size)
+    qblk.nf4_dequantize(codes, absmax, w.size, deq)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(deq.cpu().numpy().reshape(w.shape),
+                                  oracle.nf4_dequantize(packed, scales, w.shape).astype(np.float32))
