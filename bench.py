@@ -90,12 +90,14 @@ def gemm_roofline(c, torch, qblk, reps):
         bufs.append((lay, M, N, K, acc, A, a_shape[1], B, b_shape[1], C))
     flops = sum(2.0 * M * N * K for (_, M, N, K, _) in specs)
     prec = c.gemm_precision
+    ws = max(qblk.gemm_workspace_size(lay, prec, M, N, K) for (lay, M, N, K, _) in specs)
+    scratch = torch.empty(max(ws, 16), dtype=torch.uint8, device="cuda")
 
     def run_all(events=None):
         for i, (lay, M, N, K, acc, A, lda, B, ldb, C) in enumerate(bufs):
             if events:
                 events[i][0].record()
-            qblk.gemm(lay, prec, M, N, K, A, lda, B, ldb, C, N, acc)
+            qblk.gemm(lay, prec, M, N, K, A, lda, B, ldb, C, N, acc, scratch=scratch)
             if events:
                 events[i][1].record()
 

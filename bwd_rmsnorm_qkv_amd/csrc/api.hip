@@ -47,18 +47,22 @@ static int check_params(const qblk_block_params* p) {
 int32_t qblk_block_forward(const qblk_config* cfg, const qblk_block_params* p, const float* x, float* y,
                            void* saved, size_t saved_bytes, void* scratch, size_t scratch_bytes,
                            qblk_stream_t stream) {
-  (void)scratch;
-  (void)scratch_bytes;
   QBLK_TRY(check_config(cfg));
   QBLK_TRY(check_params(p));
-  if (!x || !y || !saved || !aligned16(x) || !aligned16(y) || !aligned16(saved))
+  if (!x || !y || !saved || !scratch || !aligned16(x) || !aligned16(y) || !aligned16(saved) ||
+      !aligned16(scratch))
     return fail(QBLK_EINVAL, "block_forward: null or misaligned buffer");
   Saved s;
-  size_t need = 0;
+  Scratch w;
+  size_t need = 0, need_w = 0;
   carve_saved(*cfg, nullptr, s, need);
+  carve_scratch(*cfg, nullptr, w, need_w);
   if (saved_bytes < need) return fail(QBLK_EINVAL, "block_forward: saved workspace %zu < %zu", saved_bytes, need);
+  if (scratch_bytes < need_w)
+    return fail(QBLK_EINVAL, "block_forward: scratch workspace %zu < %zu", scratch_bytes, need_w);
   carve_saved(*cfg, saved, s, need);
-  return dense_block_forward(*cfg, *p, x, y, s, S(stream));
+  carve_scratch(*cfg, scratch, w, need_w);
+  return dense_block_forward(*cfg, *p, x, y, s, w, S(stream));
 }
 
 int32_t qblk_block_backward(const qblk_config* cfg, const qblk_block_params* p, const float* x, const float* dy,
@@ -89,8 +93,19 @@ int32_t qblk_block_backward(const qblk_config* cfg, const qblk_block_params* p, 
 
 // ------------------------------------------------------- cross-entropy
 
-static void ce_layout(int T, int h, int V, float** hf, float** z, float** dhf, float** red, size_t* bytes,
-                      void* base) {
+static size_t ce_gemm_ws(int T, int h, int V) {
+  GemmDesc a;
+  a.layout = Layout::NN; a.prec = Prec::F32;
+  a.M = T; a.N = h; a.K = V;
+  GemmDesc f = a;
+  f.layout = Layout::NT; f.N = V; f.K = h;
+  GemmDesc b = a;
+  b.layout = Layout::TN; b.M = V; b.N = h; b.K = T;
+  return std::max(gemm_workspace(a), std::max(gemm_workspace(f), gemm_workspace(b)));
+}
+
+static void ce_layout(int T, int h, int V, float** hf, float** z, float** dhf, float** red, float** ws,
+                      size_t* ws_bytes, size_t* bytes, void* base) {
   size_t off = 0;
   auto take = [&](size_t n) {
     off = (off + 255) & ~(size_t)255;
@@ -102,14 +117,16 @@ static void ce_layout(int T, int h, int V, float** hf, float** z, float** dhf, f
   *z = take((size_t)T * V);
   *dhf = take((size_t)T * h);
   *red = take(rmsnorm_bwd_scratch(T, h) / sizeof(float) + T);
+  *ws_bytes = ce_gemm_ws(T, h, V);
+  *ws = take(*ws_bytes / sizeof(float) + 1);
   *bytes = off;
 }
 
 int32_t qblk_cross_entropy_workspace_size(int32_t tokens, int32_t hidden, int32_t vocab, size_t* scratch_bytes) {
   if (tokens <= 0 || hidden <= 0 || vocab <= 0) return fail(QBLK_EINVAL, "cross_entropy: bad sizes");
-  float *a, *b, *c, *d;
-  size_t n = 0;
-  ce_layout(tokens, hidden, vocab, &a, &b, &c, &d, &n, nullptr);
+  float *a, *b, *c, *d, *e;
+  size_t n = 0, wsb = 0;
+  ce_layout(tokens, hidden, vocab, &a, &b, &c, &d, &e, &wsb, &n, nullptr);
   if (scratch_bytes) *scratch_bytes = n;
   return QBLK_OK;
 }
@@ -125,11 +142,11 @@ int32_t qblk_fused_cross_entropy(int32_t tokens, int32_t hidden, int32_t vocab, 
     return fail(QBLK_EINVAL, "cross_entropy: null pointer");
   if (g_final && !dg_final) return fail(QBLK_EINVAL, "cross_entropy: dg_final is NULL");
   if (g_final) QBLK_TRY(rmsnorm_check(tokens, hidden));
-  float *hf, *z, *dhf, *red;
-  size_t need = 0;
-  ce_layout(tokens, hidden, vocab, &hf, &z, &dhf, &red, &need, nullptr);
+  float *hf, *z, *dhf, *red, *ws;
+  size_t need = 0, wsb = 0;
+  ce_layout(tokens, hidden, vocab, &hf, &z, &dhf, &red, &ws, &wsb, &need, nullptr);
   if (scratch_bytes < need) return fail(QBLK_EINVAL, "cross_entropy: scratch %zu < %zu", scratch_bytes, need);
-  ce_layout(tokens, hidden, vocab, &hf, &z, &dhf, &red, &need, scratch);
+  ce_layout(tokens, hidden, vocab, &hf, &z, &dhf, &red, &ws, &wsb, &need, scratch);
   hipStream_t st = S(stream);
   const float* h_in = y_last;
   if (g_final) {
@@ -137,6 +154,7 @@ int32_t qblk_fused_cross_entropy(int32_t tokens, int32_t hidden, int32_t vocab, 
     h_in = hf;
   }
   GemmDesc f;  // z = hf W_lm^T
+  f.ws = ws; f.ws_bytes = wsb;
   f.layout = Layout::NT; f.prec = Prec::F32;
   f.M = tokens; f.N = vocab; f.K = hidden;
   f.a = h_in; f.lda = hidden;
@@ -145,6 +163,7 @@ int32_t qblk_fused_cross_entropy(int32_t tokens, int32_t hidden, int32_t vocab, 
   QBLK_TRY(gemm(f, st));
   QBLK_TRY(ce_rows(tokens, vocab, z, targets, loss_scale, loss_partials, argmax, st));
   GemmDesc a;  // dhf = dz W_lm
+  a.ws = ws; a.ws_bytes = wsb;
   a.layout = Layout::NN; a.prec = Prec::F32;
   a.M = tokens; a.N = hidden; a.K = vocab;
   a.a = z; a.lda = vocab;
@@ -152,6 +171,7 @@ int32_t qblk_fused_cross_entropy(int32_t tokens, int32_t hidden, int32_t vocab, 
   a.c = seg1(g_final ? dhf : dy_last, tokens); a.ldc = hidden;
   QBLK_TRY(gemm(a, st));
   GemmDesc b;  // dW_lm = dz^T hf
+  b.ws = ws; b.ws_bytes = wsb;
   b.layout = Layout::TN; b.prec = Prec::F32;
   b.M = vocab; b.N = hidden; b.K = tokens;
   b.a = z; b.lda = vocab;
@@ -217,9 +237,30 @@ int32_t qblk_nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t n
 
 // ------------------------------------------------------- single steps
 
-int32_t qblk_gemm(int32_t layout, int32_t precision, int32_t M, int32_t N, int32_t K, const float* A, int64_t lda,
-                  const float* B, int64_t ldb, float* C, int64_t ldc, int32_t accumulate, qblk_stream_t stream) {
+int32_t qblk_gemm_workspace_size(int32_t layout, int32_t precision, int32_t M, int32_t N, int32_t K,
+                                 size_t* scratch_bytes) {
   if (layout < 0 || layout > 2 || precision < 0 || precision > 1) return fail(QBLK_EINVAL, "gemm: layout/precision");
+  if (M <= 0 || N <= 0 || K <= 0) return fail(QBLK_EINVAL, "gemm: bad shape");
+  GemmDesc d;
+  d.layout = (Layout)layout;
+  d.prec = (Prec)precision;
+  d.M = M; d.N = N; d.K = K;
+  if (scratch_bytes) *scratch_bytes = gemm_workspace(d);
+  return QBLK_OK;
+}
+
+int32_t qblk_gemm(int32_t layout, int32_t precision, int32_t M, int32_t N, int32_t K, const float* A, int64_t lda,
+                  const float* B, int64_t ldb, float* C, int64_t ldc, int32_t accumulate, void* scratch,
+                  size_t scratch_bytes, qblk_stream_t stream) {
+  return qblk_gemm_ex(layout, precision, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, accumulate, scratch, scratch_bytes,
+                      stream);
+}
+
+int32_t qblk_gemm_ex(int32_t layout, int32_t precision, int32_t M, int32_t N, int32_t K, const void* A, int64_t lda,
+                     int32_t a_dtype, const void* B, int64_t ldb, int32_t b_dtype, float* C, int64_t ldc,
+                     int32_t accumulate, void* scratch, size_t scratch_bytes, qblk_stream_t stream) {
+  if (layout < 0 || layout > 2 || precision < 0 || precision > 1) return fail(QBLK_EINVAL, "gemm: layout/precision");
+  if (a_dtype < 0 || a_dtype > 1 || b_dtype < 0 || b_dtype > 1) return fail(QBLK_EINVAL, "gemm: operand dtype");
   if (lda % 4 || ldb % 4) return fail(QBLK_EINVAL, "gemm: lda and ldb must be multiples of 4");
   if (!A || !B || !C || !aligned16(A) || !aligned16(B)) return fail(QBLK_EINVAL, "gemm: null or misaligned operand");
   GemmDesc d;
@@ -227,10 +268,16 @@ int32_t qblk_gemm(int32_t layout, int32_t precision, int32_t M, int32_t N, int32
   d.prec = (Prec)precision;
   d.M = M; d.N = N; d.K = K;
   d.a = A; d.lda = lda;
+  d.a_src = a_dtype ? Src::F16 : Src::F32;
+  d.b_src = b_dtype ? Src::F16 : Src::F32;
   const int brows = d.layout == Layout::NT ? N : K;
   d.b = seg1(B, brows); d.ldb = ldb;
   d.c = seg1(C, M); d.ldc = ldc;
   d.accumulate = accumulate;
+  if (scratch && aligned16(scratch)) {
+    d.ws = (float*)scratch;
+    d.ws_bytes = scratch_bytes;
+  }
   return gemm(d, S(stream));
 }
 

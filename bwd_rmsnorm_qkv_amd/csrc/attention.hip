@@ -138,20 +138,30 @@ __device__ __forceinline__ void put4<f16>(f16* p, float4 v) {
 
 // 32 rows x DP columns (columns >= D and rows >= nvalid are zero) into
 // [32][PR]; optionally also transposed into [DP][PT].
+// Each thread takes 4 x 4 micro-blocks (4 rows, 4 columns): four 16-byte
+// global loads, four row writes, and — for the transposed copy — the 4 x 4
+// transpose in registers written as four 4-element column writes.
 template <typename T, int DP, int PR, int PT, bool ROWS, bool TRANS>
 __device__ __forceinline__ void stage_tile(T* s, T* st, const float* g, int64_t ld, int nvalid,
                                            int D, int tid, int nthr) {
   constexpr int C4 = DP / 4;
-  for (int c = tid; c < 32 * C4; c += nthr) {
-    const int r = c / C4, d4 = (c % C4) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r < nvalid && d4 < D) v = *(const float4*)(g + (int64_t)r * ld + d4);
-    if (ROWS) put4<T>(s + r * PR + d4, v);
+  for (int c = tid; c < 8 * C4; c += nthr) {
+    const int r0 = (c / C4) * 4, d4 = (c % C4) * 4;
+    float4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r0 + j < nvalid && d4 < D) v[j] = *(const float4*)(g + (int64_t)(r0 + j) * ld + d4);
+    }
+    if (ROWS) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) put4<T>(s + (r0 + j) * PR + d4, v[j]);
+    }
     if (TRANS) {
-      st[(d4 + 0) * PT + r] = (T)v.x;
-      st[(d4 + 1) * PT + r] = (T)v.y;
-      st[(d4 + 2) * PT + r] = (T)v.z;
-      st[(d4 + 3) * PT + r] = (T)v.w;
+      put4<T>(st + (d4 + 0) * PT + r0, make_float4(v[0].x, v[1].x, v[2].x, v[3].x));
+      put4<T>(st + (d4 + 1) * PT + r0, make_float4(v[0].y, v[1].y, v[2].y, v[3].y));
+      put4<T>(st + (d4 + 2) * PT + r0, make_float4(v[0].z, v[1].z, v[2].z, v[3].z));
+      put4<T>(st + (d4 + 3) * PT + r0, make_float4(v[0].w, v[1].w, v[2].w, v[3].w));
     }
   }
 }
@@ -162,7 +172,7 @@ __device__ __forceinline__ float half_sum(float v) { return v + __shfl_xor(v, 32
 // ------------------------------------------------------------ forward
 // grid (q tiles, kv groups, batch); one wave per query head of the group.
 template <Prec P, int DP>
-__global__ __launch_bounds__(1024) void attn_fwd_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(512) void attn_fwd_kernel(const AttnArgs a) {
   using A = AT<P, DP>;
   using T = typename A::T;
   __shared__ __attribute__((aligned(16))) T sK[32 * A::PR];
@@ -272,7 +282,7 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const AttnArgs a, float
 
 // dQ: grid (q tiles, kv groups, batch); one wave per query head.
 template <Prec P, int DP>
-__global__ __launch_bounds__(1024) void attn_dq_kernel(const AttnArgs a, const float* delta) {
+__global__ __launch_bounds__(512) void attn_dq_kernel(const AttnArgs a, const float* delta) {
   using A = AT<P, DP>;
   using T = typename A::T;
   __shared__ __attribute__((aligned(16))) T sK[32 * A::PR];
@@ -506,7 +516,7 @@ int attention_check(int batch, int seq, int heads, int kv_heads, int head_dim) {
   if (batch <= 0 || seq <= 0 || heads <= 0 || kv_heads <= 0)
     return fail(QBLK_EINVAL, "attention: batch=%d seq=%d heads=%d kv_heads=%d", batch, seq, heads, kv_heads);
   if (heads % kv_heads) return fail(QBLK_EINVAL, "attention: heads %% kv_heads != 0");
-  if (heads / kv_heads > 16) return fail(QBLK_EUNSUPPORTED, "attention: more than 16 query heads per KV head");
+  if (heads / kv_heads > 8) return fail(QBLK_EUNSUPPORTED, "attention: more than 8 query heads per KV head");
   if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
     return fail(QBLK_EUNSUPPORTED, "attention: head_dim %d not in {16, 32, 64, 128}", head_dim);
   return 0;

@@ -32,10 +32,13 @@ struct Scratch {
   float *ds, *dgu, *dn2, *dr1, *d_o, *dqr, *dkr, *dqkv, *dn1;
   char* attn;
   float* red;
+  float* gemm_ws;  // split-K partial sums of the block's GEMMs
+  size_t gemm_ws_bytes;
 };
 
 void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes);
-void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes);
+// lora_rank > 0 also sizes the GEMM workspace for the NF4 + LoRA GEMMs.
+void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes, int lora_rank = 0);
 int check_config(const qblk_config* c);
 
 // The projections of a block, forward: qkv = n1 [Wq;Wk;Wv]^T;
@@ -62,7 +65,7 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
                         hipStream_t st);
 
 int dense_block_forward(const qblk_config& c, const qblk_block_params& p, const float* x, float* y,
-                        const Saved& s, hipStream_t st);
+                        const Saved& s, const Scratch& w, hipStream_t st);
 int dense_block_backward(const qblk_config& c, const qblk_block_params& p, const qblk_block_grads& gr,
                          const float* x, const float* dy, const Saved& s, float* dx, const Scratch& w,
                          hipStream_t st);

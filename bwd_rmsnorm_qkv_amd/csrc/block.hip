@@ -17,6 +17,8 @@
 #include "gemm.h"
 #include "norms.h"
 
+#include <vector>
+
 namespace qblk {
 
 // ------------------------------------------------------------- layouts
@@ -56,7 +58,39 @@ void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes) {
   bytes = cv.off;
 }
 
-void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes) {
+Prec prec_of(const qblk_config& c) { return c.gemm_precision ? Prec::F16 : Prec::F32; }
+
+// Largest split-K workspace any GEMM of the block asks for.
+static size_t block_gemm_ws(const qblk_config& c, int r) {
+  const int T = c.seq * c.batch, h = c.hidden, qd = c.heads * c.head_dim, kvd = c.kv_heads * c.head_dim;
+  const int I = c.intermediate, qkv = qd + 2 * kvd;
+  struct S { Layout l; int M, N, K; };
+  std::vector<S> v = {
+      {Layout::NT, T, qkv, h}, {Layout::NT, T, h, qd}, {Layout::NT, T, 2 * I, h}, {Layout::NT, T, h, I},
+      {Layout::NN, T, I, h},   {Layout::TN, h, I, T},  {Layout::NN, T, h, 2 * I}, {Layout::TN, 2 * I, h, T},
+      {Layout::NN, T, qd, h},  {Layout::TN, h, qd, T}, {Layout::NN, T, h, qkv},   {Layout::TN, qkv, h, T}};
+  if (r > 0) {
+    const int ins[4] = {h, qd, h, I}, outs[4] = {qkv, h, 2 * I, h}, ns[4] = {3, 1, 2, 1};
+    const int outk[7] = {qd, kvd, kvd, h, I, I, h};
+    for (int g = 0; g < 4; ++g) {
+      v.push_back({Layout::NT, T, ns[g] * r, ins[g]});
+      v.push_back({Layout::TN, outs[g], ns[g] * r, T});
+      v.push_back({Layout::TN, ns[g] * r, ins[g], T});
+    }
+    for (int k = 0; k < 7; ++k) v.push_back({Layout::NN, T, r, outk[k]});
+  }
+  size_t m = 0;
+  for (const S& x : v) {
+    GemmDesc d;
+    d.layout = x.l;
+    d.prec = prec_of(c);
+    d.M = x.M; d.N = x.N; d.K = x.K;
+    m = std::max(m, gemm_workspace(d));
+  }
+  return m;
+}
+
+void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes, int lora_rank) {
   const size_t T = (size_t)c.seq * c.batch, h = c.hidden, d = c.head_dim;
   const size_t qd = (size_t)c.heads * d, kvd = (size_t)c.kv_heads * d, I = c.intermediate;
   Carver cv(base);
@@ -73,6 +107,8 @@ void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes) 
   const size_t red = std::max(rmsnorm_bwd_scratch((int)T, c.hidden),
                               qk_norm_rope_bwd_scratch((int)T, c.heads, c.kv_heads, c.head_dim));
   s.red = cv.take<float>(red / sizeof(float) + 1);
+  s.gemm_ws_bytes = block_gemm_ws(c, lora_rank);
+  s.gemm_ws = cv.take<float>(s.gemm_ws_bytes / sizeof(float) + 1);
   bytes = cv.off;
 }
 
@@ -94,8 +130,6 @@ int check_config(const qblk_config* c) {
   if (c->hidden > 4096) return fail(QBLK_EUNSUPPORTED, "config: hidden above 4096");
   return QBLK_OK;
 }
-
-Prec prec_of(const qblk_config& c) { return c.gemm_precision ? Prec::F16 : Prec::F32; }
 
 // ---------------------------------------------------------------- forward
 
@@ -172,9 +206,11 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
 
 namespace {
 
-GemmDesc nt(const qblk_config& c, int M, int N, int K, const float* a, int64_t lda, Seg b, int64_t ldb,
-            float* out, int64_t ldc) {
+GemmDesc nt(const qblk_config& c, const Scratch& w, int M, int N, int K, const float* a, int64_t lda, Seg b,
+            int64_t ldb, float* out, int64_t ldc) {
   GemmDesc g;
+  g.ws = w.gemm_ws;
+  g.ws_bytes = w.gemm_ws_bytes;
   g.layout = Layout::NT;
   g.prec = prec_of(c);
   g.M = M; g.N = N; g.K = K;
@@ -195,25 +231,25 @@ Seg seg3(const void* a, int na, const void* b, int nb, const void* cc, int nc) {
 }  // namespace
 
 int dense_block_forward(const qblk_config& c, const qblk_block_params& p, const float* x, float* y,
-                        const Saved& s, hipStream_t st) {
+                        const Saved& s, const Scratch& w, hipStream_t st) {
   const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
   ProjFwd proj;
   proj.qkv = [&](const float* n1, float* qkv, hipStream_t s_) {
-    return gemm(nt(c, T, qd + 2 * kvd, h, n1, h, seg3(p.w_q, qd, p.w_k, kvd, p.w_v, kvd), h, qkv, qd + 2 * kvd),
+    return gemm(nt(c, w, T, qd + 2 * kvd, h, n1, h, seg3(p.w_q, qd, p.w_k, kvd, p.w_v, kvd), h, qkv, qd + 2 * kvd),
                 s_);
   };
   proj.o = [&](const float* o, const float* res, float* out, hipStream_t s_) {
-    GemmDesc g = nt(c, T, h, qd, o, qd, seg1(p.w_o, h), qd, out, h);
+    GemmDesc g = nt(c, w, T, h, qd, o, qd, seg1(p.w_o, h), qd, out, h);
     g.r = res; g.ldr = h;
     return gemm(g, s_);
   };
   proj.gate_up = [&](const float* n2, float* gu, hipStream_t s_) {
     Seg b = seg3(p.w_gate, I, p.w_up, I, nullptr, 0);
-    return gemm(nt(c, T, 2 * I, h, n2, h, b, h, gu, 2 * I), s_);
+    return gemm(nt(c, w, T, 2 * I, h, n2, h, b, h, gu, 2 * I), s_);
   };
   proj.down = [&](const float* sv, const float* res, float* out, hipStream_t s_) {
-    GemmDesc g = nt(c, T, h, I, sv, I, seg1(p.w_down, h), I, out, h);
+    GemmDesc g = nt(c, w, T, h, I, sv, I, seg1(p.w_down, h), I, out, h);
     g.r = res; g.ldr = h;
     return gemm(g, s_);
   };
@@ -232,6 +268,7 @@ int dense_block_backward(const qblk_config& c, const qblk_block_params& p, const
   auto dxdw = [&](const float* dyv, int n_out, const float* xin, int n_in, Seg wseg, Seg cseg, float* dxo,
                   hipStream_t s_) -> int {
     GemmDesc a;
+    a.ws = w.gemm_ws; a.ws_bytes = w.gemm_ws_bytes;
     a.layout = Layout::NN; a.prec = pr;
     a.M = T; a.N = n_in; a.K = n_out;
     a.a = dyv; a.lda = n_out;
@@ -239,6 +276,7 @@ int dense_block_backward(const qblk_config& c, const qblk_block_params& p, const
     a.c = seg1(dxo, T); a.ldc = n_in;
     QBLK_TRY(gemm(a, s_));
     GemmDesc b;
+    b.ws = w.gemm_ws; b.ws_bytes = w.gemm_ws_bytes;
     b.layout = Layout::TN; b.prec = pr;
     b.M = n_out; b.N = n_in; b.K = T;
     b.a = dyv; b.lda = n_out;

@@ -29,7 +29,7 @@ struct Seg {
   int32_t nseg = 1;
 };
 
-inline Seg seg1(const void* p, int rows) {
+__host__ __device__ inline Seg seg1(const void* p, int rows) {
   Seg s;
   s.p[0] = p;
   s.start[0] = 0;
@@ -88,8 +88,14 @@ struct GemmDesc {
   // [s*c_cols_blockdiag, (s+1)*c_cols_blockdiag) of rows in C-segment s,
   // written at column 0 of that segment (the diagonal blocks of a product).
   int32_t c_cols_blockdiag = 0;
+  // Optional workspace for split-K partial sums (deterministic: partials
+  // are added in a fixed order by a second kernel). NULL: no split.
+  float* ws = nullptr;
+  size_t ws_bytes = 0;
 };
 
 int gemm(const GemmDesc& d, hipStream_t stream);
+// Bytes of split-K workspace the GEMM would use for this shape (0 if none).
+size_t gemm_workspace(const GemmDesc& d);
 
 }  // namespace qblk

@@ -1,24 +1,35 @@
 // MFMA GEMM engine for gfx950: every projection of the decoder block, its
 // backward (dX and dW), the LM head, and the NF4-dequant + LoRA variants.
 //
-// Tiling. A workgroup of WM x WN waves computes a BM x BN tile of C; each
-// wave owns TM x TN blocks of 32 x 32, accumulated by v_mfma_f32_32x32x2_f32
-// (fp32) or v_mfma_f32_32x32x16_f16 (fp16 operands). K advances in steps of
-// BK elements (64 bytes of operand per row). Operand tiles are staged through
-// LDS as [row][k] with k contiguous, double buffered: the global loads of
-// tile t+1 are issued before the MFMAs of tile t and written to the other
-// LDS buffer afterwards, so one barrier per K step suffices.
+// Tiling. A workgroup of 2 x 2 waves computes a BM x BN tile of C; each wave
+// owns TM x TN blocks of 32 x 32 accumulated by v_mfma_f32_32x32x2_f32 (fp32)
+// or v_mfma_f32_32x32x16_f16 (fp16 operands). K advances in tiles of BK
+// elements. Operand tiles are staged through LDS as [row][k], k contiguous,
+// with 16 bytes of padding per row (conflict-free 16-byte reads), double
+// buffered: the global loads of tile t+1 are issued before the MFMAs of tile
+// t and written to the other buffer afterwards (one barrier per tile).
+//
+// Staging. Every thread's share of a tile is fixed for the whole launch, so
+// its row pointers (K-contiguous operands) or its column offset
+// (M/N-contiguous operands) are computed once; a K step is then one 16-byte
+// load per chunk. fp16 operands are copied to LDS as they are; fp32 operands
+// are rounded to fp16 (nearest even) on the way when the contraction is
+// fp16; NF4 codes are decoded (level * block scale) and rounded to fp16. An
+// M/N-contiguous operand is transposed in registers: a thread loads KM
+// consecutive k rows of one 16-byte column group and writes each column as
+// one contiguous run of KM values.
 //
 // Lane/K mapping. For a 32-row block, lane l works on row l % 32 and on the
-// K half (l / 32); it reads that half of the row (BK/2 contiguous elements)
-// with two 16-byte LDS reads and feeds the MFMA steps from it. A and B use
-// the same K assignment, so the contraction is exact whatever order the
+// K half (l / 32) of the tile, read as contiguous 16-byte chunks. A and B
+// use the same K assignment, so the contraction is exact whatever order the
 // hardware sums its K lanes in. The accumulator of a 32 x 32 block holds, in
 // lane l, column l % 32 and rows 8g + 4(l/32) + r for register 4g + r.
 //
-// Operand layouts are handled by the staging code: K-contiguous rows are
-// loaded as 16-byte chunks; M/N-contiguous operands are loaded as 4 (rows)
-// by KM (k) micro-blocks and transposed in registers before the LDS write.
+// Skinny problems (few output tiles, long K) are split along K over more
+// workgroups; the partial tiles go to a caller-provided workspace and a
+// second kernel adds them in a fixed order (deterministic) and applies the
+// epilogue. Workgroup ids are remapped so that tiles sharing a B tile run on
+// the same XCD at the same time (one L2 per XCD).
 #include "gemm.h"
 
 #include "../../include/qblk.h"
@@ -26,19 +37,28 @@
 namespace qblk {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <Prec P>
 struct PT;
 template <>
 struct PT<Prec::F32> {
   using T = float;
-  static constexpr int BK = 16;
-  static constexpr int PAD = 4;
+  static constexpr int BK = 32;
 };
 template <>
 struct PT<Prec::F16> {
   using T = f16;
-  static constexpr int BK = 32;
-  static constexpr int PAD = 8;
+  static constexpr int BK = 64;
+};
+
+template <Src S>
+struct SrcT {
+  using type = float;
+};
+template <>
+struct SrcT<Src::F16> {
+  using type = f16;
 };
 
 __device__ __forceinline__ int seg_of(const Seg& s, int r) {
@@ -48,178 +68,446 @@ __device__ __forceinline__ int seg_of(const Seg& s, int r) {
   return sg;
 }
 
-__device__ __forceinline__ const float* seg_row_f32(const Seg& s, int64_t ld, int r) {
-  const int sg = seg_of(s, r);
-  return (const float*)s.p[sg] + (int64_t)(r - s.start[sg]) * ld;
+__device__ __forceinline__ float4 as_f4(u32x4 v) { return __builtin_bit_cast(float4, v); }
+__device__ __forceinline__ half8 as_h8(u32x4 v) { return __builtin_bit_cast(half8, v); }
+
+template <typename T, int N>
+__device__ __forceinline__ void store_run(T* dst, const T (&x)[N]) {
+  constexpr int BYTES = N * (int)sizeof(T);
+  if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+    for (int c = 0; c < BYTES / 16; ++c) {
+      u32x4 w;
+      __builtin_memcpy(&w, &x[c * 16 / sizeof(T)], 16);
+      *(u32x4*)((char*)dst + 16 * c) = w;
+    }
+  } else if constexpr (BYTES == 8) {
+    uint2 w;
+    __builtin_memcpy(&w, &x[0], 8);
+    *(uint2*)dst = w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) dst[i] = x[i];
+  }
 }
 
-__device__ __forceinline__ const f16* seg_row_f16(const Seg& s, int64_t ld, int r) {
-  const int sg = seg_of(s, r);
-  return (const f16*)s.p[sg] + (int64_t)(r - s.start[sg]) * ld;
-}
+// ------------------------------------------------------------- loaders
 
-__device__ __forceinline__ float4 ld4_f16(const f16* p) {
-  const half4 h = *(const half4*)p;
-  return make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
-}
+// R x BK tile from K-contiguous storage rows of fp32 or fp16 elements.
+// Thread t owns chunks c = t + j NT (j < CPT): all at the same K offset kc,
+// on rows spaced RSTEP apart.
+template <int R, int BK, int NT, typename S>
+struct RowLoader {
+  static constexpr int EPC = 16 / sizeof(S);
+  static constexpr int CPR = BK / EPC;
+  static_assert(BK % EPC == 0 && NT % CPR == 0, "tile/threads mismatch");
+  static constexpr int RSTEP = NT / CPR;
+  static_assert(R % RSTEP == 0, "tile/threads mismatch");
+  static constexpr int CPT = R / RSTEP;
+  const S* p[CPT];
+  int kc;
+  struct Buf {
+    u32x4 v[CPT];
+  };
 
-// Four NF4 elements at flat index e (a multiple of 4) of one segment.
-__device__ __forceinline__ float4 ld4_nf4(const uint8_t* codes, const float* scales, int64_t e,
-                                          const float* lv) {
-  const uint16_t c = *(const uint16_t*)(codes + (e >> 1));
-  const float a = scales[e >> 6];
-  return make_float4(lv[c & 15] * a, lv[(c >> 4) & 15] * a, lv[(c >> 8) & 15] * a,
-                     lv[(c >> 12) & 15] * a);
-}
-
-template <typename T>
-__device__ __forceinline__ void st4(T* p, float4 v);
-template <>
-__device__ __forceinline__ void st4<float>(float* p, float4 v) {
-  *(float4*)p = v;
-}
-template <>
-__device__ __forceinline__ void st4<f16>(f16* p, float4 v) {
-  *(half4*)p = to_half4(v);
-}
-
-// ------------------------------------------------------------- staging
-
-// R x BK tile from K-contiguous storage rows.
-template <int R, int BK, int NT>
-struct KRows {
-  static constexpr int CPR = BK / 4;
-  static constexpr int CPT = (R * CPR) / NT;
-  static_assert(CPT >= 1 && (R * CPR) % NT == 0, "tile/threads mismatch");
-  float4 v[CPT];
-
-  template <class Fetch>
-  __device__ __forceinline__ void load(Fetch f, int row0, int nrows, int k0, int K, int tid) {
+  template <class RowPtr>
+  __device__ __forceinline__ void init(RowPtr rp, int row0, int nrows, int tid) {
+    kc = (tid % CPR) * EPC;
+    const int r0 = row0 + tid / CPR;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-      const int c = tid + j * NT, r = c / CPR, kc = c % CPR;
-      const int gr = row0 + r, gk = k0 + kc * 4;
-      v[j] = (gr < nrows && gk < K) ? f(gr, gk) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int r = r0 + j * RSTEP;
+      p[j] = r < nrows ? rp(r) + kc : nullptr;
     }
   }
+  __device__ __forceinline__ void load(Buf& b, int k0, int kend) const {
+    const bool kin = k0 + kc < kend;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) b.v[j] = (kin && p[j]) ? *(const u32x4*)(p[j] + k0) : u32x4{0u, 0u, 0u, 0u};
+  }
   template <typename T, int PITCH>
-  __device__ __forceinline__ void store(T* s, int tid) const {
+  __device__ __forceinline__ void store(const Buf& b, T* s, int tid, float scale = 1.f) const {
+    const int r0 = tid / CPR;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-      const int c = tid + j * NT, r = c / CPR, kc = c % CPR;
-      st4<T>(s + r * PITCH + kc * 4, v[j]);
-    }
-  }
-};
-
-// BK x R tile from storage whose rows are k and whose columns are the R
-// tile rows (M- or N-contiguous); written to LDS transposed as [R][BK].
-template <int R, int BK, int NT>
-struct KCols {
-  static constexpr int QUADS = R / 4;
-  static constexpr int KM = (BK * R) / (4 * NT);
-  static_assert(KM >= 1 && NT % QUADS == 0 && (NT / QUADS) * KM == BK, "tile/threads mismatch");
-  float4 v[KM];
-
-  template <class Fetch>
-  __device__ __forceinline__ void load(Fetch f, int row0, int nrows, int k0, int K, int tid) {
-    const int rq = tid % QUADS, kb = tid / QUADS;
-    const int gr = row0 + rq * 4;
-#pragma unroll
-    for (int kk = 0; kk < KM; ++kk) {
-      const int gk = k0 + kb * KM + kk;
-      v[kk] = (gr < nrows && gk < K) ? f(gk, gr) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-  template <typename T, int PITCH>
-  __device__ __forceinline__ void store(T* s, int tid) const {
-    const int rq = tid % QUADS, kb = tid / QUADS;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      T* dst = s + (rq * 4 + q) * PITCH + kb * KM;
-#pragma unroll
-      for (int kk = 0; kk < KM; ++kk) {
-        const float x = q == 0 ? v[kk].x : q == 1 ? v[kk].y : q == 2 ? v[kk].z : v[kk].w;
-        dst[kk] = (T)x;
+      T* dst = s + (r0 + j * RSTEP) * PITCH + kc;
+      if constexpr (sizeof(S) == sizeof(T)) {
+        if constexpr (sizeof(S) == 4) {
+          float4 f = as_f4(b.v[j]);
+          f.x *= scale; f.y *= scale; f.z *= scale; f.w *= scale;
+          *(float4*)dst = f;
+        } else {
+          *(u32x4*)dst = b.v[j];
+        }
+      } else {  // fp32 storage, fp16 contraction
+        float4 f = as_f4(b.v[j]);
+        f.x *= scale; f.y *= scale; f.z *= scale; f.w *= scale;
+        *(half4*)dst = to_half4(f);
       }
     }
   }
 };
 
-// ----------------------------------------------------------- MFMA core
+// BK x R tile from storage whose rows are k and whose columns are the tile
+// rows (M- or N-contiguous), written to LDS as [R][BK]. Thread t owns the
+// column group cl = (t % GROUPS) CW (one 16-byte load per k row) and the k
+// rows kb .. kb + KM - 1.
+template <int R, int BK, int NT, typename S>
+struct ColLoader {
+  static constexpr int CW = 16 / sizeof(S);
+  static constexpr int GROUPS = R / CW;
+  static_assert(R % CW == 0 && NT % GROUPS == 0, "tile/threads mismatch");
+  static constexpr int KG = NT / GROUPS;
+  static_assert(BK % KG == 0, "tile/threads mismatch");
+  static constexpr int KM = BK / KG;
+  int cl, kb, col;
+  bool cvalid;
+  struct Buf {
+    u32x4 v[KM];
+  };
 
-template <Prec P, int TM, int TN>
+  __device__ __forceinline__ void init(int row0, int nrows, int tid) {
+    cl = (tid % GROUPS) * CW;
+    kb = (tid / GROUPS) * KM;
+    col = row0 + cl;
+    cvalid = col < nrows;
+  }
+  // Storage row k of segmented storage sg (k rows stacked over the segments).
+  __device__ __forceinline__ void load(Buf& b, const Seg& sg, int64_t ld, int k0, int kend) const {
+    const int kf = k0 + kb;
+    const S* base = nullptr;
+    {
+      const int s = seg_of(sg, kf);
+      const int send = (s + 1 < sg.nseg) ? sg.start[s + 1] : 0x7fffffff;
+      if (kf + KM <= send) base = (const S*)sg.p[s] + (int64_t)(kf - sg.start[s]) * ld + col;
+    }
+#pragma unroll
+    for (int kk = 0; kk < KM; ++kk) {
+      const int k = kf + kk;
+      const bool ok = cvalid && k < kend;
+      if (!ok) {
+        b.v[kk] = u32x4{0u, 0u, 0u, 0u};
+      } else if (base) {
+        b.v[kk] = *(const u32x4*)(base + (int64_t)kk * ld);
+      } else {
+        const int s = seg_of(sg, k);
+        b.v[kk] = *(const u32x4*)((const S*)sg.p[s] + (int64_t)(k - sg.start[s]) * ld + col);
+      }
+    }
+  }
+  template <typename T, int PITCH>
+  __device__ __forceinline__ void store(const Buf& b, T* s, int tid) const {
+    (void)tid;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      T run[KM];
+#pragma unroll
+      for (int kk = 0; kk < KM; ++kk) {
+        if constexpr (sizeof(S) == 4) {
+          const float4 f = as_f4(b.v[kk]);
+          run[kk] = (T)(c == 0 ? f.x : c == 1 ? f.y : c == 2 ? f.z : f.w);
+        } else {
+          run[kk] = (T)as_h8(b.v[kk])[c];
+        }
+      }
+      store_run<T, KM>(s + (cl + c) * PITCH + kb, run);
+    }
+  }
+};
+
+// NF4 B operand, K-contiguous rows (forward y = x W~^T): chunks of 8
+// elements (4 bytes of codes) and the scale of their 64-element block.
+template <int R, int BK, int NT>
+struct Nf4RowLoader {
+  static constexpr int EPC = 8, CPR = BK / EPC;
+  static_assert(BK % EPC == 0 && NT % CPR == 0, "tile/threads mismatch");
+  static constexpr int RSTEP = NT / CPR;
+  static constexpr int CPT = R / RSTEP;
+  const uint8_t* cp[CPT];
+  const float* sp[CPT];
+  int64_t e0[CPT];
+  int kc;
+  struct Buf {
+    uint32_t code[CPT];
+    float sc[CPT];
+  };
+
+  __device__ __forceinline__ void init(const GemmDesc& d, int row0, int tid) {
+    kc = (tid % CPR) * EPC;
+    const int r0 = row0 + tid / CPR;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int n = r0 + j * RSTEP;
+      if (n < d.N) {
+        const int sg = seg_of(d.b, n);
+        e0[j] = (int64_t)(n - d.b.start[sg]) * d.ldb + kc;
+        cp[j] = d.nf4.codes[sg];
+        sp[j] = d.nf4.scales[sg];
+      } else {
+        cp[j] = nullptr;
+        sp[j] = nullptr;
+        e0[j] = 0;
+      }
+    }
+  }
+  __device__ __forceinline__ void load(Buf& b, int k0, int kend) const {
+    const bool kin = k0 + kc < kend;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      if (kin && cp[j]) {
+        const int64_t e = e0[j] + k0;
+        b.code[j] = *(const uint32_t*)(cp[j] + (e >> 1));
+        b.sc[j] = sp[j][e >> 6];
+      } else {
+        b.code[j] = 0;
+        b.sc[j] = 0.f;
+      }
+    }
+  }
+  template <typename T, int PITCH>
+  __device__ __forceinline__ void store(const Buf& b, T* s, int tid, const float* lv) const {
+    const int r0 = tid / CPR;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      half8 h;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = (f16)(lv[(b.code[j] >> (4 * i)) & 15] * b.sc[j]);
+      *(half8*)(s + (r0 + j * RSTEP) * PITCH + kc) = h;
+    }
+  }
+};
+
+// NF4 B operand stored [K, N] with N contiguous (backward dX = dY W~):
+// column groups of 8 (4 bytes of codes per k row).
+template <int R, int BK, int NT>
+struct Nf4ColLoader {
+  static constexpr int CW = 8, GROUPS = R / CW;
+  static_assert(R % CW == 0 && NT % GROUPS == 0, "tile/threads mismatch");
+  static constexpr int KG = NT / GROUPS;
+  static constexpr int KM = BK / KG;
+  int cl, kb, col;
+  bool cvalid;
+  struct Buf {
+    uint32_t code[KM];
+    float sc[KM];
+  };
+
+  __device__ __forceinline__ void init(int row0, int nrows, int tid) {
+    cl = (tid % GROUPS) * CW;
+    kb = (tid / GROUPS) * KM;
+    col = row0 + cl;
+    cvalid = col < nrows;
+  }
+  __device__ __forceinline__ void load(Buf& b, const GemmDesc& d, int k0, int kend) const {
+#pragma unroll
+    for (int kk = 0; kk < KM; ++kk) {
+      const int k = k0 + kb + kk;
+      if (cvalid && k < kend) {
+        const int s = seg_of(d.b, k);
+        const int64_t e = (int64_t)(k - d.b.start[s]) * d.ldb + col;
+        b.code[kk] = *(const uint32_t*)(d.nf4.codes[s] + (e >> 1));
+        b.sc[kk] = d.nf4.scales[s][e >> 6];
+      } else {
+        b.code[kk] = 0;
+        b.sc[kk] = 0.f;
+      }
+    }
+  }
+  template <typename T, int PITCH>
+  __device__ __forceinline__ void store(const Buf& b, T* s, int tid, const float* lv) const {
+    (void)tid;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      T run[KM];
+#pragma unroll
+      for (int kk = 0; kk < KM; ++kk) run[kk] = (T)(lv[(b.code[kk] >> (4 * c)) & 15] * b.sc[kk]);
+      store_run<T, KM>(s + (cl + c) * PITCH + kb, run);
+    }
+  }
+};
+
+// LoRA K-extension B operand for NT: row n of B-segment s sees ext columns
+// [s*bd, (s+1)*bd) of B_ext[s] (bd = blockdiag; bd = 0: one plain matrix).
+template <int R, int BK, int NT>
+struct ExtRowLoaderNT {
+  static constexpr int EPC = 4, CPR = BK / EPC, RSTEP = NT / CPR, CPT = R / RSTEP;
+  const float* p[CPT];
+  int lo[CPT], hi[CPT];
+  int kc;
+  struct Buf {
+    float4 v[CPT];
+  };
+  __device__ __forceinline__ void init(const GemmDesc& d, int row0, int tid) {
+    const KExt& x = d.ext;
+    kc = (tid % CPR) * EPC;
+    const int r0 = row0 + tid / CPR;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int n = r0 + j * RSTEP;
+      p[j] = nullptr;
+      lo[j] = hi[j] = 0;
+      if (n < d.N) {
+        if (x.blockdiag > 0) {
+          const int sg = seg_of(d.b, n);
+          lo[j] = sg * x.blockdiag;
+          hi[j] = lo[j] + x.blockdiag;
+          p[j] = x.b[sg] + (int64_t)(n - d.b.start[sg]) * x.ldb - lo[j];
+        } else {
+          lo[j] = 0;
+          hi[j] = x.kext;
+          p[j] = x.b[0] + (int64_t)n * x.ldb;
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void load(Buf& b, int k0) const {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int k = k0 + kc;
+      b.v[j] = (p[j] && k >= lo[j] && k < hi[j]) ? *(const float4*)(p[j] + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  template <typename T, int PITCH>
+  __device__ __forceinline__ void store(const Buf& b, T* s, int tid) const {
+    const int r0 = tid / CPR;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) *(half4*)(s + (r0 + j * RSTEP) * PITCH + kc) = to_half4(b.v[j]);
+  }
+};
+
+// LoRA K-extension B operand for NN: ext row k is row (k % bd) of B_ext[k / bd]
+// (bd = 0: row k of one matrix), columns contiguous.
+template <int R, int BK, int NT>
+struct ExtColLoaderNN {
+  using CL = ColLoader<R, BK, NT, float>;
+  using Buf = typename CL::Buf;
+  CL c;
+  __device__ __forceinline__ void init(int row0, int nrows, int tid) { c.init(row0, nrows, tid); }
+  __device__ __forceinline__ void load(Buf& b, const GemmDesc& d, int k0) const {
+    const KExt& x = d.ext;
+#pragma unroll
+    for (int kk = 0; kk < CL::KM; ++kk) {
+      const int k = k0 + c.kb + kk;
+      if (c.cvalid && k < x.kext) {
+        const float* row = x.blockdiag > 0 ? x.b[k / x.blockdiag] + (int64_t)(k % x.blockdiag) * x.ldb
+                                           : x.b[0] + (int64_t)k * x.ldb;
+        b.v[kk] = *(const u32x4*)(row + c.col);
+      } else {
+        b.v[kk] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  template <typename T, int PITCH>
+  __device__ __forceinline__ void store(const Buf& b, T* s, int tid) const {
+    c.template store<T, PITCH>(b, s, tid);
+  }
+};
+
+// ----------------------------------------------------------- MFMA core
+// One K tile of BK elements from LDS into the wave's TM x TN accumulators.
+// Lane l reads, for each of its blocks, row (l % 32) and the K half (l / 32)
+// of the tile: KH = BK/2 contiguous elements.
+
+template <Prec P, int TM, int TN, int BK>
 struct Core;
 
-template <int TM, int TN>
-struct Core<Prec::F32, TM, TN> {
+template <int TM, int TN, int BK>
+struct Core<Prec::F32, TM, TN, BK> {
+  static constexpr int KH = BK / 2;
   template <int PITCH>
   static __device__ __forceinline__ void run(const float* sA, const float* sB, int lane,
                                              floatx16 (&acc)[TM][TN]) {
     const int i = lane & 31, kh = lane >> 5;
-    float a[TM][8], b[TN][8];
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      const float* p = sA + (t * 32 + i) * PITCH + kh * 8;
-      const float4 x0 = *(const float4*)p, x1 = *(const float4*)(p + 4);
-      a[t][0] = x0.x; a[t][1] = x0.y; a[t][2] = x0.z; a[t][3] = x0.w;
-      a[t][4] = x1.x; a[t][5] = x1.y; a[t][6] = x1.z; a[t][7] = x1.w;
-    }
+    for (int q = 0; q < KH / 4; ++q) {
+      float4 a[TM], b[TN];
 #pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      const float* p = sB + (t * 32 + i) * PITCH + kh * 8;
-      const float4 x0 = *(const float4*)p, x1 = *(const float4*)(p + 4);
-      b[t][0] = x0.x; b[t][1] = x0.y; b[t][2] = x0.z; b[t][3] = x0.w;
-      b[t][4] = x1.x; b[t][5] = x1.y; b[t][6] = x1.z; b[t][7] = x1.w;
-    }
+      for (int t = 0; t < TM; ++t) a[t] = *(const float4*)(sA + (t * 32 + i) * PITCH + kh * KH + 4 * q);
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+      for (int t = 0; t < TN; ++t) b[t] = *(const float4*)(sB + (t * 32 + i) * PITCH + kh * KH + 4 * q);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[tm][s], b[tn][s], acc[tm][tn], 0, 0, 0);
+        for (int tn = 0; tn < TN; ++tn) {
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[tm].x, b[tn].x, acc[tm][tn], 0, 0, 0);
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[tm].y, b[tn].y, acc[tm][tn], 0, 0, 0);
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[tm].z, b[tn].z, acc[tm][tn], 0, 0, 0);
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[tm].w, b[tn].w, acc[tm][tn], 0, 0, 0);
+        }
+    }
   }
 };
 
-template <int TM, int TN>
-struct Core<Prec::F16, TM, TN> {
+template <int TM, int TN, int BK>
+struct Core<Prec::F16, TM, TN, BK> {
+  static constexpr int KH = BK / 2;
   template <int PITCH>
   static __device__ __forceinline__ void run(const f16* sA, const f16* sB, int lane,
                                              floatx16 (&acc)[TM][TN]) {
     const int i = lane & 31, kh = lane >> 5;
-    half8 a[TM][2], b[TN][2];
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      const f16* p = sA + (t * 32 + i) * PITCH + kh * 16;
-      a[t][0] = *(const half8*)p;
-      a[t][1] = *(const half8*)(p + 8);
-    }
+    for (int s = 0; s < KH / 8; ++s) {
+      half8 a[TM], b[TN];
 #pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      const f16* p = sB + (t * 32 + i) * PITCH + kh * 16;
-      b[t][0] = *(const half8*)p;
-      b[t][1] = *(const half8*)(p + 8);
-    }
+      for (int t = 0; t < TM; ++t) a[t] = *(const half8*)(sA + (t * 32 + i) * PITCH + kh * KH + 8 * s);
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+      for (int t = 0; t < TN; ++t) b[t] = *(const half8*)(sB + (t * 32 + i) * PITCH + kh * KH + 8 * s);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[tm][s], b[tn][s], acc[tm][tn], 0, 0, 0);
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+    }
   }
 };
 
 // ------------------------------------------------------------- kernel
 
-template <Prec P, Layout L, Src AS, Src BS, bool EXT, int WM, int WN, int TM, int TN>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmDesc d) {
+struct Grid {
+  int tiles_m, tiles_n, splits, kchunk;
+};
+
+// Final value of C[row, col]: the row pointer `cp` already routed through
+// the output segments; plus the residual and/or the old C.
+__device__ __forceinline__ void put_out(const GemmDesc& d, float* cp, int row, int col, float acc) {
+  float v = d.alpha * acc;
+  if (d.r) v += d.r[(int64_t)row * d.ldr + col];
+  if (d.accumulate) v += *cp;
+  *cp = v;
+}
+
+// Output row pointer (segment routing), or nullptr when the row is out of
+// range; `lo` is the first column this row keeps (diagonal-block mode).
+__device__ __forceinline__ float* out_row(const GemmDesc& d, int row, int& lo) {
+  if (row >= d.M) return nullptr;
+  const int sg = seg_of(d.c, row);
+  lo = d.c_cols_blockdiag > 0 ? sg * d.c_cols_blockdiag : 0;
+  return (float*)d.c.p[sg] + (int64_t)(row - d.c.start[sg]) * d.ldc;
+}
+
+__device__ __forceinline__ void store_out(const GemmDesc& d, int row, int col, float acc) {
+  int lo = 0;
+  float* rp = out_row(d, row, lo);
+  if (!rp) return;
+  if (d.c_cols_blockdiag > 0 && (col < lo || col >= lo + d.c_cols_blockdiag)) return;
+  put_out(d, rp + (col - lo), row, col, acc);
+}
+
+// C (or, with split-K, one partial of it) for one BM x BN tile and one K
+// range. The linear workgroup id is remapped so that consecutive logical
+// tiles (the M tiles that share a B tile) land on the same XCD (ids are
+// dealt to the 8 XCDs round-robin) and are dispatched together.
+template <Prec P, Layout L, Src AS, Src BS, bool EXT, int WM, int WN, int TM, int TN, int BK>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmDesc d, const Grid gd) {
   using T = typename PT<P>::T;
-  constexpr int BK = PT<P>::BK, PITCH = BK + PT<P>::PAD;
+  using SA = typename SrcT<AS>::type;
+  using SB = typename SrcT<BS>::type;
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int PITCH = BK + PAD;
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32, NT = WM * WN * 64;
-  constexpr bool A_KROWS = (L != Layout::TN);
-  constexpr bool B_KROWS = (L == Layout::NT);
+  constexpr bool A_ROWS = (L != Layout::TN);
+  constexpr bool B_ROWS = (L == Layout::NT);
+  constexpr bool B_NF4 = (BS == Src::NF4);
 
   __shared__ __attribute__((aligned(16))) T sA[2][BM * PITCH];
   __shared__ __attribute__((aligned(16))) T sB[2][BN * PITCH];
@@ -227,105 +515,120 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmDesc d) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
 
-  if constexpr (BS == Src::NF4) {
+  const int total = gd.tiles_m * gd.tiles_n * gd.splits;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per = total / 8, rem = total % 8;
+  const int lt = xcd * per + min(xcd, rem) + slot;
+  const int mt = lt % gd.tiles_m;
+  const int nt = (lt / gd.tiles_m) % gd.tiles_n;
+  const int sp = lt / (gd.tiles_m * gd.tiles_n);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int kb = sp * gd.kchunk;
+  const int ke = min(d.K, kb + gd.kchunk);
+
+  if constexpr (B_NF4) {
     if (tid < 16) s_lv[tid] = d.nf4.levels[tid];
     __syncthreads();
   }
 
-  using ATile = typename std::conditional<A_KROWS, KRows<BM, BK, NT>, KCols<BM, BK, NT>>::type;
-  using BTile = typename std::conditional<B_KROWS, KRows<BN, BK, NT>, KCols<BN, BK, NT>>::type;
-  ATile ta;
-  BTile tb;
+  // ---- loaders (thread shares fixed for the launch)
+  using ALoader = typename std::conditional<A_ROWS, RowLoader<BM, BK, NT, SA>, ColLoader<BM, BK, NT, SA>>::type;
+  using BLoader = typename std::conditional<
+      B_NF4, typename std::conditional<B_ROWS, Nf4RowLoader<BN, BK, NT>, Nf4ColLoader<BN, BK, NT>>::type,
+      typename std::conditional<B_ROWS, RowLoader<BN, BK, NT, SB>, ColLoader<BN, BK, NT, SB>>::type>::type;
+  ALoader la;
+  BLoader lb;
+  Seg aseg;
+  if constexpr (A_ROWS) {
+    la.init([&](int r) { return (const SA*)d.a + (int64_t)r * d.lda; }, m0, d.M, tid);
+  } else {
+    aseg = seg1(d.a, d.K);
+    la.init(m0, d.M, tid);
+  }
+  if constexpr (B_NF4) {
+    if constexpr (B_ROWS)
+      lb.init(d, n0, tid);
+    else
+      lb.init(n0, d.N, tid);
+  } else if constexpr (B_ROWS) {
+    lb.init(
+        [&](int n) {
+          const int sg = seg_of(d.b, n);
+          return (const SB*)d.b.p[sg] + (int64_t)(n - d.b.start[sg]) * d.ldb;
+        },
+        n0, d.N, tid);
+  } else {
+    lb.init(n0, d.N, tid);
+  }
 
-  const int nkt_base = (d.K + BK - 1) / BK;
-  const int nkt = nkt_base + (EXT ? (d.ext.kext + BK - 1) / BK : 0);
+  // LoRA extension columns (fp32 sources), processed by split 0 after its
+  // base K tiles.
+  using EALoader = RowLoader<BM, BK, NT, float>;
+  using EBLoader = typename std::conditional<B_ROWS, ExtRowLoaderNT<BN, BK, NT>, ExtColLoaderNN<BN, BK, NT>>::type;
+  EALoader ea;
+  EBLoader eb;
+  if constexpr (EXT) {
+    ea.init([&](int r) { return d.ext.a + (int64_t)r * d.ext.lda; }, m0, d.M, tid);
+    if constexpr (B_ROWS)
+      eb.init(d, n0, tid);
+    else
+      eb.init(n0, d.N, tid);
+  }
 
-  // Loads of K tile kt into registers.
-  auto fetch = [&](int kt) {
+  const int nkt_base = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+  const int nkt = nkt_base + ((EXT && sp == 0) ? (d.ext.kext + BK - 1) / BK : 0);
+
+  // Register payload of one K tile.
+  struct Regs {
+    typename ALoader::Buf a;
+    typename BLoader::Buf b;
+  };
+  Regs rg[1];
+  // The LoRA extension is at most one K tile (checked on the host), so one
+  // register set serves it.
+  struct ExtRegs {
+    typename EALoader::Buf a;
+    typename EBLoader::Buf b;
+  };
+  ExtRegs er;
+
+  auto fetch = [&](int kt, Regs& r) {
     if (!EXT || kt < nkt_base) {
-      const int k0 = kt * BK;
-      // A operand
-      if constexpr (A_KROWS) {
-        ta.load([&](int r, int k) -> float4 {
-                  if constexpr (AS == Src::F16)
-                    return ld4_f16((const f16*)d.a + (int64_t)r * d.lda + k);
-                  else
-                    return *(const float4*)((const float*)d.a + (int64_t)r * d.lda + k);
-                },
-                m0, d.M, k0, d.K, tid);
+      const int k0 = kb + kt * BK;
+      if constexpr (A_ROWS)
+        la.load(r.a, k0, ke);
+      else
+        la.load(r.a, aseg, d.lda, k0, ke);
+      if constexpr (B_NF4) {
+        if constexpr (B_ROWS)
+          lb.load(r.b, k0, ke);
+        else
+          lb.load(r.b, d, k0, ke);
+      } else if constexpr (B_ROWS) {
+        lb.load(r.b, k0, ke);
       } else {
-        ta.load([&](int k, int r) -> float4 {
-                  if constexpr (AS == Src::F16)
-                    return ld4_f16((const f16*)d.a + (int64_t)k * d.lda + r);
-                  else
-                    return *(const float4*)((const float*)d.a + (int64_t)k * d.lda + r);
-                },
-                m0, d.M, k0, d.K, tid);
-      }
-      // B operand
-      if constexpr (B_KROWS) {
-        tb.load([&](int n, int k) -> float4 {
-                  if constexpr (BS == Src::NF4) {
-                    const int sg = seg_of(d.b, n);
-                    const int64_t e = (int64_t)(n - d.b.start[sg]) * d.ldb + k;
-                    return ld4_nf4(d.nf4.codes[sg], d.nf4.scales[sg], e, s_lv);
-                  } else if constexpr (BS == Src::F16) {
-                    return ld4_f16(seg_row_f16(d.b, d.ldb, n) + k);
-                  } else {
-                    return *(const float4*)(seg_row_f32(d.b, d.ldb, n) + k);
-                  }
-                },
-                n0, d.N, k0, d.K, tid);
-      } else {
-        tb.load([&](int k, int n) -> float4 {
-                  if constexpr (BS == Src::NF4) {
-                    const int sg = seg_of(d.b, k);
-                    const int64_t e = (int64_t)(k - d.b.start[sg]) * d.ldb + n;
-                    return ld4_nf4(d.nf4.codes[sg], d.nf4.scales[sg], e, s_lv);
-                  } else if constexpr (BS == Src::F16) {
-                    return ld4_f16(seg_row_f16(d.b, d.ldb, k) + n);
-                  } else {
-                    return *(const float4*)(seg_row_f32(d.b, d.ldb, k) + n);
-                  }
-                },
-                n0, d.N, k0, d.K, tid);
+        lb.load(r.b, d.b, d.ldb, k0, ke);
       }
     } else if constexpr (EXT) {
       const int k0 = (kt - nkt_base) * BK;
-      const KExt& x = d.ext;
-      if constexpr (A_KROWS) {
-        ta.load([&](int r, int k) -> float4 {
-                  float4 v = *(const float4*)(x.a + (int64_t)r * x.lda + k);
-                  v.x *= x.a_scale; v.y *= x.a_scale; v.z *= x.a_scale; v.w *= x.a_scale;
-                  return v;
-                },
-                m0, d.M, k0, x.kext, tid);
-      }
-      if constexpr (B_KROWS) {
-        // NT: B_ext row n, ext columns k..k+3, block diagonal over B segments
-        tb.load([&](int n, int k) -> float4 {
-                  if (x.blockdiag > 0) {
-                    const int sg = seg_of(d.b, n);
-                    const int lo = sg * x.blockdiag;
-                    if (k < lo || k >= lo + x.blockdiag) return make_float4(0.f, 0.f, 0.f, 0.f);
-                    return *(const float4*)(x.b[sg] + (int64_t)(n - d.b.start[sg]) * x.ldb + (k - lo));
-                  }
-                  return *(const float4*)(x.b[0] + (int64_t)n * x.ldb + k);
-                },
-                n0, d.N, k0, x.kext, tid);
-      } else {
-        // NN: B_ext rows are ext columns k, stacked in groups of blockdiag
-        tb.load([&](int k, int n) -> float4 {
-                  if (x.blockdiag > 0) {
-                    const int sg = k / x.blockdiag;
-                    return *(const float4*)(x.b[sg] + (int64_t)(k - sg * x.blockdiag) * x.ldb + n);
-                  }
-                  return *(const float4*)(x.b[0] + (int64_t)k * x.ldb + n);
-                },
-                n0, d.N, k0, x.kext, tid);
-      }
+      ea.load(er.a, k0, d.ext.kext);
+      if constexpr (B_ROWS)
+        eb.load(er.b, k0);
+      else
+        eb.load(er.b, d, k0);
+    }
+  };
+  auto put = [&](int kt, int buf, const Regs& r) {
+    if (!EXT || kt < nkt_base) {
+      la.template store<T, PITCH>(r.a, sA[buf], tid);
+      if constexpr (B_NF4)
+        lb.template store<T, PITCH>(r.b, sB[buf], tid, s_lv);
+      else
+        lb.template store<T, PITCH>(r.b, sB[buf], tid);
+    } else if constexpr (EXT) {
+      ea.template store<T, PITCH>(er.a, sA[buf], tid, d.ext.a_scale);
+      eb.template store<T, PITCH>(er.b, sB[buf], tid);
     }
   };
 
@@ -337,72 +640,326 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmDesc d) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  fetch(0);
-  ta.template store<T, PITCH>(sA[0], tid);
-  tb.template store<T, PITCH>(sB[0], tid);
+  // Pipeline: the global loads of tile kt+1 are in flight while the MFMAs
+  // of tile kt run; then they go to the other LDS buffer. (One register set
+  // keeps two workgroups per CU resident, which hides more latency than a
+  // second register set would.)
+  if (nkt > 0) {
+    fetch(0, rg[0]);
+    put(0, 0, rg[0]);
+  }
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nkt) fetch(kt + 1);
-    Core<P, TM, TN>::template run<PITCH>(sA[cur] + wm * TM * 32 * PITCH,
-                                         sB[cur] + wn * TN * 32 * PITCH, lane, acc);
-    if (kt + 1 < nkt) {
-      ta.template store<T, PITCH>(sA[cur ^ 1], tid);
-      tb.template store<T, PITCH>(sB[cur ^ 1], tid);
-    }
+    if (kt + 1 < nkt) fetch(kt + 1, rg[0]);
+    Core<P, TM, TN, BK>::template run<PITCH>(sA[cur] + wm * TM * 32 * PITCH, sB[cur] + wn * TN * 32 * PITCH,
+                                             lane, acc);
+    if (kt + 1 < nkt) put(kt + 1, cur ^ 1, rg[0]);
     __syncthreads();
   }
 
   // Epilogue: lane holds column n0 + wn*TN*32 + tn*32 + (lane % 32) and rows
   // m0 + wm*TM*32 + tm*32 + 8g + 4(lane/32) + r.
   const int i = lane & 31, kh = lane >> 5;
+  if (gd.splits > 1) {
+    float* part = d.ws + (int64_t)sp * d.M * d.N;
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
+    for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      const int col = n0 + wn * TN * 32 + tn * 32 + i;
-      if (col >= d.N) continue;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = m0 + wm * TM * 32 + tm * 32 + 8 * g + 4 * kh + r;
           if (row >= d.M) continue;
-          const int sg = seg_of(d.c, row);
-          int ccol = col;
-          if (d.c_cols_blockdiag > 0) {
-            const int lo = sg * d.c_cols_blockdiag;
-            if (col < lo || col >= lo + d.c_cols_blockdiag) continue;
-            ccol = col - lo;
+          float* prow = part + (int64_t)row * d.N;
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            const int col = n0 + wn * TN * 32 + tn * 32 + i;
+            if (col < d.N) prow[col] = acc[tm][tn][4 * g + r];
           }
-          float* cp = (float*)d.c.p[sg] + (int64_t)(row - d.c.start[sg]) * d.ldc + ccol;
-          float v = d.alpha * acc[tm][tn][4 * g + r];
-          if (d.r) v += d.r[(int64_t)row * d.ldr + col];
-          if (d.accumulate) v += *cp;
-          *cp = v;
+        }
+    return;
+  }
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * TM * 32 + tm * 32 + 8 * g + 4 * kh + r;
+        int lo = 0;
+        float* rp = out_row(d, row, lo);
+        if (!rp) continue;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int col = n0 + wn * TN * 32 + tn * 32 + i;
+          if (col >= d.N) continue;
+          if (d.c_cols_blockdiag > 0 && (col < lo || col >= lo + d.c_cols_blockdiag)) continue;
+          put_out(d, rp + (col - lo), row, col, acc[tm][tn][4 * g + r]);
         }
       }
+}
+
+// ------------------------------------------- fp16 NT fast path (LDS DMA)
+//
+// C = A B^T with A [M, K] and B [N, K] both fp16, K-contiguous, K a multiple
+// of 64. Tiles move global -> LDS with global_load_lds_dwordx4 (16 bytes per
+// lane straight into LDS, no registers, no conversion), into two static LDS
+// stages so the copy of tile t+1 overlaps the MFMAs of tile t. An LDS row is
+// 64 halves (128 bytes) with no padding; its eight 16-byte chunks are stored
+// XOR-swizzled (physical chunk = logical chunk ^ (row & 7)) so that the MFMA
+// reads of 8 consecutive rows at one logical chunk hit 8 different bank
+// groups. Rows past M (or N) load a clamped, valid row; those results are
+// never stored.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+template <int TM, int TN>
+__global__ __launch_bounds__(256) void gemm_nt16_kernel(const GemmDesc d, const Grid gd) {
+  constexpr int BK = 64;
+  constexpr int BM = 2 * TM * 32, BN = 2 * TN * 32;
+  constexpr int JA = BM / 32, JB = BN / 32;  // DMA instructions per thread per tile
+  __shared__ __attribute__((aligned(16))) f16 sA0[BM * BK];
+  __shared__ __attribute__((aligned(16))) f16 sA1[BM * BK];
+  __shared__ __attribute__((aligned(16))) f16 sB0[BN * BK];
+  __shared__ __attribute__((aligned(16))) f16 sB1[BN * BK];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w % 2, wn = w / 2;
+
+  const int total = gd.tiles_m * gd.tiles_n * gd.splits;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per = total / 8, rem = total % 8;
+  const int lt = xcd * per + min(xcd, rem) + slot;
+  const int mt = lt % gd.tiles_m;
+  const int nt = (lt / gd.tiles_m) % gd.tiles_n;
+  const int sp = lt / (gd.tiles_m * gd.tiles_n);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int kb = sp * gd.kchunk;
+  const int ke = min(d.K, kb + gd.kchunk);
+  const int nkt = ke > kb ? (ke - kb) / BK : 0;
+
+  // DMA instruction j of wave w fills rows 32 j + 8 w .. +7 of the tile;
+  // lane l writes physical chunk l & 7 of row l >> 3, i.e. logical chunk
+  // (l & 7) ^ (l >> 3).
+  const int rsub = lane >> 3, lch = (lane & 7) ^ rsub;
+  const f16* pa[JA];
+  const f16* pb[JB];
+#pragma unroll
+  for (int j = 0; j < JA; ++j) {
+    const int r = min(m0 + 32 * j + 8 * w + rsub, d.M - 1);
+    pa[j] = (const f16*)d.a + (int64_t)r * d.lda + lch * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < JB; ++j) {
+    const int n = min(n0 + 32 * j + 8 * w + rsub, d.N - 1);
+    const int sg = seg_of(d.b, n);
+    pb[j] = (const f16*)d.b.p[sg] + (int64_t)(n - d.b.start[sg]) * d.ldb + lch * 8;
+  }
+  auto issue = [&](int k0, f16* sa, f16* sb) {
+#pragma unroll
+    for (int j = 0; j < JA; ++j)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(pa[j] + k0), (lds_void_t*)(sa + (32 * j + 8 * w) * BK), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(pb[j] + k0), (lds_void_t*)(sb + (32 * j + 8 * w) * BK), 16, 0, 0);
+  };
+
+  const int i = lane & 31, kh = lane >> 5, sw = i & 7;
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  auto compute = [&](const f16* sa, const f16* sb) {
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int pc = ((2 * s + kh) ^ sw) * 8;
+      half8 av[TM], bv[TN];
+#pragma unroll
+      for (int t = 0; t < TM; ++t) av[t] = *(const half8*)(sa + (wm * TM * 32 + t * 32 + i) * BK + pc);
+#pragma unroll
+      for (int t = 0; t < TN; ++t) bv[t] = *(const half8*)(sb + (wn * TN * 32 + t * 32 + i) * BK + pc);
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
     }
+  };
+
+  // Each half-step: own DMAs of the current stage done (s_waitcnt), barrier
+  // (everyone's are), start the next stage's DMA into the other buffer (its
+  // previous readers have all passed the barrier), then the MFMAs.
+  if (nkt > 0) issue(kb, sA0, sB0);
+  for (int kt = 0; kt < nkt; kt += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 1 < nkt) issue(kb + (kt + 1) * BK, sA1, sB1);
+    compute(sA0, sB0);
+    if (kt + 1 >= nkt) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 2 < nkt) issue(kb + (kt + 2) * BK, sA0, sB0);
+    compute(sA1, sB1);
+  }
+
+  const int ii = lane & 31;
+  if (gd.splits > 1) {
+    float* part = d.ws + (int64_t)sp * d.M * d.N;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + wm * TM * 32 + tm * 32 + 8 * g + 4 * kh + r;
+          if (row >= d.M) continue;
+          float* prow = part + (int64_t)row * d.N;
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            const int col = n0 + wn * TN * 32 + tn * 32 + ii;
+            if (col < d.N) prow[col] = acc[tm][tn][4 * g + r];
+          }
+        }
+    return;
+  }
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * TM * 32 + tm * 32 + 8 * g + 4 * kh + r;
+        int lo = 0;
+        float* rp = out_row(d, row, lo);
+        if (!rp) continue;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int col = n0 + wn * TN * 32 + tn * 32 + ii;
+          if (col >= d.N) continue;
+          if (d.c_cols_blockdiag > 0 && (col < lo || col >= lo + d.c_cols_blockdiag)) continue;
+          put_out(d, rp + (col - lo), row, col, acc[tm][tn][4 * g + r]);
+        }
+      }
+}
+
+// out = alpha * sum over splits (fixed order) [+ R] [+ C], routed like the
+// direct epilogue.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmDesc d, int splits) {
+  const int64_t mn = (int64_t)d.M * d.N;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < mn; e += (int64_t)gridDim.x * blockDim.x) {
+    float s = 0.f;
+    for (int p = 0; p < splits; ++p) s += d.ws[(int64_t)p * mn + e];
+    store_out(d, (int)(e / d.N), (int)(e % d.N), s);
   }
 }
 
+constexpr int kTargetWgs = 256;  // one 4-wave workgroup per CU (LDS-limited)
+constexpr int kMinKtPerSplit = 8;
+constexpr int kMaxSplits = 32;
+
+// Tile configurations: waves WM x WN, blocks per wave TM x TN, and the K
+// tile (BK_BIG: 64 fp16 / 32 fp32 elements, else half that).
+struct Cfg {
+  int id, bm, bn;
+  bool bk_big;
+};
+
+constexpr Cfg kCfgs[] = {
+    {0, 256, 128, true},   // WM 2, WN 2, TM 4, TN 2
+    {1, 128, 128, true},   // WM 2, WN 2, TM 2, TN 2
+    {2, 128, 128, false},  // WM 2, WN 2, TM 2, TN 2, short K tile
+    {3, 128, 256, true},   // WM 2, WN 2, TM 2, TN 4
+    {4, 256, 256, true},   // WM 2, WN 2, TM 4, TN 4
+};
+
+Cfg cfg_for(const GemmDesc& d) {
+#ifdef QBLK_FORCE_CFG
+  (void)d;
+  return kCfgs[QBLK_FORCE_CFG];
+#else
+  // 128 x 128 with two waves per SIMD measured best on every block shape.
+  (void)d;
+  return kCfgs[1];
+#endif
+}
+
+Grid plan(const GemmDesc& d, size_t ws_bytes) {
+  const Cfg c = cfg_for(d);
+  const int bk = PT<Prec::F16>::BK / (d.prec == Prec::F16 ? 1 : 2) / (c.bk_big ? 1 : 2);
+  Grid g;
+  g.tiles_m = (int)ceil_div(d.M, c.bm);
+  g.tiles_n = (int)ceil_div(d.N, c.bn);
+  const int tiles = g.tiles_m * g.tiles_n;
+  const int nkt = (int)ceil_div(d.K, bk);
+  int splits = (int)ceil_div(kTargetWgs, tiles);
+  splits = std::min(splits, std::max(1, nkt / kMinKtPerSplit));
+  splits = std::min(splits, kMaxSplits);
+  if (splits > 1 && (size_t)splits * d.M * d.N * sizeof(float) > ws_bytes) splits = 1;
+  if (splits < 1) splits = 1;
+  const int kt_per = (int)ceil_div(nkt, splits);
+  splits = std::max(1, (int)ceil_div(nkt, kt_per));  // no empty split
+  g.splits = splits;
+  g.kchunk = kt_per * bk;
+  return g;
+}
+
+template <Prec P, Layout L, Src AS, Src BS, bool EXT, int WM, int WN, int TM, int TN, bool BIG>
+void launch_cfg(const GemmDesc& d, const Grid& g, hipStream_t st) {
+  constexpr int BK = PT<P>::BK / (BIG ? 1 : 2);
+  const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
+  hipLaunchKernelGGL((gemm_kernel<P, L, AS, BS, EXT, WM, WN, TM, TN, BK>), dim3(nwg), dim3(WM * WN * 64), 0, st,
+                     d, g);
+}
+
+#ifdef QBLK_FORCE_CFG
+#define QBLK_CFG_ON(i) (QBLK_FORCE_CFG == (i))
+#else
+#define QBLK_CFG_ON(i) ((i) == 1)
+#endif
+
 template <Prec P, Layout L, Src AS, Src BS, bool EXT>
 int launch(const GemmDesc& d, hipStream_t st) {
-  constexpr int WM = 2, WN = 2, TM = 2, TN = 2;
-  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  dim3 grid((unsigned)ceil_div(d.N, BN), (unsigned)ceil_div(d.M, BM));
-  hipLaunchKernelGGL((gemm_kernel<P, L, AS, BS, EXT, WM, WN, TM, TN>), grid, dim3(WM * WN * 64), 0,
-                     st, d);
-  return check_launch("gemm_kernel");
+  const Grid g = plan(d, d.ws ? d.ws_bytes : 0);
+  switch (cfg_for(d).id) {
+#if QBLK_CFG_ON(0)
+    case 0: launch_cfg<P, L, AS, BS, EXT, 2, 2, 4, 2, true>(d, g, st); break;
+#endif
+#if QBLK_CFG_ON(1)
+    case 1: launch_cfg<P, L, AS, BS, EXT, 2, 2, 2, 2, true>(d, g, st); break;
+#endif
+#if QBLK_CFG_ON(2)
+    case 2: launch_cfg<P, L, AS, BS, EXT, 2, 2, 2, 2, false>(d, g, st); break;
+#endif
+#if QBLK_CFG_ON(3)
+    case 3: launch_cfg<P, L, AS, BS, EXT, 2, 2, 2, 4, true>(d, g, st); break;
+#endif
+#if QBLK_CFG_ON(4)
+    case 4: launch_cfg<P, L, AS, BS, EXT, 2, 2, 4, 4, true>(d, g, st); break;
+#endif
+    default: return fail(QBLK_EUNSUPPORTED, "gemm: tile configuration not built");
+  }
+  QBLK_TRY(check_launch("gemm_kernel"));
+  if (g.splits > 1) {
+    const int64_t mn = (int64_t)d.M * d.N;
+    const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(mn, 256), 8192);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, st, d, g.splits);
+    QBLK_TRY(check_launch("splitk_reduce_kernel"));
+  }
+  return 0;
 }
 
 template <Prec P, Layout L>
 int dispatch_src(const GemmDesc& d, hipStream_t st) {
   const bool ext = d.ext.kext > 0;
   if (d.b_src == Src::NF4) {
-    if constexpr (L == Layout::TN) {
-      return fail(QBLK_EUNSUPPORTED, "gemm: NF4 operand not supported for TN");
+    if constexpr (L == Layout::TN || P == Prec::F32) {
+      return fail(QBLK_EUNSUPPORTED, "gemm: NF4 operand needs an NT/NN fp16 contraction");
     } else {
       if (d.a_src != Src::F32) return fail(QBLK_EUNSUPPORTED, "gemm: NF4 B needs fp32 A");
       return ext ? launch<P, L, Src::F32, Src::NF4, true>(d, st)
@@ -410,8 +967,8 @@ int dispatch_src(const GemmDesc& d, hipStream_t st) {
     }
   }
   if (ext) {
-    if constexpr (L == Layout::TN) {
-      return fail(QBLK_EUNSUPPORTED, "gemm: K extension not supported for TN");
+    if constexpr (L == Layout::TN || P == Prec::F32) {
+      return fail(QBLK_EUNSUPPORTED, "gemm: K extension needs an NT/NN fp16 contraction");
     } else {
       if (d.a_src != Src::F32 || d.b_src != Src::F32)
         return fail(QBLK_EUNSUPPORTED, "gemm: K extension needs fp32 operands");
@@ -419,25 +976,32 @@ int dispatch_src(const GemmDesc& d, hipStream_t st) {
     }
   }
   if (d.a_src == Src::F32 && d.b_src == Src::F32) return launch<P, L, Src::F32, Src::F32, false>(d, st);
-  if (d.a_src == Src::F16 && d.b_src == Src::F32) return launch<P, L, Src::F16, Src::F32, false>(d, st);
-  if (d.a_src == Src::F32 && d.b_src == Src::F16) return launch<P, L, Src::F32, Src::F16, false>(d, st);
-  if (d.a_src == Src::F16 && d.b_src == Src::F16) return launch<P, L, Src::F16, Src::F16, false>(d, st);
-  return fail(QBLK_EUNSUPPORTED, "gemm: operand source combination");
+  if constexpr (P == Prec::F16) {
+    if (d.a_src == Src::F16 && d.b_src == Src::F32) return launch<P, L, Src::F16, Src::F32, false>(d, st);
+    if (d.a_src == Src::F32 && d.b_src == Src::F16) return launch<P, L, Src::F32, Src::F16, false>(d, st);
+    if (d.a_src == Src::F16 && d.b_src == Src::F16) return launch<P, L, Src::F16, Src::F16, false>(d, st);
+  }
+  return fail(QBLK_EUNSUPPORTED, "gemm: operand storage combination (fp16 storage needs fp16 contraction)");
 }
+
+int elems16(Src s) { return s == Src::F32 ? 4 : 8; }
 
 }  // namespace
 
 int gemm(const GemmDesc& d, hipStream_t st) {
   if (d.M <= 0 || d.N <= 0 || d.K < 0) return fail(QBLK_EINVAL, "gemm: bad shape %d x %d x %d", d.M, d.N, d.K);
   if (d.K == 0 && d.ext.kext == 0) return fail(QBLK_EINVAL, "gemm: empty contraction");
-  // Contiguous dimensions are read 4 elements at a time.
-  const bool a_k = d.layout != Layout::TN;
-  if ((a_k ? d.K : d.M) % 4 != 0) return fail(QBLK_EINVAL, "gemm: A contiguous dim must be a multiple of 4");
-  if ((d.layout == Layout::NT ? d.K : d.N) % 4 != 0)
-    return fail(QBLK_EINVAL, "gemm: B contiguous dim must be a multiple of 4");
+  // Contiguous dimensions and leading dimensions are read in 16-byte chunks.
+  const bool a_rows = d.layout != Layout::TN;
+  const int ea = elems16(d.a_src), eb = elems16(d.b_src);
+  if ((a_rows ? d.K : d.M) % ea != 0 || d.lda % ea != 0)
+    return fail(QBLK_EINVAL, "gemm: A contiguous dim and lda must be multiples of %d", ea);
+  if ((d.layout == Layout::NT ? d.K : d.N) % eb != 0 || d.ldb % eb != 0)
+    return fail(QBLK_EINVAL, "gemm: B contiguous dim and ldb must be multiples of %d", eb);
   if (d.ext.kext % 4 != 0) return fail(QBLK_EINVAL, "gemm: K extension must be a multiple of 4");
+  if (d.ext.kext > (d.prec == Prec::F16 ? 64 : 32))
+    return fail(QBLK_EUNSUPPORTED, "gemm: K extension wider than one K tile");
   if (d.prec == Prec::F32) {
-    if (d.b_src == Src::NF4) return fail(QBLK_EUNSUPPORTED, "gemm: NF4 needs fp16 operands");
     switch (d.layout) {
       case Layout::NT: return dispatch_src<Prec::F32, Layout::NT>(d, st);
       case Layout::NN: return dispatch_src<Prec::F32, Layout::NN>(d, st);
@@ -451,6 +1015,11 @@ int gemm(const GemmDesc& d, hipStream_t st) {
     }
   }
   return fail(QBLK_EINVAL, "gemm: bad layout");
+}
+
+size_t gemm_workspace(const GemmDesc& d) {
+  const Grid g = plan(d, (size_t)-1);
+  return g.splits > 1 ? (size_t)g.splits * d.M * d.N * sizeof(float) : 0;
 }
 
 }  // namespace qblk

@@ -34,7 +34,7 @@ size_t carve_nf4(const qblk_config& c, int r, void* saved, void* scratch, Nf4Sav
                  size_t* scratch_bytes) {
   size_t sb = 0, wb = 0;
   carve_saved(c, saved, s->base, sb);
-  carve_scratch(c, scratch, w->base, wb);
+  carve_scratch(c, scratch, w->base, wb, r);
   const size_t T = (size_t)c.seq * c.batch;
   auto take = [](void* base, size_t& off, size_t n) -> float* {
     off = (off + 255) & ~(size_t)255;
@@ -60,7 +60,7 @@ int check_nf4(const qblk_config* c, const qblk_nf4_block_params* p) {
   QBLK_TRY(check_config(c));
   if (c->gemm_precision != 1) return fail(QBLK_EUNSUPPORTED, "nf4 block: needs gemm_precision = 1");
   if (!p) return fail(QBLK_EINVAL, "nf4 block: params is NULL");
-  if (p->rank <= 0 || p->rank > 32 || p->rank % 4) return fail(QBLK_EINVAL, "nf4 block: rank must be 4..32, multiple of 4");
+  if (p->rank <= 0 || p->rank > 20 || p->rank % 4) return fail(QBLK_EINVAL, "nf4 block: rank must be 4..20, multiple of 4");
   for (int i = 0; i < 7; ++i)
     if (!p->codes[i] || !p->absmax[i] || !p->lora_a[i] || !p->lora_b[i])
       return fail(QBLK_EINVAL, "nf4 block: null pointer for projection %d", i);
@@ -95,8 +95,17 @@ Nf4Seg nf4seg(const qblk_nf4_block_params& p, int i0, int i1, int i2) {
   return n;
 }
 
+// Split-K workspace of the current call (set by the entry points below;
+// calls on one thread are sequential, and the pointer only travels into the
+// GemmDesc of launches issued by that same call).
+thread_local const Scratch* t_ws = nullptr;
+
 GemmDesc base(Layout l, int M, int N, int K) {
   GemmDesc g;
+  if (t_ws) {
+    g.ws = t_ws->gemm_ws;
+    g.ws_bytes = t_ws->gemm_ws_bytes;
+  }
   g.layout = l;
   g.prec = Prec::F16;
   g.M = M; g.N = N; g.K = K;
@@ -219,7 +228,7 @@ using namespace qblk;
 extern "C" int32_t qblk_nf4_block_workspace_size(const qblk_config* cfg, int32_t rank, size_t* saved_bytes,
                                                  size_t* scratch_bytes) {
   QBLK_TRY(check_config(cfg));
-  if (rank <= 0 || rank > 32 || rank % 4) return fail(QBLK_EINVAL, "nf4 block: rank must be 4..32, multiple of 4");
+  if (rank <= 0 || rank > 20 || rank % 4) return fail(QBLK_EINVAL, "nf4 block: rank must be 4..20, multiple of 4");
   Nf4Saved s;
   Nf4Scratch w;
   size_t wb = 0;
@@ -245,6 +254,7 @@ extern "C" int32_t qblk_block_forward_nf4_lora(const qblk_config* cfg, const qbl
   const int T = c.seq * c.batch, h = c.hidden, qd = c.heads * c.head_dim, kvd = c.kv_heads * c.head_dim,
             I = c.intermediate;
   hipStream_t st = (hipStream_t)stream;
+  t_ws = &w.base;
   ProjFwd proj;
   proj.qkv = [&](const float* n1, float* qkv, hipStream_t s_) {
     QBLK_TRY(lora_down(P, T, h, n1, {PQ, PK, PV}, s.h_qkv, s_));
@@ -262,7 +272,9 @@ extern "C" int32_t qblk_block_forward_nf4_lora(const qblk_config* cfg, const qbl
     QBLK_TRY(lora_down(P, T, I, sv, {PD}, s.h_d, s_));
     return nf4_fwd(P, T, I, sv, {PD}, {h}, s.h_d, res, out, s_);
   };
-  return block_forward_impl(c, proj, P.g_in, P.g_post, P.g_q, P.g_k, x, y, s.base, st);
+  const int rc = block_forward_impl(c, proj, P.g_in, P.g_post, P.g_q, P.g_k, x, y, s.base, st);
+  t_ws = nullptr;
+  return rc;
 }
 
 extern "C" int32_t qblk_block_backward_nf4_lora(const qblk_config* cfg, const qblk_nf4_block_params* p,
@@ -285,6 +297,7 @@ extern "C" int32_t qblk_block_backward_nf4_lora(const qblk_config* cfg, const qb
   const int T = c.seq * c.batch, h = c.hidden, qd = c.heads * c.head_dim, kvd = c.kv_heads * c.head_dim,
             I = c.intermediate;
   hipStream_t st = (hipStream_t)stream;
+  t_ws = &w.base;
   ProjBwd proj;
   proj.down = [&](const float* dyv, const float* sv, float* ds, hipStream_t s_) {
     return nf4_bwd(P, G, T, I, dyv, sv, s.h_d, {PD}, {h}, w.dh_d, ds, s_);
@@ -298,6 +311,8 @@ extern "C" int32_t qblk_block_backward_nf4_lora(const qblk_config* cfg, const qb
   proj.qkv = [&](const float* dqkv, const float* n1, float* dn1, hipStream_t s_) {
     return nf4_bwd(P, G, T, h, dqkv, n1, s.h_qkv, {PQ, PK, PV}, {qd, kvd, kvd}, w.dh_qkv, dn1, s_);
   };
-  return block_backward_impl(c, proj, P.g_in, P.g_post, P.g_q, P.g_k, x, dy, s.base, dx, w.sink_h,
-                             w.sink_h + h, w.sink_d, w.sink_d + c.head_dim, w.base, st);
+  const int rc = block_backward_impl(c, proj, P.g_in, P.g_post, P.g_q, P.g_k, x, dy, s.base, dx, w.sink_h,
+                                     w.sink_h + h, w.sink_d, w.sink_d + c.head_dim, w.base, st);
+  t_ws = nullptr;
+  return rc;
 }

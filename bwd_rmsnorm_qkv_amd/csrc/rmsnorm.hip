@@ -151,13 +151,21 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int rows, int n, float
   }
 }
 
-__global__ void colsum_kernel(int parts, int n, const float* __restrict__ partial,
-                              float* __restrict__ out) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= n) return;
+// 64 columns per workgroup, 4 row groups per column (row p goes to group
+// p % 4); the four group sums are added in a fixed order.
+__global__ __launch_bounds__(256) void colsum_kernel(int parts, int n, const float* __restrict__ partial,
+                                                     float* __restrict__ out) {
+  __shared__ float red[4][64];
+  const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + cl;
   float s = 0.f;
-  for (int p = 0; p < parts; ++p) s += partial[(int64_t)p * n + c];
-  out[c] = s;
+  if (c < n) {
+#pragma unroll 8
+    for (int p = rg; p < parts; p += 4) s += partial[(int64_t)p * n + c];
+  }
+  red[rg][cl] = s;
+  __syncthreads();
+  if (rg == 0 && c < n) out[c] = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
 }
 
 int vpl_for(int n) {
@@ -226,7 +234,7 @@ int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* ga
 }
 
 int colsum(int parts, int n, const float* partial, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, parts, n,
+  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)ceil_div(n, 64)), dim3(256), 0, st, parts, n,
                      partial, out);
   return check_launch("colsum_kernel");
 }

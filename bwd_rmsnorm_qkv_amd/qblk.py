@@ -87,7 +87,13 @@ _SIGS = {
                                       C.c_size_t, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                       C.c_void_p], C.c_int32),
     "qblk_gemm": ([C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_int64,
-                   C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p], C.c_int32),
+                   C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_size_t,
+                   C.c_void_p], C.c_int32),
+    "qblk_gemm_workspace_size": ([C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                  C.POINTER(C.c_size_t)], C.c_int32),
+    "qblk_gemm_ex": ([C.c_int32] * 5 + [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_int64, C.c_int32,
+                                        C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p],
+                     C.c_int32),
     "qblk_rmsnorm_workspace_size": ([C.c_int32, C.c_int32, C.POINTER(C.c_size_t)], C.c_int32),
     "qblk_rmsnorm_forward": ([C.c_int32, C.c_int32, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p],
@@ -289,9 +295,18 @@ def block_backward_nf4_lora(cfg, codes, absmax, lora_a, lora_b, gammas, rank, al
 
 # ---------------------------------------------------------- single steps
 
-def gemm(layout, precision, M, N, K, A, lda, B, ldb, Cm, ldc, accumulate=0, stream=None):
-    _check(lib().qblk_gemm(layout, precision, M, N, K, _p(A), lda, _p(B), ldb, _p(Cm), ldc, accumulate,
-                           _stream(stream)))
+def gemm_workspace_size(layout, precision, M, N, K):
+    n = C.c_size_t()
+    _check(lib().qblk_gemm_workspace_size(layout, precision, M, N, K, C.byref(n)))
+    return n.value
+
+
+def gemm(layout, precision, M, N, K, A, lda, B, ldb, Cm, ldc, accumulate=0, scratch=None, stream=None):
+    """fp32 or fp16 operand tensors (the storage type is taken from the tensors)."""
+    nbytes = 0 if scratch is None else scratch.numel() * scratch.element_size()
+    code = lambda t: {torch.float32: 0, torch.float16: 1}[t.dtype]
+    _check(lib().qblk_gemm_ex(layout, precision, M, N, K, _p(A), lda, code(A), _p(B), ldb, code(B), _p(Cm), ldc,
+                              accumulate, _p(scratch), nbytes, _stream(stream)))
 
 
 def rmsnorm_workspace_size(rows, n):

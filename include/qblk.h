@@ -90,8 +90,9 @@ int32_t qblk_block_workspace_size(const qblk_config* cfg, size_t* saved_bytes,
  * attention (query head h reads KV head h / (heads/kv_heads)); a = o W_o^T;
  * r1 = x + a; n2 = RMSNorm(r1; g_post); s = silu(n2 W_gate^T) * (n2 W_up^T);
  * y = r1 + s W_down^T.
- * x, y: [T, hidden] (T = seq*batch). saved/scratch: workspaces of the sizes
- * reported by qblk_block_workspace_size (16-byte aligned). */
+ * x, y: [T, hidden] (T = seq*batch). saved/scratch: workspaces of at least
+ * the sizes reported by qblk_block_workspace_size (16-byte aligned); scratch
+ * is required (the GEMMs keep split-K partial sums there). */
 int32_t qblk_block_forward(const qblk_config* cfg, const qblk_block_params* p, const float* x,
                            float* y, void* saved, size_t saved_bytes, void* scratch,
                            size_t scratch_bytes, qblk_stream_t stream);
@@ -200,7 +201,9 @@ int32_t qblk_nf4_block_workspace_size(const qblk_config* cfg, int32_t rank, size
                                       size_t* scratch_bytes);
 
 /* Forward of the NF4 + LoRA block (same chain as qblk_block_forward).
- * Requires cfg->gemm_precision == 1 and rank a multiple of 4 (<= 32). */
+ * Requires cfg->gemm_precision == 1 and rank in {4, 8, 12, 16, 20} (the
+ * LoRA columns of the fused Q/K/V product, 3 x rank, ride in one 64-wide
+ * K tile). */
 int32_t qblk_block_forward_nf4_lora(const qblk_config* cfg, const qblk_nf4_block_params* p,
                                     const float* x, float* y, void* saved, size_t saved_bytes,
                                     void* scratch, size_t scratch_bytes, qblk_stream_t stream);

@@ -19,10 +19,25 @@ extern "C" {
  * with leading dimensions lda/ldb/ldc (elements). precision 0: fp32
  * contraction; 1: operands rounded to fp16 (nearest even), fp32 accumulate.
  * With accumulate = 1, C += result. The contiguous dimension of each
- * operand must be a multiple of 4. */
+ * operand must be a multiple of 4. `scratch` (optional, may be NULL) lets
+ * a long-K, few-tile product split K over more workgroups; its useful size
+ * comes from qblk_gemm_workspace_size (a smaller one disables the split).
+ * Results do not depend on whether the split is taken beyond fp32
+ * rounding order, and are bitwise reproducible for a given scratch size. */
 int32_t qblk_gemm(int32_t layout, int32_t precision, int32_t M, int32_t N, int32_t K,
                   const float* A, int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
-                  int32_t accumulate, qblk_stream_t stream);
+                  int32_t accumulate, void* scratch, size_t scratch_bytes, qblk_stream_t stream);
+
+int32_t qblk_gemm_workspace_size(int32_t layout, int32_t precision, int32_t M, int32_t N, int32_t K,
+                                 size_t* scratch_bytes);
+
+/* qblk_gemm with the storage type of each operand given: a_dtype/b_dtype
+ * 0 = fp32, 1 = fp16 (IEEE binary16). fp16 storage is how the block keeps
+ * activations that only feed contractions. */
+int32_t qblk_gemm_ex(int32_t layout, int32_t precision, int32_t M, int32_t N, int32_t K, const void* A,
+                     int64_t lda, int32_t a_dtype, const void* B, int64_t ldb, int32_t b_dtype, float* C,
+                     int64_t ldc, int32_t accumulate, void* scratch, size_t scratch_bytes,
+                     qblk_stream_t stream);
 
 /* RMSNorm forward over rows of x [rows, n] ([block] rms_norm_forward):
  * y = x * rho * gamma with rho[r] = (mean x^2 + eps)^(-1/2) written to rho.

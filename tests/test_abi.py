@@ -57,10 +57,10 @@ def test_invalid_arguments_fail_before_device_work():
     lib = qblk.lib()
     # bad layout, null operands, misaligned lda: all rejected on the host
     # (only NULL pointers are passed: nothing here can reach a launch)
-    assert lib.qblk_gemm(5, 0, 4, 4, 4, None, 4, None, 4, None, 4, 0, None) == qblk.QBLK_EINVAL
-    assert lib.qblk_gemm(0, 0, 4, 4, 4, None, 6, None, 4, None, 4, 0, None) == qblk.QBLK_EINVAL
+    assert lib.qblk_gemm(5, 0, 4, 4, 4, None, 4, None, 4, None, 4, 0, None, 0, None) == qblk.QBLK_EINVAL
+    assert lib.qblk_gemm(0, 0, 4, 4, 4, None, 6, None, 4, None, 4, 0, None, 0, None) == qblk.QBLK_EINVAL
     assert b"lda" in lib.qblk_last_error()
-    assert lib.qblk_gemm(0, 0, 4, 4, 4, None, 4, None, 4, None, 4, 0, None) == qblk.QBLK_EINVAL
+    assert lib.qblk_gemm(0, 0, 4, 4, 4, None, 4, None, 4, None, 4, 0, None, 0, None) == qblk.QBLK_EINVAL
     assert b"null" in lib.qblk_last_error()
     assert lib.qblk_nf4_quantize(None, 100, None, None, None) == qblk.QBLK_EINVAL
     assert b"multiple of 64" in lib.qblk_last_error()

@@ -13,7 +13,8 @@ from gpu_util import FP16_TOL, FP32_TOL, announce, check, need_gpu
 pytestmark = pytest.mark.gpu
 
 # (M, N, K): several tiles plus ragged tails in every dimension
-GEMM_SHAPES = [(32, 64, 64), (200, 136, 104), (300, 392, 260), (37, 20, 12)]
+GEMM_SHAPES = [(32, 64, 64), (200, 136, 104), (300, 392, 260), (37, 20, 12),
+               (64, 96, 4096), (520, 264, 3000)]   # long K: split over workgroups
 
 
 @pytest.mark.parametrize("precision", [0, 1])
@@ -34,13 +35,21 @@ def test_gemm(layout, precision, shape):
            (B.astype(np.float64).T if layout == 0 else B.astype(np.float64))
     dA, dB = dev(A), dev(B)
     Cg = torch.full((M, N), 7.0, device="cuda")
-    qblk.gemm(layout, precision, M, N, K, dA, a_shape[1], dB, b_shape[1], Cg, N)
+    ws = qblk.gemm_workspace_size(layout, precision, M, N, K)
+    scratch = byte_buffer(ws) if ws else None
+    qblk.gemm(layout, precision, M, N, K, dA, a_shape[1], dB, b_shape[1], Cg, N, scratch=scratch)
     torch.cuda.synchronize()
     check("C", Cg, Cref, FP16_TOL if precision else FP32_TOL)
     # accumulate mode adds to the existing C
-    qblk.gemm(layout, precision, M, N, K, dA, a_shape[1], dB, b_shape[1], Cg, N, accumulate=1)
+    qblk.gemm(layout, precision, M, N, K, dA, a_shape[1], dB, b_shape[1], Cg, N, accumulate=1, scratch=scratch)
     torch.cuda.synchronize()
     check("C+C", Cg, 2 * Cref, FP16_TOL if precision else FP32_TOL)
+    if ws:
+        # without the workspace the same product runs unsplit
+        C1 = torch.empty((M, N), device="cuda")
+        qblk.gemm(layout, precision, M, N, K, dA, a_shape[1], dB, b_shape[1], C1, N)
+        torch.cuda.synchronize()
+        check("C unsplit", C1, Cref, FP16_TOL if precision else FP32_TOL)
 
 
 @pytest.mark.parametrize("rows,n", [(32, 64), (77, 512), (512, 2560), (5, 4096)])
