@@ -775,37 +775,49 @@ __global__ __launch_bounds__(256) void gemm_nt16_kernel(const GemmDesc d, const 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
+  // Fragments of K-step s+1 are read from LDS while the MFMAs of step s run.
   auto compute = [&](const f16* sa, const f16* sb) {
+    half8 av[2][TM], bv[2][TN];
+    auto frag = [&](int s, half8* a, half8* b) {
+      const int pc = ((2 * s + kh) ^ sw) * 8;
+#pragma unroll
+      for (int t = 0; t < TM; ++t) a[t] = *(const half8*)(sa + (wm * TM * 32 + t * 32 + i) * BK + pc);
+#pragma unroll
+      for (int t = 0; t < TN; ++t) b[t] = *(const half8*)(sb + (wn * TN * 32 + t * 32 + i) * BK + pc);
+    };
+    frag(0, av[0], bv[0]);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-      const int pc = ((2 * s + kh) ^ sw) * 8;
-      half8 av[TM], bv[TN];
-#pragma unroll
-      for (int t = 0; t < TM; ++t) av[t] = *(const half8*)(sa + (wm * TM * 32 + t * 32 + i) * BK + pc);
-#pragma unroll
-      for (int t = 0; t < TN; ++t) bv[t] = *(const half8*)(sb + (wn * TN * 32 + t * 32 + i) * BK + pc);
+      if (s + 1 < BK / 16) frag(s + 1, av[(s + 1) & 1], bv[(s + 1) & 1]);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[s & 1][tm], bv[s & 1][tn], acc[tm][tn], 0, 0, 0);
     }
   };
 
   // Each half-step: own DMAs of the current stage done (s_waitcnt), barrier
   // (everyone's are), start the next stage's DMA into the other buffer (its
-  // previous readers have all passed the barrier), then the MFMAs.
+  // previous readers have all passed the barrier), then the MFMAs. Tiles go
+  // in pairs so the loop body has one straight path; an odd last tile
+  // follows the loop.
   if (nkt > 0) issue(kb, sA0, sB0);
-  for (int kt = 0; kt < nkt; kt += 2) {
+  int kt = 0;
+  for (; kt + 1 < nkt; kt += 2) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 1 < nkt) issue(kb + (kt + 1) * BK, sA1, sB1);
+    issue(kb + (kt + 1) * BK, sA1, sB1);
     compute(sA0, sB0);
-    if (kt + 1 >= nkt) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (kt + 2 < nkt) issue(kb + (kt + 2) * BK, sA0, sB0);
     compute(sA1, sB1);
+  }
+  if (kt < nkt) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    compute(sA0, sB0);
   }
 
   const int ii = lane & 31;
@@ -889,12 +901,10 @@ Cfg cfg_for(const GemmDesc& d) {
 #endif
 }
 
-Grid plan(const GemmDesc& d, size_t ws_bytes) {
-  const Cfg c = cfg_for(d);
-  const int bk = PT<Prec::F16>::BK / (d.prec == Prec::F16 ? 1 : 2) / (c.bk_big ? 1 : 2);
+Grid plan_tiles(const GemmDesc& d, size_t ws_bytes, int bm, int bn, int bk) {
   Grid g;
-  g.tiles_m = (int)ceil_div(d.M, c.bm);
-  g.tiles_n = (int)ceil_div(d.N, c.bn);
+  g.tiles_m = (int)ceil_div(d.M, bm);
+  g.tiles_n = (int)ceil_div(d.N, bn);
   const int tiles = g.tiles_m * g.tiles_n;
   const int nkt = (int)ceil_div(d.K, bk);
   int splits = (int)ceil_div(kTargetWgs, tiles);
@@ -907,6 +917,49 @@ Grid plan(const GemmDesc& d, size_t ws_bytes) {
   g.splits = splits;
   g.kchunk = kt_per * bk;
   return g;
+}
+
+// The fp16 NT DMA kernel applies when both operands are fp16 in storage,
+// K-contiguous with 16-byte aligned rows, K is a whole number of 64-wide
+// tiles and nothing extends the contraction.
+bool nt16_ok(const GemmDesc& d) {
+#ifdef QBLK_NO_NT16
+  (void)d;
+  return false;
+#else
+  if (d.layout != Layout::NT || d.prec != Prec::F16) return false;
+  if (d.a_src != Src::F16 || d.b_src != Src::F16 || d.ext.kext > 0) return false;
+  if (d.K % 64 != 0 || d.lda % 8 != 0 || d.ldb % 8 != 0) return false;
+  if ((uintptr_t)d.a % 16 != 0) return false;
+  for (int s = 0; s < d.b.nseg; ++s)
+    if ((uintptr_t)d.b.p[s] % 16 != 0) return false;
+  return true;
+#endif
+}
+
+Grid plan(const GemmDesc& d, size_t ws_bytes) {
+  if (nt16_ok(d)) return plan_tiles(d, ws_bytes, 128, 128, 64);
+  const Cfg c = cfg_for(d);
+  const int bk = PT<Prec::F16>::BK / (d.prec == Prec::F16 ? 1 : 2) / (c.bk_big ? 1 : 2);
+  return plan_tiles(d, ws_bytes, c.bm, c.bn, bk);
+}
+
+int finish_splits(const GemmDesc& d, const Grid& g, hipStream_t st) {
+  if (g.splits > 1) {
+    const int64_t mn = (int64_t)d.M * d.N;
+    const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(mn, 256), 8192);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, st, d, g.splits);
+    QBLK_TRY(check_launch("splitk_reduce_kernel"));
+  }
+  return 0;
+}
+
+int launch_nt16(const GemmDesc& d, hipStream_t st) {
+  const Grid g = plan(d, d.ws ? d.ws_bytes : 0);
+  const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
+  hipLaunchKernelGGL((gemm_nt16_kernel<2, 2>), dim3(nwg), dim3(256), 0, st, d, g);
+  QBLK_TRY(check_launch("gemm_nt16_kernel"));
+  return finish_splits(d, g, st);
 }
 
 template <Prec P, Layout L, Src AS, Src BS, bool EXT, int WM, int WN, int TM, int TN, bool BIG>
@@ -945,13 +998,7 @@ int launch(const GemmDesc& d, hipStream_t st) {
     default: return fail(QBLK_EUNSUPPORTED, "gemm: tile configuration not built");
   }
   QBLK_TRY(check_launch("gemm_kernel"));
-  if (g.splits > 1) {
-    const int64_t mn = (int64_t)d.M * d.N;
-    const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(mn, 256), 8192);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, st, d, g.splits);
-    QBLK_TRY(check_launch("splitk_reduce_kernel"));
-  }
-  return 0;
+  return finish_splits(d, g, st);
 }
 
 template <Prec P, Layout L>
@@ -979,7 +1026,10 @@ int dispatch_src(const GemmDesc& d, hipStream_t st) {
   if constexpr (P == Prec::F16) {
     if (d.a_src == Src::F16 && d.b_src == Src::F32) return launch<P, L, Src::F16, Src::F32, false>(d, st);
     if (d.a_src == Src::F32 && d.b_src == Src::F16) return launch<P, L, Src::F32, Src::F16, false>(d, st);
-    if (d.a_src == Src::F16 && d.b_src == Src::F16) return launch<P, L, Src::F16, Src::F16, false>(d, st);
+    if (d.a_src == Src::F16 && d.b_src == Src::F16) {
+      if (nt16_ok(d)) return launch_nt16(d, st);
+      return launch<P, L, Src::F16, Src::F16, false>(d, st);
+    }
   }
   return fail(QBLK_EUNSUPPORTED, "gemm: operand storage combination (fp16 storage needs fp16 contraction)");
 }

@@ -52,6 +52,49 @@ def test_gemm(layout, precision, shape):
         check("C unsplit", C1, Cref, FP16_TOL if precision else FP32_TOL)
 
 
+# fp16-stored operands: K a multiple of 64 takes the NT direct-to-LDS kernel,
+# the others the general one
+GEMM16_SHAPES = [(200, 136, 128), (37, 24, 64), (300, 392, 256), (130, 130, 192),
+                 (64, 96, 4096), (520, 264, 3008), (520, 264, 3000), (72, 40, 104)]
+
+
+@pytest.mark.parametrize("storage", ["h16", "f32h16", "h16f32"])
+@pytest.mark.parametrize("layout", [0, 1, 2])
+@pytest.mark.parametrize("shape", GEMM16_SHAPES)
+def test_gemm_fp16_storage(layout, storage, shape):
+    """Operands held as IEEE half. Both sides contract the same fp16 values
+    (fp32 operands are rounded to nearest even), so the only difference is
+    fp32 accumulation order: the fp32 tolerance applies."""
+    need_gpu()
+    M, N, K = shape
+    announce(f"gemm16 layout={layout} storage={storage} M={M} N={N} K={K}")
+    a_cont = K if layout in (0, 1) else M
+    b_cont = K if layout == 0 else N
+    if (storage != "f32h16" and a_cont % 8) or (storage != "h16f32" and b_cont % 8) or a_cont % 4 or b_cont % 4:
+        pytest.skip("fp16 operands need their contiguous dimension a multiple of 8")
+    rng = np.random.default_rng(M * 5 + N * 11 + K)
+    a_shape = (M, K) if layout in (0, 1) else (K, M)
+    b_shape = (N, K) if layout == 0 else (K, N)
+    A = rng.standard_normal(a_shape).astype(np.float32)
+    B = rng.standard_normal(b_shape).astype(np.float32)
+    A16 = A.astype(np.float16)
+    B16 = B.astype(np.float16)
+    a64 = A16.astype(np.float64)
+    b64 = B16.astype(np.float64)
+    Cref = (a64 if layout != 2 else a64.T) @ (b64.T if layout == 0 else b64)
+    dA = dev(A16) if storage in ("h16", "h16f32") else dev(A)
+    dB = dev(B16) if storage in ("h16", "f32h16") else dev(B)
+    ws = qblk.gemm_workspace_size(layout, 1, M, N, K)
+    scratch = byte_buffer(ws) if ws else None
+    Cg = torch.full((M, N), 3.0, device="cuda")
+    qblk.gemm(layout, 1, M, N, K, dA, a_shape[1], dB, b_shape[1], Cg, N, scratch=scratch)
+    torch.cuda.synchronize()
+    check("C", Cg, Cref, FP32_TOL)
+    qblk.gemm(layout, 1, M, N, K, dA, a_shape[1], dB, b_shape[1], Cg, N, accumulate=1, scratch=scratch)
+    torch.cuda.synchronize()
+    check("C+C", Cg, 2 * Cref, FP32_TOL)
+
+
 @pytest.mark.parametrize("rows,n", [(32, 64), (77, 512), (512, 2560), (5, 4096)])
 def test_rmsnorm(rows, n):
     need_gpu()
