@@ -41,7 +41,29 @@ static int check_params(const qblk_block_params* p) {
                         p->g_in, p->g_post, p->g_q, p->g_k};
   for (const void* q : ptrs)
     if (!q || !aligned16(q)) return fail(QBLK_EINVAL, "params: null or misaligned (16 B) pointer");
+  if (p->w16 && !aligned16(p->w16)) return fail(QBLK_EINVAL, "params: misaligned (16 B) w16");
   return QBLK_OK;
+}
+
+int32_t qblk_block_pack_f16_size(const qblk_config* cfg, size_t* bytes) {
+  QBLK_TRY(check_config(cfg));
+  if (!bytes) return fail(QBLK_EINVAL, "block_pack_f16_size: bytes is NULL");
+  Packed16 pk;
+  carve_pack16(*cfg, nullptr, pk, *bytes);
+  return QBLK_OK;
+}
+
+int32_t qblk_block_pack_f16(const qblk_config* cfg, const qblk_block_params* p, void* packed,
+                            size_t packed_bytes, qblk_stream_t stream) {
+  QBLK_TRY(check_config(cfg));
+  QBLK_TRY(check_params(p));
+  if (!packed || !aligned16(packed)) return fail(QBLK_EINVAL, "block_pack_f16: null or misaligned buffer");
+  Packed16 pk;
+  size_t need = 0;
+  carve_pack16(*cfg, nullptr, pk, need);
+  if (packed_bytes < need) return fail(QBLK_EINVAL, "block_pack_f16: buffer %zu < %zu", packed_bytes, need);
+  carve_pack16(*cfg, packed, pk, need);
+  return pack16(*cfg, *p, pk, true, true, S(stream));
 }
 
 int32_t qblk_block_forward(const qblk_config* cfg, const qblk_block_params* p, const float* x, float* y,

@@ -27,6 +27,19 @@ struct Saved {
   float* s;        // [T, I] SwiGLU output
 };
 
+// fp16 copies of the dense block's projection weights, as every fp16
+// contraction reads them: W [out, in] for the forward (x W^T) and W^T
+// [in, out] for dX = dY W. [Wq; Wk; Wv] and [Wg; Wu] are stored stacked.
+struct Packed16 {
+  f16 *qkv, *o, *gu, *d;      // [qkv, h], [h, qd], [2I, h], [h, I]
+  f16 *qkvT, *oT, *guT, *dT;  // [h, qkv], [qd, h], [h, 2I], [I, h]
+};
+void carve_pack16(const qblk_config& c, void* base, Packed16& p, size_t& bytes);
+// Casts (round to nearest even) the weights of p into `out`: the forward
+// copies when fwd, the transposed ones when bwd.
+int pack16(const qblk_config& c, const qblk_block_params& p, const Packed16& out, bool fwd, bool bwd,
+           hipStream_t st);
+
 // Backward temporaries (caller-owned `scratch`).
 struct Scratch {
   float *ds, *dgu, *dn2, *dr1, *d_o, *dqr, *dkr, *dqkv, *dn1;
@@ -34,10 +47,15 @@ struct Scratch {
   float* red;
   float* gemm_ws;  // split-K partial sums of the block's GEMMs
   size_t gemm_ws_bytes;
+  // fp16-operand dense block only: operand copies and, when the caller
+  // passes no packed weights, the weights' fp16 copies.
+  f16 *a16, *aT16, *bT16;
+  Packed16 pack;
 };
 
 void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes);
-// lora_rank > 0 also sizes the GEMM workspace for the NF4 + LoRA GEMMs.
+// lora_rank > 0 (the NF4 block) sizes the GEMM workspace for the NF4 +
+// LoRA GEMMs and leaves out the dense fp16 buffers.
 void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes, int lora_rank = 0);
 int check_config(const qblk_config* c);
 

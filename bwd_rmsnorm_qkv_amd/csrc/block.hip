@@ -17,6 +17,7 @@
 #include "gemm.h"
 #include "norms.h"
 
+#include <algorithm>
 #include <vector>
 
 namespace qblk {
@@ -109,7 +110,53 @@ void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes, 
   s.red = cv.take<float>(red / sizeof(float) + 1);
   s.gemm_ws_bytes = block_gemm_ws(c, lora_rank);
   s.gemm_ws = cv.take<float>(s.gemm_ws_bytes / sizeof(float) + 1);
+  s.a16 = s.aT16 = s.bT16 = nullptr;
+  s.pack = Packed16{};
+  if (c.gemm_precision == 1 && lora_rank == 0) {
+    const size_t wide = std::max({qd + 2 * kvd, 2 * I, h, qd});
+    s.a16 = cv.take<f16>(T * wide);
+    s.aT16 = cv.take<f16>(T * wide);
+    s.bT16 = cv.take<f16>(T * std::max({h, I, qd}));
+    size_t pb = 0;
+    carve_pack16(c, nullptr, s.pack, pb);
+    char* pbase = cv.take<char>(pb);
+    carve_pack16(c, pbase, s.pack, pb);
+  }
   bytes = cv.off;
+}
+
+void carve_pack16(const qblk_config& c, void* base, Packed16& p, size_t& bytes) {
+  const size_t h = c.hidden, d = c.head_dim;
+  const size_t qd = (size_t)c.heads * d, kvd = (size_t)c.kv_heads * d, I = c.intermediate;
+  const size_t qkv = qd + 2 * kvd;
+  Carver cv(base);
+  p.qkv = cv.take<f16>(qkv * h);
+  p.o = cv.take<f16>(h * qd);
+  p.gu = cv.take<f16>(2 * I * h);
+  p.d = cv.take<f16>(h * I);
+  p.qkvT = cv.take<f16>(h * qkv);
+  p.oT = cv.take<f16>(qd * h);
+  p.guT = cv.take<f16>(h * 2 * I);
+  p.dT = cv.take<f16>(I * h);
+  bytes = cv.off;
+}
+
+int pack16(const qblk_config& c, const qblk_block_params& p, const Packed16& o, bool fwd, bool bwd,
+           hipStream_t st) {
+  const int h = c.hidden, d = c.head_dim;
+  const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
+  const int qkv = qd + 2 * kvd;
+  auto one = [&](int rows, int cols, const float* w, f16* out, f16* outT, int ldt) {
+    return cast_f16(rows, cols, w, cols, fwd ? out : nullptr, cols, bwd ? outT : nullptr, ldt, st);
+  };
+  QBLK_TRY(one(qd, h, p.w_q, o.qkv, o.qkvT, qkv));
+  QBLK_TRY(one(kvd, h, p.w_k, o.qkv + (size_t)qd * h, o.qkvT + qd, qkv));
+  QBLK_TRY(one(kvd, h, p.w_v, o.qkv + (size_t)(qd + kvd) * h, o.qkvT + qd + kvd, qkv));
+  QBLK_TRY(one(h, qd, p.w_o, o.o, o.oT, h));
+  QBLK_TRY(one(I, h, p.w_gate, o.gu, o.guT, 2 * I));
+  QBLK_TRY(one(I, h, p.w_up, o.gu + (size_t)I * h, o.guT + I, 2 * I));
+  QBLK_TRY(one(h, I, p.w_down, o.d, o.dT, h));
+  return QBLK_OK;
 }
 
 int check_config(const qblk_config* c) {
@@ -228,12 +275,107 @@ Seg seg3(const void* a, int na, const void* b, int nb, const void* cc, int nc) {
   return s;
 }
 
+// Both operands fp16 and K-contiguous (the layout the direct-to-LDS GEMM
+// kernel takes); `b` is a stacked fp16 weight or activation copy.
+GemmDesc nt16(const Scratch& w, int M, int N, int K, const f16* a, int64_t lda, const f16* b, int64_t ldb,
+              Seg c, int64_t ldc) {
+  GemmDesc g;
+  g.ws = w.gemm_ws;
+  g.ws_bytes = w.gemm_ws_bytes;
+  g.layout = Layout::NT;
+  g.prec = Prec::F16;
+  g.M = M; g.N = N; g.K = K;
+  g.a = a; g.lda = lda; g.a_src = Src::F16;
+  g.b = seg1(b, N); g.ldb = ldb; g.b_src = Src::F16;
+  g.c = c; g.ldc = ldc;
+  return g;
+}
+
+// The fp16 copies path needs fp16 leading dimensions (T for the transposed
+// activations) that are multiples of 8.
+bool use_f16_copies(const qblk_config& c) {
+  return c.gemm_precision == 1 && (c.seq * c.batch) % 8 == 0;
+}
+
+// The weights' fp16 copies: the caller's packed set, or cast into scratch.
+int weights16(const qblk_config& c, const qblk_block_params& p, const Scratch& w, bool fwd, Packed16& W,
+              hipStream_t st) {
+  if (p.w16) {
+    size_t b = 0;
+    carve_pack16(c, (void*)p.w16, W, b);
+    return QBLK_OK;
+  }
+  W = w.pack;
+  return pack16(c, p, W, fwd, !fwd, st);
+}
+
+int dense16_forward(const qblk_config& c, const qblk_block_params& p, const float* x, float* y, const Saved& s,
+                    const Scratch& w, hipStream_t st) {
+  const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
+  const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate, qkv = qd + 2 * kvd;
+  Packed16 W;
+  QBLK_TRY(weights16(c, p, w, true, W, st));
+  // y_out (+ res) = act W^T with act cast to fp16 first.
+  auto proj = [&](const float* act, int n_in, const f16* wt, int n_out, const float* res, float* out,
+                  hipStream_t s_) -> int {
+    QBLK_TRY(cast_f16(T, n_in, act, n_in, w.a16, n_in, nullptr, 0, s_));
+    GemmDesc g = nt16(w, T, n_out, n_in, w.a16, n_in, wt, n_in, seg1(out, T), n_out);
+    g.r = res; g.ldr = n_out;
+    return gemm(g, s_);
+  };
+  ProjFwd pf;
+  pf.qkv = [&](const float* n1, float* out, hipStream_t s_) { return proj(n1, h, W.qkv, qkv, nullptr, out, s_); };
+  pf.o = [&](const float* o, const float* res, float* out, hipStream_t s_) {
+    return proj(o, qd, W.o, h, res, out, s_);
+  };
+  pf.gate_up = [&](const float* n2, float* out, hipStream_t s_) { return proj(n2, h, W.gu, 2 * I, nullptr, out, s_); };
+  pf.down = [&](const float* sv, const float* res, float* out, hipStream_t s_) {
+    return proj(sv, I, W.d, h, res, out, s_);
+  };
+  return block_forward_impl(c, pf, p.g_in, p.g_post, p.g_q, p.g_k, x, y, s, st);
+}
+
+int dense16_backward(const qblk_config& c, const qblk_block_params& p, const qblk_block_grads& gr,
+                     const float* x, const float* dy, const Saved& s, float* dx, const Scratch& w,
+                     hipStream_t st) {
+  const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
+  const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate, qkv = qd + 2 * kvd;
+  Packed16 W;
+  QBLK_TRY(weights16(c, p, w, false, W, st));
+  // dX = dY W as dY [T, n_out] times (W^T [n_in, n_out])^T, and
+  // dW = dY^T X as (dY^T [n_out, T]) times (X^T [n_in, T])^T: both NT with
+  // fp16 copies made here.
+  auto dxdw = [&](const float* dyv, int n_out, const float* xin, int n_in, const f16* wT, Seg cseg, float* dxo,
+                  hipStream_t s_) -> int {
+    QBLK_TRY(cast_f16(T, n_out, dyv, n_out, w.a16, n_out, w.aT16, T, s_));
+    QBLK_TRY(cast_f16(T, n_in, xin, n_in, nullptr, 0, w.bT16, T, s_));
+    QBLK_TRY(gemm(nt16(w, T, n_in, n_out, w.a16, n_out, wT, n_out, seg1(dxo, T), n_in), s_));
+    return gemm(nt16(w, n_out, n_in, T, w.aT16, T, w.bT16, T, cseg, n_in), s_);
+  };
+  ProjBwd pb;
+  pb.down = [&](const float* dyv, const float* sv, float* ds, hipStream_t s_) {
+    return dxdw(dyv, h, sv, I, W.dT, seg1(gr.w_down, h), ds, s_);
+  };
+  pb.gate_up = [&](const float* dgu, const float* n2, float* dn2, hipStream_t s_) {
+    return dxdw(dgu, 2 * I, n2, h, W.guT, seg3(gr.w_gate, I, gr.w_up, I, nullptr, 0), dn2, s_);
+  };
+  pb.o = [&](const float* dr1, const float* o, float* d_o, hipStream_t s_) {
+    return dxdw(dr1, h, o, qd, W.oT, seg1(gr.w_o, h), d_o, s_);
+  };
+  pb.qkv = [&](const float* dqkv, const float* n1, float* dn1, hipStream_t s_) {
+    return dxdw(dqkv, qkv, n1, h, W.qkvT, seg3(gr.w_q, qd, gr.w_k, kvd, gr.w_v, kvd), dn1, s_);
+  };
+  return block_backward_impl(c, pb, p.g_in, p.g_post, p.g_q, p.g_k, x, dy, s, dx, gr.g_in, gr.g_post,
+                             gr.g_q, gr.g_k, w, st);
+}
+
 }  // namespace
 
 int dense_block_forward(const qblk_config& c, const qblk_block_params& p, const float* x, float* y,
                         const Saved& s, const Scratch& w, hipStream_t st) {
   const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
+  if (use_f16_copies(c)) return dense16_forward(c, p, x, y, s, w, st);
   ProjFwd proj;
   proj.qkv = [&](const float* n1, float* qkv, hipStream_t s_) {
     return gemm(nt(c, w, T, qd + 2 * kvd, h, n1, h, seg3(p.w_q, qd, p.w_k, kvd, p.w_v, kvd), h, qkv, qd + 2 * kvd),
@@ -262,6 +404,7 @@ int dense_block_backward(const qblk_config& c, const qblk_block_params& p, const
   const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
   const Prec pr = prec_of(c);
+  if (use_f16_copies(c)) return dense16_backward(c, p, gr, x, dy, s, dx, w, st);
   // dX = dY W (NN, B = W [out, in] with out the contraction) and
   // dW = dY^T X (TN). `wseg` are the weights stacked along out; `cseg` the
   // gradient tensors split the same way.

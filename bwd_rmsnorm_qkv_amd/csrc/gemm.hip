@@ -32,6 +32,8 @@
 // the same XCD at the same time (one L2 per XCD).
 #include "gemm.h"
 
+#include <type_traits>
+
 #include "../../include/qblk.h"
 
 namespace qblk {
@@ -705,28 +707,46 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmDesc d, con
 //
 // C = A B^T with A [M, K] and B [N, K] both fp16, K-contiguous, K a multiple
 // of 64. Tiles move global -> LDS with global_load_lds_dwordx4 (16 bytes per
-// lane straight into LDS, no registers, no conversion), into two static LDS
-// stages so the copy of tile t+1 overlaps the MFMAs of tile t. An LDS row is
-// 64 halves (128 bytes) with no padding; its eight 16-byte chunks are stored
-// XOR-swizzled (physical chunk = logical chunk ^ (row & 7)) so that the MFMA
-// reads of 8 consecutive rows at one logical chunk hit 8 different bank
-// groups. Rows past M (or N) load a clamped, valid row; those results are
-// never stored.
+// lane straight into LDS: no registers, no conversion) into a ring of NS
+// LDS stages, so the copies of the next NS-1 K tiles overlap the MFMAs of
+// the current one. An LDS row is 64 halves (128 bytes) with no padding, so
+// two rows span the 64 four-byte banks; the eight 16-byte chunks of a row
+// are stored XOR-swizzled (physical chunk = logical chunk ^ ((row >> 1) & 7))
+// so that the MFMA reads of 16 consecutive rows at one logical chunk (one
+// 256-byte LDS cycle of ds_read_b128) hit 16 different bank groups. Rows
+// past M (or N) load a clamped, valid row; those results are never stored.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-template <int TM, int TN>
-__global__ __launch_bounds__(256) void gemm_nt16_kernel(const GemmDesc d, const Grid gd) {
+// One LDS stage as its own __shared__ object: stages are distinct objects,
+// so the compiler knows a copy into one cannot alias reads of another and
+// adds no wait of its own between them.
+template <int TAG, int ELEMS>
+__device__ __forceinline__ f16* lds_stage() {
+  __shared__ __attribute__((aligned(16))) f16 buf[ELEMS];
+  return buf;
+}
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM, int BN, int WM, int WN, int NS>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_nt16_kernel(const GemmDesc d, const Grid gd) {
   constexpr int BK = 64;
-  constexpr int BM = 2 * TM * 32, BN = 2 * TN * 32;
-  constexpr int JA = BM / 32, JB = BN / 32;  // DMA instructions per thread per tile
-  __shared__ __attribute__((aligned(16))) f16 sA0[BM * BK];
-  __shared__ __attribute__((aligned(16))) f16 sA1[BM * BK];
-  __shared__ __attribute__((aligned(16))) f16 sB0[BN * BK];
-  __shared__ __attribute__((aligned(16))) f16 sB1[BN * BK];
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "tile");
+  constexpr int JA = BM / 8 / NW, JB = BN / 8 / NW;  // DMA instructions per wave per stage
+  static_assert(JA * 8 * NW == BM && JB * 8 * NW == BN, "DMA split");
+  constexpr int JS = JA + JB;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w % 2, wn = w / 2;
+  const int wm = w % WM, wn = w / WM;
 
   const int total = gd.tiles_m * gd.tiles_n * gd.splits;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
@@ -740,33 +760,37 @@ __global__ __launch_bounds__(256) void gemm_nt16_kernel(const GemmDesc d, const 
   const int ke = min(d.K, kb + gd.kchunk);
   const int nkt = ke > kb ? (ke - kb) / BK : 0;
 
-  // DMA instruction j of wave w fills rows 32 j + 8 w .. +7 of the tile;
-  // lane l writes physical chunk l & 7 of row l >> 3, i.e. logical chunk
-  // (l & 7) ^ (l >> 3).
-  const int rsub = lane >> 3, lch = (lane & 7) ^ rsub;
+  // DMA instruction j of wave w fills tile rows 8 blk .. 8 blk + 7 with
+  // blk = NW j + w; lane l writes physical chunk l & 7 of row 8 blk + (l >> 3),
+  // which holds logical chunk (l & 7) ^ (((blk & 1) << 2) | (l >> 4)).
+  const int rsub = lane >> 3;
+  auto lchunk = [&](int blk) { return (lane & 7) ^ (((blk & 1) << 2) | (rsub >> 1)); };
   const f16* pa[JA];
   const f16* pb[JB];
 #pragma unroll
   for (int j = 0; j < JA; ++j) {
-    const int r = min(m0 + 32 * j + 8 * w + rsub, d.M - 1);
-    pa[j] = (const f16*)d.a + (int64_t)r * d.lda + lch * 8;
+    const int blk = NW * j + w;
+    const int r = min(m0 + 8 * blk + rsub, d.M - 1);
+    pa[j] = (const f16*)d.a + (int64_t)r * d.lda + kb + lchunk(blk) * 8;
   }
 #pragma unroll
   for (int j = 0; j < JB; ++j) {
-    const int n = min(n0 + 32 * j + 8 * w + rsub, d.N - 1);
+    const int blk = NW * j + w;
+    const int n = min(n0 + 8 * blk + rsub, d.N - 1);
     const int sg = seg_of(d.b, n);
-    pb[j] = (const f16*)d.b.p[sg] + (int64_t)(n - d.b.start[sg]) * d.ldb + lch * 8;
+    pb[j] = (const f16*)d.b.p[sg] + (int64_t)(n - d.b.start[sg]) * d.ldb + kb + lchunk(blk) * 8;
   }
-  auto issue = [&](int k0, f16* sa, f16* sb) {
+  auto issue = [&](int kt, f16* sa, f16* sb) {
+    const int k0 = kt * BK;
 #pragma unroll
     for (int j = 0; j < JA; ++j)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(pa[j] + k0), (lds_void_t*)(sa + (32 * j + 8 * w) * BK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(pa[j] + k0), (lds_void_t*)(sa + 8 * (NW * j + w) * BK), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < JB; ++j)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(pb[j] + k0), (lds_void_t*)(sb + (32 * j + 8 * w) * BK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(pb[j] + k0), (lds_void_t*)(sb + 8 * (NW * j + w) * BK), 16, 0, 0);
   };
 
-  const int i = lane & 31, kh = lane >> 5, sw = i & 7;
+  const int i = lane & 31, kh = lane >> 5, sw = (i >> 1) & 7;
   floatx16 acc[TM][TN];
 #pragma unroll
   for (int a = 0; a < TM; ++a)
@@ -775,7 +799,12 @@ __global__ __launch_bounds__(256) void gemm_nt16_kernel(const GemmDesc d, const 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  // Fragments of K-step s+1 are read from LDS while the MFMAs of step s run.
+#ifndef QBLK_NT16_PIPE
+#define QBLK_NT16_PIPE 1
+#endif
+  // The fragments of K step s+1 are read from LDS while the MFMAs of step s
+  // run; sched_group_barrier pins that interleave (left alone, the
+  // scheduler reads each step's fragments right before its MFMAs and waits).
   auto compute = [&](const f16* sa, const f16* sb) {
     half8 av[2][TM], bv[2][TN];
     auto frag = [&](int s, half8* a, half8* b) {
@@ -794,31 +823,63 @@ __global__ __launch_bounds__(256) void gemm_nt16_kernel(const GemmDesc d, const 
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[s & 1][tm], bv[s & 1][tn], acc[tm][tn], 0, 0, 0);
+#if QBLK_NT16_PIPE
+      if (s + 1 < BK / 16) {
+        // reads of step s+1 spread between the MFMAs of step s
+#pragma unroll
+        for (int q = 0; q < TM + TN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        if constexpr (TM * TN > TM + TN) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - TM - TN, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+      }
+#endif
     }
   };
 
-  // Each half-step: own DMAs of the current stage done (s_waitcnt), barrier
-  // (everyone's are), start the next stage's DMA into the other buffer (its
-  // previous readers have all passed the barrier), then the MFMAs. Tiles go
-  // in pairs so the loop body has one straight path; an odd last tile
-  // follows the loop.
-  if (nkt > 0) issue(kb, sA0, sB0);
-  int kt = 0;
-  for (; kt + 1 < nkt; kt += 2) {
-    __builtin_amdgcn_s_waitcnt(0);
+  auto stA = [](auto S) { return lds_stage<2 * decltype(S)::value, BM * BK>(); };
+  auto stB = [](auto S) { return lds_stage<2 * decltype(S)::value + 1, BN * BK>(); };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  // Prologue: tiles 0 .. NS-2 in flight.
+  if (0 < nkt) issue(0, stA(I0{}), stB(I0{}));
+  if constexpr (NS > 2) if (1 < nkt) issue(1, stA(I1{}), stB(I1{}));
+  if constexpr (NS > 3) if (2 < nkt) issue(2, stA(I2{}), stB(I2{}));
+
+  // Step kt: wait for this wave's copies of tile kt (tiles kt+1 .. kt+NS-2
+  // may stay in flight), barrier (every wave's copies of tile kt landed and
+  // every wave is done with tile kt-1), refill the stage of tile kt-1 with
+  // tile kt+NS-1, then the MFMAs of tile kt.
+  auto step = [&](auto S, int kt) {
+    constexpr int s = decltype(S)::value;
+    if (kt + NS - 2 < nkt) wait_vmcnt<JS * (NS - 2)>();
+    else wait_vmcnt<0>();
     __syncthreads();
-    issue(kb + (kt + 1) * BK, sA1, sB1);
-    compute(sA0, sB0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (kt + 2 < nkt) issue(kb + (kt + 2) * BK, sA0, sB0);
-    compute(sA1, sB1);
+    if (kt + NS - 1 < nkt)
+      issue(kt + NS - 1, stA(std::integral_constant<int, (s + NS - 1) % NS>{}),
+            stB(std::integral_constant<int, (s + NS - 1) % NS>{}));
+    compute(stA(S), stB(S));
+  };
+  // Whole rounds of NS tiles run without branches around the MFMAs (a
+  // conditional step inside the loop makes the compiler copy every
+  // accumulator out of and back into AGPRs each iteration); the last
+  // nkt % NS tiles follow.
+  const int nfull = nkt / NS * NS;
+  for (int kt = 0; kt < nfull; kt += NS) {
+    step(I0{}, kt);
+    step(I1{}, kt + 1);
+    if constexpr (NS > 2) step(I2{}, kt + 2);
+    if constexpr (NS > 3) step(I3{}, kt + 3);
   }
-  if (kt < nkt) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    compute(sA0, sB0);
-  }
+  const int left = nkt - nfull;
+  if (left > 0) step(I0{}, nfull);
+  if constexpr (NS > 2) if (left > 1) step(I1{}, nfull + 1);
+  if constexpr (NS > 3) if (left > 2) step(I2{}, nfull + 2);
 
   const int ii = lane & 31;
   if (gd.splits > 1) {
@@ -919,6 +980,29 @@ Grid plan_tiles(const GemmDesc& d, size_t ws_bytes, int bm, int bn, int bk) {
   return g;
 }
 
+template <int BM, int BN, int WM, int WN, int NS>
+struct Nt16Cfg {
+  static constexpr int bm = BM, bn = BN, threads = WM * WN * 64;
+  static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
+    const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
+    hipLaunchKernelGGL((gemm_nt16_kernel<BM, BN, WM, WN, NS>), dim3(nwg), dim3(threads), 0, st, d, g);
+  }
+};
+#ifdef QBLK_NT16_CFG  // one forced configuration (tuning builds)
+using Nt16Small = Nt16Cfg<QBLK_NT16_CFG>;
+using Nt16Big = Nt16Small;
+#else
+// 128 x 128 tiles, 4 waves, two workgroups per CU (64 KB LDS each); and
+// 256 x 256 tiles, 8 waves of 64 x 128, one workgroup per CU (128 KB LDS).
+using Nt16Small = Nt16Cfg<128, 128, 2, 2, 2>;
+using Nt16Big = Nt16Cfg<256, 256, 4, 2, 2>;
+#endif
+
+// Big tiles pay off once they alone give at least half the CUs a tile.
+bool nt16_big(const GemmDesc& d) {
+  return ceil_div(d.M, Nt16Big::bm) * ceil_div(d.N, Nt16Big::bn) >= 128;
+}
+
 // The fp16 NT DMA kernel applies when both operands are fp16 in storage,
 // K-contiguous with 16-byte aligned rows, K is a whole number of 64-wide
 // tiles and nothing extends the contraction.
@@ -938,7 +1022,10 @@ bool nt16_ok(const GemmDesc& d) {
 }
 
 Grid plan(const GemmDesc& d, size_t ws_bytes) {
-  if (nt16_ok(d)) return plan_tiles(d, ws_bytes, 128, 128, 64);
+  if (nt16_ok(d)) {
+    if (nt16_big(d)) return plan_tiles(d, ws_bytes, Nt16Big::bm, Nt16Big::bn, 64);
+    return plan_tiles(d, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64);
+  }
   const Cfg c = cfg_for(d);
   const int bk = PT<Prec::F16>::BK / (d.prec == Prec::F16 ? 1 : 2) / (c.bk_big ? 1 : 2);
   return plan_tiles(d, ws_bytes, c.bm, c.bn, bk);
@@ -956,8 +1043,8 @@ int finish_splits(const GemmDesc& d, const Grid& g, hipStream_t st) {
 
 int launch_nt16(const GemmDesc& d, hipStream_t st) {
   const Grid g = plan(d, d.ws ? d.ws_bytes : 0);
-  const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
-  hipLaunchKernelGGL((gemm_nt16_kernel<2, 2>), dim3(nwg), dim3(256), 0, st, d, g);
+  if (nt16_big(d)) Nt16Big::launch(d, g, st);
+  else Nt16Small::launch(d, g, st);
   QBLK_TRY(check_launch("gemm_nt16_kernel"));
   return finish_splits(d, g, st);
 }

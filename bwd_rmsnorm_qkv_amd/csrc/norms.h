@@ -60,4 +60,10 @@ int swiglu_forward(int T, int I, const float* gu, float* s, f16* s16, hipStream_
 // dgu = [ds * u * silu'(g) | ds * silu(g)].
 int swiglu_backward(int T, int I, const float* gu, const float* ds, float* dgu, hipStream_t st);
 
+// fp16 copies of an fp32 matrix in [R, C] (row stride ldi): out [R, C]
+// (stride ldo) and/or outT [C, R] (stride ldt); either may be NULL.
+// C and every stride must be multiples of 4.
+int cast_f16(int R, int C, const float* in, int64_t ldi, f16* out, int64_t ldo, f16* outT, int64_t ldt,
+             hipStream_t st);
+
 }  // namespace qblk

@@ -37,7 +37,7 @@ class Config(C.Structure):
 
 
 class BlockParams(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in PARAMS]
+    _fields_ = [(n, C.c_void_p) for n in PARAMS] + [("w16", C.c_void_p)]
 
 
 class BlockGrads(C.Structure):
@@ -64,6 +64,8 @@ _SIGS = {
                             C.c_void_p, C.c_size_t, C.c_void_p], C.c_int32),
     "qblk_block_backward": ([C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                              C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int32),
+    "qblk_block_pack_f16_size": ([C.c_void_p, C.POINTER(C.c_size_t)], C.c_int32),
+    "qblk_block_pack_f16": ([C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int32),
     "qblk_cross_entropy_workspace_size": ([C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_size_t)], C.c_int32),
     "qblk_fused_cross_entropy": ([C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_void_p, C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -173,7 +175,22 @@ def block_workspace_size(cfg):
 
 
 def _params(p: dict) -> BlockParams:
-    return BlockParams(*[_p(p[n]) for n in PARAMS])
+    """p: the 11 tensors by name, plus an optional packed fp16 set under "w16"."""
+    return BlockParams(*[_p(p[n]) for n in PARAMS], _p(p.get("w16")))
+
+
+def block_pack_f16_size(cfg):
+    c = _cfg(cfg)
+    n = C.c_size_t()
+    _check(lib().qblk_block_pack_f16_size(C.byref(c), C.byref(n)))
+    return n.value
+
+
+def block_pack_f16(cfg, params: dict, packed, stream=None):
+    c = _cfg(cfg)
+    bp = _params({**params, "w16": None})
+    _check(lib().qblk_block_pack_f16(C.byref(c), C.byref(bp), _p(packed), packed.numel() * packed.element_size(),
+                                     _stream(stream)))
 
 
 def block_forward(cfg, params: dict, x, y, saved, scratch=None, stream=None):

@@ -77,6 +77,14 @@ class Block:
         self.y = empty((T, h))
         self.dx = empty((T, h))
 
+    def pack_f16(self, params, stream=None):
+        """params plus "w16": the packed fp16 weight copies (fp16-operand
+        configurations), refreshed from params' fp32 weights now."""
+        if not hasattr(self, "packed"):
+            self.packed = byte_buffer(qblk.block_pack_f16_size(self.c))
+        qblk.block_pack_f16(self.c, params, self.packed, stream)
+        return {**params, "w16": self.packed}
+
     def forward(self, params, x, saved=None, y=None, stream=None):
         qblk.block_forward(self.c, params, x, self.y if y is None else y,
                            self.saved if saved is None else saved, self.scratch, stream)

@@ -66,10 +66,17 @@ typedef struct {
 
 /* The 11 trainable tensors of a block: w_q [H*d, h], w_k [KV*d, h],
  * w_v [KV*d, h], w_o [h, H*d], w_gate [I, h], w_up [I, h], w_down [h, I],
- * g_in [h], g_post [h], g_q [d], g_k [d] (fp32, device). */
+ * g_in [h], g_post [h], g_q [d], g_k [d] (fp32, device).
+ * w16 (optional, gemm_precision 1 only): the fp16 copies of the seven
+ * projection weights written by qblk_block_pack_f16 from these same fp32
+ * weights ([block] set_fp16_weights keeps such copies). NULL: each
+ * forward/backward call casts the weights into its scratch instead, with
+ * identical results. The caller re-packs after changing the fp32 weights;
+ * the library never checks that the copies are current. */
 typedef struct {
   const float *w_q, *w_k, *w_v, *w_o, *w_gate, *w_up, *w_down;
   const float *g_in, *g_post, *g_q, *g_k;
+  const void* w16;
 } qblk_block_params;
 
 /* Gradient outputs, same shapes; every field is OVERWRITTEN (not added). */
@@ -83,6 +90,16 @@ typedef struct {
  * untouched in between); `scratch` is temporary for either call. */
 int32_t qblk_block_workspace_size(const qblk_config* cfg, size_t* saved_bytes,
                                   size_t* scratch_bytes);
+
+/* Bytes of the packed fp16 weight set of a block (qblk_block_params.w16). */
+int32_t qblk_block_pack_f16_size(const qblk_config* cfg, size_t* bytes);
+
+/* Writes the packed fp16 weight set ([block] set_fp16_weights, cast_f32_to_f16
+ * with round to nearest even) of p's fp32 projection weights into `packed`
+ * (device, 16-byte aligned, at least qblk_block_pack_f16_size bytes): each
+ * weight as stored and transposed, for the forward and the dX products. */
+int32_t qblk_block_pack_f16(const qblk_config* cfg, const qblk_block_params* p, void* packed,
+                            size_t packed_bytes, qblk_stream_t stream);
 
 /* Block forward, [block] CudaTransformerBlock::forward and
  * compute_attention_cuda: n1 = RMSNorm(x; g_in); q, k, v = n1 W^T;

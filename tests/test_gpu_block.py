@@ -18,6 +18,12 @@ CASES = {
     "small": synth.SMALL_BLOCK,
     "small_ragged_fp16": synth.BlockShape(hidden=512, heads=8, kv_heads=2, head_dim=64, intermediate=1408,
                                           seq=77, batch=2, rope_theta=1e4, gemm_precision=1),
+    # fp16 operands with T a multiple of 64 (every product on the direct-to-LDS
+    # kernel) and of 8 only (the weight-gradient products on the general one)
+    "small_fp16_t192": synth.BlockShape(hidden=512, heads=8, kv_heads=2, head_dim=64, intermediate=1408,
+                                        seq=96, batch=2, rope_theta=1e4, gemm_precision=1),
+    "small_fp16_t200": synth.BlockShape(hidden=512, heads=8, kv_heads=2, head_dim=64, intermediate=1408,
+                                        seq=100, batch=2, rope_theta=1e4, gemm_precision=1),
     "qwen3_4b": synth.QWEN3_4B_BLOCK,
 }
 
@@ -44,6 +50,8 @@ def test_block_forward_backward(name, unit_gammas):
     P = {k: dev(v) for k, v in params.items()}
     X, DY = dev(inp["x"]), dev(inp["dy"])
     blk = Block(c)
+    if name == "qwen3_4b":
+        P = blk.pack_f16(P)  # weights cast once, as the benchmark runs it
     y = blk.forward(P, X)
     grads = {k: empty(v.shape) for k, v in params.items()}
     dx = blk.backward(P, X, DY, grads)
@@ -57,6 +65,30 @@ def test_block_forward_backward(name, unit_gammas):
     for k in qblk.PARAMS:
         check("d" + k, grads[k], g_ref[k], tol, rep)
     announce("  " + " ".join(f"{k}={v:.1e}" for k, v in rep.items()))
+
+
+@pytest.mark.parametrize("name", ["small_fp16_t192", "small_fp16_t200"])
+def test_block_packed_weights_match(name):
+    """Caller-packed fp16 weights and the per-call cast into scratch are the
+    same numbers, so the results are bitwise equal."""
+    need_gpu()
+    c = CASES[name]
+    announce(f"block packed vs per-call cast {name}")
+    inp = synth.block_inputs(c)
+    P = {k: dev(v) for k, v in inp["params"].items()}
+    X, DY = dev(inp["x"]), dev(inp["dy"])
+    blk = Block(c)
+    outs = []
+    for params in (P, blk.pack_f16(P)):
+        y = blk.forward(params, X).clone()
+        grads = {k: empty(v.shape) for k, v in inp["params"].items()}
+        dx = blk.backward(params, X, DY, grads).clone()
+        torch.cuda.synchronize()
+        outs.append((y, dx, grads))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+    for k in qblk.PARAMS:
+        assert torch.equal(outs[0][2][k], outs[1][2][k]), k
 
 
 def test_block_backward_deterministic():
