@@ -348,6 +348,44 @@ int32_t qblk_attention_forward(int32_t batch, int32_t seq, int32_t heads, int32_
   return attention_forward(a, precision ? Prec::F16 : Prec::F32, S(stream));
 }
 
+static Attn16Args attn16_dense(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads, int32_t head_dim) {
+  Attn16Args a{};
+  a.batch = batch; a.seq = seq; a.heads = heads; a.kv_heads = kv_heads; a.head_dim = head_dim;
+  a.ldq = (int64_t)heads * head_dim;
+  a.ldk = a.ldv = (int64_t)kv_heads * head_dim;
+  a.ldt = (int64_t)batch * seq;
+  a.ldo = a.lddo = a.lddo32 = a.lddq = (int64_t)heads * head_dim;
+  a.lddk = a.lddv = (int64_t)kv_heads * head_dim;
+  return a;
+}
+
+int32_t qblk_attention_forward_f16(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                   const void* q16, const void* k16, const void* vT16, float* o, float* lse,
+                                   qblk_stream_t stream) {
+  Attn16Args a = attn16_dense(batch, seq, heads, kv_heads, head_dim);
+  a.q = (const f16*)q16; a.k = (const f16*)k16; a.vT = (const f16*)vT16;
+  a.o = o; a.lse = lse;
+  return attention16_forward(a, S(stream));
+}
+
+int32_t qblk_attention_backward_f16(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads,
+                                    int32_t head_dim, const void* q16, const void* qT16, const void* k16,
+                                    const void* kT16, const void* v16, const float* o, const float* lse,
+                                    const void* do16, const void* doT16, const float* do32, float* dq,
+                                    float* dk, float* dv, void* scratch, size_t scratch_bytes,
+                                    qblk_stream_t stream) {
+  QBLK_TRY(attention_check(batch, seq, heads, kv_heads, head_dim));
+  if (scratch_bytes < attention_bwd_scratch(batch, seq, heads, head_dim))
+    return fail(QBLK_EINVAL, "attention_backward_f16: scratch too small");
+  Attn16Args a = attn16_dense(batch, seq, heads, kv_heads, head_dim);
+  a.q = (const f16*)q16; a.qT = (const f16*)qT16; a.k = (const f16*)k16; a.kT = (const f16*)kT16;
+  a.v = (const f16*)v16; a.vT = (const f16*)kT16;  // the backward never reads vT
+  a.o = (float*)o; a.lse = (float*)lse;
+  a.d_o = (const f16*)do16; a.doT = (const f16*)doT16; a.do32 = do32;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  return attention16_backward(a, scratch, S(stream));
+}
+
 int32_t qblk_attention_workspace_size(int32_t batch, int32_t seq, int32_t heads, size_t* scratch_bytes) {
   if (batch <= 0 || seq <= 0 || heads <= 0) return fail(QBLK_EINVAL, "attention: bad sizes");
   // head_dim 128 upper bound

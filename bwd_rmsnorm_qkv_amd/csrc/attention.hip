@@ -26,6 +26,8 @@
 
 #include "../../include/qblk.h"
 
+#include <type_traits>
+
 namespace qblk {
 namespace {
 
@@ -510,6 +512,494 @@ int bwd_launch(const AttnArgs& a, float* delta, float* dk_part, float* dv_part, 
   return check_launch("attn_gqa_reduce_kernel");
 }
 
+// ====================================================================
+// fp16 copies + direct global -> LDS tiles (head_dim 64 / 128)
+//
+// Same orientations as above; what changes is how tiles reach LDS and how
+// P (or dS) becomes an MFMA operand. Every tile is a plain copy of a 32-row
+// slab of an fp16 matrix: row tiles [32][D] from the row-major copies and
+// transposed tiles [D][32] from the transposed ones, so no thread converts
+// or transposes anything and the copies run as global_load_lds_dwordx4
+// (1 KB per wave instruction) into two LDS stages. For the products whose
+// contraction runs over the 32 keys (or queries) of an accumulator, the
+// lane halves trade four packed values with v_permlane32_swap so that each
+// lane holds 8 consecutive keys, the natural order of the transposed tile.
+
+// Row tile: 32 rows x D halves, rows unpadded, 16-byte chunks XOR-swizzled
+// so that 16 consecutive rows read at one chunk hit distinct bank groups.
+template <int D>
+struct RowTile {
+  static constexpr int NCH = D / 8;     // 16-byte chunks per row
+  static constexpr int RPI = 64 / NCH;  // rows per 1 KB wave copy
+  static constexpr int NI = 32 / RPI;   // wave copies per tile
+  static __device__ __forceinline__ int sw(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  static __device__ __forceinline__ half8 read(const f16* t, int row, int lc) {
+    return *(const half8*)(t + row * D + ((lc ^ sw(row)) << 3));
+  }
+};
+
+// Transposed tile: D rows x 32 halves (64 bytes), 4 chunks per row, swizzled
+// over groups of 4 rows.
+template <int D>
+struct TrTile {
+  static constexpr int NI = D / 16;  // 16 rows per 1 KB wave copy
+  static __device__ __forceinline__ int sw(int row) { return (row >> 2) & 3; }
+  static __device__ __forceinline__ half8 read(const f16* t, int row, int lc) {
+    return *(const half8*)(t + row * 32 + ((lc ^ sw(row)) << 3));
+  }
+};
+
+// Wave copy j of a row tile: rows r0 .. r0+31 of a [T, *] fp16 matrix
+// (sequence-local rows past S clamp to S-1), columns col0 .. col0+D-1.
+template <int D>
+__device__ __forceinline__ void copy_rows(f16* tile, int j, int lane, const f16* base, int64_t ld, int64_t tok0,
+                                          int r0, int S, int col0) {
+  using RT = RowTile<D>;
+  const int row = j * RT::RPI + lane / RT::NCH;
+  const int lc = (lane % RT::NCH) ^ RT::sw(row);
+  dma16(base + (tok0 + min(r0 + row, S - 1)) * ld + col0 + lc * 8, tile + j * 512);
+}
+
+// Wave copy j of a transposed tile: rows row0 .. row0+D-1 of a [*, T] fp16
+// matrix, columns tok0 + c0 .. +31 (8-column chunks past S read chunk 0;
+// they are masked).
+template <int D>
+__device__ __forceinline__ void copy_tr(f16* tile, int j, int lane, const f16* base, int64_t ldt, int64_t tok0,
+                                        int c0, int S, int row0) {
+  using TT = TrTile<D>;
+  const int row = j * 16 + (lane >> 2);
+  const int lc = (lane & 3) ^ TT::sw(row);
+  int c = c0 + lc * 8;
+  if (c >= S) c = 0;
+  dma16(base + (int64_t)(row0 + row) * ldt + tok0 + c, tile + j * 512);
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef unsigned uint4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+  half2v h;
+  h[0] = (f16)a;
+  h[1] = (f16)b;
+  return __builtin_bit_cast(unsigned, h);
+}
+
+// Accumulator values 8 s2 .. 8 s2 + 7 of a 32 x 32 accumulator, whose rows
+// (keys or queries) are 8g + 4(lane/32) + r, as the B operand of a product
+// contracting over rows 16 s2 .. 16 s2 + 15: after the swap, lane half kh
+// holds rows 16 s2 + 8 kh + j, j = 0..7, in order.
+__device__ __forceinline__ half8 acc_rows_operand(const floatx16& p, int s2) {
+  unsigned r0a = pack2(p[8 * s2 + 0], p[8 * s2 + 1]), r0b = pack2(p[8 * s2 + 2], p[8 * s2 + 3]);
+  unsigned r1a = pack2(p[8 * s2 + 4], p[8 * s2 + 5]), r1b = pack2(p[8 * s2 + 6], p[8 * s2 + 7]);
+  const auto x = __builtin_amdgcn_permlane32_swap(r0a, r1a, false, false);
+  const auto y = __builtin_amdgcn_permlane32_swap(r0b, r1b, false, false);
+  uint4v u;
+  u[0] = x[0];
+  u[1] = y[0];
+  u[2] = x[1];
+  u[3] = y[1];
+  return __builtin_bit_cast(half8, u);
+}
+
+using I0 = std::integral_constant<int, 0>;
+using I1 = std::integral_constant<int, 1>;
+
+// Forward: grid (q tiles, kv groups, batch), longest query tiles first; one
+// wave per query head of the group, K and V^T tiles shared through LDS.
+template <int D>
+__global__ __launch_bounds__(512) void attn16_fwd_kernel(const Attn16Args a) {
+  using RT = RowTile<D>;
+  using TT = TrTile<D>;
+  __shared__ __attribute__((aligned(16))) f16 sK0[32 * D];
+  __shared__ __attribute__((aligned(16))) f16 sK1[32 * D];
+  __shared__ __attribute__((aligned(16))) f16 sV0[D * 32];
+  __shared__ __attribute__((aligned(16))) f16 sV1[D * 32];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, NW = blockDim.x >> 6;
+  const int G = a.heads / a.kv_heads, grp = blockIdx.y, b = blockIdx.z;
+  const int h = grp * G + w;
+  const int S = a.seq;
+  const int qt = gridDim.x - 1 - blockIdx.x, q0 = qt * 32;
+  const int64_t tok0 = (int64_t)b * S;
+  const int i = lane & 31, kh = lane >> 5;
+  const float sc = kLog2e / sqrtf((float)D);
+  const int qi = q0 + i;
+
+  half8 qc[D / 16];
+  {
+    const f16* row = a.q + (tok0 + min(qi, S - 1)) * a.ldq + (int64_t)h * D + 8 * kh;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) qc[c] = *(const half8*)(row + 16 * c);
+  }
+  floatx16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const int nkt = qt + 1;
+
+  auto issue = [&](int kt, f16* sk, f16* sv) __attribute__((always_inline)) {
+    for (int j = w; j < RT::NI + TT::NI; j += NW) {
+      if (j < RT::NI) copy_rows<D>(sk, j, lane, a.k, a.ldk, tok0, kt * 32, S, grp * D);
+      else copy_tr<D>(sv, j - RT::NI, lane, a.vT, a.ldt, tok0, kt * 32, S, grp * D);
+    }
+  };
+  auto compute = [&](const f16* sk, const f16* sv, int kt) __attribute__((always_inline)) {
+    const int kv0 = kt * 32;
+    floatx16 s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(RT::read(sk, i, 2 * c + kh), qc[c], s, 0, 0, 0);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kj = kv0 + 8 * g + 4 * kh + r;
+        float v = s[4 * g + r] * sc;
+        if (kj > qi || kj >= S) v = -INFINITY;
+        s[4 * g + r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = half_max(mx);
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2f(m - mn);
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = exp2f(s[e] - mn);
+      s[e] = p;
+      ps += p;
+    }
+    l = l * alpha + half_sum(ps);
+    m = mn;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const half8 bp = acc_rows_operand(s, s2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(TT::read(sv, db * 32 + i, 2 * s2 + kh), bp, o[db], 0, 0, 0);
+    }
+  };
+  auto step = [&](auto St, int kt) __attribute__((always_inline)) {
+    constexpr int st = decltype(St)::value;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + 1 < nkt) {
+      if constexpr (st == 0) issue(kt + 1, sK1, sV1);
+      else issue(kt + 1, sK0, sV0);
+    }
+    if constexpr (st == 0) compute(sK0, sV0, kt);
+    else compute(sK1, sV1, kt);
+  };
+  issue(0, sK0, sV0);
+  const int nfull = nkt & ~1;
+  for (int kt = 0; kt < nfull; kt += 2) {
+    step(I0{}, kt);
+    step(I1{}, kt + 1);
+  }
+  if (nkt & 1) step(I0{}, nfull);
+
+  if (qi < S) {
+    const float inv = 1.0f / l;
+    float* orow = a.o + (tok0 + qi) * a.ldo + (int64_t)h * D + 4 * kh;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(float4*)(orow + db * 32 + 8 * g) =
+            make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+    if (kh == 0) a.lse[((int64_t)b * a.heads + h) * S + qi] = (m + log2f(l)) * kLn2;
+  }
+}
+
+// dQ: grid (q tiles, kv groups, batch), one wave per query head; K, V and
+// K^T tiles shared through LDS.
+template <int D>
+__global__ __launch_bounds__(512) void attn16_dq_kernel(const Attn16Args a, const float* delta) {
+  using RT = RowTile<D>;
+  using TT = TrTile<D>;
+  __shared__ __attribute__((aligned(16))) f16 sK0[32 * D];
+  __shared__ __attribute__((aligned(16))) f16 sK1[32 * D];
+  __shared__ __attribute__((aligned(16))) f16 sV0[32 * D];
+  __shared__ __attribute__((aligned(16))) f16 sV1[32 * D];
+  __shared__ __attribute__((aligned(16))) f16 sKt0[D * 32];
+  __shared__ __attribute__((aligned(16))) f16 sKt1[D * 32];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, NW = blockDim.x >> 6;
+  const int G = a.heads / a.kv_heads, grp = blockIdx.y, b = blockIdx.z;
+  const int h = grp * G + w;
+  const int S = a.seq;
+  const int qt = gridDim.x - 1 - blockIdx.x, q0 = qt * 32;
+  const int64_t tok0 = (int64_t)b * S;
+  const int i = lane & 31, kh = lane >> 5;
+  const float sc = kLog2e / sqrtf((float)D);
+  const int qi = q0 + i, qc_i = min(qi, S - 1);
+
+  half8 qc[D / 16], dc[D / 16];
+  {
+    const f16* qrow = a.q + (tok0 + qc_i) * a.ldq + (int64_t)h * D + 8 * kh;
+    const f16* drow = a.d_o + (tok0 + qc_i) * a.lddo + (int64_t)h * D + 8 * kh;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      qc[c] = *(const half8*)(qrow + 16 * c);
+      dc[c] = *(const half8*)(drow + 16 * c);
+    }
+  }
+  const int64_t rowi = ((int64_t)b * a.heads + h) * S + qc_i;
+  const float lse2 = a.lse[rowi] * kLog2e;
+  const float dl = delta[rowi];
+  floatx16 dq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[db][e] = 0.f;
+  const int nkt = qt + 1;
+
+  auto issue = [&](int kt, f16* sk, f16* sv, f16* skt) __attribute__((always_inline)) {
+    for (int j = w; j < 2 * RT::NI + TT::NI; j += NW) {
+      if (j < RT::NI) copy_rows<D>(sk, j, lane, a.k, a.ldk, tok0, kt * 32, S, grp * D);
+      else if (j < 2 * RT::NI) copy_rows<D>(sv, j - RT::NI, lane, a.v, a.ldv, tok0, kt * 32, S, grp * D);
+      else copy_tr<D>(skt, j - 2 * RT::NI, lane, a.kT, a.ldt, tok0, kt * 32, S, grp * D);
+    }
+  };
+  auto compute = [&](const f16* sk, const f16* sv, const f16* skt, int kt) __attribute__((always_inline)) {
+    const int kv0 = kt * 32;
+    floatx16 s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s[e] = 0.f;
+      dp[e] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(RT::read(sk, i, 2 * c + kh), qc[c], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(RT::read(sv, i, 2 * c + kh), dc[c], dp, 0, 0, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = 4 * g + r;
+        const int kj = kv0 + 8 * g + 4 * kh + r;
+        const float p = (kj > qi || kj >= S) ? 0.f : exp2f(s[e] * sc - lse2);
+        s[e] = p * (dp[e] - dl);  // dS^T, unscaled
+      }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const half8 bp = acc_rows_operand(s, s2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(TT::read(skt, db * 32 + i, 2 * s2 + kh), bp, dq[db], 0, 0, 0);
+    }
+  };
+  auto step = [&](auto St, int kt) __attribute__((always_inline)) {
+    constexpr int st = decltype(St)::value;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + 1 < nkt) {
+      if constexpr (st == 0) issue(kt + 1, sK1, sV1, sKt1);
+      else issue(kt + 1, sK0, sV0, sKt0);
+    }
+    if constexpr (st == 0) compute(sK0, sV0, sKt0, kt);
+    else compute(sK1, sV1, sKt1, kt);
+  };
+  issue(0, sK0, sV0, sKt0);
+  const int nfull = nkt & ~1;
+  for (int kt = 0; kt < nfull; kt += 2) {
+    step(I0{}, kt);
+    step(I1{}, kt + 1);
+  }
+  if (nkt & 1) step(I0{}, nfull);
+
+  if (qi < S) {
+    const float inv = 1.0f / sqrtf((float)D);
+    float* row = a.dq + (tok0 + qi) * a.lddq + (int64_t)h * D + 4 * kh;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(float4*)(row + db * 32 + 8 * g) = make_float4(dq[db][4 * g] * inv, dq[db][4 * g + 1] * inv,
+                                                        dq[db][4 * g + 2] * inv, dq[db][4 * g + 3] * inv);
+  }
+}
+
+// dK, dV per query head: grid (kv tiles, heads, batch), one wave; Q, dO,
+// Q^T and dO^T tiles through LDS. Results go to per-head partials
+// [T, heads, D], summed over each group in a fixed order afterwards.
+template <int D>
+__global__ __launch_bounds__(64) void attn16_dkv_kernel(const Attn16Args a, const float* delta, float* dk_part,
+                                                        float* dv_part) {
+  using RT = RowTile<D>;
+  using TT = TrTile<D>;
+  __shared__ __attribute__((aligned(16))) f16 sQ0[32 * D];
+  __shared__ __attribute__((aligned(16))) f16 sQ1[32 * D];
+  __shared__ __attribute__((aligned(16))) f16 sO0[32 * D];
+  __shared__ __attribute__((aligned(16))) f16 sO1[32 * D];
+  __shared__ __attribute__((aligned(16))) f16 sQt0[D * 32];
+  __shared__ __attribute__((aligned(16))) f16 sQt1[D * 32];
+  __shared__ __attribute__((aligned(16))) f16 sOt0[D * 32];
+  __shared__ __attribute__((aligned(16))) f16 sOt1[D * 32];
+  const int lane = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int G = a.heads / a.kv_heads, grp = h / G;
+  const int S = a.seq;
+  const int kt = gridDim.x - 1 - blockIdx.x, kv0 = kt * 32;
+  const int64_t tok0 = (int64_t)b * S;
+  const int i = lane & 31, kh = lane >> 5;
+  const float sc = kLog2e / sqrtf((float)D);
+  const int kj = kv0 + i;  // this lane's key (column of every accumulator)
+
+  half8 kc[D / 16], vc[D / 16];
+  {
+    const int kr = min(kj, S - 1);
+    const f16* krow = a.k + (tok0 + kr) * a.ldk + (int64_t)grp * D + 8 * kh;
+    const f16* vrow = a.v + (tok0 + kr) * a.ldv + (int64_t)grp * D + 8 * kh;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      kc[c] = *(const half8*)(krow + 16 * c);
+      vc[c] = *(const half8*)(vrow + 16 * c);
+    }
+  }
+  floatx16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dk[db][e] = 0.f;
+      dv[db][e] = 0.f;
+    }
+  const int nqt = (S + 31) / 32;
+  const float* lse_h = a.lse + ((int64_t)b * a.heads + h) * S;
+  const float* dl_h = delta + ((int64_t)b * a.heads + h) * S;
+
+  auto issue = [&](int qt, f16* sq, f16* so, f16* sqt, f16* sot) __attribute__((always_inline)) {
+    const int q0 = qt * 32;
+#pragma unroll
+    for (int j = 0; j < RT::NI; ++j) {
+      copy_rows<D>(sq, j, lane, a.q, a.ldq, tok0, q0, S, h * D);
+      copy_rows<D>(so, j, lane, a.d_o, a.lddo, tok0, q0, S, h * D);
+    }
+#pragma unroll
+    for (int j = 0; j < TT::NI; ++j) {
+      copy_tr<D>(sqt, j, lane, a.qT, a.ldt, tok0, q0, S, h * D);
+      copy_tr<D>(sot, j, lane, a.doT, a.ldt, tok0, q0, S, h * D);
+    }
+  };
+  auto compute = [&](const f16* sq, const f16* so, const f16* sqt, const f16* sot, int qt) __attribute__((always_inline)) {
+    const int q0 = qt * 32;
+    // log-sum-exp and delta of this lane's 16 query rows q0 + 8g + 4kh + r
+    float4 lq[4], dq4[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int qr = q0 + 8 * g + 4 * kh;
+      lq[g] = qr < S ? *(const float4*)(lse_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
+      dq4[g] = qr < S ? *(const float4*)(dl_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    floatx16 s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s[e] = 0.f;
+      dp[e] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(RT::read(sq, i, 2 * c + kh), kc[c], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(RT::read(so, i, 2 * c + kh), vc[c], dp, 0, 0, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = 4 * g + r;
+        const int qq = q0 + 8 * g + 4 * kh + r;
+        const float L = r == 0 ? lq[g].x : r == 1 ? lq[g].y : r == 2 ? lq[g].z : lq[g].w;
+        const float Dl = r == 0 ? dq4[g].x : r == 1 ? dq4[g].y : r == 2 ? dq4[g].z : dq4[g].w;
+        const float p = (kj > qq || qq >= S || kj >= S) ? 0.f : exp2f(s[e] * sc - L * kLog2e);
+        s[e] = p;
+        dp[e] = p * (dp[e] - Dl);
+      }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const half8 bp = acc_rows_operand(s, s2);
+      const half8 bd = acc_rows_operand(dp, s2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(TT::read(sot, db * 32 + i, 2 * s2 + kh), bp, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(TT::read(sqt, db * 32 + i, 2 * s2 + kh), bd, dk[db], 0, 0, 0);
+      }
+    }
+  };
+  const int n = nqt - kt;  // query tiles kt .. nqt-1
+  auto step = [&](auto St, int t) __attribute__((always_inline)) {
+    constexpr int st = decltype(St)::value;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (t + 1 < n) {
+      if constexpr (st == 0) issue(kt + t + 1, sQ1, sO1, sQt1, sOt1);
+      else issue(kt + t + 1, sQ0, sO0, sQt0, sOt0);
+    }
+    if constexpr (st == 0) compute(sQ0, sO0, sQt0, sOt0, kt + t);
+    else compute(sQ1, sO1, sQt1, sOt1, kt + t);
+  };
+  issue(kt, sQ0, sO0, sQt0, sOt0);
+  const int nfull = n & ~1;
+  for (int t = 0; t < nfull; t += 2) {
+    step(I0{}, t);
+    step(I1{}, t + 1);
+  }
+  if (n & 1) step(I0{}, nfull);
+
+  if (kj < S) {
+    const float inv = 1.0f / sqrtf((float)D);
+    float* krow = dk_part + ((tok0 + kj) * a.heads + h) * (int64_t)D + 4 * kh;
+    float* vrow = dv_part + ((tok0 + kj) * a.heads + h) * (int64_t)D + 4 * kh;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        *(float4*)(krow + db * 32 + 8 * g) = make_float4(dk[db][4 * g] * inv, dk[db][4 * g + 1] * inv,
+                                                         dk[db][4 * g + 2] * inv, dk[db][4 * g + 3] * inv);
+        *(float4*)(vrow + db * 32 + 8 * g) =
+            make_float4(dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
+      }
+  }
+}
+
+template <int D>
+int fwd16_launch(const Attn16Args& a, hipStream_t st) {
+  const int G = a.heads / a.kv_heads;
+  dim3 grid((unsigned)ceil_div(a.seq, 32), (unsigned)a.kv_heads, (unsigned)a.batch);
+  hipLaunchKernelGGL((attn16_fwd_kernel<D>), grid, dim3(64 * G), 0, st, a);
+  return check_launch("attn16_fwd_kernel");
+}
+
+template <int D>
+int bwd16_launch(const Attn16Args& a, float* delta, float* dk_part, float* dv_part, hipStream_t st) {
+  const int G = a.heads / a.kv_heads;
+  const int64_t T = (int64_t)a.batch * a.seq;
+  AttnArgs da{};
+  da.batch = a.batch; da.seq = a.seq; da.heads = a.heads; da.kv_heads = a.kv_heads; da.head_dim = D;
+  da.o = a.o; da.ldo = a.ldo;
+  da.d_o = a.do32; da.lddo = a.lddo32;
+  hipLaunchKernelGGL(attn_delta_kernel, dim3((unsigned)ceil_div(T * a.heads, 4)), dim3(256), 0, st, da, delta);
+  QBLK_TRY(check_launch("attn_delta_kernel"));
+  dim3 gq((unsigned)ceil_div(a.seq, 32), (unsigned)a.kv_heads, (unsigned)a.batch);
+  hipLaunchKernelGGL((attn16_dq_kernel<D>), gq, dim3(64 * G), 0, st, a, (const float*)delta);
+  QBLK_TRY(check_launch("attn16_dq_kernel"));
+  dim3 gk((unsigned)ceil_div(a.seq, 32), (unsigned)a.heads, (unsigned)a.batch);
+  hipLaunchKernelGGL((attn16_dkv_kernel<D>), gk, dim3(64), 0, st, a, (const float*)delta, dk_part, dv_part);
+  QBLK_TRY(check_launch("attn16_dkv_kernel"));
+  const int64_t n = T * a.kv_heads * D;
+  hipLaunchKernelGGL(attn_gqa_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, T, a.heads,
+                     a.kv_heads, D, (const float*)dk_part, (const float*)dv_part, a.dk, a.lddk, a.dv, a.lddv);
+  return check_launch("attn_gqa_reduce_kernel");
+}
+
 }  // namespace
 
 int attention_check(int batch, int seq, int heads, int kv_heads, int head_dim) {
@@ -555,6 +1045,44 @@ int attention_backward(const AttnArgs& a, Prec p, void* scratch, hipStream_t st)
   if (dp == 32) return bwd_launch<Prec::F32, 32>(a, delta, dk_part, dv_part, st);
   if (dp == 64) return bwd_launch<Prec::F32, 64>(a, delta, dk_part, dv_part, st);
   return fail(QBLK_EUNSUPPORTED, "attention backward: fp32 needs head_dim <= 64");
+}
+
+bool attention16_supported(int batch, int seq, int heads, int kv_heads, int head_dim) {
+  return attention_check(batch, seq, heads, kv_heads, head_dim) == 0 && (head_dim == 64 || head_dim == 128) &&
+         seq % 8 == 0;
+}
+
+static int check16(const Attn16Args& a) {
+  QBLK_TRY(attention_check(a.batch, a.seq, a.heads, a.kv_heads, a.head_dim));
+  if (!attention16_supported(a.batch, a.seq, a.heads, a.kv_heads, a.head_dim))
+    return fail(QBLK_EUNSUPPORTED, "attention16: head_dim must be 64 or 128 and seq a multiple of 8");
+  const int64_t T = (int64_t)a.batch * a.seq;
+  if (a.ldt != T || a.ldq % 8 || a.ldk % 8 || a.ldv % 8 || a.ldo % 4)
+    return fail(QBLK_EINVAL, "attention16: strides (ldt must be T; row strides multiples of 8)");
+  const void* ptrs[] = {a.q, a.k, a.vT, a.o, a.lse};
+  for (const void* p : ptrs)
+    if (!p || ((uintptr_t)p & 15)) return fail(QBLK_EINVAL, "attention16: null or misaligned pointer");
+  return 0;
+}
+
+int attention16_forward(const Attn16Args& a, hipStream_t st) {
+  QBLK_TRY(check16(a));
+  return a.head_dim == 64 ? fwd16_launch<64>(a, st) : fwd16_launch<128>(a, st);
+}
+
+int attention16_backward(const Attn16Args& a, void* scratch, hipStream_t st) {
+  QBLK_TRY(check16(a));
+  const void* ptrs[] = {a.v, a.qT, a.kT, a.d_o, a.doT, a.do32, a.dq, a.dk, a.dv, scratch};
+  for (const void* p : ptrs)
+    if (!p || ((uintptr_t)p & 15)) return fail(QBLK_EINVAL, "attention16 backward: null or misaligned pointer");
+  if (a.lddo % 8 || a.lddo32 % 4 || a.lddq % 4 || a.lddk % 4 || a.lddv % 4)
+    return fail(QBLK_EINVAL, "attention16 backward: row strides");
+  const int64_t T = (int64_t)a.batch * a.seq;
+  float* delta = (float*)scratch;
+  float* dk_part = delta + T * a.heads;
+  float* dv_part = dk_part + T * a.heads * a.head_dim;
+  return a.head_dim == 64 ? bwd16_launch<64>(a, delta, dk_part, dv_part, st)
+                          : bwd16_launch<128>(a, delta, dk_part, dv_part, st);
 }
 
 }  // namespace qblk

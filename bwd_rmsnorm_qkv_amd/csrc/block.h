@@ -25,7 +25,13 @@ struct Saved {
   float* n2;       // [T, h]
   float* gu;       // [T, 2I] gate | up
   float* s;        // [T, I] SwiGLU output
+  // fp16-operand attention (when attention16_supported): fp16 copies of the
+  // attention inputs, row-major and transposed; NULL otherwise.
+  f16 *q16, *qT16, *k16, *kT16, *v16, *vT16;
 };
+
+// The fp16 attention kernels apply to this config.
+bool use_attention16(const qblk_config& c);
 
 // fp16 copies of the dense block's projection weights, as every fp16
 // contraction reads them: W [out, in] for the forward (x W^T) and W^T
@@ -51,6 +57,7 @@ struct Scratch {
   // passes no packed weights, the weights' fp16 copies.
   f16 *a16, *aT16, *bT16;
   Packed16 pack;
+  f16 *do16, *doT16;  // fp16 attention: dO copies (NULL otherwise)
 };
 
 void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes);

@@ -56,7 +56,20 @@ void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes) {
   s.n2 = cv.take<float>(T * h);
   s.gu = cv.take<float>(T * 2 * I);
   s.s = cv.take<float>(T * I);
+  s.q16 = s.qT16 = s.k16 = s.kT16 = s.v16 = s.vT16 = nullptr;
+  if (use_attention16(c)) {
+    s.q16 = cv.take<f16>(T * qd);
+    s.qT16 = cv.take<f16>(T * qd);
+    s.k16 = cv.take<f16>(T * kvd);
+    s.kT16 = cv.take<f16>(T * kvd);
+    s.v16 = cv.take<f16>(T * kvd);
+    s.vT16 = cv.take<f16>(T * kvd);
+  }
   bytes = cv.off;
+}
+
+bool use_attention16(const qblk_config& c) {
+  return c.gemm_precision == 1 && attention16_supported(c.batch, c.seq, c.heads, c.kv_heads, c.head_dim);
 }
 
 Prec prec_of(const qblk_config& c) { return c.gemm_precision ? Prec::F16 : Prec::F32; }
@@ -112,6 +125,11 @@ void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes, 
   s.gemm_ws = cv.take<float>(s.gemm_ws_bytes / sizeof(float) + 1);
   s.a16 = s.aT16 = s.bT16 = nullptr;
   s.pack = Packed16{};
+  s.do16 = s.doT16 = nullptr;
+  if (use_attention16(c)) {
+    s.do16 = cv.take<f16>(T * qd);
+    s.doT16 = cv.take<f16>(T * qd);
+  }
   if (c.gemm_precision == 1 && lora_rank == 0) {
     const size_t wide = std::max({qd + 2 * kvd, 2 * I, h, qd});
     s.a16 = cv.take<f16>(T * wide);
@@ -180,6 +198,24 @@ int check_config(const qblk_config* c) {
 
 // ---------------------------------------------------------------- forward
 
+namespace {
+
+Attn16Args attn16_args(const qblk_config& c, const Saved& s) {
+  const int T = c.seq * c.batch, d = c.head_dim;
+  const int qd = c.heads * d, kvd = c.kv_heads * d;
+  Attn16Args a{};
+  a.batch = c.batch; a.seq = c.seq; a.heads = c.heads; a.kv_heads = c.kv_heads; a.head_dim = d;
+  a.q = s.q16; a.ldq = qd;
+  a.k = s.k16; a.ldk = kvd;
+  a.v = s.v16; a.ldv = kvd;
+  a.qT = s.qT16; a.kT = s.kT16; a.vT = s.vT16; a.ldt = T;
+  a.o = s.o; a.ldo = qd;
+  a.lse = s.lse;
+  return a;
+}
+
+}  // namespace
+
 // Projection hooks: the fp32/fp16 block uses the dense fp32 weights; the
 // NF4 block substitutes dequant + LoRA GEMMs (nf4_block.hip).
 int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g_in, const float* g_post,
@@ -195,14 +231,21 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
   QkRopeArgs qa{T, c.seq, c.heads, c.kv_heads, d, c.qk_norm, c.eps, s.qkv, ldqkv, g_q, g_k, s.tab,
                 s.qr, s.kr, s.rho_q, s.rho_k};
   QBLK_TRY(qk_norm_rope_forward(qa, st));
-  AttnArgs aa{};
-  aa.batch = c.batch; aa.seq = c.seq; aa.heads = c.heads; aa.kv_heads = c.kv_heads; aa.head_dim = d;
-  aa.q = s.qr; aa.ldq = qd;
-  aa.k = s.kr; aa.ldk = kvd;
-  aa.v = s.qkv + qd + kvd; aa.ldv = ldqkv;
-  aa.o = s.o; aa.ldo = qd;
-  aa.lse = s.lse;
-  QBLK_TRY(attention_forward(aa, prec_of(c), st));
+  if (s.q16) {
+    QBLK_TRY(cast_f16(T, qd, s.qr, qd, s.q16, qd, s.qT16, T, st));
+    QBLK_TRY(cast_f16(T, kvd, s.kr, kvd, s.k16, kvd, s.kT16, T, st));
+    QBLK_TRY(cast_f16(T, kvd, s.qkv + qd + kvd, ldqkv, s.v16, kvd, s.vT16, T, st));
+    QBLK_TRY(attention16_forward(attn16_args(c, s), st));
+  } else {
+    AttnArgs aa{};
+    aa.batch = c.batch; aa.seq = c.seq; aa.heads = c.heads; aa.kv_heads = c.kv_heads; aa.head_dim = d;
+    aa.q = s.qr; aa.ldq = qd;
+    aa.k = s.kr; aa.ldk = kvd;
+    aa.v = s.qkv + qd + kvd; aa.ldv = ldqkv;
+    aa.o = s.o; aa.ldo = qd;
+    aa.lse = s.lse;
+    QBLK_TRY(attention_forward(aa, prec_of(c), st));
+  }
   QBLK_TRY(proj.o(s.o, x, s.r1, st));  // r1 = x + o Wo^T
   QBLK_TRY(rmsnorm_forward(T, h, c.eps, s.r1, nullptr, g_post, s.n2, nullptr, nullptr, s.rho2, st));
   QBLK_TRY(proj.gate_up(s.n2, s.gu, st));
@@ -228,6 +271,16 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
   // O projection
   QBLK_TRY(proj.o(w.dr1, s.o, w.d_o, st));
   // attention backward: dq, dk at the attention inputs; dv straight into dqkv
+  if (s.q16) {
+    QBLK_TRY(cast_f16(T, qd, w.d_o, qd, w.do16, qd, w.doT16, T, st));
+    Attn16Args ab = attn16_args(c, s);
+    ab.d_o = w.do16; ab.doT = w.doT16; ab.lddo = qd;
+    ab.do32 = w.d_o; ab.lddo32 = qd;
+    ab.dq = w.dqr; ab.lddq = qd;
+    ab.dk = w.dkr; ab.lddk = kvd;
+    ab.dv = w.dqkv + qd + kvd; ab.lddv = ldqkv;
+    QBLK_TRY(attention16_backward(ab, w.attn, st));
+  } else {
   AttnArgs aa{};
   aa.batch = c.batch; aa.seq = c.seq; aa.heads = c.heads; aa.kv_heads = c.kv_heads; aa.head_dim = d;
   aa.q = s.qr; aa.ldq = qd;
@@ -240,6 +293,7 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
   aa.dk = w.dkr; aa.lddk = kvd;
   aa.dv = w.dqkv + qd + kvd; aa.lddv = ldqkv;
   QBLK_TRY(attention_backward(aa, prec_of(c), w.attn, st));
+  }
   QkRopeBwdArgs qb{T, c.seq, c.heads, c.kv_heads, d, c.qk_norm, c.eps, s.qkv, ldqkv, g_q, g_k, s.tab,
                    w.dqr, w.dkr, w.dqkv, dg_q, dg_k};
   QBLK_TRY(qk_norm_rope_backward(qb, w.red, st));

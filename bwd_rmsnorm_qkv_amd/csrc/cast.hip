@@ -12,10 +12,6 @@
 namespace qblk {
 namespace {
 
-struct half4 {
-  f16 x, y, z, w;
-};
-
 __global__ __launch_bounds__(256) void cast_f16_kernel(int R, int C, const float* __restrict__ in, int64_t ldi,
                                                        f16* __restrict__ out, int64_t ldo,
                                                        f16* __restrict__ outT, int64_t ldt) {
@@ -31,8 +27,7 @@ __global__ __launch_bounds__(256) void cast_f16_kernel(int R, int C, const float
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (row < R && col < C) v = *(const float4*)(in + (int64_t)row * ldi + col);
     if (out && row < R && col < C) {
-      half4 h{(f16)v.x, (f16)v.y, (f16)v.z, (f16)v.w};
-      *(half4*)(out + (int64_t)row * ldo + col) = h;
+      *(half4*)(out + (int64_t)row * ldo + col) = to_half4(v);
     }
     tile[lr][lc] = v.x;
     tile[lr][lc + 1] = v.y;
@@ -51,8 +46,7 @@ __global__ __launch_bounds__(256) void cast_f16_kernel(int R, int C, const float
     if (c >= C) continue;
     f16* dst = outT + (int64_t)c * ldt + row;
     if (row + 3 < R) {
-      half4 h{(f16)tile[lr][lcc], (f16)tile[lr + 1][lcc], (f16)tile[lr + 2][lcc], (f16)tile[lr + 3][lcc]};
-      *(half4*)dst = h;
+      *(half4*)dst = to_half4(make_float4(tile[lr][lcc], tile[lr + 1][lcc], tile[lr + 2][lcc], tile[lr + 3][lcc]));
     } else {
       for (int j = 0; j < 4 && row + j < R; ++j) dst[j] = (f16)tile[lr + j][lcc];
     }

@@ -62,4 +62,23 @@ __device__ __forceinline__ half4 to_half4(float4 v) {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// ------------------------------------------- direct global -> LDS copies
+// global_load_lds_dwordx4: each lane reads 16 bytes at its own global
+// address; the wave's 64 results land contiguously (lane order) at one
+// wave-uniform LDS address. Completion is counted by vmcnt.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 }  // namespace qblk

@@ -715,8 +715,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmDesc d, con
 // so that the MFMA reads of 16 consecutive rows at one logical chunk (one
 // 256-byte LDS cycle of ds_read_b128) hit 16 different bank groups. Rows
 // past M (or N) load a clamped, valid row; those results are never stored.
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 
 // One LDS stage as its own __shared__ object: stages are distinct objects,
 // so the compiler knows a copy into one cannot alias reads of another and
@@ -725,14 +723,6 @@ template <int TAG, int ELEMS>
 __device__ __forceinline__ f16* lds_stage() {
   __shared__ __attribute__((aligned(16))) f16 buf[ELEMS];
   return buf;
-}
-
-// s_waitcnt with only the vector-memory count limited (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <int BM, int BN, int WM, int WN, int NS>

@@ -178,6 +178,45 @@ def test_attention(shape):
     check("dv", dv, dv_ref, tol)
 
 
+ATTN16_SHAPES = [  # batch, seq, heads, kv_heads, head_dim: fp16 copies, direct-to-LDS tiles
+    (1, 32, 4, 2, 64),
+    (2, 96, 4, 1, 64),      # G = 4, several tiles per sequence
+    (1, 144, 8, 2, 128),    # ragged last tile (144 = 4.5 tiles)
+    (3, 40, 8, 8, 128),     # G = 1, ragged, batch > 1
+    (1, 512, 32, 8, 128),   # the Qwen3-4B-shaped attention
+]
+
+
+@pytest.mark.parametrize("shape", ATTN16_SHAPES)
+def test_attention_f16(shape):
+    """The fp16 kernels take fp16 copies; the oracle gets the same fp16
+    values widened to float64. P and dS are rounded to fp16 inside, so the
+    fp16-operand tolerance applies."""
+    need_gpu()
+    B, S, H, KV, D = shape
+    announce(f"attention16 batch={B} seq={S} heads={H} kv={KV} d={D}")
+    rng = np.random.default_rng(S * H + D + 1)
+    T = B * S
+    q, k, v, do = (rng.standard_normal((T, n * D)).astype(np.float16) for n in (H, KV, KV, H))
+    q64, k64, v64, do64 = (x.astype(np.float64) for x in (q, k, v, do))
+    t16 = lambda x: dev(np.ascontiguousarray(x.T))
+    o, lse = empty((T, H * D)), empty(B * H * S)
+    qblk.attention_forward_f16(B, S, H, KV, D, dev(q), dev(k), t16(v), o, lse)
+    o_ref = ops.attention_fwd(q64, k64, v64, B, S, H, KV, D)
+    torch.cuda.synchronize()
+    check("o", o, o_ref, FP16_TOL)
+    dq, dk, dv = empty((T, H * D)), empty((T, KV * D)), empty((T, KV * D))
+    scratch = byte_buffer(qblk.attention_workspace_size(B, S, H))
+    # dO in fp32 for the row term; its fp16 copies for the products
+    qblk.attention_backward_f16(B, S, H, KV, D, dev(q), t16(q), dev(k), t16(k), dev(v), o, lse, dev(do), t16(do),
+                                dev(do.astype(np.float32)), dq, dk, dv, scratch)
+    dq_ref, dk_ref, dv_ref = ops.attention_bwd(q64, k64, v64, do64, B, S, H, KV, D)
+    torch.cuda.synchronize()
+    check("dq", dq, dq_ref, FP16_TOL)
+    check("dk", dk, dk_ref, FP16_TOL)
+    check("dv", dv, dv_ref, FP16_TOL)
+
+
 def test_nf4_quantize_bit_exact():
     need_gpu()
     announce("nf4 quantize")
