@@ -63,42 +63,45 @@ def timed(fn, steps, warmup, torch):
 
 
 def block_gemms(c):
-    """(M, N, K, accumulate) of every GEMM launch of one block forward +
-    backward as the block entry points issue them on the fp16 path: all NT
-    with fp16 operands (activations and their transposes cast by the block,
-    weights from the packed fp16 set); accumulate stands in for the
-    residual read of the O-projection and down epilogues."""
+    """(layout, M, N, K, accumulate) of every GEMM launch of one block
+    forward + backward as the block entry points issue them on the fp16
+    path: fp16 operands throughout (activation copies written by their
+    producers, weights from the packed fp16 set); forward NT, dX NN, dW TN;
+    accumulate stands in for the residual read of the O-projection and
+    down epilogues."""
     T, h, q, kv, I = c.tokens, c.hidden, c.q_dim, c.kv_dim, c.intermediate
     qkv = q + 2 * kv
     return [
-        (T, qkv, h, 0), (T, h, q, 1), (T, 2 * I, h, 0), (T, h, I, 1),   # forward
-        (T, I, h, 0), (h, I, T, 0),                                     # down: dX, dW
-        (T, h, 2 * I, 0), (2 * I, h, T, 0),                             # gate/up
-        (T, q, h, 0), (h, q, T, 0),                                     # o
-        (T, h, qkv, 0), (qkv, h, T, 0),                                 # qkv
+        (0, T, qkv, h, 0), (0, T, h, q, 1), (0, T, 2 * I, h, 0), (0, T, h, I, 1),   # forward
+        (1, T, I, h, 0), (2, h, I, T, 0),                                         # down: dX, dW
+        (1, T, h, 2 * I, 0), (2, 2 * I, h, T, 0),                                 # gate/up
+        (1, T, q, h, 0), (2, h, q, T, 0),                                         # o
+        (1, T, h, qkv, 0), (2, qkv, h, T, 0),                                     # qkv
     ]
 
 
 def gemm_roofline(c, torch, qblk, reps):
-    """Replay the step's GEMMs (same kernels, shapes and operand types as
-    the block), each bracketed by HIP events on the current stream, the
-    stream the launches go to; achieved TFLOP/s over summed durations."""
+    """Replay the step's GEMMs (same kernels, shapes, layouts and operand
+    types as the block), each bracketed by HIP events on the current stream,
+    the stream the launches go to; achieved TFLOP/s over summed durations."""
     specs = block_gemms(c)
     bufs = []
-    for (M, N, K, acc) in specs:
-        A = (torch.randn((M, K), device="cuda") * 0.02).half()
-        B = torch.randn((N, K), device="cuda").half()
+    for (lay, M, N, K, acc) in specs:
+        a_shape = (M, K) if lay in (0, 1) else (K, M)
+        b_shape = (N, K) if lay == 0 else (K, N)
+        A = (torch.randn(a_shape, device="cuda") * 0.02).half()
+        B = torch.randn(b_shape, device="cuda").half()
         C = torch.zeros((M, N), device="cuda")
-        bufs.append((M, N, K, acc, A, B, C))
-    flops = sum(2.0 * M * N * K for (M, N, K, _) in specs)
-    ws = max(qblk.gemm_workspace_size(0, 1, M, N, K) for (M, N, K, _) in specs)
+        bufs.append((lay, M, N, K, acc, A, a_shape[1], B, b_shape[1], C))
+    flops = sum(2.0 * M * N * K for (_, M, N, K, _) in specs)
+    ws = max(qblk.gemm_workspace_size(lay, 1, M, N, K) for (lay, M, N, K, _) in specs)
     scratch = torch.empty(max(ws, 16), dtype=torch.uint8, device="cuda")
 
     def run_all(events=None):
-        for i, (M, N, K, acc, A, B, C) in enumerate(bufs):
+        for i, (lay, M, N, K, acc, A, lda, B, ldb, C) in enumerate(bufs):
             if events:
                 events[i][0].record()
-            qblk.gemm(0, 1, M, N, K, A, K, B, K, C, N, acc, scratch=scratch)
+            qblk.gemm(lay, 1, M, N, K, A, lda, B, ldb, C, N, acc, scratch=scratch)
             if events:
                 events[i][1].record()
 
@@ -118,7 +121,7 @@ def gemm_roofline(c, torch, qblk, reps):
     return {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK, "unit": "TFLOP/s",
         "frac": round(achieved / MFMA_F16_PEAK, 4), "traffic": None,
-        "kernel": "gemm_nt16_kernel (the 12 GEMM launches of one block fwd+bwd, split-K reduce included)",
+        "kernel": "gemm_dma_kernel (the 12 GEMM launches of one block fwd+bwd, split-K reduce included)",
         "flops_per_step": flops, "gemm_ms_per_step": round(step_ms, 4),
         "avg_launch_us": round(1e3 * step_ms / len(bufs), 2),
         "per_launch_us": [round(1e3 * x / reps, 1) for x in per],

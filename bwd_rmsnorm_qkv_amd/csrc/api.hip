@@ -63,7 +63,7 @@ int32_t qblk_block_pack_f16(const qblk_config* cfg, const qblk_block_params* p, 
   carve_pack16(*cfg, nullptr, pk, need);
   if (packed_bytes < need) return fail(QBLK_EINVAL, "block_pack_f16: buffer %zu < %zu", packed_bytes, need);
   carve_pack16(*cfg, packed, pk, need);
-  return pack16(*cfg, *p, pk, true, true, S(stream));
+  return pack16(*cfg, *p, pk, S(stream));
 }
 
 int32_t qblk_block_forward(const qblk_config* cfg, const qblk_block_params* p, const float* x, float* y,

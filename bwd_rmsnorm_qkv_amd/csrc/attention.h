@@ -39,6 +39,7 @@ struct Attn16Args {
   const f16 *q, *k, *v;    int64_t ldq, ldk, ldv;
   const f16 *qT, *kT, *vT; int64_t ldt;
   float* o; int64_t ldo;   // fp32 [T, heads*d]
+  f16* o16;                // optional fp16 copy of o (same stride), may be NULL
   float* lse;              // [batch, heads, seq], natural log
   // backward only
   const f16 *d_o, *doT; int64_t lddo;

@@ -708,13 +708,16 @@ __global__ __launch_bounds__(512) void attn16_fwd_kernel(const Attn16Args a) {
 
   if (qi < S) {
     const float inv = 1.0f / l;
-    float* orow = a.o + (tok0 + qi) * a.ldo + (int64_t)h * D + 4 * kh;
+    const int64_t ooff = (tok0 + qi) * a.ldo + (int64_t)h * D + 4 * kh;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(float4*)(orow + db * 32 + 8 * g) =
+      for (int g = 0; g < 4; ++g) {
+        const float4 v =
             make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+        *(float4*)(a.o + ooff + db * 32 + 8 * g) = v;
+        if (a.o16) *(half4*)(a.o16 + ooff + db * 32 + 8 * g) = to_half4(v);
+      }
     if (kh == 0) a.lse[((int64_t)b * a.heads + h) * S + qi] = (m + log2f(l)) * kLn2;
   }
 }

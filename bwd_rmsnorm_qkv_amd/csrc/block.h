@@ -28,23 +28,23 @@ struct Saved {
   // fp16-operand attention (when attention16_supported): fp16 copies of the
   // attention inputs, row-major and transposed; NULL otherwise.
   f16 *q16, *qT16, *k16, *kT16, *v16, *vT16;
+  // fp16 copies of the projection inputs n1, o, n2, s (fp16-operand configs
+  // with T a multiple of 8), written by their producers; NULL otherwise.
+  f16 *n1_16, *o16, *n2_16, *s16;
 };
 
 // The fp16 attention kernels apply to this config.
 bool use_attention16(const qblk_config& c);
 
-// fp16 copies of the dense block's projection weights, as every fp16
-// contraction reads them: W [out, in] for the forward (x W^T) and W^T
-// [in, out] for dX = dY W. [Wq; Wk; Wv] and [Wg; Wu] are stored stacked.
+// fp16 copies of the dense block's projection weights W [out, in], read
+// K-major by the forward (x W^T) and out-major by dX = dY W; [Wq; Wk; Wv]
+// and [Wg; Wu] are stored stacked.
 struct Packed16 {
-  f16 *qkv, *o, *gu, *d;      // [qkv, h], [h, qd], [2I, h], [h, I]
-  f16 *qkvT, *oT, *guT, *dT;  // [h, qkv], [qd, h], [h, 2I], [I, h]
+  f16 *qkv, *o, *gu, *d;  // [qkv, h], [h, qd], [2I, h], [h, I]
 };
 void carve_pack16(const qblk_config& c, void* base, Packed16& p, size_t& bytes);
-// Casts (round to nearest even) the weights of p into `out`: the forward
-// copies when fwd, the transposed ones when bwd.
-int pack16(const qblk_config& c, const qblk_block_params& p, const Packed16& out, bool fwd, bool bwd,
-           hipStream_t st);
+// Casts (round to nearest even) the weights of p into `out`.
+int pack16(const qblk_config& c, const qblk_block_params& p, const Packed16& out, hipStream_t st);
 
 // Backward temporaries (caller-owned `scratch`).
 struct Scratch {
@@ -55,7 +55,7 @@ struct Scratch {
   size_t gemm_ws_bytes;
   // fp16-operand dense block only: operand copies and, when the caller
   // passes no packed weights, the weights' fp16 copies.
-  f16 *a16, *aT16, *bT16;
+  f16* a16;  // fp16 copy of the current output gradient
   Packed16 pack;
   f16 *do16, *doT16;  // fp16 attention: dO copies (NULL otherwise)
 };

@@ -56,6 +56,13 @@ void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes) {
   s.n2 = cv.take<float>(T * h);
   s.gu = cv.take<float>(T * 2 * I);
   s.s = cv.take<float>(T * I);
+  s.n1_16 = s.o16 = s.n2_16 = s.s16 = nullptr;
+  if (c.gemm_precision == 1 && T % 8 == 0) {
+    s.n1_16 = cv.take<f16>(T * h);
+    s.o16 = cv.take<f16>(T * qd);
+    s.n2_16 = cv.take<f16>(T * h);
+    s.s16 = cv.take<f16>(T * I);
+  }
   s.q16 = s.qT16 = s.k16 = s.kT16 = s.v16 = s.vT16 = nullptr;
   if (use_attention16(c)) {
     s.q16 = cv.take<f16>(T * qd);
@@ -123,7 +130,7 @@ void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes, 
   s.red = cv.take<float>(red / sizeof(float) + 1);
   s.gemm_ws_bytes = block_gemm_ws(c, lora_rank);
   s.gemm_ws = cv.take<float>(s.gemm_ws_bytes / sizeof(float) + 1);
-  s.a16 = s.aT16 = s.bT16 = nullptr;
+  s.a16 = nullptr;
   s.pack = Packed16{};
   s.do16 = s.doT16 = nullptr;
   if (use_attention16(c)) {
@@ -131,10 +138,7 @@ void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes, 
     s.doT16 = cv.take<f16>(T * qd);
   }
   if (c.gemm_precision == 1 && lora_rank == 0) {
-    const size_t wide = std::max({qd + 2 * kvd, 2 * I, h, qd});
-    s.a16 = cv.take<f16>(T * wide);
-    s.aT16 = cv.take<f16>(T * wide);
-    s.bT16 = cv.take<f16>(T * std::max({h, I, qd}));
+    s.a16 = cv.take<f16>(T * std::max({qd + 2 * kvd, 2 * I, h, qd}));
     size_t pb = 0;
     carve_pack16(c, nullptr, s.pack, pb);
     char* pbase = cv.take<char>(pb);
@@ -152,28 +156,22 @@ void carve_pack16(const qblk_config& c, void* base, Packed16& p, size_t& bytes) 
   p.o = cv.take<f16>(h * qd);
   p.gu = cv.take<f16>(2 * I * h);
   p.d = cv.take<f16>(h * I);
-  p.qkvT = cv.take<f16>(h * qkv);
-  p.oT = cv.take<f16>(qd * h);
-  p.guT = cv.take<f16>(h * 2 * I);
-  p.dT = cv.take<f16>(I * h);
   bytes = cv.off;
 }
 
-int pack16(const qblk_config& c, const qblk_block_params& p, const Packed16& o, bool fwd, bool bwd,
-           hipStream_t st) {
+int pack16(const qblk_config& c, const qblk_block_params& p, const Packed16& o, hipStream_t st) {
   const int h = c.hidden, d = c.head_dim;
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
-  const int qkv = qd + 2 * kvd;
-  auto one = [&](int rows, int cols, const float* w, f16* out, f16* outT, int ldt) {
-    return cast_f16(rows, cols, w, cols, fwd ? out : nullptr, cols, bwd ? outT : nullptr, ldt, st);
+  auto one = [&](int rows, int cols, const float* w, f16* out) {
+    return cast_f16(rows, cols, w, cols, out, cols, nullptr, 0, st);
   };
-  QBLK_TRY(one(qd, h, p.w_q, o.qkv, o.qkvT, qkv));
-  QBLK_TRY(one(kvd, h, p.w_k, o.qkv + (size_t)qd * h, o.qkvT + qd, qkv));
-  QBLK_TRY(one(kvd, h, p.w_v, o.qkv + (size_t)(qd + kvd) * h, o.qkvT + qd + kvd, qkv));
-  QBLK_TRY(one(h, qd, p.w_o, o.o, o.oT, h));
-  QBLK_TRY(one(I, h, p.w_gate, o.gu, o.guT, 2 * I));
-  QBLK_TRY(one(I, h, p.w_up, o.gu + (size_t)I * h, o.guT + I, 2 * I));
-  QBLK_TRY(one(h, I, p.w_down, o.d, o.dT, h));
+  QBLK_TRY(one(qd, h, p.w_q, o.qkv));
+  QBLK_TRY(one(kvd, h, p.w_k, o.qkv + (size_t)qd * h));
+  QBLK_TRY(one(kvd, h, p.w_v, o.qkv + (size_t)(qd + kvd) * h));
+  QBLK_TRY(one(h, qd, p.w_o, o.o));
+  QBLK_TRY(one(I, h, p.w_gate, o.gu));
+  QBLK_TRY(one(I, h, p.w_up, o.gu + (size_t)I * h));
+  QBLK_TRY(one(h, I, p.w_down, o.d));
   return QBLK_OK;
 }
 
@@ -226,7 +224,7 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
   const int ldqkv = qd + 2 * kvd;
 
   QBLK_TRY(rope_table(c.seq, d, c.rope_theta, s.tab, st));
-  QBLK_TRY(rmsnorm_forward(T, h, c.eps, x, nullptr, g_in, s.n1, nullptr, nullptr, s.rho1, st));
+  QBLK_TRY(rmsnorm_forward(T, h, c.eps, x, nullptr, g_in, s.n1, s.n1_16, nullptr, s.rho1, st));
   QBLK_TRY(proj.qkv(s.n1, s.qkv, st));
   QkRopeArgs qa{T, c.seq, c.heads, c.kv_heads, d, c.qk_norm, c.eps, s.qkv, ldqkv, g_q, g_k, s.tab,
                 s.qr, s.kr, s.rho_q, s.rho_k};
@@ -235,7 +233,9 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
     QBLK_TRY(cast_f16(T, qd, s.qr, qd, s.q16, qd, s.qT16, T, st));
     QBLK_TRY(cast_f16(T, kvd, s.kr, kvd, s.k16, kvd, s.kT16, T, st));
     QBLK_TRY(cast_f16(T, kvd, s.qkv + qd + kvd, ldqkv, s.v16, kvd, s.vT16, T, st));
-    QBLK_TRY(attention16_forward(attn16_args(c, s), st));
+    Attn16Args af = attn16_args(c, s);
+    af.o16 = s.o16;
+    QBLK_TRY(attention16_forward(af, st));
   } else {
     AttnArgs aa{};
     aa.batch = c.batch; aa.seq = c.seq; aa.heads = c.heads; aa.kv_heads = c.kv_heads; aa.head_dim = d;
@@ -245,11 +245,12 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
     aa.o = s.o; aa.ldo = qd;
     aa.lse = s.lse;
     QBLK_TRY(attention_forward(aa, prec_of(c), st));
+    if (s.o16) QBLK_TRY(cast_f16(T, qd, s.o, qd, s.o16, qd, nullptr, 0, st));
   }
   QBLK_TRY(proj.o(s.o, x, s.r1, st));  // r1 = x + o Wo^T
-  QBLK_TRY(rmsnorm_forward(T, h, c.eps, s.r1, nullptr, g_post, s.n2, nullptr, nullptr, s.rho2, st));
+  QBLK_TRY(rmsnorm_forward(T, h, c.eps, s.r1, nullptr, g_post, s.n2, s.n2_16, nullptr, s.rho2, st));
   QBLK_TRY(proj.gate_up(s.n2, s.gu, st));
-  QBLK_TRY(swiglu_forward(T, I, s.gu, s.s, nullptr, st));
+  QBLK_TRY(swiglu_forward(T, I, s.gu, s.s, s.s16, st));
   QBLK_TRY(proj.down(s.s, s.r1, y, st));  // y = r1 + s Wd^T
   return QBLK_OK;
 }
@@ -329,95 +330,94 @@ Seg seg3(const void* a, int na, const void* b, int nb, const void* cc, int nc) {
   return s;
 }
 
-// Both operands fp16 and K-contiguous (the layout the direct-to-LDS GEMM
-// kernel takes); `b` is a stacked fp16 weight or activation copy.
-GemmDesc nt16(const Scratch& w, int M, int N, int K, const f16* a, int64_t lda, const f16* b, int64_t ldb,
-              Seg c, int64_t ldc) {
+// Both operands fp16 (the direct-to-LDS GEMM kernel's operands).
+GemmDesc g16(const Scratch& w, Layout l, int M, int N, int K, const f16* a, int64_t lda, const f16* b,
+             int64_t ldb, Seg c, int64_t ldc) {
   GemmDesc g;
   g.ws = w.gemm_ws;
   g.ws_bytes = w.gemm_ws_bytes;
-  g.layout = Layout::NT;
+  g.layout = l;
   g.prec = Prec::F16;
   g.M = M; g.N = N; g.K = K;
   g.a = a; g.lda = lda; g.a_src = Src::F16;
-  g.b = seg1(b, N); g.ldb = ldb; g.b_src = Src::F16;
+  g.b = seg1(b, l == Layout::NT ? N : K); g.ldb = ldb; g.b_src = Src::F16;
   g.c = c; g.ldc = ldc;
   return g;
 }
 
-// The fp16 copies path needs fp16 leading dimensions (T for the transposed
-// activations) that are multiples of 8.
+// The fp16 copies path needs fp16 row strides (T for the transposed
+// attention copies) that are multiples of 8.
 bool use_f16_copies(const qblk_config& c) {
   return c.gemm_precision == 1 && (c.seq * c.batch) % 8 == 0;
 }
 
 // The weights' fp16 copies: the caller's packed set, or cast into scratch.
-int weights16(const qblk_config& c, const qblk_block_params& p, const Scratch& w, bool fwd, Packed16& W,
-              hipStream_t st) {
+int weights16(const qblk_config& c, const qblk_block_params& p, const Scratch& w, Packed16& W, hipStream_t st) {
   if (p.w16) {
     size_t b = 0;
     carve_pack16(c, (void*)p.w16, W, b);
     return QBLK_OK;
   }
   W = w.pack;
-  return pack16(c, p, W, fwd, !fwd, st);
+  return pack16(c, p, W, st);
 }
 
+// Forward products read the fp16 copies the producers wrote into `saved`
+// (n1, o, n2, s) and the weights' fp16 copies: y (+ res) = act16 W16^T.
 int dense16_forward(const qblk_config& c, const qblk_block_params& p, const float* x, float* y, const Saved& s,
                     const Scratch& w, hipStream_t st) {
   const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate, qkv = qd + 2 * kvd;
   Packed16 W;
-  QBLK_TRY(weights16(c, p, w, true, W, st));
-  // y_out (+ res) = act W^T with act cast to fp16 first.
-  auto proj = [&](const float* act, int n_in, const f16* wt, int n_out, const float* res, float* out,
+  QBLK_TRY(weights16(c, p, w, W, st));
+  auto proj = [&](const f16* act, int n_in, const f16* wt, int n_out, const float* res, float* out,
                   hipStream_t s_) -> int {
-    QBLK_TRY(cast_f16(T, n_in, act, n_in, w.a16, n_in, nullptr, 0, s_));
-    GemmDesc g = nt16(w, T, n_out, n_in, w.a16, n_in, wt, n_in, seg1(out, T), n_out);
+    GemmDesc g = g16(w, Layout::NT, T, n_out, n_in, act, n_in, wt, n_in, seg1(out, T), n_out);
     g.r = res; g.ldr = n_out;
     return gemm(g, s_);
   };
   ProjFwd pf;
-  pf.qkv = [&](const float* n1, float* out, hipStream_t s_) { return proj(n1, h, W.qkv, qkv, nullptr, out, s_); };
-  pf.o = [&](const float* o, const float* res, float* out, hipStream_t s_) {
-    return proj(o, qd, W.o, h, res, out, s_);
+  pf.qkv = [&](const float*, float* out, hipStream_t s_) { return proj(s.n1_16, h, W.qkv, qkv, nullptr, out, s_); };
+  pf.o = [&](const float*, const float* res, float* out, hipStream_t s_) {
+    return proj(s.o16, qd, W.o, h, res, out, s_);
   };
-  pf.gate_up = [&](const float* n2, float* out, hipStream_t s_) { return proj(n2, h, W.gu, 2 * I, nullptr, out, s_); };
-  pf.down = [&](const float* sv, const float* res, float* out, hipStream_t s_) {
-    return proj(sv, I, W.d, h, res, out, s_);
+  pf.gate_up = [&](const float*, float* out, hipStream_t s_) {
+    return proj(s.n2_16, h, W.gu, 2 * I, nullptr, out, s_);
+  };
+  pf.down = [&](const float*, const float* res, float* out, hipStream_t s_) {
+    return proj(s.s16, I, W.d, h, res, out, s_);
   };
   return block_forward_impl(c, pf, p.g_in, p.g_post, p.g_q, p.g_k, x, y, s, st);
 }
 
+// dX = dY W (NN: dY16 [T, n_out] K-major, W16 [n_out, n_in] read out-major)
+// and dW = dY^T X (TN: dY16 and the saved X16 [T, n_in], both read
+// token-major); dY is cast to fp16 once for both.
 int dense16_backward(const qblk_config& c, const qblk_block_params& p, const qblk_block_grads& gr,
                      const float* x, const float* dy, const Saved& s, float* dx, const Scratch& w,
                      hipStream_t st) {
   const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate, qkv = qd + 2 * kvd;
   Packed16 W;
-  QBLK_TRY(weights16(c, p, w, false, W, st));
-  // dX = dY W as dY [T, n_out] times (W^T [n_in, n_out])^T, and
-  // dW = dY^T X as (dY^T [n_out, T]) times (X^T [n_in, T])^T: both NT with
-  // fp16 copies made here.
-  auto dxdw = [&](const float* dyv, int n_out, const float* xin, int n_in, const f16* wT, Seg cseg, float* dxo,
+  QBLK_TRY(weights16(c, p, w, W, st));
+  auto dxdw = [&](const float* dyv, int n_out, const f16* x16, int n_in, const f16* wt, Seg cseg, float* dxo,
                   hipStream_t s_) -> int {
-    QBLK_TRY(cast_f16(T, n_out, dyv, n_out, w.a16, n_out, w.aT16, T, s_));
-    QBLK_TRY(cast_f16(T, n_in, xin, n_in, nullptr, 0, w.bT16, T, s_));
-    QBLK_TRY(gemm(nt16(w, T, n_in, n_out, w.a16, n_out, wT, n_out, seg1(dxo, T), n_in), s_));
-    return gemm(nt16(w, n_out, n_in, T, w.aT16, T, w.bT16, T, cseg, n_in), s_);
+    QBLK_TRY(cast_f16(T, n_out, dyv, n_out, w.a16, n_out, nullptr, 0, s_));
+    QBLK_TRY(gemm(g16(w, Layout::NN, T, n_in, n_out, w.a16, n_out, wt, n_in, seg1(dxo, T), n_in), s_));
+    return gemm(g16(w, Layout::TN, n_out, n_in, T, w.a16, n_out, x16, n_in, cseg, n_in), s_);
   };
   ProjBwd pb;
-  pb.down = [&](const float* dyv, const float* sv, float* ds, hipStream_t s_) {
-    return dxdw(dyv, h, sv, I, W.dT, seg1(gr.w_down, h), ds, s_);
+  pb.down = [&](const float* dyv, const float*, float* ds, hipStream_t s_) {
+    return dxdw(dyv, h, s.s16, I, W.d, seg1(gr.w_down, h), ds, s_);
   };
-  pb.gate_up = [&](const float* dgu, const float* n2, float* dn2, hipStream_t s_) {
-    return dxdw(dgu, 2 * I, n2, h, W.guT, seg3(gr.w_gate, I, gr.w_up, I, nullptr, 0), dn2, s_);
+  pb.gate_up = [&](const float* dgu, const float*, float* dn2, hipStream_t s_) {
+    return dxdw(dgu, 2 * I, s.n2_16, h, W.gu, seg3(gr.w_gate, I, gr.w_up, I, nullptr, 0), dn2, s_);
   };
-  pb.o = [&](const float* dr1, const float* o, float* d_o, hipStream_t s_) {
-    return dxdw(dr1, h, o, qd, W.oT, seg1(gr.w_o, h), d_o, s_);
+  pb.o = [&](const float* dr1, const float*, float* d_o, hipStream_t s_) {
+    return dxdw(dr1, h, s.o16, qd, W.o, seg1(gr.w_o, h), d_o, s_);
   };
-  pb.qkv = [&](const float* dqkv, const float* n1, float* dn1, hipStream_t s_) {
-    return dxdw(dqkv, qkv, n1, h, W.qkvT, seg3(gr.w_q, qd, gr.w_k, kvd, gr.w_v, kvd), dn1, s_);
+  pb.qkv = [&](const float* dqkv, const float*, float* dn1, hipStream_t s_) {
+    return dxdw(dqkv, qkv, s.n1_16, h, W.qkv, seg3(gr.w_q, qd, gr.w_k, kvd, gr.w_v, kvd), dn1, s_);
   };
   return block_backward_impl(c, pb, p.g_in, p.g_post, p.g_q, p.g_k, x, dy, s, dx, gr.g_in, gr.g_post,
                              gr.g_q, gr.g_k, w, st);

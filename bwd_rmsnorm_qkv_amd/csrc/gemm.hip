@@ -703,18 +703,25 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmDesc d, con
       }
 }
 
-// ------------------------------------------- fp16 NT fast path (LDS DMA)
+// --------------------------------------- fp16 fast path (direct LDS DMA)
 //
-// C = A B^T with A [M, K] and B [N, K] both fp16, K-contiguous, K a multiple
-// of 64. Tiles move global -> LDS with global_load_lds_dwordx4 (16 bytes per
-// lane straight into LDS: no registers, no conversion) into a ring of NS
-// LDS stages, so the copies of the next NS-1 K tiles overlap the MFMAs of
-// the current one. An LDS row is 64 halves (128 bytes) with no padding, so
-// two rows span the 64 four-byte banks; the eight 16-byte chunks of a row
-// are stored XOR-swizzled (physical chunk = logical chunk ^ ((row >> 1) & 7))
-// so that the MFMA reads of 16 consecutive rows at one logical chunk (one
-// 256-byte LDS cycle of ds_read_b128) hit 16 different bank groups. Rows
-// past M (or N) load a clamped, valid row; those results are never stored.
+// Both operands fp16 in storage, K a multiple of 64, any of the three
+// layouts. Tiles move global -> LDS with global_load_lds_dwordx4 (16 bytes
+// per lane straight into LDS: no registers, no conversion) into a ring of
+// NS LDS stages, so the copies of the next NS-1 K tiles overlap the MFMAs
+// of the current one. Each operand tile is a plain copy of its storage:
+//
+// * K-major (A of NT/NN, B of NT): BM rows x 64 halves, 128-byte rows;
+//   16-byte chunks XOR-swizzled by (row >> 1) & 7, so the ds_read_b128 of
+//   16 consecutive rows at one chunk hit 16 different bank groups.
+// * MN-major (A of TN, B of NN/TN): 64 K-rows x BM halves; chunks swizzled
+//   by (row & 3) << 2. The MFMA operand (8 consecutive K of one row m) is
+//   gathered by two ds_read_b64_tr_b16: within each 16-lane group, output
+//   lane j takes element k from the lane 4k + j/4 that read 4 consecutive
+//   m at K-row k, so lane j ends up with 4 consecutive K of column j.
+//
+// Rows (or columns) past M or N read a clamped, valid address; their
+// results are never stored.
 
 // One LDS stage as its own __shared__ object: stages are distinct objects,
 // so the compiler knows a copy into one cannot alias reads of another and
@@ -725,15 +732,93 @@ __device__ __forceinline__ f16* lds_stage() {
   return buf;
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_nt16_kernel(const GemmDesc d, const Grid gd) {
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// One operand of the DMA kernel: R rows of the tile (BM or BN), K-major or
+// MN-major, copied by NW waves.
+template <int R, bool KMAJ, int NW>
+struct DmaOperand {
+  static constexpr int BK = 64;
+  static constexpr int J = R / 8 / NW;  // 1 KB wave copies per stage per wave
+  static_assert(J * 8 * NW == R, "DMA split");
+  const f16* p[J];
+
+  // Wave w's copy j fills the 1 KB at tile + 512 (NW j + w) halves.
+  // K-major: 8 rows x 128 B; MN-major: 1024 / (2R) K-rows x 2R bytes.
+  __device__ __forceinline__ void init(const f16* base, int64_t ld, int r0, int rmax, int64_t kb, int lane, int w,
+                                       const Seg* seg) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int blk = NW * j + w;
+      if constexpr (KMAJ) {
+        const int rsub = lane >> 3;
+        const int lc = (lane & 7) ^ (((blk & 1) << 2) | (rsub >> 1));
+        const int r = min(r0 + 8 * blk + rsub, rmax - 1);
+        if (seg) {
+          const int sg = seg_of(*seg, r);
+          p[j] = (const f16*)seg->p[sg] + (int64_t)(r - seg->start[sg]) * ld + kb + lc * 8;
+        } else {
+          p[j] = base + (int64_t)r * ld + kb + lc * 8;
+        }
+      } else {
+        constexpr int CPR = R / 8;         // 16-byte chunks per K-row
+        constexpr int RPI = 64 / CPR;      // K-rows per wave copy
+        const int krow = blk * RPI + lane / CPR;
+        const int lc = (lane % CPR) ^ ((krow & 3) << 2);
+        const int col = min(r0 + lc * 8, rmax - 8);
+        p[j] = base + (kb + krow) * ld + col;
+      }
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, f16* tile, int64_t ld, int w) const {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int64_t adv = KMAJ ? (int64_t)kt * BK : (int64_t)kt * BK * ld;
+      dma16(p[j] + adv, tile + 512 * (NW * j + w));
+    }
+  }
+  // Per-lane element offset of the K-major fragment of K step s within a
+  // 32-row block (the swizzle of row rb + i equals that of i, rb being a
+  // multiple of 32): computed once so each read is one base + immediate.
+  static __device__ __forceinline__ int koff(int s, int lane) {
+    const int i = lane & 31, kh = lane >> 5;
+    return i * BK + (((2 * s + kh) ^ ((i >> 1) & 7)) << 3);
+  }
+  // MFMA operand for K step s (16 K) of the 32-row block starting at tile
+  // row (K-major) or column (MN-major) rb: lane (i, kh) gets rows rb + i,
+  // K = 16 s + 8 kh + 0..7. `ko` is koff(s, lane) (K-major only).
+  static __device__ __forceinline__ half8 frag(const f16* tile, int rb, int s, int lane, int ko) {
+    if constexpr (KMAJ) {
+      return *(const half8*)(tile + rb * BK + ko);
+    } else {
+      const int sl = lane & 15, q1 = (lane >> 4) & 1, kh = lane >> 5;
+      const int col = rb + 16 * q1 + 4 * (sl & 3);
+      const int cpart = col & 7;
+      half8 out;
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int krow = 16 * s + 8 * kh + 4 * rr + (sl >> 2);
+        const int ch = (col >> 3) ^ ((krow & 3) << 2);
+        const f16* addr = tile + krow * R + ch * 8 + cpart;
+        const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)addr);
+        const half4 h = __builtin_bit_cast(half4, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[4 * rr + e] = h[e];
+      }
+      return out;
+    }
+  }
+};
+
+template <int BM, int BN, int WM, int WN, int NS, bool AK, bool BK_>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d, const Grid gd) {
   constexpr int BK = 64;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "tile");
-  constexpr int JA = BM / 8 / NW, JB = BN / 8 / NW;  // DMA instructions per wave per stage
-  static_assert(JA * 8 * NW == BM && JB * 8 * NW == BN, "DMA split");
-  constexpr int JS = JA + JB;
+  using OA = DmaOperand<BM, AK, NW>;
+  using OB = DmaOperand<BN, BK_, NW>;
+  constexpr int JS = OA::J + OB::J;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w % WM, wn = w / WM;
@@ -750,37 +835,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt16_kernel(const GemmDesc d
   const int ke = min(d.K, kb + gd.kchunk);
   const int nkt = ke > kb ? (ke - kb) / BK : 0;
 
-  // DMA instruction j of wave w fills tile rows 8 blk .. 8 blk + 7 with
-  // blk = NW j + w; lane l writes physical chunk l & 7 of row 8 blk + (l >> 3),
-  // which holds logical chunk (l & 7) ^ (((blk & 1) << 2) | (l >> 4)).
-  const int rsub = lane >> 3;
-  auto lchunk = [&](int blk) { return (lane & 7) ^ (((blk & 1) << 2) | (rsub >> 1)); };
-  const f16* pa[JA];
-  const f16* pb[JB];
-#pragma unroll
-  for (int j = 0; j < JA; ++j) {
-    const int blk = NW * j + w;
-    const int r = min(m0 + 8 * blk + rsub, d.M - 1);
-    pa[j] = (const f16*)d.a + (int64_t)r * d.lda + kb + lchunk(blk) * 8;
-  }
-#pragma unroll
-  for (int j = 0; j < JB; ++j) {
-    const int blk = NW * j + w;
-    const int n = min(n0 + 8 * blk + rsub, d.N - 1);
-    const int sg = seg_of(d.b, n);
-    pb[j] = (const f16*)d.b.p[sg] + (int64_t)(n - d.b.start[sg]) * d.ldb + kb + lchunk(blk) * 8;
-  }
-  auto issue = [&](int kt, f16* sa, f16* sb) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int j = 0; j < JA; ++j)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(pa[j] + k0), (lds_void_t*)(sa + 8 * (NW * j + w) * BK), 16, 0, 0);
-#pragma unroll
-    for (int j = 0; j < JB; ++j)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(pb[j] + k0), (lds_void_t*)(sb + 8 * (NW * j + w) * BK), 16, 0, 0);
-  };
+  OA oa;
+  OB ob;
+  oa.init((const f16*)d.a, d.lda, m0, d.M, kb, lane, w, nullptr);
+  ob.init((const f16*)d.b.p[0], d.ldb, n0, d.N, kb, lane, w, BK_ ? &d.b : nullptr);
 
-  const int i = lane & 31, kh = lane >> 5, sw = (i >> 1) & 7;
   floatx16 acc[TM][TN];
 #pragma unroll
   for (int a = 0; a < TM; ++a)
@@ -789,20 +848,18 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt16_kernel(const GemmDesc d
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-#ifndef QBLK_NT16_PIPE
-#define QBLK_NT16_PIPE 1
-#endif
   // The fragments of K step s+1 are read from LDS while the MFMAs of step s
-  // run; sched_group_barrier pins that interleave (left alone, the
-  // scheduler reads each step's fragments right before its MFMAs and waits).
-  auto compute = [&](const f16* sa, const f16* sb) {
+  // run; sched_group_barrier pins that interleave.
+  int ko[BK / 16];
+#pragma unroll
+  for (int s = 0; s < BK / 16; ++s) ko[s] = OA::koff(s, lane);
+  auto compute = [&](const f16* sa, const f16* sb) __attribute__((always_inline)) {
     half8 av[2][TM], bv[2][TN];
-    auto frag = [&](int s, half8* a, half8* b) {
-      const int pc = ((2 * s + kh) ^ sw) * 8;
+    auto frag = [&](int s, half8* a, half8* b) __attribute__((always_inline)) {
 #pragma unroll
-      for (int t = 0; t < TM; ++t) a[t] = *(const half8*)(sa + (wm * TM * 32 + t * 32 + i) * BK + pc);
+      for (int t = 0; t < TM; ++t) a[t] = OA::frag(sa, wm * TM * 32 + t * 32, s, lane, ko[s]);
 #pragma unroll
-      for (int t = 0; t < TN; ++t) b[t] = *(const half8*)(sb + (wn * TN * 32 + t * 32 + i) * BK + pc);
+      for (int t = 0; t < TN; ++t) b[t] = OB::frag(sb, wn * TN * 32 + t * 32, s, lane, ko[s]);
     };
     frag(0, av[0], bv[0]);
 #pragma unroll
@@ -813,19 +870,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt16_kernel(const GemmDesc d
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[s & 1][tm], bv[s & 1][tn], acc[tm][tn], 0, 0, 0);
-#if QBLK_NT16_PIPE
       if (s + 1 < BK / 16) {
-        // reads of step s+1 spread between the MFMAs of step s
+        constexpr int NR = (AK ? TM : 2 * TM) + (BK_ ? TN : 2 * TN);  // LDS reads per step
 #pragma unroll
-        for (int q = 0; q < TM + TN; ++q) {
+        for (int q = 0; q < NR; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (q < TM * TN) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
-        if constexpr (TM * TN > TM + TN) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - TM - TN, 0);
+        if constexpr (TM * TN > NR) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - NR, 0);
       } else {
         __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
       }
-#endif
     }
   };
 
@@ -835,6 +890,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt16_kernel(const GemmDesc d
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
+  auto issue = [&](int kt, f16* sa, f16* sb) __attribute__((always_inline)) {
+    oa.issue(kt, sa, d.lda, w);
+    ob.issue(kt, sb, d.ldb, w);
+  };
 
   // Prologue: tiles 0 .. NS-2 in flight.
   if (0 < nkt) issue(0, stA(I0{}), stB(I0{}));
@@ -845,7 +904,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt16_kernel(const GemmDesc d
   // may stay in flight), barrier (every wave's copies of tile kt landed and
   // every wave is done with tile kt-1), refill the stage of tile kt-1 with
   // tile kt+NS-1, then the MFMAs of tile kt.
-  auto step = [&](auto S, int kt) {
+  auto step = [&](auto S, int kt) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
     if (kt + NS - 2 < nkt) wait_vmcnt<JS * (NS - 2)>();
     else wait_vmcnt<0>();
@@ -871,7 +930,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt16_kernel(const GemmDesc d
   if constexpr (NS > 2) if (left > 1) step(I1{}, nfull + 1);
   if constexpr (NS > 3) if (left > 2) step(I2{}, nfull + 2);
 
-  const int ii = lane & 31;
+  const int ii = lane & 31, kh = lane >> 5;
   if (gd.splits > 1) {
     float* part = d.ws + (int64_t)sp * d.M * d.N;
 #pragma unroll
@@ -971,21 +1030,29 @@ Grid plan_tiles(const GemmDesc& d, size_t ws_bytes, int bm, int bn, int bk) {
 }
 
 template <int BM, int BN, int WM, int WN, int NS>
-struct Nt16Cfg {
+struct DmaCfg {
   static constexpr int bm = BM, bn = BN, threads = WM * WN * 64;
+  template <bool AK, bool BKM>
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
-    hipLaunchKernelGGL((gemm_nt16_kernel<BM, BN, WM, WN, NS>), dim3(nwg), dim3(threads), 0, st, d, g);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, AK, BKM>), dim3(nwg), dim3(threads), 0, st, d, g);
+  }
+  static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
+    switch (d.layout) {
+      case Layout::NT: launch<true, true>(d, g, st); break;
+      case Layout::NN: launch<true, false>(d, g, st); break;
+      case Layout::TN: launch<false, false>(d, g, st); break;
+    }
   }
 };
 #ifdef QBLK_NT16_CFG  // one forced configuration (tuning builds)
-using Nt16Small = Nt16Cfg<QBLK_NT16_CFG>;
+using Nt16Small = DmaCfg<QBLK_NT16_CFG>;
 using Nt16Big = Nt16Small;
 #else
 // 128 x 128 tiles, 4 waves, two workgroups per CU (64 KB LDS each); and
 // 256 x 256 tiles, 8 waves of 64 x 128, one workgroup per CU (128 KB LDS).
-using Nt16Small = Nt16Cfg<128, 128, 2, 2, 2>;
-using Nt16Big = Nt16Cfg<256, 256, 4, 2, 2>;
+using Nt16Small = DmaCfg<128, 128, 2, 2, 2>;
+using Nt16Big = DmaCfg<256, 256, 4, 2, 2>;
 #endif
 
 // Big tiles pay off once they alone give at least half the CUs a tile.
@@ -993,20 +1060,23 @@ bool nt16_big(const GemmDesc& d) {
   return ceil_div(d.M, Nt16Big::bm) * ceil_div(d.N, Nt16Big::bn) >= 128;
 }
 
-// The fp16 NT DMA kernel applies when both operands are fp16 in storage,
-// K-contiguous with 16-byte aligned rows, K is a whole number of 64-wide
-// tiles and nothing extends the contraction.
+// The DMA kernel applies when both operands are fp16 in storage with
+// 16-byte aligned rows, K is a whole number of 64-wide tiles, nothing
+// extends the contraction, an MN-major operand has M (or N) a multiple of 8
+// and is a single segment.
 bool nt16_ok(const GemmDesc& d) {
 #ifdef QBLK_NO_NT16
   (void)d;
   return false;
 #else
-  if (d.layout != Layout::NT || d.prec != Prec::F16) return false;
-  if (d.a_src != Src::F16 || d.b_src != Src::F16 || d.ext.kext > 0) return false;
+  if (d.prec != Prec::F16) return false;
+  if (d.a_src != Src::F16 || d.b_src != Src::F16 || d.ext.kext > 0 || d.b_src == Src::NF4) return false;
   if (d.K % 64 != 0 || d.lda % 8 != 0 || d.ldb % 8 != 0) return false;
   if ((uintptr_t)d.a % 16 != 0) return false;
   for (int s = 0; s < d.b.nseg; ++s)
     if ((uintptr_t)d.b.p[s] % 16 != 0) return false;
+  if (d.layout == Layout::TN && (d.M % 8 != 0 || d.M < 8)) return false;
+  if (d.layout != Layout::NT && (d.N % 8 != 0 || d.N < 8 || d.b.nseg != 1)) return false;
   return true;
 #endif
 }
@@ -1035,7 +1105,7 @@ int launch_nt16(const GemmDesc& d, hipStream_t st) {
   const Grid g = plan(d, d.ws ? d.ws_bytes : 0);
   if (nt16_big(d)) Nt16Big::launch(d, g, st);
   else Nt16Small::launch(d, g, st);
-  QBLK_TRY(check_launch("gemm_nt16_kernel"));
+  QBLK_TRY(check_launch("gemm_dma_kernel"));
   return finish_splits(d, g, st);
 }
 
