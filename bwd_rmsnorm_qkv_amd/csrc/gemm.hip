@@ -848,11 +848,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  // The fragments of K step s+1 are read from LDS while the MFMAs of step s
-  // run; sched_group_barrier pins that interleave.
   int ko[BK / 16];
 #pragma unroll
   for (int s = 0; s < BK / 16; ++s) ko[s] = OA::koff(s, lane);
+  // The fragments of K step s+1 are read from LDS (into the other register
+  // set) before the MFMAs of step s; scheduling fences keep the two phases
+  // apart, so every MFMA's operands were requested a whole phase earlier
+  // (left to itself the scheduler pairs each read with the MFMA that
+  // consumes it and waits on the LDS latency every time).
   auto compute = [&](const f16* sa, const f16* sb) __attribute__((always_inline)) {
     half8 av[2][TM], bv[2][TN];
     auto frag = [&](int s, half8* a, half8* b) __attribute__((always_inline)) {
@@ -865,22 +868,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       if (s + 1 < BK / 16) frag(s + 1, av[(s + 1) & 1], bv[(s + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[s & 1][tm], bv[s & 1][tn], acc[tm][tn], 0, 0, 0);
-      if (s + 1 < BK / 16) {
-        constexpr int NR = (AK ? TM : 2 * TM) + (BK_ ? TN : 2 * TN);  // LDS reads per step
-#pragma unroll
-        for (int q = 0; q < NR; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          if (q < TM * TN) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
-        if constexpr (TM * TN > NR) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - NR, 0);
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
