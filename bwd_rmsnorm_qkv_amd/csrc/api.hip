@@ -348,8 +348,8 @@ int32_t qblk_attention_forward(int32_t batch, int32_t seq, int32_t heads, int32_
   return attention_forward(a, precision ? Prec::F16 : Prec::F32, S(stream));
 }
 
-static Attn16Args attn16_dense(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads, int32_t head_dim) {
-  Attn16Args a{};
+static AttnDmaArgs attn16_dense(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads, int32_t head_dim) {
+  AttnDmaArgs a{};
   a.batch = batch; a.seq = seq; a.heads = heads; a.kv_heads = kv_heads; a.head_dim = head_dim;
   a.ldq = (int64_t)heads * head_dim;
   a.ldk = a.ldv = (int64_t)kv_heads * head_dim;
@@ -362,10 +362,10 @@ static Attn16Args attn16_dense(int32_t batch, int32_t seq, int32_t heads, int32_
 int32_t qblk_attention_forward_f16(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads, int32_t head_dim,
                                    const void* q16, const void* k16, const void* vT16, float* o, float* lse,
                                    qblk_stream_t stream) {
-  Attn16Args a = attn16_dense(batch, seq, heads, kv_heads, head_dim);
-  a.q = (const f16*)q16; a.k = (const f16*)k16; a.vT = (const f16*)vT16;
+  AttnDmaArgs a = attn16_dense(batch, seq, heads, kv_heads, head_dim);
+  a.q = q16; a.k = k16; a.vT = vT16;
   a.o = o; a.lse = lse;
-  return attention16_forward(a, S(stream));
+  return attention_dma_forward(a, S(stream));
 }
 
 int32_t qblk_attention_backward_f16(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads,
@@ -377,13 +377,13 @@ int32_t qblk_attention_backward_f16(int32_t batch, int32_t seq, int32_t heads, i
   QBLK_TRY(attention_check(batch, seq, heads, kv_heads, head_dim));
   if (scratch_bytes < attention_bwd_scratch(batch, seq, heads, head_dim))
     return fail(QBLK_EINVAL, "attention_backward_f16: scratch too small");
-  Attn16Args a = attn16_dense(batch, seq, heads, kv_heads, head_dim);
-  a.q = (const f16*)q16; a.qT = (const f16*)qT16; a.k = (const f16*)k16; a.kT = (const f16*)kT16;
-  a.v = (const f16*)v16; a.vT = (const f16*)kT16;  // the backward never reads vT
+  AttnDmaArgs a = attn16_dense(batch, seq, heads, kv_heads, head_dim);
+  a.q = q16; a.qT = qT16; a.k = k16; a.kT = kT16;
+  a.v = v16; a.vT = kT16;  // the backward never reads vT
   a.o = (float*)o; a.lse = (float*)lse;
-  a.d_o = (const f16*)do16; a.doT = (const f16*)doT16; a.do32 = do32;
+  a.d_o = do16; a.doT = doT16; a.do32 = do32;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  return attention16_backward(a, scratch, S(stream));
+  return attention_dma_backward(a, scratch, S(stream));
 }
 
 int32_t qblk_attention_workspace_size(int32_t batch, int32_t seq, int32_t heads, size_t* scratch_bytes) {

@@ -29,29 +29,31 @@ int attention_backward(const AttnArgs& a, Prec p, void* scratch, hipStream_t st)
 
 namespace qblk {
 
-// fp16-operand attention on fp16 copies of its inputs (head_dim 64 or 128,
-// seq a multiple of 8): q, k, v row-major [T, heads*d] / [T, kv_heads*d]
-// and the transposed copies qT [heads*d, T], kT, vT [kv_heads*d, T],
-// d_o [T, heads*d], doT [heads*d, T] (row stride ldt = T for the transposed
-// ones). Every tile reaches LDS by direct global -> LDS copies.
-struct Attn16Args {
+// Attention on tiled copies (head_dim 64 or 128, seq a multiple of 8): the
+// operands are fp16 copies (fp32 = 0) or fp32 tensors (fp32 = 1): q, k, v
+// row-major [T, heads*d] / [T, kv_heads*d] and the transposed copies
+// qT [heads*d, T], kT, vT [kv_heads*d, T], d_o [T, heads*d], doT
+// [heads*d, T] (row stride ldt = T for the transposed ones). Every tile
+// reaches LDS by direct global -> LDS copies.
+struct AttnDmaArgs {
   int batch, seq, heads, kv_heads, head_dim;
-  const f16 *q, *k, *v;    int64_t ldq, ldk, ldv;
-  const f16 *qT, *kT, *vT; int64_t ldt;
+  int fp32;
+  const void *q, *k, *v;    int64_t ldq, ldk, ldv;
+  const void *qT, *kT, *vT; int64_t ldt;
   float* o; int64_t ldo;   // fp32 [T, heads*d]
   f16* o16;                // optional fp16 copy of o (same stride), may be NULL
   float* lse;              // [batch, heads, seq], natural log
   // backward only
-  const f16 *d_o, *doT; int64_t lddo;
+  const void *d_o, *doT; int64_t lddo;
   const float* do32; int64_t lddo32;  // fp32 dO (for delta = rowsum(dO o))
   float* dq; int64_t lddq;
   float* dk; int64_t lddk;
   float* dv; int64_t lddv;
 };
 
-bool attention16_supported(int batch, int seq, int heads, int kv_heads, int head_dim);
-int attention16_forward(const Attn16Args& a, hipStream_t st);
+bool attention_dma_supported(int batch, int seq, int heads, int kv_heads, int head_dim);
+int attention_dma_forward(const AttnDmaArgs& a, hipStream_t st);
 // scratch: attention_bwd_scratch bytes.
-int attention16_backward(const Attn16Args& a, void* scratch, hipStream_t st);
+int attention_dma_backward(const AttnDmaArgs& a, void* scratch, hipStream_t st);
 
 }  // namespace qblk

@@ -513,65 +513,111 @@ int bwd_launch(const AttnArgs& a, float* delta, float* dk_part, float* dv_part, 
 }
 
 // ====================================================================
-// fp16 copies + direct global -> LDS tiles (head_dim 64 / 128)
+// Direct global -> LDS tiles (head_dim 64 / 128; fp16 or fp32 elements)
 //
 // Same orientations as above; what changes is how tiles reach LDS and how
 // P (or dS) becomes an MFMA operand. Every tile is a plain copy of a 32-row
-// slab of an fp16 matrix: row tiles [32][D] from the row-major copies and
-// transposed tiles [D][32] from the transposed ones, so no thread converts
-// or transposes anything and the copies run as global_load_lds_dwordx4
-// (1 KB per wave instruction) into two LDS stages. For the products whose
-// contraction runs over the 32 keys (or queries) of an accumulator, the
-// lane halves trade four packed values with v_permlane32_swap so that each
-// lane holds 8 consecutive keys, the natural order of the transposed tile.
+// slab of a matrix: row tiles [32][D] from the row-major inputs and
+// transposed tiles [D][32] from transposed copies, so no thread converts or
+// transposes anything and the copies run as global_load_lds_dwordx4 (1 KB
+// per wave instruction) into two LDS stages.
+//
+// A lane reads the 16-byte logical chunk 2c + (lane / 32) of its row for
+// contraction step c, both for LDS tiles and for the operands it keeps in
+// registers, so A and B agree on which K each MFMA lane carries:
+// * fp16 (v_mfma_f32_32x32x16_f16): one chunk = 8 halves = one MFMA;
+// * fp32 (v_mfma_f32_32x32x2f32): one chunk = 4 floats = four MFMAs.
+// For the products contracting over the 32 keys (or queries) held in an
+// accumulator (rows 8g + 4(lane/32) + r): in fp32 the accumulator value
+// 4g + r is directly the B operand of the MFMA pairing key 8g + r (lanes
+// 0-31) with key 8g + 4 + r (lanes 32-63), and the A operand is the float4
+// at chunk 2g + kh of the transposed tile. In fp16 the lane halves trade
+// four packed values with v_permlane32_swap so that each lane holds 8
+// consecutive keys, the natural order of the transposed tile.
 
-// Row tile: 32 rows x D halves, rows unpadded, 16-byte chunks XOR-swizzled
-// so that 16 consecutive rows read at one chunk hit distinct bank groups.
-template <int D>
+template <typename T>
+struct AttnElem;
+template <>
+struct AttnElem<f16> {
+  using Chunk = half8;
+  static constexpr int EPC = 8;  // elements per 16-byte chunk
+  static __device__ __forceinline__ floatx16 mma(Chunk a, Chunk b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct AttnElem<float> {
+  using Chunk = float4;
+  static constexpr int EPC = 4;
+  static __device__ __forceinline__ floatx16 mma(Chunk a, Chunk b, floatx16 c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, c, 0, 0, 0);
+    return c;
+  }
+};
+
+// Row tile: 32 rows x D elements, rows unpadded, 16-byte chunks
+// XOR-swizzled so that 16 consecutive rows read at one chunk hit distinct
+// bank groups of the 256-byte LDS cycle.
+template <typename T, int D>
 struct RowTile {
-  static constexpr int NCH = D / 8;     // 16-byte chunks per row
-  static constexpr int RPI = 64 / NCH;  // rows per 1 KB wave copy
-  static constexpr int NI = 32 / RPI;   // wave copies per tile
-  static __device__ __forceinline__ int sw(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
-  static __device__ __forceinline__ half8 read(const f16* t, int row, int lc) {
-    return *(const half8*)(t + row * D + ((lc ^ sw(row)) << 3));
+  static constexpr int NCH = D * (int)sizeof(T) / 16;  // chunks per row
+  static constexpr int RPI = 64 / NCH;                 // rows per 1 KB wave copy
+  static constexpr int NI = 32 / RPI;                  // wave copies per tile
+  static constexpr int STEPS = NCH / 2;                // contraction steps over D
+  static constexpr int ELEMS = 32 * D;
+  static __device__ __forceinline__ int sw(int row) { return NCH >= 16 ? (row & 15) : ((row >> 1) & 7); }
+  static __device__ __forceinline__ typename AttnElem<T>::Chunk read(const T* t, int row, int lc) {
+    return *(const typename AttnElem<T>::Chunk*)(t + row * D + ((lc ^ sw(row)) * AttnElem<T>::EPC));
   }
 };
 
-// Transposed tile: D rows x 32 halves (64 bytes), 4 chunks per row, swizzled
-// over groups of 4 rows.
-template <int D>
+// Transposed tile: D rows x 32 elements (64 or 128 bytes per row).
+template <typename T, int D>
 struct TrTile {
-  static constexpr int NI = D / 16;  // 16 rows per 1 KB wave copy
-  static __device__ __forceinline__ int sw(int row) { return (row >> 2) & 3; }
-  static __device__ __forceinline__ half8 read(const f16* t, int row, int lc) {
-    return *(const half8*)(t + row * 32 + ((lc ^ sw(row)) << 3));
+  static constexpr int NCH = 32 * (int)sizeof(T) / 16;  // 4 (fp16) or 8 (fp32)
+  static constexpr int RPI = 64 / NCH;                  // 16 or 8 rows per wave copy
+  static constexpr int NI = D / RPI;
+  static constexpr int ELEMS = D * 32;
+  static __device__ __forceinline__ int sw(int row) { return NCH == 4 ? ((row >> 2) & 3) : ((row >> 1) & 7); }
+  static __device__ __forceinline__ typename AttnElem<T>::Chunk read(const T* t, int row, int lc) {
+    return *(const typename AttnElem<T>::Chunk*)(t + row * 32 + ((lc ^ sw(row)) * AttnElem<T>::EPC));
   }
 };
 
-// Wave copy j of a row tile: rows r0 .. r0+31 of a [T, *] fp16 matrix
+// Wave copy j of a row tile: rows r0 .. r0+31 of a [T, *] matrix
 // (sequence-local rows past S clamp to S-1), columns col0 .. col0+D-1.
-template <int D>
-__device__ __forceinline__ void copy_rows(f16* tile, int j, int lane, const f16* base, int64_t ld, int64_t tok0,
+template <typename T, int D>
+__device__ __forceinline__ void copy_rows(T* tile, int j, int lane, const T* base, int64_t ld, int64_t tok0,
                                           int r0, int S, int col0) {
-  using RT = RowTile<D>;
+  using RT = RowTile<T, D>;
   const int row = j * RT::RPI + lane / RT::NCH;
   const int lc = (lane % RT::NCH) ^ RT::sw(row);
-  dma16(base + (tok0 + min(r0 + row, S - 1)) * ld + col0 + lc * 8, tile + j * 512);
+  dma16(base + (tok0 + min(r0 + row, S - 1)) * ld + col0 + lc * AttnElem<T>::EPC, tile + j * (1024 / sizeof(T)));
 }
 
-// Wave copy j of a transposed tile: rows row0 .. row0+D-1 of a [*, T] fp16
-// matrix, columns tok0 + c0 .. +31 (8-column chunks past S read chunk 0;
-// they are masked).
-template <int D>
-__device__ __forceinline__ void copy_tr(f16* tile, int j, int lane, const f16* base, int64_t ldt, int64_t tok0,
+// Wave copy j of a transposed tile: rows row0 .. row0+D-1 of a [*, T]
+// matrix, columns tok0 + c0 .. +31 (chunks past S read chunk 0 of the
+// sequence; they are masked).
+template <typename T, int D>
+__device__ __forceinline__ void copy_tr(T* tile, int j, int lane, const T* base, int64_t ldt, int64_t tok0,
                                         int c0, int S, int row0) {
-  using TT = TrTile<D>;
-  const int row = j * 16 + (lane >> 2);
-  const int lc = (lane & 3) ^ TT::sw(row);
-  int c = c0 + lc * 8;
+  using TT = TrTile<T, D>;
+  const int row = j * TT::RPI + lane / TT::NCH;
+  const int lc = (lane % TT::NCH) ^ TT::sw(row);
+  int c = c0 + lc * AttnElem<T>::EPC;
   if (c >= S) c = 0;
-  dma16(base + (int64_t)(row0 + row) * ldt + tok0 + c, tile + j * 512);
+  dma16(base + (int64_t)(row0 + row) * ldt + tok0 + c, tile + j * (1024 / sizeof(T)));
+}
+
+// Register operand: chunk 2c + kh of a row.
+template <typename T, int D>
+__device__ __forceinline__ void load_row_frags(const T* row, int kh, typename AttnElem<T>::Chunk (&f)[RowTile<T, D>::STEPS]) {
+#pragma unroll
+  for (int c = 0; c < RowTile<T, D>::STEPS; ++c)
+    f[c] = *(const typename AttnElem<T>::Chunk*)(row + (2 * c + kh) * AttnElem<T>::EPC);
 }
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -584,8 +630,7 @@ __device__ __forceinline__ unsigned pack2(float a, float b) {
   return __builtin_bit_cast(unsigned, h);
 }
 
-// Accumulator values 8 s2 .. 8 s2 + 7 of a 32 x 32 accumulator, whose rows
-// (keys or queries) are 8g + 4(lane/32) + r, as the B operand of a product
+// fp16: accumulator values 8 s2 .. 8 s2 + 7 as the B operand of a product
 // contracting over rows 16 s2 .. 16 s2 + 15: after the swap, lane half kh
 // holds rows 16 s2 + 8 kh + j, j = 0..7, in order.
 __device__ __forceinline__ half8 acc_rows_operand(const floatx16& p, int s2) {
@@ -601,19 +646,51 @@ __device__ __forceinline__ half8 acc_rows_operand(const floatx16& p, int s2) {
   return __builtin_bit_cast(half8, u);
 }
 
+// out[db] += Xt^T-block times the 32 x 32 accumulator p, contracting over
+// the accumulator's rows; Xt is a transposed tile [D][32].
+template <typename T, int D>
+__device__ __forceinline__ void acc_rows_product(const T* Xt, const floatx16& p, int i, int kh,
+                                                 floatx16 (&out)[D / 32]) {
+  using TT = TrTile<T, D>;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const half8 bp = acc_rows_operand(p, s2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(TT::read(Xt, db * 32 + i, 2 * s2 + kh), bp, out[db], 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const float4 a = TT::read(Xt, db * 32 + i, 2 * g + kh);
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, p[4 * g + 0], out[db], 0, 0, 0);
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, p[4 * g + 1], out[db], 0, 0, 0);
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, p[4 * g + 2], out[db], 0, 0, 0);
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, p[4 * g + 3], out[db], 0, 0, 0);
+      }
+  }
+}
+
 using I0 = std::integral_constant<int, 0>;
 using I1 = std::integral_constant<int, 1>;
 
 // Forward: grid (q tiles, kv groups, batch), longest query tiles first; one
 // wave per query head of the group, K and V^T tiles shared through LDS.
-template <int D>
-__global__ __launch_bounds__(512) void attn16_fwd_kernel(const Attn16Args a) {
-  using RT = RowTile<D>;
-  using TT = TrTile<D>;
-  __shared__ __attribute__((aligned(16))) f16 sK0[32 * D];
-  __shared__ __attribute__((aligned(16))) f16 sK1[32 * D];
-  __shared__ __attribute__((aligned(16))) f16 sV0[D * 32];
-  __shared__ __attribute__((aligned(16))) f16 sV1[D * 32];
+template <typename T, int D>
+__global__ __launch_bounds__(512) void attn_dma_fwd_kernel(const AttnDmaArgs a) {
+  using RT = RowTile<T, D>;
+  using TT = TrTile<T, D>;
+  using E = AttnElem<T>;
+  __shared__ __attribute__((aligned(16))) T sK0[RT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sK1[RT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sV0[TT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sV1[TT::ELEMS];
+  const T* q = (const T*)a.q;
+  const T* k = (const T*)a.k;
+  const T* vT = (const T*)a.vT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, NW = blockDim.x >> 6;
   const int G = a.heads / a.kv_heads, grp = blockIdx.y, b = blockIdx.z;
   const int h = grp * G + w;
@@ -624,12 +701,8 @@ __global__ __launch_bounds__(512) void attn16_fwd_kernel(const Attn16Args a) {
   const float sc = kLog2e / sqrtf((float)D);
   const int qi = q0 + i;
 
-  half8 qc[D / 16];
-  {
-    const f16* row = a.q + (tok0 + min(qi, S - 1)) * a.ldq + (int64_t)h * D + 8 * kh;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) qc[c] = *(const half8*)(row + 16 * c);
-  }
+  typename E::Chunk qc[RT::STEPS];
+  load_row_frags<T, D>(q + (tok0 + min(qi, S - 1)) * a.ldq + (int64_t)h * D, kh, qc);
   floatx16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -638,20 +711,19 @@ __global__ __launch_bounds__(512) void attn16_fwd_kernel(const Attn16Args a) {
   float m = -INFINITY, l = 0.f;
   const int nkt = qt + 1;
 
-  auto issue = [&](int kt, f16* sk, f16* sv) __attribute__((always_inline)) {
+  auto issue = [&](int kt, T* sk, T* sv) __attribute__((always_inline)) {
     for (int j = w; j < RT::NI + TT::NI; j += NW) {
-      if (j < RT::NI) copy_rows<D>(sk, j, lane, a.k, a.ldk, tok0, kt * 32, S, grp * D);
-      else copy_tr<D>(sv, j - RT::NI, lane, a.vT, a.ldt, tok0, kt * 32, S, grp * D);
+      if (j < RT::NI) copy_rows<T, D>(sk, j, lane, k, a.ldk, tok0, kt * 32, S, grp * D);
+      else copy_tr<T, D>(sv, j - RT::NI, lane, vT, a.ldt, tok0, kt * 32, S, grp * D);
     }
   };
-  auto compute = [&](const f16* sk, const f16* sv, int kt) __attribute__((always_inline)) {
+  auto compute = [&](const T* sk, const T* sv, int kt) __attribute__((always_inline)) {
     const int kv0 = kt * 32;
     floatx16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(RT::read(sk, i, 2 * c + kh), qc[c], s, 0, 0, 0);
+    for (int c = 0; c < RT::STEPS; ++c) s = E::mma(RT::read(sk, i, 2 * c + kh), qc[c], s);
     float mx = -INFINITY;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -679,13 +751,7 @@ __global__ __launch_bounds__(512) void attn16_fwd_kernel(const Attn16Args a) {
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const half8 bp = acc_rows_operand(s, s2);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(TT::read(sv, db * 32 + i, 2 * s2 + kh), bp, o[db], 0, 0, 0);
-    }
+    acc_rows_product<T, D>(sv, s, i, kh, o);
   };
   auto step = [&](auto St, int kt) __attribute__((always_inline)) {
     constexpr int st = decltype(St)::value;
@@ -724,16 +790,22 @@ __global__ __launch_bounds__(512) void attn16_fwd_kernel(const Attn16Args a) {
 
 // dQ: grid (q tiles, kv groups, batch), one wave per query head; K, V and
 // K^T tiles shared through LDS.
-template <int D>
-__global__ __launch_bounds__(512) void attn16_dq_kernel(const Attn16Args a, const float* delta) {
-  using RT = RowTile<D>;
-  using TT = TrTile<D>;
-  __shared__ __attribute__((aligned(16))) f16 sK0[32 * D];
-  __shared__ __attribute__((aligned(16))) f16 sK1[32 * D];
-  __shared__ __attribute__((aligned(16))) f16 sV0[32 * D];
-  __shared__ __attribute__((aligned(16))) f16 sV1[32 * D];
-  __shared__ __attribute__((aligned(16))) f16 sKt0[D * 32];
-  __shared__ __attribute__((aligned(16))) f16 sKt1[D * 32];
+template <typename T, int D>
+__global__ __launch_bounds__(512) void attn_dma_dq_kernel(const AttnDmaArgs a, const float* delta) {
+  using RT = RowTile<T, D>;
+  using TT = TrTile<T, D>;
+  using E = AttnElem<T>;
+  __shared__ __attribute__((aligned(16))) T sK0[RT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sK1[RT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sV0[RT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sV1[RT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sKt0[TT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sKt1[TT::ELEMS];
+  const T* q = (const T*)a.q;
+  const T* k = (const T*)a.k;
+  const T* v = (const T*)a.v;
+  const T* kT = (const T*)a.kT;
+  const T* d_o = (const T*)a.d_o;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, NW = blockDim.x >> 6;
   const int G = a.heads / a.kv_heads, grp = blockIdx.y, b = blockIdx.z;
   const int h = grp * G + w;
@@ -744,16 +816,9 @@ __global__ __launch_bounds__(512) void attn16_dq_kernel(const Attn16Args a, cons
   const float sc = kLog2e / sqrtf((float)D);
   const int qi = q0 + i, qc_i = min(qi, S - 1);
 
-  half8 qc[D / 16], dc[D / 16];
-  {
-    const f16* qrow = a.q + (tok0 + qc_i) * a.ldq + (int64_t)h * D + 8 * kh;
-    const f16* drow = a.d_o + (tok0 + qc_i) * a.lddo + (int64_t)h * D + 8 * kh;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      qc[c] = *(const half8*)(qrow + 16 * c);
-      dc[c] = *(const half8*)(drow + 16 * c);
-    }
-  }
+  typename E::Chunk qc[RT::STEPS], dc[RT::STEPS];
+  load_row_frags<T, D>(q + (tok0 + qc_i) * a.ldq + (int64_t)h * D, kh, qc);
+  load_row_frags<T, D>(d_o + (tok0 + qc_i) * a.lddo + (int64_t)h * D, kh, dc);
   const int64_t rowi = ((int64_t)b * a.heads + h) * S + qc_i;
   const float lse2 = a.lse[rowi] * kLog2e;
   const float dl = delta[rowi];
@@ -764,14 +829,14 @@ __global__ __launch_bounds__(512) void attn16_dq_kernel(const Attn16Args a, cons
     for (int e = 0; e < 16; ++e) dq[db][e] = 0.f;
   const int nkt = qt + 1;
 
-  auto issue = [&](int kt, f16* sk, f16* sv, f16* skt) __attribute__((always_inline)) {
+  auto issue = [&](int kt, T* sk, T* sv, T* skt) __attribute__((always_inline)) {
     for (int j = w; j < 2 * RT::NI + TT::NI; j += NW) {
-      if (j < RT::NI) copy_rows<D>(sk, j, lane, a.k, a.ldk, tok0, kt * 32, S, grp * D);
-      else if (j < 2 * RT::NI) copy_rows<D>(sv, j - RT::NI, lane, a.v, a.ldv, tok0, kt * 32, S, grp * D);
-      else copy_tr<D>(skt, j - 2 * RT::NI, lane, a.kT, a.ldt, tok0, kt * 32, S, grp * D);
+      if (j < RT::NI) copy_rows<T, D>(sk, j, lane, k, a.ldk, tok0, kt * 32, S, grp * D);
+      else if (j < 2 * RT::NI) copy_rows<T, D>(sv, j - RT::NI, lane, v, a.ldv, tok0, kt * 32, S, grp * D);
+      else copy_tr<T, D>(skt, j - 2 * RT::NI, lane, kT, a.ldt, tok0, kt * 32, S, grp * D);
     }
   };
-  auto compute = [&](const f16* sk, const f16* sv, const f16* skt, int kt) __attribute__((always_inline)) {
+  auto compute = [&](const T* sk, const T* sv, const T* skt, int kt) __attribute__((always_inline)) {
     const int kv0 = kt * 32;
     floatx16 s, dp;
 #pragma unroll
@@ -780,9 +845,9 @@ __global__ __launch_bounds__(512) void attn16_dq_kernel(const Attn16Args a, cons
       dp[e] = 0.f;
     }
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(RT::read(sk, i, 2 * c + kh), qc[c], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(RT::read(sv, i, 2 * c + kh), dc[c], dp, 0, 0, 0);
+    for (int c = 0; c < RT::STEPS; ++c) {
+      s = E::mma(RT::read(sk, i, 2 * c + kh), qc[c], s);
+      dp = E::mma(RT::read(sv, i, 2 * c + kh), dc[c], dp);
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -793,13 +858,7 @@ __global__ __launch_bounds__(512) void attn16_dq_kernel(const Attn16Args a, cons
         const float p = (kj > qi || kj >= S) ? 0.f : exp2f(s[e] * sc - lse2);
         s[e] = p * (dp[e] - dl);  // dS^T, unscaled
       }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const half8 bp = acc_rows_operand(s, s2);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(TT::read(skt, db * 32 + i, 2 * s2 + kh), bp, dq[db], 0, 0, 0);
-    }
+    acc_rows_product<T, D>(skt, s, i, kh, dq);
   };
   auto step = [&](auto St, int kt) __attribute__((always_inline)) {
     constexpr int st = decltype(St)::value;
@@ -835,19 +894,26 @@ __global__ __launch_bounds__(512) void attn16_dq_kernel(const Attn16Args a, cons
 // dK, dV per query head: grid (kv tiles, heads, batch), one wave; Q, dO,
 // Q^T and dO^T tiles through LDS. Results go to per-head partials
 // [T, heads, D], summed over each group in a fixed order afterwards.
-template <int D>
-__global__ __launch_bounds__(64) void attn16_dkv_kernel(const Attn16Args a, const float* delta, float* dk_part,
-                                                        float* dv_part) {
-  using RT = RowTile<D>;
-  using TT = TrTile<D>;
-  __shared__ __attribute__((aligned(16))) f16 sQ0[32 * D];
-  __shared__ __attribute__((aligned(16))) f16 sQ1[32 * D];
-  __shared__ __attribute__((aligned(16))) f16 sO0[32 * D];
-  __shared__ __attribute__((aligned(16))) f16 sO1[32 * D];
-  __shared__ __attribute__((aligned(16))) f16 sQt0[D * 32];
-  __shared__ __attribute__((aligned(16))) f16 sQt1[D * 32];
-  __shared__ __attribute__((aligned(16))) f16 sOt0[D * 32];
-  __shared__ __attribute__((aligned(16))) f16 sOt1[D * 32];
+template <typename T, int D>
+__global__ __launch_bounds__(64) void attn_dma_dkv_kernel(const AttnDmaArgs a, const float* delta,
+                                                          float* dk_part, float* dv_part) {
+  using RT = RowTile<T, D>;
+  using TT = TrTile<T, D>;
+  using E = AttnElem<T>;
+  __shared__ __attribute__((aligned(16))) T sQ0[RT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sQ1[RT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sO0[RT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sO1[RT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sQt0[TT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sQt1[TT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sOt0[TT::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sOt1[TT::ELEMS];
+  const T* q = (const T*)a.q;
+  const T* k = (const T*)a.k;
+  const T* v = (const T*)a.v;
+  const T* qT = (const T*)a.qT;
+  const T* d_o = (const T*)a.d_o;
+  const T* doT = (const T*)a.doT;
   const int lane = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int G = a.heads / a.kv_heads, grp = h / G;
   const int S = a.seq;
@@ -857,16 +923,11 @@ __global__ __launch_bounds__(64) void attn16_dkv_kernel(const Attn16Args a, cons
   const float sc = kLog2e / sqrtf((float)D);
   const int kj = kv0 + i;  // this lane's key (column of every accumulator)
 
-  half8 kc[D / 16], vc[D / 16];
+  typename E::Chunk kc[RT::STEPS], vc[RT::STEPS];
   {
     const int kr = min(kj, S - 1);
-    const f16* krow = a.k + (tok0 + kr) * a.ldk + (int64_t)grp * D + 8 * kh;
-    const f16* vrow = a.v + (tok0 + kr) * a.ldv + (int64_t)grp * D + 8 * kh;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      kc[c] = *(const half8*)(krow + 16 * c);
-      vc[c] = *(const half8*)(vrow + 16 * c);
-    }
+    load_row_frags<T, D>(k + (tok0 + kr) * a.ldk + (int64_t)grp * D, kh, kc);
+    load_row_frags<T, D>(v + (tok0 + kr) * a.ldv + (int64_t)grp * D, kh, vc);
   }
   floatx16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -880,20 +941,20 @@ __global__ __launch_bounds__(64) void attn16_dkv_kernel(const Attn16Args a, cons
   const float* lse_h = a.lse + ((int64_t)b * a.heads + h) * S;
   const float* dl_h = delta + ((int64_t)b * a.heads + h) * S;
 
-  auto issue = [&](int qt, f16* sq, f16* so, f16* sqt, f16* sot) __attribute__((always_inline)) {
+  auto issue = [&](int qt, T* sq, T* so, T* sqt, T* sot) __attribute__((always_inline)) {
     const int q0 = qt * 32;
 #pragma unroll
     for (int j = 0; j < RT::NI; ++j) {
-      copy_rows<D>(sq, j, lane, a.q, a.ldq, tok0, q0, S, h * D);
-      copy_rows<D>(so, j, lane, a.d_o, a.lddo, tok0, q0, S, h * D);
+      copy_rows<T, D>(sq, j, lane, q, a.ldq, tok0, q0, S, h * D);
+      copy_rows<T, D>(so, j, lane, d_o, a.lddo, tok0, q0, S, h * D);
     }
 #pragma unroll
     for (int j = 0; j < TT::NI; ++j) {
-      copy_tr<D>(sqt, j, lane, a.qT, a.ldt, tok0, q0, S, h * D);
-      copy_tr<D>(sot, j, lane, a.doT, a.ldt, tok0, q0, S, h * D);
+      copy_tr<T, D>(sqt, j, lane, qT, a.ldt, tok0, q0, S, h * D);
+      copy_tr<T, D>(sot, j, lane, doT, a.ldt, tok0, q0, S, h * D);
     }
   };
-  auto compute = [&](const f16* sq, const f16* so, const f16* sqt, const f16* sot, int qt) __attribute__((always_inline)) {
+  auto compute = [&](const T* sq, const T* so, const T* sqt, const T* sot, int qt) __attribute__((always_inline)) {
     const int q0 = qt * 32;
     // log-sum-exp and delta of this lane's 16 query rows q0 + 8g + 4kh + r
     float4 lq[4], dq4[4];
@@ -910,9 +971,9 @@ __global__ __launch_bounds__(64) void attn16_dkv_kernel(const Attn16Args a, cons
       dp[e] = 0.f;
     }
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(RT::read(sq, i, 2 * c + kh), kc[c], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(RT::read(so, i, 2 * c + kh), vc[c], dp, 0, 0, 0);
+    for (int c = 0; c < RT::STEPS; ++c) {
+      s = E::mma(RT::read(sq, i, 2 * c + kh), kc[c], s);
+      dp = E::mma(RT::read(so, i, 2 * c + kh), vc[c], dp);
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -926,16 +987,8 @@ __global__ __launch_bounds__(64) void attn16_dkv_kernel(const Attn16Args a, cons
         s[e] = p;
         dp[e] = p * (dp[e] - Dl);
       }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const half8 bp = acc_rows_operand(s, s2);
-      const half8 bd = acc_rows_operand(dp, s2);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(TT::read(sot, db * 32 + i, 2 * s2 + kh), bp, dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(TT::read(sqt, db * 32 + i, 2 * s2 + kh), bd, dk[db], 0, 0, 0);
-      }
-    }
+    acc_rows_product<T, D>(sot, s, i, kh, dv);   // dV^T += dO^T P
+    acc_rows_product<T, D>(sqt, dp, i, kh, dk);  // dK^T += Q^T dS
   };
   const int n = nqt - kt;  // query tiles kt .. nqt-1
   auto step = [&](auto St, int t) __attribute__((always_inline)) {
@@ -973,32 +1026,32 @@ __global__ __launch_bounds__(64) void attn16_dkv_kernel(const Attn16Args a, cons
   }
 }
 
-template <int D>
-int fwd16_launch(const Attn16Args& a, hipStream_t st) {
+template <typename T, int D>
+int fwd_dma_launch(const AttnDmaArgs& a, hipStream_t st) {
   const int G = a.heads / a.kv_heads;
   dim3 grid((unsigned)ceil_div(a.seq, 32), (unsigned)a.kv_heads, (unsigned)a.batch);
-  hipLaunchKernelGGL((attn16_fwd_kernel<D>), grid, dim3(64 * G), 0, st, a);
-  return check_launch("attn16_fwd_kernel");
+  hipLaunchKernelGGL((attn_dma_fwd_kernel<T, D>), grid, dim3(64 * G), 0, st, a);
+  return check_launch("attn_dma_fwd_kernel");
 }
 
-template <int D>
-int bwd16_launch(const Attn16Args& a, float* delta, float* dk_part, float* dv_part, hipStream_t st) {
+template <typename T, int D>
+int bwd_dma_launch(const AttnDmaArgs& a, float* delta, float* dk_part, float* dv_part, hipStream_t st) {
   const int G = a.heads / a.kv_heads;
-  const int64_t T = (int64_t)a.batch * a.seq;
+  const int64_t T_ = (int64_t)a.batch * a.seq;
   AttnArgs da{};
   da.batch = a.batch; da.seq = a.seq; da.heads = a.heads; da.kv_heads = a.kv_heads; da.head_dim = D;
   da.o = a.o; da.ldo = a.ldo;
   da.d_o = a.do32; da.lddo = a.lddo32;
-  hipLaunchKernelGGL(attn_delta_kernel, dim3((unsigned)ceil_div(T * a.heads, 4)), dim3(256), 0, st, da, delta);
+  hipLaunchKernelGGL(attn_delta_kernel, dim3((unsigned)ceil_div(T_ * a.heads, 4)), dim3(256), 0, st, da, delta);
   QBLK_TRY(check_launch("attn_delta_kernel"));
   dim3 gq((unsigned)ceil_div(a.seq, 32), (unsigned)a.kv_heads, (unsigned)a.batch);
-  hipLaunchKernelGGL((attn16_dq_kernel<D>), gq, dim3(64 * G), 0, st, a, (const float*)delta);
-  QBLK_TRY(check_launch("attn16_dq_kernel"));
+  hipLaunchKernelGGL((attn_dma_dq_kernel<T, D>), gq, dim3(64 * G), 0, st, a, (const float*)delta);
+  QBLK_TRY(check_launch("attn_dma_dq_kernel"));
   dim3 gk((unsigned)ceil_div(a.seq, 32), (unsigned)a.heads, (unsigned)a.batch);
-  hipLaunchKernelGGL((attn16_dkv_kernel<D>), gk, dim3(64), 0, st, a, (const float*)delta, dk_part, dv_part);
-  QBLK_TRY(check_launch("attn16_dkv_kernel"));
-  const int64_t n = T * a.kv_heads * D;
-  hipLaunchKernelGGL(attn_gqa_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, T, a.heads,
+  hipLaunchKernelGGL((attn_dma_dkv_kernel<T, D>), gk, dim3(64), 0, st, a, (const float*)delta, dk_part, dv_part);
+  QBLK_TRY(check_launch("attn_dma_dkv_kernel"));
+  const int64_t n = T_ * a.kv_heads * D;
+  hipLaunchKernelGGL(attn_gqa_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, T_, a.heads,
                      a.kv_heads, D, (const float*)dk_part, (const float*)dv_part, a.dk, a.lddk, a.dv, a.lddv);
   return check_launch("attn_gqa_reduce_kernel");
 }
@@ -1050,42 +1103,50 @@ int attention_backward(const AttnArgs& a, Prec p, void* scratch, hipStream_t st)
   return fail(QBLK_EUNSUPPORTED, "attention backward: fp32 needs head_dim <= 64");
 }
 
-bool attention16_supported(int batch, int seq, int heads, int kv_heads, int head_dim) {
+bool attention_dma_supported(int batch, int seq, int heads, int kv_heads, int head_dim) {
   return attention_check(batch, seq, heads, kv_heads, head_dim) == 0 && (head_dim == 64 || head_dim == 128) &&
          seq % 8 == 0;
 }
 
-static int check16(const Attn16Args& a) {
+static int check_dma(const AttnDmaArgs& a) {
   QBLK_TRY(attention_check(a.batch, a.seq, a.heads, a.kv_heads, a.head_dim));
-  if (!attention16_supported(a.batch, a.seq, a.heads, a.kv_heads, a.head_dim))
-    return fail(QBLK_EUNSUPPORTED, "attention16: head_dim must be 64 or 128 and seq a multiple of 8");
+  if (!attention_dma_supported(a.batch, a.seq, a.heads, a.kv_heads, a.head_dim))
+    return fail(QBLK_EUNSUPPORTED, "attention (tiled copies): head_dim must be 64 or 128 and seq a multiple of 8");
   const int64_t T = (int64_t)a.batch * a.seq;
   if (a.ldt != T || a.ldq % 8 || a.ldk % 8 || a.ldv % 8 || a.ldo % 4)
-    return fail(QBLK_EINVAL, "attention16: strides (ldt must be T; row strides multiples of 8)");
+    return fail(QBLK_EINVAL, "attention (tiled copies): strides (ldt must be T; row strides multiples of 8)");
   const void* ptrs[] = {a.q, a.k, a.vT, a.o, a.lse};
   for (const void* p : ptrs)
-    if (!p || ((uintptr_t)p & 15)) return fail(QBLK_EINVAL, "attention16: null or misaligned pointer");
+    if (!p || ((uintptr_t)p & 15)) return fail(QBLK_EINVAL, "attention (tiled copies): null or misaligned pointer");
   return 0;
 }
 
-int attention16_forward(const Attn16Args& a, hipStream_t st) {
-  QBLK_TRY(check16(a));
-  return a.head_dim == 64 ? fwd16_launch<64>(a, st) : fwd16_launch<128>(a, st);
+int attention_dma_forward(const AttnDmaArgs& a, hipStream_t st) {
+  QBLK_TRY(check_dma(a));
+  if (a.fp32) {
+    if (a.head_dim != 64) return fail(QBLK_EUNSUPPORTED, "attention (tiled copies): fp32 needs head_dim 64");
+    return fwd_dma_launch<float, 64>(a, st);
+  }
+  return a.head_dim == 64 ? fwd_dma_launch<f16, 64>(a, st) : fwd_dma_launch<f16, 128>(a, st);
 }
 
-int attention16_backward(const Attn16Args& a, void* scratch, hipStream_t st) {
-  QBLK_TRY(check16(a));
+int attention_dma_backward(const AttnDmaArgs& a, void* scratch, hipStream_t st) {
+  QBLK_TRY(check_dma(a));
   const void* ptrs[] = {a.v, a.qT, a.kT, a.d_o, a.doT, a.do32, a.dq, a.dk, a.dv, scratch};
   for (const void* p : ptrs)
-    if (!p || ((uintptr_t)p & 15)) return fail(QBLK_EINVAL, "attention16 backward: null or misaligned pointer");
+    if (!p || ((uintptr_t)p & 15)) return fail(QBLK_EINVAL, "attention backward (tiled copies): null or misaligned pointer");
   if (a.lddo % 8 || a.lddo32 % 4 || a.lddq % 4 || a.lddk % 4 || a.lddv % 4)
-    return fail(QBLK_EINVAL, "attention16 backward: row strides");
+    return fail(QBLK_EINVAL, "attention backward (tiled copies): row strides");
   const int64_t T = (int64_t)a.batch * a.seq;
   float* delta = (float*)scratch;
   float* dk_part = delta + T * a.heads;
   float* dv_part = dk_part + T * a.heads * a.head_dim;
-  return a.head_dim == 64 ? bwd16_launch<64>(a, delta, dk_part, dv_part, st)
-                          : bwd16_launch<128>(a, delta, dk_part, dv_part, st);
+  if (a.fp32) {
+    if (a.head_dim != 64) return fail(QBLK_EUNSUPPORTED, "attention backward (tiled copies): fp32 needs head_dim 64");
+    return bwd_dma_launch<float, 64>(a, delta, dk_part, dv_part, st);
+  }
+  return a.head_dim == 64 ? bwd_dma_launch<f16, 64>(a, delta, dk_part, dv_part, st)
+                          : bwd_dma_launch<f16, 128>(a, delta, dk_part, dv_part, st);
 }
 
 }  // namespace qblk

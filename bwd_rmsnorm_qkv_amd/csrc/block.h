@@ -25,16 +25,18 @@ struct Saved {
   float* n2;       // [T, h]
   float* gu;       // [T, 2I] gate | up
   float* s;        // [T, I] SwiGLU output
-  // fp16-operand attention (when attention16_supported): fp16 copies of the
-  // attention inputs, row-major and transposed; NULL otherwise.
+  // Attention on tiled copies (when use_attention_dma): fp16 copies of the
+  // attention inputs, row-major and transposed (fp16-operand configs), or
+  // fp32 transposed copies (fp32 configs); NULL otherwise.
   f16 *q16, *qT16, *k16, *kT16, *v16, *vT16;
+  float *qT32, *kT32, *vT32;
   // fp16 copies of the projection inputs n1, o, n2, s (fp16-operand configs
   // with T a multiple of 8), written by their producers; NULL otherwise.
   f16 *n1_16, *o16, *n2_16, *s16;
 };
 
-// The fp16 attention kernels apply to this config.
-bool use_attention16(const qblk_config& c);
+// The attention kernels on tiled copies apply to this config.
+bool use_attention_dma(const qblk_config& c);
 
 // fp16 copies of the dense block's projection weights W [out, in], read
 // K-major by the forward (x W^T) and out-major by dX = dY W; [Wq; Wk; Wv]
@@ -57,7 +59,8 @@ struct Scratch {
   // passes no packed weights, the weights' fp16 copies.
   f16* a16;  // fp16 copy of the current output gradient
   Packed16 pack;
-  f16 *do16, *doT16;  // fp16 attention: dO copies (NULL otherwise)
+  f16 *do16, *doT16;  // attention on tiled copies: dO copies (fp16 configs)
+  float* doT32;       // attention on tiled copies: dO transposed (fp32 configs)
 };
 
 void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes);

@@ -64,19 +64,25 @@ void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes) {
     s.s16 = cv.take<f16>(T * I);
   }
   s.q16 = s.qT16 = s.k16 = s.kT16 = s.v16 = s.vT16 = nullptr;
-  if (use_attention16(c)) {
+  s.qT32 = s.kT32 = s.vT32 = nullptr;
+  if (use_attention_dma(c) && c.gemm_precision == 1) {
     s.q16 = cv.take<f16>(T * qd);
     s.qT16 = cv.take<f16>(T * qd);
     s.k16 = cv.take<f16>(T * kvd);
     s.kT16 = cv.take<f16>(T * kvd);
     s.v16 = cv.take<f16>(T * kvd);
     s.vT16 = cv.take<f16>(T * kvd);
+  } else if (use_attention_dma(c)) {
+    s.qT32 = cv.take<float>(T * qd);
+    s.kT32 = cv.take<float>(T * kvd);
+    s.vT32 = cv.take<float>(T * kvd);
   }
   bytes = cv.off;
 }
 
-bool use_attention16(const qblk_config& c) {
-  return c.gemm_precision == 1 && attention16_supported(c.batch, c.seq, c.heads, c.kv_heads, c.head_dim);
+bool use_attention_dma(const qblk_config& c) {
+  return attention_dma_supported(c.batch, c.seq, c.heads, c.kv_heads, c.head_dim) &&
+         (c.gemm_precision == 1 || c.head_dim == 64);
 }
 
 Prec prec_of(const qblk_config& c) { return c.gemm_precision ? Prec::F16 : Prec::F32; }
@@ -133,9 +139,12 @@ void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes, 
   s.a16 = nullptr;
   s.pack = Packed16{};
   s.do16 = s.doT16 = nullptr;
-  if (use_attention16(c)) {
+  s.doT32 = nullptr;
+  if (use_attention_dma(c) && c.gemm_precision == 1) {
     s.do16 = cv.take<f16>(T * qd);
     s.doT16 = cv.take<f16>(T * qd);
+  } else if (use_attention_dma(c)) {
+    s.doT32 = cv.take<float>(T * qd);
   }
   if (c.gemm_precision == 1 && lora_rank == 0) {
     s.a16 = cv.take<f16>(T * std::max({qd + 2 * kvd, 2 * I, h, qd}));
@@ -198,15 +207,25 @@ int check_config(const qblk_config* c) {
 
 namespace {
 
-Attn16Args attn16_args(const qblk_config& c, const Saved& s) {
+AttnDmaArgs attn_dma_args(const qblk_config& c, const Saved& s) {
   const int T = c.seq * c.batch, d = c.head_dim;
   const int qd = c.heads * d, kvd = c.kv_heads * d;
-  Attn16Args a{};
+  AttnDmaArgs a{};
   a.batch = c.batch; a.seq = c.seq; a.heads = c.heads; a.kv_heads = c.kv_heads; a.head_dim = d;
-  a.q = s.q16; a.ldq = qd;
-  a.k = s.k16; a.ldk = kvd;
-  a.v = s.v16; a.ldv = kvd;
-  a.qT = s.qT16; a.kT = s.kT16; a.vT = s.vT16; a.ldt = T;
+  if (s.q16) {  // fp16 copies
+    a.fp32 = 0;
+    a.q = s.q16; a.ldq = qd;
+    a.k = s.k16; a.ldk = kvd;
+    a.v = s.v16; a.ldv = kvd;
+    a.qT = s.qT16; a.kT = s.kT16; a.vT = s.vT16;
+  } else {  // fp32: the tensors themselves plus transposed copies
+    a.fp32 = 1;
+    a.q = s.qr; a.ldq = qd;
+    a.k = s.kr; a.ldk = kvd;
+    a.v = s.qkv + qd + kvd; a.ldv = qd + 2 * kvd;
+    a.qT = s.qT32; a.kT = s.kT32; a.vT = s.vT32;
+  }
+  a.ldt = T;
   a.o = s.o; a.ldo = qd;
   a.lse = s.lse;
   return a;
@@ -229,13 +248,19 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
   QkRopeArgs qa{T, c.seq, c.heads, c.kv_heads, d, c.qk_norm, c.eps, s.qkv, ldqkv, g_q, g_k, s.tab,
                 s.qr, s.kr, s.rho_q, s.rho_k};
   QBLK_TRY(qk_norm_rope_forward(qa, st));
-  if (s.q16) {
-    QBLK_TRY(cast_f16(T, qd, s.qr, qd, s.q16, qd, s.qT16, T, st));
-    QBLK_TRY(cast_f16(T, kvd, s.kr, kvd, s.k16, kvd, s.kT16, T, st));
-    QBLK_TRY(cast_f16(T, kvd, s.qkv + qd + kvd, ldqkv, s.v16, kvd, s.vT16, T, st));
-    Attn16Args af = attn16_args(c, s);
+  if (s.q16 || s.qT32) {
+    if (s.q16) {
+      QBLK_TRY(cast_f16(T, qd, s.qr, qd, s.q16, qd, s.qT16, T, st));
+      QBLK_TRY(cast_f16(T, kvd, s.kr, kvd, s.k16, kvd, s.kT16, T, st));
+      QBLK_TRY(cast_f16(T, kvd, s.qkv + qd + kvd, ldqkv, s.v16, kvd, s.vT16, T, st));
+    } else {
+      QBLK_TRY(transpose_f32(T, qd, s.qr, qd, s.qT32, T, st));
+      QBLK_TRY(transpose_f32(T, kvd, s.kr, kvd, s.kT32, T, st));
+      QBLK_TRY(transpose_f32(T, kvd, s.qkv + qd + kvd, ldqkv, s.vT32, T, st));
+    }
+    AttnDmaArgs af = attn_dma_args(c, s);
     af.o16 = s.o16;
-    QBLK_TRY(attention16_forward(af, st));
+    QBLK_TRY(attention_dma_forward(af, st));
   } else {
     AttnArgs aa{};
     aa.batch = c.batch; aa.seq = c.seq; aa.heads = c.heads; aa.kv_heads = c.kv_heads; aa.head_dim = d;
@@ -272,28 +297,34 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
   // O projection
   QBLK_TRY(proj.o(w.dr1, s.o, w.d_o, st));
   // attention backward: dq, dk at the attention inputs; dv straight into dqkv
-  if (s.q16) {
-    QBLK_TRY(cast_f16(T, qd, w.d_o, qd, w.do16, qd, w.doT16, T, st));
-    Attn16Args ab = attn16_args(c, s);
-    ab.d_o = w.do16; ab.doT = w.doT16; ab.lddo = qd;
+  if (s.q16 || s.qT32) {
+    AttnDmaArgs ab = attn_dma_args(c, s);
+    if (s.q16) {
+      QBLK_TRY(cast_f16(T, qd, w.d_o, qd, w.do16, qd, w.doT16, T, st));
+      ab.d_o = w.do16; ab.doT = w.doT16;
+    } else {
+      QBLK_TRY(transpose_f32(T, qd, w.d_o, qd, w.doT32, T, st));
+      ab.d_o = w.d_o; ab.doT = w.doT32;
+    }
+    ab.lddo = qd;
     ab.do32 = w.d_o; ab.lddo32 = qd;
     ab.dq = w.dqr; ab.lddq = qd;
     ab.dk = w.dkr; ab.lddk = kvd;
     ab.dv = w.dqkv + qd + kvd; ab.lddv = ldqkv;
-    QBLK_TRY(attention16_backward(ab, w.attn, st));
+    QBLK_TRY(attention_dma_backward(ab, w.attn, st));
   } else {
-  AttnArgs aa{};
-  aa.batch = c.batch; aa.seq = c.seq; aa.heads = c.heads; aa.kv_heads = c.kv_heads; aa.head_dim = d;
-  aa.q = s.qr; aa.ldq = qd;
-  aa.k = s.kr; aa.ldk = kvd;
-  aa.v = s.qkv + qd + kvd; aa.ldv = ldqkv;
-  aa.o = s.o; aa.ldo = qd;
-  aa.lse = s.lse;
-  aa.d_o = w.d_o; aa.lddo = qd;
-  aa.dq = w.dqr; aa.lddq = qd;
-  aa.dk = w.dkr; aa.lddk = kvd;
-  aa.dv = w.dqkv + qd + kvd; aa.lddv = ldqkv;
-  QBLK_TRY(attention_backward(aa, prec_of(c), w.attn, st));
+    AttnArgs aa{};
+    aa.batch = c.batch; aa.seq = c.seq; aa.heads = c.heads; aa.kv_heads = c.kv_heads; aa.head_dim = d;
+    aa.q = s.qr; aa.ldq = qd;
+    aa.k = s.kr; aa.ldk = kvd;
+    aa.v = s.qkv + qd + kvd; aa.ldv = ldqkv;
+    aa.o = s.o; aa.ldo = qd;
+    aa.lse = s.lse;
+    aa.d_o = w.d_o; aa.lddo = qd;
+    aa.dq = w.dqr; aa.lddq = qd;
+    aa.dk = w.dkr; aa.lddk = kvd;
+    aa.dv = w.dqkv + qd + kvd; aa.lddv = ldqkv;
+    QBLK_TRY(attention_backward(aa, prec_of(c), w.attn, st));
   }
   QkRopeBwdArgs qb{T, c.seq, c.heads, c.kv_heads, d, c.qk_norm, c.eps, s.qkv, ldqkv, g_q, g_k, s.tab,
                    w.dqr, w.dkr, w.dqkv, dg_q, dg_k};

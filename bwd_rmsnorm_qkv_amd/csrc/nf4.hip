@@ -99,9 +99,34 @@ __global__ void nf4_dequant_kernel(const uint8_t* __restrict__ codes, const floa
   w[i] = L.level[c] * absmax[i >> 6];
 }
 
+// fp16 decode for the GEMMs: 8 elements (4 code bytes, one scale) per
+// thread; L[c] * a in fp32, rounded once to fp16.
+__global__ void nf4_dequant_f16_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ absmax,
+                                       int64_t n8, half8* __restrict__ w, LevelArgs L) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const uint32_t b = codes[i];
+  const float a = absmax[i >> 3];
+  half8 o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = (f16)(L.level[(b >> (4 * j)) & 15] * a);
+  w[i] = o;
+}
+
 }  // namespace
 
 const float* nf4_codebook_host() { return codebook().level; }
+
+int nf4_dequantize_f16(const uint8_t* codes, const float* absmax, int64_t numel, f16* w, hipStream_t st) {
+  if (numel <= 0 || numel % 64) return fail(QBLK_EINVAL, "nf4_dequantize_f16: numel %lld not a positive multiple of 64", (long long)numel);
+  if (((uintptr_t)codes & 3) || ((uintptr_t)w & 15)) return fail(QBLK_EINVAL, "nf4_dequantize_f16: misaligned buffer");
+  LevelArgs L;
+  for (int i = 0; i < 16; ++i) L.level[i] = codebook().level[i];
+  const int64_t n8 = numel / 8;
+  hipLaunchKernelGGL(nf4_dequant_f16_kernel, dim3((unsigned)ceil_div(n8, 256)), dim3(256), 0, st,
+                     (const uint32_t*)codes, absmax, n8, (half8*)w, L);
+  return check_launch("nf4_dequant_f16_kernel");
+}
 
 int nf4_quantize(const float* w, int64_t numel, uint8_t* codes, float* absmax, hipStream_t st) {
   if (numel <= 0 || numel % 64) return fail(QBLK_EINVAL, "nf4_quantize: numel %lld not a positive multiple of 64", (long long)numel);

@@ -6,15 +6,24 @@
 // lora_forward / lora_backward (A [rank, in], B [out, rank], scale
 // alpha/rank, with h = x A^T kept from the forward).
 //
-// Design. The NF4 codes are decoded while the GEMM stages its B operand
-// (no dequantized copy of any weight exists), and the LoRA branch rides in
-// the same GEMM as extra K columns: y = [x | s*h] [W~ | B]^T with h = x A^T,
-// s = alpha/rank. For the fused Q/K/V (and gate/up) GEMM the extra columns
-// are [h_q | h_k | h_v] against a block-diagonal B. The backward uses the
-// same trick for dX = dY W~ + (s dY B) A, and small TN GEMMs for dA, dB.
+// Design. Two paths share the launch sequence of the dense block:
+// * fp16 copies (T a multiple of 8): each projection group's NF4 codes are
+//   decoded once per call into an fp16 scratch copy of W~ (HBM-bound, a
+//   fraction of the product's time), the product runs on the direct-to-LDS
+//   GEMM kernel with the activations' fp16 copies, and the LoRA branch adds
+//   s h B^T (forward) or dh A (backward) with small accumulating GEMMs.
+// * otherwise: the codes are decoded while the GEMM stages its B operand and
+//   the LoRA branch rides in the same GEMM as extra K columns:
+//   y = [x | s*h] [W~ | B]^T with h = x A^T, s = alpha/rank, against a
+//   block-diagonal B for the fused groups; dX = dY W~ + (s dY B) A likewise.
+// dA and dB are small TN GEMMs either way.
 #include "../../include/qblk.h"
 #include "block.h"
 #include "gemm.h"
+#include "norms.h"
+#include "step.h"
+
+#include <algorithm>
 
 namespace qblk {
 namespace {
@@ -28,6 +37,8 @@ struct Nf4Scratch {
   Scratch base;
   float *dh_qkv, *dh_o, *dh_gu, *dh_d;  // s dY B
   float *sink_h, *sink_d;               // gamma gradients are not outputs
+  f16* w16;                             // fp16 W~ of the current group (fp16 copies path)
+  f16* dy16;                            // fp16 dY of the current group
 };
 
 size_t carve_nf4(const qblk_config& c, int r, void* saved, void* scratch, Nf4Saved* s, Nf4Scratch* w,
@@ -52,6 +63,19 @@ size_t carve_nf4(const qblk_config& c, int r, void* saved, void* scratch, Nf4Sav
   w->dh_d = take(scratch, wb, T * r);
   w->sink_h = take(scratch, wb, 2 * (size_t)c.hidden);
   w->sink_d = take(scratch, wb, 2 * (size_t)c.head_dim);
+  w->w16 = w->dy16 = nullptr;
+  if (s->base.n1_16 || !saved) {  // sizing call, or the fp16 copies exist
+    const size_t h = c.hidden, qd = (size_t)c.heads * c.head_dim, kvd = (size_t)c.kv_heads * c.head_dim;
+    const size_t I = c.intermediate, qkv = qd + 2 * kvd;
+    const size_t wmax = std::max({qkv * h, h * qd, 2 * I * h, h * I});
+    const size_t dmax = std::max({qkv, h, 2 * I});
+    float* a = take(scratch, wb, wmax / 2 + 64);
+    float* b = take(scratch, wb, T * dmax / 2 + 64);
+    if (s->base.n1_16) {
+      w->w16 = (f16*)a;
+      w->dy16 = (f16*)b;
+    }
+  }
   *scratch_bytes = wb;
   return sb;
 }
@@ -220,6 +244,116 @@ int nf4_bwd(const qblk_nf4_block_params& p, const qblk_lora_grads& gr, int T, in
   return QBLK_OK;
 }
 
+// fp16 W~ of a projection group, stacked along out, into w16.
+int dequant_group(const qblk_nf4_block_params& p, const int* id3, const int* outd, int n, int in, f16* w16,
+                  hipStream_t st) {
+  size_t off = 0;
+  for (int k = 0; k < n; ++k) {
+    const int64_t numel = (int64_t)outd[k] * in;
+    QBLK_TRY(nf4_dequantize_f16(p.codes[id3[k]], p.absmax[id3[k]], numel, w16 + off, st));
+    off += (size_t)numel;
+  }
+  return QBLK_OK;
+}
+
+// out (+ res) = x16 W~^T + s h blockdiag(B)^T on the fp16 copies path.
+int nf4_fwd16(const qblk_nf4_block_params& p, const Nf4Scratch& w, int T, int in, const f16* x16,
+              std::initializer_list<int> ids, std::initializer_list<int> outs, const float* h, const float* res,
+              float* out, hipStream_t st) {
+  const int r = p.rank, n = (int)ids.size();
+  int outd[3] = {0, 0, 0}, id3[3] = {-1, -1, -1}, j = 0;
+  for (int o : outs) outd[j++] = o;
+  j = 0;
+  for (int id : ids) id3[j++] = id;
+  int N = 0;
+  for (int k = 0; k < n; ++k) N += outd[k];
+  QBLK_TRY(dequant_group(p, id3, outd, n, in, w.w16, st));
+  GemmDesc g = base(Layout::NT, T, N, in);
+  g.a = x16; g.lda = in; g.a_src = Src::F16;
+  g.b = seg1(w.w16, N); g.ldb = in; g.b_src = Src::F16;
+  g.c = seg1(out, T); g.ldc = N;
+  g.r = res; g.ldr = N;
+  QBLK_TRY(gemm(g, st));
+  int col = 0;
+  for (int k = 0; k < n; ++k) {  // out[:, block k] += s h_k B_k^T
+    GemmDesc u = base(Layout::NT, T, outd[k], r);
+    u.a = h + k * r; u.lda = n * r;
+    u.b = seg1(p.lora_b[id3[k]], outd[k]); u.ldb = r;
+    u.c = seg1(out + col, T); u.ldc = N;
+    u.alpha = p.alpha / (float)r;
+    u.accumulate = 1;
+    QBLK_TRY(gemm(u, st));
+    col += outd[k];
+  }
+  return QBLK_OK;
+}
+
+// Backward on the fp16 copies path: dX = dY16 W~ + dh [A stacked]; dA, dB
+// as in nf4_bwd.
+int nf4_bwd16(const qblk_nf4_block_params& p, const qblk_lora_grads& gr, const Nf4Scratch& w, int T, int in,
+              const float* dy, const f16* x16, const float* x, const float* h, std::initializer_list<int> ids,
+              std::initializer_list<int> outs, float* dh, float* dx, hipStream_t st) {
+  const int r = p.rank, n = (int)ids.size();
+  const float sc = p.alpha / (float)r;
+  int outd[3] = {0, 0, 0}, id3[3] = {-1, -1, -1}, j = 0;
+  for (int o : outs) outd[j++] = o;
+  j = 0;
+  for (int id : ids) id3[j++] = id;
+  int Nout = 0;
+  for (int k = 0; k < n; ++k) Nout += outd[k];
+  (void)x16;
+  int col = 0;
+  for (int k = 0; k < n; ++k) {  // dh[:, k r:(k+1) r] = s dY_k B_k
+    GemmDesc g = base(Layout::NN, T, r, outd[k]);
+    g.a = dy + col; g.lda = Nout;
+    g.b = seg1(p.lora_b[id3[k]], outd[k]); g.ldb = r;
+    g.c = seg1(dh + k * r, T); g.ldc = n * r;
+    g.alpha = sc;
+    QBLK_TRY(gemm(g, st));
+    col += outd[k];
+  }
+  QBLK_TRY(cast_f16(T, Nout, dy, Nout, w.dy16, Nout, nullptr, 0, st));
+  QBLK_TRY(dequant_group(p, id3, outd, n, in, w.w16, st));
+  {  // dX = dY W~
+    GemmDesc g = base(Layout::NN, T, in, Nout);
+    g.a = w.dy16; g.lda = Nout; g.a_src = Src::F16;
+    g.b = seg1(w.w16, Nout); g.ldb = in; g.b_src = Src::F16;
+    g.c = seg1(dx, T); g.ldc = in;
+    QBLK_TRY(gemm(g, st));
+  }
+  {  // dX += dh [A_0; A_1; A_2]
+    GemmDesc g = base(Layout::NN, T, in, n * r);
+    g.a = dh; g.lda = n * r;
+    g.b = rows3(r, n > 1 ? r : 0, n > 2 ? r : 0);
+    for (int k = 0; k < n; ++k) g.b.p[k] = p.lora_a[id3[k]];
+    g.ldb = in;
+    g.c = seg1(dx, T); g.ldc = in;
+    g.accumulate = 1;
+    QBLK_TRY(gemm(g, st));
+  }
+  {  // dB_k = s dY_k^T h_k
+    GemmDesc g = base(Layout::TN, Nout, n * r, T);
+    g.a = dy; g.lda = Nout;
+    g.b = seg1(h, T); g.ldb = n * r;
+    g.c = rows3(outd[0], outd[1], outd[2]);
+    for (int k = 0; k < n; ++k) g.c.p[k] = gr.lora_b[id3[k]];
+    g.ldc = r;
+    g.c_cols_blockdiag = r;
+    g.alpha = sc;
+    QBLK_TRY(gemm(g, st));
+  }
+  {  // dA_k = dh_k^T X
+    GemmDesc g = base(Layout::TN, n * r, in, T);
+    g.a = dh; g.lda = n * r;
+    g.b = seg1(x, T); g.ldb = in;
+    g.c = rows3(r, n > 1 ? r : 0, n > 2 ? r : 0);
+    for (int k = 0; k < n; ++k) g.c.p[k] = gr.lora_a[id3[k]];
+    g.ldc = in;
+    QBLK_TRY(gemm(g, st));
+  }
+  return QBLK_OK;
+}
+
 }  // namespace
 }  // namespace qblk
 
@@ -256,20 +390,25 @@ extern "C" int32_t qblk_block_forward_nf4_lora(const qblk_config* cfg, const qbl
   hipStream_t st = (hipStream_t)stream;
   t_ws = &w.base;
   ProjFwd proj;
+  const bool f16p = w.w16 != nullptr;
   proj.qkv = [&](const float* n1, float* qkv, hipStream_t s_) {
     QBLK_TRY(lora_down(P, T, h, n1, {PQ, PK, PV}, s.h_qkv, s_));
+    if (f16p) return nf4_fwd16(P, w, T, h, s.base.n1_16, {PQ, PK, PV}, {qd, kvd, kvd}, s.h_qkv, nullptr, qkv, s_);
     return nf4_fwd(P, T, h, n1, {PQ, PK, PV}, {qd, kvd, kvd}, s.h_qkv, nullptr, qkv, s_);
   };
   proj.o = [&](const float* o, const float* res, float* out, hipStream_t s_) {
     QBLK_TRY(lora_down(P, T, qd, o, {PO}, s.h_o, s_));
+    if (f16p) return nf4_fwd16(P, w, T, qd, s.base.o16, {PO}, {h}, s.h_o, res, out, s_);
     return nf4_fwd(P, T, qd, o, {PO}, {h}, s.h_o, res, out, s_);
   };
   proj.gate_up = [&](const float* n2, float* gu, hipStream_t s_) {
     QBLK_TRY(lora_down(P, T, h, n2, {PG, PU}, s.h_gu, s_));
+    if (f16p) return nf4_fwd16(P, w, T, h, s.base.n2_16, {PG, PU}, {I, I}, s.h_gu, nullptr, gu, s_);
     return nf4_fwd(P, T, h, n2, {PG, PU}, {I, I}, s.h_gu, nullptr, gu, s_);
   };
   proj.down = [&](const float* sv, const float* res, float* out, hipStream_t s_) {
     QBLK_TRY(lora_down(P, T, I, sv, {PD}, s.h_d, s_));
+    if (f16p) return nf4_fwd16(P, w, T, I, s.base.s16, {PD}, {h}, s.h_d, res, out, s_);
     return nf4_fwd(P, T, I, sv, {PD}, {h}, s.h_d, res, out, s_);
   };
   const int rc = block_forward_impl(c, proj, P.g_in, P.g_post, P.g_q, P.g_k, x, y, s.base, st);
@@ -299,16 +438,23 @@ extern "C" int32_t qblk_block_backward_nf4_lora(const qblk_config* cfg, const qb
   hipStream_t st = (hipStream_t)stream;
   t_ws = &w.base;
   ProjBwd proj;
+  const bool f16p = w.w16 != nullptr;
   proj.down = [&](const float* dyv, const float* sv, float* ds, hipStream_t s_) {
+    if (f16p) return nf4_bwd16(P, G, w, T, I, dyv, s.base.s16, sv, s.h_d, {PD}, {h}, w.dh_d, ds, s_);
     return nf4_bwd(P, G, T, I, dyv, sv, s.h_d, {PD}, {h}, w.dh_d, ds, s_);
   };
   proj.gate_up = [&](const float* dgu, const float* n2, float* dn2, hipStream_t s_) {
+    if (f16p) return nf4_bwd16(P, G, w, T, h, dgu, s.base.n2_16, n2, s.h_gu, {PG, PU}, {I, I}, w.dh_gu, dn2, s_);
     return nf4_bwd(P, G, T, h, dgu, n2, s.h_gu, {PG, PU}, {I, I}, w.dh_gu, dn2, s_);
   };
   proj.o = [&](const float* dr1, const float* o, float* d_o, hipStream_t s_) {
+    if (f16p) return nf4_bwd16(P, G, w, T, qd, dr1, s.base.o16, o, s.h_o, {PO}, {h}, w.dh_o, d_o, s_);
     return nf4_bwd(P, G, T, qd, dr1, o, s.h_o, {PO}, {h}, w.dh_o, d_o, s_);
   };
   proj.qkv = [&](const float* dqkv, const float* n1, float* dn1, hipStream_t s_) {
+    if (f16p)
+      return nf4_bwd16(P, G, w, T, h, dqkv, s.base.n1_16, n1, s.h_qkv, {PQ, PK, PV}, {qd, kvd, kvd}, w.dh_qkv,
+                       dn1, s_);
     return nf4_bwd(P, G, T, h, dqkv, n1, s.h_qkv, {PQ, PK, PV}, {qd, kvd, kvd}, w.dh_qkv, dn1, s_);
   };
   const int rc = block_backward_impl(c, proj, P.g_in, P.g_post, P.g_q, P.g_k, x, dy, s.base, dx, w.sink_h,

@@ -19,6 +19,8 @@ int adamw(int n, float* const* w, const float* const* g, float* const* m, float*
           const float* scale_dev, hipStream_t st);
 
 int nf4_quantize(const float* w, int64_t numel, uint8_t* codes, float* absmax, hipStream_t st);
+// fp16 decode (L[c] * a in fp32, rounded to nearest even) for the GEMMs.
+int nf4_dequantize_f16(const uint8_t* codes, const float* absmax, int64_t numel, f16* w, hipStream_t st);
 int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t numel, float* w,
                    hipStream_t st);
 

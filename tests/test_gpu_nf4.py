@@ -16,7 +16,12 @@ pytestmark = pytest.mark.gpu
 SMALL = synth.BlockShape(hidden=256, heads=4, kv_heads=2, head_dim=64, intermediate=512, seq=70, batch=2,
                          rope_theta=1e6, gemm_precision=1)
 
-CASES = [("small_ragged", SMALL, 8), ("qwen3_4b_seq2048", synth.NF4_LORA_QWEN3_4B, synth.LORA_RANK)]
+# T = 72 (a multiple of 8): the fp16 copies path with contractions whose K is
+# not a multiple of 64 (general GEMM kernel); T = 140: the fused-decode path
+SMALL_T72 = synth.BlockShape(hidden=256, heads=4, kv_heads=2, head_dim=64, intermediate=480, seq=36, batch=2,
+                             rope_theta=1e6, gemm_precision=1)
+CASES = [("small_ragged", SMALL, 8), ("small_t72", SMALL_T72, 8),
+         ("qwen3_4b_seq2048", synth.NF4_LORA_QWEN3_4B, synth.LORA_RANK)]
 
 
 @pytest.mark.parametrize("name,c,rank", CASES)
