@@ -360,28 +360,26 @@ static AttnDmaArgs attn16_dense(int32_t batch, int32_t seq, int32_t heads, int32
 }
 
 int32_t qblk_attention_forward_f16(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads, int32_t head_dim,
-                                   const void* q16, const void* k16, const void* vT16, float* o, float* lse,
+                                   const void* q16, const void* k16, const void* v16, float* o, float* lse,
                                    qblk_stream_t stream) {
   AttnDmaArgs a = attn16_dense(batch, seq, heads, kv_heads, head_dim);
-  a.q = q16; a.k = k16; a.vT = vT16;
+  a.q = q16; a.k = k16; a.v = v16;
   a.o = o; a.lse = lse;
   return attention_dma_forward(a, S(stream));
 }
 
 int32_t qblk_attention_backward_f16(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads,
-                                    int32_t head_dim, const void* q16, const void* qT16, const void* k16,
-                                    const void* kT16, const void* v16, const float* o, const float* lse,
-                                    const void* do16, const void* doT16, const float* do32, float* dq,
-                                    float* dk, float* dv, void* scratch, size_t scratch_bytes,
+                                    int32_t head_dim, const void* q16, const void* k16, const void* v16,
+                                    const float* o, const float* lse, const void* do16, const float* do32,
+                                    float* dq, float* dk, float* dv, void* scratch, size_t scratch_bytes,
                                     qblk_stream_t stream) {
   QBLK_TRY(attention_check(batch, seq, heads, kv_heads, head_dim));
   if (scratch_bytes < attention_bwd_scratch(batch, seq, heads, head_dim))
     return fail(QBLK_EINVAL, "attention_backward_f16: scratch too small");
   AttnDmaArgs a = attn16_dense(batch, seq, heads, kv_heads, head_dim);
-  a.q = q16; a.qT = qT16; a.k = k16; a.kT = kT16;
-  a.v = v16; a.vT = kT16;  // the backward never reads vT
+  a.q = q16; a.k = k16; a.v = v16;
   a.o = (float*)o; a.lse = (float*)lse;
-  a.d_o = do16; a.doT = doT16; a.do32 = do32;
+  a.d_o = do16; a.do32 = do32;
   a.dq = dq; a.dk = dk; a.dv = dv;
   return attention_dma_backward(a, scratch, S(stream));
 }

@@ -674,8 +674,105 @@ __device__ __forceinline__ void acc_rows_product(const T* Xt, const floatx16& p,
   }
 }
 
+// fp16: the same product with Xt read out of the ROW tile X [32][D] by
+// ds_read_b64_tr_b16. Within each 16-lane group, output lane j takes element
+// k from the lane 4k + j/4, which read 4 consecutive columns at tile row
+// (4k + j/4) / 4 + base; so source lane s reads columns 4(s % 4) .. +3 of
+// tile row base + s / 4, and lane j ends up with 4 consecutive rows of
+// column j: 8 consecutive keys of one head_dim column after two reads.
+template <int D>
+__device__ __forceinline__ half8 row_tile_tr_frag(const f16* X, int db, int s2, int lane) {
+  using RT = RowTile<f16, D>;
+  typedef short short4v __attribute__((ext_vector_type(4)));
+  const int sl = lane & 15, q1 = (lane >> 4) & 1, kh = lane >> 5;
+  const int col = db * 32 + 16 * q1 + 4 * (sl & 3);
+  half8 out;
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int row = 16 * s2 + 8 * kh + 4 * rr + (sl >> 2);
+    const f16* addr = X + row * D + (((col >> 3) ^ RT::sw(row)) << 3) + (col & 7);
+    const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)addr);
+    const half4 h = __builtin_bit_cast(half4, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[4 * rr + e] = h[e];
+  }
+  return out;
+}
+
+template <int D>
+__device__ __forceinline__ void acc_rows_product_tr(const f16* X, const floatx16& p, int lane,
+                                                    floatx16 (&out)[D / 32]) {
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const half8 bp = acc_rows_operand(p, s2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      out[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(row_tile_tr_frag<D>(X, db, s2, lane), bp, out[db], 0, 0, 0);
+  }
+}
+
 using I0 = std::integral_constant<int, 0>;
 using I1 = std::integral_constant<int, 1>;
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// One LDS stage as its own __shared__ object (distinct objects: the
+// compiler adds no waits between a copy into one and reads of another).
+template <typename T, int TAG, int ELEMS>
+__device__ __forceinline__ T* att_lds() {
+  __shared__ __attribute__((aligned(16))) T buf[ELEMS];
+  return buf;
+}
+
+// s_waitcnt vmcnt with a runtime bound, rounded down to a power of two
+// (a smaller count only waits longer).
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if (n >= 32) wait_vmcnt<32>();
+  else if (n >= 16) wait_vmcnt<16>();
+  else if (n >= 8) wait_vmcnt<8>();
+  else if (n >= 4) wait_vmcnt<4>();
+  else if (n >= 2) wait_vmcnt<2>();
+  else if (n >= 1) wait_vmcnt<1>();
+  else wait_vmcnt<0>();
+}
+
+// Ring of NS LDS stages over n tiles: issue(t, IC<s>) starts the copies of
+// tile t into stage s (per_tile vector-memory instructions of this wave),
+// pre(t) runs after the barrier of step t and before the refill, and
+// body(t, IC<s>) consumes tile t from stage s. Step t waits for this wave's
+// copies of tile t (tiles t+1 .. t+NS-2 may stay in flight), then a barrier
+// makes every wave's copies visible and frees the stage of tile t-1, which
+// is refilled with tile t+NS-1. Whole rounds of NS steps run without
+// branches around the bodies; the last n % NS follow.
+template <int NS, typename Issue, typename Pre, typename Body>
+__device__ __forceinline__ void lds_ring(int n, int per_tile, Issue&& issue, Pre&& pre, Body&& body) {
+  static_assert(NS >= 2 && NS <= 4, "stages");
+  if (0 < n) issue(0, IC<0>{});
+  if constexpr (NS > 2) if (1 < n) issue(1, IC<1>{});
+  if constexpr (NS > 3) if (2 < n) issue(2, IC<2>{});
+  auto one = [&](auto S, int t) __attribute__((always_inline)) {
+    constexpr int st = decltype(S)::value;
+    const int ahead = min(NS - 2, n - 1 - t);
+    wait_vmcnt_le(ahead > 0 ? ahead * per_tile : 0);
+    __syncthreads();
+    pre(t);
+    if (t + NS - 1 < n) issue(t + NS - 1, IC<(st + NS - 1) % NS>{});
+    body(t, S);
+  };
+  const int nfull = n / NS * NS;
+  for (int t = 0; t < nfull; t += NS) {
+    one(IC<0>{}, t);
+    one(IC<1>{}, t + 1);
+    if constexpr (NS > 2) one(IC<2>{}, t + 2);
+    if constexpr (NS > 3) one(IC<3>{}, t + 3);
+  }
+  const int left = n - nfull;
+  if (left > 0) one(IC<0>{}, nfull);
+  if constexpr (NS > 2) if (left > 1) one(IC<1>{}, nfull + 1);
+  if constexpr (NS > 3) if (left > 2) one(IC<2>{}, nfull + 2);
+}
+
+constexpr int kFwdStages = 4, kDqStages = 3, kDkvStages = 2;
 
 // Forward: grid (q tiles, kv groups, batch), longest query tiles first; one
 // wave per query head of the group, K and V^T tiles shared through LDS.
@@ -684,12 +781,15 @@ __global__ __launch_bounds__(512) void attn_dma_fwd_kernel(const AttnDmaArgs a) 
   using RT = RowTile<T, D>;
   using TT = TrTile<T, D>;
   using E = AttnElem<T>;
-  __shared__ __attribute__((aligned(16))) T sK0[RT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sK1[RT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sV0[TT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sV1[TT::ELEMS];
+  // fp16 stages V as a row tile and reads V^T out of it; fp32 stages V^T
+  constexpr bool TR = sizeof(T) == 2;
+  constexpr int VE = TR ? RT::ELEMS : TT::ELEMS;
+  constexpr int VNI = TR ? RT::NI : TT::NI;
+  auto sK = [](auto S) { return att_lds<T, 2 * decltype(S)::value, RT::ELEMS>(); };
+  auto sV = [](auto S) { return att_lds<T, 2 * decltype(S)::value + 1, VE>(); };
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
+  const T* v = (const T*)a.v;
   const T* vT = (const T*)a.vT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, NW = blockDim.x >> 6;
   const int G = a.heads / a.kv_heads, grp = blockIdx.y, b = blockIdx.z;
@@ -712,8 +812,9 @@ __global__ __launch_bounds__(512) void attn_dma_fwd_kernel(const AttnDmaArgs a) 
   const int nkt = qt + 1;
 
   auto issue = [&](int kt, T* sk, T* sv) __attribute__((always_inline)) {
-    for (int j = w; j < RT::NI + TT::NI; j += NW) {
+    for (int j = w; j < RT::NI + VNI; j += NW) {
       if (j < RT::NI) copy_rows<T, D>(sk, j, lane, k, a.ldk, tok0, kt * 32, S, grp * D);
+      else if constexpr (TR) copy_rows<T, D>(sv, j - RT::NI, lane, v, a.ldv, tok0, kt * 32, S, grp * D);
       else copy_tr<T, D>(sv, j - RT::NI, lane, vT, a.ldt, tok0, kt * 32, S, grp * D);
     }
   };
@@ -751,26 +852,13 @@ __global__ __launch_bounds__(512) void attn_dma_fwd_kernel(const AttnDmaArgs a) 
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-    acc_rows_product<T, D>(sv, s, i, kh, o);
+    if constexpr (TR) acc_rows_product_tr<D>((const f16*)sv, s, lane, o);
+    else acc_rows_product<T, D>(sv, s, i, kh, o);
   };
-  auto step = [&](auto St, int kt) __attribute__((always_inline)) {
-    constexpr int st = decltype(St)::value;
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (kt + 1 < nkt) {
-      if constexpr (st == 0) issue(kt + 1, sK1, sV1);
-      else issue(kt + 1, sK0, sV0);
-    }
-    if constexpr (st == 0) compute(sK0, sV0, kt);
-    else compute(sK1, sV1, kt);
-  };
-  issue(0, sK0, sV0);
-  const int nfull = nkt & ~1;
-  for (int kt = 0; kt < nfull; kt += 2) {
-    step(I0{}, kt);
-    step(I1{}, kt + 1);
-  }
-  if (nkt & 1) step(I0{}, nfull);
+  const int per_tile = (RT::NI + VNI - w + NW - 1) / NW;
+  lds_ring<kFwdStages>(
+      nkt, per_tile, [&](int kt, auto St) __attribute__((always_inline)) { issue(kt, sK(St), sV(St)); },
+      [](int) {}, [&](int kt, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), kt); });
 
   if (qi < S) {
     const float inv = 1.0f / l;
@@ -790,25 +878,28 @@ __global__ __launch_bounds__(512) void attn_dma_fwd_kernel(const AttnDmaArgs a) 
 
 // dQ: grid (q tiles, kv groups, batch), one wave per query head; K, V and
 // K^T tiles shared through LDS.
+// (block: waves_per_group(G) waves, grid.y: kv_heads * G / that)
 template <typename T, int D>
-__global__ __launch_bounds__(512) void attn_dma_dq_kernel(const AttnDmaArgs a, const float* delta) {
+__global__ __launch_bounds__(256) void attn_dma_dq_kernel(const AttnDmaArgs a, const float* delta) {
   using RT = RowTile<T, D>;
   using TT = TrTile<T, D>;
   using E = AttnElem<T>;
-  __shared__ __attribute__((aligned(16))) T sK0[RT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sK1[RT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sV0[RT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sV1[RT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sKt0[TT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sKt1[TT::ELEMS];
+  // fp16 reads K^T out of the K row tile; fp32 stages K^T too
+  constexpr bool TR = sizeof(T) == 2;
+  constexpr int KTE = TR ? 16 : TT::ELEMS;
+  constexpr int KTNI = TR ? 0 : TT::NI;
+  auto sK = [](auto S) { return att_lds<T, 3 * decltype(S)::value, RT::ELEMS>(); };
+  auto sV = [](auto S) { return att_lds<T, 3 * decltype(S)::value + 1, RT::ELEMS>(); };
+  auto sKt = [](auto S) { return att_lds<T, 3 * decltype(S)::value + 2, KTE>(); };
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
   const T* v = (const T*)a.v;
   const T* kT = (const T*)a.kT;
   const T* d_o = (const T*)a.d_o;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, NW = blockDim.x >> 6;
-  const int G = a.heads / a.kv_heads, grp = blockIdx.y, b = blockIdx.z;
-  const int h = grp * G + w;
+  const int G = a.heads / a.kv_heads, b = blockIdx.z;
+  const int nsub = G / NW, grp = blockIdx.y / nsub;
+  const int h = grp * G + (blockIdx.y % nsub) * NW + w;
   const int S = a.seq;
   const int qt = gridDim.x - 1 - blockIdx.x, q0 = qt * 32;
   const int64_t tok0 = (int64_t)b * S;
@@ -830,7 +921,7 @@ __global__ __launch_bounds__(512) void attn_dma_dq_kernel(const AttnDmaArgs a, c
   const int nkt = qt + 1;
 
   auto issue = [&](int kt, T* sk, T* sv, T* skt) __attribute__((always_inline)) {
-    for (int j = w; j < 2 * RT::NI + TT::NI; j += NW) {
+    for (int j = w; j < 2 * RT::NI + KTNI; j += NW) {
       if (j < RT::NI) copy_rows<T, D>(sk, j, lane, k, a.ldk, tok0, kt * 32, S, grp * D);
       else if (j < 2 * RT::NI) copy_rows<T, D>(sv, j - RT::NI, lane, v, a.ldv, tok0, kt * 32, S, grp * D);
       else copy_tr<T, D>(skt, j - 2 * RT::NI, lane, kT, a.ldt, tok0, kt * 32, S, grp * D);
@@ -858,26 +949,13 @@ __global__ __launch_bounds__(512) void attn_dma_dq_kernel(const AttnDmaArgs a, c
         const float p = (kj > qi || kj >= S) ? 0.f : exp2f(s[e] * sc - lse2);
         s[e] = p * (dp[e] - dl);  // dS^T, unscaled
       }
-    acc_rows_product<T, D>(skt, s, i, kh, dq);
+    if constexpr (TR) acc_rows_product_tr<D>((const f16*)sk, s, lane, dq);
+    else acc_rows_product<T, D>(skt, s, i, kh, dq);
   };
-  auto step = [&](auto St, int kt) __attribute__((always_inline)) {
-    constexpr int st = decltype(St)::value;
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (kt + 1 < nkt) {
-      if constexpr (st == 0) issue(kt + 1, sK1, sV1, sKt1);
-      else issue(kt + 1, sK0, sV0, sKt0);
-    }
-    if constexpr (st == 0) compute(sK0, sV0, sKt0, kt);
-    else compute(sK1, sV1, sKt1, kt);
-  };
-  issue(0, sK0, sV0, sKt0);
-  const int nfull = nkt & ~1;
-  for (int kt = 0; kt < nfull; kt += 2) {
-    step(I0{}, kt);
-    step(I1{}, kt + 1);
-  }
-  if (nkt & 1) step(I0{}, nfull);
+  const int per_tile = (2 * RT::NI + KTNI - w + NW - 1) / NW;
+  lds_ring<kDqStages>(
+      nkt, per_tile, [&](int kt, auto St) __attribute__((always_inline)) { issue(kt, sK(St), sV(St), sKt(St)); },
+      [](int) {}, [&](int kt, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), sKt(St), kt); });
 
   if (qi < S) {
     const float inv = 1.0f / sqrtf((float)D);
@@ -900,14 +978,13 @@ __global__ __launch_bounds__(64) void attn_dma_dkv_kernel(const AttnDmaArgs a, c
   using RT = RowTile<T, D>;
   using TT = TrTile<T, D>;
   using E = AttnElem<T>;
-  __shared__ __attribute__((aligned(16))) T sQ0[RT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sQ1[RT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sO0[RT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sO1[RT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sQt0[TT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sQt1[TT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sOt0[TT::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sOt1[TT::ELEMS];
+  // fp16 reads Q^T and dO^T out of the row tiles; fp32 stages them too
+  constexpr bool TR = sizeof(T) == 2;
+  constexpr int XTE = TR ? 16 : TT::ELEMS;
+  auto sQ = [](auto S) { return att_lds<T, 4 * decltype(S)::value, RT::ELEMS>(); };
+  auto sO = [](auto S) { return att_lds<T, 4 * decltype(S)::value + 1, RT::ELEMS>(); };
+  auto sQt = [](auto S) { return att_lds<T, 4 * decltype(S)::value + 2, XTE>(); };
+  auto sOt = [](auto S) { return att_lds<T, 4 * decltype(S)::value + 3, XTE>(); };
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
   const T* v = (const T*)a.v;
@@ -948,22 +1025,29 @@ __global__ __launch_bounds__(64) void attn_dma_dkv_kernel(const AttnDmaArgs a, c
       copy_rows<T, D>(sq, j, lane, q, a.ldq, tok0, q0, S, h * D);
       copy_rows<T, D>(so, j, lane, d_o, a.lddo, tok0, q0, S, h * D);
     }
+    if constexpr (!TR) {
 #pragma unroll
-    for (int j = 0; j < TT::NI; ++j) {
-      copy_tr<T, D>(sqt, j, lane, qT, a.ldt, tok0, q0, S, h * D);
-      copy_tr<T, D>(sot, j, lane, doT, a.ldt, tok0, q0, S, h * D);
+      for (int j = 0; j < TT::NI; ++j) {
+        copy_tr<T, D>(sqt, j, lane, qT, a.ldt, tok0, q0, S, h * D);
+        copy_tr<T, D>(sot, j, lane, doT, a.ldt, tok0, q0, S, h * D);
+      }
+    }
+  };
+  // log-sum-exp and delta of this lane's 16 query rows q0 + 8g + 4kh + r of
+  // the next query tile, loaded one step ahead and before that step's tile
+  // copies are issued, so waiting for them never waits for the copies.
+  float4 lq[4], dq4[4], lq_n[4], dq4_n[4];
+  auto load_ld = [&](int qt, float4 (&L)[4], float4 (&Dl)[4]) __attribute__((always_inline)) {
+    const int q0 = qt * 32;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int qr = q0 + 8 * g + 4 * kh;
+      L[g] = qr < S ? *(const float4*)(lse_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
+      Dl[g] = qr < S ? *(const float4*)(dl_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
   auto compute = [&](const T* sq, const T* so, const T* sqt, const T* sot, int qt) __attribute__((always_inline)) {
     const int q0 = qt * 32;
-    // log-sum-exp and delta of this lane's 16 query rows q0 + 8g + 4kh + r
-    float4 lq[4], dq4[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int qr = q0 + 8 * g + 4 * kh;
-      lq[g] = qr < S ? *(const float4*)(lse_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
-      dq4[g] = qr < S ? *(const float4*)(dl_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
     floatx16 s, dp;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -987,28 +1071,28 @@ __global__ __launch_bounds__(64) void attn_dma_dkv_kernel(const AttnDmaArgs a, c
         s[e] = p;
         dp[e] = p * (dp[e] - Dl);
       }
-    acc_rows_product<T, D>(sot, s, i, kh, dv);   // dV^T += dO^T P
-    acc_rows_product<T, D>(sqt, dp, i, kh, dk);  // dK^T += Q^T dS
+    if constexpr (TR) {
+      acc_rows_product_tr<D>((const f16*)so, s, lane, dv);   // dV^T += dO^T P
+      acc_rows_product_tr<D>((const f16*)sq, dp, lane, dk);  // dK^T += Q^T dS
+    } else {
+      acc_rows_product<T, D>(sot, s, i, kh, dv);
+      acc_rows_product<T, D>(sqt, dp, i, kh, dk);
+    }
   };
   const int n = nqt - kt;  // query tiles kt .. nqt-1
-  auto step = [&](auto St, int t) __attribute__((always_inline)) {
-    constexpr int st = decltype(St)::value;
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (t + 1 < n) {
-      if constexpr (st == 0) issue(kt + t + 1, sQ1, sO1, sQt1, sOt1);
-      else issue(kt + t + 1, sQ0, sO0, sQt0, sOt0);
-    }
-    if constexpr (st == 0) compute(sQ0, sO0, sQt0, sOt0, kt + t);
-    else compute(sQ1, sO1, sQt1, sOt1, kt + t);
-  };
-  issue(kt, sQ0, sO0, sQt0, sOt0);
-  const int nfull = n & ~1;
-  for (int t = 0; t < nfull; t += 2) {
-    step(I0{}, t);
-    step(I1{}, t + 1);
-  }
-  if (n & 1) step(I0{}, nfull);
+  load_ld(kt, lq_n, dq4_n);
+  lds_ring<kDkvStages>(
+      n, 2 * RT::NI + (TR ? 0 : 2 * TT::NI),
+      [&](int t, auto St) __attribute__((always_inline)) { issue(kt + t, sQ(St), sO(St), sQt(St), sOt(St)); },
+      [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          lq[g] = lq_n[g];
+          dq4[g] = dq4_n[g];
+        }
+        if (t + 1 < n) load_ld(kt + t + 1, lq_n, dq4_n);
+      },
+      [&](int t, auto St) __attribute__((always_inline)) { compute(sQ(St), sO(St), sQt(St), sOt(St), kt + t); });
 
   if (kj < S) {
     const float inv = 1.0f / sqrtf((float)D);
@@ -1044,8 +1128,11 @@ int bwd_dma_launch(const AttnDmaArgs& a, float* delta, float* dk_part, float* dv
   da.d_o = a.do32; da.lddo = a.lddo32;
   hipLaunchKernelGGL(attn_delta_kernel, dim3((unsigned)ceil_div(T_ * a.heads, 4)), dim3(256), 0, st, da, delta);
   QBLK_TRY(check_launch("attn_delta_kernel"));
-  dim3 gq((unsigned)ceil_div(a.seq, 32), (unsigned)a.kv_heads, (unsigned)a.batch);
-  hipLaunchKernelGGL((attn_dma_dq_kernel<T, D>), gq, dim3(64 * G), 0, st, a, (const float*)delta);
+  int wq = 1;  // waves per dQ workgroup: the largest divisor of G up to 4
+  for (int c = 4; c >= 1; --c)
+    if (G % c == 0) { wq = c; break; }
+  dim3 gq((unsigned)ceil_div(a.seq, 32), (unsigned)(a.kv_heads * (G / wq)), (unsigned)a.batch);
+  hipLaunchKernelGGL((attn_dma_dq_kernel<T, D>), gq, dim3(64 * wq), 0, st, a, (const float*)delta);
   QBLK_TRY(check_launch("attn_dma_dq_kernel"));
   dim3 gk((unsigned)ceil_div(a.seq, 32), (unsigned)a.heads, (unsigned)a.batch);
   hipLaunchKernelGGL((attn_dma_dkv_kernel<T, D>), gk, dim3(64), 0, st, a, (const float*)delta, dk_part, dv_part);
@@ -1115,7 +1202,7 @@ static int check_dma(const AttnDmaArgs& a) {
   const int64_t T = (int64_t)a.batch * a.seq;
   if (a.ldt != T || a.ldq % 8 || a.ldk % 8 || a.ldv % 8 || a.ldo % 4)
     return fail(QBLK_EINVAL, "attention (tiled copies): strides (ldt must be T; row strides multiples of 8)");
-  const void* ptrs[] = {a.q, a.k, a.vT, a.o, a.lse};
+  const void* ptrs[] = {a.q, a.k, a.fp32 ? a.vT : a.v, a.o, a.lse};
   for (const void* p : ptrs)
     if (!p || ((uintptr_t)p & 15)) return fail(QBLK_EINVAL, "attention (tiled copies): null or misaligned pointer");
   return 0;
@@ -1132,9 +1219,11 @@ int attention_dma_forward(const AttnDmaArgs& a, hipStream_t st) {
 
 int attention_dma_backward(const AttnDmaArgs& a, void* scratch, hipStream_t st) {
   QBLK_TRY(check_dma(a));
-  const void* ptrs[] = {a.v, a.qT, a.kT, a.d_o, a.doT, a.do32, a.dq, a.dk, a.dv, scratch};
+  const void* ptrs[] = {a.v, a.d_o, a.do32, a.dq, a.dk, a.dv, scratch};
   for (const void* p : ptrs)
     if (!p || ((uintptr_t)p & 15)) return fail(QBLK_EINVAL, "attention backward (tiled copies): null or misaligned pointer");
+  if (a.fp32 && (!a.qT || !a.kT || !a.doT))
+    return fail(QBLK_EINVAL, "attention backward (tiled copies): fp32 needs the transposed copies");
   if (a.lddo % 8 || a.lddo32 % 4 || a.lddq % 4 || a.lddk % 4 || a.lddv % 4)
     return fail(QBLK_EINVAL, "attention backward (tiled copies): row strides");
   const int64_t T = (int64_t)a.batch * a.seq;

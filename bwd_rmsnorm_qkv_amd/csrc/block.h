@@ -26,9 +26,9 @@ struct Saved {
   float* gu;       // [T, 2I] gate | up
   float* s;        // [T, I] SwiGLU output
   // Attention on tiled copies (when use_attention_dma): fp16 copies of the
-  // attention inputs, row-major and transposed (fp16-operand configs), or
-  // fp32 transposed copies (fp32 configs); NULL otherwise.
-  f16 *q16, *qT16, *k16, *kT16, *v16, *vT16;
+  // attention inputs (fp16-operand configs), or fp32 transposed copies
+  // (fp32 configs); NULL otherwise.
+  f16 *q16, *k16, *v16;
   float *qT32, *kT32, *vT32;
   // fp16 copies of the projection inputs n1, o, n2, s (fp16-operand configs
   // with T a multiple of 8), written by their producers; NULL otherwise.
@@ -59,7 +59,7 @@ struct Scratch {
   // passes no packed weights, the weights' fp16 copies.
   f16* a16;  // fp16 copy of the current output gradient
   Packed16 pack;
-  f16 *do16, *doT16;  // attention on tiled copies: dO copies (fp16 configs)
+  f16* do16;          // attention on tiled copies: dO copy (fp16 configs)
   float* doT32;       // attention on tiled copies: dO transposed (fp32 configs)
 };
 

@@ -63,15 +63,12 @@ void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes) {
     s.n2_16 = cv.take<f16>(T * h);
     s.s16 = cv.take<f16>(T * I);
   }
-  s.q16 = s.qT16 = s.k16 = s.kT16 = s.v16 = s.vT16 = nullptr;
+  s.q16 = s.k16 = s.v16 = nullptr;
   s.qT32 = s.kT32 = s.vT32 = nullptr;
   if (use_attention_dma(c) && c.gemm_precision == 1) {
     s.q16 = cv.take<f16>(T * qd);
-    s.qT16 = cv.take<f16>(T * qd);
     s.k16 = cv.take<f16>(T * kvd);
-    s.kT16 = cv.take<f16>(T * kvd);
     s.v16 = cv.take<f16>(T * kvd);
-    s.vT16 = cv.take<f16>(T * kvd);
   } else if (use_attention_dma(c)) {
     s.qT32 = cv.take<float>(T * qd);
     s.kT32 = cv.take<float>(T * kvd);
@@ -138,11 +135,10 @@ void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes, 
   s.gemm_ws = cv.take<float>(s.gemm_ws_bytes / sizeof(float) + 1);
   s.a16 = nullptr;
   s.pack = Packed16{};
-  s.do16 = s.doT16 = nullptr;
+  s.do16 = nullptr;
   s.doT32 = nullptr;
   if (use_attention_dma(c) && c.gemm_precision == 1) {
     s.do16 = cv.take<f16>(T * qd);
-    s.doT16 = cv.take<f16>(T * qd);
   } else if (use_attention_dma(c)) {
     s.doT32 = cv.take<float>(T * qd);
   }
@@ -217,7 +213,6 @@ AttnDmaArgs attn_dma_args(const qblk_config& c, const Saved& s) {
     a.q = s.q16; a.ldq = qd;
     a.k = s.k16; a.ldk = kvd;
     a.v = s.v16; a.ldv = kvd;
-    a.qT = s.qT16; a.kT = s.kT16; a.vT = s.vT16;
   } else {  // fp32: the tensors themselves plus transposed copies
     a.fp32 = 1;
     a.q = s.qr; a.ldq = qd;
@@ -250,9 +245,9 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
   QBLK_TRY(qk_norm_rope_forward(qa, st));
   if (s.q16 || s.qT32) {
     if (s.q16) {
-      QBLK_TRY(cast_f16(T, qd, s.qr, qd, s.q16, qd, s.qT16, T, st));
-      QBLK_TRY(cast_f16(T, kvd, s.kr, kvd, s.k16, kvd, s.kT16, T, st));
-      QBLK_TRY(cast_f16(T, kvd, s.qkv + qd + kvd, ldqkv, s.v16, kvd, s.vT16, T, st));
+      QBLK_TRY(cast_f16(T, qd, s.qr, qd, s.q16, qd, nullptr, 0, st));
+      QBLK_TRY(cast_f16(T, kvd, s.kr, kvd, s.k16, kvd, nullptr, 0, st));
+      QBLK_TRY(cast_f16(T, kvd, s.qkv + qd + kvd, ldqkv, s.v16, kvd, nullptr, 0, st));
     } else {
       QBLK_TRY(transpose_f32(T, qd, s.qr, qd, s.qT32, T, st));
       QBLK_TRY(transpose_f32(T, kvd, s.kr, kvd, s.kT32, T, st));
@@ -300,8 +295,8 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
   if (s.q16 || s.qT32) {
     AttnDmaArgs ab = attn_dma_args(c, s);
     if (s.q16) {
-      QBLK_TRY(cast_f16(T, qd, w.d_o, qd, w.do16, qd, w.doT16, T, st));
-      ab.d_o = w.do16; ab.doT = w.doT16;
+      QBLK_TRY(cast_f16(T, qd, w.d_o, qd, w.do16, qd, nullptr, 0, st));
+      ab.d_o = w.do16;
     } else {
       QBLK_TRY(transpose_f32(T, qd, w.d_o, qd, w.doT32, T, st));
       ab.d_o = w.d_o; ab.doT = w.doT32;

@@ -65,7 +65,7 @@ _SIGS = {
     "qblk_block_backward": ([C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                              C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int32),
     "qblk_attention_forward_f16": ([C.c_int32] * 5 + [C.c_void_p] * 5 + [C.c_void_p], C.c_int32),
-    "qblk_attention_backward_f16": ([C.c_int32] * 5 + [C.c_void_p] * 14 + [C.c_size_t, C.c_void_p], C.c_int32),
+    "qblk_attention_backward_f16": ([C.c_int32] * 5 + [C.c_void_p] * 11 + [C.c_size_t, C.c_void_p], C.c_int32),
     "qblk_block_pack_f16_size": ([C.c_void_p, C.POINTER(C.c_size_t)], C.c_int32),
     "qblk_block_pack_f16": ([C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int32),
     "qblk_cross_entropy_workspace_size": ([C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_size_t)], C.c_int32),
@@ -356,17 +356,17 @@ def attention_workspace_size(batch, seq, heads):
     return s.value
 
 
-def attention_forward_f16(batch, seq, heads, kv_heads, head_dim, q16, k16, vT16, o, lse, stream=None):
-    _check(lib().qblk_attention_forward_f16(batch, seq, heads, kv_heads, head_dim, _p(q16), _p(k16), _p(vT16),
+def attention_forward_f16(batch, seq, heads, kv_heads, head_dim, q16, k16, v16, o, lse, stream=None):
+    _check(lib().qblk_attention_forward_f16(batch, seq, heads, kv_heads, head_dim, _p(q16), _p(k16), _p(v16),
                                             _p(o), _p(lse), _stream(stream)))
 
 
-def attention_backward_f16(batch, seq, heads, kv_heads, head_dim, q16, qT16, k16, kT16, v16, o, lse, do16, doT16,
-                           do32, dq, dk, dv, scratch, stream=None):
-    _check(lib().qblk_attention_backward_f16(batch, seq, heads, kv_heads, head_dim, _p(q16), _p(qT16), _p(k16),
-                                             _p(kT16), _p(v16), _p(o), _p(lse), _p(do16), _p(doT16), _p(do32),
-                                             _p(dq), _p(dk), _p(dv), _p(scratch),
-                                             scratch.numel() * scratch.element_size(), _stream(stream)))
+def attention_backward_f16(batch, seq, heads, kv_heads, head_dim, q16, k16, v16, o, lse, do16, do32, dq, dk, dv,
+                           scratch, stream=None):
+    _check(lib().qblk_attention_backward_f16(batch, seq, heads, kv_heads, head_dim, _p(q16), _p(k16), _p(v16),
+                                             _p(o), _p(lse), _p(do16), _p(do32), _p(dq), _p(dk), _p(dv),
+                                             _p(scratch), scratch.numel() * scratch.element_size(),
+                                             _stream(stream)))
 
 
 def attention_backward(batch, seq, heads, kv_heads, head_dim, precision, q, ldq, k, ldk, v, ldv, o, ldo, lse,

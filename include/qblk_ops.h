@@ -84,24 +84,22 @@ int32_t qblk_attention_workspace_size(int32_t batch, int32_t seq, int32_t heads,
                                       size_t* scratch_bytes);
 
 /* The attention the fp16-operand block runs (head_dim 64 or 128, seq a
- * multiple of 8), on fp16 (IEEE half) copies of its inputs, all dense:
- * q16 [T, heads*d], k16 [T, kv_heads*d], vT16 [kv_heads*d, T] (V
- * transposed). Writes o [T, heads*d] (fp32) and lse [batch, heads, seq].
- * Same computation as qblk_attention_forward with precision 1. */
+ * multiple of 8), on fp16 (IEEE half) copies of its inputs, all dense
+ * row-major: q16 [T, heads*d], k16, v16 [T, kv_heads*d]. Writes o
+ * [T, heads*d] (fp32) and lse [batch, heads, seq]. Same computation as
+ * qblk_attention_forward with precision 1. */
 int32_t qblk_attention_forward_f16(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads,
                                    int32_t head_dim, const void* q16, const void* k16,
-                                   const void* vT16, float* o, float* lse, qblk_stream_t stream);
+                                   const void* v16, float* o, float* lse, qblk_stream_t stream);
 
-/* Its backward: fp16 copies q16, qT16 [heads*d, T], k16, kT16
- * [kv_heads*d, T], v16, do16 [T, heads*d], doT16 [heads*d, T]; fp32 o and
+/* Its backward: fp16 copies q16, k16, v16 and do16 [T, heads*d]; fp32 o and
  * do32 (for rowsum(dO o)) and the forward's lse. Writes dq, dk, dv (fp32,
  * dense, overwritten; dk and dv summed over each KV group). scratch:
  * qblk_attention_workspace_size bytes. */
 int32_t qblk_attention_backward_f16(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads,
-                                    int32_t head_dim, const void* q16, const void* qT16,
-                                    const void* k16, const void* kT16, const void* v16,
-                                    const float* o, const float* lse, const void* do16,
-                                    const void* doT16, const float* do32, float* dq, float* dk,
+                                    int32_t head_dim, const void* q16, const void* k16,
+                                    const void* v16, const float* o, const float* lse,
+                                    const void* do16, const float* do32, float* dq, float* dk,
                                     float* dv, void* scratch, size_t scratch_bytes,
                                     qblk_stream_t stream);
 

@@ -184,6 +184,8 @@ ATTN16_SHAPES = [  # batch, seq, heads, kv_heads, head_dim: fp16 copies, direct-
     (1, 144, 8, 2, 128),    # ragged last tile (144 = 4.5 tiles)
     (3, 40, 8, 8, 128),     # G = 1, ragged, batch > 1
     (1, 512, 32, 8, 128),   # the Qwen3-4B-shaped attention
+    (1, 64, 8, 1, 64),      # G = 8: two dQ workgroups per group
+    (2, 48, 12, 2, 64),     # G = 6: dQ workgroups of 3 waves
 ]
 
 
@@ -199,16 +201,15 @@ def test_attention_f16(shape):
     T = B * S
     q, k, v, do = (rng.standard_normal((T, n * D)).astype(np.float16) for n in (H, KV, KV, H))
     q64, k64, v64, do64 = (x.astype(np.float64) for x in (q, k, v, do))
-    t16 = lambda x: dev(np.ascontiguousarray(x.T))
     o, lse = empty((T, H * D)), empty(B * H * S)
-    qblk.attention_forward_f16(B, S, H, KV, D, dev(q), dev(k), t16(v), o, lse)
+    qblk.attention_forward_f16(B, S, H, KV, D, dev(q), dev(k), dev(v), o, lse)
     o_ref = ops.attention_fwd(q64, k64, v64, B, S, H, KV, D)
     torch.cuda.synchronize()
     check("o", o, o_ref, FP16_TOL)
     dq, dk, dv = empty((T, H * D)), empty((T, KV * D)), empty((T, KV * D))
     scratch = byte_buffer(qblk.attention_workspace_size(B, S, H))
-    # dO in fp32 for the row term; its fp16 copies for the products
-    qblk.attention_backward_f16(B, S, H, KV, D, dev(q), t16(q), dev(k), t16(k), dev(v), o, lse, dev(do), t16(do),
+    # dO in fp32 for the row term; its fp16 copy for the products
+    qblk.attention_backward_f16(B, S, H, KV, D, dev(q), dev(k), dev(v), o, lse, dev(do),
                                 dev(do.astype(np.float32)), dq, dk, dv, scratch)
     dq_ref, dk_ref, dv_ref = ops.attention_bwd(q64, k64, v64, do64, B, S, H, KV, D)
     torch.cuda.synchronize()
