@@ -736,26 +736,25 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
   else wait_vmcnt<0>();
 }
 
-// Ring of NS LDS stages over n tiles: issue(t, IC<s>) starts the copies of
-// tile t into stage s (per_tile vector-memory instructions of this wave),
-// pre(t) runs after the barrier of step t and before the refill, and
-// body(t, IC<s>) consumes tile t from stage s. Step t waits for this wave's
-// copies of tile t (tiles t+1 .. t+NS-2 may stay in flight), then a barrier
-// makes every wave's copies visible and frees the stage of tile t-1, which
-// is refilled with tile t+NS-1. Whole rounds of NS steps run without
-// branches around the bodies; the last n % NS follow.
+// Ring of NS LDS stages private to one wave over its n tiles: issue(t,
+// IC<s>) starts the copies of tile t into stage s (per_tile vector-memory
+// instructions), pre(t) runs before the refill of step t, body(t, IC<s>)
+// consumes tile t from stage s. Step t waits for the wave's own copies of
+// tile t (tiles t+1 .. t+NS-2 may stay in flight); no barrier is needed, as
+// no other wave touches these stages, and the stage refilled at step t was
+// last read in step t-1, whose reads have all returned. Whole rounds of NS
+// steps run without branches around the bodies; the last n % NS follow.
 template <int NS, typename Issue, typename Pre, typename Body>
-__device__ __forceinline__ void lds_ring(int n, int per_tile, Issue&& issue, Pre&& pre, Body&& body) {
+__device__ __forceinline__ void wave_ring(int n, int per_tile, Issue&& issue, Pre&& pre, Body&& body) {
   static_assert(NS >= 2 && NS <= 4, "stages");
   if (0 < n) issue(0, IC<0>{});
   if constexpr (NS > 2) if (1 < n) issue(1, IC<1>{});
   if constexpr (NS > 3) if (2 < n) issue(2, IC<2>{});
   auto one = [&](auto S, int t) __attribute__((always_inline)) {
     constexpr int st = decltype(S)::value;
+    pre(t);
     const int ahead = min(NS - 2, n - 1 - t);
     wait_vmcnt_le(ahead > 0 ? ahead * per_tile : 0);
-    __syncthreads();
-    pre(t);
     if (t + NS - 1 < n) issue(t + NS - 1, IC<(st + NS - 1) % NS>{});
     body(t, S);
   };
@@ -772,28 +771,57 @@ __device__ __forceinline__ void lds_ring(int n, int per_tile, Issue&& issue, Pre
   if constexpr (NS > 3) if (left > 2) one(IC<2>{}, nfull + 2);
 }
 
-constexpr int kFwdStages = 4, kDqStages = 3, kDkvStages = 2;
+// Waves per workgroup and LDS stages per wave of the three kernels: the W
+// waves of a workgroup split one (tile, head) unit's key (or query) range
+// between them, each with private stages, and combine at the end.
+template <typename T>
+struct AttnSplit {
+  static constexpr bool F16 = sizeof(T) == 2;
+  static constexpr int FWD_W = 4, DQ_W = F16 ? 4 : 2, DKV_W = F16 ? 4 : 2;
+  static constexpr int NS = 2;
+};
 
-// Forward: grid (q tiles, kv groups, batch), longest query tiles first; one
-// wave per query head of the group, K and V^T tiles shared through LDS.
+// Fixed-order sum over the W waves of NV floats per lane, through LDS x
+// ((W-1) * NV * 64 floats, reused after the barriers): waves 1..W-1 park
+// their values, wave 0 adds them in wave order into v.
+template <int W, int NV>
+__device__ __forceinline__ void wave_sum_into0(float* x, int w, int lane, float* v) {
+  __syncthreads();
+  if (w > 0) {
+#pragma unroll
+    for (int e = 0; e < NV; ++e) x[((w - 1) * NV + e) * 64 + lane] = v[e];
+  }
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int ww = 1; ww < W; ++ww)
+#pragma unroll
+      for (int e = 0; e < NV; ++e) v[e] += x[((ww - 1) * NV + e) * 64 + lane];
+  }
+}
+
+// Forward: grid (q tiles, heads, batch), longest query tiles first. The W
+// waves take key tiles w, w+W, ...; each keeps its own running max, sum and
+// output; they are merged with a log-sum-exp combine and wave 0 writes o
+// and lse.
 template <typename T, int D>
-__global__ __launch_bounds__(512) void attn_dma_fwd_kernel(const AttnDmaArgs a) {
+__global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(const AttnDmaArgs a) {
   using RT = RowTile<T, D>;
   using TT = TrTile<T, D>;
   using E = AttnElem<T>;
+  constexpr int W = AttnSplit<T>::FWD_W, NS = AttnSplit<T>::NS;
   // fp16 stages V as a row tile and reads V^T out of it; fp32 stages V^T
   constexpr bool TR = sizeof(T) == 2;
   constexpr int VE = TR ? RT::ELEMS : TT::ELEMS;
   constexpr int VNI = TR ? RT::NI : TT::NI;
-  auto sK = [](auto S) { return att_lds<T, 2 * decltype(S)::value, RT::ELEMS>(); };
-  auto sV = [](auto S) { return att_lds<T, 2 * decltype(S)::value + 1, VE>(); };
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  auto sK = [w](auto S) { return att_lds<T, 2 * decltype(S)::value, W * RT::ELEMS>() + w * RT::ELEMS; };
+  auto sV = [w](auto S) { return att_lds<T, 2 * decltype(S)::value + 1, W * VE>() + w * VE; };
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
   const T* v = (const T*)a.v;
   const T* vT = (const T*)a.vT;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, NW = blockDim.x >> 6;
-  const int G = a.heads / a.kv_heads, grp = blockIdx.y, b = blockIdx.z;
-  const int h = grp * G + w;
+  const int G = a.heads / a.kv_heads, h = blockIdx.y, grp = h / G, b = blockIdx.z;
   const int S = a.seq;
   const int qt = gridDim.x - 1 - blockIdx.x, q0 = qt * 32;
   const int64_t tok0 = (int64_t)b * S;
@@ -809,17 +837,20 @@ __global__ __launch_bounds__(512) void attn_dma_fwd_kernel(const AttnDmaArgs a) 
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   float m = -INFINITY, l = 0.f;
-  const int nkt = qt + 1;
+  const int n = w <= qt ? (qt - w) / W + 1 : 0;  // key tiles w, w+W, .. <= qt
 
-  auto issue = [&](int kt, T* sk, T* sv) __attribute__((always_inline)) {
-    for (int j = w; j < RT::NI + VNI; j += NW) {
-      if (j < RT::NI) copy_rows<T, D>(sk, j, lane, k, a.ldk, tok0, kt * 32, S, grp * D);
-      else if constexpr (TR) copy_rows<T, D>(sv, j - RT::NI, lane, v, a.ldv, tok0, kt * 32, S, grp * D);
-      else copy_tr<T, D>(sv, j - RT::NI, lane, vT, a.ldt, tok0, kt * 32, S, grp * D);
+  auto issue = [&](int t, T* sk, T* sv) __attribute__((always_inline)) {
+    const int kv0 = (w + W * t) * 32;
+#pragma unroll
+    for (int j = 0; j < RT::NI; ++j) copy_rows<T, D>(sk, j, lane, k, a.ldk, tok0, kv0, S, grp * D);
+#pragma unroll
+    for (int j = 0; j < VNI; ++j) {
+      if constexpr (TR) copy_rows<T, D>(sv, j, lane, v, a.ldv, tok0, kv0, S, grp * D);
+      else copy_tr<T, D>(sv, j, lane, vT, a.ldt, tok0, kv0, S, grp * D);
     }
   };
-  auto compute = [&](const T* sk, const T* sv, int kt) __attribute__((always_inline)) {
-    const int kv0 = kt * 32;
+  auto compute = [&](const T* sk, const T* sv, int t) __attribute__((always_inline)) {
+    const int kv0 = (w + W * t) * 32;
     floatx16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -831,10 +862,10 @@ __global__ __launch_bounds__(512) void attn_dma_fwd_kernel(const AttnDmaArgs a) 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kj = kv0 + 8 * g + 4 * kh + r;
-        float v = s[4 * g + r] * sc;
-        if (kj > qi || kj >= S) v = -INFINITY;
-        s[4 * g + r] = v;
-        mx = fmaxf(mx, v);
+        float x = s[4 * g + r] * sc;
+        if (kj > qi || kj >= S) x = -INFINITY;
+        s[4 * g + r] = x;
+        mx = fmaxf(mx, x);
       }
     mx = half_max(mx);
     const float mn = fmaxf(m, mx);
@@ -855,51 +886,71 @@ __global__ __launch_bounds__(512) void attn_dma_fwd_kernel(const AttnDmaArgs a) 
     if constexpr (TR) acc_rows_product_tr<D>((const f16*)sv, s, lane, o);
     else acc_rows_product<T, D>(sv, s, i, kh, o);
   };
-  const int per_tile = (RT::NI + VNI - w + NW - 1) / NW;
-  lds_ring<kFwdStages>(
-      nkt, per_tile, [&](int kt, auto St) __attribute__((always_inline)) { issue(kt, sK(St), sV(St)); },
-      [](int) {}, [&](int kt, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), kt); });
+  wave_ring<NS>(
+      n, RT::NI + VNI, [&](int t, auto St) __attribute__((always_inline)) { issue(t, sK(St), sV(St)); },
+      [](int) {}, [&](int t, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), t); });
 
+  // Combine through the (now free) first stage buffer: every wave learns
+  // every wave's running max, rescales its own sum and output to the common
+  // max, and wave 0 adds them in wave order, 16 values at a time.
+  static_assert((W - 1) * 16 * 64 * 4 <= W * RT::ELEMS * (int)sizeof(T), "combine space");
+  float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
+  __syncthreads();
+  x[w * 64 + lane] = m;
+  __syncthreads();
+  float M = x[lane];
+#pragma unroll
+  for (int ww = 1; ww < W; ++ww) M = fmaxf(M, x[ww * 64 + lane]);
+  const float f = m == -INFINITY ? 0.f : exp2f(m - M);
+  float L = l * f;
+  wave_sum_into0<W, 1>(x, w, lane, &L);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] *= f;
+    wave_sum_into0<W, 16>(x, w, lane, (float*)&o[db]);
+  }
+  if (w != 0) return;
   if (qi < S) {
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / L;
     const int64_t ooff = (tok0 + qi) * a.ldo + (int64_t)h * D + 4 * kh;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 v =
+        const float4 vv =
             make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        *(float4*)(a.o + ooff + db * 32 + 8 * g) = v;
-        if (a.o16) *(half4*)(a.o16 + ooff + db * 32 + 8 * g) = to_half4(v);
+        *(float4*)(a.o + ooff + db * 32 + 8 * g) = vv;
+        if (a.o16) *(half4*)(a.o16 + ooff + db * 32 + 8 * g) = to_half4(vv);
       }
-    if (kh == 0) a.lse[((int64_t)b * a.heads + h) * S + qi] = (m + log2f(l)) * kLn2;
+    if (kh == 0) a.lse[((int64_t)b * a.heads + h) * S + qi] = (M + log2f(L)) * kLn2;
   }
 }
 
-// dQ: grid (q tiles, kv groups, batch), one wave per query head; K, V and
-// K^T tiles shared through LDS.
-// (block: waves_per_group(G) waves, grid.y: kv_heads * G / that)
+// dQ: grid (q tiles, heads, batch); the W waves take key tiles w, w+W, ...
+// (K, V and, in fp32, K^T through private LDS stages); wave 0 sums the
+// partial dQ in wave order and writes it.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_dma_dq_kernel(const AttnDmaArgs a, const float* delta) {
+__global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(const AttnDmaArgs a,
+                                                                             const float* delta) {
   using RT = RowTile<T, D>;
   using TT = TrTile<T, D>;
   using E = AttnElem<T>;
+  constexpr int W = AttnSplit<T>::DQ_W, NS = AttnSplit<T>::NS;
   // fp16 reads K^T out of the K row tile; fp32 stages K^T too
   constexpr bool TR = sizeof(T) == 2;
   constexpr int KTE = TR ? 16 : TT::ELEMS;
   constexpr int KTNI = TR ? 0 : TT::NI;
-  auto sK = [](auto S) { return att_lds<T, 3 * decltype(S)::value, RT::ELEMS>(); };
-  auto sV = [](auto S) { return att_lds<T, 3 * decltype(S)::value + 1, RT::ELEMS>(); };
-  auto sKt = [](auto S) { return att_lds<T, 3 * decltype(S)::value + 2, KTE>(); };
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  auto sK = [w](auto S) { return att_lds<T, 3 * decltype(S)::value, W * RT::ELEMS>() + w * RT::ELEMS; };
+  auto sV = [w](auto S) { return att_lds<T, 3 * decltype(S)::value + 1, W * RT::ELEMS>() + w * RT::ELEMS; };
+  auto sKt = [w](auto S) { return att_lds<T, 3 * decltype(S)::value + 2, W * KTE>() + w * KTE; };
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
   const T* v = (const T*)a.v;
   const T* kT = (const T*)a.kT;
   const T* d_o = (const T*)a.d_o;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, NW = blockDim.x >> 6;
-  const int G = a.heads / a.kv_heads, b = blockIdx.z;
-  const int nsub = G / NW, grp = blockIdx.y / nsub;
-  const int h = grp * G + (blockIdx.y % nsub) * NW + w;
+  const int G = a.heads / a.kv_heads, h = blockIdx.y, grp = h / G, b = blockIdx.z;
   const int S = a.seq;
   const int qt = gridDim.x - 1 - blockIdx.x, q0 = qt * 32;
   const int64_t tok0 = (int64_t)b * S;
@@ -918,17 +969,20 @@ __global__ __launch_bounds__(256) void attn_dma_dq_kernel(const AttnDmaArgs a, c
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) dq[db][e] = 0.f;
-  const int nkt = qt + 1;
+  const int n = w <= qt ? (qt - w) / W + 1 : 0;
 
-  auto issue = [&](int kt, T* sk, T* sv, T* skt) __attribute__((always_inline)) {
-    for (int j = w; j < 2 * RT::NI + KTNI; j += NW) {
-      if (j < RT::NI) copy_rows<T, D>(sk, j, lane, k, a.ldk, tok0, kt * 32, S, grp * D);
-      else if (j < 2 * RT::NI) copy_rows<T, D>(sv, j - RT::NI, lane, v, a.ldv, tok0, kt * 32, S, grp * D);
-      else copy_tr<T, D>(skt, j - 2 * RT::NI, lane, kT, a.ldt, tok0, kt * 32, S, grp * D);
+  auto issue = [&](int t, T* sk, T* sv, T* skt) __attribute__((always_inline)) {
+    const int kv0 = (w + W * t) * 32;
+#pragma unroll
+    for (int j = 0; j < RT::NI; ++j) {
+      copy_rows<T, D>(sk, j, lane, k, a.ldk, tok0, kv0, S, grp * D);
+      copy_rows<T, D>(sv, j, lane, v, a.ldv, tok0, kv0, S, grp * D);
     }
+#pragma unroll
+    for (int j = 0; j < KTNI; ++j) copy_tr<T, D>(skt, j, lane, kT, a.ldt, tok0, kv0, S, grp * D);
   };
-  auto compute = [&](const T* sk, const T* sv, const T* skt, int kt) __attribute__((always_inline)) {
-    const int kv0 = kt * 32;
+  auto compute = [&](const T* sk, const T* sv, const T* skt, int t) __attribute__((always_inline)) {
+    const int kv0 = (w + W * t) * 32;
     floatx16 s, dp;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -952,11 +1006,16 @@ __global__ __launch_bounds__(256) void attn_dma_dq_kernel(const AttnDmaArgs a, c
     if constexpr (TR) acc_rows_product_tr<D>((const f16*)sk, s, lane, dq);
     else acc_rows_product<T, D>(skt, s, i, kh, dq);
   };
-  const int per_tile = (2 * RT::NI + KTNI - w + NW - 1) / NW;
-  lds_ring<kDqStages>(
-      nkt, per_tile, [&](int kt, auto St) __attribute__((always_inline)) { issue(kt, sK(St), sV(St), sKt(St)); },
-      [](int) {}, [&](int kt, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), sKt(St), kt); });
+  wave_ring<NS>(
+      n, 2 * RT::NI + KTNI,
+      [&](int t, auto St) __attribute__((always_inline)) { issue(t, sK(St), sV(St), sKt(St)); }, [](int) {},
+      [&](int t, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), sKt(St), t); });
 
+  static_assert((W - 1) * 16 * 64 * 4 <= W * RT::ELEMS * (int)sizeof(T), "combine space");
+  float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) wave_sum_into0<W, 16>(x, w, lane, (float*)&dq[db]);
+  if (w != 0) return;
   if (qi < S) {
     const float inv = 1.0f / sqrtf((float)D);
     float* row = a.dq + (tok0 + qi) * a.lddq + (int64_t)h * D + 4 * kh;
@@ -969,29 +1028,33 @@ __global__ __launch_bounds__(256) void attn_dma_dq_kernel(const AttnDmaArgs a, c
   }
 }
 
-// dK, dV per query head: grid (kv tiles, heads, batch), one wave; Q, dO,
-// Q^T and dO^T tiles through LDS. Results go to per-head partials
-// [T, heads, D], summed over each group in a fixed order afterwards.
+// dK, dV per query head: grid (kv tiles, heads, batch); the W waves take
+// query tiles kt+w, kt+w+W, ... (Q, dO and, in fp32, their transposes
+// through private LDS stages); wave 0 sums the partials in wave order into
+// per-head buffers [T, heads, D], summed over each group afterwards.
 template <typename T, int D>
-__global__ __launch_bounds__(64) void attn_dma_dkv_kernel(const AttnDmaArgs a, const float* delta,
-                                                          float* dk_part, float* dv_part) {
+__global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(const AttnDmaArgs a,
+                                                                               const float* delta,
+                                                                               float* dk_part, float* dv_part) {
   using RT = RowTile<T, D>;
   using TT = TrTile<T, D>;
   using E = AttnElem<T>;
+  constexpr int W = AttnSplit<T>::DKV_W, NS = AttnSplit<T>::NS;
   // fp16 reads Q^T and dO^T out of the row tiles; fp32 stages them too
   constexpr bool TR = sizeof(T) == 2;
   constexpr int XTE = TR ? 16 : TT::ELEMS;
-  auto sQ = [](auto S) { return att_lds<T, 4 * decltype(S)::value, RT::ELEMS>(); };
-  auto sO = [](auto S) { return att_lds<T, 4 * decltype(S)::value + 1, RT::ELEMS>(); };
-  auto sQt = [](auto S) { return att_lds<T, 4 * decltype(S)::value + 2, XTE>(); };
-  auto sOt = [](auto S) { return att_lds<T, 4 * decltype(S)::value + 3, XTE>(); };
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  auto sQ = [w](auto S) { return att_lds<T, 4 * decltype(S)::value, W * RT::ELEMS>() + w * RT::ELEMS; };
+  auto sO = [w](auto S) { return att_lds<T, 4 * decltype(S)::value + 1, W * RT::ELEMS>() + w * RT::ELEMS; };
+  auto sQt = [w](auto S) { return att_lds<T, 4 * decltype(S)::value + 2, W * XTE>() + w * XTE; };
+  auto sOt = [w](auto S) { return att_lds<T, 4 * decltype(S)::value + 3, W * XTE>() + w * XTE; };
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
   const T* v = (const T*)a.v;
   const T* qT = (const T*)a.qT;
   const T* d_o = (const T*)a.d_o;
   const T* doT = (const T*)a.doT;
-  const int lane = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.y, b = blockIdx.z;
   const int G = a.heads / a.kv_heads, grp = h / G;
   const int S = a.seq;
   const int kt = gridDim.x - 1 - blockIdx.x, kv0 = kt * 32;
@@ -1017,9 +1080,11 @@ __global__ __launch_bounds__(64) void attn_dma_dkv_kernel(const AttnDmaArgs a, c
   const int nqt = (S + 31) / 32;
   const float* lse_h = a.lse + ((int64_t)b * a.heads + h) * S;
   const float* dl_h = delta + ((int64_t)b * a.heads + h) * S;
+  const int n = kt + w < nqt ? (nqt - 1 - kt - w) / W + 1 : 0;  // query tiles kt+w, kt+w+W, ..
+  auto qtile = [&](int t) { return kt + w + W * t; };
 
-  auto issue = [&](int qt, T* sq, T* so, T* sqt, T* sot) __attribute__((always_inline)) {
-    const int q0 = qt * 32;
+  auto issue = [&](int t, T* sq, T* so, T* sqt, T* sot) __attribute__((always_inline)) {
+    const int q0 = qtile(t) * 32;
 #pragma unroll
     for (int j = 0; j < RT::NI; ++j) {
       copy_rows<T, D>(sq, j, lane, q, a.ldq, tok0, q0, S, h * D);
@@ -1037,8 +1102,8 @@ __global__ __launch_bounds__(64) void attn_dma_dkv_kernel(const AttnDmaArgs a, c
   // the next query tile, loaded one step ahead and before that step's tile
   // copies are issued, so waiting for them never waits for the copies.
   float4 lq[4], dq4[4], lq_n[4], dq4_n[4];
-  auto load_ld = [&](int qt, float4 (&L)[4], float4 (&Dl)[4]) __attribute__((always_inline)) {
-    const int q0 = qt * 32;
+  auto load_ld = [&](int t, float4 (&L)[4], float4 (&Dl)[4]) __attribute__((always_inline)) {
+    const int q0 = qtile(t) * 32;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int qr = q0 + 8 * g + 4 * kh;
@@ -1046,8 +1111,8 @@ __global__ __launch_bounds__(64) void attn_dma_dkv_kernel(const AttnDmaArgs a, c
       Dl[g] = qr < S ? *(const float4*)(dl_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  auto compute = [&](const T* sq, const T* so, const T* sqt, const T* sot, int qt) __attribute__((always_inline)) {
-    const int q0 = qt * 32;
+  auto compute = [&](const T* sq, const T* so, const T* sqt, const T* sot, int t) __attribute__((always_inline)) {
+    const int q0 = qtile(t) * 32;
     floatx16 s, dp;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -1079,21 +1144,28 @@ __global__ __launch_bounds__(64) void attn_dma_dkv_kernel(const AttnDmaArgs a, c
       acc_rows_product<T, D>(sqt, dp, i, kh, dk);
     }
   };
-  const int n = nqt - kt;  // query tiles kt .. nqt-1
-  load_ld(kt, lq_n, dq4_n);
-  lds_ring<kDkvStages>(
+  if (n > 0) load_ld(0, lq_n, dq4_n);
+  wave_ring<NS>(
       n, 2 * RT::NI + (TR ? 0 : 2 * TT::NI),
-      [&](int t, auto St) __attribute__((always_inline)) { issue(kt + t, sQ(St), sO(St), sQt(St), sOt(St)); },
+      [&](int t, auto St) __attribute__((always_inline)) { issue(t, sQ(St), sO(St), sQt(St), sOt(St)); },
       [&](int t) __attribute__((always_inline)) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           lq[g] = lq_n[g];
           dq4[g] = dq4_n[g];
         }
-        if (t + 1 < n) load_ld(kt + t + 1, lq_n, dq4_n);
+        if (t + 1 < n) load_ld(t + 1, lq_n, dq4_n);
       },
-      [&](int t, auto St) __attribute__((always_inline)) { compute(sQ(St), sO(St), sQt(St), sOt(St), kt + t); });
+      [&](int t, auto St) __attribute__((always_inline)) { compute(sQ(St), sO(St), sQt(St), sOt(St), t); });
 
+  static_assert((W - 1) * 16 * 64 * 4 <= W * RT::ELEMS * (int)sizeof(T), "combine space");
+  float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    wave_sum_into0<W, 16>(x, w, lane, (float*)&dk[db]);
+    wave_sum_into0<W, 16>(x, w, lane, (float*)&dv[db]);
+  }
+  if (w != 0) return;
   if (kj < S) {
     const float inv = 1.0f / sqrtf((float)D);
     float* krow = dk_part + ((tok0 + kj) * a.heads + h) * (int64_t)D + 4 * kh;
@@ -1112,15 +1184,13 @@ __global__ __launch_bounds__(64) void attn_dma_dkv_kernel(const AttnDmaArgs a, c
 
 template <typename T, int D>
 int fwd_dma_launch(const AttnDmaArgs& a, hipStream_t st) {
-  const int G = a.heads / a.kv_heads;
-  dim3 grid((unsigned)ceil_div(a.seq, 32), (unsigned)a.kv_heads, (unsigned)a.batch);
-  hipLaunchKernelGGL((attn_dma_fwd_kernel<T, D>), grid, dim3(64 * G), 0, st, a);
+  dim3 grid((unsigned)ceil_div(a.seq, 32), (unsigned)a.heads, (unsigned)a.batch);
+  hipLaunchKernelGGL((attn_dma_fwd_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::FWD_W), 0, st, a);
   return check_launch("attn_dma_fwd_kernel");
 }
 
 template <typename T, int D>
 int bwd_dma_launch(const AttnDmaArgs& a, float* delta, float* dk_part, float* dv_part, hipStream_t st) {
-  const int G = a.heads / a.kv_heads;
   const int64_t T_ = (int64_t)a.batch * a.seq;
   AttnArgs da{};
   da.batch = a.batch; da.seq = a.seq; da.heads = a.heads; da.kv_heads = a.kv_heads; da.head_dim = D;
@@ -1128,14 +1198,12 @@ int bwd_dma_launch(const AttnDmaArgs& a, float* delta, float* dk_part, float* dv
   da.d_o = a.do32; da.lddo = a.lddo32;
   hipLaunchKernelGGL(attn_delta_kernel, dim3((unsigned)ceil_div(T_ * a.heads, 4)), dim3(256), 0, st, da, delta);
   QBLK_TRY(check_launch("attn_delta_kernel"));
-  int wq = 1;  // waves per dQ workgroup: the largest divisor of G up to 4
-  for (int c = 4; c >= 1; --c)
-    if (G % c == 0) { wq = c; break; }
-  dim3 gq((unsigned)ceil_div(a.seq, 32), (unsigned)(a.kv_heads * (G / wq)), (unsigned)a.batch);
-  hipLaunchKernelGGL((attn_dma_dq_kernel<T, D>), gq, dim3(64 * wq), 0, st, a, (const float*)delta);
+  dim3 grid((unsigned)ceil_div(a.seq, 32), (unsigned)a.heads, (unsigned)a.batch);
+  hipLaunchKernelGGL((attn_dma_dq_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DQ_W), 0, st, a,
+                     (const float*)delta);
   QBLK_TRY(check_launch("attn_dma_dq_kernel"));
-  dim3 gk((unsigned)ceil_div(a.seq, 32), (unsigned)a.heads, (unsigned)a.batch);
-  hipLaunchKernelGGL((attn_dma_dkv_kernel<T, D>), gk, dim3(64), 0, st, a, (const float*)delta, dk_part, dv_part);
+  hipLaunchKernelGGL((attn_dma_dkv_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DKV_W), 0, st, a,
+                     (const float*)delta, dk_part, dv_part);
   QBLK_TRY(check_launch("attn_dma_dkv_kernel"));
   const int64_t n = T_ * a.kv_heads * D;
   hipLaunchKernelGGL(attn_gqa_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, T_, a.heads,
