@@ -558,58 +558,176 @@ struct AttnElem<float> {
   }
 };
 
-// Row tile: 32 rows x D elements, rows unpadded, 16-byte chunks
-// XOR-swizzled so that 16 consecutive rows read at one chunk hit distinct
-// bank groups of the 256-byte LDS cycle.
+// Row tile: 32 rows x D elements, rows unpadded, 16-byte chunks permuted
+// within each row by an XOR with a function of the row. The function is
+// chosen so that (a) 16 consecutive rows read at one logical chunk hit 16
+// distinct 16-byte bank groups of the 256-byte LDS cycle, and (b) the
+// transposed fp16 reads, which take 4 consecutive rows x 4 consecutive
+// chunks per half-wave, hit 16 distinct groups as well:
+// * 256-byte rows (16 chunks): row bits 0-1 -> chunk bits 2-3, row bits
+//   2-3 -> chunk bits 0-1;
+// * 128-byte rows (8 chunks, two rows per bank cycle): row bit 1 -> chunk
+//   bit 2, row bits 2-3 -> chunk bits 0-1.
 template <typename T, int D>
 struct RowTile {
   static constexpr int NCH = D * (int)sizeof(T) / 16;  // chunks per row
-  static constexpr int RPI = 64 / NCH;                 // rows per 1 KB wave copy
-  static constexpr int NI = 32 / RPI;                  // wave copies per tile
-  static constexpr int STEPS = NCH / 2;                // contraction steps over D
+  static_assert(NCH == 8 || NCH == 16, "row tile width");
+  static constexpr int RPI = 64 / NCH;  // rows per 1 KB wave copy
+  static constexpr int NI = 32 / RPI;   // wave copies per tile
+  static constexpr int STEPS = NCH / 2; // contraction steps over D
   static constexpr int ELEMS = 32 * D;
-  static __device__ __forceinline__ int sw(int row) { return NCH >= 16 ? (row & 15) : ((row >> 1) & 7); }
-  static __device__ __forceinline__ typename AttnElem<T>::Chunk read(const T* t, int row, int lc) {
-    return *(const typename AttnElem<T>::Chunk*)(t + row * D + ((lc ^ sw(row)) * AttnElem<T>::EPC));
+  static __device__ __forceinline__ int sw(int row) {
+    return NCH == 16 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
   }
 };
 
-// Transposed tile: D rows x 32 elements (64 or 128 bytes per row).
+// Transposed tile (fp32 only): D rows x 32 floats (128 bytes per row).
 template <typename T, int D>
 struct TrTile {
-  static constexpr int NCH = 32 * (int)sizeof(T) / 16;  // 4 (fp16) or 8 (fp32)
-  static constexpr int RPI = 64 / NCH;                  // 16 or 8 rows per wave copy
+  static constexpr int NCH = 32 * (int)sizeof(T) / 16;
+  static_assert(NCH == 8, "transposed tiles are fp32");
+  static constexpr int RPI = 64 / NCH;  // 8 rows per wave copy
   static constexpr int NI = D / RPI;
   static constexpr int ELEMS = D * 32;
-  static __device__ __forceinline__ int sw(int row) { return NCH == 4 ? ((row >> 2) & 3) : ((row >> 1) & 7); }
-  static __device__ __forceinline__ typename AttnElem<T>::Chunk read(const T* t, int row, int lc) {
-    return *(const typename AttnElem<T>::Chunk*)(t + row * 32 + ((lc ^ sw(row)) * AttnElem<T>::EPC));
+  static __device__ __forceinline__ int sw(int row) { return (row >> 1) & 7; }
+};
+
+template <typename C>
+__device__ __forceinline__ C lds_at(const void* base, uint32_t off) {
+  return *(const C*)((const char*)base + off);
+}
+
+// Per-lane byte offsets, inside one stage, of the row reads of a row tile:
+// contraction step c reads the chunk 2c + kh of row i of the wave's slot.
+template <typename T, int D>
+struct RowReads {
+  using RT = RowTile<T, D>;
+  uint32_t v[RT::STEPS];
+  __device__ __forceinline__ RowReads(int i, int kh, int slot) {
+#pragma unroll
+    for (int c = 0; c < RT::STEPS; ++c)
+      v[c] = (uint32_t)((slot + i * D + (((2 * c + kh) ^ RT::sw(i)) * AttnElem<T>::EPC)) * (int)sizeof(T));
   }
 };
 
-// Wave copy j of a row tile: rows r0 .. r0+31 of a [T, *] matrix
-// (sequence-local rows past S clamp to S-1), columns col0 .. col0+D-1.
+// Per-lane byte offsets of the fp16 transposed reads (ds_read_b64_tr_b16)
+// of a row tile X [32][D]: fragment (db, s2) holds, for head_dim column
+// db*32 + (lane % 32), the 8 keys 16 s2 + 8 kh .. +7 as two reads rr = 0, 1.
+// Within each 16-lane group, output lane j takes element k from source lane
+// 4k + j/4, so source lane s reads columns 4(s % 4) .. +3 of row s / 4 + base
+// and lane j ends up with 4 consecutive rows of column j. s2 adds 16 rows,
+// which leaves the swizzle unchanged.
+template <int D>
+struct TrReads {
+  using RT = RowTile<f16, D>;
+  uint32_t v[D / 32][2];
+  __device__ __forceinline__ TrReads(int lane, int slot) {
+    const int sl = lane & 15, q1 = (lane >> 4) & 1, kh = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int row = 8 * kh + 4 * rr + (sl >> 2);
+        const int col = db * 32 + 16 * q1 + 4 * (sl & 3);
+        v[db][rr] = (uint32_t)((slot + row * D + (((col >> 3) ^ RT::sw(row)) << 3) + (col & 7)) * 2);
+      }
+  }
+  __device__ __forceinline__ half8 frag(const f16* X, int db, int s2) const {
+    typedef short short4v __attribute__((ext_vector_type(4)));
+    half8 out;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const char* addr = (const char*)X + v[db][rr] + s2 * 16 * D * 2;
+      const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)addr);
+      const half4 h = __builtin_bit_cast(half4, r);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[4 * rr + e] = h[e];
+    }
+    return out;
+  }
+};
+
+// Per-lane byte offsets of the fp32 transposed-tile reads: block db, group
+// g reads the chunk 2g + kh of row db*32 + i.
+template <int D>
+struct TtReads {
+  using TT = TrTile<float, D>;
+  uint32_t v[D / 32][4];
+  __device__ __forceinline__ TtReads(int i, int kh, int slot) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = db * 32 + i;
+        v[db][g] = (uint32_t)((slot + row * 32 + (((2 * g + kh) ^ TT::sw(row)) * 4)) * 4);
+      }
+  }
+};
+
+// Source offsets (bytes) of the wave copies of a tile: copy j moves rows
+// j*RPI .. j*RPI + RPI-1, one 16-byte chunk per lane into the lane's slot,
+// fetched from the logical chunk that the swizzle stores there. Rows are
+// ld elements apart in the source.
+template <typename T, int NCH, int NI, typename Tile>
+struct CopyOffsets {
+  uint32_t v[NI];
+  __device__ __forceinline__ CopyOffsets(int lane, int64_t ld) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int row = j * (64 / NCH) + lane / NCH;
+      const int lc = (lane % NCH) ^ Tile::sw(row);
+      v[j] = (uint32_t)((row * ld + lc * (16 / (int)sizeof(T))) * (int64_t)sizeof(T));
+    }
+  }
+};
 template <typename T, int D>
-__device__ __forceinline__ void copy_rows(T* tile, int j, int lane, const T* base, int64_t ld, int64_t tok0,
-                                          int r0, int S, int col0) {
+using RowCopy = CopyOffsets<T, RowTile<T, D>::NCH, RowTile<T, D>::NI, RowTile<T, D>>;
+template <int D>
+using TrCopy = CopyOffsets<float, TrTile<float, D>::NCH, TrTile<float, D>::NI, TrTile<float, D>>;
+
+// Row tile: rows r0 .. r0+31 of a [T, *] matrix, columns col0 .. col0+D-1.
+// Whole tiles use the precomputed offsets; a tile running past the end of
+// the sequence clamps its rows to S-1 (those rows are masked).
+template <typename T, int D>
+__device__ __forceinline__ void copy_row_tile(T* tile, const T* base, int64_t ld, int64_t tok0, int r0, int S,
+                                              int col0, const RowCopy<T, D>& off, int lane) {
   using RT = RowTile<T, D>;
-  const int row = j * RT::RPI + lane / RT::NCH;
-  const int lc = (lane % RT::NCH) ^ RT::sw(row);
-  dma16(base + (tok0 + min(r0 + row, S - 1)) * ld + col0 + lc * AttnElem<T>::EPC, tile + j * (1024 / sizeof(T)));
+  if (r0 + 32 <= S) {
+    const char* slab = (const char*)(base + (tok0 + r0) * ld + col0);
+#pragma unroll
+    for (int j = 0; j < RT::NI; ++j) dma16(slab + off.v[j], tile + j * (1024 / sizeof(T)));
+  } else {
+#pragma unroll
+    for (int j = 0; j < RT::NI; ++j) {
+      const int row = j * RT::RPI + lane / RT::NCH;
+      const int lc = (lane % RT::NCH) ^ RT::sw(row);
+      dma16(base + (tok0 + min(r0 + row, S - 1)) * ld + col0 + lc * AttnElem<T>::EPC,
+            tile + j * (1024 / sizeof(T)));
+    }
+  }
 }
 
-// Wave copy j of a transposed tile: rows row0 .. row0+D-1 of a [*, T]
-// matrix, columns tok0 + c0 .. +31 (chunks past S read chunk 0 of the
-// sequence; they are masked).
-template <typename T, int D>
-__device__ __forceinline__ void copy_tr(T* tile, int j, int lane, const T* base, int64_t ldt, int64_t tok0,
-                                        int c0, int S, int row0) {
+// Transposed tile (fp32): rows row0 .. row0+D-1 of a [*, T] matrix, columns
+// tok0 + c0 .. +31; chunks past S read chunk 0 of the sequence (masked).
+template <int D>
+__device__ __forceinline__ void copy_tr_tile(float* tile, const float* base, int64_t ldt, int64_t tok0, int c0,
+                                             int S, int row0, const TrCopy<D>& off, int lane) {
+  using T = float;
   using TT = TrTile<T, D>;
-  const int row = j * TT::RPI + lane / TT::NCH;
-  const int lc = (lane % TT::NCH) ^ TT::sw(row);
-  int c = c0 + lc * AttnElem<T>::EPC;
-  if (c >= S) c = 0;
-  dma16(base + (int64_t)(row0 + row) * ldt + tok0 + c, tile + j * (1024 / sizeof(T)));
+  if (c0 + 32 <= S) {
+    const char* slab = (const char*)(base + (int64_t)row0 * ldt + tok0 + c0);
+#pragma unroll
+    for (int j = 0; j < TT::NI; ++j) dma16(slab + off.v[j], tile + j * (1024 / sizeof(T)));
+  } else {
+#pragma unroll
+    for (int j = 0; j < TT::NI; ++j) {
+      const int row = j * TT::RPI + lane / TT::NCH;
+      const int lc = (lane % TT::NCH) ^ TT::sw(row);
+      int c = c0 + lc * AttnElem<T>::EPC;
+      if (c >= S) c = 0;
+      dma16(base + (int64_t)(row0 + row) * ldt + tok0 + c, tile + j * (1024 / sizeof(T)));
+    }
+  }
 }
 
 // Register operand: chunk 2c + kh of a row.
@@ -646,69 +764,54 @@ __device__ __forceinline__ half8 acc_rows_operand(const floatx16& p, int s2) {
   return __builtin_bit_cast(half8, u);
 }
 
-// out[db] += Xt^T-block times the 32 x 32 accumulator p, contracting over
-// the accumulator's rows; Xt is a transposed tile [D][32].
-template <typename T, int D>
-__device__ __forceinline__ void acc_rows_product(const T* Xt, const floatx16& p, int i, int kh,
-                                                 floatx16 (&out)[D / 32]) {
-  using TT = TrTile<T, D>;
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const half8 bp = acc_rows_operand(p, s2);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        out[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(TT::read(Xt, db * 32 + i, 2 * s2 + kh), bp, out[db], 0, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const float4 a = TT::read(Xt, db * 32 + i, 2 * g + kh);
-        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, p[4 * g + 0], out[db], 0, 0, 0);
-        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, p[4 * g + 1], out[db], 0, 0, 0);
-        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, p[4 * g + 2], out[db], 0, 0, 0);
-        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, p[4 * g + 3], out[db], 0, 0, 0);
-      }
-  }
-}
-
-// fp16: the same product with Xt read out of the ROW tile X [32][D] by
-// ds_read_b64_tr_b16. Within each 16-lane group, output lane j takes element
-// k from the lane 4k + j/4, which read 4 consecutive columns at tile row
-// (4k + j/4) / 4 + base; so source lane s reads columns 4(s % 4) .. +3 of
-// tile row base + s / 4, and lane j ends up with 4 consecutive rows of
-// column j: 8 consecutive keys of one head_dim column after two reads.
+// fp16: out[db] += X^T-block times the 32 x 32 accumulator p, contracting
+// over the accumulator's rows; X is a row tile [32][D] read transposed.
 template <int D>
-__device__ __forceinline__ half8 row_tile_tr_frag(const f16* X, int db, int s2, int lane) {
-  using RT = RowTile<f16, D>;
-  typedef short short4v __attribute__((ext_vector_type(4)));
-  const int sl = lane & 15, q1 = (lane >> 4) & 1, kh = lane >> 5;
-  const int col = db * 32 + 16 * q1 + 4 * (sl & 3);
-  half8 out;
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int row = 16 * s2 + 8 * kh + 4 * rr + (sl >> 2);
-    const f16* addr = X + row * D + (((col >> 3) ^ RT::sw(row)) << 3) + (col & 7);
-    const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)addr);
-    const half4 h = __builtin_bit_cast(half4, v);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[4 * rr + e] = h[e];
-  }
-  return out;
-}
-
-template <int D>
-__device__ __forceinline__ void acc_rows_product_tr(const f16* X, const floatx16& p, int lane,
+__device__ __forceinline__ void acc_rows_product_tr(const f16* X, const TrReads<D>& rd, const floatx16& p,
                                                     floatx16 (&out)[D / 32]) {
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
     const half8 bp = acc_rows_operand(p, s2);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
-      out[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(row_tile_tr_frag<D>(X, db, s2, lane), bp, out[db], 0, 0, 0);
+      out[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rd.frag(X, db, s2), bp, out[db], 0, 0, 0);
   }
+}
+
+// fp32: the same product with X^T staged as a transposed tile [D][32]: the
+// accumulator value 4g + r is directly the B operand pairing key 8g + r
+// (lanes 0-31) with key 8g + 4 + r (lanes 32-63).
+template <int D>
+__device__ __forceinline__ void acc_rows_product_tt(const float* Xt, const TtReads<D>& rd, const floatx16& p,
+                                                    floatx16 (&out)[D / 32]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const float4 a = lds_at<float4>(Xt, rd.v[db][g]);
+      out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, p[4 * g + 0], out[db], 0, 0, 0);
+      out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, p[4 * g + 1], out[db], 0, 0, 0);
+      out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, p[4 * g + 2], out[db], 0, 0, 0);
+      out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, p[4 * g + 3], out[db], 0, 0, 0);
+    }
+}
+
+// Transposed-operand reads of the kernels: fp16 reads row tiles through
+// the transposing LDS instruction, fp32 reads staged transposed tiles.
+template <typename T, int D>
+using XtReads = std::conditional_t<sizeof(T) == 2, TrReads<D>, TtReads<D>>;
+
+template <typename T, int D>
+__device__ __forceinline__ XtReads<T, D> make_xt_reads(int lane, int slot_rows, int slot_tt) {
+  if constexpr (sizeof(T) == 2) return TrReads<D>(lane, slot_rows);
+  else return TtReads<D>(lane & 31, lane >> 5, slot_tt);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void acc_rows_product_any(const T* X, const XtReads<T, D>& rd, const floatx16& p,
+                                                     floatx16 (&out)[D / 32]) {
+  if constexpr (sizeof(T) == 2) acc_rows_product_tr<D>(X, rd, p, out);
+  else acc_rows_product_tt<D>(X, rd, p, out);
 }
 
 using I0 = std::integral_constant<int, 0>;
@@ -800,23 +903,34 @@ __device__ __forceinline__ void wave_sum_into0(float* x, int w, int lane, float*
   }
 }
 
+// 2^x on the hardware unit: no denormal rescaling; inputs are <= 0 except
+// under the bounded stale maximum of the forward pass (<= kRescaleSlack).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The forward pass keeps each row's reference maximum m stale until a tile
+// raises the row maximum more than this many powers of two above it, so the
+// output rescale runs on few tiles; probabilities relative to m stay below
+// 2^kRescaleSlack, far inside fp16 range.
+constexpr float kRescaleSlack = 8.f;
+
 // Forward: grid (q tiles, heads, batch), longest query tiles first. The W
-// waves take key tiles w, w+W, ...; each keeps its own running max, sum and
-// output; they are merged with a log-sum-exp combine and wave 0 writes o
-// and lse.
+// waves take key tiles w, w+W, ...; each keeps its own reference max, sum
+// and output; they are merged with a log-sum-exp combine and wave 0 writes
+// o and lse. Only the diagonal tile needs the causal mask: every earlier
+// key tile lies wholly below the diagonal and inside the sequence.
 template <typename T, int D>
 __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(const AttnDmaArgs a) {
   using RT = RowTile<T, D>;
-  using TT = TrTile<T, D>;
+  using TT = TrTile<float, (sizeof(T) == 4 ? D : 64)>;
   using E = AttnElem<T>;
   constexpr int W = AttnSplit<T>::FWD_W, NS = AttnSplit<T>::NS;
   // fp16 stages V as a row tile and reads V^T out of it; fp32 stages V^T
   constexpr bool TR = sizeof(T) == 2;
   constexpr int VE = TR ? RT::ELEMS : TT::ELEMS;
   constexpr int VNI = TR ? RT::NI : TT::NI;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  auto sK = [w](auto S) { return att_lds<T, 2 * decltype(S)::value, W * RT::ELEMS>() + w * RT::ELEMS; };
-  auto sV = [w](auto S) { return att_lds<T, 2 * decltype(S)::value + 1, W * VE>() + w * VE; };
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  auto sK = [](auto S) { return att_lds<T, 2 * decltype(S)::value, W * RT::ELEMS>(); };
+  auto sV = [](auto S) { return att_lds<T, 2 * decltype(S)::value + 1, W * VE>(); };
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
   const T* v = (const T*)a.v;
@@ -828,6 +942,12 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
   const int i = lane & 31, kh = lane >> 5;
   const float sc = kLog2e / sqrtf((float)D);
   const int qi = q0 + i;
+
+  const RowReads<T, D> rk(i, kh, w * RT::ELEMS);
+  const XtReads<T, D> rv = make_xt_reads<T, D>(lane, w * RT::ELEMS, w * VE);
+  const RowCopy<T, D> ck(lane, a.ldk);
+  using VCopy = std::conditional_t<TR, RowCopy<T, D>, TrCopy<(TR ? 64 : D)>>;
+  const VCopy cv(lane, TR ? a.ldv : a.ldt);
 
   typename E::Chunk qc[RT::STEPS];
   load_row_frags<T, D>(q + (tok0 + min(qi, S - 1)) * a.ldq + (int64_t)h * D, kh, qc);
@@ -841,13 +961,9 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
 
   auto issue = [&](int t, T* sk, T* sv) __attribute__((always_inline)) {
     const int kv0 = (w + W * t) * 32;
-#pragma unroll
-    for (int j = 0; j < RT::NI; ++j) copy_rows<T, D>(sk, j, lane, k, a.ldk, tok0, kv0, S, grp * D);
-#pragma unroll
-    for (int j = 0; j < VNI; ++j) {
-      if constexpr (TR) copy_rows<T, D>(sv, j, lane, v, a.ldv, tok0, kv0, S, grp * D);
-      else copy_tr<T, D>(sv, j, lane, vT, a.ldt, tok0, kv0, S, grp * D);
-    }
+    copy_row_tile<T, D>(sk + w * RT::ELEMS, k, a.ldk, tok0, kv0, S, grp * D, ck, lane);
+    if constexpr (TR) copy_row_tile<T, D>(sv + w * VE, v, a.ldv, tok0, kv0, S, grp * D, cv, lane);
+    else copy_tr_tile<D>(sv + w * VE, vT, a.ldt, tok0, kv0, S, grp * D, cv, lane);
   };
   auto compute = [&](const T* sk, const T* sv, int t) __attribute__((always_inline)) {
     const int kv0 = (w + W * t) * 32;
@@ -855,44 +971,45 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
-    for (int c = 0; c < RT::STEPS; ++c) s = E::mma(RT::read(sk, i, 2 * c + kh), qc[c], s);
-    float mx = -INFINITY;
+    for (int c = 0; c < RT::STEPS; ++c) s = E::mma(lds_at<typename E::Chunk>(sk, rk.v[c]), qc[c], s);
+    if (kv0 == q0) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kj = kv0 + 8 * g + 4 * kh + r;
-        float x = s[4 * g + r] * sc;
-        if (kj > qi || kj >= S) x = -INFINITY;
-        s[4 * g + r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = half_max(mx);
-    const float mn = fmaxf(m, mx);
-    const float alpha = exp2f(m - mn);
+        for (int r = 0; r < 4; ++r)
+          if (kv0 + 8 * g + 4 * kh + r > qi) s[4 * g + r] = -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+    mx = half_max(mx) * sc;
+    if (__any(mx > m + kRescaleSlack)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = exp2_hw(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+      m = mn;
+    }
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = exp2f(s[e] - mn);
+      const float p = exp2_hw(fmaf(s[e], sc, -m));
       s[e] = p;
       ps += p;
     }
-    l = l * alpha + half_sum(ps);
-    m = mn;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-    if constexpr (TR) acc_rows_product_tr<D>((const f16*)sv, s, lane, o);
-    else acc_rows_product<T, D>(sv, s, i, kh, o);
+    l += half_sum(ps);
+    acc_rows_product_any<T, D>(sv, rv, s, o);
   };
   wave_ring<NS>(
       n, RT::NI + VNI, [&](int t, auto St) __attribute__((always_inline)) { issue(t, sK(St), sV(St)); },
       [](int) {}, [&](int t, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), t); });
 
   // Combine through the (now free) first stage buffer: every wave learns
-  // every wave's running max, rescales its own sum and output to the common
-  // max, and wave 0 adds them in wave order, 16 values at a time.
+  // every wave's reference max, rescales its own sum and output to the
+  // common max, and wave 0 adds them in wave order, 16 values at a time.
   static_assert((W - 1) * 16 * 64 * 4 <= W * RT::ELEMS * (int)sizeof(T), "combine space");
   float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
   __syncthreads();
@@ -929,22 +1046,21 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
 
 // dQ: grid (q tiles, heads, batch); the W waves take key tiles w, w+W, ...
 // (K, V and, in fp32, K^T through private LDS stages); wave 0 sums the
-// partial dQ in wave order and writes it.
+// partial dQ in wave order and writes it. Only the diagonal tile is masked.
 template <typename T, int D>
 __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(const AttnDmaArgs a,
                                                                              const float* delta) {
   using RT = RowTile<T, D>;
-  using TT = TrTile<T, D>;
+  using TT = TrTile<float, (sizeof(T) == 4 ? D : 64)>;
   using E = AttnElem<T>;
   constexpr int W = AttnSplit<T>::DQ_W, NS = AttnSplit<T>::NS;
   // fp16 reads K^T out of the K row tile; fp32 stages K^T too
   constexpr bool TR = sizeof(T) == 2;
   constexpr int KTE = TR ? 16 : TT::ELEMS;
-  constexpr int KTNI = TR ? 0 : TT::NI;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  auto sK = [w](auto S) { return att_lds<T, 3 * decltype(S)::value, W * RT::ELEMS>() + w * RT::ELEMS; };
-  auto sV = [w](auto S) { return att_lds<T, 3 * decltype(S)::value + 1, W * RT::ELEMS>() + w * RT::ELEMS; };
-  auto sKt = [w](auto S) { return att_lds<T, 3 * decltype(S)::value + 2, W * KTE>() + w * KTE; };
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  auto sK = [](auto S) { return att_lds<T, 3 * decltype(S)::value, W * RT::ELEMS>(); };
+  auto sV = [](auto S) { return att_lds<T, 3 * decltype(S)::value + 1, W * RT::ELEMS>(); };
+  auto sKt = [](auto S) { return att_lds<T, 3 * decltype(S)::value + 2, W * KTE>(); };
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
   const T* v = (const T*)a.v;
@@ -957,6 +1073,10 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
   const int i = lane & 31, kh = lane >> 5;
   const float sc = kLog2e / sqrtf((float)D);
   const int qi = q0 + i, qc_i = min(qi, S - 1);
+
+  const RowReads<T, D> rr(i, kh, w * RT::ELEMS);
+  const XtReads<T, D> rkt = make_xt_reads<T, D>(lane, w * RT::ELEMS, w * KTE);
+  const RowCopy<T, D> ck(lane, a.ldk), cv(lane, a.ldv);
 
   typename E::Chunk qc[RT::STEPS], dc[RT::STEPS];
   load_row_frags<T, D>(q + (tok0 + qc_i) * a.ldq + (int64_t)h * D, kh, qc);
@@ -973,13 +1093,12 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
 
   auto issue = [&](int t, T* sk, T* sv, T* skt) __attribute__((always_inline)) {
     const int kv0 = (w + W * t) * 32;
-#pragma unroll
-    for (int j = 0; j < RT::NI; ++j) {
-      copy_rows<T, D>(sk, j, lane, k, a.ldk, tok0, kv0, S, grp * D);
-      copy_rows<T, D>(sv, j, lane, v, a.ldv, tok0, kv0, S, grp * D);
+    copy_row_tile<T, D>(sk + w * RT::ELEMS, k, a.ldk, tok0, kv0, S, grp * D, ck, lane);
+    copy_row_tile<T, D>(sv + w * RT::ELEMS, v, a.ldv, tok0, kv0, S, grp * D, cv, lane);
+    if constexpr (!TR) {
+      const TrCopy<D> ckt(lane, a.ldt);
+      copy_tr_tile<D>(skt + w * KTE, kT, a.ldt, tok0, kv0, S, grp * D, ckt, lane);
     }
-#pragma unroll
-    for (int j = 0; j < KTNI; ++j) copy_tr<T, D>(skt, j, lane, kT, a.ldt, tok0, kv0, S, grp * D);
   };
   auto compute = [&](const T* sk, const T* sv, const T* skt, int t) __attribute__((always_inline)) {
     const int kv0 = (w + W * t) * 32;
@@ -991,23 +1110,28 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
     }
 #pragma unroll
     for (int c = 0; c < RT::STEPS; ++c) {
-      s = E::mma(RT::read(sk, i, 2 * c + kh), qc[c], s);
-      dp = E::mma(RT::read(sv, i, 2 * c + kh), dc[c], dp);
+      s = E::mma(lds_at<typename E::Chunk>(sk, rr.v[c]), qc[c], s);
+      dp = E::mma(lds_at<typename E::Chunk>(sv, rr.v[c]), dc[c], dp);
     }
+    if (kv0 == q0) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = 4 * g + r;
-        const int kj = kv0 + 8 * g + 4 * kh + r;
-        const float p = (kj > qi || kj >= S) ? 0.f : exp2f(s[e] * sc - lse2);
-        s[e] = p * (dp[e] - dl);  // dS^T, unscaled
-      }
-    if constexpr (TR) acc_rows_product_tr<D>((const f16*)sk, s, lane, dq);
-    else acc_rows_product<T, D>(skt, s, i, kh, dq);
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * g + r;
+          const int kj = kv0 + 8 * g + 4 * kh + r;
+          const float p = (kj > qi || kj >= S) ? 0.f : exp2_hw(fmaf(s[e], sc, -lse2));
+          s[e] = p * (dp[e] - dl);  // dS^T, unscaled
+        }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = exp2_hw(fmaf(s[e], sc, -lse2)) * (dp[e] - dl);
+    }
+    if constexpr (TR) acc_rows_product_any<T, D>(sk, rkt, s, dq);
+    else acc_rows_product_any<T, D>(skt, rkt, s, dq);
   };
   wave_ring<NS>(
-      n, 2 * RT::NI + KTNI,
+      n, 2 * RT::NI + (TR ? 0 : TT::NI),
       [&](int t, auto St) __attribute__((always_inline)) { issue(t, sK(St), sV(St), sKt(St)); }, [](int) {},
       [&](int t, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), sKt(St), t); });
 
@@ -1031,23 +1155,25 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
 // dK, dV per query head: grid (kv tiles, heads, batch); the W waves take
 // query tiles kt+w, kt+w+W, ... (Q, dO and, in fp32, their transposes
 // through private LDS stages); wave 0 sums the partials in wave order into
-// per-head buffers [T, heads, D], summed over each group afterwards.
+// per-head buffers [T, heads, D], summed over each group afterwards. Masks
+// apply only on the diagonal tile and on a query tile that runs past the
+// end of the sequence.
 template <typename T, int D>
 __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(const AttnDmaArgs a,
                                                                                const float* delta,
                                                                                float* dk_part, float* dv_part) {
   using RT = RowTile<T, D>;
-  using TT = TrTile<T, D>;
+  using TT = TrTile<float, (sizeof(T) == 4 ? D : 64)>;
   using E = AttnElem<T>;
   constexpr int W = AttnSplit<T>::DKV_W, NS = AttnSplit<T>::NS;
   // fp16 reads Q^T and dO^T out of the row tiles; fp32 stages them too
   constexpr bool TR = sizeof(T) == 2;
   constexpr int XTE = TR ? 16 : TT::ELEMS;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  auto sQ = [w](auto S) { return att_lds<T, 4 * decltype(S)::value, W * RT::ELEMS>() + w * RT::ELEMS; };
-  auto sO = [w](auto S) { return att_lds<T, 4 * decltype(S)::value + 1, W * RT::ELEMS>() + w * RT::ELEMS; };
-  auto sQt = [w](auto S) { return att_lds<T, 4 * decltype(S)::value + 2, W * XTE>() + w * XTE; };
-  auto sOt = [w](auto S) { return att_lds<T, 4 * decltype(S)::value + 3, W * XTE>() + w * XTE; };
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  auto sQ = [](auto S) { return att_lds<T, 4 * decltype(S)::value, W * RT::ELEMS>(); };
+  auto sO = [](auto S) { return att_lds<T, 4 * decltype(S)::value + 1, W * RT::ELEMS>(); };
+  auto sQt = [](auto S) { return att_lds<T, 4 * decltype(S)::value + 2, W * XTE>(); };
+  auto sOt = [](auto S) { return att_lds<T, 4 * decltype(S)::value + 3, W * XTE>(); };
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
   const T* v = (const T*)a.v;
@@ -1062,6 +1188,10 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
   const int i = lane & 31, kh = lane >> 5;
   const float sc = kLog2e / sqrtf((float)D);
   const int kj = kv0 + i;  // this lane's key (column of every accumulator)
+
+  const RowReads<T, D> rr(i, kh, w * RT::ELEMS);
+  const XtReads<T, D> rxt = make_xt_reads<T, D>(lane, w * RT::ELEMS, w * XTE);
+  const RowCopy<T, D> cq(lane, a.ldq), co(lane, a.lddo);
 
   typename E::Chunk kc[RT::STEPS], vc[RT::STEPS];
   {
@@ -1085,22 +1215,18 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
 
   auto issue = [&](int t, T* sq, T* so, T* sqt, T* sot) __attribute__((always_inline)) {
     const int q0 = qtile(t) * 32;
-#pragma unroll
-    for (int j = 0; j < RT::NI; ++j) {
-      copy_rows<T, D>(sq, j, lane, q, a.ldq, tok0, q0, S, h * D);
-      copy_rows<T, D>(so, j, lane, d_o, a.lddo, tok0, q0, S, h * D);
-    }
+    copy_row_tile<T, D>(sq + w * RT::ELEMS, q, a.ldq, tok0, q0, S, h * D, cq, lane);
+    copy_row_tile<T, D>(so + w * RT::ELEMS, d_o, a.lddo, tok0, q0, S, h * D, co, lane);
     if constexpr (!TR) {
-#pragma unroll
-      for (int j = 0; j < TT::NI; ++j) {
-        copy_tr<T, D>(sqt, j, lane, qT, a.ldt, tok0, q0, S, h * D);
-        copy_tr<T, D>(sot, j, lane, doT, a.ldt, tok0, q0, S, h * D);
-      }
+      const TrCopy<D> ct(lane, a.ldt);
+      copy_tr_tile<D>(sqt + w * XTE, qT, a.ldt, tok0, q0, S, h * D, ct, lane);
+      copy_tr_tile<D>(sot + w * XTE, doT, a.ldt, tok0, q0, S, h * D, ct, lane);
     }
   };
-  // log-sum-exp and delta of this lane's 16 query rows q0 + 8g + 4kh + r of
-  // the next query tile, loaded one step ahead and before that step's tile
-  // copies are issued, so waiting for them never waits for the copies.
+  // log-sum-exp (in powers of two) and delta of this lane's 16 query rows
+  // q0 + 8g + 4kh + r of the next query tile, loaded one step ahead and
+  // before that step's tile copies are issued, so waiting for them never
+  // waits for the copies.
   float4 lq[4], dq4[4], lq_n[4], dq4_n[4];
   auto load_ld = [&](int t, float4 (&L)[4], float4 (&Dl)[4]) __attribute__((always_inline)) {
     const int q0 = qtile(t) * 32;
@@ -1121,27 +1247,34 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
     }
 #pragma unroll
     for (int c = 0; c < RT::STEPS; ++c) {
-      s = E::mma(RT::read(sq, i, 2 * c + kh), kc[c], s);
-      dp = E::mma(RT::read(so, i, 2 * c + kh), vc[c], dp);
+      s = E::mma(lds_at<typename E::Chunk>(sq, rr.v[c]), kc[c], s);
+      dp = E::mma(lds_at<typename E::Chunk>(so, rr.v[c]), vc[c], dp);
     }
+    auto sm = [&](auto Masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = 4 * g + r;
-        const int qq = q0 + 8 * g + 4 * kh + r;
-        const float L = r == 0 ? lq[g].x : r == 1 ? lq[g].y : r == 2 ? lq[g].z : lq[g].w;
-        const float Dl = r == 0 ? dq4[g].x : r == 1 ? dq4[g].y : r == 2 ? dq4[g].z : dq4[g].w;
-        const float p = (kj > qq || qq >= S || kj >= S) ? 0.f : exp2f(s[e] * sc - L * kLog2e);
-        s[e] = p;
-        dp[e] = p * (dp[e] - Dl);
-      }
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * g + r;
+          const float L = r == 0 ? lq[g].x : r == 1 ? lq[g].y : r == 2 ? lq[g].z : lq[g].w;
+          const float Dl = r == 0 ? dq4[g].x : r == 1 ? dq4[g].y : r == 2 ? dq4[g].z : dq4[g].w;
+          float p = exp2_hw(fmaf(s[e], sc, -L * kLog2e));
+          if constexpr (decltype(Masked)::value) {
+            const int qq = q0 + 8 * g + 4 * kh + r;
+            if (kj > qq || qq >= S || kj >= S) p = 0.f;
+          }
+          s[e] = p;
+          dp[e] = p * (dp[e] - Dl);
+        }
+    };
+    if (q0 == kv0 || q0 + 32 > S) sm(std::true_type{});
+    else sm(std::false_type{});
     if constexpr (TR) {
-      acc_rows_product_tr<D>((const f16*)so, s, lane, dv);   // dV^T += dO^T P
-      acc_rows_product_tr<D>((const f16*)sq, dp, lane, dk);  // dK^T += Q^T dS
+      acc_rows_product_any<T, D>(so, rxt, s, dv);   // dV^T += dO^T P
+      acc_rows_product_any<T, D>(sq, rxt, dp, dk);  // dK^T += Q^T dS
     } else {
-      acc_rows_product<T, D>(sot, s, i, kh, dv);
-      acc_rows_product<T, D>(sqt, dp, i, kh, dk);
+      acc_rows_product_any<T, D>(sot, rxt, s, dv);
+      acc_rows_product_any<T, D>(sqt, rxt, dp, dk);
     }
   };
   if (n > 0) load_ld(0, lq_n, dq4_n);
