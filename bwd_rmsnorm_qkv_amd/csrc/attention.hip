@@ -695,13 +695,13 @@ __device__ __forceinline__ void copy_row_tile(T* tile, const T* base, int64_t ld
   if (r0 + 32 <= S) {
     const char* slab = (const char*)(base + (tok0 + r0) * ld + col0);
 #pragma unroll
-    for (int j = 0; j < RT::NI; ++j) dma16(slab + off.v[j], tile + j * (1024 / sizeof(T)));
+    for (int j = 0; j < RT::NI; ++j) dma16_asm(slab + off.v[j], tile + j * (1024 / sizeof(T)));
   } else {
 #pragma unroll
     for (int j = 0; j < RT::NI; ++j) {
       const int row = j * RT::RPI + lane / RT::NCH;
       const int lc = (lane % RT::NCH) ^ RT::sw(row);
-      dma16(base + (tok0 + min(r0 + row, S - 1)) * ld + col0 + lc * AttnElem<T>::EPC,
+      dma16_asm(base + (tok0 + min(r0 + row, S - 1)) * ld + col0 + lc * AttnElem<T>::EPC,
             tile + j * (1024 / sizeof(T)));
     }
   }
@@ -717,7 +717,7 @@ __device__ __forceinline__ void copy_tr_tile(float* tile, const float* base, int
   if (c0 + 32 <= S) {
     const char* slab = (const char*)(base + (int64_t)row0 * ldt + tok0 + c0);
 #pragma unroll
-    for (int j = 0; j < TT::NI; ++j) dma16(slab + off.v[j], tile + j * (1024 / sizeof(T)));
+    for (int j = 0; j < TT::NI; ++j) dma16_asm(slab + off.v[j], tile + j * (1024 / sizeof(T)));
   } else {
 #pragma unroll
     for (int j = 0; j < TT::NI; ++j) {
@@ -725,7 +725,7 @@ __device__ __forceinline__ void copy_tr_tile(float* tile, const float* base, int
       const int lc = (lane % TT::NCH) ^ TT::sw(row);
       int c = c0 + lc * AttnElem<T>::EPC;
       if (c >= S) c = 0;
-      dma16(base + (int64_t)(row0 + row) * ldt + tok0 + c, tile + j * (1024 / sizeof(T)));
+      dma16_asm(base + (int64_t)(row0 + row) * ldt + tok0 + c, tile + j * (1024 / sizeof(T)));
     }
   }
 }

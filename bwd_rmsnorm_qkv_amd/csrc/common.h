@@ -73,6 +73,17 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds, 16, 0, 0);
 }
 
+// The same copy issued through inline assembly, invisible to the compiler's
+// wait-count tracking: with copies the compiler knows to be in flight it
+// makes every LDS read's consumer wait for all outstanding LDS reads. The
+// caller orders these copies itself (wait_vmcnt, then a barrier, before
+// the tile is read); M0 carries the wave-uniform LDS address.
+__device__ __forceinline__ void dma16_asm(const void* g, void* lds) {
+  // the low 32 bits of a generic LDS address are its LDS offset
+  const unsigned m = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m) : "memory", "m0");
+}
+
 // s_waitcnt with only the vector-memory count limited (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
 template <int N>

@@ -467,6 +467,8 @@ struct Core<Prec::F16, TM, TN, BK> {
 
 struct Grid {
   int tiles_m, tiles_n, splits, kchunk;
+  int nfast = 0;  // 1: consecutive tiles walk N first (share the A tile)
+  int vec = 0;    // 1: output rows (and partials, residual) take 16-byte stores
 };
 
 // Final value of C[row, col]: the row pointer `cp` already routed through
@@ -774,7 +776,7 @@ struct DmaOperand {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int64_t adv = KMAJ ? (int64_t)kt * BK : (int64_t)kt * BK * ld;
-      dma16(p[j] + adv, tile + 512 * (NW * j + w));
+      dma16_asm(p[j] + adv, tile + 512 * (NW * j + w));
     }
   }
   // Per-lane element offset of the K-major fragment of K step s within a
@@ -827,8 +829,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int per = total / 8, rem = total % 8;
   const int lt = xcd * per + min(xcd, rem) + slot;
-  const int mt = lt % gd.tiles_m;
-  const int nt = (lt / gd.tiles_m) % gd.tiles_n;
+  const int mt = gd.nfast ? (lt / gd.tiles_n) % gd.tiles_m : lt % gd.tiles_m;
+  const int nt = gd.nfast ? lt % gd.tiles_n : (lt / gd.tiles_m) % gd.tiles_n;
   const int sp = lt / (gd.tiles_m * gd.tiles_n);
   const int m0 = mt * BM, n0 = nt * BN;
   const int kb = sp * gd.kchunk;
@@ -924,54 +926,141 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   if constexpr (NS > 2) if (left > 1) step(I1{}, nfull + 1);
   if constexpr (NS > 3) if (left > 2) step(I2{}, nfull + 2);
 
+  // Epilogue through LDS: the wave parks one 32-row block (tm) of its tile
+  // at a time in its own slice of the (now idle) stage buffers and reads it
+  // back so that every lane writes 16 contiguous bytes and each wave
+  // instruction whole rows of the output: a quarter of the store
+  // instructions of element-wise stores. The float4 slots of a row are
+  // XOR-swizzled by row bit 2, so the two half-waves, which park rows r and
+  // r + 4, write different banks.
+  constexpr int WC = TN * 32;  // wave tile width
+  constexpr int CPR = WC / 4;  // float4 slots per row
+  static_assert(CPR >= 16 && (32 * CPR) % 64 == 0, "epilogue row width");
+  static_assert(BM == BN && 2 * 32 * WC * 4 <= BM * BK * 2 && NW <= 8, "epilogue staging space");
   const int ii = lane & 31, kh = lane >> 5;
-  if (gd.splits > 1) {
-    float* part = d.ws + (int64_t)sp * d.M * d.N;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = m0 + wm * TM * 32 + tm * 32 + 8 * g + 4 * kh + r;
-          if (row >= d.M) continue;
-          float* prow = part + (int64_t)row * d.N;
-#pragma unroll
-          for (int tn = 0; tn < TN; ++tn) {
-            const int col = n0 + wn * TN * 32 + tn * 32 + ii;
-            if (col < d.N) prow[col] = acc[tm][tn][4 * g + r];
-          }
-        }
-    return;
+  __syncthreads();  // every wave is done reading the stages
+  float* ep;
+  switch (w >> 1) {  // two wave slices per stage buffer
+    case 0: ep = (float*)stA(I0{}); break;
+    case 1: ep = (float*)stB(I0{}); break;
+    case 2: ep = (float*)stA(I1{}); break;
+    default: ep = (float*)stB(I1{}); break;
   }
+  ep += (w & 1) * 32 * WC;
+  auto eslot = [](int r, int c) { return r * WC + ((c ^ (((r >> 2) & 1) << 3)) << 2); };
+  const int col0 = n0 + wn * WC;
+  float* part = gd.splits > 1 ? d.ws + (int64_t)sp * d.M * d.N : nullptr;
+  const int bd = d.c_cols_blockdiag;
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
+  for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * TM * 32 + tm * 32 + 8 * g + 4 * kh + r;
-        int lo = 0;
-        float* rp = out_row(d, row, lo);
-        if (!rp) continue;
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          const int col = n0 + wn * TN * 32 + tn * 32 + ii;
-          if (col >= d.N) continue;
-          if (d.c_cols_blockdiag > 0 && (col < lo || col >= lo + d.c_cols_blockdiag)) continue;
-          put_out(d, rp + (col - lo), row, col, acc[tm][tn][4 * g + r]);
+          const int c = tn * 32 + ii;
+          ep[eslot(8 * g + 4 * kh + r, c >> 2) + (c & 3)] = acc[tm][tn][4 * g + r];
+        }
+    const int rowb = m0 + wm * TM * 32 + tm * 32;
+#pragma unroll 1
+    for (int q = 0; q < 32 * CPR / 64; ++q) {
+      const int L = q * 64 + lane, rr = L / CPR, c = L % CPR;
+      const float4 v = *(const float4*)(ep + eslot(rr, c));
+      const int row = rowb + rr, col = col0 + 4 * c;
+      if (row >= d.M || col >= d.N) continue;
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+      if (part) {
+        float* pp = part + (int64_t)row * d.N + col;
+        if (gd.vec && col + 4 <= d.N) *(float4*)pp = v;
+        else
+          for (int j = 0; j < 4 && col + j < d.N; ++j) pp[j] = vv[j];
+        continue;
+      }
+      int lo = 0;
+      float* rp = out_row(d, row, lo);
+      if (!rp) continue;
+      if (gd.vec && col + 4 <= d.N && (bd == 0 || (col >= lo && col + 4 <= lo + bd))) {
+        float4 o = make_float4(d.alpha * v.x, d.alpha * v.y, d.alpha * v.z, d.alpha * v.w);
+        if (d.r) {
+          const float4 rv = *(const float4*)(d.r + (int64_t)row * d.ldr + col);
+          o.x += rv.x;
+          o.y += rv.y;
+          o.z += rv.z;
+          o.w += rv.w;
+        }
+        float4* cp = (float4*)(rp + (col - lo));
+        if (d.accumulate) {
+          const float4 cv = *cp;
+          o.x += cv.x;
+          o.y += cv.y;
+          o.z += cv.z;
+          o.w += cv.w;
+        }
+        *cp = o;
+      } else {
+        for (int j = 0; j < 4 && col + j < d.N; ++j) {
+          if (bd > 0 && (col + j < lo || col + j >= lo + bd)) continue;
+          put_out(d, rp + (col + j - lo), row, col + j, vv[j]);
         }
       }
+    }
+  }
 }
 
 // out = alpha * sum over splits (fixed order) [+ R] [+ C], routed like the
 // direct epilogue.
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmDesc d, int splits) {
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmDesc d, int splits, int vec) {
   const int64_t mn = (int64_t)d.M * d.N;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < mn; e += (int64_t)gridDim.x * blockDim.x) {
-    float s = 0.f;
-    for (int p = 0; p < splits; ++p) s += d.ws[(int64_t)p * mn + e];
-    store_out(d, (int)(e / d.N), (int)(e % d.N), s);
+  const int c0 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c0 >= d.N) return;
+  const int bd = d.c_cols_blockdiag;
+  for (int row = blockIdx.y; row < d.M; row += gridDim.y) {
+    int lo = 0;
+    float* rp = out_row(d, row, lo);
+    if (!rp) return;
+    const float* src = d.ws + (int64_t)row * d.N + c0;
+    if (vec && c0 + 4 <= d.N) {
+      float4 v = *(const float4*)src;
+      for (int p = 1; p < splits; ++p) {
+        const float4 u = *(const float4*)(src + p * mn);
+        v.x += u.x;
+        v.y += u.y;
+        v.z += u.z;
+        v.w += u.w;
+      }
+      if (bd == 0 || (c0 >= lo && c0 + 4 <= lo + bd)) {
+        float4 o = make_float4(d.alpha * v.x, d.alpha * v.y, d.alpha * v.z, d.alpha * v.w);
+        if (d.r) {
+          const float4 rv = *(const float4*)(d.r + (int64_t)row * d.ldr + c0);
+          o.x += rv.x;
+          o.y += rv.y;
+          o.z += rv.z;
+          o.w += rv.w;
+        }
+        float4* cp = (float4*)(rp + (c0 - lo));
+        if (d.accumulate) {
+          const float4 cv = *cp;
+          o.x += cv.x;
+          o.y += cv.y;
+          o.z += cv.z;
+          o.w += cv.w;
+        }
+        *cp = o;
+      } else {
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+        for (int j = 0; j < 4; ++j)
+          if (c0 + j >= lo && c0 + j < lo + bd) put_out(d, rp + (c0 + j - lo), row, c0 + j, vv[j]);
+      }
+    } else {
+      for (int j = 0; j < 4 && c0 + j < d.N; ++j) {
+        float sj = 0.f;
+        for (int p = 0; p < splits; ++p) sj += src[p * mn + j];
+        const int col = c0 + j;
+        if (bd > 0 && (col < lo || col >= lo + bd)) continue;
+        put_out(d, rp + (col - lo), row, col, sj);
+      }
+    }
   }
 }
 
@@ -1075,10 +1164,24 @@ bool nt16_ok(const GemmDesc& d) {
 #endif
 }
 
+// 16-byte epilogue stores: every output row (segment base and stride),
+// the residual and the split-K partials start 16-byte aligned and N and
+// the diagonal-block width are multiples of 4.
+bool out_vec4(const GemmDesc& d, const Grid& g) {
+  if (d.N % 4 != 0 || d.ldc % 4 != 0 || d.c_cols_blockdiag % 4 != 0) return false;
+  for (int s = 0; s < d.c.nseg; ++s)
+    if ((uintptr_t)d.c.p[s] % 16 != 0) return false;
+  if (d.r && ((uintptr_t)d.r % 16 != 0 || d.ldr % 4 != 0)) return false;
+  if (g.splits > 1 && (uintptr_t)d.ws % 16 != 0) return false;
+  return true;
+}
+
 Grid plan(const GemmDesc& d, size_t ws_bytes) {
   if (nt16_ok(d)) {
-    if (nt16_big(d)) return plan_tiles(d, ws_bytes, Nt16Big::bm, Nt16Big::bn, 64);
-    return plan_tiles(d, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64);
+    Grid g = nt16_big(d) ? plan_tiles(d, ws_bytes, Nt16Big::bm, Nt16Big::bn, 64)
+                         : plan_tiles(d, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64);
+    g.vec = out_vec4(d, g);
+    return g;
   }
   const Cfg c = cfg_for(d);
   const int bk = PT<Prec::F16>::BK / (d.prec == Prec::F16 ? 1 : 2) / (c.bk_big ? 1 : 2);
@@ -1087,9 +1190,8 @@ Grid plan(const GemmDesc& d, size_t ws_bytes) {
 
 int finish_splits(const GemmDesc& d, const Grid& g, hipStream_t st) {
   if (g.splits > 1) {
-    const int64_t mn = (int64_t)d.M * d.N;
-    const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(mn, 256), 8192);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, st, d, g.splits);
+    const dim3 grid((unsigned)ceil_div(d.N, 1024), (unsigned)std::min(d.M, 65535));
+    hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, st, d, g.splits, (int)out_vec4(d, g));
     QBLK_TRY(check_launch("splitk_reduce_kernel"));
   }
   return 0;
