@@ -201,7 +201,7 @@ int32_t qblk_fused_cross_entropy(int32_t tokens, int32_t hidden, int32_t vocab, 
   b.c = seg1(dw_lm, vocab); b.ldc = hidden;
   QBLK_TRY(gemm(b, st));
   if (g_final)
-    QBLK_TRY(rmsnorm_backward(tokens, hidden, eps, y_last, g_final, dhf, nullptr, dy_last, dg_final, red, st));
+    QBLK_TRY(rmsnorm_backward(tokens, hidden, eps, y_last, g_final, dhf, nullptr, dy_last, nullptr, dg_final, red, st));
   return QBLK_OK;
 }
 
@@ -325,7 +325,7 @@ int32_t qblk_rmsnorm_backward(int32_t rows, int32_t n, float eps, const float* x
   if (!x || !gamma || !dy || !dx || !dgamma || !scratch) return fail(QBLK_EINVAL, "rmsnorm_backward: null pointer");
   QBLK_TRY(rmsnorm_check(rows, n));
   if (scratch_bytes < rmsnorm_bwd_scratch(rows, n)) return fail(QBLK_EINVAL, "rmsnorm_backward: scratch too small");
-  return rmsnorm_backward(rows, n, eps, x, gamma, dy, dres, dx, dgamma, (float*)scratch, S(stream));
+  return rmsnorm_backward(rows, n, eps, x, gamma, dy, dres, dx, nullptr, dgamma, (float*)scratch, S(stream));
 }
 
 static int check_attn_ld(int32_t heads_or_kv, int32_t d, int64_t ld) {

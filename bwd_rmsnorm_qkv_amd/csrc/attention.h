@@ -49,6 +49,7 @@ struct AttnDmaArgs {
   float* dq; int64_t lddq;
   float* dk; int64_t lddk;
   float* dv; int64_t lddv;
+  f16* dv16 = nullptr; int64_t lddv16 = 0;  // optional fp16 copy of dv
 };
 
 bool attention_dma_supported(int batch, int seq, int heads, int kv_heads, int head_dim);

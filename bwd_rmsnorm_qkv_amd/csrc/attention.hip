@@ -465,7 +465,7 @@ __global__ __launch_bounds__(64) void attn_dkv_kernel(const AttnArgs a, const fl
 
 __global__ void attn_gqa_reduce_kernel(int64_t T, int heads, int kv_heads, int D,
                                        const float* dk_part, const float* dv_part, float* dk,
-                                       int64_t lddk, float* dv, int64_t lddv) {
+                                       int64_t lddk, float* dv, int64_t lddv, f16* dv16, int64_t lddv16) {
   const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   const int64_t n = T * kv_heads * D;
   if (idx >= n) return;
@@ -481,6 +481,7 @@ __global__ void attn_gqa_reduce_kernel(int64_t T, int heads, int kv_heads, int D
   }
   dk[t * lddk + g * D + j] = sk;
   dv[t * lddv + g * D + j] = sv;
+  if (dv16) dv16[t * lddv16 + g * D + j] = (f16)sv;
 }
 
 template <Prec P, int DP>
@@ -508,7 +509,7 @@ int bwd_launch(const AttnArgs& a, float* delta, float* dk_part, float* dv_part, 
   const int64_t n = T * a.kv_heads * a.head_dim;
   hipLaunchKernelGGL(attn_gqa_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, T,
                      a.heads, a.kv_heads, a.head_dim, (const float*)dk_part, (const float*)dv_part, a.dk,
-                     a.lddk, a.dv, a.lddv);
+                     a.lddk, a.dv, a.lddv, (f16*)nullptr, (int64_t)0);
   return check_launch("attn_gqa_reduce_kernel");
 }
 
@@ -1340,7 +1341,8 @@ int bwd_dma_launch(const AttnDmaArgs& a, float* delta, float* dk_part, float* dv
   QBLK_TRY(check_launch("attn_dma_dkv_kernel"));
   const int64_t n = T_ * a.kv_heads * D;
   hipLaunchKernelGGL(attn_gqa_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, T_, a.heads,
-                     a.kv_heads, D, (const float*)dk_part, (const float*)dv_part, a.dk, a.lddk, a.dv, a.lddv);
+                     a.kv_heads, D, (const float*)dk_part, (const float*)dv_part, a.dk, a.lddk, a.dv, a.lddv,
+                     a.dv16, a.lddv16);
   return check_launch("attn_gqa_reduce_kernel");
 }
 

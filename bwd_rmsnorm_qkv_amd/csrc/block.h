@@ -61,6 +61,10 @@ struct Scratch {
   Packed16 pack;
   f16* do16;          // attention on tiled copies: dO copy (fp16 configs)
   float* doT32;       // attention on tiled copies: dO transposed (fp32 configs)
+  // Set by the fp16-copies backward: producers write each output gradient's
+  // fp16 copy straight into a16 and the projection hooks are then passed a
+  // null fp32 gradient (the copy is already in a16).
+  bool prod16 = false;
 };
 
 void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes);

@@ -242,13 +242,15 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
   QBLK_TRY(proj.qkv(s.n1, s.qkv, st));
   QkRopeArgs qa{T, c.seq, c.heads, c.kv_heads, d, c.qk_norm, c.eps, s.qkv, ldqkv, g_q, g_k, s.tab,
                 s.qr, s.kr, s.rho_q, s.rho_k};
+  if (s.q16) {  // attention reads only the fp16 operand copies, written here
+    qa.q16 = s.q16;
+    qa.k16 = s.k16;
+    qa.v16 = s.v16;
+    qa.qr = qa.kr = nullptr;
+  }
   QBLK_TRY(qk_norm_rope_forward(qa, st));
   if (s.q16 || s.qT32) {
-    if (s.q16) {
-      QBLK_TRY(cast_f16(T, qd, s.qr, qd, s.q16, qd, nullptr, 0, st));
-      QBLK_TRY(cast_f16(T, kvd, s.kr, kvd, s.k16, kvd, nullptr, 0, st));
-      QBLK_TRY(cast_f16(T, kvd, s.qkv + qd + kvd, ldqkv, s.v16, kvd, nullptr, 0, st));
-    } else {
+    if (!s.q16) {
       QBLK_TRY(transpose_f32(T, qd, s.qr, qd, s.qT32, T, st));
       QBLK_TRY(transpose_f32(T, kvd, s.kr, kvd, s.kT32, T, st));
       QBLK_TRY(transpose_f32(T, kvd, s.qkv + qd + kvd, ldqkv, s.vT32, T, st));
@@ -283,19 +285,24 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
   const int ldqkv = qd + 2 * kvd;
 
+  // With prod16 each output gradient's fp16 copy comes from its producer
+  // (SwiGLU backward, norm backward, the O projection's dX product, the
+  // attention and QK-norm backward) and the hooks get a null fp32 pointer.
+  const bool p16 = w.prod16, qkv16 = p16 && s.q16 != nullptr;
   // FFN: ds = dy Wd; dWd = dy^T s; SwiGLU backward; dn2 = dg Wg + du Wu; dWg, dWu.
   QBLK_TRY(proj.down(dy, s.s, w.ds, st));
-  QBLK_TRY(swiglu_backward(T, I, s.gu, w.ds, w.dgu, st));
-  QBLK_TRY(proj.gate_up(w.dgu, s.n2, w.dn2, st));
+  QBLK_TRY(swiglu_backward(T, I, s.gu, w.ds, p16 ? nullptr : w.dgu, p16 ? w.a16 : nullptr, st));
+  QBLK_TRY(proj.gate_up(p16 ? nullptr : w.dgu, s.n2, w.dn2, st));
   // post-attention norm backward, plus the second residual's gradient dy
-  QBLK_TRY(rmsnorm_backward(T, h, c.eps, s.r1, g_post, w.dn2, dy, w.dr1, dg_post, w.red, st));
+  QBLK_TRY(rmsnorm_backward(T, h, c.eps, s.r1, g_post, w.dn2, dy, w.dr1, p16 ? w.a16 : nullptr, dg_post, w.red,
+                            st));
   // O projection
-  QBLK_TRY(proj.o(w.dr1, s.o, w.d_o, st));
+  QBLK_TRY(proj.o(p16 ? nullptr : w.dr1, s.o, w.d_o, st));
   // attention backward: dq, dk at the attention inputs; dv straight into dqkv
   if (s.q16 || s.qT32) {
     AttnDmaArgs ab = attn_dma_args(c, s);
     if (s.q16) {
-      QBLK_TRY(cast_f16(T, qd, w.d_o, qd, w.do16, qd, nullptr, 0, st));
+      if (!p16) QBLK_TRY(cast_f16(T, qd, w.d_o, qd, w.do16, qd, nullptr, 0, st));
       ab.d_o = w.do16;
     } else {
       QBLK_TRY(transpose_f32(T, qd, w.d_o, qd, w.doT32, T, st));
@@ -306,6 +313,10 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
     ab.dq = w.dqr; ab.lddq = qd;
     ab.dk = w.dkr; ab.lddk = kvd;
     ab.dv = w.dqkv + qd + kvd; ab.lddv = ldqkv;
+    if (qkv16) {
+      ab.dv16 = w.a16 + qd + kvd;
+      ab.lddv16 = ldqkv;
+    }
     QBLK_TRY(attention_dma_backward(ab, w.attn, st));
   } else {
     AttnArgs aa{};
@@ -323,10 +334,14 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
   }
   QkRopeBwdArgs qb{T, c.seq, c.heads, c.kv_heads, d, c.qk_norm, c.eps, s.qkv, ldqkv, g_q, g_k, s.tab,
                    w.dqr, w.dkr, w.dqkv, dg_q, dg_k};
+  if (qkv16) {
+    qb.dqkv = nullptr;
+    qb.dqkv16 = w.a16;
+  }
   QBLK_TRY(qk_norm_rope_backward(qb, w.red, st));
-  QBLK_TRY(proj.qkv(w.dqkv, s.n1, w.dn1, st));
+  QBLK_TRY(proj.qkv(qkv16 ? nullptr : w.dqkv, s.n1, w.dn1, st));
   // input norm backward, plus the first residual's gradient dr1
-  QBLK_TRY(rmsnorm_backward(T, h, c.eps, x, g_in, w.dn1, w.dr1, dx, dg_in, w.red, st));
+  QBLK_TRY(rmsnorm_backward(T, h, c.eps, x, g_in, w.dn1, w.dr1, dx, nullptr, dg_in, w.red, st));
   return QBLK_OK;
 }
 
@@ -426,27 +441,35 @@ int dense16_backward(const qblk_config& c, const qblk_block_params& p, const qbl
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate, qkv = qd + 2 * kvd;
   Packed16 W;
   QBLK_TRY(weights16(c, p, w, W, st));
+  // dY's fp16 copy is in a16 already when the hook is passed no fp32 dY;
+  // dx16 (optional) receives an fp16 copy of dX.
   auto dxdw = [&](const float* dyv, int n_out, const f16* x16, int n_in, const f16* wt, Seg cseg, float* dxo,
-                  hipStream_t s_) -> int {
-    QBLK_TRY(cast_f16(T, n_out, dyv, n_out, w.a16, n_out, nullptr, 0, s_));
-    QBLK_TRY(gemm(g16(w, Layout::NN, T, n_in, n_out, w.a16, n_out, wt, n_in, seg1(dxo, T), n_in), s_));
+                  f16* dx16, hipStream_t s_) -> int {
+    if (dyv) QBLK_TRY(cast_f16(T, n_out, dyv, n_out, w.a16, n_out, nullptr, 0, s_));
+    GemmDesc gx = g16(w, Layout::NN, T, n_in, n_out, w.a16, n_out, wt, n_in, seg1(dxo, T), n_in);
+    gx.c16 = dx16;
+    gx.ldc16 = n_in;
+    QBLK_TRY(gemm(gx, s_));
     return gemm(g16(w, Layout::TN, n_out, n_in, T, w.a16, n_out, x16, n_in, cseg, n_in), s_);
   };
   ProjBwd pb;
   pb.down = [&](const float* dyv, const float*, float* ds, hipStream_t s_) {
-    return dxdw(dyv, h, s.s16, I, W.d, seg1(gr.w_down, h), ds, s_);
+    return dxdw(dyv, h, s.s16, I, W.d, seg1(gr.w_down, h), ds, nullptr, s_);
   };
   pb.gate_up = [&](const float* dgu, const float*, float* dn2, hipStream_t s_) {
-    return dxdw(dgu, 2 * I, s.n2_16, h, W.gu, seg3(gr.w_gate, I, gr.w_up, I, nullptr, 0), dn2, s_);
+    return dxdw(dgu, 2 * I, s.n2_16, h, W.gu, seg3(gr.w_gate, I, gr.w_up, I, nullptr, 0), dn2, nullptr, s_);
   };
   pb.o = [&](const float* dr1, const float*, float* d_o, hipStream_t s_) {
-    return dxdw(dr1, h, s.o16, qd, W.o, seg1(gr.w_o, h), d_o, s_);
+    // the attention backward reads dO's fp16 copy
+    return dxdw(dr1, h, s.o16, qd, W.o, seg1(gr.w_o, h), d_o, s.q16 ? w.do16 : nullptr, s_);
   };
   pb.qkv = [&](const float* dqkv, const float*, float* dn1, hipStream_t s_) {
-    return dxdw(dqkv, qkv, s.n1_16, h, W.qkv, seg3(gr.w_q, qd, gr.w_k, kvd, gr.w_v, kvd), dn1, s_);
+    return dxdw(dqkv, qkv, s.n1_16, h, W.qkv, seg3(gr.w_q, qd, gr.w_k, kvd, gr.w_v, kvd), dn1, nullptr, s_);
   };
+  Scratch w16 = w;
+  w16.prod16 = true;
   return block_backward_impl(c, pb, p.g_in, p.g_post, p.g_q, p.g_k, x, dy, s, dx, gr.g_in, gr.g_post,
-                             gr.g_q, gr.g_k, w, st);
+                             gr.g_q, gr.g_k, w16, st);
 }
 
 }  // namespace

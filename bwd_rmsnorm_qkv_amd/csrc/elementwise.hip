@@ -29,81 +29,129 @@ __global__ void rope_table_kernel(int seq, int half, int d, double log_theta, fl
   tab[idx] = make_float2((float)cos(a), (float)sin(a));
 }
 
-// Forward: one wave per (t, head) over the H + KV heads.
+// Forward: one wave per (t, head) over the H + KV heads (plus the KV value
+// heads when their fp16 copy is requested).
 __global__ __launch_bounds__(256) void qk_rope_fwd_kernel(QkRopeArgs a) {
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nh = a.heads + a.kv_heads;
+  const int nqk = a.heads + a.kv_heads;
+  const int nh = nqk + (a.v16 ? a.kv_heads : 0);
   if (item >= a.T * nh) return;
   const int t = item / nh, head = item % nh;
   const int d = a.head_dim, half = d >> 1;
+  if (head >= nqk) {  // value head: fp16 copy only
+    const int hh = head - nqk;
+    const float* src = a.qkv + (int64_t)t * a.ld_qkv + (int64_t)nqk * d + hh * d;
+    f16* dst = a.v16 + ((int64_t)t * a.kv_heads + hh) * d;
+    for (int c = lane; c < d; c += 64) dst[c] = (f16)src[c];
+    return;
+  }
   const bool is_q = head < a.heads;
   const int hh = is_q ? head : head - a.heads;
+  const int64_t orow = is_q ? ((int64_t)t * a.heads + hh) * d : ((int64_t)t * a.kv_heads + hh) * d;
   const float* src = a.qkv + (int64_t)t * a.ld_qkv + (is_q ? 0 : a.heads * d) + hh * d;
-  float* dst = is_q ? a.qr + ((int64_t)t * a.heads + hh) * d : a.kr + ((int64_t)t * a.kv_heads + hh) * d;
+  float* dst = is_q ? a.qr : a.kr;
+  f16* dst16 = is_q ? a.q16 : a.k16;
   const float* g = is_q ? a.g_q : a.g_k;
   const bool act = lane < half;
-  float x0 = act ? src[lane] : 0.f, x1 = act ? src[lane + half] : 0.f;
+  const int li = act ? lane : 0;
+  float x0 = src[li], x1 = src[li + half];
+  const float2 cs = a.tab[(t % a.seq) * half + li];
+  if (!act) x0 = x1 = 0.f;
   if (a.qk_norm) {
+    const float ga = g[li], gb = g[li + half];
     const float ss = wave_sum(x0 * x0 + x1 * x1);
     const float rho = 1.0f / sqrtf(ss / (float)d + a.eps);
     if (lane == 0) (is_q ? a.rho_q[(int64_t)t * a.heads + hh] : a.rho_k[(int64_t)t * a.kv_heads + hh]) = rho;
-    if (act) {
-      x0 = x0 * rho * g[lane];
-      x1 = x1 * rho * g[lane + half];
-    }
+    x0 = x0 * rho * ga;
+    x1 = x1 * rho * gb;
   }
   if (act) {
-    const float2 cs = a.tab[(t % a.seq) * half + lane];
-    dst[lane] = x0 * cs.x - x1 * cs.y;
-    dst[lane + half] = x1 * cs.x + x0 * cs.y;
+    const float o0 = x0 * cs.x - x1 * cs.y, o1 = x1 * cs.x + x0 * cs.y;
+    if (dst) {
+      dst[orow + lane] = o0;
+      dst[orow + lane + half] = o1;
+    }
+    if (dst16) {
+      dst16[orow + lane] = (f16)o0;
+      dst16[orow + lane + half] = (f16)o1;
+    }
   }
 }
 
-// Backward for one group of heads (the q heads or the k heads): one wave per
-// (t, head), grid-stride; dgamma partials per workgroup in scratch.
-__global__ __launch_bounds__(256) void qk_rope_bwd_kernel(int T, int seq, int nh, int d, int qk_norm,
-                                                          float eps, const float* __restrict__ qkv,
-                                                          int64_t ld, int col0,
-                                                          const float* __restrict__ g,
-                                                          const float2* __restrict__ tab,
-                                                          const float* __restrict__ dsrc,
-                                                          float* __restrict__ dqkv,
-                                                          float* __restrict__ partial) {
+// Backward: blocks [0, nbq) take the q heads, the rest the k heads; each
+// wave takes kQkRows consecutive (t, head) rows with all their loads issued
+// before any arithmetic (rows past the end load the last row and are
+// skipped). dgamma partials: one row per workgroup, in a fixed order.
+constexpr int kQkRows = 8;
+
+__global__ __launch_bounds__(256) void qk_rope_bwd_kernel(QkRopeBwdArgs a, int nbq, float* __restrict__ part_q,
+                                                          float* __restrict__ part_k) {
   __shared__ float red[4][128];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int half = d >> 1;
+  const bool is_q = (int)blockIdx.x < nbq;
+  const int blk = is_q ? blockIdx.x : blockIdx.x - nbq;
+  const int nh = is_q ? a.heads : a.kv_heads;
+  const int d = a.head_dim, half = d >> 1;
+  const int col0 = is_q ? 0 : a.heads * d;
+  const float* __restrict__ dsrc = is_q ? a.dqr : a.dkr;
+  const float* __restrict__ g = is_q ? a.g_q : a.g_k;
   const bool act = lane < half;
+  const int li = act ? lane : 0;
+  const int rows = a.T * nh;
+  const int r0 = (blk * 4 + w) * kQkRows;
+  float y0[kQkRows], y1[kQkRows], x0[kQkRows], x1[kQkRows];
+  float2 cs[kQkRows];
+#pragma unroll
+  for (int j = 0; j < kQkRows; ++j) {
+    const int row = min(r0 + j, rows - 1), t = row / nh, hh = row % nh;
+    y0[j] = dsrc[(int64_t)row * d + li];
+    y1[j] = dsrc[(int64_t)row * d + li + half];
+    cs[j] = a.tab[(t % a.seq) * half + li];
+    if (a.qk_norm) {
+      const float* xr = a.qkv + (int64_t)t * a.ld_qkv + col0 + hh * d;
+      x0[j] = xr[li];
+      x1[j] = xr[li + half];
+    }
+  }
+  const float ga = a.qk_norm ? g[li] : 0.f, gb = a.qk_norm ? g[li + half] : 0.f;
   float dg0 = 0.f, dg1 = 0.f;
-  for (int item = blockIdx.x * 4 + w; item < T * nh; item += gridDim.x * 4) {
-    const int t = item / nh, hh = item % nh;
-    const float* dr = dsrc + ((int64_t)t * nh + hh) * d;
-    const float2 cs = act ? tab[(t % seq) * half + lane] : make_float2(1.f, 0.f);
-    const float y0 = act ? dr[lane] : 0.f, y1 = act ? dr[lane + half] : 0.f;
+#pragma unroll
+  for (int j = 0; j < kQkRows; ++j) {
+    const int row = r0 + j;
+    if (row >= rows) break;
+    const int t = row / nh, hh = row % nh;
     // transpose of the rotation
-    const float g0 = y0 * cs.x + y1 * cs.y;
-    const float g1 = y1 * cs.x - y0 * cs.y;
-    float* out = dqkv + (int64_t)t * ld + col0 + hh * d;
-    if (qk_norm) {
-      const float* xr = qkv + (int64_t)t * ld + col0 + hh * d;
-      const float x0 = act ? xr[lane] : 0.f, x1 = act ? xr[lane + half] : 0.f;
-      const float ss = wave_sum(x0 * x0 + x1 * x1);
-      const float rho = 1.0f / sqrtf(ss / (float)d + eps);
-      const float xh0 = x0 * rho, xh1 = x1 * rho;
-      const float e0 = act ? g[lane] * g0 : 0.f, e1 = act ? g[lane + half] * g1 : 0.f;
+    const float g0 = y0[j] * cs[j].x + y1[j] * cs[j].y;
+    const float g1 = y1[j] * cs[j].x - y0[j] * cs[j].y;
+    float o0 = g0, o1 = g1;
+    if (a.qk_norm) {
+      const float xa = act ? x0[j] : 0.f, xb = act ? x1[j] : 0.f;
+      const float ss = wave_sum(xa * xa + xb * xb);
+      const float rho = 1.0f / sqrtf(ss / (float)d + a.eps);
+      const float xh0 = xa * rho, xh1 = xb * rho;
+      const float e0 = act ? ga * g0 : 0.f, e1 = act ? gb * g1 : 0.f;
       const float dot = wave_sum(e0 * xh0 + e1 * xh1) / (float)d;
+      o0 = rho * (e0 - xh0 * dot);
+      o1 = rho * (e1 - xh1 * dot);
       if (act) {
-        out[lane] = rho * (e0 - xh0 * dot);
-        out[lane + half] = rho * (e1 - xh1 * dot);
         dg0 += g0 * xh0;
         dg1 += g1 * xh1;
       }
-    } else if (act) {
-      out[lane] = g0;
-      out[lane + half] = g1;
+    }
+    if (act) {
+      const int64_t o = (int64_t)t * a.ld_qkv + col0 + hh * d + lane;
+      if (a.dqkv) {
+        a.dqkv[o] = o0;
+        a.dqkv[o + half] = o1;
+      }
+      if (a.dqkv16) {
+        a.dqkv16[o] = (f16)o0;
+        a.dqkv16[o + half] = (f16)o1;
+      }
     }
   }
-  if (!qk_norm) return;
+  if (!a.qk_norm) return;
   if (act) {
     red[w][lane] = dg0;
     red[w][lane + half] = dg1;
@@ -111,7 +159,7 @@ __global__ __launch_bounds__(256) void qk_rope_bwd_kernel(int T, int seq, int nh
   __syncthreads();
   if (threadIdx.x < d) {
     const int c = threadIdx.x;
-    partial[(int64_t)blockIdx.x * d + c] = red[0][c] + red[1][c] + red[2][c] + red[3][c];
+    (is_q ? part_q : part_k)[(int64_t)blk * d + c] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
   }
 }
 
@@ -120,7 +168,7 @@ __global__ void fill_kernel(float* p, int n, float v) {
   if (i < n) p[i] = v;
 }
 
-int qk_parts(int T, int nh) { return (int)std::min<int64_t>(ceil_div((int64_t)T * nh, 4), 240); }
+int qk_parts(int T, int nh) { return (int)ceil_div((int64_t)T * nh, 4 * kQkRows); }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
@@ -151,7 +199,8 @@ __device__ __forceinline__ void swiglu_grad(float g, float u, float ds, float& d
 }
 
 __global__ void swiglu_bwd_kernel(int T, int I, const float* __restrict__ gu,
-                                  const float* __restrict__ ds, float* __restrict__ dgu) {
+                                  const float* __restrict__ ds, float* __restrict__ dgu,
+                                  f16* __restrict__ dgu16) {
   const int64_t n4 = (int64_t)T * I / 4;
   const int i4 = I / 4;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n4;
@@ -165,8 +214,14 @@ __global__ void swiglu_bwd_kernel(int T, int I, const float* __restrict__ gu,
     swiglu_grad(g.y, u.y, d.y, dg.y, du.y);
     swiglu_grad(g.z, u.z, d.z, dg.z, du.z);
     swiglu_grad(g.w, u.w, d.w, dg.w, du.w);
-    ((float4*)(dgu + t * 2 * I))[j] = dg;
-    ((float4*)(dgu + t * 2 * I + I))[j] = du;
+    if (dgu) {
+      ((float4*)(dgu + t * 2 * I))[j] = dg;
+      ((float4*)(dgu + t * 2 * I + I))[j] = du;
+    }
+    if (dgu16) {
+      ((half4*)(dgu16 + t * 2 * I))[j] = to_half4(dg);
+      ((half4*)(dgu16 + t * 2 * I + I))[j] = to_half4(du);
+    }
   }
 }
 
@@ -182,7 +237,7 @@ int rope_table(int seq, int head_dim, float theta, float2* tab, hipStream_t st) 
 }
 
 int qk_norm_rope_forward(const QkRopeArgs& a, hipStream_t st) {
-  const int64_t items = (int64_t)a.T * (a.heads + a.kv_heads);
+  const int64_t items = (int64_t)a.T * (a.heads + a.kv_heads + (a.v16 ? a.kv_heads : 0));
   hipLaunchKernelGGL(qk_rope_fwd_kernel, dim3((unsigned)ceil_div(items, 4)), dim3(256), 0, st, a);
   return check_launch("qk_rope_fwd_kernel");
 }
@@ -196,13 +251,8 @@ int qk_norm_rope_backward(const QkRopeBwdArgs& a, float* scratch, hipStream_t st
   const int pq = qk_parts(a.T, a.heads), pk = qk_parts(a.T, a.kv_heads);
   float* part_q = scratch;
   float* part_k = scratch + (size_t)pq * d;
-  hipLaunchKernelGGL(qk_rope_bwd_kernel, dim3((unsigned)pq), dim3(256), 0, st, a.T, a.seq, a.heads, d,
-                     a.qk_norm, a.eps, a.qkv, a.ld_qkv, 0, a.g_q, a.tab, a.dqr, a.dqkv, part_q);
-  QBLK_TRY(check_launch("qk_rope_bwd_kernel(q)"));
-  hipLaunchKernelGGL(qk_rope_bwd_kernel, dim3((unsigned)pk), dim3(256), 0, st, a.T, a.seq, a.kv_heads,
-                     d, a.qk_norm, a.eps, a.qkv, a.ld_qkv, a.heads * d, a.g_k, a.tab, a.dkr, a.dqkv,
-                     part_k);
-  QBLK_TRY(check_launch("qk_rope_bwd_kernel(k)"));
+  hipLaunchKernelGGL(qk_rope_bwd_kernel, dim3((unsigned)(pq + pk)), dim3(256), 0, st, a, pq, part_q, part_k);
+  QBLK_TRY(check_launch("qk_rope_bwd_kernel"));
   if (a.qk_norm) {
     QBLK_TRY(colsum(pq, d, part_q, a.dg_q, st));
     QBLK_TRY(colsum(pk, d, part_k, a.dg_k, st));
@@ -220,9 +270,9 @@ int swiglu_forward(int T, int I, const float* gu, float* s, f16* s16, hipStream_
   return check_launch("swiglu_fwd_kernel");
 }
 
-int swiglu_backward(int T, int I, const float* gu, const float* ds, float* dgu, hipStream_t st) {
+int swiglu_backward(int T, int I, const float* gu, const float* ds, float* dgu, f16* dgu16, hipStream_t st) {
   const int64_t n4 = (int64_t)T * I / 4;
-  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(grid_for(n4)), dim3(256), 0, st, T, I, gu, ds, dgu);
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(grid_for(n4)), dim3(256), 0, st, T, I, gu, ds, dgu, dgu16);
   return check_launch("swiglu_bwd_kernel");
 }
 

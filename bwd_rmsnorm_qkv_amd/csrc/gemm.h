@@ -92,6 +92,10 @@ struct GemmDesc {
   // are added in a fixed order by a second kernel). NULL: no split.
   float* ws = nullptr;
   size_t ws_bytes = 0;
+  // Optional fp16 copy of the final output (single C segment, no
+  // diagonal-block mode): c16[row * ldc16 + col] = (fp16) C[row, col].
+  f16* c16 = nullptr;
+  int64_t ldc16 = 0;
 };
 
 int gemm(const GemmDesc& d, hipStream_t stream);

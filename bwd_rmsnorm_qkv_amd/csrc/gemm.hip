@@ -998,10 +998,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
           o.w += cv.w;
         }
         *cp = o;
+        if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + col) = to_half4(o);
       } else {
         for (int j = 0; j < 4 && col + j < d.N; ++j) {
           if (bd > 0 && (col + j < lo || col + j >= lo + bd)) continue;
           put_out(d, rp + (col + j - lo), row, col + j, vv[j]);
+          if (d.c16) d.c16[(int64_t)row * d.ldc16 + col + j] = (f16)rp[col + j - lo];
         }
       }
     }
@@ -1047,6 +1049,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmDesc d, in
           o.w += cv.w;
         }
         *cp = o;
+        if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + c0) = to_half4(o);
       } else {
         const float vv[4] = {v.x, v.y, v.z, v.w};
         for (int j = 0; j < 4; ++j)
@@ -1059,6 +1062,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmDesc d, in
         const int col = c0 + j;
         if (bd > 0 && (col < lo || col >= lo + bd)) continue;
         put_out(d, rp + (col - lo), row, col, sj);
+        if (d.c16) d.c16[(int64_t)row * d.ldc16 + col] = (f16)rp[col - lo];
       }
     }
   }
@@ -1173,6 +1177,7 @@ bool out_vec4(const GemmDesc& d, const Grid& g) {
     if ((uintptr_t)d.c.p[s] % 16 != 0) return false;
   if (d.r && ((uintptr_t)d.r % 16 != 0 || d.ldr % 4 != 0)) return false;
   if (g.splits > 1 && (uintptr_t)d.ws % 16 != 0) return false;
+  if (d.c16 && ((uintptr_t)d.c16 % 8 != 0 || d.ldc16 % 4 != 0)) return false;
   return true;
 }
 
@@ -1281,7 +1286,30 @@ int elems16(Src s) { return s == Src::F32 ? 4 : 8; }
 
 }  // namespace
 
+namespace {
+__global__ void c16_copy_kernel(int M, int N, const float* __restrict__ c, int64_t ldc, f16* __restrict__ c16,
+                                int64_t ldc16) {
+  const int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (e >= (int64_t)M * N) return;
+  const int64_t r = e / N, col = e % N;
+  c16[r * ldc16 + col] = (f16)c[r * ldc + col];
+}
+}  // namespace
+
 int gemm(const GemmDesc& d, hipStream_t st) {
+  if (d.c16) {
+    if (d.c.nseg != 1 || d.c_cols_blockdiag > 0)
+      return fail(QBLK_EINVAL, "gemm: the fp16 output copy needs a single C segment");
+    if (!nt16_ok(d)) {  // kernels without the fp16 epilogue: copy afterwards
+      GemmDesc e = d;
+      e.c16 = nullptr;
+      QBLK_TRY(gemm(e, st));
+      const int64_t mn = (int64_t)d.M * d.N;
+      hipLaunchKernelGGL(c16_copy_kernel, dim3((unsigned)ceil_div(mn, 256)), dim3(256), 0, st, d.M, d.N,
+                         (const float*)d.c.p[0], d.ldc, d.c16, d.ldc16);
+      return check_launch("c16_copy_kernel");
+    }
+  }
   if (d.M <= 0 || d.N <= 0 || d.K < 0) return fail(QBLK_EINVAL, "gemm: bad shape %d x %d x %d", d.M, d.N, d.K);
   if (d.K == 0 && d.ext.kext == 0) return fail(QBLK_EINVAL, "gemm: empty contraction");
   // Contiguous dimensions and leading dimensions are read in 16-byte chunks.

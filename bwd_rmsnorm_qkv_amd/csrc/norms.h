@@ -16,7 +16,7 @@ int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res
                     hipStream_t st);
 // dx = RMSNorm backward (+ dres); dgamma overwritten; scratch: rmsnorm_bwd_scratch.
 int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* gamma,
-                     const float* dy, const float* dres, float* dx, float* dgamma, float* scratch,
+                     const float* dy, const float* dres, float* dx, f16* dx16, float* dgamma, float* scratch,
                      hipStream_t st);
 // out[c] = sum_p partial[p][c], fixed order.
 int colsum(int parts, int n, const float* partial, float* out, hipStream_t st);
@@ -34,7 +34,10 @@ struct QkRopeArgs {
   int64_t ld_qkv;
   const float *g_q, *g_k;
   const float2* tab;
-  float *qr, *kr, *rho_q, *rho_k;
+  float *qr, *kr, *rho_q, *rho_k;  // qr, kr may be null (fp16 outputs only)
+  // optional fp16 copies of the attention operands [T, heads d] and
+  // [T, kv_heads d] (v16 copies V from qkv unchanged)
+  f16 *q16 = nullptr, *k16 = nullptr, *v16 = nullptr;
 };
 int qk_norm_rope_forward(const QkRopeArgs& a, hipStream_t st);
 
@@ -49,8 +52,9 @@ struct QkRopeBwdArgs {
   const float *g_q, *g_k;
   const float2* tab;
   const float *dqr, *dkr;  // [T, H d], [T, KV d]
-  float* dqkv;             // [T, ld_qkv]
+  float* dqkv;             // [T, ld_qkv] (may be null)
   float *dg_q, *dg_k;
+  f16* dqkv16 = nullptr;   // optional fp16 copy of the q and k columns of dqkv
 };
 size_t qk_norm_rope_bwd_scratch(int T, int heads, int kv_heads, int head_dim);
 int qk_norm_rope_backward(const QkRopeBwdArgs& a, float* scratch, hipStream_t st);
@@ -58,7 +62,7 @@ int qk_norm_rope_backward(const QkRopeBwdArgs& a, float* scratch, hipStream_t st
 // s = silu(g) * u with g, u the two halves of gu [T, 2I]; s fp32 and/or fp16.
 int swiglu_forward(int T, int I, const float* gu, float* s, f16* s16, hipStream_t st);
 // dgu = [ds * u * silu'(g) | ds * silu(g)].
-int swiglu_backward(int T, int I, const float* gu, const float* ds, float* dgu, hipStream_t st);
+int swiglu_backward(int T, int I, const float* gu, const float* ds, float* dgu, f16* dgu16, hipStream_t st);
 
 // fp16 copies of an fp32 matrix in [R, C] (row stride ldi): out [R, C]
 // (stride ldo) and/or outT [C, R] (stride ldt); either may be NULL.

@@ -35,31 +35,35 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(int rows, int n, float
   const int n4 = n >> 2;
   const float4* xr = (const float4*)(x + (int64_t)row * n);
   const float4* rr = res ? (const float4*)(res + (int64_t)row * n) : nullptr;
+  // Loads go to clamped (always valid) columns and are masked afterwards,
+  // so a row's loads are all in flight together instead of one branch each.
   float4 v[VPL];
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
-    const int c = lane + j * 64;
-    if (c < n4) {
-      float4 a = xr[c];
-      if (rr) {
-        const float4 b = rr[c];
-        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-      }
-      v[j] = a;
-      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    const int c = lane + j * 64, cc = min(c, n4 - 1);
+    float4 a = xr[cc];
+    if (rr) {
+      const float4 b = rr[cc];
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
     }
+    if (c >= n4) a = make_float4(0.f, 0.f, 0.f, 0.f);
+    v[j] = a;
+    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
   }
   ss = wave_sum(ss);
   const float rho = 1.0f / sqrtf(ss / (float)n + eps);
   if (lane == 0 && rho_out) rho_out[row] = rho;
   const float4* gr = (const float4*)gamma;
+  float4 gv[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) gv[j] = gr[min(lane + j * 64, n4 - 1)];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int c = lane + j * 64;
     if (c < n4) {
       if (sum_out) ((float4*)(sum_out + (int64_t)row * n))[c] = v[j];
-      const float4 g = gr[c];
+      const float4 g = gv[j];
       float4 o;
       o.x = v[j].x * rho * g.x;
       o.y = v[j].y * rho * g.y;
@@ -78,6 +82,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int rows, int n, float
                                                           const float* __restrict__ dy,
                                                           const float* __restrict__ dres,
                                                           float* __restrict__ dx,
+                                                          f16* __restrict__ dx16,
                                                           float* __restrict__ partial) {
   __shared__ float4 red[kWavesPerBlock][VPL * 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -90,18 +95,25 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int rows, int n, float
   for (int row = blockIdx.x * kWavesPerBlock + w; row < rows; row += gridDim.x * kWavesPerBlock) {
     const float4* xr = (const float4*)(x + (int64_t)row * n);
     const float4* dr = (const float4*)(dy + (int64_t)row * n);
-    float4 xv[VPL], e[VPL], dv[VPL];
+    // clamped loads, masked afterwards: all of a row's loads in flight at once
+    float4 xv[VPL], e[VPL], dv[VPL], rv[VPL];
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
-      const int c = lane + j * 64;
-      if (c < n4) {
-        xv[j] = xr[c];
-        dv[j] = dr[c];
-        const float4 g = gr[c];
-        e[j] = make_float4(g.x * dv[j].x, g.y * dv[j].y, g.z * dv[j].z, g.w * dv[j].w);
-        ss += xv[j].x * xv[j].x + xv[j].y * xv[j].y + xv[j].z * xv[j].z + xv[j].w * xv[j].w;
+      const int cc = min(lane + j * 64, n4 - 1);
+      xv[j] = xr[cc];
+      dv[j] = dr[cc];
+      e[j] = gr[cc];
+      rv[j] = dres ? ((const float4*)(dres + (int64_t)row * n))[cc] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      if (lane + j * 64 >= n4) {
+        xv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        dv[j] = xv[j];
       }
+      e[j] = make_float4(e[j].x * dv[j].x, e[j].y * dv[j].y, e[j].z * dv[j].z, e[j].w * dv[j].w);
+      ss += xv[j].x * xv[j].x + xv[j].y * xv[j].y + xv[j].z * xv[j].z + xv[j].w * xv[j].w;
     }
     ss = wave_sum(ss);
     const float rho = 1.0f / sqrtf(ss / (float)n + eps);
@@ -124,11 +136,9 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int rows, int n, float
         o.y = rho * (e[j].y - xv[j].y * dot);
         o.z = rho * (e[j].z - xv[j].z * dot);
         o.w = rho * (e[j].w - xv[j].w * dot);
-        if (dres) {
-          const float4 r = ((const float4*)(dres + (int64_t)row * n))[c];
-          o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
-        }
+        o.x += rv[j].x; o.y += rv[j].y; o.z += rv[j].z; o.w += rv[j].w;
         ((float4*)(dx + (int64_t)row * n))[c] = o;
+        if (dx16) ((half4*)(dx16 + (int64_t)row * n))[c] = to_half4(o);
         dg[j].x += dv[j].x * xv[j].x;
         dg[j].y += dv[j].y * xv[j].y;
         dg[j].z += dv[j].z * xv[j].z;
@@ -151,21 +161,27 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int rows, int n, float
   }
 }
 
-// 64 columns per workgroup, 4 row groups per column (row p goes to group
-// p % 4); the four group sums are added in a fixed order.
-__global__ __launch_bounds__(256) void colsum_kernel(int parts, int n, const float* __restrict__ partial,
-                                                     float* __restrict__ out) {
-  __shared__ float red[4][64];
+// 64 columns per workgroup, 16 row groups per column (row p goes to group
+// p % 16, summed in row order); the group sums are then added in group
+// order, so results are bitwise reproducible.
+__global__ __launch_bounds__(1024) void colsum_kernel(int parts, int n, const float* __restrict__ partial,
+                                                      float* __restrict__ out) {
+  __shared__ float red[16][64];
   const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + cl;
   float s = 0.f;
   if (c < n) {
 #pragma unroll 8
-    for (int p = rg; p < parts; p += 4) s += partial[(int64_t)p * n + c];
+    for (int p = rg; p < parts; p += 16) s += partial[(int64_t)p * n + c];
   }
   red[rg][cl] = s;
   __syncthreads();
-  if (rg == 0 && c < n) out[c] = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
+  if (rg == 0 && c < n) {
+    float t = red[0][cl];
+#pragma unroll
+    for (int g = 1; g < 16; ++g) t += red[g][cl];
+    out[c] = t;
+  }
 }
 
 int vpl_for(int n) {
@@ -215,7 +231,7 @@ int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res
 }
 
 int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* gamma,
-                     const float* dy, const float* dres, float* dx, float* dgamma, float* scratch,
+                     const float* dy, const float* dres, float* dx, f16* dx16, float* dgamma, float* scratch,
                      hipStream_t st) {
   QBLK_TRY(rmsnorm_check(rows, n));
   const int parts = rmsnorm_bwd_parts(rows, n);
@@ -224,7 +240,7 @@ int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* ga
 #define QBLK_CASE(V)                                                                             \
   case V:                                                                                        \
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<V>, grid, block, 0, st, rows, n, eps, x, gamma, dy,     \
-                       dres, dx, scratch);                                                       \
+                       dres, dx, dx16, scratch);                                                 \
     break;
     QBLK_CASE(1) QBLK_CASE(2) QBLK_CASE(4) QBLK_CASE(8) QBLK_CASE(12) QBLK_CASE(16)
 #undef QBLK_CASE
@@ -234,7 +250,7 @@ int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* ga
 }
 
 int colsum(int parts, int n, const float* partial, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)ceil_div(n, 64)), dim3(256), 0, st, parts, n,
+  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)ceil_div(n, 64)), dim3(1024), 0, st, parts, n,
                      partial, out);
   return check_launch("colsum_kernel");
 }
