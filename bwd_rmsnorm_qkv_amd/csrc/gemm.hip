@@ -467,7 +467,6 @@ struct Core<Prec::F16, TM, TN, BK> {
 
 struct Grid {
   int tiles_m, tiles_n, splits, kchunk;
-  int nfast = 0;  // 1: consecutive tiles walk N first (share the A tile)
   int vec = 0;    // 1: output rows (and partials, residual) take 16-byte stores
 };
 
@@ -737,25 +736,31 @@ __device__ __forceinline__ f16* lds_stage() {
 typedef short short4v __attribute__((ext_vector_type(4)));
 
 // One operand of the DMA kernel: R rows of the tile (BM or BN), K-major or
-// MN-major, copied by NW waves.
-template <int R, bool KMAJ, int NW>
+// MN-major, BK = 64 or 32 K per stage, copied by NW waves.
+template <int R, bool KMAJ, int NW, int BK_ = 64>
 struct DmaOperand {
-  static constexpr int BK = 64;
-  static constexpr int J = R / 8 / NW;  // 1 KB wave copies per stage per wave
-  static_assert(J * 8 * NW == R, "DMA split");
+  static constexpr int BK = BK_;
+  static_assert(BK == 64 || BK == 32, "K tile");
+  static constexpr int J = R * BK / 512 / NW;  // 1 KB wave copies per stage per wave
+  static_assert(J * 512 * NW == R * BK, "DMA split");
+  // K-major rows: BK / 8 chunks of 16 bytes; the chunk swizzle puts 16
+  // consecutive rows read at one chunk on 16 different bank groups.
+  static constexpr int KCH = BK / 8;
+  static __device__ __forceinline__ int ksw(int row) { return BK == 64 ? (row >> 1) & 7 : (row >> 2) & 3; }
   const f16* p[J];
 
   // Wave w's copy j fills the 1 KB at tile + 512 (NW j + w) halves.
-  // K-major: 8 rows x 128 B; MN-major: 1024 / (2R) K-rows x 2R bytes.
+  // K-major: 512 / BK rows of 2 BK bytes; MN-major: 1024 / (2R) K-rows x 2R bytes.
   __device__ __forceinline__ void init(const f16* base, int64_t ld, int r0, int rmax, int64_t kb, int lane, int w,
                                        const Seg* seg) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int blk = NW * j + w;
       if constexpr (KMAJ) {
-        const int rsub = lane >> 3;
-        const int lc = (lane & 7) ^ (((blk & 1) << 2) | (rsub >> 1));
-        const int r = min(r0 + 8 * blk + rsub, rmax - 1);
+        const int rsub = lane / KCH;
+        const int row = (512 / BK) * blk + rsub;
+        const int lc = (lane % KCH) ^ ksw(row);
+        const int r = min(r0 + row, rmax - 1);
         if (seg) {
           const int sg = seg_of(*seg, r);
           p[j] = (const f16*)seg->p[sg] + (int64_t)(r - seg->start[sg]) * ld + kb + lc * 8;
@@ -784,7 +789,7 @@ struct DmaOperand {
   // multiple of 32): computed once so each read is one base + immediate.
   static __device__ __forceinline__ int koff(int s, int lane) {
     const int i = lane & 31, kh = lane >> 5;
-    return i * BK + (((2 * s + kh) ^ ((i >> 1) & 7)) << 3);
+    return i * BK + (((2 * s + kh) ^ ksw(i)) << 3);
   }
   // MFMA operand for K step s (16 K) of the 32-row block starting at tile
   // row (K-major) or column (MN-major) rb: lane (i, kh) gets rows rb + i,
@@ -829,8 +834,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int per = total / 8, rem = total % 8;
   const int lt = xcd * per + min(xcd, rem) + slot;
-  const int mt = gd.nfast ? (lt / gd.tiles_n) % gd.tiles_m : lt % gd.tiles_m;
-  const int nt = gd.nfast ? lt % gd.tiles_n : (lt / gd.tiles_m) % gd.tiles_n;
+  const int mt = lt % gd.tiles_m;
+  const int nt = (lt / gd.tiles_m) % gd.tiles_n;
   const int sp = lt / (gd.tiles_m * gd.tiles_n);
   const int m0 = mt * BM, n0 = nt * BN;
   const int kb = sp * gd.kchunk;
@@ -925,6 +930,222 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   if (left > 0) step(I0{}, nfull);
   if constexpr (NS > 2) if (left > 1) step(I1{}, nfull + 1);
   if constexpr (NS > 3) if (left > 2) step(I2{}, nfull + 2);
+
+  // Epilogue through LDS: the wave parks one 32-row block (tm) of its tile
+  // at a time in its own slice of the (now idle) stage buffers and reads it
+  // back so that every lane writes 16 contiguous bytes and each wave
+  // instruction whole rows of the output: a quarter of the store
+  // instructions of element-wise stores. The float4 slots of a row are
+  // XOR-swizzled by row bit 2, so the two half-waves, which park rows r and
+  // r + 4, write different banks.
+  constexpr int WC = TN * 32;  // wave tile width
+  constexpr int CPR = WC / 4;  // float4 slots per row
+  static_assert(CPR >= 16 && (32 * CPR) % 64 == 0, "epilogue row width");
+  static_assert(BM == BN && 2 * 32 * WC * 4 <= BM * BK * 2 && NW <= 8, "epilogue staging space");
+  const int ii = lane & 31, kh = lane >> 5;
+  __syncthreads();  // every wave is done reading the stages
+  float* ep;
+  switch (w >> 1) {  // two wave slices per stage buffer
+    case 0: ep = (float*)stA(I0{}); break;
+    case 1: ep = (float*)stB(I0{}); break;
+    case 2: ep = (float*)stA(I1{}); break;
+    default: ep = (float*)stB(I1{}); break;
+  }
+  ep += (w & 1) * 32 * WC;
+  auto eslot = [](int r, int c) { return r * WC + ((c ^ (((r >> 2) & 1) << 3)) << 2); };
+  const int col0 = n0 + wn * WC;
+  float* part = gd.splits > 1 ? d.ws + (int64_t)sp * d.M * d.N : nullptr;
+  const int bd = d.c_cols_blockdiag;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int c = tn * 32 + ii;
+          ep[eslot(8 * g + 4 * kh + r, c >> 2) + (c & 3)] = acc[tm][tn][4 * g + r];
+        }
+    const int rowb = m0 + wm * TM * 32 + tm * 32;
+#pragma unroll 1
+    for (int q = 0; q < 32 * CPR / 64; ++q) {
+      const int L = q * 64 + lane, rr = L / CPR, c = L % CPR;
+      const float4 v = *(const float4*)(ep + eslot(rr, c));
+      const int row = rowb + rr, col = col0 + 4 * c;
+      if (row >= d.M || col >= d.N) continue;
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+      if (part) {
+        float* pp = part + (int64_t)row * d.N + col;
+        if (gd.vec && col + 4 <= d.N) *(float4*)pp = v;
+        else
+          for (int j = 0; j < 4 && col + j < d.N; ++j) pp[j] = vv[j];
+        continue;
+      }
+      int lo = 0;
+      float* rp = out_row(d, row, lo);
+      if (!rp) continue;
+      if (gd.vec && col + 4 <= d.N && (bd == 0 || (col >= lo && col + 4 <= lo + bd))) {
+        float4 o = make_float4(d.alpha * v.x, d.alpha * v.y, d.alpha * v.z, d.alpha * v.w);
+        if (d.r) {
+          const float4 rv = *(const float4*)(d.r + (int64_t)row * d.ldr + col);
+          o.x += rv.x;
+          o.y += rv.y;
+          o.z += rv.z;
+          o.w += rv.w;
+        }
+        float4* cp = (float4*)(rp + (col - lo));
+        if (d.accumulate) {
+          const float4 cv = *cp;
+          o.x += cv.x;
+          o.y += cv.y;
+          o.z += cv.z;
+          o.w += cv.w;
+        }
+        *cp = o;
+        if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + col) = to_half4(o);
+      } else {
+        for (int j = 0; j < 4 && col + j < d.N; ++j) {
+          if (bd > 0 && (col + j < lo || col + j >= lo + bd)) continue;
+          put_out(d, rp + (col + j - lo), row, col + j, vv[j]);
+          if (d.c16) d.c16[(int64_t)row * d.ldc16 + col + j] = (f16)rp[col + j - lo];
+        }
+      }
+    }
+  }
+}
+
+// Ping-pong variant of the 256 x 256 tile: the two halves of the workgroup
+// (waves 0-3 and 4-7; each SIMD holds one of each) alternate between an
+// MFMA phase (16 MFMAs: two K steps of the wave's 64 x 128 block) and an
+// operand phase (the LDS reads of the next two K steps), with a workgroup
+// barrier between phases and raised priority for the MFMA phase, so every
+// SIMD has one wave issuing MFMAs while the other gathers operands. Per K
+// tile (stage S): the leading half runs MFMA(h0) read(h1) MFMA(h1)
+// read(next tile h0), the trailing half read(h0) MFMA(h0) read(h1)
+// MFMA(h1). Stage S is free from the fourth phase on (its last reads, the
+// trailing half's h1, returned before the third barrier) and is refilled
+// there with tile kt+2, which must have landed (wait + barrier) by the
+// fourth phase of the next tile, when the leading half reads it: copies
+// run a whole K tile ahead of their first read.
+template <bool AK, bool BK_>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Grid gd) {
+  constexpr int BM = 256, BN = 256, WM = 4, WN = 2, NS = 2, BK = 64;
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  using OA = DmaOperand<BM, AK, NW>;
+  using OB = DmaOperand<BN, BK_, NW>;
+  constexpr int JS = OA::J + OB::J;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w % WM, wn = w / WM;
+
+  const int total = gd.tiles_m * gd.tiles_n * gd.splits;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per = total / 8, rem = total % 8;
+  const int lt = xcd * per + min(xcd, rem) + slot;
+  const int mt = lt % gd.tiles_m;
+  const int nt = (lt / gd.tiles_m) % gd.tiles_n;
+  const int sp = lt / (gd.tiles_m * gd.tiles_n);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int kb = sp * gd.kchunk;
+  const int ke = min(d.K, kb + gd.kchunk);
+  const int nkt = ke > kb ? (ke - kb) / BK : 0;
+
+  OA oa;
+  OB ob;
+  oa.init((const f16*)d.a, d.lda, m0, d.M, kb, lane, w, nullptr);
+  ob.init((const f16*)d.b.p[0], d.ldb, n0, d.N, kb, lane, w, BK_ ? &d.b : nullptr);
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  int ko[BK / 16];
+#pragma unroll
+  for (int s = 0; s < BK / 16; ++s) ko[s] = OA::koff(s, lane);
+  half8 av[2][TM], bv[2][TN];  // two K steps of operands
+  auto read = [&](const f16* sa, const f16* sb, auto H) __attribute__((always_inline)) {
+    constexpr int h = decltype(H)::value;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int t = 0; t < TM; ++t) av[ks][t] = OA::frag(sa, wm * TM * 32 + t * 32, 2 * h + ks, lane, ko[2 * h + ks]);
+#pragma unroll
+      for (int t = 0; t < TN; ++t) bv[ks][t] = OB::frag(sb, wn * TN * 32 + t * 32, 2 * h + ks, lane, ko[2 * h + ks]);
+    }
+  };
+  auto mfma = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[ks][tm], bv[ks][tn], acc[tm][tn], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto phase_end = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  auto stA = [](auto S) { return lds_stage<2 * decltype(S)::value, BM * BK>(); };
+  auto stB = [](auto S) { return lds_stage<2 * decltype(S)::value + 1, BN * BK>(); };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto issue = [&](int kt, f16* sa, f16* sb) __attribute__((always_inline)) {
+    oa.issue(kt, sa, d.lda, w);
+    ob.issue(kt, sb, d.ldb, w);
+  };
+
+  // The two halves run the same barriers; each is its own instantiation,
+  // so no branch sits between a wave's MFMAs.
+  auto run = [&](auto Lead) __attribute__((always_inline)) {
+    constexpr bool lead = decltype(Lead)::value;
+    if (0 < nkt) issue(0, stA(I0{}), stB(I0{}));
+    if (1 < nkt) issue(1, stA(I1{}), stB(I1{}));
+    if (1 < nkt) wait_vmcnt<JS>();
+    else wait_vmcnt<0>();
+    phase_end();
+    if constexpr (lead) read(stA(I0{}), stB(I0{}), I0{});
+    phase_end();
+    auto step = [&](auto S, int kt) __attribute__((always_inline)) {
+      using SN = std::integral_constant<int, 1 - decltype(S)::value>;
+      if constexpr (lead) mfma();
+      else read(stA(S), stB(S), I0{});
+      phase_end();
+      if constexpr (lead) read(stA(S), stB(S), I1{});
+      else mfma();
+      phase_end();
+      if constexpr (lead) mfma();
+      else read(stA(S), stB(S), I1{});
+      wait_vmcnt<0>();  // this wave's copies of tile kt+1
+      phase_end();
+      // stage S is free now (its last reads returned before the barrier):
+      // refill it with tile kt+2, a whole K tile ahead of its first read
+      if (kt + 2 < nkt) issue(kt + 2, stA(S), stB(S));
+      if constexpr (lead) {
+        if (kt + 1 < nkt) read(stA(SN{}), stB(SN{}), I0{});
+      } else {
+        mfma();
+      }
+      phase_end();
+    };
+    for (int kt = 0; kt + 1 < nkt; kt += 2) {
+      step(I0{}, kt);
+      step(I1{}, kt + 1);
+    }
+    if (nkt & 1) step(I0{}, nkt - 1);
+  };
+  if (w < NW / 2) run(std::true_type{});
+  else run(std::false_type{});
 
   // Epilogue through LDS: the wave parks one 32-row block (tm) of its tile
   // at a time in its own slice of the (now idle) stage buffers and reads it
@@ -1116,6 +1337,23 @@ Grid plan_tiles(const GemmDesc& d, size_t ws_bytes, int bm, int bn, int bk) {
   return g;
 }
 
+// 256 x 256 ping-pong configuration.
+struct PpCfg {
+  static constexpr int bm = 256, bn = 256, threads = 512;
+  template <bool AK, bool BKM>
+  static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
+    const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
+    hipLaunchKernelGGL((gemm_pp_kernel<AK, BKM>), dim3(nwg), dim3(threads), 0, st, d, g);
+  }
+  static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
+    switch (d.layout) {
+      case Layout::NT: launch<true, true>(d, g, st); break;
+      case Layout::NN: launch<true, false>(d, g, st); break;
+      case Layout::TN: launch<false, false>(d, g, st); break;
+    }
+  }
+};
+
 template <int BM, int BN, int WM, int WN, int NS>
 struct DmaCfg {
   static constexpr int bm = BM, bn = BN, threads = WM * WN * 64;
@@ -1139,7 +1377,11 @@ using Nt16Big = Nt16Small;
 // 128 x 128 tiles, 4 waves, two workgroups per CU (64 KB LDS each); and
 // 256 x 256 tiles, 8 waves of 64 x 128, one workgroup per CU (128 KB LDS).
 using Nt16Small = DmaCfg<128, 128, 2, 2, 2>;
+#ifdef QBLK_NO_PINGPONG
 using Nt16Big = DmaCfg<256, 256, 4, 2, 2>;
+#else
+using Nt16Big = PpCfg;
+#endif
 #endif
 
 // Big tiles pay off once they alone give at least half the CUs a tile.
