@@ -1050,7 +1050,7 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
 // partial dQ in wave order and writes it. Only the diagonal tile is masked.
 template <typename T, int D>
 __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(const AttnDmaArgs a,
-                                                                             const float* delta) {
+                                                                             float* delta) {
   using RT = RowTile<T, D>;
   using TT = TrTile<float, (sizeof(T) == 4 ? D : 64)>;
   using E = AttnElem<T>;
@@ -1084,7 +1084,37 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
   load_row_frags<T, D>(d_o + (tok0 + qc_i) * a.lddo + (int64_t)h * D, kh, dc);
   const int64_t rowi = ((int64_t)b * a.heads + h) * S + qc_i;
   const float lse2 = a.lse[rowi] * kLog2e;
-  const float dl = delta[rowi];
+  // delta = rowsum(dO o) of the tile's rows (fp32 operands): wave w sums
+  // columns w D/W .. (w+1) D/W - 1, the lane halves (kh) half of them each;
+  // the waves' parts are added in wave order through the first K stage
+  // before any copy lands there, and wave 0 stores delta for the dK/dV
+  // kernel.
+  float dl;
+  {
+    constexpr int CW = D / W / 2;  // columns per lane
+    const int64_t c0 = (int64_t)h * D + w * (D / W) + kh * CW;
+    const float* orow = a.o + (tok0 + qc_i) * a.ldo + c0;
+    const float* drow = a.do32 + (tok0 + qc_i) * a.lddo32 + c0;
+    float4 o4[CW / 4], d4[CW / 4];
+#pragma unroll
+    for (int j = 0; j < CW / 4; ++j) {
+      o4[j] = *(const float4*)(orow + 4 * j);
+      d4[j] = *(const float4*)(drow + 4 * j);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < CW / 4; ++j)
+      part += o4[j].x * d4[j].x + o4[j].y * d4[j].y + o4[j].z * d4[j].z + o4[j].w * d4[j].w;
+    part += __shfl_xor(part, 32, kWave);
+    float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
+    x[w * 64 + lane] = part;
+    __syncthreads();
+    dl = x[lane];
+#pragma unroll
+    for (int ww = 1; ww < W; ++ww) dl += x[ww * 64 + lane];
+    __syncthreads();  // the stage is refilled from here on
+    if (w == 0 && kh == 0 && qi < S) delta[rowi] = dl;
+  }
   floatx16 dq[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -1326,15 +1356,8 @@ int fwd_dma_launch(const AttnDmaArgs& a, hipStream_t st) {
 template <typename T, int D>
 int bwd_dma_launch(const AttnDmaArgs& a, float* delta, float* dk_part, float* dv_part, hipStream_t st) {
   const int64_t T_ = (int64_t)a.batch * a.seq;
-  AttnArgs da{};
-  da.batch = a.batch; da.seq = a.seq; da.heads = a.heads; da.kv_heads = a.kv_heads; da.head_dim = D;
-  da.o = a.o; da.ldo = a.ldo;
-  da.d_o = a.do32; da.lddo = a.lddo32;
-  hipLaunchKernelGGL(attn_delta_kernel, dim3((unsigned)ceil_div(T_ * a.heads, 4)), dim3(256), 0, st, da, delta);
-  QBLK_TRY(check_launch("attn_delta_kernel"));
   dim3 grid((unsigned)ceil_div(a.seq, 32), (unsigned)a.heads, (unsigned)a.batch);
-  hipLaunchKernelGGL((attn_dma_dq_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DQ_W), 0, st, a,
-                     (const float*)delta);
+  hipLaunchKernelGGL((attn_dma_dq_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DQ_W), 0, st, a, delta);
   QBLK_TRY(check_launch("attn_dma_dq_kernel"));
   hipLaunchKernelGGL((attn_dma_dkv_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DKV_W), 0, st, a,
                      (const float*)delta, dk_part, dv_part);

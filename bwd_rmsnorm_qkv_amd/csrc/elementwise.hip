@@ -254,8 +254,7 @@ int qk_norm_rope_backward(const QkRopeBwdArgs& a, float* scratch, hipStream_t st
   hipLaunchKernelGGL(qk_rope_bwd_kernel, dim3((unsigned)(pq + pk)), dim3(256), 0, st, a, pq, part_q, part_k);
   QBLK_TRY(check_launch("qk_rope_bwd_kernel"));
   if (a.qk_norm) {
-    QBLK_TRY(colsum(pq, d, part_q, a.dg_q, st));
-    QBLK_TRY(colsum(pk, d, part_k, a.dg_k, st));
+    QBLK_TRY(colsum2(pq, d, part_q, a.dg_q, pk, d, part_k, a.dg_k, st));
   } else {
     if (a.dg_q) hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, a.dg_q, d, 0.f);
     if (a.dg_k) hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, a.dg_k, d, 0.f);

@@ -20,6 +20,9 @@ int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* ga
                      hipStream_t st);
 // out[c] = sum_p partial[p][c], fixed order.
 int colsum(int parts, int n, const float* partial, float* out, hipStream_t st);
+// Two such sums in one launch.
+int colsum2(int parts0, int n0, const float* p0, float* o0, int parts1, int n1, const float* p1, float* o1,
+            hipStream_t st);
 
 // RoPE table: tab[s][i] = (cos, sin)(s * theta^(-2i/d)), computed in fp64.
 int rope_table(int seq, int head_dim, float theta, float2* tab, hipStream_t st);

@@ -164,8 +164,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int rows, int n, float
 // 64 columns per workgroup, 16 row groups per column (row p goes to group
 // p % 16, summed in row order); the group sums are then added in group
 // order, so results are bitwise reproducible.
-__global__ __launch_bounds__(1024) void colsum_kernel(int parts, int n, const float* __restrict__ partial,
-                                                      float* __restrict__ out) {
+__device__ __forceinline__ void colsum_cols(int parts, int n, const float* __restrict__ partial,
+                                            float* __restrict__ out) {
   __shared__ float red[16][64];
   const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + cl;
@@ -182,6 +182,19 @@ __global__ __launch_bounds__(1024) void colsum_kernel(int parts, int n, const fl
     for (int g = 1; g < 16; ++g) t += red[g][cl];
     out[c] = t;
   }
+}
+
+__global__ __launch_bounds__(1024) void colsum_kernel(int parts, int n, const float* __restrict__ partial,
+                                                      float* __restrict__ out) {
+  colsum_cols(parts, n, partial, out);
+}
+
+// Two independent column sums in one launch (blockIdx.y picks the job).
+__global__ __launch_bounds__(1024) void colsum2_kernel(int parts0, int n0, const float* __restrict__ p0,
+                                                       float* __restrict__ o0, int parts1, int n1,
+                                                       const float* __restrict__ p1, float* __restrict__ o1) {
+  if (blockIdx.y == 0) colsum_cols(parts0, n0, p0, o0);
+  else colsum_cols(parts1, n1, p1, o1);
 }
 
 int vpl_for(int n) {
@@ -247,6 +260,14 @@ int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* ga
   }
   QBLK_TRY(check_launch("rmsnorm_bwd_kernel"));
   return colsum(parts, n, scratch, dgamma, st);
+}
+
+int colsum2(int parts0, int n0, const float* p0, float* o0, int parts1, int n1, const float* p1, float* o1,
+            hipStream_t st) {
+  const int n = n0 > n1 ? n0 : n1;
+  hipLaunchKernelGGL(colsum2_kernel, dim3((unsigned)ceil_div(n, 64), 2), dim3(1024), 0, st, parts0, n0, p0, o0,
+                     parts1, n1, p1, o1);
+  return check_launch("colsum2_kernel");
 }
 
 int colsum(int parts, int n, const float* partial, float* out, hipStream_t st) {
