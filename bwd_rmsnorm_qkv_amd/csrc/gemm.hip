@@ -468,6 +468,7 @@ struct Core<Prec::F16, TM, TN, BK> {
 struct Grid {
   int tiles_m, tiles_n, splits, kchunk;
   int vec = 0;    // 1: output rows (and partials, residual) take 16-byte stores
+  int bn = 0;     // tile width (ping-pong kernel: 256 or 192)
 };
 
 // Final value of C[row, col]: the row pointer `cp` already routed through
@@ -1028,9 +1029,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
 // there with tile kt+2, which must have landed (wait + barrier) by the
 // fourth phase of the next tile, when the leading half reads it: copies
 // run a whole K tile ahead of their first read.
-template <bool AK, bool BK_>
+template <int BN, bool AK, bool BK_>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Grid gd) {
-  constexpr int BM = 256, BN = 256, WM = 4, WN = 2, NS = 2, BK = 64;
+  constexpr int BM = 256, WM = 4, WN = 2, NS = 2, BK = 64;
+  static_assert(BN == 256 || (BN == 192 && BK_), "192-wide tiles need a K-major B");
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   using OA = DmaOperand<BM, AK, NW>;
@@ -1147,17 +1149,22 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
   if (w < NW / 2) run(std::true_type{});
   else run(std::false_type{});
 
-  // Epilogue through LDS: the wave parks one 32-row block (tm) of its tile
-  // at a time in its own slice of the (now idle) stage buffers and reads it
-  // back so that every lane writes 16 contiguous bytes and each wave
-  // instruction whole rows of the output: a quarter of the store
-  // instructions of element-wise stores. The float4 slots of a row are
-  // XOR-swizzled by row bit 2, so the two half-waves, which park rows r and
-  // r + 4, write different banks.
+  // Epilogue through LDS: the wave parks RP rows (a 32-row block tm, or
+  // half of it when two such slices would not fit a stage buffer) of its
+  // tile at a time in its own slice of the (now idle) stage buffers
+  // and reads them back so that every lane writes 16 contiguous bytes and
+  // each wave instruction whole rows of the output: a quarter of the store
+  // instructions of element-wise stores. The two half-waves park rows r and
+  // r + 4 at once: with power-of-two rows the float4 slots are XOR-swizzled
+  // by row bit 2, otherwise rows are padded by 8 floats, so the two land on
+  // different banks.
   constexpr int WC = TN * 32;  // wave tile width
   constexpr int CPR = WC / 4;  // float4 slots per row
-  static_assert(CPR >= 16 && (32 * CPR) % 64 == 0, "epilogue row width");
-  static_assert(BM == BN && 2 * 32 * WC * 4 <= BM * BK * 2 && NW <= 8, "epilogue staging space");
+  constexpr bool POW2 = (CPR & (CPR - 1)) == 0;
+  constexpr int PITCH = POW2 ? WC : WC + 8;
+  constexpr int RP = 2 * 32 * PITCH * 4 <= BN * BK * 2 ? 32 : 16;  // rows per pass
+  static_assert(CPR >= 16 && (RP * CPR) % 64 == 0, "epilogue row width");
+  static_assert(2 * RP * PITCH * 4 <= BN * BK * 2 && NW <= 8, "epilogue staging space");
   const int ii = lane & 31, kh = lane >> 5;
   __syncthreads();  // every wave is done reading the stages
   float* ep;
@@ -1167,68 +1174,70 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
     case 2: ep = (float*)stA(I1{}); break;
     default: ep = (float*)stB(I1{}); break;
   }
-  ep += (w & 1) * 32 * WC;
-  auto eslot = [](int r, int c) { return r * WC + ((c ^ (((r >> 2) & 1) << 3)) << 2); };
+  ep += (w & 1) * RP * PITCH;
+  auto eslot = [](int r, int c) { return r * PITCH + ((POW2 ? (c ^ (((r >> 2) & 1) << 3)) : c) << 2); };
   const int col0 = n0 + wn * WC;
   float* part = gd.splits > 1 ? d.ws + (int64_t)sp * d.M * d.N : nullptr;
   const int bd = d.c_cols_blockdiag;
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
+  for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int hh = 0; hh < 32 / RP; ++hh) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int g2 = 0; g2 < RP / 8; ++g2)
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const int c = tn * 32 + ii;
-          ep[eslot(8 * g + 4 * kh + r, c >> 2) + (c & 3)] = acc[tm][tn][4 * g + r];
-        }
-    const int rowb = m0 + wm * TM * 32 + tm * 32;
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            const int c = tn * 32 + ii;
+            ep[eslot(8 * g2 + 4 * kh + r, c >> 2) + (c & 3)] = acc[tm][tn][4 * (hh * (RP / 8) + g2) + r];
+          }
+      const int rowb = m0 + wm * TM * 32 + tm * 32 + RP * hh;
 #pragma unroll 1
-    for (int q = 0; q < 32 * CPR / 64; ++q) {
-      const int L = q * 64 + lane, rr = L / CPR, c = L % CPR;
-      const float4 v = *(const float4*)(ep + eslot(rr, c));
-      const int row = rowb + rr, col = col0 + 4 * c;
-      if (row >= d.M || col >= d.N) continue;
-      const float vv[4] = {v.x, v.y, v.z, v.w};
-      if (part) {
-        float* pp = part + (int64_t)row * d.N + col;
-        if (gd.vec && col + 4 <= d.N) *(float4*)pp = v;
-        else
-          for (int j = 0; j < 4 && col + j < d.N; ++j) pp[j] = vv[j];
-        continue;
-      }
-      int lo = 0;
-      float* rp = out_row(d, row, lo);
-      if (!rp) continue;
-      if (gd.vec && col + 4 <= d.N && (bd == 0 || (col >= lo && col + 4 <= lo + bd))) {
-        float4 o = make_float4(d.alpha * v.x, d.alpha * v.y, d.alpha * v.z, d.alpha * v.w);
-        if (d.r) {
-          const float4 rv = *(const float4*)(d.r + (int64_t)row * d.ldr + col);
-          o.x += rv.x;
-          o.y += rv.y;
-          o.z += rv.z;
-          o.w += rv.w;
+      for (int q = 0; q < RP * CPR / 64; ++q) {
+        const int L = q * 64 + lane, rr = L / CPR, c = L % CPR;
+        const float4 v = *(const float4*)(ep + eslot(rr, c));
+        const int row = rowb + rr, col = col0 + 4 * c;
+        if (row >= d.M || col >= d.N) continue;
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+        if (part) {
+          float* pp = part + (int64_t)row * d.N + col;
+          if (gd.vec && col + 4 <= d.N) *(float4*)pp = v;
+          else
+            for (int j = 0; j < 4 && col + j < d.N; ++j) pp[j] = vv[j];
+          continue;
         }
-        float4* cp = (float4*)(rp + (col - lo));
-        if (d.accumulate) {
-          const float4 cv = *cp;
-          o.x += cv.x;
-          o.y += cv.y;
-          o.z += cv.z;
-          o.w += cv.w;
-        }
-        *cp = o;
-        if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + col) = to_half4(o);
-      } else {
-        for (int j = 0; j < 4 && col + j < d.N; ++j) {
-          if (bd > 0 && (col + j < lo || col + j >= lo + bd)) continue;
-          put_out(d, rp + (col + j - lo), row, col + j, vv[j]);
-          if (d.c16) d.c16[(int64_t)row * d.ldc16 + col + j] = (f16)rp[col + j - lo];
+        int lo = 0;
+        float* rp = out_row(d, row, lo);
+        if (!rp) continue;
+        if (gd.vec && col + 4 <= d.N && (bd == 0 || (col >= lo && col + 4 <= lo + bd))) {
+          float4 o = make_float4(d.alpha * v.x, d.alpha * v.y, d.alpha * v.z, d.alpha * v.w);
+          if (d.r) {
+            const float4 rv = *(const float4*)(d.r + (int64_t)row * d.ldr + col);
+            o.x += rv.x;
+            o.y += rv.y;
+            o.z += rv.z;
+            o.w += rv.w;
+          }
+          float4* cp = (float4*)(rp + (col - lo));
+          if (d.accumulate) {
+            const float4 cv = *cp;
+            o.x += cv.x;
+            o.y += cv.y;
+            o.z += cv.z;
+            o.w += cv.w;
+          }
+          *cp = o;
+          if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + col) = to_half4(o);
+        } else {
+          for (int j = 0; j < 4 && col + j < d.N; ++j) {
+            if (bd > 0 && (col + j < lo || col + j >= lo + bd)) continue;
+            put_out(d, rp + (col + j - lo), row, col + j, vv[j]);
+            if (d.c16) d.c16[(int64_t)row * d.ldc16 + col + j] = (f16)rp[col + j - lo];
+          }
         }
       }
     }
-  }
 }
 
 // out = alpha * sum over splits (fixed order) [+ R] [+ C], routed like the
@@ -1337,19 +1346,23 @@ Grid plan_tiles(const GemmDesc& d, size_t ws_bytes, int bm, int bn, int bk) {
   return g;
 }
 
-// 256 x 256 ping-pong configuration.
+// Ping-pong configurations: 256 x 256 for every layout, 256 x 192 for NT.
 struct PpCfg {
   static constexpr int bm = 256, bn = 256, threads = 512;
-  template <bool AK, bool BKM>
+  static constexpr bool narrow = true;  // also runs 256 x 192 tiles (NT)
+  template <int BN, bool AK, bool BKM>
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
-    hipLaunchKernelGGL((gemm_pp_kernel<AK, BKM>), dim3(nwg), dim3(threads), 0, st, d, g);
+    hipLaunchKernelGGL((gemm_pp_kernel<BN, AK, BKM>), dim3(nwg), dim3(threads), 0, st, d, g);
   }
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     switch (d.layout) {
-      case Layout::NT: launch<true, true>(d, g, st); break;
-      case Layout::NN: launch<true, false>(d, g, st); break;
-      case Layout::TN: launch<false, false>(d, g, st); break;
+      case Layout::NT:
+        if (g.bn == 192) launch<192, true, true>(d, g, st);
+        else launch<256, true, true>(d, g, st);
+        break;
+      case Layout::NN: launch<256, true, false>(d, g, st); break;
+      case Layout::TN: launch<256, false, false>(d, g, st); break;
     }
   }
 };
@@ -1357,6 +1370,7 @@ struct PpCfg {
 template <int BM, int BN, int WM, int WN, int NS>
 struct DmaCfg {
   static constexpr int bm = BM, bn = BN, threads = WM * WN * 64;
+  static constexpr bool narrow = false;
   template <bool AK, bool BKM>
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
@@ -1423,10 +1437,23 @@ bool out_vec4(const GemmDesc& d, const Grid& g) {
   return true;
 }
 
+// Big-tile width: 192 instead of 256 (K-major B only) when it takes fewer
+// CU-rounds x tile width, i.e. when 256-wide tiles leave many CUs idle.
+int big_bn(const GemmDesc& d) {
+  if (!Nt16Big::narrow || d.layout != Layout::NT) return Nt16Big::bn;
+  const int64_t tm = ceil_div(d.M, 256);
+  const int64_t r256 = ceil_div(tm * ceil_div(d.N, 256), kTargetWgs);
+  const int64_t r192 = ceil_div(tm * ceil_div(d.N, 192), kTargetWgs);
+  return r192 * 192 < r256 * 256 ? 192 : 256;
+}
+
 Grid plan(const GemmDesc& d, size_t ws_bytes) {
   if (nt16_ok(d)) {
-    Grid g = nt16_big(d) ? plan_tiles(d, ws_bytes, Nt16Big::bm, Nt16Big::bn, 64)
-                         : plan_tiles(d, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64);
+    const bool big = nt16_big(d);
+    const int bn = big ? big_bn(d) : Nt16Small::bn;
+    Grid g = big ? plan_tiles(d, ws_bytes, Nt16Big::bm, bn, 64)
+                 : plan_tiles(d, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64);
+    g.bn = bn;
     g.vec = out_vec4(d, g);
     return g;
   }
