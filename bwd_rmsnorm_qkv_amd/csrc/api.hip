@@ -263,11 +263,17 @@ int32_t qblk_gemm_workspace_size(int32_t layout, int32_t precision, int32_t M, i
                                  size_t* scratch_bytes) {
   if (layout < 0 || layout > 2 || precision < 0 || precision > 1) return fail(QBLK_EINVAL, "gemm: layout/precision");
   if (M <= 0 || N <= 0 || K <= 0) return fail(QBLK_EINVAL, "gemm: bad shape");
-  GemmDesc d;
-  d.layout = (Layout)layout;
-  d.prec = (Prec)precision;
-  d.M = M; d.N = N; d.K = K;
-  if (scratch_bytes) *scratch_bytes = gemm_workspace(d);
+  // enough for either operand storage (fp16 storage plans its own splits)
+  size_t need = 0;
+  for (int f16src = 0; f16src < 2; ++f16src) {
+    GemmDesc d;
+    d.layout = (Layout)layout;
+    d.prec = (Prec)precision;
+    d.M = M; d.N = N; d.K = K;
+    if (f16src) d.a_src = d.b_src = Src::F16;
+    need = std::max(need, gemm_workspace(d));
+  }
+  if (scratch_bytes) *scratch_bytes = need;
   return QBLK_OK;
 }
 

@@ -103,14 +103,17 @@ static size_t block_gemm_ws(const qblk_config& c, int r) {
     }
     for (int k = 0; k < 7; ++k) v.push_back({Layout::NN, T, r, outk[k]});
   }
+  // the fp16-storage kernels plan their splits differently: size for both
   size_t m = 0;
-  for (const S& x : v) {
-    GemmDesc d;
-    d.layout = x.l;
-    d.prec = prec_of(c);
-    d.M = x.M; d.N = x.N; d.K = x.K;
-    m = std::max(m, gemm_workspace(d));
-  }
+  for (const S& x : v)
+    for (int f16src = 0; f16src < 2; ++f16src) {
+      GemmDesc d;
+      d.layout = x.l;
+      d.prec = prec_of(c);
+      d.M = x.M; d.N = x.N; d.K = x.K;
+      if (f16src) d.a_src = d.b_src = Src::F16;
+      m = std::max(m, gemm_workspace(d));
+    }
   return m;
 }
 

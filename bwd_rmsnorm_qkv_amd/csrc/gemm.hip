@@ -1328,13 +1328,16 @@ Cfg cfg_for(const GemmDesc& d) {
 #endif
 }
 
-Grid plan_tiles(const GemmDesc& d, size_t ws_bytes, int bm, int bn, int bk) {
+// target_wgs > 0: split K so that tiles x splits reaches it (rounding up);
+// target_wgs < 0: so that it stays within -target_wgs (rounding down, one
+// wave of workgroups).
+Grid plan_tiles(const GemmDesc& d, size_t ws_bytes, int bm, int bn, int bk, int target_wgs = kTargetWgs) {
   Grid g;
   g.tiles_m = (int)ceil_div(d.M, bm);
   g.tiles_n = (int)ceil_div(d.N, bn);
   const int tiles = g.tiles_m * g.tiles_n;
   const int nkt = (int)ceil_div(d.K, bk);
-  int splits = (int)ceil_div(kTargetWgs, tiles);
+  int splits = target_wgs > 0 ? (int)ceil_div(target_wgs, tiles) : -target_wgs / tiles;
   splits = std::min(splits, std::max(1, nkt / kMinKtPerSplit));
   splits = std::min(splits, kMaxSplits);
   if (splits > 1 && (size_t)splits * d.M * d.N * sizeof(float) > ws_bytes) splits = 1;
@@ -1451,8 +1454,10 @@ Grid plan(const GemmDesc& d, size_t ws_bytes) {
   if (nt16_ok(d)) {
     const bool big = nt16_big(d);
     const int bn = big ? big_bn(d) : Nt16Small::bn;
+    // the small tiles run two workgroups per CU: split K for one wave of
+    // 2 x kTargetWgs workgroups
     Grid g = big ? plan_tiles(d, ws_bytes, Nt16Big::bm, bn, 64)
-                 : plan_tiles(d, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64);
+                 : plan_tiles(d, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64, -2 * kTargetWgs);
     g.bn = bn;
     g.vec = out_vec4(d, g);
     return g;

@@ -28,6 +28,8 @@ int32_t qblk_gemm(int32_t layout, int32_t precision, int32_t M, int32_t N, int32
                   const float* A, int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
                   int32_t accumulate, void* scratch, size_t scratch_bytes, qblk_stream_t stream);
 
+/* Split-K scratch bytes for this shape, enough whichever storage type
+ * (fp32 or fp16) the operands are given in. */
 int32_t qblk_gemm_workspace_size(int32_t layout, int32_t precision, int32_t M, int32_t N, int32_t K,
                                  size_t* scratch_bytes);
 
