@@ -11,6 +11,9 @@ Also reported in the same JSON line:
                 launch by launch with HIP events on the launch stream:
                 algorithmic FLOPs / summed launch durations vs the dense
                 fp16 MFMA peak;
+  hbm           the memory-bound steps exported as calls (AdamW, the clip's
+                squared sum, RMSNorm, NF4 dequantize), each timed alone:
+                algorithmic bytes / time vs the HBM peak;
   cpu_baseline  the CPU oracle (numpy float64) on a bounded sample of the
                 same workload, on this host's cores;
   extra         the 36-layer stack training step (fused CE, global clip,
@@ -33,6 +36,7 @@ sys.path.insert(0, ROOT)
 MFMA_F16_PEAK = 2516.6   # TFLOP/s, dense
 MFMA_F32_PEAK = 157.3    # TFLOP/s
 HBM_PEAK = 8000.0        # GB/s
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "block_gemm_hbm_traffic_qwen3_4b_s512.md")
 
 
 def log(msg):
@@ -80,6 +84,26 @@ def block_gemms(c):
     ]
 
 
+def gemm_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary (see
+    bench_traffic.py), or None when it is missing or was taken on GEMM
+    sources other than the current ones."""
+    import bench_traffic
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            txt = f.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in txt.splitlines():
+        if ": " in line and line.split(": ", 1)[0] in ("traffic_bytes_per_launch", "gemm_source_sha1"):
+            k, v = line.split(": ", 1)
+            vals[k] = v.strip()
+    if vals.get("gemm_source_sha1") != bench_traffic.source_digest() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
 def gemm_roofline(c, torch, qblk, reps):
     """Replay the step's GEMMs (same kernels, shapes, layouts and operand
     types as the block), each bracketed by HIP events on the current stream,
@@ -120,12 +144,71 @@ def gemm_roofline(c, torch, qblk, reps):
     achieved = flops / (step_ms * 1e-3) / 1e12
     return {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK, "unit": "TFLOP/s",
-        "frac": round(achieved / MFMA_F16_PEAK, 4), "traffic": None,
+        "frac": round(achieved / MFMA_F16_PEAK, 4), "traffic": gemm_traffic(),
         "kernel": "gemm_dma_kernel (the 12 GEMM launches of one block fwd+bwd, split-K reduce included)",
         "flops_per_step": flops, "gemm_ms_per_step": round(step_ms, 4),
         "avg_launch_us": round(1e3 * step_ms / len(bufs), 2),
         "per_launch_us": [round(1e3 * x / reps, 1) for x in per],
     }
+
+
+def stack_param_count(synth):
+    c, L, V = synth.STACK36_SMALL, synth.STACK_LAYERS, synth.STACK_VOCAB
+    h, qd, kvd, I, d = c.hidden, c.heads * c.head_dim, c.kv_heads * c.head_dim, c.intermediate, c.head_dim
+    per_layer = h * qd + 2 * h * kvd + qd * h + 3 * h * I + 2 * h + 2 * d
+    return L * per_layer + V * h + h
+
+
+def hbm_kernels(torch, qblk, synth, reps=10):
+    """The memory-bound steps the library exports as calls, each timed
+    alone with HIP events on the current stream (reps calls after two
+    warm-ups): algorithmic bytes / time against the HBM peak. AdamW and the
+    squared sum run over the 36-layer stack's parameter count (working sets
+    of GBs, far beyond the 256 MB last-level cache); the norms run at the
+    Qwen3-4B block shape, whose working set (tens of MB) the last-level cache
+    can hold, so their rate can exceed what HBM alone delivers."""
+    out = []
+
+    def add(name, workload, nbytes, fn):
+        ms = timed(fn, reps, 2, torch)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out.append({"kernel": name, "workload": workload, "bytes": int(nbytes), "us": round(ms * 1e3, 2),
+                    "GB/s": round(gbps, 1), "frac": round(gbps / HBM_PEAK, 4)})
+
+    n = stack_param_count(synth)
+    w = torch.randn(n, device="cuda") * 0.02
+    g = torch.randn(n, device="cuda") * 1e-3
+    m = torch.zeros(n, device="cuda")
+    v = torch.zeros(n, device="cuda")
+    add("adamw_step", f"{n} fp32 parameters (36-layer stack): w, g, m, v read; w, m, v written", 28 * n,
+        lambda: qblk.adamw_step([w], [g], [m], [v], 1e-3, 0.9, 0.999, 1e-8, 0.01, 1))
+    norm = torch.zeros(1, device="cuda")
+    scale = torch.zeros(1, device="cuda")
+    cs = torch.empty(max(qblk.clip_workspace_size([g]), 16), dtype=torch.uint8, device="cuda")
+    add("clip_grad_norm (squared sum)", f"{n} fp32 gradients read once", 4 * n,
+        lambda: qblk.clip_grad_norm([g], 1.0, 0, norm, scale, cs))
+    del w, m, v, cs
+    c = synth.QWEN3_4B_BLOCK
+    T, h = c.tokens, c.hidden
+    x = torch.randn(T, h, device="cuda")
+    dy = torch.randn(T, h, device="cuda")
+    gam = torch.ones(h, device="cuda")
+    y = torch.empty_like(x)
+    rho = torch.empty(T, device="cuda")
+    add("rmsnorm_forward", f"[{T}, {h}] fp32: x read, y written", 2 * 4 * T * h,
+        lambda: qblk.rmsnorm_forward(T, h, 1e-6, x, None, gam, y, None, rho))
+    dx = torch.empty_like(x)
+    dgam = torch.empty(h, device="cuda")
+    rs = torch.empty(max(qblk.rmsnorm_workspace_size(T, h), 16), dtype=torch.uint8, device="cuda")
+    add("rmsnorm_backward", f"[{T}, {h}] fp32: x, dy read, dx written", 3 * 4 * T * h,
+        lambda: qblk.rmsnorm_backward(T, h, 1e-6, x, gam, dy, None, dx, dgam, rs))
+    numel = 2 * c.intermediate * h
+    codes = torch.randint(0, 256, (numel // 2,), dtype=torch.uint8, device="cuda")
+    absmax = torch.rand(numel // 64, device="cuda")
+    wout = torch.empty(numel, device="cuda")
+    add("nf4_dequantize", f"gate+up weights [{2 * c.intermediate}, {h}]: codes and absmax read, fp32 written",
+        numel // 2 + 4 * (numel // 64) + 4 * numel, lambda: qblk.nf4_dequantize(codes, absmax, numel, wout))
+    return out
 
 
 def cpu_baseline(c, inp, budget_s=12.0):
@@ -216,6 +299,8 @@ def main():
         "roofline": roof,
         "fp16_weight_pack_ms": round(pack_ms, 4),
     }
+    log("memory-bound kernels")
+    out["hbm"] = hbm_kernels(torch, qblk, synth)
     if not args.no_extra:
         extra = {}
         for name, fn in (("stack36_train_step", extra_stack), ("nf4_lora_block", extra_nf4)):

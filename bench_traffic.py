@@ -1,0 +1,167 @@
+"""HBM traffic and MFMA busy time of the block's GEMM launches, from
+rocprofv3 hardware counters, for bench.py's roofline entry.
+
+  python bench_traffic.py run
+      One 256 MiB fp32 device-to-device copy (the calibration kernel, the
+      runtime's plain copy: 256 MiB read, 256 MiB written), then the 12 GEMM
+      launches of one Qwen3-4B-shaped block
+      forward + backward (same kernels, shapes and operand types as
+      bench.py's replay), each once. Meant to run under
+      `rocprofv3 --pmc <counter>`, one counter set per run.
+
+  python bench_traffic.py summarize FETCH_DIR WRITE_DIR MFMA_DIR OUT.md
+      Reads the three counter runs (FETCH_SIZE; WRITE_SIZE; GRBM_GUI_ACTIVE
+      with SQ_VALU_MFMA_BUSY_CYCLES) and writes the summary: per launch the
+      counter bytes scaled by the calibration factor (known bytes of the copy
+      / what the same counter reads for it), and the MFMA busy fraction.
+      The summary records a digest of the GEMM sources; bench.py uses its
+      traffic figure only while the sources still match.
+"""
+import csv
+import glob
+import hashlib
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+COPY_BYTES = 256 << 20
+GEMM_SOURCES = ["bwd_rmsnorm_qkv_amd/csrc/gemm.hip", "bwd_rmsnorm_qkv_amd/csrc/gemm.h",
+                "bwd_rmsnorm_qkv_amd/csrc/common.h"]
+
+
+def source_digest():
+    h = hashlib.sha1()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def run():
+    import torch
+    import bench
+    from bwd_rmsnorm_qkv_amd import qblk, synth
+    torch.cuda.set_device(0)
+    qblk.lib()
+    src = torch.ones(COPY_BYTES // 4, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c = synth.QWEN3_4B_BLOCK
+    specs = bench.block_gemms(c)
+    bufs = []
+    for (lay, M, N, K, acc) in specs:
+        a_shape = (M, K) if lay in (0, 1) else (K, M)
+        b_shape = (N, K) if lay == 0 else (K, N)
+        A = (torch.randn(a_shape, device="cuda") * 0.02).half()
+        B = torch.randn(b_shape, device="cuda").half()
+        C = torch.zeros((M, N), device="cuda")
+        bufs.append((lay, M, N, K, acc, A, a_shape[1], B, b_shape[1], C))
+    ws = max(qblk.gemm_workspace_size(lay, 1, M, N, K) for (lay, M, N, K, _) in specs)
+    scratch = torch.empty(max(ws, 16), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for (lay, M, N, K, acc, A, lda, B, ldb, C) in bufs:
+        qblk.gemm(lay, 1, M, N, K, A, lda, B, ldb, C, N, acc, scratch=scratch)
+        torch.cuda.synchronize()
+    print("done", flush=True)
+
+
+def _rows(d):
+    f = glob.glob(os.path.join(d, "*counter_collection.csv"))
+    if not f:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = list(csv.DictReader(open(f[0])))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
+
+
+def _per_dispatch(rows, counter):
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] == counter:
+            out[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]))
+    return [out[k] for k in sorted(out)]
+
+
+def _split(disp):
+    """(copy, launches): the calibration copy and the 12 GEMM launches, each a
+    list of dispatches (the product, then its split-K reduce if any)."""
+    copy = [v for (n, v) in disp if "copyBuffer" in n]  # the runtime's plain copy kernel
+    gemm = [(n, v) for (n, v) in disp if "gemm" in n or "splitk_reduce" in n]
+    launches = []
+    for n, v in gemm:
+        if "splitk_reduce" in n and launches:
+            launches[-1].append((n, v))
+        else:
+            launches.append([(n, v)])
+    if len(copy) != 1 or len(launches) != 12:
+        raise SystemExit(f"expected 1 copy and 12 GEMM launches, got {len(copy)} and {len(launches)}")
+    return copy[0], launches
+
+
+def summarize(fetch_dir, write_dir, mfma_dir, out_path):
+    import bench
+    from bwd_rmsnorm_qkv_amd import synth
+    fcopy, fl = _split(_per_dispatch(_rows(fetch_dir), "FETCH_SIZE"))
+    wcopy, wl = _split(_per_dispatch(_rows(write_dir), "WRITE_SIZE"))
+    mrows = _rows(mfma_dir)
+    _, busy = _split(_per_dispatch(mrows, "SQ_VALU_MFMA_BUSY_CYCLES"))
+    _, gui = _split(_per_dispatch(mrows, "GRBM_GUI_ACTIVE"))
+    # counters are in KiB per dispatch; the copy moved COPY_BYTES each way
+    f_fac = COPY_BYTES / (fcopy * 1024.0)
+    w_fac = COPY_BYTES / (wcopy * 1024.0)
+    specs = bench.block_gemms(synth.QWEN3_4B_BLOCK)
+    lines = [
+        "# HBM traffic and MFMA busy time of the block GEMM launches (Qwen3-4B shape, S 512)",
+        "",
+        "Commands (repository root; one counter set per run):",
+        "",
+        "```",
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic/fetch -o f -- python bench_traffic.py run",
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic/write -o w -- python bench_traffic.py run",
+        "rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES --output-format csv -d gpurun_out/traffic/mfma -o m "
+        "-- python bench_traffic.py run",
+        "python bench_traffic.py summarize gpurun_out/traffic/fetch gpurun_out/traffic/write gpurun_out/traffic/mfma "
+        + os.path.relpath(out_path, ROOT),
+        "```",
+        "",
+        f"Calibration: a 256 MiB fp32 copy reads FETCH_SIZE {fcopy:.0f} KiB and writes WRITE_SIZE {wcopy:.0f} KiB; "
+        f"scale factors {f_fac:.4f} (fetch) and {w_fac:.4f} (write) turn the counters into bytes.",
+        "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 128): the first sums over the 1024 SIMDs, the",
+        "second over the 8 XCDs, so this is the busy fraction of an average SIMD over the launch.",
+        "",
+        "| launch | layout M x N x K | dispatches | read MB | written MB | MFMA busy |",
+        "|---|---|---:|---:|---:|---:|",
+    ]
+    total = 0.0
+    names = ["NT", "NN", "TN"]
+    for i, (spec, fd, wd, bd, gd) in enumerate(zip(specs, fl, wl, busy, gui)):
+        rd = sum(v for _, v in fd) * 1024 * f_fac
+        wr = sum(v for _, v in wd) * 1024 * w_fac
+        total += rd + wr
+        util = bd[0][1] / max(gd[0][1] * 128.0, 1.0)
+        lay, M, N, K, _ = spec
+        lines.append(f"| {i} | {names[lay]} {M} x {N} x {K} | {len(fd)} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
+                     f"{util:.3f} |")
+    per = total / len(specs)
+    lines += [
+        "",
+        f"traffic_bytes_per_launch: {per:.0f}",
+        f"gemm_source_sha1: {source_digest()}",
+        "",
+    ]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out_path}: {per / 1e6:.1f} MB per launch")
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 2 and sys.argv[1] == "run":
+        run()
+    elif len(sys.argv) == 6 and sys.argv[1] == "summarize":
+        summarize(*sys.argv[2:6])
+    else:
+        raise SystemExit(__doc__)
