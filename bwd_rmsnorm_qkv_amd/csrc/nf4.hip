@@ -90,26 +90,40 @@ struct LevelArgs {
   float level[16];
 };
 
-__global__ void nf4_dequant_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
-                                   int64_t numel, float* __restrict__ w, LevelArgs L) {
+// fp32 decode: 8 elements (4 code bytes, one scale) per thread, the 16
+// levels from an LDS copy of the codebook; two 16-byte stores.
+__global__ __launch_bounds__(256) void nf4_dequant_kernel(const uint32_t* __restrict__ codes,
+                                                          const float* __restrict__ absmax, int64_t n8,
+                                                          float4* __restrict__ w, LevelArgs L) {
+  __shared__ float lv[16];
+  if (threadIdx.x < 16) lv[threadIdx.x] = L.level[threadIdx.x];
+  __syncthreads();
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= numel) return;
-  const uint8_t b = codes[i >> 1];
-  const int c = (i & 1) ? (b >> 4) : (b & 15);
-  w[i] = L.level[c] * absmax[i >> 6];
+  if (i >= n8) return;
+  const uint32_t b = codes[i];
+  const float a = absmax[i >> 3];
+  float o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = lv[(b >> (4 * j)) & 15] * a;
+  w[2 * i] = make_float4(o[0], o[1], o[2], o[3]);
+  w[2 * i + 1] = make_float4(o[4], o[5], o[6], o[7]);
 }
 
 // fp16 decode for the GEMMs: 8 elements (4 code bytes, one scale) per
 // thread; L[c] * a in fp32, rounded once to fp16.
-__global__ void nf4_dequant_f16_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ absmax,
-                                       int64_t n8, half8* __restrict__ w, LevelArgs L) {
+__global__ __launch_bounds__(256) void nf4_dequant_f16_kernel(const uint32_t* __restrict__ codes,
+                                                              const float* __restrict__ absmax, int64_t n8,
+                                                              half8* __restrict__ w, LevelArgs L) {
+  __shared__ float lv[16];
+  if (threadIdx.x < 16) lv[threadIdx.x] = L.level[threadIdx.x];
+  __syncthreads();
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= n8) return;
   const uint32_t b = codes[i];
   const float a = absmax[i >> 3];
   half8 o;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = (f16)(L.level[(b >> (4 * j)) & 15] * a);
+  for (int j = 0; j < 8; ++j) o[j] = (f16)(lv[(b >> (4 * j)) & 15] * a);
   w[i] = o;
 }
 
@@ -140,10 +154,12 @@ int nf4_quantize(const float* w, int64_t numel, uint8_t* codes, float* absmax, h
 
 int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t numel, float* w, hipStream_t st) {
   if (numel <= 0 || numel % 64) return fail(QBLK_EINVAL, "nf4_dequantize: numel %lld not a positive multiple of 64", (long long)numel);
+  if (((uintptr_t)codes & 3) || ((uintptr_t)w & 15)) return fail(QBLK_EINVAL, "nf4_dequantize: misaligned buffer");
   LevelArgs L;
   for (int i = 0; i < 16; ++i) L.level[i] = codebook().level[i];
-  hipLaunchKernelGGL(nf4_dequant_kernel, dim3((unsigned)ceil_div(numel, 256)), dim3(256), 0, st, codes,
-                     absmax, numel, w, L);
+  const int64_t n8 = numel / 8;
+  hipLaunchKernelGGL(nf4_dequant_kernel, dim3((unsigned)ceil_div(n8, 256)), dim3(256), 0, st,
+                     (const uint32_t*)codes, absmax, n8, (float4*)w, L);
   return check_launch("nf4_dequant_kernel");
 }
 

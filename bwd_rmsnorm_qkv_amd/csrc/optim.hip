@@ -143,18 +143,28 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk c, const Ada
   const bool vec = base + kTile <= n &&
                    (((uintptr_t)w | (uintptr_t)g | (uintptr_t)m | (uintptr_t)v) & 15) == 0;
   if (vec) {
+    // every load of the tile is issued before any store (the stores could
+    // alias later loads as far as the compiler knows, which would otherwise
+    // serialize the four groups)
+    float4 W[4], G[4], M[4], V[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t e = base + 4 * (threadIdx.x + 256 * u);
-      float4 W = *(float4*)(w + e), G = *(const float4*)(g + e), M = *(float4*)(m + e),
-             V = *(float4*)(v + e);
-      adam1(W.x, G.x * sc, M.x, V.x, h);
-      adam1(W.y, G.y * sc, M.y, V.y, h);
-      adam1(W.z, G.z * sc, M.z, V.z, h);
-      adam1(W.w, G.w * sc, M.w, V.w, h);
-      *(float4*)(w + e) = W;
-      *(float4*)(m + e) = M;
-      *(float4*)(v + e) = V;
+      W[u] = *(const float4*)(w + e);
+      G[u] = *(const float4*)(g + e);
+      M[u] = *(const float4*)(m + e);
+      V[u] = *(const float4*)(v + e);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t e = base + 4 * (threadIdx.x + 256 * u);
+      adam1(W[u].x, G[u].x * sc, M[u].x, V[u].x, h);
+      adam1(W[u].y, G[u].y * sc, M[u].y, V[u].y, h);
+      adam1(W[u].z, G[u].z * sc, M[u].z, V[u].z, h);
+      adam1(W[u].w, G[u].w * sc, M[u].w, V[u].w, h);
+      *(float4*)(w + e) = W[u];
+      *(float4*)(m + e) = M[u];
+      *(float4*)(v + e) = V[u];
     }
   } else {
     const int64_t end = min(base + (int64_t)kTile, n);

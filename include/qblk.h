@@ -188,7 +188,8 @@ int32_t qblk_nf4_codebook(float* levels);
 int32_t qblk_nf4_quantize(const float* w, int64_t numel, uint8_t* codes, float* absmax,
                           qblk_stream_t stream);
 
-/* w[i] = level[code_i] * absmax[i/64] (fp32). */
+/* w[i] = level[code_i] * absmax[i/64] (fp32). numel must be a positive
+ * multiple of 64; codes must be 4-byte and w 16-byte aligned (EINVAL). */
 int32_t qblk_nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t numel, float* w,
                             qblk_stream_t stream);
 
