@@ -36,7 +36,12 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(int rows, int n, float
   const float4* xr = (const float4*)(x + (int64_t)row * n);
   const float4* rr = res ? (const float4*)(res + (int64_t)row * n) : nullptr;
   // Loads go to clamped (always valid) columns and are masked afterwards,
-  // so a row's loads are all in flight together instead of one branch each.
+  // so a row's loads (gamma's too) are all in flight together instead of
+  // one branch each.
+  const float4* gr = (const float4*)gamma;
+  float4 gv[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) gv[j] = gr[min(lane + j * 64, n4 - 1)];
   float4 v[VPL];
   float ss = 0.f;
 #pragma unroll
@@ -54,10 +59,6 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(int rows, int n, float
   ss = wave_sum(ss);
   const float rho = 1.0f / sqrtf(ss / (float)n + eps);
   if (lane == 0 && rho_out) rho_out[row] = rho;
-  const float4* gr = (const float4*)gamma;
-  float4 gv[VPL];
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) gv[j] = gr[min(lane + j * 64, n4 - 1)];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int c = lane + j * 64;
