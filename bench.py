@@ -53,15 +53,38 @@ def parse():
     return ap.parse_args()
 
 
+_SPIN_PER_MS = None
+
+
+def front_run(torch, ms):
+    """Queue a spin kernel that keeps the GPU busy for about `ms` so the
+    launches queued behind it are all on the GPU's queue when it ends: the
+    events that follow then time the GPU work, not the host's launch
+    latency on an idle queue (a training loop runs ahead of the GPU the
+    same way). The spin's rate is measured once with events."""
+    global _SPIN_PER_MS
+    if _SPIN_PER_MS is None:
+        torch.cuda._sleep(1000)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(1 << 20)
+        e1.record()
+        torch.cuda.synchronize()
+        _SPIN_PER_MS = (1 << 20) / max(e0.elapsed_time(e1), 1e-3)
+    torch.cuda._sleep(int(_SPIN_PER_MS * ms))
+
+
 def timed(fn, steps, warmup, torch):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    front_run(torch, min(20.0, 1.0 + 0.05 * steps))
     e0.record()
     for _ in range(steps):
         fn()
     e1.record()
+    torch.cuda._sleep(1)  # end marker for kernel traces, outside the timed region
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps  # ms per step
 
@@ -106,8 +129,13 @@ def gemm_traffic():
 
 def gemm_roofline(c, torch, qblk, reps):
     """Replay the step's GEMMs (same kernels, shapes, layouts and operand
-    types as the block), each bracketed by HIP events on the current stream,
-    the stream the launches go to; achieved TFLOP/s over summed durations."""
+    types as the block), timed with HIP events on the current stream, the
+    stream the launches go to, all queued behind a spin kernel so that the
+    events time the GPU work alone. `achieved` = the 12 products' FLOPs
+    over the time of the whole sequence (one event pair around it, so the
+    figure holds the short gaps between kernels); `per_launch_us` from
+    launches bracketed one by one (each figure also holds the event
+    packets' own few microseconds)."""
     specs = block_gemms(c)
     bufs = []
     for (lay, M, N, K, acc) in specs:
@@ -132,14 +160,26 @@ def gemm_roofline(c, torch, qblk, reps):
     for _ in range(3):
         run_all()
     torch.cuda.synchronize()
+    # the sequence: one event pair around the 12 launches (no event packets
+    # between kernels); per launch: each bracketed by its own pair, which
+    # adds the event packets' few microseconds to every figure
     total_ms, per = 0.0, np.zeros(len(bufs))
     for _ in range(reps):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in bufs]
-        run_all(ev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        front_run(torch, 3.0)
+        e0.record()
+        run_all()
+        e1.record()
+        torch.cuda._sleep(1)
         torch.cuda.synchronize()
-        d = np.array([a.elapsed_time(b) for a, b in ev])
-        per += d
-        total_ms += d.sum()
+        total_ms += e0.elapsed_time(e1)
+    for _ in range(reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in bufs]
+        front_run(torch, 3.0)
+        run_all(ev)
+        torch.cuda._sleep(1)
+        torch.cuda.synchronize()
+        per += np.array([a.elapsed_time(b) for a, b in ev])
     step_ms = total_ms / reps
     achieved = flops / (step_ms * 1e-3) / 1e12
     return {
