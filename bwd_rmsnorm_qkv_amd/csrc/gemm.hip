@@ -818,7 +818,7 @@ struct DmaOperand {
   }
 };
 
-template <int BM, int BN, int WM, int WN, int NS, bool AK, bool BK_>
+template <int BM, int BN, int WM, int WN, int NS, int NB, bool AK, bool BK_>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d, const Grid gd) {
   constexpr int BK = 64;
   constexpr int NW = WM * WN;
@@ -887,34 +887,54 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   };
 
   auto stA = [](auto S) { return lds_stage<2 * decltype(S)::value, BM * BK>(); };
-  auto stB = [](auto S) { return lds_stage<2 * decltype(S)::value + 1, BN * BK>(); };
+  // the B stages back to back; B's stage is tracked at run time (NB may
+  // differ from NS)
+  f16* const sB0 = lds_stage<1, NB * BN * BK>();
+  auto stB = [&](int i) { return sB0 + i * (BN * BK); };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  auto issue = [&](int kt, f16* sa, f16* sb) __attribute__((always_inline)) {
-    oa.issue(kt, sa, d.lda, w);
-    ob.issue(kt, sb, d.ldb, w);
-  };
 
-  // Prologue: tiles 0 .. NS-2 in flight.
-  if (0 < nkt) issue(0, stA(I0{}), stB(I0{}));
-  if constexpr (NS > 2) if (1 < nkt) issue(1, stA(I1{}), stB(I1{}));
-  if constexpr (NS > 3) if (2 < nkt) issue(2, stA(I2{}), stB(I2{}));
+  // Prologue: tiles 0 .. NS-2 in flight (A then B per tile); with a deeper
+  // B ring (NB = NS + 1) also B of tile NS-1.
+  if (0 < nkt) {
+    oa.issue(0, stA(I0{}), d.lda, w);
+    ob.issue(0, stB(0), d.ldb, w);
+  }
+  if constexpr (NS > 2) if (1 < nkt) {
+    oa.issue(1, stA(I1{}), d.lda, w);
+    ob.issue(1, stB(1), d.ldb, w);
+  }
+  if constexpr (NS > 3) if (2 < nkt) {
+    oa.issue(2, stA(I2{}), d.lda, w);
+    ob.issue(2, stB(2), d.ldb, w);
+  }
+  if constexpr (NB > NS) if (NS - 1 < nkt) ob.issue(NS - 1, stB(NS - 1), d.ldb, w);
 
-  // Step kt: wait for this wave's copies of tile kt (tiles kt+1 .. kt+NS-2
-  // may stay in flight), barrier (every wave's copies of tile kt landed and
-  // every wave is done with tile kt-1), refill the stage of tile kt-1 with
-  // tile kt+NS-1, then the MFMAs of tile kt.
+  // Step kt: wait for this wave's copies of tile kt (later copies may stay
+  // in flight), barrier (every wave's copies of tile kt landed and every
+  // wave is done with tile kt-1), refill the stages of tile kt-1 with A of
+  // tile kt+NS-1 and B of tile kt+NB-1, then the MFMAs of tile kt.
+  int bs = 0;  // B stage of tile kt
   auto step = [&](auto S, int kt) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
-    if (kt + NS - 2 < nkt) wait_vmcnt<JS * (NS - 2)>();
-    else wait_vmcnt<0>();
+    if constexpr (NB > NS) {
+      // issued after tile kt: A and B of tiles kt+1 .. kt+NS-2, then B of
+      // tile kt+NS-1 (NS = 2: only that B)
+      static_assert(NS == 2 && NB == 3, "deeper B ring: two A stages, three B stages");
+      if (kt + 1 < nkt) wait_vmcnt<OB::J>();
+      else wait_vmcnt<0>();
+    } else {
+      if (kt + NS - 2 < nkt) wait_vmcnt<JS * (NS - 2)>();
+      else wait_vmcnt<0>();
+    }
     __syncthreads();
-    if (kt + NS - 1 < nkt)
-      issue(kt + NS - 1, stA(std::integral_constant<int, (s + NS - 1) % NS>{}),
-            stB(std::integral_constant<int, (s + NS - 1) % NS>{}));
-    compute(stA(S), stB(S));
+    const int bfree = bs == 0 ? NB - 1 : bs - 1;  // B stage of tile kt-1
+    if (kt + NS - 1 < nkt) oa.issue(kt + NS - 1, stA(std::integral_constant<int, (s + NS - 1) % NS>{}), d.lda, w);
+    if (kt + NB - 1 < nkt) ob.issue(kt + NB - 1, stB(bfree), d.ldb, w);
+    compute(stA(S), stB(bs));
+    bs = bs + 1 == NB ? 0 : bs + 1;
   };
   // Whole rounds of NS tiles run without branches around the MFMAs (a
   // conditional step inside the loop makes the compiler copy every
@@ -948,9 +968,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   float* ep;
   switch (w >> 1) {  // two wave slices per stage buffer
     case 0: ep = (float*)stA(I0{}); break;
-    case 1: ep = (float*)stB(I0{}); break;
+    case 1: ep = (float*)stB(0); break;
     case 2: ep = (float*)stA(I1{}); break;
-    default: ep = (float*)stB(I1{}); break;
+    default: ep = (float*)stB(1); break;
   }
   ep += (w & 1) * 32 * WC;
   auto eslot = [](int r, int c) { return r * WC + ((c ^ (((r >> 2) & 1) << 3)) << 2); };
@@ -1028,11 +1048,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
 // trailing half's h1, returned before the third barrier) and is refilled
 // there with tile kt+2, which must have landed (wait + barrier) by the
 // fourth phase of the next tile, when the leading half reads it: copies
-// run a whole K tile ahead of their first read.
-template <int BN, bool AK, bool BK_>
+// run a whole K tile ahead of their first read. With NB = 3 the B operand
+// (the weights of a forward product, streamed from HBM while A stays in L2)
+// has a third stage and its copies run two K tiles ahead: B(kt+3) goes into
+// the stage tile kt just freed.
+template <int BN, bool AK, bool BK_, int NB>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Grid gd) {
-  constexpr int BM = 256, WM = 4, WN = 2, NS = 2, BK = 64;
+  constexpr int BM = 256, WM = 4, WN = 2, BK = 64;
   static_assert(BN == 256 || (BN == 192 && BK_), "192-wide tiles need a K-major B");
+  static_assert(NB == 2 || NB == 3, "B stages");
+  static_assert(2 * BM * BK * 2 + NB * BN * BK * 2 <= 160 * 1024, "LDS");
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   using OA = DmaOperand<BM, AK, NW>;
@@ -1099,46 +1124,61 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
   };
 
   auto stA = [](auto S) { return lds_stage<2 * decltype(S)::value, BM * BK>(); };
-  auto stB = [](auto S) { return lds_stage<2 * decltype(S)::value + 1, BN * BK>(); };
+  f16* const sB0 = lds_stage<1, NB * BN * BK>();  // the B stages, back to back
+  auto stB = [&](int i) { return sB0 + i * (BN * BK); };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  auto issue = [&](int kt, f16* sa, f16* sb) __attribute__((always_inline)) {
-    oa.issue(kt, sa, d.lda, w);
-    ob.issue(kt, sb, d.ldb, w);
-  };
 
   // The two halves run the same barriers; each is its own instantiation,
   // so no branch sits between a wave's MFMAs.
   auto run = [&](auto Lead) __attribute__((always_inline)) {
     constexpr bool lead = decltype(Lead)::value;
-    if (0 < nkt) issue(0, stA(I0{}), stB(I0{}));
-    if (1 < nkt) issue(1, stA(I1{}), stB(I1{}));
-    if (1 < nkt) wait_vmcnt<JS>();
+    if (0 < nkt) {
+      oa.issue(0, stA(I0{}), d.lda, w);
+      ob.issue(0, stB(0), d.ldb, w);
+    }
+    if (1 < nkt) {
+      oa.issue(1, stA(I1{}), d.lda, w);
+      ob.issue(1, stB(1), d.ldb, w);
+    }
+    if (NB == 3 && 2 < nkt) ob.issue(2, stB(2), d.ldb, w);
+    // tile 0 landed; the copies issued after it may still be in flight
+    if (NB == 3 && 2 < nkt) wait_vmcnt<OA::J + 2 * OB::J>();
+    else if (1 < nkt) wait_vmcnt<JS>();
     else wait_vmcnt<0>();
     phase_end();
-    if constexpr (lead) read(stA(I0{}), stB(I0{}), I0{});
+    if constexpr (lead) read(stA(I0{}), stB(0), I0{});
     phase_end();
+    int bs = 0;  // B stage of tile kt
     auto step = [&](auto S, int kt) __attribute__((always_inline)) {
       using SN = std::integral_constant<int, 1 - decltype(S)::value>;
+      const int bn1 = bs + 1 == NB ? 0 : bs + 1;
+      f16* const sb = stB(bs);
       if constexpr (lead) mfma();
-      else read(stA(S), stB(S), I0{});
+      else read(stA(S), sb, I0{});
       phase_end();
-      if constexpr (lead) read(stA(S), stB(S), I1{});
+      if constexpr (lead) read(stA(S), sb, I1{});
       else mfma();
       phase_end();
       if constexpr (lead) mfma();
-      else read(stA(S), stB(S), I1{});
-      wait_vmcnt<0>();  // this wave's copies of tile kt+1
+      else read(stA(S), sb, I1{});
+      // this wave's copies of tile kt+1; with three B stages the B copy of
+      // tile kt+2, issued after them, may stay in flight
+      if (NB == 3 && kt + 2 < nkt) wait_vmcnt<OB::J>();
+      else wait_vmcnt<0>();
       phase_end();
-      // stage S is free now (its last reads returned before the barrier):
-      // refill it with tile kt+2, a whole K tile ahead of its first read
-      if (kt + 2 < nkt) issue(kt + 2, stA(S), stB(S));
+      // the stages of tile kt are free now (their last reads returned
+      // before the barrier): refill A with tile kt+2 and B with tile
+      // kt+NB, ahead of their first reads
+      if (kt + 2 < nkt) oa.issue(kt + 2, stA(S), d.lda, w);
+      if (kt + NB < nkt) ob.issue(kt + NB, sb, d.ldb, w);
       if constexpr (lead) {
-        if (kt + 1 < nkt) read(stA(SN{}), stB(SN{}), I0{});
+        if (kt + 1 < nkt) read(stA(SN{}), stB(bn1), I0{});
       } else {
         mfma();
       }
       phase_end();
+      bs = bn1;
     };
     for (int kt = 0; kt + 1 < nkt; kt += 2) {
       step(I0{}, kt);
@@ -1170,9 +1210,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
   float* ep;
   switch (w >> 1) {  // two wave slices per stage buffer
     case 0: ep = (float*)stA(I0{}); break;
-    case 1: ep = (float*)stB(I0{}); break;
+    case 1: ep = (float*)stB(0); break;
     case 2: ep = (float*)stA(I1{}); break;
-    default: ep = (float*)stB(I1{}); break;
+    default: ep = (float*)stB(1); break;
   }
   ep += (w & 1) * RP * PITCH;
   auto eslot = [](int r, int c) { return r * PITCH + ((POW2 ? (c ^ (((r >> 2) & 1) << 3)) : c) << 2); };
@@ -1349,35 +1389,40 @@ Grid plan_tiles(const GemmDesc& d, size_t ws_bytes, int bm, int bn, int bk, int 
   return g;
 }
 
-// Ping-pong configurations: 256 x 256 for every layout, 256 x 192 for NT.
+// Ping-pong configurations: 256 x 256 for every layout, 256 x 192 for NT
+// (with a third B stage where the LDS allows it).
+#ifndef QBLK_PP_NB192
+#define QBLK_PP_NB192 3
+#endif
+constexpr int kPpNb192 = QBLK_PP_NB192;
 struct PpCfg {
   static constexpr int bm = 256, bn = 256, threads = 512;
   static constexpr bool narrow = true;  // also runs 256 x 192 tiles (NT)
-  template <int BN, bool AK, bool BKM>
+  template <int BN, bool AK, bool BKM, int NB>
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
-    hipLaunchKernelGGL((gemm_pp_kernel<BN, AK, BKM>), dim3(nwg), dim3(threads), 0, st, d, g);
+    hipLaunchKernelGGL((gemm_pp_kernel<BN, AK, BKM, NB>), dim3(nwg), dim3(threads), 0, st, d, g);
   }
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     switch (d.layout) {
       case Layout::NT:
-        if (g.bn == 192) launch<192, true, true>(d, g, st);
-        else launch<256, true, true>(d, g, st);
+        if (g.bn == 192) launch<192, true, true, kPpNb192>(d, g, st);
+        else launch<256, true, true, 2>(d, g, st);
         break;
-      case Layout::NN: launch<256, true, false>(d, g, st); break;
-      case Layout::TN: launch<256, false, false>(d, g, st); break;
+      case Layout::NN: launch<256, true, false, 2>(d, g, st); break;
+      case Layout::TN: launch<256, false, false, 2>(d, g, st); break;
     }
   }
 };
 
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN, int NS, int NB = NS>
 struct DmaCfg {
   static constexpr int bm = BM, bn = BN, threads = WM * WN * 64;
   static constexpr bool narrow = false;
   template <bool AK, bool BKM>
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, AK, BKM>), dim3(nwg), dim3(threads), 0, st, d, g);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, AK, BKM>), dim3(nwg), dim3(threads), 0, st, d, g);
   }
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     switch (d.layout) {
@@ -1391,9 +1436,13 @@ struct DmaCfg {
 using Nt16Small = DmaCfg<QBLK_NT16_CFG>;
 using Nt16Big = Nt16Small;
 #else
-// 128 x 128 tiles, 4 waves, two workgroups per CU (64 KB LDS each); and
-// 256 x 256 tiles, 8 waves of 64 x 128, one workgroup per CU (128 KB LDS).
-using Nt16Small = DmaCfg<128, 128, 2, 2, 2>;
+// 128 x 128 tiles, 4 waves, two workgroups per CU (80 KB LDS each: two A
+// stages, three B stages); and 256 x 256 tiles, 8 waves of 64 x 128, one
+// workgroup per CU.
+#ifndef QBLK_SMALL_NB
+#define QBLK_SMALL_NB 3
+#endif
+using Nt16Small = DmaCfg<128, 128, 2, 2, 2, QBLK_SMALL_NB>;
 #ifdef QBLK_NO_PINGPONG
 using Nt16Big = DmaCfg<256, 256, 4, 2, 2>;
 #else
@@ -1454,9 +1503,9 @@ Grid plan(const GemmDesc& d, size_t ws_bytes) {
   if (nt16_ok(d)) {
     const bool big = nt16_big(d);
     const int bn = big ? big_bn(d) : Nt16Small::bn;
-    // the small tiles run two workgroups per CU: split K for one wave of
-    // 2 x kTargetWgs workgroups
-    Grid g = big ? plan_tiles(d, ws_bytes, Nt16Big::bm, bn, 64)
+    // split K only as far as the workgroups still fit one wave: the big
+    // tiles run one workgroup per CU (kTargetWgs), the small ones two
+    Grid g = big ? plan_tiles(d, ws_bytes, Nt16Big::bm, bn, 64, -kTargetWgs)
                  : plan_tiles(d, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64, -2 * kTargetWgs);
     g.bn = bn;
     g.vec = out_vec4(d, g);

@@ -95,6 +95,34 @@ def test_gemm_fp16_storage(layout, storage, shape):
     check("C+C", Cg, 2 * Cref, FP32_TOL)
 
 
+# fp16 operands with enough output tiles for the 256-row tiles (256 x 192
+# for NT when that takes fewer rounds over the CUs, with a third B stage):
+# one to five K tiles (every prologue/tail case of the copy pipeline), a
+# ragged N, a ragged M, and a 128-tile product that splits K
+GEMM16_BIG = [(0, 512, 16376, 64), (0, 512, 16376, 128), (0, 512, 16376, 192), (0, 512, 16376, 256),
+              (0, 512, 16376, 320), (0, 520, 16376, 256), (1, 512, 16384, 1024), (2, 4096, 2048, 64),
+              (2, 4096, 2040, 192)]
+
+
+@pytest.mark.parametrize("layout,M,N,K", GEMM16_BIG)
+def test_gemm_fp16_big_tiles(layout, M, N, K):
+    need_gpu()
+    announce(f"gemm16 big layout={layout} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + 3 * N + 7 * K + layout)
+    a_shape = (M, K) if layout in (0, 1) else (K, M)
+    b_shape = (N, K) if layout == 0 else (K, N)
+    A16 = rng.standard_normal(a_shape).astype(np.float16)
+    B16 = rng.standard_normal(b_shape).astype(np.float16)
+    a64, b64 = A16.astype(np.float64), B16.astype(np.float64)
+    Cref = (a64 if layout != 2 else a64.T) @ (b64.T if layout == 0 else b64)
+    ws = qblk.gemm_workspace_size(layout, 1, M, N, K)
+    scratch = byte_buffer(ws) if ws else None
+    Cg = torch.full((M, N), 3.0, device="cuda")
+    qblk.gemm(layout, 1, M, N, K, dev(A16), a_shape[1], dev(B16), b_shape[1], Cg, N, scratch=scratch)
+    torch.cuda.synchronize()
+    check("C", Cg, Cref, FP32_TOL)
+
+
 @pytest.mark.parametrize("rows,n", [(32, 64), (77, 512), (512, 2560), (5, 4096)])
 def test_rmsnorm(rows, n):
     need_gpu()
