@@ -39,6 +39,20 @@ __device__ __forceinline__ int find_tensor(const int64_t* tile_end, int count, i
   return j;
 }
 
+// Streaming access for AdamW: every element of w, g, m, v is read once and
+// w, m, v written once per call, over GBs far beyond the caches, so its
+// loads and stores carry the nontemporal hint (measured faster there; the
+// squared sum's plain loads measured faster than hinted ones).
+typedef float f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream(const float* p) {
+  const f4v v = __builtin_nontemporal_load((const f4v*)p);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(float* p, const float4 x) {
+  const f4v v = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(v, (f4v*)p);
+}
+
 __global__ __launch_bounds__(256) void sqsum_kernel(const SqChunk c, double* partial) {
   __shared__ double red[256];
   const int tid = threadIdx.x;
@@ -150,10 +164,10 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk c, const Ada
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t e = base + 4 * (threadIdx.x + 256 * u);
-      W[u] = *(const float4*)(w + e);
-      G[u] = *(const float4*)(g + e);
-      M[u] = *(const float4*)(m + e);
-      V[u] = *(const float4*)(v + e);
+      W[u] = load_stream(w + e);
+      G[u] = load_stream(g + e);
+      M[u] = load_stream(m + e);
+      V[u] = load_stream(v + e);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -162,9 +176,9 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk c, const Ada
       adam1(W[u].y, G[u].y * sc, M[u].y, V[u].y, h);
       adam1(W[u].z, G[u].z * sc, M[u].z, V[u].z, h);
       adam1(W[u].w, G[u].w * sc, M[u].w, V[u].w, h);
-      *(float4*)(w + e) = W[u];
-      *(float4*)(m + e) = M[u];
-      *(float4*)(v + e) = V[u];
+      store_stream(w + e, W[u]);
+      store_stream(m + e, M[u]);
+      store_stream(v + e, V[u]);
     }
   } else {
     const int64_t end = min(base + (int64_t)kTile, n);
