@@ -480,6 +480,13 @@ __device__ __forceinline__ void put_out(const GemmDesc& d, float* cp, int row, i
   *cp = v;
 }
 
+// 16 bytes of the final output, with the nontemporal hint: the outputs are
+// written once and read back, if at all, by a later kernel (measured faster
+// for every product of the block, the weight gradients most).
+__device__ __forceinline__ void store_c4(float4* cp, const float4 o) {
+  __builtin_nontemporal_store(floatx4{o.x, o.y, o.z, o.w}, (floatx4*)cp);
+}
+
 // Output row pointer (segment routing), or nullptr when the row is out of
 // range; `lo` is the first column this row keeps (diagonal-block mode).
 __device__ __forceinline__ float* out_row(const GemmDesc& d, int row, int& lo) {
@@ -1023,7 +1030,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
           o.z += cv.z;
           o.w += cv.w;
         }
-        *cp = o;
+        store_c4(cp, o);
         if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + col) = to_half4(o);
       } else {
         for (int j = 0; j < 4 && col + j < d.N; ++j) {
@@ -1267,7 +1274,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
             o.z += cv.z;
             o.w += cv.w;
           }
-          *cp = o;
+          store_c4(cp, o);
           if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + col) = to_half4(o);
         } else {
           for (int j = 0; j < 4 && col + j < d.N; ++j) {
@@ -1318,7 +1325,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmDesc d, in
           o.z += cv.z;
           o.w += cv.w;
         }
-        *cp = o;
+        store_c4(cp, o);
         if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + c0) = to_half4(o);
       } else {
         const float vv[4] = {v.x, v.y, v.z, v.w};
