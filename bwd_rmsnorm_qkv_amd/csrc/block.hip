@@ -431,7 +431,12 @@ int dense16_forward(const qblk_config& c, const qblk_block_params& p, const floa
   pf.down = [&](const float*, const float* res, float* out, hipStream_t s_) {
     return proj(s.s16, I, W.d, h, res, out, s_);
   };
-  return block_forward_impl(c, pf, p.g_in, p.g_post, p.g_q, p.g_k, x, y, s, st);
+  // n1, n2 and s are read only through their fp16 copies on this path
+  // (products and weight gradients; the norm backwards read x, r1 and the
+  // saved rho): their fp32 forms are not written
+  Saved s16 = s;
+  s16.n1 = s16.n2 = s16.s = nullptr;
+  return block_forward_impl(c, pf, p.g_in, p.g_post, p.g_q, p.g_k, x, y, s16, st);
 }
 
 // dX = dY W (NN: dY16 [T, n_out] K-major, W16 [n_out, n_in] read out-major)
