@@ -24,6 +24,11 @@ CASES = {
                                         seq=96, batch=2, rope_theta=1e4, gemm_precision=1),
     "small_fp16_t200": synth.BlockShape(hidden=512, heads=8, kv_heads=2, head_dim=64, intermediate=1408,
                                         seq=100, batch=2, rope_theta=1e4, gemm_precision=1),
+    # few tokens and a wide hidden size: the long-K products split K, the
+    # down projection's dX among them, so its split-K reduce applies the
+    # fused SwiGLU backward
+    "fp16_wide_split": synth.BlockShape(hidden=4096, heads=8, kv_heads=2, head_dim=64, intermediate=512,
+                                        seq=64, batch=1, rope_theta=1e4, gemm_precision=1),
     "qwen3_4b": synth.QWEN3_4B_BLOCK,
 }
 
