@@ -52,7 +52,9 @@ int pack16(const qblk_config& c, const qblk_block_params& p, const Packed16& out
 struct Scratch {
   float *ds, *dgu, *dn2, *dr1, *d_o, *dqr, *dkr, *dqkv, *dn1;
   char* attn;
-  float* red;
+  // per-block gamma-gradient partial sums: the post-attention norm's, the
+  // QK norms', the input norm's (all summed by one launch at the end)
+  float *red, *red_qk, *red_in;
   float* gemm_ws;  // split-K partial sums of the block's GEMMs
   size_t gemm_ws_bytes;
   // fp16-operand dense block only: operand copies and, when the caller

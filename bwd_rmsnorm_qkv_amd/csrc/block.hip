@@ -131,9 +131,9 @@ void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes, 
   s.dqkv = cv.take<float>(T * (qd + 2 * kvd));
   s.dn1 = cv.take<float>(T * h);
   s.attn = cv.take<char>(attention_bwd_scratch(c.batch, c.seq, c.heads, c.head_dim));
-  const size_t red = std::max(rmsnorm_bwd_scratch((int)T, c.hidden),
-                              qk_norm_rope_bwd_scratch((int)T, c.heads, c.kv_heads, c.head_dim));
-  s.red = cv.take<float>(red / sizeof(float) + 1);
+  s.red = cv.take<float>(rmsnorm_bwd_scratch((int)T, c.hidden) / sizeof(float) + 1);
+  s.red_qk = cv.take<float>(qk_norm_rope_bwd_scratch((int)T, c.heads, c.kv_heads, c.head_dim) / sizeof(float) + 1);
+  s.red_in = cv.take<float>(rmsnorm_bwd_scratch((int)T, c.hidden) / sizeof(float) + 1);
   s.gemm_ws_bytes = block_gemm_ws(c, lora_rank);
   s.gemm_ws = cv.take<float>(s.gemm_ws_bytes / sizeof(float) + 1);
   s.a16 = nullptr;
@@ -297,8 +297,12 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
   QBLK_TRY(swiglu_backward(T, I, s.gu, w.ds, p16 ? nullptr : w.dgu, p16 ? w.a16 : nullptr, st));
   QBLK_TRY(proj.gate_up(p16 ? nullptr : w.dgu, s.n2, w.dn2, st));
   // post-attention norm backward, plus the second residual's gradient dy
-  QBLK_TRY(rmsnorm_backward(T, h, c.eps, s.r1, g_post, w.dn2, dy, w.dr1, p16 ? w.a16 : nullptr, dg_post, w.red,
-                            st));
+  // the gamma gradients are finished by one column-sum launch at the end
+  ColsumJob jobs[kMaxColsumJobs];
+  int nj = 0;
+  QBLK_TRY(rmsnorm_backward_partials(T, h, c.eps, s.r1, g_post, w.dn2, dy, w.dr1, p16 ? w.a16 : nullptr, w.red,
+                                     st));
+  jobs[nj++] = ColsumJob{rmsnorm_bwd_parts(T, h), h, w.red, dg_post};
   // O projection
   QBLK_TRY(proj.o(p16 ? nullptr : w.dr1, s.o, w.d_o, st));
   // attention backward: dq, dk at the attention inputs; dv straight into dqkv
@@ -341,11 +345,12 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
     qb.dqkv = nullptr;
     qb.dqkv16 = w.a16;
   }
-  QBLK_TRY(qk_norm_rope_backward(qb, w.red, st));
+  QBLK_TRY(qk_norm_rope_backward_partials(qb, w.red_qk, jobs, nj, st));
   QBLK_TRY(proj.qkv(qkv16 ? nullptr : w.dqkv, s.n1, w.dn1, st));
   // input norm backward, plus the first residual's gradient dr1
-  QBLK_TRY(rmsnorm_backward(T, h, c.eps, x, g_in, w.dn1, w.dr1, dx, nullptr, dg_in, w.red, st));
-  return QBLK_OK;
+  QBLK_TRY(rmsnorm_backward_partials(T, h, c.eps, x, g_in, w.dn1, w.dr1, dx, nullptr, w.red_in, st));
+  jobs[nj++] = ColsumJob{rmsnorm_bwd_parts(T, h), h, w.red_in, dg_in};
+  return colsum_jobs(nj, jobs, st);
 }
 
 // ------------------------------------------------- dense (fp32 master) block

@@ -247,6 +247,14 @@ size_t qk_norm_rope_bwd_scratch(int T, int heads, int kv_heads, int head_dim) {
 }
 
 int qk_norm_rope_backward(const QkRopeBwdArgs& a, float* scratch, hipStream_t st) {
+  ColsumJob jobs[2];
+  int nj = 0;
+  QBLK_TRY(qk_norm_rope_backward_partials(a, scratch, jobs, nj, st));
+  return nj ? colsum_jobs(nj, jobs, st) : 0;
+}
+
+int qk_norm_rope_backward_partials(const QkRopeBwdArgs& a, float* scratch, ColsumJob* jobs, int& njobs,
+                                   hipStream_t st) {
   const int d = a.head_dim;
   const int pq = qk_parts(a.T, a.heads), pk = qk_parts(a.T, a.kv_heads);
   float* part_q = scratch;
@@ -254,7 +262,8 @@ int qk_norm_rope_backward(const QkRopeBwdArgs& a, float* scratch, hipStream_t st
   hipLaunchKernelGGL(qk_rope_bwd_kernel, dim3((unsigned)(pq + pk)), dim3(256), 0, st, a, pq, part_q, part_k);
   QBLK_TRY(check_launch("qk_rope_bwd_kernel"));
   if (a.qk_norm) {
-    QBLK_TRY(colsum2(pq, d, part_q, a.dg_q, pk, d, part_k, a.dg_k, st));
+    jobs[njobs++] = ColsumJob{pq, d, part_q, a.dg_q};
+    jobs[njobs++] = ColsumJob{pk, d, part_k, a.dg_k};
   } else {
     if (a.dg_q) hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, a.dg_q, d, 0.f);
     if (a.dg_k) hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, a.dg_k, d, 0.f);

@@ -18,11 +18,20 @@ int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res
 int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* gamma,
                      const float* dy, const float* dres, float* dx, f16* dx16, float* dgamma, float* scratch,
                      hipStream_t st);
+// The same, leaving dgamma's per-block partial sums ([rmsnorm_bwd_parts,
+// n]) in `partial` for a later column sum.
+int rmsnorm_backward_partials(int rows, int n, float eps, const float* x, const float* gamma, const float* dy,
+                              const float* dres, float* dx, f16* dx16, float* partial, hipStream_t st);
 // out[c] = sum_p partial[p][c], fixed order.
 int colsum(int parts, int n, const float* partial, float* out, hipStream_t st);
-// Two such sums in one launch.
-int colsum2(int parts0, int n0, const float* p0, float* o0, int parts1, int n1, const float* p1, float* o1,
-            hipStream_t st);
+// Up to four such sums in one launch.
+struct ColsumJob {
+  int parts, n;
+  const float* partial;
+  float* out;
+};
+constexpr int kMaxColsumJobs = 4;
+int colsum_jobs(int njobs, const ColsumJob* jobs, hipStream_t st);
 
 // RoPE table: tab[s][i] = (cos, sin)(s * theta^(-2i/d)), computed in fp64.
 int rope_table(int seq, int head_dim, float theta, float2* tab, hipStream_t st);
@@ -61,6 +70,11 @@ struct QkRopeBwdArgs {
 };
 size_t qk_norm_rope_bwd_scratch(int T, int heads, int kv_heads, int head_dim);
 int qk_norm_rope_backward(const QkRopeBwdArgs& a, float* scratch, hipStream_t st);
+// The same with dg_q, dg_k left as per-block partial sums in `scratch`;
+// `jobs` receives the column sums that finish them (none without QK-norm,
+// when dg_q and dg_k are zero-filled here).
+int qk_norm_rope_backward_partials(const QkRopeBwdArgs& a, float* scratch, ColsumJob* jobs, int& njobs,
+                                   hipStream_t st);
 
 // s = silu(g) * u with g, u the two halves of gu [T, 2I]; s fp32 and/or fp16.
 int swiglu_forward(int T, int I, const float* gu, float* s, f16* s16, hipStream_t st);

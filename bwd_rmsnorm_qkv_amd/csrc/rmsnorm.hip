@@ -190,12 +190,13 @@ __global__ __launch_bounds__(1024) void colsum_kernel(int parts, int n, const fl
   colsum_cols(parts, n, partial, out);
 }
 
-// Two independent column sums in one launch (blockIdx.y picks the job).
-__global__ __launch_bounds__(1024) void colsum2_kernel(int parts0, int n0, const float* __restrict__ p0,
-                                                       float* __restrict__ o0, int parts1, int n1,
-                                                       const float* __restrict__ p1, float* __restrict__ o1) {
-  if (blockIdx.y == 0) colsum_cols(parts0, n0, p0, o0);
-  else colsum_cols(parts1, n1, p1, o1);
+// Independent column sums in one launch (blockIdx.y picks the job).
+struct ColsumJobs {
+  ColsumJob j[kMaxColsumJobs];
+};
+__global__ __launch_bounds__(1024) void colsum_jobs_kernel(const ColsumJobs jobs) {
+  const ColsumJob& j = jobs.j[blockIdx.y];
+  if ((int)blockIdx.x * 64 < j.n) colsum_cols(j.parts, j.n, j.partial, j.out);
 }
 
 int vpl_for(int n) {
@@ -247,6 +248,12 @@ int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res
 int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* gamma,
                      const float* dy, const float* dres, float* dx, f16* dx16, float* dgamma, float* scratch,
                      hipStream_t st) {
+  QBLK_TRY(rmsnorm_backward_partials(rows, n, eps, x, gamma, dy, dres, dx, dx16, scratch, st));
+  return colsum(rmsnorm_bwd_parts(rows, n), n, scratch, dgamma, st);
+}
+
+int rmsnorm_backward_partials(int rows, int n, float eps, const float* x, const float* gamma, const float* dy,
+                              const float* dres, float* dx, f16* dx16, float* scratch, hipStream_t st) {
   QBLK_TRY(rmsnorm_check(rows, n));
   const int parts = rmsnorm_bwd_parts(rows, n);
   const dim3 grid((unsigned)parts), block(256);
@@ -259,16 +266,19 @@ int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* ga
     QBLK_CASE(1) QBLK_CASE(2) QBLK_CASE(4) QBLK_CASE(8) QBLK_CASE(12) QBLK_CASE(16)
 #undef QBLK_CASE
   }
-  QBLK_TRY(check_launch("rmsnorm_bwd_kernel"));
-  return colsum(parts, n, scratch, dgamma, st);
+  return check_launch("rmsnorm_bwd_kernel");
 }
 
-int colsum2(int parts0, int n0, const float* p0, float* o0, int parts1, int n1, const float* p1, float* o1,
-            hipStream_t st) {
-  const int n = n0 > n1 ? n0 : n1;
-  hipLaunchKernelGGL(colsum2_kernel, dim3((unsigned)ceil_div(n, 64), 2), dim3(1024), 0, st, parts0, n0, p0, o0,
-                     parts1, n1, p1, o1);
-  return check_launch("colsum2_kernel");
+int colsum_jobs(int njobs, const ColsumJob* jobs, hipStream_t st) {
+  if (njobs <= 0 || njobs > kMaxColsumJobs) return fail(QBLK_EINVAL, "colsum: %d jobs", njobs);
+  ColsumJobs js{};
+  int n = 0;
+  for (int i = 0; i < njobs; ++i) {
+    js.j[i] = jobs[i];
+    n = std::max(n, jobs[i].n);
+  }
+  hipLaunchKernelGGL(colsum_jobs_kernel, dim3((unsigned)ceil_div(n, 64), (unsigned)njobs), dim3(1024), 0, st, js);
+  return check_launch("colsum_jobs_kernel");
 }
 
 int colsum(int parts, int n, const float* partial, float* out, hipStream_t st) {
