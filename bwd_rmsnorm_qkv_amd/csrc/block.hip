@@ -240,8 +240,9 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
   const int ldqkv = qd + 2 * kvd;
 
-  QBLK_TRY(rope_table(c.seq, d, c.rope_theta, s.tab, st));
-  QBLK_TRY(rmsnorm_forward(T, h, c.eps, x, nullptr, g_in, s.n1, s.n1_16, nullptr, s.rho1, st));
+  // the input norm's launch also writes the RoPE table (independent work)
+  const RopeTabJob tj = rope_table_job(c.seq, d, c.rope_theta, s.tab);
+  QBLK_TRY(rmsnorm_forward(T, h, c.eps, x, nullptr, g_in, s.n1, s.n1_16, nullptr, s.rho1, st, &tj));
   QBLK_TRY(proj.qkv(s.n1, s.qkv, st));
   QkRopeArgs qa{T, c.seq, c.heads, c.kv_heads, d, c.qk_norm, c.eps, s.qkv, ldqkv, g_q, g_k, s.tab,
                 s.qr, s.kr, s.rho_q, s.rho_k};

@@ -20,14 +20,7 @@
 namespace qblk {
 namespace {
 
-__global__ void rope_table_kernel(int seq, int half, int d, double log_theta, float2* tab) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= seq * half) return;
-  const int s = idx / half, i = idx % half;
-  const double f = exp(-2.0 * (double)i / (double)d * log_theta);
-  const double a = (double)s * f;
-  tab[idx] = make_float2((float)cos(a), (float)sin(a));
-}
+__global__ void rope_table_kernel(const RopeTabJob j) { rope_entry(j, blockIdx.x * blockDim.x + threadIdx.x); }
 
 // Forward: one wave per (t, head) over the H + KV heads (plus the KV value
 // heads when their fp16 copy is requested).
@@ -229,10 +222,20 @@ unsigned grid_for(int64_t n4) { return (unsigned)std::max<int64_t>(1, std::min<i
 
 }  // namespace
 
+RopeTabJob rope_table_job(int seq, int head_dim, float theta, float2* tab) {
+  RopeTabJob j;
+  j.seq = seq;
+  j.half = head_dim / 2;
+  j.d = head_dim;
+  j.log_theta = log((double)theta);
+  j.tab = tab;
+  return j;
+}
+
 int rope_table(int seq, int head_dim, float theta, float2* tab, hipStream_t st) {
-  const int half = head_dim / 2;
-  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)ceil_div((int64_t)seq * half, 256)), dim3(256), 0,
-                     st, seq, half, head_dim, log((double)theta), tab);
+  const RopeTabJob j = rope_table_job(seq, head_dim, theta, tab);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)ceil_div((int64_t)seq * j.half, 256)), dim3(256), 0,
+                     st, j);
   return check_launch("rope_table_kernel");
 }
 

@@ -11,9 +11,11 @@ int rmsnorm_bwd_parts(int rows, int n);
 size_t rmsnorm_bwd_scratch(int rows, int n);
 
 // y (fp32) and/or y16 (fp16) = RMSNorm(x [+ res]) * gamma; sum_out = x + res.
+// With `tab` the same launch also writes that RoPE table.
+struct RopeTabJob;
 int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res,
                     const float* gamma, float* y, f16* y16, float* sum_out, float* rho,
-                    hipStream_t st);
+                    hipStream_t st, const RopeTabJob* tab = nullptr);
 // dx = RMSNorm backward (+ dres); dgamma overwritten; scratch: rmsnorm_bwd_scratch.
 int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* gamma,
                      const float* dy, const float* dres, float* dx, f16* dx16, float* dgamma, float* scratch,
@@ -35,6 +37,21 @@ int colsum_jobs(int njobs, const ColsumJob* jobs, hipStream_t st);
 
 // RoPE table: tab[s][i] = (cos, sin)(s * theta^(-2i/d)), computed in fp64.
 int rope_table(int seq, int head_dim, float theta, float2* tab, hipStream_t st);
+// The same table as extra workgroups of another launch (it depends on no
+// other data): entry idx < seq * half of the job.
+struct RopeTabJob {
+  int seq = 0, half = 0, d = 0;
+  double log_theta = 0.0;
+  float2* tab = nullptr;
+};
+RopeTabJob rope_table_job(int seq, int head_dim, float theta, float2* tab);
+__device__ __forceinline__ void rope_entry(const RopeTabJob& j, int idx) {
+  if (idx >= j.seq * j.half) return;
+  const int s = idx / j.half, i = idx % j.half;
+  const double f = exp(-2.0 * (double)i / (double)j.d * j.log_theta);
+  const double a = (double)s * f;
+  j.tab[idx] = make_float2((float)cos(a), (float)sin(a));
+}
 
 // Per-head RMSNorm (optional) + NeoX RoPE of the q and k heads of a packed
 // [T, (H + 2KV) d] projection output. Writes qr [T, H d], kr [T, KV d]

@@ -28,7 +28,13 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(int rows, int n, float
                                                           float* __restrict__ y,
                                                           f16* __restrict__ y16,
                                                           float* __restrict__ sum_out,
-                                                          float* __restrict__ rho_out) {
+                                                          float* __restrict__ rho_out,
+                                                          const RopeTabJob tj) {
+  const int nb = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
+  if ((int)blockIdx.x >= nb) {  // the RoPE table's workgroups
+    rope_entry(tj, ((int)blockIdx.x - nb) * 256 + threadIdx.x);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -230,14 +236,16 @@ int rmsnorm_check(int rows, int n) {
 
 int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res,
                     const float* gamma, float* y, f16* y16, float* sum_out, float* rho,
-                    hipStream_t st) {
+                    hipStream_t st, const RopeTabJob* tab) {
   QBLK_TRY(rmsnorm_check(rows, n));
-  const dim3 grid((unsigned)ceil_div(rows, kWavesPerBlock)), block(256);
+  const RopeTabJob tj = tab ? *tab : RopeTabJob{};
+  const int64_t tab_blocks = ceil_div((int64_t)tj.seq * tj.half, 256);
+  const dim3 grid((unsigned)(ceil_div(rows, kWavesPerBlock) + tab_blocks)), block(256);
   switch (vpl_for(n)) {
 #define QBLK_CASE(V)                                                                          \
   case V:                                                                                     \
     hipLaunchKernelGGL(rmsnorm_fwd_kernel<V>, grid, block, 0, st, rows, n, eps, x, res, gamma, \
-                       y, y16, sum_out, rho);                                                 \
+                       y, y16, sum_out, rho, tj);                                             \
     break;
     QBLK_CASE(1) QBLK_CASE(2) QBLK_CASE(4) QBLK_CASE(8) QBLK_CASE(12) QBLK_CASE(16)
 #undef QBLK_CASE
