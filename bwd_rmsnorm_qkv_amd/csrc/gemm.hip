@@ -489,11 +489,23 @@ __device__ __forceinline__ void store_c4(float4* cp, const float4 o) {
 
 // Output row pointer (segment routing), or nullptr when the row is out of
 // range; `lo` is the first column this row keeps (diagonal-block mode).
+// The segment is picked by arithmetic on the scalar kernel arguments (its
+// base as an offset from segment 0's, its first row as a sum), not by
+// d.c.p[sg]: with a per-lane sg that is a vector load from the argument
+// segment, and its wait (vmcnt counts stores too) would stall every
+// epilogue iteration until all of the tile's earlier stores had completed.
+// The offsets keep the pointer derived from a global one, so the stores
+// stay global stores.
 __device__ __forceinline__ float* out_row(const GemmDesc& d, int row, int& lo) {
   if (row >= d.M) return nullptr;
-  const int sg = seg_of(d.c, row);
-  lo = d.c_cols_blockdiag > 0 ? sg * d.c_cols_blockdiag : 0;
-  return (float*)d.c.p[sg] + (int64_t)(row - d.c.start[sg]) * d.ldc;
+  const int in1 = d.c.nseg > 1 && row >= d.c.start[1];
+  const int in2 = d.c.nseg > 2 && row >= d.c.start[2];
+  const uintptr_t b0 = (uintptr_t)d.c.p[0];
+  const int64_t o1 = (int64_t)((uintptr_t)d.c.p[1] - b0), o2 = (int64_t)((uintptr_t)d.c.p[2] - b0);
+  const int64_t off = in2 * o2 + (in1 - in2) * o1;
+  const int start = in1 * d.c.start[1] + in2 * (d.c.start[2] - d.c.start[1]);
+  lo = d.c_cols_blockdiag > 0 ? (in1 + in2) * d.c_cols_blockdiag : 0;
+  return (float*)((char*)d.c.p[0] + off) + (int64_t)(row - start) * d.ldc;
 }
 
 __device__ __forceinline__ void store_out(const GemmDesc& d, int row, int col, float acc) {
