@@ -508,6 +508,67 @@ __device__ __forceinline__ float* out_row(const GemmDesc& d, int row, int& lo) {
   return (float*)((char*)d.c.p[0] + off) + (int64_t)(row - start) * d.ldc;
 }
 
+// Fast path of one epilogue pass over rows rowb .. rowb + R - 1 and the
+// wave's 4 CPR columns from col0, when they all lie inside C (and inside one
+// output segment), rows are 16-byte aligned and no diagonal-block mode is
+// set. Lane (lr, lc) = (lane / CPR, lane % CPR) takes column col0 + 4 lc of
+// rows lr, lr + RS, ... (RS = 64 / CPR rows per step; when CPR does not
+// divide 64 the last 64 - RS CPR lanes idle): its pointers are formed once
+// per pass and then advance by a constant stride, the staged values sit at
+// fixed LDS offsets, so each store costs a handful of instructions. `part`
+// (split-K partial of this tile's split) receives the raw sums instead.
+// Returns false when the pass needs the general path.
+template <int R, int CPR, class Slot>
+__device__ __forceinline__ bool epi_pass_fast(const GemmDesc& d, bool vec, float* part, int rowb, int col0,
+                                              const float* ep, Slot eslot, int lane) {
+  constexpr int RS = 64 / CPR;  // rows per step
+  static_assert(RS >= 1 && R % RS == 0, "rows per pass");
+  if (!vec || d.c_cols_blockdiag > 0 || rowb + R > d.M || col0 + 4 * CPR > d.N) return false;
+  const int last = rowb + R - 1;
+  if (!part && d.c.nseg > 1 && (rowb >= d.c.start[1]) != (last >= d.c.start[1])) return false;
+  if (!part && d.c.nseg > 2 && (rowb >= d.c.start[2]) != (last >= d.c.start[2])) return false;
+  // every test above is uniform over the wave: from here on the pass is done
+  if (lane >= RS * CPR) return true;  // idle lanes
+  const int lr = lane / CPR, lc = lane % CPR;
+  const int64_t col = col0 + 4 * lc;
+  if (part) {
+    float* pp = part + (int64_t)(rowb + lr) * d.N + col;
+    const int64_t ps = (int64_t)RS * d.N;
+#pragma unroll
+    for (int q = 0; q < R / RS; ++q) *(float4*)(pp + q * ps) = *(const float4*)(ep + eslot(lr + q * RS, lc));
+    return true;
+  }
+  int lo = 0;
+  float* const cp = out_row(d, rowb + lr, lo) + col;
+  const int64_t cs = (int64_t)RS * d.ldc;
+  const float* const rp = d.r ? d.r + (int64_t)(rowb + lr) * d.ldr + col : nullptr;
+  const int64_t rs = (int64_t)RS * d.ldr;
+  f16* const hp = d.c16 ? d.c16 + (int64_t)(rowb + lr) * d.ldc16 + col : nullptr;
+  const int64_t hs = (int64_t)RS * d.ldc16;
+#pragma unroll
+  for (int q = 0; q < R / RS; ++q) {
+    const float4 v = *(const float4*)(ep + eslot(lr + q * RS, lc));
+    float4 o = make_float4(d.alpha * v.x, d.alpha * v.y, d.alpha * v.z, d.alpha * v.w);
+    if (rp) {
+      const float4 rv = *(const float4*)(rp + q * rs);
+      o.x += rv.x;
+      o.y += rv.y;
+      o.z += rv.z;
+      o.w += rv.w;
+    }
+    if (d.accumulate) {
+      const float4 cv = *(const float4*)(cp + q * cs);
+      o.x += cv.x;
+      o.y += cv.y;
+      o.z += cv.z;
+      o.w += cv.w;
+    }
+    store_c4((float4*)(cp + q * cs), o);
+    if (hp) *(half4*)(hp + q * hs) = to_half4(o);
+  }
+  return true;
+}
+
 __device__ __forceinline__ void store_out(const GemmDesc& d, int row, int col, float acc) {
   int lo = 0;
   float* rp = out_row(d, row, lo);
@@ -1008,6 +1069,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
           ep[eslot(8 * g + 4 * kh + r, c >> 2) + (c & 3)] = acc[tm][tn][4 * g + r];
         }
     const int rowb = m0 + wm * TM * 32 + tm * 32;
+    if (epi_pass_fast<32, CPR>(d, gd.vec, part, rowb, col0, ep, eslot, lane)) continue;
 #pragma unroll 1
     for (int q = 0; q < 32 * CPR / 64; ++q) {
       const int L = q * 64 + lane, rr = L / CPR, c = L % CPR;
@@ -1252,6 +1314,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
             ep[eslot(8 * g2 + 4 * kh + r, c >> 2) + (c & 3)] = acc[tm][tn][4 * (hh * (RP / 8) + g2) + r];
           }
       const int rowb = m0 + wm * TM * 32 + tm * 32 + RP * hh;
+      if (epi_pass_fast<RP, CPR>(d, gd.vec, part, rowb, col0, ep, eslot, lane)) continue;
 #pragma unroll 1
       for (int q = 0; q < RP * CPR / 64; ++q) {
         const int L = q * 64 + lane, rr = L / CPR, c = L % CPR;
