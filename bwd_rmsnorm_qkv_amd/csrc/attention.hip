@@ -914,7 +914,7 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // 2^kRescaleSlack, far inside fp16 range.
 constexpr float kRescaleSlack = 8.f;
 
-// Forward: grid (q tiles, heads, batch), longest query tiles first. The W
+// Forward: grid (pairs of q tiles, heads, batch), the later tile first. The W
 // waves take key tiles w, w+W, ...; each keeps its own reference max, sum
 // and output; they are merged with a log-sum-exp combine and wave 0 writes
 // o and lse. Only the diagonal tile needs the causal mask: every earlier
@@ -938,114 +938,122 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
   const T* vT = (const T*)a.vT;
   const int G = a.heads / a.kv_heads, h = blockIdx.y, grp = h / G, b = blockIdx.z;
   const int S = a.seq;
-  const int qt = gridDim.x - 1 - blockIdx.x, q0 = qt * 32;
-  const int64_t tok0 = (int64_t)b * S;
-  const int i = lane & 31, kh = lane >> 5;
-  const float sc = kLog2e / sqrtf((float)D);
-  const int qi = q0 + i;
+  // tiles t and ntl-1-t share a workgroup (pass 0 the later tile): every
+  // workgroup then has the same causal work, and half as many fit one wave
+  const int ntl = (S + 31) / 32, pr = blockIdx.x;
+  const int npass = 2 * pr + 1 == ntl ? 1 : 2;
+  for (int pass = 0; pass < npass; ++pass) {
+    if (pass) __syncthreads();  // the previous tile's combine is done with the stages
+    const int qt = pass == 0 ? ntl - 1 - pr : pr, q0 = qt * 32;
+    const int64_t tok0 = (int64_t)b * S;
+    const int i = lane & 31, kh = lane >> 5;
+    const float sc = kLog2e / sqrtf((float)D);
+    const int qi = q0 + i;
 
-  const RowReads<T, D> rk(i, kh, w * RT::ELEMS);
-  const XtReads<T, D> rv = make_xt_reads<T, D>(lane, w * RT::ELEMS, w * VE);
-  const RowCopy<T, D> ck(lane, a.ldk);
-  using VCopy = std::conditional_t<TR, RowCopy<T, D>, TrCopy<(TR ? 64 : D)>>;
-  const VCopy cv(lane, TR ? a.ldv : a.ldt);
+    const RowReads<T, D> rk(i, kh, w * RT::ELEMS);
+    const XtReads<T, D> rv = make_xt_reads<T, D>(lane, w * RT::ELEMS, w * VE);
+    const RowCopy<T, D> ck(lane, a.ldk);
+    using VCopy = std::conditional_t<TR, RowCopy<T, D>, TrCopy<(TR ? 64 : D)>>;
+    const VCopy cv(lane, TR ? a.ldv : a.ldt);
 
-  typename E::Chunk qc[RT::STEPS];
-  load_row_frags<T, D>(q + (tok0 + min(qi, S - 1)) * a.ldq + (int64_t)h * D, kh, qc);
-  floatx16 o[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-  float m = -INFINITY, l = 0.f;
-  const int n = w <= qt ? (qt - w) / W + 1 : 0;  // key tiles w, w+W, .. <= qt
-
-  auto issue = [&](int t, T* sk, T* sv) __attribute__((always_inline)) {
-    const int kv0 = (w + W * t) * 32;
-    copy_row_tile<T, D>(sk + w * RT::ELEMS, k, a.ldk, tok0, kv0, S, grp * D, ck, lane);
-    if constexpr (TR) copy_row_tile<T, D>(sv + w * VE, v, a.ldv, tok0, kv0, S, grp * D, cv, lane);
-    else copy_tr_tile<D>(sv + w * VE, vT, a.ldt, tok0, kv0, S, grp * D, cv, lane);
-  };
-  auto compute = [&](const T* sk, const T* sv, int t) __attribute__((always_inline)) {
-    const int kv0 = (w + W * t) * 32;
-    floatx16 s;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = 0.f;
-#pragma unroll
-    for (int c = 0; c < RT::STEPS; ++c) s = E::mma(lds_at<typename E::Chunk>(sk, rk.v[c]), qc[c], s);
-    if (kv0 == q0) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kv0 + 8 * g + 4 * kh + r > qi) s[4 * g + r] = -INFINITY;
-    }
-    float mx = s[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-    mx = half_max(mx) * sc;
-    if (__any(mx > m + kRescaleSlack)) {
-      const float mn = fmaxf(m, mx);
-      const float alpha = exp2_hw(m - mn);
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-      m = mn;
-    }
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = exp2_hw(fmaf(s[e], sc, -m));
-      s[e] = p;
-      ps += p;
-    }
-    l += half_sum(ps);
-    acc_rows_product_any<T, D>(sv, rv, s, o);
-  };
-  wave_ring<NS>(
-      n, RT::NI + VNI, [&](int t, auto St) __attribute__((always_inline)) { issue(t, sK(St), sV(St)); },
-      [](int) {}, [&](int t, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), t); });
-
-  // Combine through the (now free) first stage buffer: every wave learns
-  // every wave's reference max, rescales its own sum and output to the
-  // common max, and wave 0 adds them in wave order, 16 values at a time.
-  static_assert((W - 1) * 16 * 64 * 4 <= W * RT::ELEMS * (int)sizeof(T), "combine space");
-  float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
-  __syncthreads();
-  x[w * 64 + lane] = m;
-  __syncthreads();
-  float M = x[lane];
-#pragma unroll
-  for (int ww = 1; ww < W; ++ww) M = fmaxf(M, x[ww * 64 + lane]);
-  const float f = m == -INFINITY ? 0.f : exp2f(m - M);
-  float L = l * f;
-  wave_sum_into0<W, 1>(x, w, lane, &L);
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[db][e] *= f;
-    wave_sum_into0<W, 16>(x, w, lane, (float*)&o[db]);
-  }
-  if (w != 0) return;
-  if (qi < S) {
-    const float inv = 1.0f / L;
-    const int64_t ooff = (tok0 + qi) * a.ldo + (int64_t)h * D + 4 * kh;
+    typename E::Chunk qc[RT::STEPS];
+    load_row_frags<T, D>(q + (tok0 + min(qi, S - 1)) * a.ldq + (int64_t)h * D, kh, qc);
+    floatx16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 vv =
-            make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        *(float4*)(a.o + ooff + db * 32 + 8 * g) = vv;
-        if (a.o16) *(half4*)(a.o16 + ooff + db * 32 + 8 * g) = to_half4(vv);
+      for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    const int n = w <= qt ? (qt - w) / W + 1 : 0;  // key tiles w, w+W, .. <= qt
+
+    auto issue = [&](int t, T* sk, T* sv) __attribute__((always_inline)) {
+      const int kv0 = (w + W * t) * 32;
+      copy_row_tile<T, D>(sk + w * RT::ELEMS, k, a.ldk, tok0, kv0, S, grp * D, ck, lane);
+      if constexpr (TR) copy_row_tile<T, D>(sv + w * VE, v, a.ldv, tok0, kv0, S, grp * D, cv, lane);
+      else copy_tr_tile<D>(sv + w * VE, vT, a.ldt, tok0, kv0, S, grp * D, cv, lane);
+    };
+    auto compute = [&](const T* sk, const T* sv, int t) __attribute__((always_inline)) {
+      const int kv0 = (w + W * t) * 32;
+      floatx16 s;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+      for (int c = 0; c < RT::STEPS; ++c) s = E::mma(lds_at<typename E::Chunk>(sk, rk.v[c]), qc[c], s);
+      if (kv0 == q0) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kv0 + 8 * g + 4 * kh + r > qi) s[4 * g + r] = -INFINITY;
       }
-    if (kh == 0) a.lse[((int64_t)b * a.heads + h) * S + qi] = (M + log2f(L)) * kLn2;
+      float mx = s[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+      mx = half_max(mx) * sc;
+      if (__any(mx > m + kRescaleSlack)) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = exp2_hw(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        m = mn;
+      }
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = exp2_hw(fmaf(s[e], sc, -m));
+        s[e] = p;
+        ps += p;
+      }
+      l += half_sum(ps);
+      acc_rows_product_any<T, D>(sv, rv, s, o);
+    };
+    wave_ring<NS>(
+        n, RT::NI + VNI, [&](int t, auto St) __attribute__((always_inline)) { issue(t, sK(St), sV(St)); },
+        [](int) {}, [&](int t, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), t); });
+
+    // Combine through the (now free) first stage buffer: every wave learns
+    // every wave's reference max, rescales its own sum and output to the
+    // common max, and wave 0 adds them in wave order, 16 values at a time.
+    static_assert((W - 1) * 16 * 64 * 4 <= W * RT::ELEMS * (int)sizeof(T), "combine space");
+    float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
+    __syncthreads();
+    x[w * 64 + lane] = m;
+    __syncthreads();
+    float M = x[lane];
+#pragma unroll
+    for (int ww = 1; ww < W; ++ww) M = fmaxf(M, x[ww * 64 + lane]);
+    const float f = m == -INFINITY ? 0.f : exp2f(m - M);
+    float L = l * f;
+    wave_sum_into0<W, 1>(x, w, lane, &L);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[db][e] *= f;
+      wave_sum_into0<W, 16>(x, w, lane, (float*)&o[db]);
+    }
+    if (w == 0) {
+      if (qi < S) {
+        const float inv = 1.0f / L;
+        const int64_t ooff = (tok0 + qi) * a.ldo + (int64_t)h * D + 4 * kh;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 vv =
+                make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+            *(float4*)(a.o + ooff + db * 32 + 8 * g) = vv;
+            if (a.o16) *(half4*)(a.o16 + ooff + db * 32 + 8 * g) = to_half4(vv);
+          }
+        if (kh == 0) a.lse[((int64_t)b * a.heads + h) * S + qi] = (M + log2f(L)) * kLn2;
+      }
+    }
   }
 }
 
-// dQ: grid (q tiles, heads, batch); the W waves take key tiles w, w+W, ...
+// dQ: grid (pairs of q tiles, heads, batch); the W waves take key tiles w, w+W, ...
 // (K, V and, in fp32, K^T through private LDS stages); wave 0 sums the
 // partial dQ in wave order and writes it. Only the diagonal tile is masked.
 template <typename T, int D>
@@ -1069,121 +1077,129 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
   const T* d_o = (const T*)a.d_o;
   const int G = a.heads / a.kv_heads, h = blockIdx.y, grp = h / G, b = blockIdx.z;
   const int S = a.seq;
-  const int qt = gridDim.x - 1 - blockIdx.x, q0 = qt * 32;
-  const int64_t tok0 = (int64_t)b * S;
-  const int i = lane & 31, kh = lane >> 5;
-  const float sc = kLog2e / sqrtf((float)D);
-  const int qi = q0 + i, qc_i = min(qi, S - 1);
+  // tiles t and ntl-1-t share a workgroup (pass 0 the later tile): every
+  // workgroup then has the same causal work, and half as many fit one wave
+  const int ntl = (S + 31) / 32, pr = blockIdx.x;
+  const int npass = 2 * pr + 1 == ntl ? 1 : 2;
+  for (int pass = 0; pass < npass; ++pass) {
+    if (pass) __syncthreads();  // the previous tile's combine is done with the stages
+    const int qt = pass == 0 ? ntl - 1 - pr : pr, q0 = qt * 32;
+    const int64_t tok0 = (int64_t)b * S;
+    const int i = lane & 31, kh = lane >> 5;
+    const float sc = kLog2e / sqrtf((float)D);
+    const int qi = q0 + i, qc_i = min(qi, S - 1);
 
-  const RowReads<T, D> rr(i, kh, w * RT::ELEMS);
-  const XtReads<T, D> rkt = make_xt_reads<T, D>(lane, w * RT::ELEMS, w * KTE);
-  const RowCopy<T, D> ck(lane, a.ldk), cv(lane, a.ldv);
+    const RowReads<T, D> rr(i, kh, w * RT::ELEMS);
+    const XtReads<T, D> rkt = make_xt_reads<T, D>(lane, w * RT::ELEMS, w * KTE);
+    const RowCopy<T, D> ck(lane, a.ldk), cv(lane, a.ldv);
 
-  typename E::Chunk qc[RT::STEPS], dc[RT::STEPS];
-  load_row_frags<T, D>(q + (tok0 + qc_i) * a.ldq + (int64_t)h * D, kh, qc);
-  load_row_frags<T, D>(d_o + (tok0 + qc_i) * a.lddo + (int64_t)h * D, kh, dc);
-  const int64_t rowi = ((int64_t)b * a.heads + h) * S + qc_i;
-  const float lse2 = a.lse[rowi] * kLog2e;
-  // delta = rowsum(dO o) of the tile's rows (fp32 operands): wave w sums
-  // columns w D/W .. (w+1) D/W - 1, the lane halves (kh) half of them each;
-  // the waves' parts are added in wave order through the first K stage
-  // before any copy lands there, and wave 0 stores delta for the dK/dV
-  // kernel.
-  float dl;
-  {
-    constexpr int CW = D / W / 2;  // columns per lane
-    const int64_t c0 = (int64_t)h * D + w * (D / W) + kh * CW;
-    const float* orow = a.o + (tok0 + qc_i) * a.ldo + c0;
-    const float* drow = a.do32 + (tok0 + qc_i) * a.lddo32 + c0;
-    float4 o4[CW / 4], d4[CW / 4];
+    typename E::Chunk qc[RT::STEPS], dc[RT::STEPS];
+    load_row_frags<T, D>(q + (tok0 + qc_i) * a.ldq + (int64_t)h * D, kh, qc);
+    load_row_frags<T, D>(d_o + (tok0 + qc_i) * a.lddo + (int64_t)h * D, kh, dc);
+    const int64_t rowi = ((int64_t)b * a.heads + h) * S + qc_i;
+    const float lse2 = a.lse[rowi] * kLog2e;
+    // delta = rowsum(dO o) of the tile's rows (fp32 operands): wave w sums
+    // columns w D/W .. (w+1) D/W - 1, the lane halves (kh) half of them each;
+    // the waves' parts are added in wave order through the first K stage
+    // before any copy lands there, and wave 0 stores delta for the dK/dV
+    // kernel.
+    float dl;
+    {
+      constexpr int CW = D / W / 2;  // columns per lane
+      const int64_t c0 = (int64_t)h * D + w * (D / W) + kh * CW;
+      const float* orow = a.o + (tok0 + qc_i) * a.ldo + c0;
+      const float* drow = a.do32 + (tok0 + qc_i) * a.lddo32 + c0;
+      float4 o4[CW / 4], d4[CW / 4];
 #pragma unroll
-    for (int j = 0; j < CW / 4; ++j) {
-      o4[j] = *(const float4*)(orow + 4 * j);
-      d4[j] = *(const float4*)(drow + 4 * j);
+      for (int j = 0; j < CW / 4; ++j) {
+        o4[j] = *(const float4*)(orow + 4 * j);
+        d4[j] = *(const float4*)(drow + 4 * j);
+      }
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < CW / 4; ++j)
+        part += o4[j].x * d4[j].x + o4[j].y * d4[j].y + o4[j].z * d4[j].z + o4[j].w * d4[j].w;
+      part += __shfl_xor(part, 32, kWave);
+      float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
+      x[w * 64 + lane] = part;
+      __syncthreads();
+      dl = x[lane];
+#pragma unroll
+      for (int ww = 1; ww < W; ++ww) dl += x[ww * 64 + lane];
+      __syncthreads();  // the stage is refilled from here on
+      if (w == 0 && kh == 0 && qi < S) delta[rowi] = dl;
     }
-    float part = 0.f;
-#pragma unroll
-    for (int j = 0; j < CW / 4; ++j)
-      part += o4[j].x * d4[j].x + o4[j].y * d4[j].y + o4[j].z * d4[j].z + o4[j].w * d4[j].w;
-    part += __shfl_xor(part, 32, kWave);
-    float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
-    x[w * 64 + lane] = part;
-    __syncthreads();
-    dl = x[lane];
-#pragma unroll
-    for (int ww = 1; ww < W; ++ww) dl += x[ww * 64 + lane];
-    __syncthreads();  // the stage is refilled from here on
-    if (w == 0 && kh == 0 && qi < S) delta[rowi] = dl;
-  }
-  floatx16 dq[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) dq[db][e] = 0.f;
-  const int n = w <= qt ? (qt - w) / W + 1 : 0;
-
-  auto issue = [&](int t, T* sk, T* sv, T* skt) __attribute__((always_inline)) {
-    const int kv0 = (w + W * t) * 32;
-    copy_row_tile<T, D>(sk + w * RT::ELEMS, k, a.ldk, tok0, kv0, S, grp * D, ck, lane);
-    copy_row_tile<T, D>(sv + w * RT::ELEMS, v, a.ldv, tok0, kv0, S, grp * D, cv, lane);
-    if constexpr (!TR) {
-      const TrCopy<D> ckt(lane, a.ldt);
-      copy_tr_tile<D>(skt + w * KTE, kT, a.ldt, tok0, kv0, S, grp * D, ckt, lane);
-    }
-  };
-  auto compute = [&](const T* sk, const T* sv, const T* skt, int t) __attribute__((always_inline)) {
-    const int kv0 = (w + W * t) * 32;
-    floatx16 s, dp;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      s[e] = 0.f;
-      dp[e] = 0.f;
-    }
-#pragma unroll
-    for (int c = 0; c < RT::STEPS; ++c) {
-      s = E::mma(lds_at<typename E::Chunk>(sk, rr.v[c]), qc[c], s);
-      dp = E::mma(lds_at<typename E::Chunk>(sv, rr.v[c]), dc[c], dp);
-    }
-    if (kv0 == q0) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * g + r;
-          const int kj = kv0 + 8 * g + 4 * kh + r;
-          const float p = (kj > qi || kj >= S) ? 0.f : exp2_hw(fmaf(s[e], sc, -lse2));
-          s[e] = p * (dp[e] - dl);  // dS^T, unscaled
-        }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = exp2_hw(fmaf(s[e], sc, -lse2)) * (dp[e] - dl);
-    }
-    if constexpr (TR) acc_rows_product_any<T, D>(sk, rkt, s, dq);
-    else acc_rows_product_any<T, D>(skt, rkt, s, dq);
-  };
-  wave_ring<NS>(
-      n, 2 * RT::NI + (TR ? 0 : TT::NI),
-      [&](int t, auto St) __attribute__((always_inline)) { issue(t, sK(St), sV(St), sKt(St)); }, [](int) {},
-      [&](int t, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), sKt(St), t); });
-
-  static_assert((W - 1) * 16 * 64 * 4 <= W * RT::ELEMS * (int)sizeof(T), "combine space");
-  float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) wave_sum_into0<W, 16>(x, w, lane, (float*)&dq[db]);
-  if (w != 0) return;
-  if (qi < S) {
-    const float inv = 1.0f / sqrtf((float)D);
-    float* row = a.dq + (tok0 + qi) * a.lddq + (int64_t)h * D + 4 * kh;
+    floatx16 dq[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(float4*)(row + db * 32 + 8 * g) = make_float4(dq[db][4 * g] * inv, dq[db][4 * g + 1] * inv,
-                                                        dq[db][4 * g + 2] * inv, dq[db][4 * g + 3] * inv);
+      for (int e = 0; e < 16; ++e) dq[db][e] = 0.f;
+    const int n = w <= qt ? (qt - w) / W + 1 : 0;
+
+    auto issue = [&](int t, T* sk, T* sv, T* skt) __attribute__((always_inline)) {
+      const int kv0 = (w + W * t) * 32;
+      copy_row_tile<T, D>(sk + w * RT::ELEMS, k, a.ldk, tok0, kv0, S, grp * D, ck, lane);
+      copy_row_tile<T, D>(sv + w * RT::ELEMS, v, a.ldv, tok0, kv0, S, grp * D, cv, lane);
+      if constexpr (!TR) {
+        const TrCopy<D> ckt(lane, a.ldt);
+        copy_tr_tile<D>(skt + w * KTE, kT, a.ldt, tok0, kv0, S, grp * D, ckt, lane);
+      }
+    };
+    auto compute = [&](const T* sk, const T* sv, const T* skt, int t) __attribute__((always_inline)) {
+      const int kv0 = (w + W * t) * 32;
+      floatx16 s, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s[e] = 0.f;
+        dp[e] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < RT::STEPS; ++c) {
+        s = E::mma(lds_at<typename E::Chunk>(sk, rr.v[c]), qc[c], s);
+        dp = E::mma(lds_at<typename E::Chunk>(sv, rr.v[c]), dc[c], dp);
+      }
+      if (kv0 == q0) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * g + r;
+            const int kj = kv0 + 8 * g + 4 * kh + r;
+            const float p = (kj > qi || kj >= S) ? 0.f : exp2_hw(fmaf(s[e], sc, -lse2));
+            s[e] = p * (dp[e] - dl);  // dS^T, unscaled
+          }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = exp2_hw(fmaf(s[e], sc, -lse2)) * (dp[e] - dl);
+      }
+      if constexpr (TR) acc_rows_product_any<T, D>(sk, rkt, s, dq);
+      else acc_rows_product_any<T, D>(skt, rkt, s, dq);
+    };
+    wave_ring<NS>(
+        n, 2 * RT::NI + (TR ? 0 : TT::NI),
+        [&](int t, auto St) __attribute__((always_inline)) { issue(t, sK(St), sV(St), sKt(St)); }, [](int) {},
+        [&](int t, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), sKt(St), t); });
+
+    static_assert((W - 1) * 16 * 64 * 4 <= W * RT::ELEMS * (int)sizeof(T), "combine space");
+    float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) wave_sum_into0<W, 16>(x, w, lane, (float*)&dq[db]);
+    if (w == 0) {
+      if (qi < S) {
+        const float inv = 1.0f / sqrtf((float)D);
+        float* row = a.dq + (tok0 + qi) * a.lddq + (int64_t)h * D + 4 * kh;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *(float4*)(row + db * 32 + 8 * g) = make_float4(dq[db][4 * g] * inv, dq[db][4 * g + 1] * inv,
+                                                            dq[db][4 * g + 2] * inv, dq[db][4 * g + 3] * inv);
+      }
+    }
   }
 }
 
-// dK, dV per query head: grid (kv tiles, heads, batch); the W waves take
+// dK, dV per query head: grid (pairs of kv tiles, heads, batch); the W waves take
 // query tiles kt+w, kt+w+W, ... (Q, dO and, in fp32, their transposes
 // through private LDS stages); wave 0 sums the partials in wave order into
 // per-head buffers [T, heads, D], summed over each group afterwards. Masks
@@ -1214,141 +1230,150 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
   const int h = blockIdx.y, b = blockIdx.z;
   const int G = a.heads / a.kv_heads, grp = h / G;
   const int S = a.seq;
-  const int kt = gridDim.x - 1 - blockIdx.x, kv0 = kt * 32;
-  const int64_t tok0 = (int64_t)b * S;
-  const int i = lane & 31, kh = lane >> 5;
-  const float sc = kLog2e / sqrtf((float)D);
-  const int kj = kv0 + i;  // this lane's key (column of every accumulator)
+  // tiles t and ntl-1-t share a workgroup (pass 0 the later tile): every
+  // workgroup then has the same causal work, and half as many fit one wave
+  const int ntl = (S + 31) / 32, pr = blockIdx.x;
+  const int npass = 2 * pr + 1 == ntl ? 1 : 2;
+  for (int pass = 0; pass < npass; ++pass) {
+    if (pass) __syncthreads();  // the previous tile's combine is done with the stages
+    const int kt = pass == 0 ? ntl - 1 - pr : pr, kv0 = kt * 32;
+    const int64_t tok0 = (int64_t)b * S;
+    const int i = lane & 31, kh = lane >> 5;
+    const float sc = kLog2e / sqrtf((float)D);
+    const int kj = kv0 + i;  // this lane's key (column of every accumulator)
 
-  const RowReads<T, D> rr(i, kh, w * RT::ELEMS);
-  const XtReads<T, D> rxt = make_xt_reads<T, D>(lane, w * RT::ELEMS, w * XTE);
-  const RowCopy<T, D> cq(lane, a.ldq), co(lane, a.lddo);
+    const RowReads<T, D> rr(i, kh, w * RT::ELEMS);
+    const XtReads<T, D> rxt = make_xt_reads<T, D>(lane, w * RT::ELEMS, w * XTE);
+    const RowCopy<T, D> cq(lane, a.ldq), co(lane, a.lddo);
 
-  typename E::Chunk kc[RT::STEPS], vc[RT::STEPS];
-  {
-    const int kr = min(kj, S - 1);
-    load_row_frags<T, D>(k + (tok0 + kr) * a.ldk + (int64_t)grp * D, kh, kc);
-    load_row_frags<T, D>(v + (tok0 + kr) * a.ldv + (int64_t)grp * D, kh, vc);
-  }
-  floatx16 dk[D / 32], dv[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      dk[db][e] = 0.f;
-      dv[db][e] = 0.f;
+    typename E::Chunk kc[RT::STEPS], vc[RT::STEPS];
+    {
+      const int kr = min(kj, S - 1);
+      load_row_frags<T, D>(k + (tok0 + kr) * a.ldk + (int64_t)grp * D, kh, kc);
+      load_row_frags<T, D>(v + (tok0 + kr) * a.ldv + (int64_t)grp * D, kh, vc);
     }
-  const int nqt = (S + 31) / 32;
-  const float* lse_h = a.lse + ((int64_t)b * a.heads + h) * S;
-  const float* dl_h = delta + ((int64_t)b * a.heads + h) * S;
-  const int n = kt + w < nqt ? (nqt - 1 - kt - w) / W + 1 : 0;  // query tiles kt+w, kt+w+W, ..
-  auto qtile = [&](int t) { return kt + w + W * t; };
-
-  auto issue = [&](int t, T* sq, T* so, T* sqt, T* sot) __attribute__((always_inline)) {
-    const int q0 = qtile(t) * 32;
-    copy_row_tile<T, D>(sq + w * RT::ELEMS, q, a.ldq, tok0, q0, S, h * D, cq, lane);
-    copy_row_tile<T, D>(so + w * RT::ELEMS, d_o, a.lddo, tok0, q0, S, h * D, co, lane);
-    if constexpr (!TR) {
-      const TrCopy<D> ct(lane, a.ldt);
-      copy_tr_tile<D>(sqt + w * XTE, qT, a.ldt, tok0, q0, S, h * D, ct, lane);
-      copy_tr_tile<D>(sot + w * XTE, doT, a.ldt, tok0, q0, S, h * D, ct, lane);
-    }
-  };
-  // log-sum-exp (in powers of two) and delta of this lane's 16 query rows
-  // q0 + 8g + 4kh + r of the next query tile, loaded one step ahead and
-  // before that step's tile copies are issued, so waiting for them never
-  // waits for the copies.
-  float4 lq[4], dq4[4], lq_n[4], dq4_n[4];
-  auto load_ld = [&](int t, float4 (&L)[4], float4 (&Dl)[4]) __attribute__((always_inline)) {
-    const int q0 = qtile(t) * 32;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int qr = q0 + 8 * g + 4 * kh;
-      L[g] = qr < S ? *(const float4*)(lse_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
-      Dl[g] = qr < S ? *(const float4*)(dl_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  auto compute = [&](const T* sq, const T* so, const T* sqt, const T* sot, int t) __attribute__((always_inline)) {
-    const int q0 = qtile(t) * 32;
-    floatx16 s, dp;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      s[e] = 0.f;
-      dp[e] = 0.f;
-    }
-#pragma unroll
-    for (int c = 0; c < RT::STEPS; ++c) {
-      s = E::mma(lds_at<typename E::Chunk>(sq, rr.v[c]), kc[c], s);
-      dp = E::mma(lds_at<typename E::Chunk>(so, rr.v[c]), vc[c], dp);
-    }
-    auto sm = [&](auto Masked) __attribute__((always_inline)) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * g + r;
-          const float L = r == 0 ? lq[g].x : r == 1 ? lq[g].y : r == 2 ? lq[g].z : lq[g].w;
-          const float Dl = r == 0 ? dq4[g].x : r == 1 ? dq4[g].y : r == 2 ? dq4[g].z : dq4[g].w;
-          float p = exp2_hw(fmaf(s[e], sc, -L * kLog2e));
-          if constexpr (decltype(Masked)::value) {
-            const int qq = q0 + 8 * g + 4 * kh + r;
-            if (kj > qq || qq >= S || kj >= S) p = 0.f;
-          }
-          s[e] = p;
-          dp[e] = p * (dp[e] - Dl);
-        }
-    };
-    if (q0 == kv0 || q0 + 32 > S) sm(std::true_type{});
-    else sm(std::false_type{});
-    if constexpr (TR) {
-      acc_rows_product_any<T, D>(so, rxt, s, dv);   // dV^T += dO^T P
-      acc_rows_product_any<T, D>(sq, rxt, dp, dk);  // dK^T += Q^T dS
-    } else {
-      acc_rows_product_any<T, D>(sot, rxt, s, dv);
-      acc_rows_product_any<T, D>(sqt, rxt, dp, dk);
-    }
-  };
-  if (n > 0) load_ld(0, lq_n, dq4_n);
-  wave_ring<NS>(
-      n, 2 * RT::NI + (TR ? 0 : 2 * TT::NI),
-      [&](int t, auto St) __attribute__((always_inline)) { issue(t, sQ(St), sO(St), sQt(St), sOt(St)); },
-      [&](int t) __attribute__((always_inline)) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          lq[g] = lq_n[g];
-          dq4[g] = dq4_n[g];
-        }
-        if (t + 1 < n) load_ld(t + 1, lq_n, dq4_n);
-      },
-      [&](int t, auto St) __attribute__((always_inline)) { compute(sQ(St), sO(St), sQt(St), sOt(St), t); });
-
-  static_assert((W - 1) * 16 * 64 * 4 <= W * RT::ELEMS * (int)sizeof(T), "combine space");
-  float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    wave_sum_into0<W, 16>(x, w, lane, (float*)&dk[db]);
-    wave_sum_into0<W, 16>(x, w, lane, (float*)&dv[db]);
-  }
-  if (w != 0) return;
-  if (kj < S) {
-    const float inv = 1.0f / sqrtf((float)D);
-    float* krow = dk_part + ((tok0 + kj) * a.heads + h) * (int64_t)D + 4 * kh;
-    float* vrow = dv_part + ((tok0 + kj) * a.heads + h) * (int64_t)D + 4 * kh;
+    floatx16 dk[D / 32], dv[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        *(float4*)(krow + db * 32 + 8 * g) = make_float4(dk[db][4 * g] * inv, dk[db][4 * g + 1] * inv,
-                                                         dk[db][4 * g + 2] * inv, dk[db][4 * g + 3] * inv);
-        *(float4*)(vrow + db * 32 + 8 * g) =
-            make_float4(dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
+      for (int e = 0; e < 16; ++e) {
+        dk[db][e] = 0.f;
+        dv[db][e] = 0.f;
       }
+    const int nqt = (S + 31) / 32;
+    const float* lse_h = a.lse + ((int64_t)b * a.heads + h) * S;
+    const float* dl_h = delta + ((int64_t)b * a.heads + h) * S;
+    const int n = kt + w < nqt ? (nqt - 1 - kt - w) / W + 1 : 0;  // query tiles kt+w, kt+w+W, ..
+    auto qtile = [&](int t) { return kt + w + W * t; };
+
+    auto issue = [&](int t, T* sq, T* so, T* sqt, T* sot) __attribute__((always_inline)) {
+      const int q0 = qtile(t) * 32;
+      copy_row_tile<T, D>(sq + w * RT::ELEMS, q, a.ldq, tok0, q0, S, h * D, cq, lane);
+      copy_row_tile<T, D>(so + w * RT::ELEMS, d_o, a.lddo, tok0, q0, S, h * D, co, lane);
+      if constexpr (!TR) {
+        const TrCopy<D> ct(lane, a.ldt);
+        copy_tr_tile<D>(sqt + w * XTE, qT, a.ldt, tok0, q0, S, h * D, ct, lane);
+        copy_tr_tile<D>(sot + w * XTE, doT, a.ldt, tok0, q0, S, h * D, ct, lane);
+      }
+    };
+    // log-sum-exp (in powers of two) and delta of this lane's 16 query rows
+    // q0 + 8g + 4kh + r of the next query tile, loaded one step ahead and
+    // before that step's tile copies are issued, so waiting for them never
+    // waits for the copies.
+    float4 lq[4], dq4[4], lq_n[4], dq4_n[4];
+    auto load_ld = [&](int t, float4 (&L)[4], float4 (&Dl)[4]) __attribute__((always_inline)) {
+      const int q0 = qtile(t) * 32;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qr = q0 + 8 * g + 4 * kh;
+        L[g] = qr < S ? *(const float4*)(lse_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
+        Dl[g] = qr < S ? *(const float4*)(dl_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    auto compute = [&](const T* sq, const T* so, const T* sqt, const T* sot, int t) __attribute__((always_inline)) {
+      const int q0 = qtile(t) * 32;
+      floatx16 s, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s[e] = 0.f;
+        dp[e] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < RT::STEPS; ++c) {
+        s = E::mma(lds_at<typename E::Chunk>(sq, rr.v[c]), kc[c], s);
+        dp = E::mma(lds_at<typename E::Chunk>(so, rr.v[c]), vc[c], dp);
+      }
+      auto sm = [&](auto Masked) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * g + r;
+            const float L = r == 0 ? lq[g].x : r == 1 ? lq[g].y : r == 2 ? lq[g].z : lq[g].w;
+            const float Dl = r == 0 ? dq4[g].x : r == 1 ? dq4[g].y : r == 2 ? dq4[g].z : dq4[g].w;
+            float p = exp2_hw(fmaf(s[e], sc, -L * kLog2e));
+            if constexpr (decltype(Masked)::value) {
+              const int qq = q0 + 8 * g + 4 * kh + r;
+              if (kj > qq || qq >= S || kj >= S) p = 0.f;
+            }
+            s[e] = p;
+            dp[e] = p * (dp[e] - Dl);
+          }
+      };
+      if (q0 == kv0 || q0 + 32 > S) sm(std::true_type{});
+      else sm(std::false_type{});
+      if constexpr (TR) {
+        acc_rows_product_any<T, D>(so, rxt, s, dv);   // dV^T += dO^T P
+        acc_rows_product_any<T, D>(sq, rxt, dp, dk);  // dK^T += Q^T dS
+      } else {
+        acc_rows_product_any<T, D>(sot, rxt, s, dv);
+        acc_rows_product_any<T, D>(sqt, rxt, dp, dk);
+      }
+    };
+    if (n > 0) load_ld(0, lq_n, dq4_n);
+    wave_ring<NS>(
+        n, 2 * RT::NI + (TR ? 0 : 2 * TT::NI),
+        [&](int t, auto St) __attribute__((always_inline)) { issue(t, sQ(St), sO(St), sQt(St), sOt(St)); },
+        [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            lq[g] = lq_n[g];
+            dq4[g] = dq4_n[g];
+          }
+          if (t + 1 < n) load_ld(t + 1, lq_n, dq4_n);
+        },
+        [&](int t, auto St) __attribute__((always_inline)) { compute(sQ(St), sO(St), sQt(St), sOt(St), t); });
+
+    static_assert((W - 1) * 16 * 64 * 4 <= W * RT::ELEMS * (int)sizeof(T), "combine space");
+    float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      wave_sum_into0<W, 16>(x, w, lane, (float*)&dk[db]);
+      wave_sum_into0<W, 16>(x, w, lane, (float*)&dv[db]);
+    }
+    if (w == 0) {
+      if (kj < S) {
+        const float inv = 1.0f / sqrtf((float)D);
+        float* krow = dk_part + ((tok0 + kj) * a.heads + h) * (int64_t)D + 4 * kh;
+        float* vrow = dv_part + ((tok0 + kj) * a.heads + h) * (int64_t)D + 4 * kh;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            *(float4*)(krow + db * 32 + 8 * g) = make_float4(dk[db][4 * g] * inv, dk[db][4 * g + 1] * inv,
+                                                             dk[db][4 * g + 2] * inv, dk[db][4 * g + 3] * inv);
+            *(float4*)(vrow + db * 32 + 8 * g) =
+                make_float4(dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
+          }
+      }
+    }
   }
 }
 
 template <typename T, int D>
 int fwd_dma_launch(const AttnDmaArgs& a, hipStream_t st) {
-  dim3 grid((unsigned)ceil_div(a.seq, 32), (unsigned)a.heads, (unsigned)a.batch);
+  // tiles are processed in pairs (one workgroup per pair)
+  dim3 grid((unsigned)ceil_div(ceil_div(a.seq, 32), 2), (unsigned)a.heads, (unsigned)a.batch);
   hipLaunchKernelGGL((attn_dma_fwd_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::FWD_W), 0, st, a);
   return check_launch("attn_dma_fwd_kernel");
 }
@@ -1356,7 +1381,8 @@ int fwd_dma_launch(const AttnDmaArgs& a, hipStream_t st) {
 template <typename T, int D>
 int bwd_dma_launch(const AttnDmaArgs& a, float* delta, float* dk_part, float* dv_part, hipStream_t st) {
   const int64_t T_ = (int64_t)a.batch * a.seq;
-  dim3 grid((unsigned)ceil_div(a.seq, 32), (unsigned)a.heads, (unsigned)a.batch);
+  // tiles are processed in pairs (one workgroup per pair)
+  dim3 grid((unsigned)ceil_div(ceil_div(a.seq, 32), 2), (unsigned)a.heads, (unsigned)a.batch);
   hipLaunchKernelGGL((attn_dma_dq_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DQ_W), 0, st, a, delta);
   QBLK_TRY(check_launch("attn_dma_dq_kernel"));
   hipLaunchKernelGGL((attn_dma_dkv_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DKV_W), 0, st, a,
