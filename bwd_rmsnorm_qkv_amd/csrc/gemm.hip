@@ -816,6 +816,15 @@ __device__ __forceinline__ f16* lds_stage() {
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 
+// f(integral_constant<int, I>) for I in [B, E), unrolled at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // One operand of the DMA kernel: R rows of the tile (BM or BN), K-major or
 // MN-major, BK = 64 or 32 K per stage, copied by NW waves.
 template <int R, bool KMAJ, int NW, int BK_ = 64>
@@ -858,12 +867,14 @@ struct DmaOperand {
       }
     }
   }
+  // Copy j of this wave's share of K tile kt (j a compile-time index).
+  __device__ __forceinline__ void issue_one(int kt, f16* tile, int64_t ld, int w, int j) const {
+    const int64_t adv = KMAJ ? (int64_t)kt * BK : (int64_t)kt * BK * ld;
+    dma16_asm(p[j] + adv, tile + 512 * (NW * j + w));
+  }
   __device__ __forceinline__ void issue(int kt, f16* tile, int64_t ld, int w) const {
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int64_t adv = KMAJ ? (int64_t)kt * BK : (int64_t)kt * BK * ld;
-      dma16_asm(p[j] + adv, tile + 512 * (NW * j + w));
-    }
+    for (int j = 0; j < J; ++j) issue_one(kt, tile, ld, w, j);
   }
   // Per-lane element offset of the K-major fragment of K step s within a
   // 32-row block (the swizzle of row rb + i equals that of i, rb being a
@@ -908,7 +919,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   using OB = DmaOperand<BN, BK_, NW>;
   constexpr int JS = OA::J + OB::J;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index as a scalar: the copies' LDS addresses (M0) then need
+  // no per-copy move from a vector register
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w % WM, wn = w / WM;
 
   const int total = gd.tiles_m * gd.tiles_n * gd.splits;
@@ -1145,7 +1158,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
   using OB = DmaOperand<BN, BK_, NW>;
   constexpr int JS = OA::J + OB::J;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index as a scalar: the copies' LDS addresses (M0) then need
+  // no per-copy move from a vector register
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w % WM, wn = w / WM;
 
   const int total = gd.tiles_m * gd.tiles_n * gd.splits;
@@ -1197,6 +1212,44 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
         for (int tn = 0; tn < TN; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[ks][tm], bv[ks][tn], acc[tm][tn], 0, 0, 0);
     __builtin_amdgcn_s_setprio(0);
+  };
+  // The wave's copies of one refill (A of tile ka into sa if ca, B of tile
+  // kb into sb if cb), spread over the slots of an instruction stream of NS
+  // steps: copy c goes after step floor(c NS / NC). Interleaved, a copy's
+  // issue overlaps the MFMA (or LDS read) before it instead of delaying
+  // the whole phase.
+  constexpr int NC = OA::J + OB::J;
+  auto copies_after = [&](auto Step, auto Steps, bool ca, int ka, f16* sa, bool cb, int kb2, f16* sb)
+      __attribute__((always_inline)) {
+    constexpr int i = decltype(Step)::value, ns = decltype(Steps)::value;
+    static_for<(i * NC) / ns, ((i + 1) * NC) / ns>([&](auto C) __attribute__((always_inline)) {
+      constexpr int c = decltype(C)::value;
+      if constexpr (c < OA::J) {
+        if (ca) oa.issue_one(ka, sa, d.lda, w, c);
+      } else {
+        if (cb) ob.issue_one(kb2, sb, d.ldb, w, c - OA::J);
+      }
+    });
+  };
+  auto mfma_copy = [&](bool ca, int ka, f16* sa, bool cb, int kb2, f16* sb) __attribute__((always_inline)) {
+    constexpr int NM = 2 * TM * TN;
+    __builtin_amdgcn_s_setprio(1);
+    static_for<0, NM>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value, ks = i / (TM * TN), tm = (i / TN) % TM, tn = i % TN;
+      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[ks][tm], bv[ks][tn], acc[tm][tn], 0, 0, 0);
+      copies_after(I, std::integral_constant<int, NM>{}, ca, ka, sa, cb, kb2, sb);
+    });
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto read_copy = [&](const f16* ra, const f16* rb, auto H, bool ca, int ka, f16* sa, bool cb, int kb2, f16* sb)
+      __attribute__((always_inline)) {
+    constexpr int h = decltype(H)::value, NR = 2 * (TM + TN);
+    static_for<0, NR>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value, ks = i / (TM + TN), t = i % (TM + TN);
+      if constexpr (t < TM) av[ks][t] = OA::frag(ra, wm * TM * 32 + t * 32, 2 * h + ks, lane, ko[2 * h + ks]);
+      else bv[ks][t - TM] = OB::frag(rb, wn * TN * 32 + (t - TM) * 32, 2 * h + ks, lane, ko[2 * h + ks]);
+      copies_after(I, std::integral_constant<int, NR>{}, ca, ka, sa, cb, kb2, sb);
+    });
   };
   auto phase_end = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
@@ -1250,13 +1303,17 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
       phase_end();
       // the stages of tile kt are free now (their last reads returned
       // before the barrier): refill A with tile kt+2 and B with tile
-      // kt+NB, ahead of their first reads
-      if (kt + 2 < nkt) oa.issue(kt + 2, stA(S), d.lda, w);
-      if (kt + NB < nkt) ob.issue(kt + NB, sb, d.ldb, w);
+      // kt+NB, ahead of their first reads, the copies interleaved with the
+      // phase's LDS reads (leading half) or MFMAs (trailing half)
+      const bool ca = kt + 2 < nkt, cb = kt + NB < nkt;
       if constexpr (lead) {
-        if (kt + 1 < nkt) read(stA(SN{}), stB(bn1), I0{});
+        if (kt + 1 < nkt) read_copy(stA(SN{}), stB(bn1), I0{}, ca, kt + 2, stA(S), cb, kt + NB, sb);
+        else {
+          if (ca) oa.issue(kt + 2, stA(S), d.lda, w);
+          if (cb) ob.issue(kt + NB, sb, d.ldb, w);
+        }
       } else {
-        mfma();
+        mfma_copy(ca, kt + 2, stA(S), cb, kt + NB, sb);
       }
       phase_end();
       bs = bn1;
