@@ -1213,44 +1213,47 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[ks][tm], bv[ks][tn], acc[tm][tn], 0, 0, 0);
     __builtin_amdgcn_s_setprio(0);
   };
-  // The wave's copies of one refill (A of tile ka into sa if ca, B of tile
-  // kb into sb if cb), spread over the slots of an instruction stream of NS
-  // steps: copy c goes after step floor(c NS / NC). Interleaved, a copy's
-  // issue overlaps the MFMA (or LDS read) before it instead of delaying
-  // the whole phase.
-  constexpr int NC = OA::J + OB::J;
-  auto copies_after = [&](auto Step, auto Steps, bool ca, int ka, f16* sa, bool cb, int kb2, f16* sb)
+  // The wave's copies of a refill (Mode bit 0: A of tile ka into sa if ca;
+  // bit 1: B of tile kb2 into sb if cb), spread over the slots of an
+  // instruction stream of ns steps: copy c goes after step floor(c ns / NC).
+  // Interleaved, a copy's issue overlaps the MFMA (or LDS read) before it
+  // instead of delaying the whole phase.
+  auto copies_after = [&](auto Step, auto Steps, auto Mode, bool ca, int ka, f16* sa, bool cb, int kb2, f16* sb)
       __attribute__((always_inline)) {
-    constexpr int i = decltype(Step)::value, ns = decltype(Steps)::value;
+    constexpr int i = decltype(Step)::value, ns = decltype(Steps)::value, mode = decltype(Mode)::value;
+    constexpr int JA = (mode & 1) ? OA::J : 0, NC = JA + ((mode & 2) ? OB::J : 0);
     static_for<(i * NC) / ns, ((i + 1) * NC) / ns>([&](auto C) __attribute__((always_inline)) {
       constexpr int c = decltype(C)::value;
-      if constexpr (c < OA::J) {
+      if constexpr (c < JA) {
         if (ca) oa.issue_one(ka, sa, d.lda, w, c);
       } else {
-        if (cb) ob.issue_one(kb2, sb, d.ldb, w, c - OA::J);
+        if (cb) ob.issue_one(kb2, sb, d.ldb, w, c - JA);
       }
     });
   };
-  auto mfma_copy = [&](bool ca, int ka, f16* sa, bool cb, int kb2, f16* sb) __attribute__((always_inline)) {
+  auto mfma_copy = [&](auto Mode, bool ca, int ka, f16* sa, bool cb, int kb2, f16* sb) __attribute__((always_inline)) {
     constexpr int NM = 2 * TM * TN;
     __builtin_amdgcn_s_setprio(1);
     static_for<0, NM>([&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value, ks = i / (TM * TN), tm = (i / TN) % TM, tn = i % TN;
       acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[ks][tm], bv[ks][tn], acc[tm][tn], 0, 0, 0);
-      copies_after(I, std::integral_constant<int, NM>{}, ca, ka, sa, cb, kb2, sb);
+      copies_after(I, std::integral_constant<int, NM>{}, Mode, ca, ka, sa, cb, kb2, sb);
     });
     __builtin_amdgcn_s_setprio(0);
   };
-  auto read_copy = [&](const f16* ra, const f16* rb, auto H, bool ca, int ka, f16* sa, bool cb, int kb2, f16* sb)
-      __attribute__((always_inline)) {
+  auto read_copy = [&](const f16* ra, const f16* rb, auto H, auto Mode, bool ca, int ka, f16* sa, bool cb, int kb2,
+                       f16* sb) __attribute__((always_inline)) {
     constexpr int h = decltype(H)::value, NR = 2 * (TM + TN);
     static_for<0, NR>([&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value, ks = i / (TM + TN), t = i % (TM + TN);
       if constexpr (t < TM) av[ks][t] = OA::frag(ra, wm * TM * 32 + t * 32, 2 * h + ks, lane, ko[2 * h + ks]);
       else bv[ks][t - TM] = OB::frag(rb, wn * TN * 32 + (t - TM) * 32, 2 * h + ks, lane, ko[2 * h + ks]);
-      copies_after(I, std::integral_constant<int, NR>{}, ca, ka, sa, cb, kb2, sb);
+      copies_after(I, std::integral_constant<int, NR>{}, Mode, ca, ka, sa, cb, kb2, sb);
     });
   };
+  using MA = std::integral_constant<int, 1>;
+  using MB = std::integral_constant<int, 2>;
+  using MAB = std::integral_constant<int, 3>;
   auto phase_end = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
@@ -1288,11 +1291,17 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
       using SN = std::integral_constant<int, 1 - decltype(S)::value>;
       const int bn1 = bs + 1 == NB ? 0 : bs + 1;
       f16* const sb = stB(bs);
+      // with two B stages the A copies of tile kt+1 (into the stage of tile
+      // kt-1) go in each half's operand phase of this tile, apart from the
+      // fourth phase's B copies
+      const bool ca1 = NB == 2 && kt >= 1 && kt + 1 < nkt;
       if constexpr (lead) mfma();
+      else if constexpr (NB == 2) read_copy(stA(S), sb, I0{}, MA{}, ca1, kt + 1, stA(SN{}), false, 0, nullptr);
       else read(stA(S), sb, I0{});
       phase_end();
-      if constexpr (lead) read(stA(S), sb, I1{});
-      else mfma();
+      if constexpr (!lead) mfma();
+      else if constexpr (NB == 2) read_copy(stA(S), sb, I1{}, MA{}, ca1, kt + 1, stA(SN{}), false, 0, nullptr);
+      else read(stA(S), sb, I1{});
       phase_end();
       if constexpr (lead) mfma();
       else read(stA(S), sb, I1{});
@@ -1302,18 +1311,20 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
       else wait_vmcnt<0>();
       phase_end();
       // the stages of tile kt are free now (their last reads returned
-      // before the barrier): refill A with tile kt+2 and B with tile
-      // kt+NB, ahead of their first reads, the copies interleaved with the
-      // phase's LDS reads (leading half) or MFMAs (trailing half)
-      const bool ca = kt + 2 < nkt, cb = kt + NB < nkt;
+      // before the barrier): refill B with tile kt+NB and, with three B
+      // stages, A with tile kt+2 (with two, A follows in the next tile's
+      // operand phases), ahead of their first reads, the copies interleaved
+      // with the phase's LDS reads (leading half) or MFMAs (trailing half)
+      const bool ca = NB != 2 && kt + 2 < nkt, cb = kt + NB < nkt;
+      using M4 = std::conditional_t<NB == 2, MB, MAB>;
       if constexpr (lead) {
-        if (kt + 1 < nkt) read_copy(stA(SN{}), stB(bn1), I0{}, ca, kt + 2, stA(S), cb, kt + NB, sb);
+        if (kt + 1 < nkt) read_copy(stA(SN{}), stB(bn1), I0{}, M4{}, ca, kt + 2, stA(S), cb, kt + NB, sb);
         else {
           if (ca) oa.issue(kt + 2, stA(S), d.lda, w);
           if (cb) ob.issue(kt + NB, sb, d.ldb, w);
         }
       } else {
-        mfma_copy(ca, kt + 2, stA(S), cb, kt + NB, sb);
+        mfma_copy(M4{}, ca, kt + 2, stA(S), cb, kt + NB, sb);
       }
       phase_end();
       bs = bn1;
