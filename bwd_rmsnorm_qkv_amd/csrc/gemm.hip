@@ -957,7 +957,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   // apart, so every MFMA's operands were requested a whole phase earlier
   // (left to itself the scheduler pairs each read with the MFMA that
   // consumes it and waits on the LDS latency every time).
-  auto compute = [&](const f16* sa, const f16* sb) __attribute__((always_inline)) {
+  // The refill copies of this tile (A of tile ka into da if ca, B of tile
+  // kb2 into db if cb) are interleaved with the MFMAs: copy c goes after
+  // MFMA floor(c NM / NC), so its issue overlaps the MFMA before it instead
+  // of holding up the whole tile.
+  auto compute = [&](const f16* sa, const f16* sb, bool ca, int ka, f16* da, bool cb, int kb2, f16* db)
+      __attribute__((always_inline)) {
     half8 av[2][TM], bv[2][TN];
     auto frag = [&](int s, half8* a, half8* b) __attribute__((always_inline)) {
 #pragma unroll
@@ -965,18 +970,26 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
 #pragma unroll
       for (int t = 0; t < TN; ++t) b[t] = OB::frag(sb, wn * TN * 32 + t * 32, s, lane, ko[s]);
     };
+    constexpr int NM = (BK / 16) * TM * TN, NC = OA::J + OB::J;
     frag(0, av[0], bv[0]);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      if (s + 1 < BK / 16) frag(s + 1, av[(s + 1) & 1], bv[(s + 1) & 1]);
+    static_for<0, BK / 16>([&](auto Sx) __attribute__((always_inline)) {
+      constexpr int s = decltype(Sx)::value;
+      if constexpr (s + 1 < BK / 16) frag(s + 1, av[(s + 1) & 1], bv[(s + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[s & 1][tm], bv[s & 1][tn], acc[tm][tn], 0, 0, 0);
+      static_for<0, TM * TN>([&](auto Jx) __attribute__((always_inline)) {
+        constexpr int j = decltype(Jx)::value, tm = j / TN, tn = j % TN, i = s * TM * TN + j;
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[s & 1][tm], bv[s & 1][tn], acc[tm][tn], 0, 0, 0);
+        static_for<(i * NC) / NM, ((i + 1) * NC) / NM>([&](auto Cx) __attribute__((always_inline)) {
+          constexpr int c = decltype(Cx)::value;
+          if constexpr (c < OA::J) {
+            if (ca) oa.issue_one(ka, da, d.lda, w, c);
+          } else {
+            if (cb) ob.issue_one(kb2, db, d.ldb, w, c - OA::J);
+          }
+        });
+      });
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
 
   auto stA = [](auto S) { return lds_stage<2 * decltype(S)::value, BM * BK>(); };
@@ -1007,8 +1020,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
 
   // Step kt: wait for this wave's copies of tile kt (later copies may stay
   // in flight), barrier (every wave's copies of tile kt landed and every
-  // wave is done with tile kt-1), refill the stages of tile kt-1 with A of
-  // tile kt+NS-1 and B of tile kt+NB-1, then the MFMAs of tile kt.
+  // wave is done with tile kt-1), then the MFMAs of tile kt, with the
+  // refill of the stages of tile kt-1 (A of tile kt+NS-1, B of tile
+  // kt+NB-1) interleaved.
   int bs = 0;  // B stage of tile kt
   auto step = [&](auto S, int kt) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
@@ -1024,9 +1038,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
     }
     __syncthreads();
     const int bfree = bs == 0 ? NB - 1 : bs - 1;  // B stage of tile kt-1
-    if (kt + NS - 1 < nkt) oa.issue(kt + NS - 1, stA(std::integral_constant<int, (s + NS - 1) % NS>{}), d.lda, w);
-    if (kt + NB - 1 < nkt) ob.issue(kt + NB - 1, stB(bfree), d.ldb, w);
-    compute(stA(S), stB(bs));
+    compute(stA(S), stB(bs), kt + NS - 1 < nkt, kt + NS - 1, stA(std::integral_constant<int, (s + NS - 1) % NS>{}),
+            kt + NB - 1 < nkt, kt + NB - 1, stB(bfree));
     bs = bs + 1 == NB ? 0 : bs + 1;
   };
   // Whole rounds of NS tiles run without branches around the MFMAs (a
