@@ -1614,8 +1614,19 @@ using Nt16Big = PpCfg;
 #endif
 
 // Big tiles pay off once they alone give at least half the CUs a tile.
+// Weight-gradient products (TN) take the small tiles instead when the big
+// ones would leave much of their last round of CUs idle and the small ones
+// fill theirs better (fraction of workgroup slots used over the rounds).
 bool nt16_big(const GemmDesc& d) {
-  return ceil_div(d.M, Nt16Big::bm) * ceil_div(d.N, Nt16Big::bn) >= 128;
+  const int64_t big = ceil_div(d.M, Nt16Big::bm) * ceil_div(d.N, Nt16Big::bn);
+  if (big < 128) return false;
+  if (d.layout == Layout::TN) {
+    const int64_t small = ceil_div(d.M, Nt16Small::bm) * ceil_div(d.N, Nt16Small::bn);
+    const double ub = (double)big / (ceil_div(big, kTargetWgs) * kTargetWgs);
+    const double us = (double)small / (ceil_div(small, 2 * kTargetWgs) * 2 * kTargetWgs);
+    if (ub < 0.8 && us > ub + 0.1) return false;
+  }
+  return true;
 }
 
 // The DMA kernel applies when both operands are fp16 in storage with

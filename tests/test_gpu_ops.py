@@ -98,10 +98,12 @@ def test_gemm_fp16_storage(layout, storage, shape):
 # fp16 operands with enough output tiles for the 256-row tiles (256 x 192
 # for NT when that takes fewer rounds over the CUs, with a third B stage):
 # one to five K tiles (every prologue/tail case of the copy pipeline), a
-# ragged N, a ragged M, and a 128-tile product that splits K
+# ragged N, a ragged M, a 128-tile product that splits K, and a weight-
+# gradient shape whose big tiles would underfill their last round (it
+# takes the small tiles)
 GEMM16_BIG = [(0, 512, 16376, 64), (0, 512, 16376, 128), (0, 512, 16376, 192), (0, 512, 16376, 256),
-              (0, 512, 16376, 320), (0, 520, 16376, 256), (1, 512, 16384, 1024), (2, 4096, 2048, 64),
-              (2, 4096, 2040, 192)]
+              (0, 512, 16376, 320), (0, 520, 16376, 256), (1, 512, 16384, 1024), (2, 4096, 4096, 64),
+              (2, 4096, 4088, 192), (2, 2560, 9728, 128)]
 
 
 @pytest.mark.parametrize("layout,M,N,K", GEMM16_BIG)
