@@ -86,7 +86,7 @@ def summarize(trace_dir, bench_json, out_path):
     avg = sum(per) / nlaunch
 
     # block step: the group holding `steps` QK-norm/RoPE backward launches
-    blk = next((g for g in gs if sum("qk_rope_bwd_kernel" in n for n, _ in g) == steps), None)
+    blk = next((g for g in gs if sum("qk_rope_bwd" in n for n, _ in g) == steps), None)
     if blk:
         blk = [(n, ns) for n, ns in blk if "at::" not in n]
 

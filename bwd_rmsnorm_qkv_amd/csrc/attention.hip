@@ -882,27 +882,71 @@ template <typename T>
 struct AttnSplit {
   static constexpr bool F16 = sizeof(T) == 2;
   static constexpr int FWD_W = 4, DQ_W = F16 ? 4 : 2, DKV_W = F16 ? 4 : 2;
-  static constexpr int NS = 2;
+  static constexpr int FWD_NS = 2, DQ_NS = 2, DKV_NS = 2;
 };
 
-// Fixed-order sum over the W waves of NV floats per lane, through LDS x
-// ((W-1) * NV * 64 floats, reused after the barriers): waves 1..W-1 park
-// their values, wave 0 adds them in wave order into v.
-template <int W, int NV>
-__device__ __forceinline__ void wave_sum_into0(float* x, int w, int lane, float* v) {
-  __syncthreads();
-  if (w > 0) {
-#pragma unroll
-    for (int e = 0; e < NV; ++e) x[((w - 1) * NV + e) * 64 + lane] = v[e];
-  }
-  __syncthreads();
-  if (w == 0) {
-#pragma unroll
-    for (int ww = 1; ww < W; ++ww)
-#pragma unroll
-      for (int e = 0; e < NV; ++e) v[e] += x[((ww - 1) * NV + e) * 64 + lane];
-  }
+// Combine of the W waves' accumulator blocks (NB blocks of 16 floats per
+// lane) in one exchange: block db belongs to wave db % W; every wave parks
+// the blocks it does not own in LDS, and each owner adds the W values of its
+// blocks in wave order (its own from registers), each times scale(ww). The
+// slots are 4 KiB regions (16 x 64 floats, float4 per lane) laid over the
+// kernel's four stage buffers, CAP per buffer; slot(db * W + ww) holds wave
+// ww's block db. The caller puts a barrier between its last reads of those
+// stages and park_blocks, and one between park_blocks and sum_owned.
+template <int CAP>
+__device__ __forceinline__ float* stage_slot(int i, void* b0, void* b1, void* b2, void* b3) {
+  const int b = i / CAP;
+  char* p = (char*)(b == 0 ? b0 : b == 1 ? b1 : b == 2 ? b2 : b3);
+  return (float*)(p + (i % CAP) * 4096);
 }
+template <int W, int NB, class Slot>
+__device__ __forceinline__ void park_blocks(const floatx16 (&v)[NB], int w, int lane, Slot&& slot) {
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
+    if (db % W != w) {
+      float4* p = (float4*)slot(db * W + w);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) p[g * 64 + lane] = make_float4(v[db][4 * g], v[db][4 * g + 1], v[db][4 * g + 2], v[db][4 * g + 3]);
+    }
+}
+template <int W, int NB, bool SCALED, class Slot, class Scale>
+__device__ __forceinline__ void sum_owned(floatx16 (&v)[NB], int w, int lane, Slot&& slot, Scale&& scale) {
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
+    if (db % W == w) {
+      floatx16 acc;
+#pragma unroll
+      for (int ww = 0; ww < W; ++ww) {
+        floatx16 x;
+        if (ww == w) {
+          x = v[db];
+        } else {
+          const float4* p = (const float4*)slot(db * W + ww);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 q = p[g * 64 + lane];
+            x[4 * g] = q.x;
+            x[4 * g + 1] = q.y;
+            x[4 * g + 2] = q.z;
+            x[4 * g + 3] = q.w;
+          }
+        }
+        if constexpr (SCALED) {
+          const float f = scale(ww);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) x[e] *= f;
+        }
+        if (ww == 0) acc = x;
+        else
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[e] += x[e];
+      }
+      v[db] = acc;
+    }
+}
+struct NoScale {
+  __device__ __forceinline__ float operator()(int) const { return 1.f; }
+};
 
 // 2^x on the hardware unit: no denormal rescaling; inputs are <= 0 except
 // under the bounded stale maximum of the forward pass (<= kRescaleSlack).
@@ -924,7 +968,7 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
   using RT = RowTile<T, D>;
   using TT = TrTile<float, (sizeof(T) == 4 ? D : 64)>;
   using E = AttnElem<T>;
-  constexpr int W = AttnSplit<T>::FWD_W, NS = AttnSplit<T>::NS;
+  constexpr int W = AttnSplit<T>::FWD_W, NS = AttnSplit<T>::FWD_NS;
   // fp16 stages V as a row tile and reads V^T out of it; fp32 stages V^T
   constexpr bool TR = sizeof(T) == 2;
   constexpr int VE = TR ? RT::ELEMS : TT::ELEMS;
@@ -1014,32 +1058,40 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
         n, RT::NI + VNI, [&](int t, auto St) __attribute__((always_inline)) { issue(t, sK(St), sV(St)); },
         [](int) {}, [&](int t, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), t); });
 
-    // Combine through the (now free) first stage buffer: every wave learns
-    // every wave's reference max, rescales its own sum and output to the
-    // common max, and wave 0 adds them in wave order, 16 values at a time.
-    static_assert((W - 1) * 16 * 64 * 4 <= W * RT::ELEMS * (int)sizeof(T), "combine space");
-    float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
+    // Log-sum-exp combine in one exchange: every wave parks its reference
+    // max and sum (slot NB W) and the output blocks it does not own; after
+    // the barrier each wave derives the common max, every wave's rescale
+    // factor and the total sum, adds its blocks in wave order and writes
+    // them (wave 0 also the lse).
+    constexpr int NB = D / 32, CAP = W * RT::ELEMS * (int)sizeof(T) / 4096;
+    static_assert(VE == RT::ELEMS && NB * W + 1 <= 4 * CAP, "combine space");
+    auto slot = [&](int i) __attribute__((always_inline)) {
+      return stage_slot<CAP>(i, sK(I0{}), sV(I0{}), sK(I1{}), sV(I1{}));
+    };
+    float* ml = slot(NB * W);
     __syncthreads();
-    x[w * 64 + lane] = m;
+    ml[(2 * w) * 64 + lane] = m;
+    ml[(2 * w + 1) * 64 + lane] = l;
+    park_blocks<W, NB>(o, w, lane, slot);
     __syncthreads();
-    float M = x[lane];
+    float M = ml[lane];
 #pragma unroll
-    for (int ww = 1; ww < W; ++ww) M = fmaxf(M, x[ww * 64 + lane]);
-    const float f = m == -INFINITY ? 0.f : exp2f(m - M);
-    float L = l * f;
-    wave_sum_into0<W, 1>(x, w, lane, &L);
+    for (int ww = 1; ww < W; ++ww) M = fmaxf(M, ml[(2 * ww) * 64 + lane]);
+    float fw[W], L = 0.f;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][e] *= f;
-      wave_sum_into0<W, 16>(x, w, lane, (float*)&o[db]);
+    for (int ww = 0; ww < W; ++ww) {
+      const float mw = ml[(2 * ww) * 64 + lane];
+      fw[ww] = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      const float lw = ml[(2 * ww + 1) * 64 + lane] * fw[ww];
+      L = ww == 0 ? lw : L + lw;
     }
-    if (w == 0) {
-      if (qi < S) {
-        const float inv = 1.0f / L;
-        const int64_t ooff = (tok0 + qi) * a.ldo + (int64_t)h * D + 4 * kh;
+    sum_owned<W, NB, true>(o, w, lane, slot, [&](int ww) __attribute__((always_inline)) { return fw[ww]; });
+    if (qi < S) {
+      const float inv = 1.0f / L;
+      const int64_t ooff = (tok0 + qi) * a.ldo + (int64_t)h * D + 4 * kh;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < NB; ++db)
+        if (db % W == w) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const float4 vv =
@@ -1047,8 +1099,8 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
             *(float4*)(a.o + ooff + db * 32 + 8 * g) = vv;
             if (a.o16) *(half4*)(a.o16 + ooff + db * 32 + 8 * g) = to_half4(vv);
           }
-        if (kh == 0) a.lse[((int64_t)b * a.heads + h) * S + qi] = (M + log2f(L)) * kLn2;
-      }
+        }
+      if (w == 0 && kh == 0) a.lse[((int64_t)b * a.heads + h) * S + qi] = (M + log2f(L)) * kLn2;
     }
   }
 }
@@ -1062,7 +1114,7 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
   using RT = RowTile<T, D>;
   using TT = TrTile<float, (sizeof(T) == 4 ? D : 64)>;
   using E = AttnElem<T>;
-  constexpr int W = AttnSplit<T>::DQ_W, NS = AttnSplit<T>::NS;
+  constexpr int W = AttnSplit<T>::DQ_W, NS = AttnSplit<T>::DQ_NS;
   // fp16 reads K^T out of the K row tile; fp32 stages K^T too
   constexpr bool TR = sizeof(T) == 2;
   constexpr int KTE = TR ? 16 : TT::ELEMS;
@@ -1180,21 +1232,28 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
         [&](int t, auto St) __attribute__((always_inline)) { issue(t, sK(St), sV(St), sKt(St)); }, [](int) {},
         [&](int t, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), sKt(St), t); });
 
-    static_assert((W - 1) * 16 * 64 * 4 <= W * RT::ELEMS * (int)sizeof(T), "combine space");
-    float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
+    // one exchange: each wave adds the blocks it owns in wave order and
+    // writes them
+    constexpr int NB = D / 32, CAP = W * RT::ELEMS * (int)sizeof(T) / 4096;
+    static_assert(NB * W <= 4 * CAP, "combine space");
+    auto slot = [&](int i) __attribute__((always_inline)) {
+      return stage_slot<CAP>(i, sK(I0{}), sV(I0{}), sK(I1{}), sV(I1{}));
+    };
+    __syncthreads();
+    park_blocks<W, NB>(dq, w, lane, slot);
+    __syncthreads();
+    sum_owned<W, NB, false>(dq, w, lane, slot, NoScale{});
+    if (qi < S) {
+      const float inv = 1.0f / sqrtf((float)D);
+      float* row = a.dq + (tok0 + qi) * a.lddq + (int64_t)h * D + 4 * kh;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) wave_sum_into0<W, 16>(x, w, lane, (float*)&dq[db]);
-    if (w == 0) {
-      if (qi < S) {
-        const float inv = 1.0f / sqrtf((float)D);
-        float* row = a.dq + (tok0 + qi) * a.lddq + (int64_t)h * D + 4 * kh;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < NB; ++db)
+        if (db % W == w) {
 #pragma unroll
           for (int g = 0; g < 4; ++g)
             *(float4*)(row + db * 32 + 8 * g) = make_float4(dq[db][4 * g] * inv, dq[db][4 * g + 1] * inv,
                                                             dq[db][4 * g + 2] * inv, dq[db][4 * g + 3] * inv);
-      }
+        }
     }
   }
 }
@@ -1212,7 +1271,7 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
   using RT = RowTile<T, D>;
   using TT = TrTile<float, (sizeof(T) == 4 ? D : 64)>;
   using E = AttnElem<T>;
-  constexpr int W = AttnSplit<T>::DKV_W, NS = AttnSplit<T>::NS;
+  constexpr int W = AttnSplit<T>::DKV_W, NS = AttnSplit<T>::DKV_NS;
   // fp16 reads Q^T and dO^T out of the row tiles; fp32 stages them too
   constexpr bool TR = sizeof(T) == 2;
   constexpr int XTE = TR ? 16 : TT::ELEMS;
@@ -1344,28 +1403,38 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
         },
         [&](int t, auto St) __attribute__((always_inline)) { compute(sQ(St), sO(St), sQt(St), sOt(St), t); });
 
-    static_assert((W - 1) * 16 * 64 * 4 <= W * RT::ELEMS * (int)sizeof(T), "combine space");
-    float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
+    // one exchange over the 2 NB blocks (dK's, then dV's): each wave adds
+    // the blocks it owns in wave order and writes them
+    constexpr int NB = D / 32, CAP = W * RT::ELEMS * (int)sizeof(T) / 4096;
+    static_assert(2 * NB * W <= 4 * CAP, "combine space");
+    auto slot = [&](int i) __attribute__((always_inline)) {
+      return stage_slot<CAP>(i, sQ(I0{}), sO(I0{}), sQ(I1{}), sO(I1{}));
+    };
+    floatx16 kv[2 * NB];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      wave_sum_into0<W, 16>(x, w, lane, (float*)&dk[db]);
-      wave_sum_into0<W, 16>(x, w, lane, (float*)&dv[db]);
+    for (int db = 0; db < NB; ++db) {
+      kv[db] = dk[db];
+      kv[NB + db] = dv[db];
     }
-    if (w == 0) {
-      if (kj < S) {
-        const float inv = 1.0f / sqrtf((float)D);
-        float* krow = dk_part + ((tok0 + kj) * a.heads + h) * (int64_t)D + 4 * kh;
-        float* vrow = dv_part + ((tok0 + kj) * a.heads + h) * (int64_t)D + 4 * kh;
+    __syncthreads();
+    park_blocks<W, 2 * NB>(kv, w, lane, slot);
+    __syncthreads();
+    sum_owned<W, 2 * NB, false>(kv, w, lane, slot, NoScale{});
+    if (kj < S) {
+      const float inv = 1.0f / sqrtf((float)D);
+      float* krow = dk_part + ((tok0 + kj) * a.heads + h) * (int64_t)D + 4 * kh;
+      float* vrow = dv_part + ((tok0 + kj) * a.heads + h) * (int64_t)D + 4 * kh;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+      for (int j = 0; j < 2 * NB; ++j)
+        if (j % W == w) {
+          const int db = j % NB;
+          const float sc = j < NB ? inv : 1.f;
+          float* row = (j < NB ? krow : vrow) + db * 32;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            *(float4*)(krow + db * 32 + 8 * g) = make_float4(dk[db][4 * g] * inv, dk[db][4 * g + 1] * inv,
-                                                             dk[db][4 * g + 2] * inv, dk[db][4 * g + 3] * inv);
-            *(float4*)(vrow + db * 32 + 8 * g) =
-                make_float4(dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
-          }
-      }
+          for (int g = 0; g < 4; ++g)
+            *(float4*)(row + 8 * g) = make_float4(kv[j][4 * g] * sc, kv[j][4 * g + 1] * sc, kv[j][4 * g + 2] * sc,
+                                                  kv[j][4 * g + 3] * sc);
+        }
     }
   }
 }

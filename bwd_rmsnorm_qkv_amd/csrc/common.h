@@ -29,6 +29,40 @@ int check_launch(const char* what);
   } while (0)
 
 // ------------------------------------------------------- wave reductions
+// Lane exchanges without the LDS crossbar: DPP within rows of 16 lanes
+// (quad permutations, then the mirrors within 8 and 16 lanes) and the
+// row swaps of v_permlane16/32_swap above. Each step adds a value equal in
+// every lane of a group to the other group's; fp addition commutes, so every
+// lane of a group ends with bitwise the same sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + dpp_f<CTRL>(v);
+}
+// Sum over aligned groups of N lanes (N a power of two, 1..64).
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "group size");
+  if constexpr (N >= 2) v = dpp_add<0xB1>(v);   // quad_perm 1,0,3,2
+  if constexpr (N >= 4) v = dpp_add<0x4E>(v);   // quad_perm 2,3,0,1
+  if constexpr (N >= 8) v = dpp_add<0x141>(v);  // row_half_mirror
+  if constexpr (N >= 16) v = dpp_add<0x140>(v); // row_mirror
+  if constexpr (N >= 32) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+  }
+  if constexpr (N >= 64) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    v = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+  }
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -156,12 +156,215 @@ __global__ __launch_bounds__(256) void qk_rope_bwd_kernel(QkRopeBwdArgs a, int n
   }
 }
 
+// The same two passes with 64 / LPH heads side by side in one wave (head_dim
+// = 4 LPH): LPH lanes per head, each holding elements 2j, 2j+1 of both
+// halves, so that every load and store moves 8 (fp32) or 4 (fp16) bytes per
+// lane; each wave takes kQkRows tokens of its heads with every load issued
+// before any arithmetic (tokens past the end load the last token and are
+// skipped). Heads past the last of a group's range are computed on head 0
+// and not stored.
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ h2v to_h2(float a, float b) {
+  h2v h;
+  h[0] = (f16)a;
+  h[1] = (f16)b;
+  return h;
+}
+
+template <int LPH>
+__global__ __launch_bounds__(256) void qk_rope_fwd_pair_kernel(QkRopeArgs a) {
+  constexpr int HPW = 64 / LPH, D = 4 * LPH, HALF = 2 * LPH, R = kQkRows;
+  const int lane = threadIdx.x & 63, j = lane % LPH;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nqk = a.heads + a.kv_heads;
+  const int nh = nqk + (a.v16 ? a.kv_heads : 0);
+  const int ng = (nh + HPW - 1) / HPW;
+  const int t0 = (wid / ng) * R;
+  if (t0 >= a.T) return;
+  const int head = (wid % ng) * HPW + lane / LPH;
+  const bool valid = head < nh;
+  const int hc = valid ? head : 0;
+  const bool is_v = hc >= nqk, is_q = hc < a.heads;
+  float2 x0[R], x1[R];
+  float4 cs[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = min(t0 + r, a.T - 1);
+    const float* src = a.qkv + (int64_t)t * a.ld_qkv + (int64_t)hc * D + 2 * j;
+    x0[r] = *(const float2*)src;
+    x1[r] = *(const float2*)(src + HALF);
+    cs[r] = *(const float4*)(a.tab + (t % a.seq) * HALF + 2 * j);
+  }
+  const float* g = is_q ? a.g_q : a.g_k;
+  float2 ga = make_float2(1.f, 1.f), gb = ga;
+  if (a.qk_norm) {
+    ga = *(const float2*)(g + 2 * j);
+    gb = *(const float2*)(g + HALF + 2 * j);
+  }
+  const int hh = is_v ? hc - nqk : is_q ? hc : hc - a.heads;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = t0 + r;
+    if (t >= a.T) break;
+    float2 p = x0[r], q = x1[r];
+    if (a.qk_norm) {
+      const float ss = group_sum<LPH>(p.x * p.x + p.y * p.y + q.x * q.x + q.y * q.y);
+      const float rho = 1.0f / sqrtf(ss / (float)D + a.eps);
+      if (valid && !is_v && j == 0) (is_q ? a.rho_q[(int64_t)t * a.heads + hh] : a.rho_k[(int64_t)t * a.kv_heads + hh]) = rho;
+      if (!is_v) {
+        p = make_float2(p.x * rho * ga.x, p.y * rho * ga.y);
+        q = make_float2(q.x * rho * gb.x, q.y * rho * gb.y);
+      }
+    }
+    if (!valid) continue;
+    if (is_v) {
+      f16* dst = a.v16 + ((int64_t)t * a.kv_heads + hh) * D + 2 * j;
+      *(h2v*)dst = to_h2(p.x, p.y);
+      *(h2v*)(dst + HALF) = to_h2(q.x, q.y);
+      continue;
+    }
+    // NeoX rotation of the pairs (2j, HALF + 2j) and (2j + 1, HALF + 2j + 1)
+    const float2 o0 = make_float2(p.x * cs[r].x - q.x * cs[r].y, p.y * cs[r].z - q.y * cs[r].w);
+    const float2 o1 = make_float2(q.x * cs[r].x + p.x * cs[r].y, q.y * cs[r].z + p.y * cs[r].w);
+    const int64_t orow = ((int64_t)t * (is_q ? a.heads : a.kv_heads) + hh) * D + 2 * j;
+    float* dst = is_q ? a.qr : a.kr;
+    f16* dst16 = is_q ? a.q16 : a.k16;
+    if (dst) {
+      *(float2*)(dst + orow) = o0;
+      *(float2*)(dst + orow + HALF) = o1;
+    }
+    if (dst16) {
+      *(h2v*)(dst16 + orow) = to_h2(o0.x, o0.y);
+      *(h2v*)(dst16 + orow + HALF) = to_h2(o1.x, o1.y);
+    }
+  }
+}
+
+// Backward in the same layout: blocks [0, nbq) take the q heads, the rest
+// the k heads; the gamma-gradient partials of a block (its 4 waves, each
+// over its HPW heads and R tokens) form one row, summed in a fixed order.
+template <int LPH>
+__global__ __launch_bounds__(256) void qk_rope_bwd_pair_kernel(QkRopeBwdArgs a, int nbq, float* __restrict__ part_q,
+                                                               float* __restrict__ part_k) {
+  constexpr int HPW = 64 / LPH, D = 4 * LPH, HALF = 2 * LPH, R = kQkRows;
+  __shared__ float4 red[4][LPH];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, j = lane % LPH;
+  const bool is_q = (int)blockIdx.x < nbq;
+  const int blk = is_q ? blockIdx.x : blockIdx.x - nbq;
+  const int nh = is_q ? a.heads : a.kv_heads;
+  const int ng = (nh + HPW - 1) / HPW;
+  const int wid = blk * 4 + w;
+  const int t0 = (wid / ng) * R;
+  const int head = (wid % ng) * HPW + lane / LPH;
+  const bool valid = head < nh && t0 < a.T;
+  const int hc = head < nh ? head : 0;
+  const int col0 = (is_q ? 0 : a.heads * D) + hc * D + 2 * j;
+  const float* __restrict__ dsrc = (is_q ? a.dqr : a.dkr) + (int64_t)hc * D + 2 * j;
+  float2 y0[R], y1[R], x0[R], x1[R];
+  float4 cs[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = min(t0 + r, a.T - 1);
+    y0[r] = *(const float2*)(dsrc + (int64_t)t * nh * D);
+    y1[r] = *(const float2*)(dsrc + (int64_t)t * nh * D + HALF);
+    cs[r] = *(const float4*)(a.tab + (t % a.seq) * HALF + 2 * j);
+    if (a.qk_norm) {
+      const float* xr = a.qkv + (int64_t)t * a.ld_qkv + col0;
+      x0[r] = *(const float2*)xr;
+      x1[r] = *(const float2*)(xr + HALF);
+    }
+  }
+  float2 ga = make_float2(0.f, 0.f), gb = ga;
+  if (a.qk_norm) {
+    const float* g = is_q ? a.g_q : a.g_k;
+    ga = *(const float2*)(g + 2 * j);
+    gb = *(const float2*)(g + HALF + 2 * j);
+  }
+  float4 dg = make_float4(0.f, 0.f, 0.f, 0.f);  // elements 2j, 2j+1, HALF+2j, HALF+2j+1
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = t0 + r;
+    if (t >= a.T) break;
+    // transpose of the rotation
+    float2 o0 = make_float2(y0[r].x * cs[r].x + y1[r].x * cs[r].y, y0[r].y * cs[r].z + y1[r].y * cs[r].w);
+    float2 o1 = make_float2(y1[r].x * cs[r].x - y0[r].x * cs[r].y, y1[r].y * cs[r].z - y0[r].y * cs[r].w);
+    if (a.qk_norm) {
+      const float2 p = x0[r], q = x1[r];
+      const float ss = group_sum<LPH>(p.x * p.x + p.y * p.y + q.x * q.x + q.y * q.y);
+      const float rho = 1.0f / sqrtf(ss / (float)D + a.eps);
+      const float2 hp = make_float2(p.x * rho, p.y * rho), hq = make_float2(q.x * rho, q.y * rho);
+      const float2 ep = make_float2(ga.x * o0.x, ga.y * o0.y), eq = make_float2(gb.x * o1.x, gb.y * o1.y);
+      const float dot = group_sum<LPH>(ep.x * hp.x + ep.y * hp.y + eq.x * hq.x + eq.y * hq.y) / (float)D;
+      if (valid) {
+        dg.x += o0.x * hp.x;
+        dg.y += o0.y * hp.y;
+        dg.z += o1.x * hq.x;
+        dg.w += o1.y * hq.y;
+      }
+      o0 = make_float2(rho * (ep.x - hp.x * dot), rho * (ep.y - hp.y * dot));
+      o1 = make_float2(rho * (eq.x - hq.x * dot), rho * (eq.y - hq.y * dot));
+    }
+    if (!valid) continue;
+    const int64_t o = (int64_t)t * a.ld_qkv + col0;
+    if (a.dqkv) {
+      *(float2*)(a.dqkv + o) = o0;
+      *(float2*)(a.dqkv + o + HALF) = o1;
+    }
+    if (a.dqkv16) {
+      *(h2v*)(a.dqkv16 + o) = to_h2(o0.x, o0.y);
+      *(h2v*)(a.dqkv16 + o + HALF) = to_h2(o1.x, o1.y);
+    }
+  }
+  if (!a.qk_norm) return;
+  // the wave's heads, then the waves in order
+  if constexpr (LPH < 64) {
+    __shared__ float4 hs[4][64];
+    hs[w][lane] = dg;
+    __syncthreads();
+    if (lane < LPH) {
+#pragma unroll
+      for (int k = 1; k < HPW; ++k) {
+        const float4 e = hs[w][k * LPH + lane];
+        dg = make_float4(dg.x + e.x, dg.y + e.y, dg.z + e.z, dg.w + e.w);
+      }
+    }
+  }
+  if (lane < LPH) red[w][lane] = dg;
+  __syncthreads();
+  if (threadIdx.x < LPH) {
+    const int c = threadIdx.x;
+    const float4 a0 = red[0][c], a1 = red[1][c], a2 = red[2][c], a3 = red[3][c];
+    float* pr = (is_q ? part_q : part_k) + (int64_t)blk * D;
+    *(float2*)(pr + 2 * c) = make_float2(((a0.x + a1.x) + a2.x) + a3.x, ((a0.y + a1.y) + a2.y) + a3.y);
+    *(float2*)(pr + HALF + 2 * c) = make_float2(((a0.z + a1.z) + a2.z) + a3.z, ((a0.w + a1.w) + a2.w) + a3.w);
+  }
+}
+
+// Lanes per head of the paired layout, or 0 where it does not apply.
+int qk_pair_lph(int head_dim) {
+  if (head_dim % 4) return 0;
+  const int lph = head_dim / 4;
+  return (lph == 8 || lph == 16 || lph == 32 || lph == 64) ? lph : 0;
+}
+bool al(const void* p, int n) { return (uintptr_t)p % n == 0; }
+// The paired kernels' 8- and 16-byte accesses need these alignments.
+bool qk_pair_fits(int64_t ld_qkv, const float2* tab, const float* g_q, const float* g_k,
+                  std::initializer_list<const void*> p8) {
+  bool ok = ld_qkv % 2 == 0 && al(tab, 16) && al(g_q, 8) && al(g_k, 8);
+  for (const void* q : p8) ok = ok && al(q, 8);
+  return ok;
+}
+
 __global__ void fill_kernel(float* p, int n, float v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
 }
 
-int qk_parts(int T, int nh) { return (int)ceil_div((int64_t)T * nh, 4 * kQkRows); }
+// Partial rows of the backward with the paired layout (lph > 0) or without.
+int qk_parts(int T, int nh, int lph) {
+  if (lph) return (int)ceil_div(ceil_div((int64_t)T, kQkRows) * ceil_div(nh, 64 / lph), 4);
+  return (int)ceil_div((int64_t)T * nh, 4 * kQkRows);
+}
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
@@ -239,14 +442,37 @@ int rope_table(int seq, int head_dim, float theta, float2* tab, hipStream_t st) 
   return check_launch("rope_table_kernel");
 }
 
+template <class K>
+static void launch_pair(int lph, K k) {
+  switch (lph) {
+    case 8: k(std::integral_constant<int, 8>{}); break;
+    case 16: k(std::integral_constant<int, 16>{}); break;
+    case 32: k(std::integral_constant<int, 32>{}); break;
+    default: k(std::integral_constant<int, 64>{}); break;
+  }
+}
+
 int qk_norm_rope_forward(const QkRopeArgs& a, hipStream_t st) {
-  const int64_t items = (int64_t)a.T * (a.heads + a.kv_heads + (a.v16 ? a.kv_heads : 0));
+  const int nh = a.heads + a.kv_heads + (a.v16 ? a.kv_heads : 0);
+  const int lph = qk_pair_lph(a.head_dim);
+  if (lph && qk_pair_fits(a.ld_qkv, a.tab, a.g_q, a.g_k, {a.qkv, a.qr, a.kr, a.q16, a.k16, a.v16})) {
+    const int64_t waves = ceil_div((int64_t)a.T, kQkRows) * ceil_div(nh, 64 / lph);
+    launch_pair(lph, [&](auto L) {
+      hipLaunchKernelGGL(qk_rope_fwd_pair_kernel<decltype(L)::value>, dim3((unsigned)ceil_div(waves, 4)), dim3(256),
+                         0, st, a);
+    });
+    return check_launch("qk_rope_fwd_pair_kernel");
+  }
+  const int64_t items = (int64_t)a.T * nh;
   hipLaunchKernelGGL(qk_rope_fwd_kernel, dim3((unsigned)ceil_div(items, 4)), dim3(256), 0, st, a);
   return check_launch("qk_rope_fwd_kernel");
 }
 
 size_t qk_norm_rope_bwd_scratch(int T, int heads, int kv_heads, int head_dim) {
-  return (size_t)(qk_parts(T, heads) + qk_parts(T, kv_heads)) * head_dim * sizeof(float);
+  const int lph = qk_pair_lph(head_dim);
+  const int rows = std::max(qk_parts(T, heads, lph) + qk_parts(T, kv_heads, lph),
+                            qk_parts(T, heads, 0) + qk_parts(T, kv_heads, 0));
+  return (size_t)rows * head_dim * sizeof(float);
 }
 
 int qk_norm_rope_backward(const QkRopeBwdArgs& a, float* scratch, hipStream_t st) {
@@ -259,11 +485,21 @@ int qk_norm_rope_backward(const QkRopeBwdArgs& a, float* scratch, hipStream_t st
 int qk_norm_rope_backward_partials(const QkRopeBwdArgs& a, float* scratch, ColsumJob* jobs, int& njobs,
                                    hipStream_t st) {
   const int d = a.head_dim;
-  const int pq = qk_parts(a.T, a.heads), pk = qk_parts(a.T, a.kv_heads);
+  int lph = qk_pair_lph(d);
+  if (!qk_pair_fits(a.ld_qkv, a.tab, a.g_q, a.g_k, {a.qkv, a.dqr, a.dkr, a.dqkv, a.dqkv16})) lph = 0;
+  const int pq = qk_parts(a.T, a.heads, lph), pk = qk_parts(a.T, a.kv_heads, lph);
   float* part_q = scratch;
   float* part_k = scratch + (size_t)pq * d;
-  hipLaunchKernelGGL(qk_rope_bwd_kernel, dim3((unsigned)(pq + pk)), dim3(256), 0, st, a, pq, part_q, part_k);
-  QBLK_TRY(check_launch("qk_rope_bwd_kernel"));
+  if (lph) {
+    launch_pair(lph, [&](auto L) {
+      hipLaunchKernelGGL(qk_rope_bwd_pair_kernel<decltype(L)::value>, dim3((unsigned)(pq + pk)), dim3(256), 0, st,
+                         a, pq, part_q, part_k);
+    });
+    QBLK_TRY(check_launch("qk_rope_bwd_pair_kernel"));
+  } else {
+    hipLaunchKernelGGL(qk_rope_bwd_kernel, dim3((unsigned)(pq + pk)), dim3(256), 0, st, a, pq, part_q, part_k);
+    QBLK_TRY(check_launch("qk_rope_bwd_kernel"));
+  }
   if (a.qk_norm) {
     jobs[njobs++] = ColsumJob{pq, d, part_q, a.dg_q};
     jobs[njobs++] = ColsumJob{pk, d, part_k, a.dg_k};
