@@ -168,8 +168,8 @@ __device__ __forceinline__ void stage_tile(T* s, T* st, const float* g, int64_t 
   }
 }
 
-__device__ __forceinline__ float half_max(float v) { return fmaxf(v, __shfl_xor(v, 32, kWave)); }
-__device__ __forceinline__ float half_sum(float v) { return v + __shfl_xor(v, 32, kWave); }
+__device__ __forceinline__ float half_max(float v) { return cross_half_max(v); }
+__device__ __forceinline__ float half_sum(float v) { return cross_half_sum(v); }
 
 // ------------------------------------------------------------ forward
 // grid (q tiles, kv groups, batch); one wave per query head of the group.
@@ -1171,7 +1171,7 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
 #pragma unroll
       for (int j = 0; j < CW / 4; ++j)
         part += o4[j].x * d4[j].x + o4[j].y * d4[j].y + o4[j].z * d4[j].z + o4[j].w * d4[j].w;
-      part += __shfl_xor(part, 32, kWave);
+      part = cross_half_sum(part);
       float* x = (float*)att_lds<T, 0, W * RT::ELEMS>();
       x[w * 64 + lane] = part;
       __syncthreads();

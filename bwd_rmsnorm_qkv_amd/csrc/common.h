@@ -42,6 +42,21 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_add(float v) {
   return v + dpp_f<CTRL>(v);
 }
+// Lane i's value combined with lane i ^ 32's (v_permlane32_swap), the same
+// in both lanes.
+__device__ __forceinline__ float2 cross_half(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return make_float2(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float cross_half_sum(float v) {
+  const float2 r = cross_half(v);
+  return r.x + r.y;
+}
+__device__ __forceinline__ float cross_half_max(float v) {
+  const float2 r = cross_half(v);
+  return fmaxf(r.x, r.y);
+}
 // Sum over aligned groups of N lanes (N a power of two, 1..64).
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
@@ -55,19 +70,12 @@ __device__ __forceinline__ float group_sum(float v) {
     const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
     v = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
   }
-  if constexpr (N >= 64) {
-    const unsigned u = __builtin_bit_cast(unsigned, v);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    v = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
-  }
+  if constexpr (N >= 64) v = cross_half_sum(v);
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
+// Whole-wave sum; call in uniform control flow (every lane active).
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
