@@ -469,6 +469,7 @@ struct Grid {
   int tiles_m, tiles_n, splits, kchunk;
   int vec = 0;    // 1: output rows (and partials, residual) take 16-byte stores
   int bn = 0;     // tile width (ping-pong kernel: 256 or 192)
+  int nfast = 0;  // ping-pong kernel: N tiles fastest (consecutive workgroups share an A tile)
 };
 
 // Final value of C[row, col]: the row pointer `cp` already routed through
@@ -1180,8 +1181,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int per = total / 8, rem = total % 8;
   const int lt = xcd * per + min(xcd, rem) + slot;
-  const int mt = lt % gd.tiles_m;
-  const int nt = (lt / gd.tiles_m) % gd.tiles_n;
+  const int mt = gd.nfast ? (lt / gd.tiles_n) % gd.tiles_m : lt % gd.tiles_m;
+  const int nt = gd.nfast ? lt % gd.tiles_n : (lt / gd.tiles_m) % gd.tiles_n;
   const int sp = lt / (gd.tiles_m * gd.tiles_n);
   const int m0 = mt * BM, n0 = nt * BN;
   const int kb = sp * gd.kchunk;
@@ -1683,6 +1684,10 @@ Grid plan(const GemmDesc& d, size_t ws_bytes) {
                  : plan_tiles(d, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64, -2 * kTargetWgs);
     g.bn = bn;
     g.vec = out_vec4(d, g);
+    // weight gradients (TN): the N tiles of one A tile on neighbouring
+    // workgroups, so that the long A operand is read about once while the
+    // short B operand stays in L2 (fewer bytes fetched past L2)
+    g.nfast = big && d.layout == Layout::TN;
     return g;
   }
   const Cfg c = cfg_for(d);
