@@ -344,7 +344,7 @@ __global__ __launch_bounds__(256) void qk_rope_bwd_pair_kernel(QkRopeBwdArgs a, 
 int qk_pair_lph(int head_dim) {
   if (head_dim % 4) return 0;
   const int lph = head_dim / 4;
-  return (lph == 8 || lph == 16 || lph == 32 || lph == 64) ? lph : 0;
+  return (lph == 8 || lph == 16 || lph == 32) ? lph : 0;  // head_dim 32, 64, 128
 }
 bool al(const void* p, int n) { return (uintptr_t)p % n == 0; }
 // The paired kernels' 8- and 16-byte accesses need these alignments.
@@ -447,8 +447,7 @@ static void launch_pair(int lph, K k) {
   switch (lph) {
     case 8: k(std::integral_constant<int, 8>{}); break;
     case 16: k(std::integral_constant<int, 16>{}); break;
-    case 32: k(std::integral_constant<int, 32>{}); break;
-    default: k(std::integral_constant<int, 64>{}); break;
+    default: k(std::integral_constant<int, 32>{}); break;
   }
 }
 

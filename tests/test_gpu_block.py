@@ -29,6 +29,12 @@ CASES = {
     # fused SwiGLU backward
     "fp16_wide_split": synth.BlockShape(hidden=4096, heads=8, kv_heads=2, head_dim=64, intermediate=512,
                                         seq=64, batch=1, rope_theta=1e4, gemm_precision=1),
+    # head_dim 32: QK-norm/RoPE with four heads per wave, ragged token count
+    "small_d32_ragged": synth.BlockShape(hidden=256, heads=8, kv_heads=2, head_dim=32, intermediate=512,
+                                         seq=37, batch=2, rope_theta=1e4),
+    # no QK-norm (RoPE only; the q/k gamma gradients are zero)
+    "small_fp16_no_qk_norm": synth.BlockShape(hidden=512, heads=8, kv_heads=2, head_dim=64, intermediate=1408,
+                                              seq=96, batch=2, rope_theta=1e4, qk_norm=0, gemm_precision=1),
     "qwen3_4b": synth.QWEN3_4B_BLOCK,
 }
 
