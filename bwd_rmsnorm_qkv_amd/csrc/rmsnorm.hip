@@ -168,6 +168,166 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int rows, int n, float
   }
 }
 
+// Wide rows on few rows (n >= 1024, rows <= 4096, e.g. 512 tokens x 2560):
+// one 256-thread workgroup per row (forward) or per run of rows (backward),
+// VPT float4 per thread, so every SIMD of a CU takes part in a row and each
+// lane holds a quarter of what a wave-per-row layout gives it. The row sums
+// go through the waves' DPP sums and a fixed-order add of the four.
+bool rms_rowwg(int rows, int n) { return n >= 1024 && n <= 4096 && rows <= 4096; }
+constexpr int kRowWgMaxParts = 1024;
+int rowwg_parts(int rows) { return (int)std::min<int64_t>(ceil_div(rows, 2), kRowWgMaxParts); }
+
+__device__ __forceinline__ float sum4(const float* r) { return ((r[0] + r[1]) + r[2]) + r[3]; }
+__device__ __forceinline__ float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
+
+template <int VPT>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_row_kernel(int rows, int n, float eps, const float* __restrict__ x,
+                                                              const float* __restrict__ res,
+                                                              const float* __restrict__ gamma, float* __restrict__ y,
+                                                              f16* __restrict__ y16, float* __restrict__ sum_out,
+                                                              float* __restrict__ rho_out, const RopeTabJob tj) {
+  __shared__ float red[4];
+  if ((int)blockIdx.x >= rows) {  // the RoPE table's workgroups
+    rope_entry(tj, ((int)blockIdx.x - rows) * 256 + threadIdx.x);
+    return;
+  }
+  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int n4 = n >> 2;
+  const float4* xr = (const float4*)(x + (int64_t)row * n);
+  const float4* rr = res ? (const float4*)(res + (int64_t)row * n) : nullptr;
+  const float4* gr = (const float4*)gamma;
+  float4 v[VPT], gv[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int cc = min(t + j * 256, n4 - 1);
+    v[j] = xr[cc];
+    gv[j] = gr[cc];
+  }
+  float4 rv[VPT];
+  if (rr) {
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) rv[j] = rr[min(t + j * 256, n4 - 1)];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    if (rr) v[j] = make_float4(v[j].x + rv[j].x, v[j].y + rv[j].y, v[j].z + rv[j].z, v[j].w + rv[j].w);
+    if (t + j * 256 >= n4) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += dot4(v[j], v[j]);
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[w] = ss;
+  __syncthreads();
+  const float rho = 1.0f / sqrtf(sum4(red) / (float)n + eps);
+  if (t == 0 && rho_out) rho_out[row] = rho;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int c = t + j * 256;
+    if (c < n4) {
+      if (sum_out) ((float4*)(sum_out + (int64_t)row * n))[c] = v[j];
+      const float4 o = make_float4(v[j].x * rho * gv[j].x, v[j].y * rho * gv[j].y, v[j].z * rho * gv[j].z,
+                                   v[j].w * rho * gv[j].w);
+      if (y) ((float4*)(y + (int64_t)row * n))[c] = o;
+      if (y16) ((half4*)(y16 + (int64_t)row * n))[c] = to_half4(o);
+    }
+  }
+}
+
+// Backward: workgroup b takes rows [b rpb, (b+1) rpb), two at a time with
+// all their loads issued together; each thread keeps the dgamma sums of
+// its own columns over those rows and writes them as partial row b.
+template <int VPT>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_row_kernel(int rows, int n, float eps, const float* __restrict__ x,
+                                                              const float* __restrict__ gamma,
+                                                              const float* __restrict__ dy,
+                                                              const float* __restrict__ dres, float* __restrict__ dx,
+                                                              f16* __restrict__ dx16, float* __restrict__ partial,
+                                                              int rpb) {
+  __shared__ float red[2][2][4];  // [row of the pair][row sum, dot][wave]
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int n4 = n >> 2;
+  const float4* gr = (const float4*)gamma;
+  float4 gv[VPT], dg[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    gv[j] = gr[min(t + j * 256, n4 - 1)];
+    dg[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const int rb = blockIdx.x * rpb, re = min(rows, rb + rpb);
+  for (int r0 = rb; r0 < re; r0 += 2) {
+    const bool two = r0 + 1 < re;
+    float4 xv[2][VPT], dv[2][VPT], rv[2][VPT];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int row = two ? r0 + k : r0;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int cc = min(t + j * 256, n4 - 1);
+        xv[k][j] = ((const float4*)(x + (int64_t)row * n))[cc];
+        dv[k][j] = ((const float4*)(dy + (int64_t)row * n))[cc];
+        rv[k][j] = dres ? ((const float4*)(dres + (int64_t)row * n))[cc] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float ss[2] = {0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        if (t + j * 256 >= n4) {
+          xv[k][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+          dv[k][j] = xv[k][j];
+        }
+        ss[k] += dot4(xv[k][j], xv[k][j]);
+      }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      ss[k] = wave_sum(ss[k]);
+      if (lane == 0) red[k][0][w] = ss[k];
+    }
+    __syncthreads();
+    float rho[2], dot[2] = {0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      rho[k] = 1.0f / sqrtf(sum4(red[k][0]) / (float)n + eps);
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        xv[k][j] = make_float4(xv[k][j].x * rho[k], xv[k][j].y * rho[k], xv[k][j].z * rho[k], xv[k][j].w * rho[k]);
+        const float4 e = make_float4(gv[j].x * dv[k][j].x, gv[j].y * dv[k][j].y, gv[j].z * dv[k][j].z,
+                                     gv[j].w * dv[k][j].w);
+        dot[k] += dot4(e, xv[k][j]);
+      }
+      dot[k] = wave_sum(dot[k]);
+      if (lane == 0) red[k][1][w] = dot[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (k == 1 && !two) break;
+      const int row = r0 + k;
+      const float dm = sum4(red[k][1]) / (float)n;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int c = t + j * 256;
+        if (c >= n4) continue;
+        const float4 xh = xv[k][j], d = dv[k][j], r = rv[k][j];
+        float4 o;
+        o.x = rho[k] * (gv[j].x * d.x - xh.x * dm) + r.x;
+        o.y = rho[k] * (gv[j].y * d.y - xh.y * dm) + r.y;
+        o.z = rho[k] * (gv[j].z * d.z - xh.z * dm) + r.z;
+        o.w = rho[k] * (gv[j].w * d.w - xh.w * dm) + r.w;
+        ((float4*)(dx + (int64_t)row * n))[c] = o;
+        if (dx16) ((half4*)(dx16 + (int64_t)row * n))[c] = to_half4(o);
+        dg[j] = make_float4(dg[j].x + d.x * xh.x, dg[j].y + d.y * xh.y, dg[j].z + d.z * xh.z, dg[j].w + d.w * xh.w);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int c = t + j * 256;
+    if (c < n4) ((float4*)(partial + (int64_t)blockIdx.x * n))[c] = dg[j];
+  }
+}
+
 // 64 columns per workgroup, 16 row groups per column (row p goes to group
 // p % 16, summed in row order); the group sums are then added in group
 // order, so results are bitwise reproducible.
@@ -219,7 +379,7 @@ int vpl_for(int n) {
 }  // namespace
 
 int rmsnorm_bwd_parts(int rows, int n) {
-  (void)n;
+  if (rms_rowwg(rows, n)) return rowwg_parts(rows);
   return (int)std::min<int64_t>(ceil_div(rows, kWavesPerBlock), 240);
 }
 
@@ -240,6 +400,19 @@ int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res
   QBLK_TRY(rmsnorm_check(rows, n));
   const RopeTabJob tj = tab ? *tab : RopeTabJob{};
   const int64_t tab_blocks = ceil_div((int64_t)tj.seq * tj.half, 256);
+  if (rms_rowwg(rows, n)) {
+    const dim3 g((unsigned)(rows + tab_blocks));
+    switch ((int)ceil_div(n / 4, 256)) {
+#define QBLK_CASE(V)                                                                                       \
+  case V:                                                                                                  \
+    hipLaunchKernelGGL(rmsnorm_fwd_row_kernel<V>, g, dim3(256), 0, st, rows, n, eps, x, res, gamma, y, y16, \
+                       sum_out, rho, tj);                                                                  \
+    break;
+      QBLK_CASE(1) QBLK_CASE(2) QBLK_CASE(3) QBLK_CASE(4)
+#undef QBLK_CASE
+    }
+    return check_launch("rmsnorm_fwd_row_kernel");
+  }
   const dim3 grid((unsigned)(ceil_div(rows, kWavesPerBlock) + tab_blocks)), block(256);
   switch (vpl_for(n)) {
 #define QBLK_CASE(V)                                                                          \
@@ -264,6 +437,19 @@ int rmsnorm_backward_partials(int rows, int n, float eps, const float* x, const 
                               const float* dres, float* dx, f16* dx16, float* scratch, hipStream_t st) {
   QBLK_TRY(rmsnorm_check(rows, n));
   const int parts = rmsnorm_bwd_parts(rows, n);
+  if (rms_rowwg(rows, n)) {
+    const int rpb = (int)ceil_div(rows, parts);
+    switch ((int)ceil_div(n / 4, 256)) {
+#define QBLK_CASE(V)                                                                                         \
+  case V:                                                                                                    \
+    hipLaunchKernelGGL(rmsnorm_bwd_row_kernel<V>, dim3((unsigned)parts), dim3(256), 0, st, rows, n, eps, x, \
+                       gamma, dy, dres, dx, dx16, scratch, rpb);                                             \
+    break;
+      QBLK_CASE(1) QBLK_CASE(2) QBLK_CASE(3) QBLK_CASE(4)
+#undef QBLK_CASE
+    }
+    return check_launch("rmsnorm_bwd_row_kernel");
+  }
   const dim3 grid((unsigned)parts), block(256);
   switch (vpl_for(n)) {
 #define QBLK_CASE(V)                                                                             \

@@ -125,7 +125,9 @@ def test_gemm_fp16_big_tiles(layout, M, N, K):
     check("C", Cg, Cref, FP32_TOL)
 
 
-@pytest.mark.parametrize("rows,n", [(32, 64), (77, 512), (512, 2560), (5, 4096)])
+# (512, 2560), (5, 4096), (3000, 1028): one workgroup per row (run of rows), the
+# last with more rows than partials; (4100, 1024) and the narrow rows: one wave per row
+@pytest.mark.parametrize("rows,n", [(32, 64), (77, 512), (512, 2560), (5, 4096), (3000, 1028), (4100, 1024)])
 def test_rmsnorm(rows, n):
     need_gpu()
     announce(f"rmsnorm rows={rows} n={n}")
