@@ -5,12 +5,14 @@
 // the NF4 forward, and rms_norm_backward in backward_post_attn_norm and
 // backward_residual_and_input_norm. eps sits inside the square root.
 //
-// One 64-lane wave owns a row: the row is read once with 16-byte loads into
-// registers (VPL float4 per lane, n <= 256 * VPL), reduced with cross-lane
-// shuffles, then written. The backward's dgamma uses no atomics: each
-// workgroup (a fixed function of rows and n) reduces its rows into one
-// partial row in scratch, and colsum_kernel adds the partials in a fixed
-// order, so results are bitwise reproducible.
+// A row is read once with 16-byte loads into registers, reduced with DPP
+// lane exchanges, then written: one 64-lane wave per row (VPL float4 per
+// lane, n <= 256 * VPL), or for wide rows and few of them one 256-thread
+// workgroup per row, whose four wave sums are added in a fixed order. The
+// backward's dgamma uses no atomics: each workgroup (a fixed function of
+// rows and n) reduces its rows into one partial row in scratch, and
+// colsum_kernel adds the partials in a fixed order, so results are bitwise
+// reproducible.
 #include "norms.h"
 
 #include "../../include/qblk.h"
