@@ -53,6 +53,16 @@ __global__ __launch_bounds__(256) void cast_f16_kernel(int R, int C, const float
   }
 }
 
+// The copy alone (no transpose): float4 column j of row blockIdx.y (+
+// k gridDim.y) per thread, no LDS.
+__global__ __launch_bounds__(256) void cast_f16_rows_kernel(int R, int C, const float* __restrict__ in, int64_t ldi,
+                                                            f16* __restrict__ out, int64_t ldo) {
+  const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (j >= C) return;
+  for (int r = blockIdx.y; r < R; r += gridDim.y)
+    *(half4*)(out + (int64_t)r * ldo + j) = to_half4(*(const float4*)(in + (int64_t)r * ldi + j));
+}
+
 // fp32 transpose through the same 64 x 64 LDS tile.
 __global__ __launch_bounds__(256) void transpose_f32_kernel(int R, int C, const float* __restrict__ in, int64_t ldi,
                                                             float* __restrict__ outT, int64_t ldt) {
@@ -106,6 +116,11 @@ int cast_f16(int R, int C, const float* in, int64_t ldi, f16* out, int64_t ldo, 
   if (C % 4 || ldi % 4 || (out && ldo % 4) || (outT && ldt % 4))
     return fail(QBLK_EINVAL, "cast_f16: columns and leading dimensions must be multiples of 4");
   if (!in || (!out && !outT)) return fail(QBLK_EINVAL, "cast_f16: null pointer");
+  if (!outT) {
+    const dim3 g((unsigned)ceil_div(C, 1024), (unsigned)std::min(R, 65535));
+    hipLaunchKernelGGL(cast_f16_rows_kernel, g, dim3(256), 0, st, R, C, in, ldi, out, ldo);
+    return check_launch("cast_f16_rows_kernel");
+  }
   const dim3 grid((unsigned)ceil_div(C, 64), (unsigned)ceil_div(R, 64));
   hipLaunchKernelGGL(cast_f16_kernel, grid, dim3(256), 0, st, R, C, in, ldi, out, ldo, outT, ldt);
   return check_launch("cast_f16_kernel");

@@ -368,20 +368,21 @@ int qk_parts(int T, int nh, int lph) {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-__global__ void swiglu_fwd_kernel(int T, int I, const float* __restrict__ gu, float* __restrict__ s,
-                                  f16* __restrict__ s16) {
-  const int64_t n4 = (int64_t)T * I / 4;
-  const int i4 = I / 4;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n4;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = e / i4, j = e % i4;
-    const float4 g = ((const float4*)(gu + t * 2 * I))[j];
-    const float4 u = ((const float4*)(gu + t * 2 * I + I))[j];
+// One row of gu per blockIdx.y step, float4 column j per thread (a 2-D
+// grid: no index division per element).
+__global__ __launch_bounds__(256) void swiglu_fwd_kernel(int T, int I, const float* __restrict__ gu,
+                                                         float* __restrict__ s, f16* __restrict__ s16) {
+  const int i4 = I / 4, j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= i4) return;
+  for (int t = blockIdx.y; t < T; t += gridDim.y) {
+    const float4 g = ((const float4*)(gu + (int64_t)t * 2 * I))[j];
+    const float4 u = ((const float4*)(gu + (int64_t)t * 2 * I + I))[j];
     float4 o;
     o.x = g.x * sigmoidf_(g.x) * u.x;
     o.y = g.y * sigmoidf_(g.y) * u.y;
     o.z = g.z * sigmoidf_(g.z) * u.z;
     o.w = g.w * sigmoidf_(g.w) * u.w;
+    const int64_t e = (int64_t)t * i4 + j;
     if (s) ((float4*)s)[e] = o;
     if (s16) ((half4*)s16)[e] = to_half4(o);
   }
@@ -394,34 +395,35 @@ __device__ __forceinline__ void swiglu_grad(float g, float u, float ds, float& d
   du = ds * silu;
 }
 
-__global__ void swiglu_bwd_kernel(int T, int I, const float* __restrict__ gu,
-                                  const float* __restrict__ ds, float* __restrict__ dgu,
-                                  f16* __restrict__ dgu16) {
-  const int64_t n4 = (int64_t)T * I / 4;
-  const int i4 = I / 4;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n4;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = e / i4, j = e % i4;
-    const float4 g = ((const float4*)(gu + t * 2 * I))[j];
-    const float4 u = ((const float4*)(gu + t * 2 * I + I))[j];
-    const float4 d = ((const float4*)ds)[e];
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(int T, int I, const float* __restrict__ gu,
+                                                         const float* __restrict__ ds, float* __restrict__ dgu,
+                                                         f16* __restrict__ dgu16) {
+  const int i4 = I / 4, j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= i4) return;
+  for (int t = blockIdx.y; t < T; t += gridDim.y) {
+    const float4 g = ((const float4*)(gu + (int64_t)t * 2 * I))[j];
+    const float4 u = ((const float4*)(gu + (int64_t)t * 2 * I + I))[j];
+    const float4 d = ((const float4*)ds)[(int64_t)t * i4 + j];
     float4 dg, du;
     swiglu_grad(g.x, u.x, d.x, dg.x, du.x);
     swiglu_grad(g.y, u.y, d.y, dg.y, du.y);
     swiglu_grad(g.z, u.z, d.z, dg.z, du.z);
     swiglu_grad(g.w, u.w, d.w, dg.w, du.w);
     if (dgu) {
-      ((float4*)(dgu + t * 2 * I))[j] = dg;
-      ((float4*)(dgu + t * 2 * I + I))[j] = du;
+      ((float4*)(dgu + (int64_t)t * 2 * I))[j] = dg;
+      ((float4*)(dgu + (int64_t)t * 2 * I + I))[j] = du;
     }
     if (dgu16) {
-      ((half4*)(dgu16 + t * 2 * I))[j] = to_half4(dg);
-      ((half4*)(dgu16 + t * 2 * I + I))[j] = to_half4(du);
+      ((half4*)(dgu16 + (int64_t)t * 2 * I))[j] = to_half4(dg);
+      ((half4*)(dgu16 + (int64_t)t * 2 * I + I))[j] = to_half4(du);
     }
   }
 }
 
-unsigned grid_for(int64_t n4) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(n4, 256), 4096)); }
+dim3 swiglu_grid(int T, int I) {
+  return dim3((unsigned)ceil_div(I / 4, 256), (unsigned)std::min(T, 65535));
+}
+
 
 }  // namespace
 
@@ -511,14 +513,12 @@ int qk_norm_rope_backward_partials(const QkRopeBwdArgs& a, float* scratch, Colsu
 }
 
 int swiglu_forward(int T, int I, const float* gu, float* s, f16* s16, hipStream_t st) {
-  const int64_t n4 = (int64_t)T * I / 4;
-  hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(grid_for(n4)), dim3(256), 0, st, T, I, gu, s, s16);
+  hipLaunchKernelGGL(swiglu_fwd_kernel, swiglu_grid(T, I), dim3(256), 0, st, T, I, gu, s, s16);
   return check_launch("swiglu_fwd_kernel");
 }
 
 int swiglu_backward(int T, int I, const float* gu, const float* ds, float* dgu, f16* dgu16, hipStream_t st) {
-  const int64_t n4 = (int64_t)T * I / 4;
-  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(grid_for(n4)), dim3(256), 0, st, T, I, gu, ds, dgu, dgu16);
+  hipLaunchKernelGGL(swiglu_bwd_kernel, swiglu_grid(T, I), dim3(256), 0, st, T, I, gu, ds, dgu, dgu16);
   return check_launch("swiglu_bwd_kernel");
 }
 
