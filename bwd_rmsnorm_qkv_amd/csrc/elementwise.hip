@@ -76,7 +76,10 @@ __global__ __launch_bounds__(256) void qk_rope_fwd_kernel(QkRopeArgs a) {
 // wave takes kQkRows consecutive (t, head) rows with all their loads issued
 // before any arithmetic (rows past the end load the last row and are
 // skipped). dgamma partials: one row per workgroup, in a fixed order.
-constexpr int kQkRows = 8;
+constexpr int kQkRows = 2;
+// Waves per workgroup of the paired backward: each workgroup leaves one
+// gamma-gradient partial row, so more waves mean fewer rows to sum after.
+constexpr int kQkBwdWaves = 4;
 
 __global__ __launch_bounds__(256) void qk_rope_bwd_kernel(QkRopeBwdArgs a, int nbq, float* __restrict__ part_q,
                                                           float* __restrict__ part_k) {
@@ -241,19 +244,20 @@ __global__ __launch_bounds__(256) void qk_rope_fwd_pair_kernel(QkRopeArgs a) {
 }
 
 // Backward in the same layout: blocks [0, nbq) take the q heads, the rest
-// the k heads; the gamma-gradient partials of a block (its 4 waves, each
+// the k heads; the gamma-gradient partials of a block (its kQkBwdWaves waves, each
 // over its HPW heads and R tokens) form one row, summed in a fixed order.
 template <int LPH>
-__global__ __launch_bounds__(256) void qk_rope_bwd_pair_kernel(QkRopeBwdArgs a, int nbq, float* __restrict__ part_q,
-                                                               float* __restrict__ part_k) {
-  constexpr int HPW = 64 / LPH, D = 4 * LPH, HALF = 2 * LPH, R = kQkRows;
-  __shared__ float4 red[4][LPH];
+__global__ __launch_bounds__(64 * kQkBwdWaves) void qk_rope_bwd_pair_kernel(QkRopeBwdArgs a, int nbq,
+                                                                           float* __restrict__ part_q,
+                                                                           float* __restrict__ part_k) {
+  constexpr int HPW = 64 / LPH, D = 4 * LPH, HALF = 2 * LPH, R = kQkRows, WB = kQkBwdWaves;
+  __shared__ float4 red[WB][LPH];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, j = lane % LPH;
   const bool is_q = (int)blockIdx.x < nbq;
   const int blk = is_q ? blockIdx.x : blockIdx.x - nbq;
   const int nh = is_q ? a.heads : a.kv_heads;
   const int ng = (nh + HPW - 1) / HPW;
-  const int wid = blk * 4 + w;
+  const int wid = blk * WB + w;
   const int t0 = (wid / ng) * R;
   const int head = (wid % ng) * HPW + lane / LPH;
   const bool valid = head < nh && t0 < a.T;
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(256) void qk_rope_bwd_pair_kernel(QkRopeBwdArgs a, 
   if (!a.qk_norm) return;
   // the wave's heads, then the waves in order
   if constexpr (LPH < 64) {
-    __shared__ float4 hs[4][64];
+    __shared__ float4 hs[WB][64];
     hs[w][lane] = dg;
     __syncthreads();
     if (lane < LPH) {
@@ -333,10 +337,15 @@ __global__ __launch_bounds__(256) void qk_rope_bwd_pair_kernel(QkRopeBwdArgs a, 
   __syncthreads();
   if (threadIdx.x < LPH) {
     const int c = threadIdx.x;
-    const float4 a0 = red[0][c], a1 = red[1][c], a2 = red[2][c], a3 = red[3][c];
+    float4 t = red[0][c];
+#pragma unroll
+    for (int ww = 1; ww < WB; ++ww) {
+      const float4 e = red[ww][c];
+      t = make_float4(t.x + e.x, t.y + e.y, t.z + e.z, t.w + e.w);
+    }
     float* pr = (is_q ? part_q : part_k) + (int64_t)blk * D;
-    *(float2*)(pr + 2 * c) = make_float2(((a0.x + a1.x) + a2.x) + a3.x, ((a0.y + a1.y) + a2.y) + a3.y);
-    *(float2*)(pr + HALF + 2 * c) = make_float2(((a0.z + a1.z) + a2.z) + a3.z, ((a0.w + a1.w) + a2.w) + a3.w);
+    *(float2*)(pr + 2 * c) = make_float2(t.x, t.y);
+    *(float2*)(pr + HALF + 2 * c) = make_float2(t.z, t.w);
   }
 }
 
@@ -362,7 +371,7 @@ __global__ void fill_kernel(float* p, int n, float v) {
 
 // Partial rows of the backward with the paired layout (lph > 0) or without.
 int qk_parts(int T, int nh, int lph) {
-  if (lph) return (int)ceil_div(ceil_div((int64_t)T, kQkRows) * ceil_div(nh, 64 / lph), 4);
+  if (lph) return (int)ceil_div(ceil_div((int64_t)T, kQkRows) * ceil_div(nh, 64 / lph), kQkBwdWaves);
   return (int)ceil_div((int64_t)T * nh, 4 * kQkRows);
 }
 
@@ -493,7 +502,8 @@ int qk_norm_rope_backward_partials(const QkRopeBwdArgs& a, float* scratch, Colsu
   float* part_k = scratch + (size_t)pq * d;
   if (lph) {
     launch_pair(lph, [&](auto L) {
-      hipLaunchKernelGGL(qk_rope_bwd_pair_kernel<decltype(L)::value>, dim3((unsigned)(pq + pk)), dim3(256), 0, st,
+      hipLaunchKernelGGL(qk_rope_bwd_pair_kernel<decltype(L)::value>, dim3((unsigned)(pq + pk)),
+                         dim3(64 * kQkBwdWaves), 0, st,
                          a, pq, part_q, part_k);
     });
     QBLK_TRY(check_launch("qk_rope_bwd_pair_kernel"));
