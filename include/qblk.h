@@ -47,7 +47,7 @@ enum {
   QBLK_OK = 0,
   QBLK_EINVAL = -1,      /* bad argument: null pointer, shape, workspace too small */
   QBLK_EHIP = -2,        /* HIP launch or runtime error */
-  QBLK_EUNSUPPORTED = -3 /* valid request this build does not implement */
+  QBLK_EUNSUPPORTED = -3 /* valid request the library does not implement */
 };
 
 /* Shapes of one decoder block ([block] TransformerConfig fields used by
