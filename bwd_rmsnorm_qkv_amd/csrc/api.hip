@@ -87,9 +87,10 @@ int32_t qblk_block_forward(const qblk_config* cfg, const qblk_block_params* p, c
   return dense_block_forward(*cfg, *p, x, y, s, w, S(stream));
 }
 
-int32_t qblk_block_backward(const qblk_config* cfg, const qblk_block_params* p, const float* x, const float* dy,
-                            const void* saved, size_t saved_bytes, float* dx, const qblk_block_grads* grads,
-                            void* scratch, size_t scratch_bytes, qblk_stream_t stream) {
+static int32_t block_backward_common(const qblk_config* cfg, const qblk_block_params* p, const float* x,
+                                     const float* dy, const void* saved, size_t saved_bytes, float* dx,
+                                     const qblk_block_grads* grads, void* scratch, size_t scratch_bytes,
+                                     qblk_stream_t stream, bool accumulate) {
   QBLK_TRY(check_config(cfg));
   QBLK_TRY(check_params(p));
   if (!grads) return fail(QBLK_EINVAL, "block_backward: grads is NULL");
@@ -110,7 +111,22 @@ int32_t qblk_block_backward(const qblk_config* cfg, const qblk_block_params* p, 
     return fail(QBLK_EINVAL, "block_backward: scratch workspace %zu < %zu", scratch_bytes, need_w);
   carve_saved(*cfg, (void*)saved, s, need_s);
   carve_scratch(*cfg, scratch, w, need_w);
-  return dense_block_backward(*cfg, *p, *grads, x, dy, s, dx, w, S(stream));
+  return dense_block_backward(*cfg, *p, *grads, x, dy, s, dx, w, S(stream), accumulate);
+}
+
+int32_t qblk_block_backward(const qblk_config* cfg, const qblk_block_params* p, const float* x, const float* dy,
+                            const void* saved, size_t saved_bytes, float* dx, const qblk_block_grads* grads,
+                            void* scratch, size_t scratch_bytes, qblk_stream_t stream) {
+  return block_backward_common(cfg, p, x, dy, saved, saved_bytes, dx, grads, scratch, scratch_bytes, stream,
+                               false);
+}
+
+int32_t qblk_block_backward_accumulate(const qblk_config* cfg, const qblk_block_params* p, const float* x,
+                                       const float* dy, const void* saved, size_t saved_bytes, float* dx,
+                                       const qblk_block_grads* grads, void* scratch, size_t scratch_bytes,
+                                       qblk_stream_t stream) {
+  return block_backward_common(cfg, p, x, dy, saved, saved_bytes, dx, grads, scratch, scratch_bytes, stream,
+                               true);
 }
 
 // ------------------------------------------------------- cross-entropy

@@ -96,12 +96,14 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
 int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* g_in, const float* g_post,
                         const float* g_q, const float* g_k, const float* x, const float* dy, const Saved& s,
                         float* dx, float* dg_in, float* dg_post, float* dg_q, float* dg_k, const Scratch& w,
-                        hipStream_t st);
+                        hipStream_t st, bool accumulate = false);
 
 int dense_block_forward(const qblk_config& c, const qblk_block_params& p, const float* x, float* y,
                         const Saved& s, const Scratch& w, hipStream_t st);
+// accumulate: the parameter gradients are added into gr (micro-batch
+// accumulation) instead of overwritten; dx is written either way.
 int dense_block_backward(const qblk_config& c, const qblk_block_params& p, const qblk_block_grads& gr,
                          const float* x, const float* dy, const Saved& s, float* dx, const Scratch& w,
-                         hipStream_t st);
+                         hipStream_t st, bool accumulate = false);
 
 }  // namespace qblk

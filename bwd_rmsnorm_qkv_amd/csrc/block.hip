@@ -284,7 +284,7 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
 int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* g_in, const float* g_post,
                         const float* g_q, const float* g_k, const float* x, const float* dy, const Saved& s,
                         float* dx, float* dg_in, float* dg_post, float* dg_q, float* dg_k, const Scratch& w,
-                        hipStream_t st) {
+                        hipStream_t st, bool accumulate) {
   const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
   const int ldqkv = qd + 2 * kvd;
@@ -303,7 +303,7 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
   int nj = 0;
   QBLK_TRY(rmsnorm_backward_partials(T, h, c.eps, s.r1, g_post, w.dn2, dy, w.dr1, p16 ? w.a16 : nullptr, w.red,
                                      st));
-  jobs[nj++] = ColsumJob{rmsnorm_bwd_parts(T, h), h, w.red, dg_post};
+  jobs[nj++] = ColsumJob{rmsnorm_bwd_parts(T, h), h, w.red, dg_post, accumulate};
   // O projection
   QBLK_TRY(proj.o(p16 ? nullptr : w.dr1, s.o, w.d_o, st));
   // attention backward: dq, dk at the attention inputs; dv straight into dqkv
@@ -346,11 +346,12 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
     qb.dqkv = nullptr;
     qb.dqkv16 = w.a16;
   }
+  qb.accumulate_dg = accumulate;
   QBLK_TRY(qk_norm_rope_backward_partials(qb, w.red_qk, jobs, nj, st));
   QBLK_TRY(proj.qkv(qkv16 ? nullptr : w.dqkv, s.n1, w.dn1, st));
   // input norm backward, plus the first residual's gradient dr1
   QBLK_TRY(rmsnorm_backward_partials(T, h, c.eps, x, g_in, w.dn1, w.dr1, dx, nullptr, w.red_in, st));
-  jobs[nj++] = ColsumJob{rmsnorm_bwd_parts(T, h), h, w.red_in, dg_in};
+  jobs[nj++] = ColsumJob{rmsnorm_bwd_parts(T, h), h, w.red_in, dg_in, accumulate};
   return colsum_jobs(nj, jobs, st);
 }
 
@@ -450,7 +451,7 @@ int dense16_forward(const qblk_config& c, const qblk_block_params& p, const floa
 // token-major); dY is cast to fp16 once for both.
 int dense16_backward(const qblk_config& c, const qblk_block_params& p, const qblk_block_grads& gr,
                      const float* x, const float* dy, const Saved& s, float* dx, const Scratch& w,
-                     hipStream_t st) {
+                     hipStream_t st, bool accumulate) {
   const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate, qkv = qd + 2 * kvd;
   Packed16 W;
@@ -464,7 +465,9 @@ int dense16_backward(const qblk_config& c, const qblk_block_params& p, const qbl
     gx.c16 = dx16;
     gx.ldc16 = n_in;
     QBLK_TRY(gemm(gx, s_));
-    return gemm(g16(w, Layout::TN, n_out, n_in, T, w.a16, n_out, x16, n_in, cseg, n_in), s_);
+    GemmDesc gw = g16(w, Layout::TN, n_out, n_in, T, w.a16, n_out, x16, n_in, cseg, n_in);
+    gw.accumulate = accumulate;
+    return gemm(gw, s_);
   };
   ProjBwd pb;
   pb.down = [&](const float* dyv, const float*, float* ds, hipStream_t s_) {
@@ -483,7 +486,7 @@ int dense16_backward(const qblk_config& c, const qblk_block_params& p, const qbl
   Scratch w16 = w;
   w16.prod16 = true;
   return block_backward_impl(c, pb, p.g_in, p.g_post, p.g_q, p.g_k, x, dy, s, dx, gr.g_in, gr.g_post,
-                             gr.g_q, gr.g_k, w16, st);
+                             gr.g_q, gr.g_k, w16, st, accumulate);
 }
 
 }  // namespace
@@ -517,11 +520,11 @@ int dense_block_forward(const qblk_config& c, const qblk_block_params& p, const 
 
 int dense_block_backward(const qblk_config& c, const qblk_block_params& p, const qblk_block_grads& gr,
                          const float* x, const float* dy, const Saved& s, float* dx, const Scratch& w,
-                         hipStream_t st) {
+                         hipStream_t st, bool accumulate) {
   const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
   const Prec pr = prec_of(c);
-  if (use_f16_copies(c)) return dense16_backward(c, p, gr, x, dy, s, dx, w, st);
+  if (use_f16_copies(c)) return dense16_backward(c, p, gr, x, dy, s, dx, w, st, accumulate);
   // dX = dY W (NN, B = W [out, in] with out the contraction) and
   // dW = dY^T X (TN). `wseg` are the weights stacked along out; `cseg` the
   // gradient tensors split the same way.
@@ -542,6 +545,7 @@ int dense_block_backward(const qblk_config& c, const qblk_block_params& p, const
     b.a = dyv; b.lda = n_out;
     b.b = seg1(xin, T); b.ldb = n_in;
     b.c = cseg; b.ldc = n_in;
+    b.accumulate = accumulate;
     return gemm(b, s_);
   };
   ProjBwd proj;
@@ -560,7 +564,7 @@ int dense_block_backward(const qblk_config& c, const qblk_block_params& p, const
                 seg3(gr.w_q, qd, gr.w_k, kvd, gr.w_v, kvd), dn1, s_);
   };
   return block_backward_impl(c, proj, p.g_in, p.g_post, p.g_q, p.g_k, x, dy, s, dx, gr.g_in, gr.g_post,
-                             gr.g_q, gr.g_k, w, st);
+                             gr.g_q, gr.g_k, w, st, accumulate);
 }
 
 }  // namespace qblk

@@ -512,9 +512,9 @@ int qk_norm_rope_backward_partials(const QkRopeBwdArgs& a, float* scratch, Colsu
     QBLK_TRY(check_launch("qk_rope_bwd_kernel"));
   }
   if (a.qk_norm) {
-    jobs[njobs++] = ColsumJob{pq, d, part_q, a.dg_q};
-    jobs[njobs++] = ColsumJob{pk, d, part_k, a.dg_k};
-  } else {
+    jobs[njobs++] = ColsumJob{pq, d, part_q, a.dg_q, a.accumulate_dg};
+    jobs[njobs++] = ColsumJob{pk, d, part_k, a.dg_k, a.accumulate_dg};
+  } else if (!a.accumulate_dg) {
     if (a.dg_q) hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, a.dg_q, d, 0.f);
     if (a.dg_k) hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, a.dg_k, d, 0.f);
     QBLK_TRY(check_launch("fill_kernel"));

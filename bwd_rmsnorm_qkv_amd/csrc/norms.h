@@ -31,6 +31,7 @@ struct ColsumJob {
   int parts, n;
   const float* partial;
   float* out;
+  int accumulate = 0;  // 1: out[c] += the sum
 };
 constexpr int kMaxColsumJobs = 4;
 int colsum_jobs(int njobs, const ColsumJob* jobs, hipStream_t st);
@@ -84,6 +85,7 @@ struct QkRopeBwdArgs {
   float* dqkv;             // [T, ld_qkv] (may be null)
   float *dg_q, *dg_k;
   f16* dqkv16 = nullptr;   // optional fp16 copy of the q and k columns of dqkv
+  int accumulate_dg = 0;   // 1: dg_q, dg_k receive += (and stay as they are without QK-norm)
 };
 size_t qk_norm_rope_bwd_scratch(int T, int heads, int kv_heads, int head_dim);
 int qk_norm_rope_backward(const QkRopeBwdArgs& a, float* scratch, hipStream_t st);

@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_row_kernel(int rows, int n, f
 // p % 16, summed in row order); the group sums are then added in group
 // order, so results are bitwise reproducible.
 __device__ __forceinline__ void colsum_cols(int parts, int n, const float* __restrict__ partial,
-                                            float* __restrict__ out) {
+                                            float* __restrict__ out, int accumulate) {
   __shared__ float red[16][64];
   const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + cl;
@@ -349,13 +349,13 @@ __device__ __forceinline__ void colsum_cols(int parts, int n, const float* __res
     float t = red[0][cl];
 #pragma unroll
     for (int g = 1; g < 16; ++g) t += red[g][cl];
-    out[c] = t;
+    out[c] = accumulate ? out[c] + t : t;
   }
 }
 
 __global__ __launch_bounds__(1024) void colsum_kernel(int parts, int n, const float* __restrict__ partial,
                                                       float* __restrict__ out) {
-  colsum_cols(parts, n, partial, out);
+  colsum_cols(parts, n, partial, out, 0);
 }
 
 // Independent column sums in one launch (blockIdx.y picks the job).
@@ -364,7 +364,7 @@ struct ColsumJobs {
 };
 __global__ __launch_bounds__(1024) void colsum_jobs_kernel(const ColsumJobs jobs) {
   const ColsumJob& j = jobs.j[blockIdx.y];
-  if ((int)blockIdx.x * 64 < j.n) colsum_cols(j.parts, j.n, j.partial, j.out);
+  if ((int)blockIdx.x * 64 < j.n) colsum_cols(j.parts, j.n, j.partial, j.out, j.accumulate);
 }
 
 int vpl_for(int n) {

@@ -64,6 +64,8 @@ _SIGS = {
                             C.c_void_p, C.c_size_t, C.c_void_p], C.c_int32),
     "qblk_block_backward": ([C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                              C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int32),
+    "qblk_block_backward_accumulate": ([C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                        C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int32),
     "qblk_attention_forward_f16": ([C.c_int32] * 5 + [C.c_void_p] * 5 + [C.c_void_p], C.c_int32),
     "qblk_attention_backward_f16": ([C.c_int32] * 5 + [C.c_void_p] * 11 + [C.c_size_t, C.c_void_p], C.c_int32),
     "qblk_block_pack_f16_size": ([C.c_void_p, C.POINTER(C.c_size_t)], C.c_int32),
@@ -203,13 +205,16 @@ def block_forward(cfg, params: dict, x, y, saved, scratch=None, stream=None):
                                     _stream(stream)))
 
 
-def block_backward(cfg, params: dict, x, dy, saved, dx, grads: dict, scratch, stream=None):
+def block_backward(cfg, params: dict, x, dy, saved, dx, grads: dict, scratch, stream=None, accumulate=False):
+    """accumulate: qblk_block_backward_accumulate (parameter gradients added
+    into `grads`) instead of qblk_block_backward (overwritten)."""
     c = _cfg(cfg)
     bp = _params(params)
     gp = BlockGrads(*[_p(grads[n]) for n in PARAMS])
-    _check(lib().qblk_block_backward(C.byref(c), C.byref(bp), _p(x), _p(dy), _p(saved),
-                                     saved.numel() * saved.element_size(), _p(dx), C.byref(gp), _p(scratch),
-                                     scratch.numel() * scratch.element_size(), _stream(stream)))
+    fn = lib().qblk_block_backward_accumulate if accumulate else lib().qblk_block_backward
+    _check(fn(C.byref(c), C.byref(bp), _p(x), _p(dy), _p(saved),
+              saved.numel() * saved.element_size(), _p(dx), C.byref(gp), _p(scratch),
+              scratch.numel() * scratch.element_size(), _stream(stream)))
 
 
 # ----------------------------------------------------------- LM head + CE

@@ -90,9 +90,9 @@ class Block:
                            self.saved if saved is None else saved, self.scratch, stream)
         return self.y if y is None else y
 
-    def backward(self, params, x, dy, grads, saved=None, dx=None, stream=None):
+    def backward(self, params, x, dy, grads, saved=None, dx=None, stream=None, accumulate=False):
         qblk.block_backward(self.c, params, x, dy, self.saved if saved is None else saved,
-                            self.dx if dx is None else dx, grads, self.scratch, stream)
+                            self.dx if dx is None else dx, grads, self.scratch, stream, accumulate)
         return self.dx if dx is None else dx
 
 

@@ -124,6 +124,20 @@ int32_t qblk_block_backward(const qblk_config* cfg, const qblk_block_params* p, 
                             const qblk_block_grads* grads, void* scratch, size_t scratch_bytes,
                             qblk_stream_t stream);
 
+/* The same backward for gradient accumulation over micro-batches ([trainer]
+ * GPU-resident gradient accumulation over the accumulation steps: the
+ * micro-batches' gradients summed on the device before one clip and one
+ * AdamW step): the 11 parameter gradients are added
+ * into `grads` (dW products with beta = 1, gamma column sums added), so
+ * after k calls they hold the sum over the k micro-batches; a call adds
+ * exactly the value qblk_block_backward would write (one fp32 addition per
+ * element). dx is overwritten as in qblk_block_backward. Same arguments,
+ * workspaces and errors. */
+int32_t qblk_block_backward_accumulate(const qblk_config* cfg, const qblk_block_params* p, const float* x,
+                                       const float* dy, const void* saved, size_t saved_bytes, float* dx,
+                                       const qblk_block_grads* grads, void* scratch, size_t scratch_bytes,
+                                       qblk_stream_t stream);
+
 /* Scratch bytes of qblk_fused_cross_entropy (holds the normalised hidden
  * states and the [tokens, vocab] fp32 logits, overwritten by their
  * gradient). */

@@ -122,6 +122,38 @@ def test_block_backward_deterministic():
         assert torch.equal(outs[0][1][k], outs[1][1][k]), k
 
 
+@pytest.mark.parametrize("name", ["small", "small_fp16_t192", "fp16_wide_split", "small_d32_ragged",
+                                  "small_fp16_no_qk_norm"])
+def test_block_backward_accumulate(name):
+    """Two micro-batches through qblk_block_backward_accumulate: every
+    parameter gradient equals, bit for bit, the sum of the two gradients the
+    overwriting backward gives (one fp32 addition per element); dx is the
+    second micro-batch's."""
+    need_gpu()
+    c = CASES[name]
+    announce(f"block backward accumulate {name} T={c.tokens}")
+    inp1, inp2 = synth.block_inputs(c, seed=1), synth.block_inputs(c, seed=2)
+    P = {k: dev(v) for k, v in _gammas_perturbed(inp1["params"], 5).items()}
+    blk = Block(c)
+    if c.gemm_precision == 1:
+        P = blk.pack_f16(P)
+    mb = [(dev(i["x"]), dev(i["dy"])) for i in (inp1, inp2)]
+    single = []
+    for X, DY in mb:
+        blk.forward(P, X)
+        g = {k: empty(v.shape) for k, v in inp1["params"].items()}
+        dx = blk.backward(P, X, DY, g).clone()
+        single.append((dx, g))
+    acc = {k: v.clone() for k, v in single[0][1].items()}
+    X, DY = mb[1]
+    blk.forward(P, X)
+    dx = blk.backward(P, X, DY, acc, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, single[1][0])
+    for k in qblk.PARAMS:
+        assert torch.equal(acc[k], single[0][1][k] + single[1][1][k]), k
+
+
 def test_block_rejects_bad_config():
     need_gpu()
     c = synth.TINY_BLOCK
