@@ -169,11 +169,10 @@ int32_t qblk_cross_entropy_workspace_size(int32_t tokens, int32_t hidden, int32_
   return QBLK_OK;
 }
 
-int32_t qblk_fused_cross_entropy(int32_t tokens, int32_t hidden, int32_t vocab, float eps, const float* y_last,
-                                 const float* g_final, const float* w_lm, const int32_t* targets,
-                                 float loss_scale, float* loss_partials, int32_t* argmax, float* dy_last,
-                                 float* dg_final, float* dw_lm, void* scratch, size_t scratch_bytes,
-                                 qblk_stream_t stream) {
+static int32_t fused_ce_common(int32_t tokens, int32_t hidden, int32_t vocab, float eps, const float* y_last,
+                               const float* g_final, const float* w_lm, const int32_t* targets, float loss_scale,
+                               float* loss_partials, int32_t* argmax, float* dy_last, float* dg_final, float* dw_lm,
+                               void* scratch, size_t scratch_bytes, qblk_stream_t stream, bool accumulate) {
   if (tokens <= 0 || hidden <= 0 || vocab <= 0) return fail(QBLK_EINVAL, "cross_entropy: bad sizes");
   if (hidden % 4 || vocab % 4) return fail(QBLK_EINVAL, "cross_entropy: hidden and vocab must be multiples of 4");
   if (!y_last || !w_lm || !targets || !loss_partials || !dy_last || !dw_lm || !scratch)
@@ -215,10 +214,33 @@ int32_t qblk_fused_cross_entropy(int32_t tokens, int32_t hidden, int32_t vocab, 
   b.a = z; b.lda = vocab;
   b.b = seg1(h_in, tokens); b.ldb = hidden;
   b.c = seg1(dw_lm, vocab); b.ldc = hidden;
+  b.accumulate = accumulate;
   QBLK_TRY(gemm(b, st));
-  if (g_final)
-    QBLK_TRY(rmsnorm_backward(tokens, hidden, eps, y_last, g_final, dhf, nullptr, dy_last, nullptr, dg_final, red, st));
+  if (g_final) {
+    QBLK_TRY(rmsnorm_backward_partials(tokens, hidden, eps, y_last, g_final, dhf, nullptr, dy_last, nullptr, red,
+                                       st));
+    const ColsumJob j{rmsnorm_bwd_parts(tokens, hidden), hidden, red, dg_final, accumulate};
+    QBLK_TRY(colsum_jobs(1, &j, st));
+  }
   return QBLK_OK;
+}
+
+int32_t qblk_fused_cross_entropy(int32_t tokens, int32_t hidden, int32_t vocab, float eps, const float* y_last,
+                                 const float* g_final, const float* w_lm, const int32_t* targets,
+                                 float loss_scale, float* loss_partials, int32_t* argmax, float* dy_last,
+                                 float* dg_final, float* dw_lm, void* scratch, size_t scratch_bytes,
+                                 qblk_stream_t stream) {
+  return fused_ce_common(tokens, hidden, vocab, eps, y_last, g_final, w_lm, targets, loss_scale, loss_partials,
+                         argmax, dy_last, dg_final, dw_lm, scratch, scratch_bytes, stream, false);
+}
+
+int32_t qblk_fused_cross_entropy_accumulate(int32_t tokens, int32_t hidden, int32_t vocab, float eps,
+                                            const float* y_last, const float* g_final, const float* w_lm,
+                                            const int32_t* targets, float loss_scale, float* loss_partials,
+                                            int32_t* argmax, float* dy_last, float* dg_final, float* dw_lm,
+                                            void* scratch, size_t scratch_bytes, qblk_stream_t stream) {
+  return fused_ce_common(tokens, hidden, vocab, eps, y_last, g_final, w_lm, targets, loss_scale, loss_partials,
+                         argmax, dy_last, dg_final, dw_lm, scratch, scratch_bytes, stream, true);
 }
 
 int32_t qblk_cross_entropy_rows(int32_t tokens, int32_t vocab, float* z, const int32_t* targets, float loss_scale,

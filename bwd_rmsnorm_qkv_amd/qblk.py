@@ -74,6 +74,10 @@ _SIGS = {
     "qblk_fused_cross_entropy": ([C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_void_p, C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int32),
+    "qblk_fused_cross_entropy_accumulate": ([C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_void_p, C.c_void_p,
+                                             C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_void_p,
+                                             C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                             C.c_void_p], C.c_int32),
     "qblk_cross_entropy_rows": ([C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_float, C.c_void_p,
                                  C.c_void_p, C.c_void_p], C.c_int32),
     "qblk_clip_workspace_size": ([C.c_int32, C.c_void_p, C.POINTER(C.c_size_t)], C.c_int32),
@@ -226,11 +230,12 @@ def cross_entropy_workspace_size(tokens, hidden, vocab):
 
 
 def fused_cross_entropy(tokens, hidden, vocab, eps, y_last, g_final, w_lm, targets, loss_scale,
-                        loss_partials, argmax, dy_last, dg_final, dw_lm, scratch, stream=None):
-    _check(lib().qblk_fused_cross_entropy(tokens, hidden, vocab, eps, _p(y_last), _p(g_final), _p(w_lm),
-                                          _p(targets), loss_scale, _p(loss_partials), _p(argmax), _p(dy_last),
-                                          _p(dg_final), _p(dw_lm), _p(scratch),
-                                          scratch.numel() * scratch.element_size(), _stream(stream)))
+                        loss_partials, argmax, dy_last, dg_final, dw_lm, scratch, stream=None, accumulate=False):
+    """accumulate: qblk_fused_cross_entropy_accumulate (dw_lm, dg_final added into)."""
+    fn = lib().qblk_fused_cross_entropy_accumulate if accumulate else lib().qblk_fused_cross_entropy
+    _check(fn(tokens, hidden, vocab, eps, _p(y_last), _p(g_final), _p(w_lm), _p(targets), loss_scale,
+              _p(loss_partials), _p(argmax), _p(dy_last), _p(dg_final), _p(dw_lm), _p(scratch),
+              scratch.numel() * scratch.element_size(), _stream(stream)))
 
 
 def cross_entropy_rows(tokens, vocab, z, targets, loss_scale, loss_partials, argmax, stream=None):

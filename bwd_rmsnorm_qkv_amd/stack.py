@@ -20,13 +20,26 @@ from .runtime import FlatParams, block_shapes, byte_buffer, empty
 
 
 class StackStep:
-    def __init__(self, cfg, layers, vocab, adamw=None, max_norm=1.0):
+    """micro_batches = k > 1: the batch is taken as k micro-batches of
+    cfg.batch / k sequences, each run forward and backward with the
+    accumulating backward and cross-entropy (loss scale 1/T of the whole
+    batch), then one clip and one AdamW step ([trainer] GPU-resident
+    gradient accumulation)."""
+
+    def __init__(self, cfg, layers, vocab, adamw=None, max_norm=1.0, micro_batches=1):
         from .synth import ADAMW
+        if micro_batches < 1 or cfg.batch % micro_batches:
+            raise ValueError(f"micro_batches={micro_batches} must divide batch={cfg.batch}")
+        self.full = cfg
+        self.k = micro_batches
+        cfg = cfg.with_tokens(seq=cfg.seq, batch=cfg.batch // micro_batches)
         self.cfg, self.L, self.V = cfg, layers, vocab
         self.hp = dict(ADAMW if adamw is None else adamw)
         self.max_norm = max_norm
         self.c = qblk.make_config(cfg)
         T, h = cfg.tokens, cfg.hidden
+        self.x_all = empty((micro_batches, T, h))
+        self.targets_all = torch.zeros((micro_batches, T), dtype=torch.int32, device="cuda")
         shapes = []
         for l in range(layers):
             shapes += block_shapes(cfg, prefix=f"{l}.")
@@ -44,7 +57,7 @@ class StackStep:
         self.targets = torch.zeros(T, dtype=torch.int32, device="cuda")
         self.loss_partials = empty(T)
         self.argmax = torch.empty(T, dtype=torch.int32, device="cuda")
-        self.loss_host = torch.empty(T, dtype=torch.float32, pin_memory=True)
+        self.loss_host = torch.empty(micro_batches * T, dtype=torch.float32, pin_memory=True)
         self.norm = empty(1)
         self.scale = empty(1)
         self.clip_scratch = byte_buffer(qblk.clip_workspace_size([self.g.buf]))
@@ -54,8 +67,11 @@ class StackStep:
         for l, p in enumerate(inp["layers"]):
             self.w.load({f"{l}.{n}": p[n] for n in PARAMS})
         self.w.load({"g_final": inp["g_final"], "w_lm": inp["w_lm"]})
-        self.acts[0].copy_(torch.from_numpy(inp["x"] if x is None else x))
-        self.targets.copy_(torch.from_numpy(inp["targets"]))
+        T = self.cfg.tokens
+        self.x_all.copy_(torch.from_numpy(inp["x"] if x is None else x).reshape(self.k, T, -1))
+        self.targets_all.copy_(torch.from_numpy(inp["targets"]).reshape(self.k, T))
+        self.acts[0].copy_(self.x_all[0])
+        self.targets.copy_(self.targets_all[0])
         self.m.buf.zero_()
         self.v.buf.zero_()
         self.t = 0
@@ -67,19 +83,25 @@ class StackStep:
         """Forward, loss, backward, global clip and AdamW; returns the loss
         (the host sum of the partials) lazily as a callable."""
         cfg, T, h, V = self.cfg, self.cfg.tokens, self.cfg.hidden, self.V
-        for l in range(self.L):
-            qblk.block_forward(self.c, self._layer(self.w, l), self.acts[l], self.acts[l + 1],
-                               self.saved[l], self.scratch)
-        qblk.fused_cross_entropy(T, h, V, cfg.eps, self.acts[self.L], self.w["g_final"], self.w["w_lm"],
-                                 self.targets, 1.0 / T, self.loss_partials, self.argmax, self.dh[0],
-                                 self.g["g_final"], self.g["w_lm"], self.ce_scratch)
-        self.loss_host.copy_(self.loss_partials, non_blocking=True)
-        cur = 0
-        for l in range(self.L - 1, -1, -1):
-            qblk.block_backward(self.c, self._layer(self.w, l), self.acts[l], self.dh[cur], self.saved[l],
-                                self.dh[cur ^ 1], self._layer(self.g, l), self.scratch)
-            cur ^= 1
-        self.dx = self.dh[cur]
+        for mb in range(self.k):
+            acc = mb > 0
+            if self.k > 1:
+                self.acts[0].copy_(self.x_all[mb])
+                self.targets.copy_(self.targets_all[mb])
+            for l in range(self.L):
+                qblk.block_forward(self.c, self._layer(self.w, l), self.acts[l], self.acts[l + 1],
+                                   self.saved[l], self.scratch)
+            qblk.fused_cross_entropy(T, h, V, cfg.eps, self.acts[self.L], self.w["g_final"], self.w["w_lm"],
+                                     self.targets, 1.0 / (T * self.k), self.loss_partials, self.argmax,
+                                     self.dh[0], self.g["g_final"], self.g["w_lm"], self.ce_scratch,
+                                     accumulate=acc)
+            self.loss_host[mb * T:(mb + 1) * T].copy_(self.loss_partials, non_blocking=True)
+            cur = 0
+            for l in range(self.L - 1, -1, -1):
+                qblk.block_backward(self.c, self._layer(self.w, l), self.acts[l], self.dh[cur], self.saved[l],
+                                    self.dh[cur ^ 1], self._layer(self.g, l), self.scratch, accumulate=acc)
+                cur ^= 1
+            self.dx = self.dh[cur]
         qblk.clip_grad_norm([self.g.buf], self.max_norm, 0, self.norm, self.scale, self.clip_scratch)
         self.t += 1
         hp = self.hp
@@ -88,4 +110,4 @@ class StackStep:
 
     def loss(self):
         torch.cuda.current_stream().synchronize()
-        return float(np.sum(self.loss_host.numpy().astype(np.float64))) / self.cfg.tokens
+        return float(np.sum(self.loss_host.numpy().astype(np.float64))) / self.full.tokens

@@ -161,6 +161,17 @@ int32_t qblk_fused_cross_entropy(int32_t tokens, int32_t hidden, int32_t vocab, 
                                  int32_t* argmax, float* dy_last, float* dg_final, float* dw_lm,
                                  void* scratch, size_t scratch_bytes, qblk_stream_t stream);
 
+/* The same for gradient accumulation over micro-batches: dw_lm and
+ * dg_final are added into (dz^T hf and the gamma column sum added with one
+ * fp32 addition per element); loss_partials, argmax and dy_last are written
+ * as above. With loss_scale = 1 / (all micro-batches' tokens) the sums over
+ * the micro-batches are the gradients of the whole batch's mean loss. */
+int32_t qblk_fused_cross_entropy_accumulate(int32_t tokens, int32_t hidden, int32_t vocab, float eps,
+                                            const float* y_last, const float* g_final, const float* w_lm,
+                                            const int32_t* targets, float loss_scale, float* loss_partials,
+                                            int32_t* argmax, float* dy_last, float* dg_final, float* dw_lm,
+                                            void* scratch, size_t scratch_bytes, qblk_stream_t stream);
+
 /* Scratch bytes of qblk_clip_grad_norm for n tensors (numel: host array). */
 int32_t qblk_clip_workspace_size(int32_t n, const int64_t* numel, size_t* scratch_bytes);
 

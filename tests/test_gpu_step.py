@@ -186,3 +186,27 @@ def test_stack36_train_step(stack_case):
     agree = float(np.mean(st.argmax.cpu().numpy() == ref["argmax"]))
     announce(f"  worst grad err {worst:.2e}; argmax agreement {agree:.4f}; "
              f"excluded {sum(v[1] for v in rep.values())} near-zero-gradient weights")
+
+
+def test_stack_micro_batches():
+    """A batch of 4 sequences as 1, 2 and 4 micro-batches (accumulating
+    backward and cross-entropy, one clip and AdamW): the loss, the
+    gradient norm and every gradient agree (only the order of the token sums
+    differs)."""
+    need_gpu()
+    from bwd_rmsnorm_qkv_amd.stack import StackStep
+    c = synth.STACK36_SMALL.with_tokens(seq=128, batch=4)
+    layers, vocab = 2, 2048
+    inp = synth.stack_inputs(c, layers=layers, vocab=vocab, seed=3)
+    out = []
+    for k in (1, 2, 4):
+        announce(f"stack micro-batches k={k}")
+        st = StackStep(c, layers, vocab, micro_batches=k)
+        st.load(inp)
+        st.step()
+        out.append((st.loss(), st.norm.item(), st.g.buf.clone(), st.w.buf.clone()))
+    loss0, norm0, g0, w0 = out[0]
+    for k, (loss, norm, g, w) in zip((2, 4), out[1:]):
+        assert abs(loss - loss0) <= 1e-5 * abs(loss0), (k, loss, loss0)
+        assert abs(norm - norm0) <= FP32_TOL * norm0, (k, norm, norm0)
+        check(f"grads k={k}", g, g0.cpu().numpy().astype(np.float64), FP32_TOL)
