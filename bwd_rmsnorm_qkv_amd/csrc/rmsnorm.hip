@@ -330,25 +330,29 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_row_kernel(int rows, int n, f
   }
 }
 
-// 64 columns per workgroup, 16 row groups per column (row p goes to group
-// p % 16, summed in row order); the group sums are then added in group
-// order, so results are bitwise reproducible.
+// Column sums of partial rows: cw columns per workgroup and 1024 / cw row
+// groups per column (row p goes to group p % groups, summed in row order);
+// the group sums are then added in group order, so results are bitwise
+// reproducible. Narrow sums (n <= 256: the QK gammas, whose partial rows
+// are many) take 16 columns and 64 groups, the rest 64 and 16.
+__host__ __device__ __forceinline__ int colsum_width(int n) { return n <= 256 ? 16 : 64; }
+
 __device__ __forceinline__ void colsum_cols(int parts, int n, const float* __restrict__ partial,
                                             float* __restrict__ out, int accumulate) {
-  __shared__ float red[16][64];
-  const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
-  const int c = blockIdx.x * 64 + cl;
+  __shared__ float red[1024];
+  const int cw = colsum_width(n), ng = 1024 / cw;
+  const int cl = threadIdx.x % cw, rg = threadIdx.x / cw;
+  const int c = blockIdx.x * cw + cl;
   float s = 0.f;
   if (c < n) {
 #pragma unroll 8
-    for (int p = rg; p < parts; p += 16) s += partial[(int64_t)p * n + c];
+    for (int p = rg; p < parts; p += ng) s += partial[(int64_t)p * n + c];
   }
-  red[rg][cl] = s;
+  red[rg * cw + cl] = s;
   __syncthreads();
   if (rg == 0 && c < n) {
-    float t = red[0][cl];
-#pragma unroll
-    for (int g = 1; g < 16; ++g) t += red[g][cl];
+    float t = red[cl];
+    for (int g = 1; g < ng; ++g) t += red[g * cw + cl];
     out[c] = accumulate ? out[c] + t : t;
   }
 }
@@ -364,7 +368,7 @@ struct ColsumJobs {
 };
 __global__ __launch_bounds__(1024) void colsum_jobs_kernel(const ColsumJobs jobs) {
   const ColsumJob& j = jobs.j[blockIdx.y];
-  if ((int)blockIdx.x * 64 < j.n) colsum_cols(j.parts, j.n, j.partial, j.out, j.accumulate);
+  if ((int)blockIdx.x * colsum_width(j.n) < j.n) colsum_cols(j.parts, j.n, j.partial, j.out, j.accumulate);
 }
 
 int vpl_for(int n) {
@@ -468,17 +472,17 @@ int rmsnorm_backward_partials(int rows, int n, float eps, const float* x, const 
 int colsum_jobs(int njobs, const ColsumJob* jobs, hipStream_t st) {
   if (njobs <= 0 || njobs > kMaxColsumJobs) return fail(QBLK_EINVAL, "colsum: %d jobs", njobs);
   ColsumJobs js{};
-  int n = 0;
+  int64_t nb = 0;
   for (int i = 0; i < njobs; ++i) {
     js.j[i] = jobs[i];
-    n = std::max(n, jobs[i].n);
+    nb = std::max<int64_t>(nb, ceil_div(jobs[i].n, colsum_width(jobs[i].n)));
   }
-  hipLaunchKernelGGL(colsum_jobs_kernel, dim3((unsigned)ceil_div(n, 64), (unsigned)njobs), dim3(1024), 0, st, js);
+  hipLaunchKernelGGL(colsum_jobs_kernel, dim3((unsigned)nb, (unsigned)njobs), dim3(1024), 0, st, js);
   return check_launch("colsum_jobs_kernel");
 }
 
 int colsum(int parts, int n, const float* partial, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)ceil_div(n, 64)), dim3(1024), 0, st, parts, n,
+  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)ceil_div(n, colsum_width(n))), dim3(1024), 0, st, parts, n,
                      partial, out);
   return check_launch("colsum_kernel");
 }
