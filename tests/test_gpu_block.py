@@ -126,14 +126,17 @@ def test_block_backward_deterministic():
                                   "small_fp16_no_qk_norm"])
 def test_block_backward_accumulate(name):
     """Two micro-batches through qblk_block_backward_accumulate: every
-    parameter gradient equals, bit for bit, the sum of the two gradients the
-    overwriting backward gives (one fp32 addition per element); dx is the
-    second micro-batch's."""
+    parameter gradient matches the sum of the oracle's gradients of the two
+    micro-batches (the tolerance of the configuration), and equals, bit for
+    bit, the sum of the two gradients the overwriting backward gives (one
+    fp32 addition per element); dx is the second micro-batch's and matches
+    the oracle's."""
     need_gpu()
     c = CASES[name]
     announce(f"block backward accumulate {name} T={c.tokens}")
     inp1, inp2 = synth.block_inputs(c, seed=1), synth.block_inputs(c, seed=2)
-    P = {k: dev(v) for k, v in _gammas_perturbed(inp1["params"], 5).items()}
+    params = _gammas_perturbed(inp1["params"], 5)
+    P = {k: dev(v) for k, v in params.items()}
     blk = Block(c)
     if c.gemm_precision == 1:
         P = blk.pack_f16(P)
@@ -152,6 +155,17 @@ def test_block_backward_accumulate(name):
     assert torch.equal(dx, single[1][0])
     for k in qblk.PARAMS:
         assert torch.equal(acc[k], single[0][1][k] + single[1][1][k]), k
+    ref, dx_ref = None, None
+    for i in (inp1, inp2):
+        _, cache = oracle.block_forward(c, params, i["x"])
+        dx_ref, g = oracle.block_backward(c, params, cache, i["dy"])
+        ref = g if ref is None else {k: ref[k] + g[k] for k in ref}
+    tol = FP16_TOL if c.gemm_precision else FP32_TOL
+    rep = {}
+    check("dx", dx, dx_ref, tol, rep)
+    for k in qblk.PARAMS:
+        check("sum d" + k, acc[k], ref[k], tol, rep)
+    announce("  " + " ".join(f"{k}={v:.1e}" for k, v in rep.items()))
 
 
 def test_block_rejects_bad_config():

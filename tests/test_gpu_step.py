@@ -190,23 +190,39 @@ def test_stack36_train_step(stack_case):
 
 def test_stack_micro_batches():
     """A batch of 4 sequences as 1, 2 and 4 micro-batches (accumulating
-    backward and cross-entropy, one clip and AdamW): the loss, the
-    gradient norm and every gradient agree (only the order of the token sums
-    differs)."""
+    backward and cross-entropy, one clip and AdamW) against oracle.stack_step
+    on the whole 4-sequence batch: loss, gradient norm, clip scale, every
+    gradient, the updated weights (first-step sign rule) and moments; the
+    three runs also agree with each other."""
     need_gpu()
     from bwd_rmsnorm_qkv_amd.stack import StackStep
     c = synth.STACK36_SMALL.with_tokens(seq=128, batch=4)
     layers, vocab = 2, 2048
     inp = synth.stack_inputs(c, layers=layers, vocab=vocab, seed=3)
+    ref = oracle.stack_step(c, inp["layers"], inp["x"], inp["g_final"], inp["w_lm"], inp["targets"],
+                            synth.CLIP_MAX_NORM, synth.ADAMW)
+    names = [f"{l}.{n}" for l in range(layers) for n in qblk.PARAMS] + ["g_final", "w_lm"]
     out = []
     for k in (1, 2, 4):
         announce(f"stack micro-batches k={k}")
         st = StackStep(c, layers, vocab, micro_batches=k)
         st.load(inp)
         st.step()
-        out.append((st.loss(), st.norm.item(), st.g.buf.clone(), st.w.buf.clone()))
-    loss0, norm0, g0, w0 = out[0]
-    for k, (loss, norm, g, w) in zip((2, 4), out[1:]):
+        loss = st.loss()
+        assert abs(loss - ref["loss"]) <= 1e-5 * abs(ref["loss"]), (k, loss, ref["loss"])
+        assert abs(st.norm.item() - ref["norm"]) <= FP32_TOL * ref["norm"], (k, st.norm.item(), ref["norm"])
+        assert abs(st.scale.item() - ref["scale"]) <= FP32_TOL * ref["scale"]
+        rep, worst = {}, 0.0
+        for i, n in enumerate(names):
+            worst = max(worst, check(f"k={k} g_{n}", st.g[n], ref["grads"][i], FP32_TOL))
+            _adamw_weight_check(f"k={k} w_{n}", st.w[n], ref["new_w"][i], ref["grads"][i] * ref["scale"], rep)
+            check(f"k={k} m_{n}", st.m[n], ref["new_m"][i], FP32_TOL)
+            check(f"k={k} v_{n}", st.v[n], ref["new_v"][i], FP32_TOL)
+        announce(f"  k={k}: loss {loss:.6f} (ref {ref['loss']:.6f}), worst grad err {worst:.2e}, "
+                 f"excluded {sum(v[1] for v in rep.values())} near-zero-gradient weights")
+        out.append((loss, st.norm.item(), st.g.buf.clone()))
+    loss0, norm0, g0 = out[0]
+    for k, (loss, norm, g) in zip((2, 4), out[1:]):
         assert abs(loss - loss0) <= 1e-5 * abs(loss0), (k, loss, loss0)
         assert abs(norm - norm0) <= FP32_TOL * norm0, (k, norm, norm0)
-        check(f"grads k={k}", g, g0.cpu().numpy().astype(np.float64), FP32_TOL)
+        check(f"grads k={k} vs k=1", g, g0.cpu().numpy().astype(np.float64), FP32_TOL)

@@ -247,13 +247,12 @@ def test_swiglu_closed_forms_and_fd(rng):
 
 # -------------------------------------------------------------------- Block
 
-def _torch_block_loss(c, p, x, dy):
+def _torch_block(c, tp, tx, linear=None):
     """The block written with torch library routines (rms_norm, linear, SDPA,
-    silu) in float64; autograd supplies the derivatives independently of the
-    oracle's hand-written backward."""
-    t = lambda a: torch.tensor(np.asarray(a, np.float64), requires_grad=True)
-    tp = {n: t(p[n]) for n in PARAM_NAMES}
-    tx = t(x)
+    silu) on torch float64 tensors; autograd supplies the derivatives
+    independently of the oracle's hand-written backward. ``linear(name, a)``
+    replaces ``F.linear(a, tp[name])`` (the NF4 + LoRA block uses it)."""
+    lin = linear or (lambda name, a: F.linear(a, tp[name]))
     T, H, KV, d = c.tokens, c.heads, c.kv_heads, c.head_dim
     pos = torch.tensor(positions(c.seq, c.batch), dtype=torch.float64)
     inv = c.rope_theta ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
@@ -266,9 +265,9 @@ def _torch_block_loss(c, p, x, dy):
         return torch.cat([a0 * cos - a1 * sin, a1 * cos + a0 * sin], -1)
 
     n1 = F.rms_norm(tx, (c.hidden,), tp["g_in"], eps=c.eps)
-    q = F.linear(n1, tp["w_q"]).reshape(T, H, d)
-    k = F.linear(n1, tp["w_k"]).reshape(T, KV, d)
-    v = F.linear(n1, tp["w_v"]).reshape(T, KV, d)
+    q = lin("w_q", n1).reshape(T, H, d)
+    k = lin("w_k", n1).reshape(T, KV, d)
+    v = lin("w_v", n1).reshape(T, KV, d)
     q = F.rms_norm(q, (d,), tp["g_q"], eps=c.eps)
     k = F.rms_norm(k, (d,), tp["g_k"], eps=c.eps)
     q, k = rope(q, H), rope(k, KV)
@@ -277,10 +276,22 @@ def _torch_block_loss(c, p, x, dy):
     vb = v.reshape(c.batch, c.seq, KV, d).transpose(1, 2).repeat_interleave(H // KV, 1)
     o = F.scaled_dot_product_attention(qb, kb, vb, is_causal=True)
     o = o.transpose(1, 2).reshape(T, H * d)
-    r1 = tx + F.linear(o, tp["w_o"])
+    r1 = tx + lin("w_o", o)
     n2 = F.rms_norm(r1, (c.hidden,), tp["g_post"], eps=c.eps)
-    s = F.silu(F.linear(n2, tp["w_gate"])) * F.linear(n2, tp["w_up"])
-    y = r1 + F.linear(s, tp["w_down"])
+    s = F.silu(lin("w_gate", n2)) * lin("w_up", n2)
+    return r1 + lin("w_down", s)
+
+
+def _leaf(a):
+    return torch.tensor(np.asarray(a, np.float64), requires_grad=True)
+
+
+def _torch_block_loss(c, p, x, dy):
+    """y, dx and the 11 parameter gradients of L = sum(y * dy) by autograd
+    through ``_torch_block``."""
+    tp = {n: _leaf(p[n]) for n in PARAM_NAMES}
+    tx = _leaf(x)
+    y = _torch_block(c, tp, tx)
     (y * torch.tensor(dy, dtype=torch.float64)).sum().backward()
     return y.detach().numpy(), tx.grad.numpy(), {n: tp[n].grad.numpy() for n in PARAM_NAMES}
 
@@ -553,3 +564,177 @@ def test_nf4_block_reduces_to_block_when_b_is_zero(rng):
     for n in synth.PROJ_NAMES:
         assert np.all(da[n] == 0.0)
         assert np.any(db[n] != 0.0)
+
+
+def test_nf4_block_lora_matches_torch_autograd(rng):
+    """B != 0 (every LoRA branch live): the NF4 block's output, dx and the 14
+    LoRA gradients against torch autograd through the torch block with
+    F.linear(x, W~) + s * F.linear(F.linear(x, A), B) as each projection,
+    on the oracle's dequantized base weights; then central differences of
+    L = sum(y * dy) along random directions of dA and dB per projection."""
+    c = synth.TINY_BLOCK.with_tokens(seq=11, batch=2)
+    inp = synth.nf4_lora_inputs(c, rank=4, b_std=1e-2, seed=5)
+    scale = 2.0
+    deq = {}
+    for n in synth.PROJ_NAMES:
+        packed, scales, _ = oracle.nf4_quantize(inp["params"][n])
+        deq[n] = oracle.nf4_dequantize(packed, scales, inp["params"][n].shape)
+    gam = {n: (1.0 + 0.3 * rng.standard_normal(inp["params"][n].shape)).astype(np.float32)
+           for n in ("g_in", "g_post", "g_q", "g_k")}
+    y, cache = oracle.nf4_block_forward(c, gam, deq, inp["lora_a"], inp["lora_b"], inp["x"], scale)
+    dx, da, db = oracle.nf4_block_backward(c, gam, deq, inp["lora_a"], inp["lora_b"], cache, inp["dy"], scale)
+
+    ta = {n: _leaf(inp["lora_a"][n]) for n in synth.PROJ_NAMES}
+    tb = {n: _leaf(inp["lora_b"][n]) for n in synth.PROJ_NAMES}
+    tw = {n: torch.tensor(deq[n]) for n in synth.PROJ_NAMES}
+    tp = {n: torch.tensor(np.asarray(gam[n], np.float64)) for n in gam}
+    tx = _leaf(inp["x"])
+    lin = lambda name, a: F.linear(a, tw[name]) + scale * F.linear(F.linear(a, ta[name]), tb[name])
+    ty = _torch_block(c, tp, tx, linear=lin)
+    (ty * torch.tensor(inp["dy"], dtype=torch.float64)).sum().backward()
+    np.testing.assert_allclose(y, ty.detach().numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dx, tx.grad.numpy(), rtol=1e-9, atol=1e-12)
+    for n in synth.PROJ_NAMES:
+        assert np.max(np.abs(da[n])) > 0 and np.max(np.abs(db[n])) > 0, n
+        np.testing.assert_allclose(da[n], ta[n].grad.numpy(), rtol=1e-9, atol=1e-13, err_msg=n)
+        np.testing.assert_allclose(db[n], tb[n].grad.numpy(), rtol=1e-9, atol=1e-13, err_msg=n)
+
+    x64, dy64 = inp["x"].astype(np.float64), inp["dy"].astype(np.float64)
+
+    def loss(a_over=None, b_over=None):
+        la = dict(inp["lora_a"], **(a_over or {}))
+        lb = dict(inp["lora_b"], **(b_over or {}))
+        return float(np.sum(oracle.nf4_block_forward(c, gam, deq, la, lb, x64, scale)[0] * dy64))
+
+    for n in synth.PROJ_NAMES:
+        for base, g, which in ((inp["lora_a"][n], da[n], "a"), (inp["lora_b"][n], db[n], "b")):
+            base = base.astype(np.float64)
+            v = rng.standard_normal(base.shape)
+            h = 1e-4 * float(np.max(np.abs(base)))
+            f = (lambda t: loss(a_over={n: t})) if which == "a" else (lambda t: loss(b_over={n: t}))
+            num = fd_directional(f, base, v, h)
+            ana = float(np.sum(g * v))
+            assert abs(num - ana) <= 1e-6 * max(1e-3, abs(ana)), (n, which, num, ana)
+
+
+# ------------------------------------------------------------- stack step
+
+def _tiny_stack():
+    c = synth.TINY_BLOCK.with_tokens(seq=9, batch=2)
+    inp = synth.stack_inputs(c, layers=2, vocab=37, seed=7)
+    rng = np.random.default_rng(71)
+    for p in inp["layers"]:
+        for n in ("g_in", "g_post", "g_q", "g_k"):
+            p[n] = (1.0 + 0.2 * rng.standard_normal(p[n].shape)).astype(np.float32)
+    inp["g_final"] = (1.0 + 0.2 * rng.standard_normal(c.hidden)).astype(np.float32)
+    return c, inp
+
+
+def test_stack_step_matches_torch():
+    """oracle.stack_step on a 2-layer stack (vocab 37, two sequences of 9)
+    against torch float64: autograd through two torch blocks, the final
+    F.rms_norm, F.linear and mean F.cross_entropy; the global norm from
+    torch.nn.utils.clip_grad_norm_ (clipping active: the norm is above
+    max_norm); then one torch.optim.AdamW step on every tensor with the
+    clipped gradients. Checks the loss, partials, every gradient in the
+    flat order (layers' 11 tensors, then g_final, then W_lm), norm, scale,
+    dx and the updated weights and moments."""
+    c, inp = _tiny_stack()
+    max_norm = 0.05
+    hp = synth.ADAMW
+    ref = oracle.stack_step(c, inp["layers"], inp["x"], inp["g_final"], inp["w_lm"], inp["targets"],
+                            max_norm, hp)
+    tl = [{n: _leaf(p[n]) for n in PARAM_NAMES} for p in inp["layers"]]
+    tgf, twl, tx = _leaf(inp["g_final"]), _leaf(inp["w_lm"]), _leaf(inp["x"])
+    h = tx
+    for tp in tl:
+        h = _torch_block(c, tp, h)
+    z = F.linear(F.rms_norm(h, (c.hidden,), tgf, eps=c.eps), twl)
+    tgt = torch.tensor(inp["targets"], dtype=torch.int64)
+    loss = F.cross_entropy(z, tgt)
+    loss.backward()
+    partials = F.cross_entropy(z.detach(), tgt, reduction="none").numpy()
+    params = [tp[n] for tp in tl for n in PARAM_NAMES] + [tgf, twl]
+    np.testing.assert_allclose(ref["loss"], loss.item(), rtol=1e-12)
+    np.testing.assert_allclose(ref["loss_partials"], partials, rtol=1e-12)
+    np.testing.assert_allclose(ref["dx"], tx.grad.numpy(), rtol=1e-9, atol=1e-13)
+    assert len(ref["grads"]) == len(params)
+    for i, (g, prm) in enumerate(zip(ref["grads"], params)):
+        np.testing.assert_allclose(g, prm.grad.numpy(), rtol=1e-9, atol=1e-13, err_msg=str(i))
+    tnorm = torch.nn.utils.clip_grad_norm_(params, max_norm).item()
+    np.testing.assert_allclose(ref["norm"], tnorm, rtol=1e-13)
+    assert tnorm > max_norm
+    np.testing.assert_allclose(ref["scale"], max_norm / tnorm, rtol=1e-13)
+    # torch scales by max_norm / (norm + 1e-6): undo that, apply the exact scale
+    for g, prm in zip(ref["grads"], params):
+        prm.grad = torch.tensor(np.asarray(g, np.float64) * (max_norm / tnorm))
+    opt = torch.optim.AdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["weight_decay"])
+    opt.step()
+    for i, prm in enumerate(params):
+        st = opt.state[prm]
+        np.testing.assert_allclose(ref["new_w"][i], prm.detach().numpy(), rtol=1e-13, atol=1e-16, err_msg=str(i))
+        np.testing.assert_allclose(ref["new_m"][i], st["exp_avg"].numpy(), rtol=1e-12, atol=1e-18, err_msg=str(i))
+        np.testing.assert_allclose(ref["new_v"][i], st["exp_avg_sq"].numpy(), rtol=1e-12, atol=1e-22,
+                                   err_msg=str(i))
+
+
+def test_stack_step_finite_differences():
+    """Central differences of the stack's mean cross-entropy (forward only:
+    the blocks, final norm, LM head and log-sum-exp) along a random direction
+    of x and at single W_lm elements, against oracle.stack_step's dx and
+    W_lm gradient."""
+    c, inp = _tiny_stack()
+    ref = oracle.stack_step(c, inp["layers"], inp["x"], inp["g_final"], inp["w_lm"], inp["targets"],
+                            1.0, synth.ADAMW)
+    rng = np.random.default_rng(72)
+    x64, wl64 = inp["x"].astype(np.float64), inp["w_lm"].astype(np.float64)
+
+    def loss(x, wl):
+        h = x
+        for p in inp["layers"]:
+            h = block_forward(c, p, h)[0]
+        return oracle.lm_head_cross_entropy(h, inp["g_final"], wl, inp["targets"], c.eps)["loss"]
+
+    v = rng.standard_normal(x64.shape)
+    num = fd_directional(lambda t: loss(t, wl64), x64, v, 1e-6)
+    ana = float(np.sum(ref["dx"] * v))
+    assert abs(num - ana) <= 1e-7 * max(1e-3, abs(ana)), (num, ana)
+    dwl = ref["grads"][-1]
+    for (i, j) in ((int(inp["targets"][0]), 3), (5, 17), (36, 63)):
+        e = np.zeros_like(wl64)
+        e[i, j] = 1.0
+        num = fd_directional(lambda t: loss(x64, t), wl64, e, 1e-5)
+        assert abs(num - dwl[i, j]) <= 1e-7 * max(1e-3, abs(num)), (i, j, num, dwl[i, j])
+
+
+def test_gradient_of_whole_batch_is_sum_over_micro_batches():
+    """The reading behind gradient accumulation: with the loss scale 1/T of
+    the whole batch, the stack's gradients summed over two micro-batches of
+    one sequence each equal the gradients of the two-sequence batch (the
+    blocks see each sequence independently)."""
+    c, inp = _tiny_stack()
+    T = c.tokens
+    whole = oracle.stack_step(c, inp["layers"], inp["x"], inp["g_final"], inp["w_lm"], inp["targets"],
+                              1.0, synth.ADAMW)
+    c1 = c.with_tokens(seq=c.seq, batch=1)
+    acc = None
+    for mb in range(2):
+        sl = slice(mb * c.seq, (mb + 1) * c.seq)
+        h = inp["x"][sl].astype(np.float64)
+        caches = []
+        for p in inp["layers"]:
+            h, ch = block_forward(c1, p, h)
+            caches.append(ch)
+        ce = oracle.lm_head_cross_entropy(h, inp["g_final"], inp["w_lm"], inp["targets"][sl], c.eps,
+                                          loss_scale=1.0 / T)
+        dh, flat = ce["dy_last"], []
+        per_layer = [None] * len(inp["layers"])
+        for li in range(len(inp["layers"]) - 1, -1, -1):
+            dh, per_layer[li] = block_backward(c1, inp["layers"][li], caches[li], dh)
+        for g in per_layer:
+            flat += [g[n] for n in PARAM_NAMES]
+        flat += [ce["dg_final"], ce["dw_lm"]]
+        acc = flat if acc is None else [a + b for a, b in zip(acc, flat)]
+    for i, (a, b) in enumerate(zip(acc, whole["grads"])):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-15, err_msg=str(i))
