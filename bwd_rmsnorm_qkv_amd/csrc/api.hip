@@ -271,6 +271,21 @@ int32_t qblk_clip_grad_norm(int32_t n, float* const* grads, const int64_t* numel
   return clip_grad_norm(n, grads, numel, max_norm, apply, norm_dev, scale_dev, scratch, S(stream));
 }
 
+int32_t qblk_clip_grad_norm_noalloc(int32_t n, float* const* grads, const int64_t* numel, float max_norm,
+                                    int32_t apply, float* norm_dev, float* scale_dev, qblk_stream_t stream) {
+  if (n <= 0 || !grads || !numel || !norm_dev || !scale_dev)
+    return fail(QBLK_EINVAL, "clip (no workspace): null argument or n <= 0");
+  if (!(max_norm > 0.f)) return fail(QBLK_EINVAL, "clip (no workspace): max_norm must be positive");
+  for (int i = 0; i < n; ++i)
+    if (!grads[i] || numel[i] < 0) return fail(QBLK_EINVAL, "clip (no workspace): tensor %d", i);
+  if (clip_scratch(n, numel) > static_clip_scratch_bytes())
+    return fail(QBLK_EINVAL, "clip (no workspace): %d tensors exceed the limit of %d", n,
+                QBLK_CLIP_NOALLOC_MAX_TENSORS);
+  void* ws = nullptr;
+  QBLK_TRY(static_clip_scratch(&ws));
+  return clip_grad_norm(n, grads, numel, max_norm, apply, norm_dev, scale_dev, ws, S(stream));
+}
+
 int32_t qblk_adamw_step(int32_t n, float* const* w, const float* const* g, float* const* m, float* const* v,
                         const int64_t* numel, float lr, float beta1, float beta2, float eps, float weight_decay,
                         int32_t step, const float* grad_scale_dev, qblk_stream_t stream) {

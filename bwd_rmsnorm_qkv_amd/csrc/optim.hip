@@ -15,6 +15,7 @@
 // bitwise reproducible.
 #include "step.h"
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/qblk.h"
@@ -241,6 +242,38 @@ int clip_grad_norm(int n, float* const* g, const int64_t* numel, float max_norm,
   }
   return 0;
 }
+
+// ------------------------------------------ the clip without a workspace
+// For callers that cannot allocate (graph capture, tight loops): the
+// squared-sum partials live in a file-scope device array, one copy per GPU,
+// whose address is looked up once per device with that device current.
+// In host code `scratch` names a host-side stand-in, never device memory:
+// only the looked-up pointer is passed to kernels.
+constexpr int kStaticClipChunks = 64;  // 2048 tensors
+static __device__ __align__(256) double scratch[kStaticClipChunks * kSqGrid];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices] = {};
+}  // namespace
+
+int static_clip_scratch(void** out) {
+  int dev = 0;
+  QBLK_TRY(check_hip(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(QBLK_EUNSUPPORTED, "clip (no workspace): device %d", dev);
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* p = nullptr;
+    QBLK_TRY(check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(clip scratch)"));
+    if (!p) return fail(QBLK_EHIP, "hipGetSymbolAddress(clip scratch) returned NULL");
+    g_static_ptr[dev] = p;
+  }
+  *out = g_static_ptr[dev];
+  return QBLK_OK;
+}
+
+size_t static_clip_scratch_bytes() { return sizeof(double) * kStaticClipChunks * kSqGrid; }
 
 int adamw(int n, float* const* w, const float* const* g, float* const* m, float* const* v,
           const int64_t* numel, float lr, float b1, float b2, float eps, float wd, int step,

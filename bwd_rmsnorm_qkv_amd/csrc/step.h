@@ -14,6 +14,10 @@ int ce_rows(int T, int V, float* z, const int32_t* tgt, float scale, float* loss
 size_t clip_scratch(int n, const int64_t* numel);
 int clip_grad_norm(int n, float* const* g, const int64_t* numel, float max_norm, int apply,
                    float* norm_dev, float* scale_dev, void* scratch, hipStream_t st);
+// The per-device static partial-sum array of the no-workspace clip (looked
+// up on the current device) and its size in bytes.
+int static_clip_scratch(void** out);
+size_t static_clip_scratch_bytes();
 int adamw(int n, float* const* w, const float* const* g, float* const* m, float* const* v,
           const int64_t* numel, float lr, float b1, float b2, float eps, float wd, int step,
           const float* scale_dev, hipStream_t st);

@@ -83,6 +83,8 @@ _SIGS = {
     "qblk_clip_workspace_size": ([C.c_int32, C.c_void_p, C.POINTER(C.c_size_t)], C.c_int32),
     "qblk_clip_grad_norm": ([C.c_int32, C.c_void_p, C.c_void_p, C.c_float, C.c_int32, C.c_void_p,
                              C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int32),
+    "qblk_clip_grad_norm_noalloc": ([C.c_int32, C.c_void_p, C.c_void_p, C.c_float, C.c_int32, C.c_void_p,
+                                     C.c_void_p, C.c_void_p], C.c_int32),
     "qblk_adamw_step": ([C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                          C.c_float, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, C.c_void_p,
                          C.c_void_p], C.c_int32),
@@ -263,6 +265,11 @@ def clip_grad_norm(grads, max_norm, apply, norm_dev, scale_dev, scratch, stream=
     _check(lib().qblk_clip_grad_norm(len(grads), _ptr_array(grads), _numel_array(grads), max_norm, int(apply),
                                      _p(norm_dev), _p(scale_dev), _p(scratch),
                                      scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def clip_grad_norm_noalloc(grads, max_norm, apply, norm_dev, scale_dev, stream=None):
+    _check(lib().qblk_clip_grad_norm_noalloc(len(grads), _ptr_array(grads), _numel_array(grads), max_norm,
+                                             int(apply), _p(norm_dev), _p(scale_dev), _stream(stream)))
 
 
 def adamw_step(w, g, m, v, lr, beta1, beta2, eps, weight_decay, step, grad_scale_dev=None, stream=None):

@@ -28,8 +28,9 @@
  *     message (thread-local). Invalid arguments are rejected before any
  *     device work. Non-finite values are data, not errors.
  *   - Inputs and outputs must not overlap unless an argument says so.
- *   - Calls are re-entrant: the only library state is the loaded code and
- *     the per-thread error string.
+ *   - Calls are re-entrant: the only library state is the loaded code, the
+ *     per-thread error string and the static partial-sum array of
+ *     qblk_clip_grad_norm_noalloc (the one entry point that shares state).
  */
 #ifndef QBLK_H
 #define QBLK_H
@@ -185,6 +186,22 @@ int32_t qblk_clip_workspace_size(int32_t n, const int64_t* numel, size_t* scratc
 int32_t qblk_clip_grad_norm(int32_t n, float* const* grads, const int64_t* numel, float max_norm,
                             int32_t apply, float* norm_dev, float* scale_dev, void* scratch,
                             size_t scratch_bytes, qblk_stream_t stream);
+
+/* The same clip without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight loops,
+ * harnesses that forbid allocation). Same arguments, results (bitwise
+ * those of qblk_clip_grad_norm) and errors, minus `scratch`. Its partial
+ * sums live in a library-owned static device array, one per GPU (about
+ * 256 KiB, held until the process ends), looked up on the first call on
+ * each device; `stream` must belong to the current device. At most
+ * QBLK_CLIP_NOALLOC_MAX_TENSORS tensors (QBLK_EINVAL above). Every call on a
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must not be
+ * issued; calls ordered on one stream are fine. No allocation, no host
+ * synchronisation. */
+#define QBLK_CLIP_NOALLOC_MAX_TENSORS 2048
+int32_t qblk_clip_grad_norm_noalloc(int32_t n, float* const* grads, const int64_t* numel, float max_norm,
+                                    int32_t apply, float* norm_dev, float* scale_dev, qblk_stream_t stream);
 
 /* AdamW on n tensors ([block] optimizer_step, adamw_step_cuda; the formula
  * is not printed: decoupled weight decay with bias correction):
