@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["stack36_train_step", "nf4_lora_block"],
+                    help="time only this workload (for kernel traces) and print its JSON object")
     return ap.parse_args()
 
 
@@ -303,6 +305,11 @@ def main():
 
     torch.cuda.set_device(0)
     qblk.lib()
+    if args.only:
+        fn = {"stack36_train_step": extra_stack, "nf4_lora_block": extra_nf4}[args.only]
+        print(json.dumps({"only": args.only, "steps": args.steps, **fn(torch, qblk, synth, args.steps, args.warmup)}),
+              flush=True)
+        return
     c = synth.QWEN3_4B_BLOCK
     log("generating Qwen3-4B-shaped block inputs")
     inp = synth.block_inputs(c)

@@ -2,6 +2,7 @@
 trace, written as the markdown file kept under profiles/.
 
   python bench_trace.py summarize TRACE_DIR BENCH_JSON OUT.md
+  python bench_trace.py steps TRACE_DIR BENCH_JSON OUT.md TITLE COMMAND
 
 TRACE_DIR holds the csv output of
 
@@ -154,8 +155,51 @@ def summarize(trace_dir, bench_json, out_path):
     print(f"wrote {out_path}: replay {avg:.2f} us/launch (events {roof['avg_launch_us']})")
 
 
+def summarize_steps(trace_dir, bench_json, out_path, title, command):
+    """Per-step kernel table of a `bench.py --only NAME` run: its timed loop
+    is the group of dispatches between the spin kernel queued in front of
+    it and the end-marker spin (the group with the most dispatches)."""
+    stats = _csv(trace_dir, "kernel_stats.csv")
+    trace = _csv(trace_dir, "kernel_trace.csv")
+    bench = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    steps = bench["steps"]
+    loop = max(groups(trace), key=len)
+    agg = {}
+    for n, ns in loop:
+        c, t = agg.get(n, (0, 0))
+        agg[n] = (c + 1, t + ns)
+    busy = sum(t for _, t in agg.values()) / steps / 1e3
+    lines = [f"# Kernel durations: {title}", "", "Commands (repository root, one MI355X):", "", "```",
+             "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o bench -- " + command
+             + " > gpurun_out/trace/bench.json",
+             f"python bench_trace.py steps gpurun_out/trace gpurun_out/trace/bench.json "
+             f"{os.path.relpath(out_path, ROOT)} \"{title}\" \"{command}\"", "```", "",
+             "## Timed loop, per step", "",
+             f"{steps} steps; kernel busy time {busy:.1f} us per step; bench: {bench['ms_per_step'] * 1e3:.1f} us "
+             f"per step by events.", "",
+             "| kernel | launches/step | us/step | % of busy |", "|---|---:|---:|---:|"]
+    for n, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"| `{short(n)}` | {c / steps:.2f} | {t / steps / 1e3:.1f} | "
+                     f"{100.0 * t / steps / 1e3 / busy:.1f} |")
+    lines += ["", "## Whole run (rocprofv3 --stats)", "",
+              "| kernel | calls | total us | avg us | min us | max us | % |",
+              "|---|---:|---:|---:|---:|---:|---:|"]
+    for r in stats:
+        if float(r["Percentage"]) < 0.05:
+            continue
+        lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    lines += ["", "Bench output of the same run:", "", "```", json.dumps(bench), "```", ""]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out_path}: {busy:.1f} us kernel time per step")
+
+
 if __name__ == "__main__":
     if len(sys.argv) == 5 and sys.argv[1] == "summarize":
         summarize(*sys.argv[2:5])
+    elif len(sys.argv) == 7 and sys.argv[1] == "steps":
+        summarize_steps(*sys.argv[2:7])
     else:
         raise SystemExit(__doc__)

@@ -93,18 +93,28 @@ static size_t block_gemm_ws(const qblk_config& c, int r) {
       {Layout::NT, T, qkv, h}, {Layout::NT, T, h, qd}, {Layout::NT, T, 2 * I, h}, {Layout::NT, T, h, I},
       {Layout::NN, T, I, h},   {Layout::TN, h, I, T},  {Layout::NN, T, h, 2 * I}, {Layout::TN, 2 * I, h, T},
       {Layout::NN, T, qd, h},  {Layout::TN, h, qd, T}, {Layout::NN, T, h, qkv},   {Layout::TN, qkv, h, T}};
+  size_t m = 0;
   if (r > 0) {
     const int ins[4] = {h, qd, h, I}, outs[4] = {qkv, h, 2 * I, h}, ns[4] = {3, 1, 2, 1};
     const int outk[7] = {qd, kvd, kvd, h, I, I, h};
     for (int g = 0; g < 4; ++g) {
+      // register-kernel path (fp32 LoRA operands)
       v.push_back({Layout::NT, T, ns[g] * r, ins[g]});
       v.push_back({Layout::TN, outs[g], ns[g] * r, T});
       v.push_back({Layout::TN, ns[g] * r, ins[g], T});
+      // fp16 path: h and dh over 64 padded columns, dB, dA, the base
+      // products (dense fallback) and the fused NF4 products with the LoRA tile
+      v.push_back({Layout::NT, T, 64, ins[g]});
+      v.push_back({Layout::NT, T, 64, outs[g]});
+      v.push_back({Layout::TN, outs[g], 64, T});
+      v.push_back({Layout::NT, T, outs[g], 64});
+      v.push_back({Layout::NN, T, ins[g], 64});
+      m = std::max(m, gemm_nf4_workspace(T, outs[g], ins[g] + 64));
+      m = std::max(m, gemm_nf4_workspace(T, ins[g], outs[g] + 64));
     }
     for (int k = 0; k < 7; ++k) v.push_back({Layout::NN, T, r, outk[k]});
   }
   // the fp16-storage kernels plan their splits differently: size for both
-  size_t m = 0;
   for (const S& x : v)
     for (int f16src = 0; f16src < 2; ++f16src) {
       GemmDesc d;
@@ -145,8 +155,9 @@ void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes, 
   } else if (use_attention_dma(c)) {
     s.doT32 = cv.take<float>(T * qd);
   }
-  if (c.gemm_precision == 1 && lora_rank == 0) {
+  if (c.gemm_precision == 1 && (lora_rank == 0 || T % 8 == 0))
     s.a16 = cv.take<f16>(T * std::max({qd + 2 * kvd, 2 * I, h, qd}));
+  if (c.gemm_precision == 1 && lora_rank == 0) {
     size_t pb = 0;
     carve_pack16(c, nullptr, s.pack, pb);
     char* pbase = cv.take<char>(pb);

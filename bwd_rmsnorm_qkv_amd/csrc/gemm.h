@@ -96,9 +96,23 @@ struct GemmDesc {
   // diagonal-block mode): c16[row * ldc16 + col] = (fp16) C[row, col].
   f16* c16 = nullptr;
   int64_t ldc16 = 0;
+  // Fused-NF4 kernel (fp16 A, NF4 B) only: one more 64-wide K tile of fp16
+  // operands contracted after the K columns of A and B (the LoRA branch):
+  // C += ext16_a [M, 64] * ext16_b^T with ext16_b [N, 64] (NT) or
+  // [64, N] (NN), row strides ext16_lda / ext16_ldb. NULL: none.
+  const f16* ext16_a = nullptr;
+  int64_t ext16_lda = 0;
+  const f16* ext16_b = nullptr;
+  int64_t ext16_ldb = 0;
 };
 
 int gemm(const GemmDesc& d, hipStream_t stream);
+// Whether gemm() runs this NF4-B product on the fused decode kernel (fp16
+// A, NT or NN, K and ldb multiples of 64, see gemm.hip); ext16_* need it.
+bool gemm_nf4_fused(const GemmDesc& d);
+// Split-K workspace bytes of the fused NF4 kernel for an M x N product over
+// k_total K columns (the LoRA tile included).
+size_t gemm_nf4_workspace(int M, int N, int k_total);
 // Bytes of split-K workspace the GEMM would use for this shape (0 if none).
 size_t gemm_workspace(const GemmDesc& d);
 

@@ -1144,6 +1144,289 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   }
 }
 
+// ------------------------------------------ NF4 B operand, decoded in LDS
+//
+// The fused dequant + GEMM of the frozen NF4 weights (y = x W~^T forward,
+// NT; dX = dY W~ backward, NN). A (fp16 activations, K-major) is copied
+// global -> LDS by DMA exactly as in gemm_dma_kernel. B arrives as NF4
+// codes (half a byte per weight, one fp32 scale per 64 consecutive
+// elements of the row-major [out, in] storage): every thread loads 16 bytes
+// of codes (32 weights of one storage row, inside one 64-element block) and
+// their scale one step ahead, and at the start of the next step decodes
+// them into the B stage in the layout the DMA kernel's fragment reads
+// expect (K-major rows with the (row >> 1) & 7 chunk swizzle for NT,
+// K-rows with the (krow & 3) << 2 swizzle for NN). Decode: a 256-entry LDS
+// table maps a code byte to its two levels as an fp16 pair, which one
+// packed fp16 multiply scales by the block's scale (rounded to fp16): one
+// table read and one multiply per two weights. The codes are 4x smaller
+// than an fp16 copy, so B's traffic drops by 4x; A and the MFMA loop are
+// those of gemm_dma_kernel (128 x 128 tiles, 4 waves, two workgroups per
+// CU, two stages per operand).
+//
+// LoRA rides as one more K tile after the NF4 ones: A from ext16_a
+// ([M, 64] fp16, DMA), B from ext16_b (fp16, copied to LDS as it is).
+
+struct Nf4Lut {
+  uint32_t v[256];  // byte b -> (fp16 L[b & 15]) | (fp16 L[b >> 4]) << 16
+};
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_scale(uint32_t pair, half2v s) {
+  const half2v v = __builtin_bit_cast(half2v, pair) * s;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <bool NN>
+__global__ __launch_bounds__(256) void gemm_nf4_kernel(const GemmDesc d, const Grid gd) {
+  constexpr int BM = 128, BN = 128, BK = 64, WM = 2, WN = 2, NW = 4, TM = 2, TN = 2;
+  using OA = DmaOperand<BM, true, NW>;
+  using OB = DmaOperand<BN, !NN, NW>;  // fragment reads of the decoded stage
+
+  __shared__ Nf4Lut lut;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w % WM, wn = w / WM;
+  {
+    const f16 lo = (f16)d.nf4.levels[tid & 15], hi = (f16)d.nf4.levels[tid >> 4];
+    lut.v[tid] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+
+  const int total = gd.tiles_m * gd.tiles_n * gd.splits;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per = total / 8, rem = total % 8;
+  const int lt = xcd * per + min(xcd, rem) + slot;
+  const int mt = lt % gd.tiles_m;
+  const int nt = (lt / gd.tiles_m) % gd.tiles_n;
+  const int sp = lt / (gd.tiles_m * gd.tiles_n);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int nkt_main = d.K / BK;
+  const int nkt_all = nkt_main + (d.ext16_a ? 1 : 0);
+  const int kt0 = sp * (gd.kchunk / BK);
+  const int kt1 = min(nkt_all, kt0 + gd.kchunk / BK);
+
+  OA oa, oax;
+  oa.init((const f16*)d.a, d.lda, m0, d.M, 0, lane, w, nullptr);
+  if (d.ext16_a) oax.init(d.ext16_a, d.ext16_lda, m0, d.M, 0, lane, w, nullptr);
+  auto issueA = [&](int kt, f16* st, int j) __attribute__((always_inline)) {
+    if (kt < nkt_main) oa.issue_one(kt, st, d.lda, w, j);
+    else oax.issue_one(0, st, d.ext16_lda, w, j);
+  };
+
+  // This thread's share of a B tile: NT, storage row n0 + (tid >> 1),
+  // K elements 32 (tid & 1) .. + 31 of the tile; NN, K-row tid >> 2 of the
+  // tile, columns n0 + 32 (tid & 3) .. + 31.
+  const int brow = NN ? tid >> 2 : tid >> 1;
+  const int bpart = NN ? tid & 3 : tid & 1;
+  const uint8_t* ncodes = nullptr;  // NT: codes of this row at K = 32 bpart
+  const float* nscale = nullptr;    // NT: scales of this row
+  int bcol = 0;                     // NN: first column
+  if constexpr (!NN) {
+    const int n = min(n0 + brow, d.N - 1);
+    const int sg = seg_of(d.b, n);
+    const int64_t e = (int64_t)(n - d.b.start[sg]) * d.ldb;
+    ncodes = d.nf4.codes[sg] + (e + 32 * bpart) / 2;
+    nscale = d.nf4.scales[sg] + e / 64;
+  } else {
+    bcol = min(n0 + 32 * bpart, d.N - 32);
+  }
+  struct BReg {
+    u32x4 q[4];
+    float sc;
+  };
+  auto loadB = [&](int kt, BReg& r) __attribute__((always_inline)) {
+    if (kt < nkt_main) {
+      if constexpr (!NN) {
+        r.q[0] = *(const u32x4*)(ncodes + (int64_t)kt * (BK / 2));
+        r.sc = nscale[kt];
+      } else {
+        const int k0 = kt * BK;  // the tile's K-rows lie in one segment
+        const int sg = seg_of(d.b, k0);
+        const int64_t e = (int64_t)(k0 + brow - d.b.start[sg]) * d.ldb + bcol;
+        r.q[0] = *(const u32x4*)(d.nf4.codes[sg] + e / 2);
+        r.sc = d.nf4.scales[sg][e / 64];
+      }
+    } else {
+      const f16* src = NN ? d.ext16_b + (int64_t)brow * d.ext16_ldb + bcol
+                          : d.ext16_b + (int64_t)min(n0 + brow, d.N - 1) * d.ext16_ldb + 32 * bpart;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.q[i] = *(const u32x4*)(src + 8 * i);
+    }
+  };
+  // Decode (or copy, for the LoRA tile) 8-element chunk i of the thread's
+  // share into stage sb at the position the fragment reads expect. The
+  // table reads (lut_read) and the scaling + store (lut_store) are split so
+  // that the MFMAs of a K step run while the reads are in flight.
+  auto lut_read = [&](int kt, const BReg& r, int i, uint32_t (&lv)[4]) __attribute__((always_inline)) {
+    if (kt < nkt_main) {
+      const uint32_t c = r.q[0][i];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) lv[b] = lut.v[(c >> (8 * b)) & 255];
+    }
+  };
+  auto lut_store = [&](int kt, const BReg& r, int i, const uint32_t (&lv)[4], f16* sb) __attribute__((always_inline)) {
+    u32x4 out;
+    if (kt < nkt_main) {
+      const f16 s16 = (f16)r.sc;
+      const half2v s2 = {s16, s16};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) out[b] = pk_scale(lv[b], s2);
+    } else {
+      out = r.q[i];
+    }
+    const int c = 4 * bpart + i;  // 8-element chunk within the tile row
+    int pos;
+    if constexpr (!NN) pos = brow * BK + ((c ^ ((brow >> 1) & 7)) << 3);
+    else pos = brow * BN + ((c ^ ((brow & 3) << 2)) << 3);
+    *(u32x4*)(sb + pos) = out;
+  };
+  auto storeB = [&](int kt, const BReg& r, f16* sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lv[4] = {0u, 0u, 0u, 0u};
+      lut_read(kt, r, i, lv);
+      lut_store(kt, r, i, lv, sb);
+    }
+  };
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  int ko[BK / 16];
+#pragma unroll
+  for (int s = 0; s < BK / 16; ++s) ko[s] = OA::koff(s, lane);
+
+  f16* const sA0 = lds_stage<20, BM * BK>();
+  f16* const sA1 = lds_stage<21, BM * BK>();
+  f16* const sB0 = lds_stage<22, BN * BK>();
+  f16* const sB1 = lds_stage<23, BN * BK>();
+
+  // MFMAs of one tile; the A copies of tile kn (into da) are spread over
+  // them as in gemm_dma_kernel, and the decode of B tile kd (codes in rd,
+  // into db) is cut into the four K steps: chunk s's table reads are issued
+  // before step s's MFMAs, its scaling and store after them.
+  auto compute = [&](const f16* sa, const f16* sb, bool ca, int kn, f16* da, bool cd, int kd, const BReg& rd,
+                     f16* db) __attribute__((always_inline)) {
+    half8 av[2][TM], bv[2][TN];
+    auto frag = [&](int s, half8* a, half8* b) __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < TM; ++t) a[t] = OA::frag(sa, wm * TM * 32 + t * 32, s, lane, ko[s]);
+#pragma unroll
+      for (int t = 0; t < TN; ++t) b[t] = OB::frag(sb, wn * TN * 32 + t * 32, s, lane, ko[s]);
+    };
+    constexpr int NM = (BK / 16) * TM * TN, NC = OA::J;
+    frag(0, av[0], bv[0]);
+    static_for<0, BK / 16>([&](auto Sx) __attribute__((always_inline)) {
+      constexpr int s = decltype(Sx)::value;
+      if constexpr (s + 1 < BK / 16) frag(s + 1, av[(s + 1) & 1], bv[(s + 1) & 1]);
+      uint32_t lv[4] = {0u, 0u, 0u, 0u};
+      if (cd) lut_read(kd, rd, s, lv);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, TM * TN>([&](auto Jx) __attribute__((always_inline)) {
+        constexpr int j = decltype(Jx)::value, tm = j / TN, tn = j % TN, i = s * TM * TN + j;
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[s & 1][tm], bv[s & 1][tn], acc[tm][tn], 0, 0, 0);
+        static_for<(i * NC) / NM, ((i + 1) * NC) / NM>([&](auto Cx) __attribute__((always_inline)) {
+          constexpr int c = decltype(Cx)::value;
+          if (ca) issueA(kn, da, c);
+        });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      if (cd) lut_store(kd, rd, s, lv, db);
+    });
+  };
+
+  // Prologue: A of the first tile in flight, its B decoded (the table
+  // written above is complete after the barrier), the codes of the second
+  // tile in flight.
+  BReg rb0, rb1;
+  if (kt0 < kt1) {
+    loadB(kt0, rb0);
+#pragma unroll
+    for (int j = 0; j < OA::J; ++j) issueA(kt0, sA0, j);
+  }
+  __syncthreads();
+  if (kt0 < kt1) storeB(kt0, rb0, sB0);
+  if (kt0 + 1 < kt1) loadB(kt0 + 1, rb1);
+
+  // Step kt (stage p = (kt - kt0) & 1): wait for A of tile kt and the codes
+  // of tile kt+1 (both issued in the previous step), barrier (the decoded B
+  // of tile kt is visible, every wave is done with tile kt-1's stages), then
+  // load the codes of tile kt+2 and run tile kt's MFMAs with A of tile kt+1
+  // copied and B of tile kt+1 decoded into the other stages alongside.
+  auto step = [&](auto P, int kt) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+    f16* const sa = p ? sA1 : sA0;
+    f16* const sb = p ? sB1 : sB0;
+    f16* const na = p ? sA0 : sA1;
+    f16* const nb = p ? sB0 : sB1;
+    BReg& cur = p ? rb0 : rb1;  // codes of tile kt+1
+    BReg& nxt = p ? rb1 : rb0;  // receives the codes of tile kt+2
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + 2 < kt1) loadB(kt + 2, nxt);
+    compute(sa, sb, kt + 1 < kt1, kt + 1, na, kt + 1 < kt1, kt + 1, cur, nb);
+  };
+  int kt = kt0;
+  for (; kt + 1 < kt1; kt += 2) {
+    step(std::integral_constant<int, 0>{}, kt);
+    step(std::integral_constant<int, 1>{}, kt + 1);
+  }
+  if (kt < kt1) step(std::integral_constant<int, 0>{}, kt);
+
+  // Epilogue: as gemm_dma_kernel's (staged through the idle stages).
+  constexpr int WC = TN * 32;
+  constexpr int CPR = WC / 4;
+  const int ii = lane & 31, kh = lane >> 5;
+  __syncthreads();
+  float* ep;
+  switch (w >> 1) {
+    case 0: ep = (float*)sA0; break;
+    default: ep = (float*)sB0; break;
+  }
+  ep += (w & 1) * 32 * WC;
+  auto eslot = [](int r, int c) { return r * WC + ((c ^ (((r >> 2) & 1) << 3)) << 2); };
+  const int col0 = n0 + wn * WC;
+  float* part = gd.splits > 1 ? d.ws + (int64_t)sp * d.M * d.N : nullptr;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int c = tn * 32 + ii;
+          ep[eslot(8 * g + 4 * kh + r, c >> 2) + (c & 3)] = acc[tm][tn][4 * g + r];
+        }
+    const int rowb = m0 + wm * TM * 32 + tm * 32;
+    if (epi_pass_fast<32, CPR>(d, gd.vec, part, rowb, col0, ep, eslot, lane)) continue;
+#pragma unroll 1
+    for (int q = 0; q < 32 * CPR / 64; ++q) {
+      const int L = q * 64 + lane, rr = L / CPR, c = L % CPR;
+      const float4 v = *(const float4*)(ep + eslot(rr, c));
+      const int row = rowb + rr, col = col0 + 4 * c;
+      if (row >= d.M || col >= d.N) continue;
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+      if (part) {
+        float* pp = part + (int64_t)row * d.N + col;
+        for (int j = 0; j < 4 && col + j < d.N; ++j) pp[j] = vv[j];
+        continue;
+      }
+      int lo = 0;
+      float* rp = out_row(d, row, lo);
+      if (!rp) continue;
+      for (int j = 0; j < 4 && col + j < d.N; ++j) {
+        put_out(d, rp + (col + j - lo), row, col + j, vv[j]);
+        if (d.c16) d.c16[(int64_t)row * d.ldc16 + col + j] = (f16)rp[col + j - lo];
+      }
+    }
+  }
+}
+
 // Ping-pong variant of the 256 x 256 tile: the two halves of the workgroup
 // (waves 0-3 and 4-7; each SIMD holds one of each) alternate between an
 // MFMA phase (16 MFMAs: two K steps of the wave's 64 x 128 block) and an
@@ -1506,31 +1789,10 @@ constexpr int kTargetWgs = 256;  // one 4-wave workgroup per CU (LDS-limited)
 constexpr int kMinKtPerSplit = 8;
 constexpr int kMaxSplits = 32;
 
-// Tile configurations: waves WM x WN, blocks per wave TM x TN, and the K
-// tile (BK_BIG: 64 fp16 / 32 fp32 elements, else half that).
-struct Cfg {
-  int id, bm, bn;
-  bool bk_big;
-};
-
-constexpr Cfg kCfgs[] = {
-    {0, 256, 128, true},   // WM 2, WN 2, TM 4, TN 2
-    {1, 128, 128, true},   // WM 2, WN 2, TM 2, TN 2
-    {2, 128, 128, false},  // WM 2, WN 2, TM 2, TN 2, short K tile
-    {3, 128, 256, true},   // WM 2, WN 2, TM 2, TN 4
-    {4, 256, 256, true},   // WM 2, WN 2, TM 4, TN 4
-};
-
-Cfg cfg_for(const GemmDesc& d) {
-#ifdef QBLK_FORCE_CFG
-  (void)d;
-  return kCfgs[QBLK_FORCE_CFG];
-#else
-  // 128 x 128 with two waves per SIMD measured best on every block shape.
-  (void)d;
-  return kCfgs[1];
-#endif
-}
+// Register-staged kernel tile: 128 x 128 (2 x 2 waves of 2 x 2 blocks of
+// 32 x 32, two waves per SIMD), the K tile 64 fp16 / 32 fp32 elements.
+// Other tile shapes measured slower on every product of the block.
+constexpr int kRegBM = 128, kRegBN = 128;
 
 // target_wgs > 0: split K so that tiles x splits reaches it (rounding up);
 // target_wgs < 0: so that it stays within -target_wgs (rounding down, one
@@ -1555,10 +1817,7 @@ Grid plan_tiles(const GemmDesc& d, size_t ws_bytes, int bm, int bn, int bk, int 
 
 // Ping-pong configurations: 256 x 256 for every layout, 256 x 192 for NT
 // (with a third B stage where the LDS allows it).
-#ifndef QBLK_PP_NB192
-#define QBLK_PP_NB192 3
-#endif
-constexpr int kPpNb192 = QBLK_PP_NB192;
+constexpr int kPpNb192 = 3;
 struct PpCfg {
   static constexpr int bm = 256, bn = 256, threads = 512;
   static constexpr bool narrow = true;  // also runs 256 x 192 tiles (NT)
@@ -1596,23 +1855,11 @@ struct DmaCfg {
     }
   }
 };
-#ifdef QBLK_NT16_CFG  // one forced configuration (tuning builds)
-using Nt16Small = DmaCfg<QBLK_NT16_CFG>;
-using Nt16Big = Nt16Small;
-#else
 // 128 x 128 tiles, 4 waves, two workgroups per CU (80 KB LDS each: two A
 // stages, three B stages); and 256 x 256 tiles, 8 waves of 64 x 128, one
-// workgroup per CU.
-#ifndef QBLK_SMALL_NB
-#define QBLK_SMALL_NB 3
-#endif
-using Nt16Small = DmaCfg<128, 128, 2, 2, 2, QBLK_SMALL_NB>;
-#ifdef QBLK_NO_PINGPONG
-using Nt16Big = DmaCfg<256, 256, 4, 2, 2>;
-#else
+// workgroup per CU (the ping-pong kernel).
+using Nt16Small = DmaCfg<128, 128, 2, 2, 2, 3>;
 using Nt16Big = PpCfg;
-#endif
-#endif
 
 // Big tiles pay off once they alone give at least half the CUs a tile.
 // Weight-gradient products (TN) take the small tiles instead when the big
@@ -1635,10 +1882,6 @@ bool nt16_big(const GemmDesc& d) {
 // extends the contraction, an MN-major operand has M (or N) a multiple of 8
 // and is a single segment.
 bool nt16_ok(const GemmDesc& d) {
-#ifdef QBLK_NO_NT16
-  (void)d;
-  return false;
-#else
   if (d.prec != Prec::F16) return false;
   if (d.a_src != Src::F16 || d.b_src != Src::F16 || d.ext.kext > 0 || d.b_src == Src::NF4) return false;
   if (d.K % 64 != 0 || d.lda % 8 != 0 || d.ldb % 8 != 0) return false;
@@ -1648,7 +1891,6 @@ bool nt16_ok(const GemmDesc& d) {
   if (d.layout == Layout::TN && (d.M % 8 != 0 || d.M < 8)) return false;
   if (d.layout != Layout::NT && (d.N % 8 != 0 || d.N < 8 || d.b.nseg != 1)) return false;
   return true;
-#endif
 }
 
 // 16-byte epilogue stores: every output row (segment base and stride),
@@ -1690,9 +1932,82 @@ Grid plan(const GemmDesc& d, size_t ws_bytes) {
     g.nfast = big && d.layout == Layout::TN;
     return g;
   }
-  const Cfg c = cfg_for(d);
-  const int bk = PT<Prec::F16>::BK / (d.prec == Prec::F16 ? 1 : 2) / (c.bk_big ? 1 : 2);
-  return plan_tiles(d, ws_bytes, c.bm, c.bn, bk);
+  const int bk = d.prec == Prec::F16 ? PT<Prec::F16>::BK : PT<Prec::F32>::BK;
+  return plan_tiles(d, ws_bytes, kRegBM, kRegBN, bk);
+}
+
+// The fused NF4 kernel applies to fp16 A (K-major, 16-byte aligned rows),
+// NF4 B with ldb a multiple of 64 (every 64-element block inside one
+// storage row), K a multiple of 64, for NN N a multiple of 32 and B's
+// segment boundaries on 64-row tiles, and no diagonal-block output.
+bool nf4_fused_ok(const GemmDesc& d) {
+  if (d.prec != Prec::F16 || d.a_src != Src::F16 || d.b_src != Src::NF4) return false;
+  if (d.layout == Layout::TN || d.ext.kext > 0 || d.c_cols_blockdiag > 0) return false;
+  if (d.K % 64 != 0 || d.K == 0 || d.lda % 8 != 0 || d.ldb % 64 != 0 || (uintptr_t)d.a % 16 != 0) return false;
+  for (int s = 0; s < d.b.nseg; ++s)
+    if ((uintptr_t)d.nf4.codes[s] % 16 != 0 || (uintptr_t)d.nf4.scales[s] % 4 != 0) return false;
+  if (d.layout == Layout::NN) {
+    if (d.N % 32 != 0) return false;
+    for (int s = 1; s < d.b.nseg; ++s)
+      if (d.b.start[s] % 64 != 0) return false;
+  }
+  if (d.ext16_a) {
+    if (!d.ext16_b || d.ext16_lda % 8 != 0 || d.ext16_ldb % 8 != 0 || (uintptr_t)d.ext16_a % 16 != 0 ||
+        (uintptr_t)d.ext16_b % 16 != 0)
+      return false;
+    if (d.layout == Layout::NN && d.N % 32 != 0) return false;
+  }
+  return true;
+}
+
+// Split count of the fused NF4 kernel: a product with fewer tiles than
+// workgroup slots (two per CU) leaves CUs with a single workgroup, whose
+// MFMA pipe then idles through the decode and barrier phases. The split
+// minimises an estimate in units of one K tile's time at two workgroups
+// per CU: per round of slots, a full round costs 1 and a last round of at
+// most one workgroup per CU about 0.6; each split adds the partial sums'
+// write and read (M N 8 bytes at about 5 TB/s, with ~1.9 us per K tile
+// measured at the Qwen3-4B shapes).
+int nf4_splits(int tiles, int nkt, int64_t mn) {
+  const int slots = 2 * kTargetWgs;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int sp = 1; sp <= 8 && nkt / sp >= kMinKtPerSplit / 2; ++sp) {
+    const int64_t w = (int64_t)tiles * sp;
+    const int64_t full = w / slots, rem = w % slots;
+    const double rounds = (double)full + (rem == 0 ? 0.0 : rem <= kTargetWgs ? 0.6 : 1.0);
+    const double cost = (double)ceil_div(nkt, sp) * rounds + (sp > 1 ? sp * (double)mn * 8.0 / 5e12 / 1.9e-6 : 0.0);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  return best;
+}
+
+Grid plan_nf4(const GemmDesc& d, size_t ws_bytes) {
+  Grid g;
+  g.tiles_m = (int)ceil_div(d.M, 128);
+  g.tiles_n = (int)ceil_div(d.N, 128);
+  const int nkt = d.K / 64 + (d.ext16_a ? 1 : 0);
+  int splits = nf4_splits(g.tiles_m * g.tiles_n, nkt, (int64_t)d.M * d.N);
+  if (splits > 1 && (size_t)splits * d.M * d.N * sizeof(float) > ws_bytes) splits = 1;
+  const int kt_per = (int)ceil_div(nkt, splits);
+  g.splits = std::max(1, (int)ceil_div(nkt, kt_per));
+  g.kchunk = kt_per * 64;
+  g.vec = out_vec4(d, g);
+  return g;
+}
+
+int finish_splits(const GemmDesc& d, const Grid& g, hipStream_t st);
+
+int launch_nf4(const GemmDesc& d, hipStream_t st) {
+  const Grid g = plan_nf4(d, d.ws ? d.ws_bytes : 0);
+  const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
+  if (d.layout == Layout::NT) hipLaunchKernelGGL(gemm_nf4_kernel<false>, dim3(nwg), dim3(256), 0, st, d, g);
+  else hipLaunchKernelGGL(gemm_nf4_kernel<true>, dim3(nwg), dim3(256), 0, st, d, g);
+  QBLK_TRY(check_launch("gemm_nf4_kernel"));
+  return finish_splits(d, g, st);
 }
 
 int finish_splits(const GemmDesc& d, const Grid& g, hipStream_t st) {
@@ -1712,41 +2027,11 @@ int launch_nt16(const GemmDesc& d, hipStream_t st) {
   return finish_splits(d, g, st);
 }
 
-template <Prec P, Layout L, Src AS, Src BS, bool EXT, int WM, int WN, int TM, int TN, bool BIG>
-void launch_cfg(const GemmDesc& d, const Grid& g, hipStream_t st) {
-  constexpr int BK = PT<P>::BK / (BIG ? 1 : 2);
-  const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
-  hipLaunchKernelGGL((gemm_kernel<P, L, AS, BS, EXT, WM, WN, TM, TN, BK>), dim3(nwg), dim3(WM * WN * 64), 0, st,
-                     d, g);
-}
-
-#ifdef QBLK_FORCE_CFG
-#define QBLK_CFG_ON(i) (QBLK_FORCE_CFG == (i))
-#else
-#define QBLK_CFG_ON(i) ((i) == 1)
-#endif
-
 template <Prec P, Layout L, Src AS, Src BS, bool EXT>
 int launch(const GemmDesc& d, hipStream_t st) {
   const Grid g = plan(d, d.ws ? d.ws_bytes : 0);
-  switch (cfg_for(d).id) {
-#if QBLK_CFG_ON(0)
-    case 0: launch_cfg<P, L, AS, BS, EXT, 2, 2, 4, 2, true>(d, g, st); break;
-#endif
-#if QBLK_CFG_ON(1)
-    case 1: launch_cfg<P, L, AS, BS, EXT, 2, 2, 2, 2, true>(d, g, st); break;
-#endif
-#if QBLK_CFG_ON(2)
-    case 2: launch_cfg<P, L, AS, BS, EXT, 2, 2, 2, 2, false>(d, g, st); break;
-#endif
-#if QBLK_CFG_ON(3)
-    case 3: launch_cfg<P, L, AS, BS, EXT, 2, 2, 2, 4, true>(d, g, st); break;
-#endif
-#if QBLK_CFG_ON(4)
-    case 4: launch_cfg<P, L, AS, BS, EXT, 2, 2, 4, 4, true>(d, g, st); break;
-#endif
-    default: return fail(QBLK_EUNSUPPORTED, "gemm: tile configuration not built");
-  }
+  const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
+  hipLaunchKernelGGL((gemm_kernel<P, L, AS, BS, EXT, 2, 2, 2, 2, PT<P>::BK>), dim3(nwg), dim3(256), 0, st, d, g);
   QBLK_TRY(check_launch("gemm_kernel"));
   return finish_splits(d, g, st);
 }
@@ -1754,6 +2039,7 @@ int launch(const GemmDesc& d, hipStream_t st) {
 template <Prec P, Layout L>
 int dispatch_src(const GemmDesc& d, hipStream_t st) {
   const bool ext = d.ext.kext > 0;
+  if (nf4_fused_ok(d)) return launch_nf4(d, st);
   if (d.b_src == Src::NF4) {
     if constexpr (L == Layout::TN || P == Prec::F32) {
       return fail(QBLK_EUNSUPPORTED, "gemm: NF4 operand needs an NT/NN fp16 contraction");
@@ -1802,7 +2088,7 @@ int gemm(const GemmDesc& d, hipStream_t st) {
   if (d.c16) {
     if (d.c.nseg != 1 || d.c_cols_blockdiag > 0)
       return fail(QBLK_EINVAL, "gemm: the fp16 output copy needs a single C segment");
-    if (!nt16_ok(d)) {  // kernels without the fp16 epilogue: copy afterwards
+    if (!nt16_ok(d) && !nf4_fused_ok(d)) {  // kernels without the fp16 epilogue: copy afterwards
       GemmDesc e = d;
       e.c16 = nullptr;
       QBLK_TRY(gemm(e, st));
@@ -1840,8 +2126,17 @@ int gemm(const GemmDesc& d, hipStream_t st) {
   return fail(QBLK_EINVAL, "gemm: bad layout");
 }
 
+bool gemm_nf4_fused(const GemmDesc& d) { return nf4_fused_ok(d); }
+
+size_t gemm_nf4_workspace(int M, int N, int k_total) {
+  GemmDesc e;
+  e.M = M; e.N = N; e.K = k_total;
+  const Grid g = plan_nf4(e, (size_t)-1);
+  return g.splits > 1 ? (size_t)g.splits * M * N * sizeof(float) : 0;
+}
+
 size_t gemm_workspace(const GemmDesc& d) {
-  const Grid g = plan(d, (size_t)-1);
+  const Grid g = nf4_fused_ok(d) ? plan_nf4(d, (size_t)-1) : plan(d, (size_t)-1);
   return g.splits > 1 ? (size_t)g.splits * d.M * d.N * sizeof(float) : 0;
 }
 

@@ -7,16 +7,19 @@
 // alpha/rank, with h = x A^T kept from the forward).
 //
 // Design. Two paths share the launch sequence of the dense block:
-// * fp16 copies (T a multiple of 8): each projection group's NF4 codes are
-//   decoded once per call into an fp16 scratch copy of W~ (HBM-bound, a
-//   fraction of the product's time), the product runs on the direct-to-LDS
-//   GEMM kernel with the activations' fp16 copies, and the LoRA branch adds
-//   s h B^T (forward) or dh A (backward) with small accumulating GEMMs.
-// * otherwise: the codes are decoded while the GEMM stages its B operand and
-//   the LoRA branch rides in the same GEMM as extra K columns:
-//   y = [x | s*h] [W~ | B]^T with h = x A^T, s = alpha/rank, against a
-//   block-diagonal B for the fused groups; dX = dY W~ + (s dY B) A likewise.
-// dA and dB are small TN GEMMs either way.
+// * fp16 operands (T a multiple of 8): the activations' fp16 copies are
+//   written by their producers. Each projection group runs ONE fused
+//   dequant + GEMM (gemm_nf4_kernel: the NF4 codes are decoded into LDS
+//   while the tile is staged, never written out) whose last K tile is the
+//   LoRA branch: y = [x | s h] [W~ | B]^T with h = x A^T, s = alpha/rank,
+//   B block-diagonal over the group's projections; backward dX = [dY | dh]
+//   [W~ ; A] with dh = s dY B. The rank-r products (h, dh, dA, dB) run on
+//   the fp16 DMA GEMM over 64 zero-padded LoRA columns. Shapes the fused
+//   kernel does not take (K or the row length not a multiple of 64) decode
+//   the group into an fp16 scratch copy and run the dense product instead.
+// * otherwise (fp32 operand storage): the codes are decoded while the
+//   register-staged GEMM stages its B operand and the LoRA branch rides in
+//   the same GEMM as extra K columns; dA and dB are small TN GEMMs.
 #include "../../include/qblk.h"
 #include "block.h"
 #include "gemm.h"
@@ -30,15 +33,22 @@ namespace {
 
 struct Nf4Saved {
   Saved base;
-  float *h_qkv, *h_o, *h_gu, *h_d;  // x A^T of each projection group
+  // x A^T of each projection group: [T, n r] (fp32 operand path) or, on
+  // the fp16 path, s x A^T over 64 zero-padded columns [T, 64] and its
+  // fp16 copy (the LoRA K tile of the forward, the B side of dB).
+  float *h_qkv, *h_o, *h_gu, *h_d;
+  f16 *hs16_qkv, *hs16_o, *hs16_gu, *hs16_d;
 };
 
 struct Nf4Scratch {
   Scratch base;
-  float *dh_qkv, *dh_o, *dh_gu, *dh_d;  // s dY B
+  float *dh_qkv, *dh_o, *dh_gu, *dh_d;  // s dY B ([T, n r]; fp16 path: [T, 64])
+  f16* dh16;                            // fp16 path: fp16 copy of the current group's dh [T, 64]
+  f16* a16x;                            // fp16 path: [A_0; A_1; A_2; 0] [64, in]
+  f16* bx16;                            // fp16 path: block-diagonal B [out, 64]
+  f16* bt16;                            // fp16 path: block-diagonal B^T [64, out]
   float *sink_h, *sink_d;               // gamma gradients are not outputs
-  f16* w16;                             // fp16 W~ of the current group (fp16 copies path)
-  f16* dy16;                            // fp16 dY of the current group
+  f16* w16;                             // fp16 W~ of the current group (dense fallback)
 };
 
 size_t carve_nf4(const qblk_config& c, int r, void* saved, void* scratch, Nf4Saved* s, Nf4Scratch* w,
@@ -53,28 +63,36 @@ size_t carve_nf4(const qblk_config& c, int r, void* saved, void* scratch, Nf4Sav
     off += n * sizeof(float);
     return p;
   };
-  s->h_qkv = take(saved, sb, T * 3 * r);
-  s->h_o = take(saved, sb, T * r);
-  s->h_gu = take(saved, sb, T * 2 * r);
-  s->h_d = take(saved, sb, T * r);
-  w->dh_qkv = take(scratch, wb, T * 3 * r);
-  w->dh_o = take(scratch, wb, T * r);
-  w->dh_gu = take(scratch, wb, T * 2 * r);
-  w->dh_d = take(scratch, wb, T * r);
+  const bool f16p = c.gemm_precision == 1 && T % 8 == 0;
+  const size_t hw = f16p ? 64 : 3 * (size_t)r;
+  s->h_qkv = take(saved, sb, T * hw);
+  s->h_o = take(saved, sb, T * hw);
+  s->h_gu = take(saved, sb, T * hw);
+  s->h_d = take(saved, sb, T * hw);
+  s->hs16_qkv = s->hs16_o = s->hs16_gu = s->hs16_d = nullptr;
+  w->dh16 = w->a16x = w->bx16 = w->bt16 = w->w16 = nullptr;
+  if (f16p) {
+    s->hs16_qkv = (f16*)take(saved, sb, T * 32);
+    s->hs16_o = (f16*)take(saved, sb, T * 32);
+    s->hs16_gu = (f16*)take(saved, sb, T * 32);
+    s->hs16_d = (f16*)take(saved, sb, T * 32);
+  }
+  w->dh_qkv = take(scratch, wb, T * hw);
+  w->dh_o = take(scratch, wb, T * hw);
+  w->dh_gu = take(scratch, wb, T * hw);
+  w->dh_d = take(scratch, wb, T * hw);
   w->sink_h = take(scratch, wb, 2 * (size_t)c.hidden);
   w->sink_d = take(scratch, wb, 2 * (size_t)c.head_dim);
-  w->w16 = w->dy16 = nullptr;
-  if (s->base.n1_16 || !saved) {  // sizing call, or the fp16 copies exist
+  if (f16p) {
     const size_t h = c.hidden, qd = (size_t)c.heads * c.head_dim, kvd = (size_t)c.kv_heads * c.head_dim;
     const size_t I = c.intermediate, qkv = qd + 2 * kvd;
     const size_t wmax = std::max({qkv * h, h * qd, 2 * I * h, h * I});
-    const size_t dmax = std::max({qkv, h, 2 * I});
-    float* a = take(scratch, wb, wmax / 2 + 64);
-    float* b = take(scratch, wb, T * dmax / 2 + 64);
-    if (s->base.n1_16) {
-      w->w16 = (f16*)a;
-      w->dy16 = (f16*)b;
-    }
+    const size_t omax = std::max({qkv, h, 2 * I}), imax = std::max({h, qd, I});
+    w->dh16 = (f16*)take(scratch, wb, T * 32);
+    w->a16x = (f16*)take(scratch, wb, 32 * imax);
+    w->bx16 = (f16*)take(scratch, wb, 32 * omax);
+    w->bt16 = (f16*)take(scratch, wb, 32 * omax);
+    w->w16 = (f16*)take(scratch, wb, wmax / 2 + 64);
   }
   *scratch_bytes = wb;
   return sb;
@@ -244,7 +262,8 @@ int nf4_bwd(const qblk_nf4_block_params& p, const qblk_lora_grads& gr, int T, in
   return QBLK_OK;
 }
 
-// fp16 W~ of a projection group, stacked along out, into w16.
+// fp16 W~ of a projection group, stacked along out, into w16 (the dense
+// fallback of the fp16 path).
 int dequant_group(const qblk_nf4_block_params& p, const int* id3, const int* outd, int n, int in, f16* w16,
                   hipStream_t st) {
   size_t off = 0;
@@ -256,100 +275,173 @@ int dequant_group(const qblk_nf4_block_params& p, const int* id3, const int* out
   return QBLK_OK;
 }
 
-// out (+ res) = x16 W~^T + s h blockdiag(B)^T on the fp16 copies path.
-int nf4_fwd16(const qblk_nf4_block_params& p, const Nf4Scratch& w, int T, int in, const f16* x16,
-              std::initializer_list<int> ids, std::initializer_list<int> outs, const float* h, const float* res,
-              float* out, hipStream_t st) {
-  const int r = p.rank, n = (int)ids.size();
-  int outd[3] = {0, 0, 0}, id3[3] = {-1, -1, -1}, j = 0;
-  for (int o : outs) outd[j++] = o;
-  j = 0;
-  for (int id : ids) id3[j++] = id;
-  int N = 0;
-  for (int k = 0; k < n; ++k) N += outd[k];
-  QBLK_TRY(dequant_group(p, id3, outd, n, in, w.w16, st));
-  GemmDesc g = base(Layout::NT, T, N, in);
-  g.a = x16; g.lda = in; g.a_src = Src::F16;
-  g.b = seg1(w.w16, N); g.ldb = in; g.b_src = Src::F16;
-  g.c = seg1(out, T); g.ldc = N;
-  g.r = res; g.ldr = N;
-  QBLK_TRY(gemm(g, st));
-  int col = 0;
-  for (int k = 0; k < n; ++k) {  // out[:, block k] += s h_k B_k^T
-    GemmDesc u = base(Layout::NT, T, outd[k], r);
-    u.a = h + k * r; u.lda = n * r;
-    u.b = seg1(p.lora_b[id3[k]], outd[k]); u.ldb = r;
-    u.c = seg1(out + col, T); u.ldc = N;
-    u.alpha = p.alpha / (float)r;
-    u.accumulate = 1;
-    QBLK_TRY(gemm(u, st));
-    col += outd[k];
+// The LoRA matrices of a group as fp16 operands over 64 padded columns:
+//   mode 0: a16x [64, in],  row k r + j = A_k[j, :];
+//   mode 1: bx16 [out, 64], row o of segment k holds B_k[o - start_k, :] at
+//           columns k r .. k r + r - 1;
+//   mode 2: bt16 [64, out], the transpose of mode 1.
+// Every other element is zero.
+struct LoraPack {
+  const float* m[3];
+  int start[4];  // segment starts along out (modes 1, 2)
+  int n, r, in, out, mode;
+};
+
+__global__ __launch_bounds__(256) void lora_pack16_kernel(const LoraPack a, f16* __restrict__ dst) {
+  const int64_t e = blockIdx.x * (int64_t)256 + threadIdx.x;
+  const int64_t total = a.mode == 0 ? 64 * (int64_t)a.in : 64 * (int64_t)a.out;
+  if (e >= total) return;
+  float v = 0.f;
+  if (a.mode == 0) {
+    const int row = (int)(e / a.in), col = (int)(e % a.in);
+    if (row < a.n * a.r) v = a.m[row / a.r][(int64_t)(row % a.r) * a.in + col];
+  } else {
+    const int o = a.mode == 1 ? (int)(e / 64) : (int)(e % a.out);
+    const int c = a.mode == 1 ? (int)(e % 64) : (int)(e / a.out);
+    int k = 0;
+    while (k + 1 < a.n && o >= a.start[k + 1]) ++k;
+    if (c >= k * a.r && c < (k + 1) * a.r) v = a.m[k][(int64_t)(o - a.start[k]) * a.r + (c - k * a.r)];
   }
-  return QBLK_OK;
+  dst[e] = (f16)v;
 }
 
-// Backward on the fp16 copies path: dX = dY16 W~ + dh [A stacked]; dA, dB
-// as in nf4_bwd.
+int lora_pack16(const qblk_nf4_block_params& p, const int* id3, const int* outd, int n, int in, int mode,
+                f16* dst, hipStream_t st) {
+  LoraPack a{};
+  a.n = n; a.r = p.rank; a.in = in; a.mode = mode;
+  int o = 0;
+  for (int k = 0; k < n; ++k) {
+    a.m[k] = mode == 0 ? p.lora_a[id3[k]] : p.lora_b[id3[k]];
+    a.start[k] = o;
+    o += outd[k];
+  }
+  a.start[n] = o;
+  a.out = o;
+  const int64_t total = mode == 0 ? 64 * (int64_t)in : 64 * (int64_t)o;
+  hipLaunchKernelGGL(lora_pack16_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, st, a, dst);
+  return check_launch("lora_pack16_kernel");
+}
+
+struct Group {
+  int id3[3] = {-1, -1, -1}, outd[3] = {0, 0, 0}, n = 0, N = 0;
+  Group(std::initializer_list<int> ids, std::initializer_list<int> outs) {
+    for (int id : ids) id3[n++] = id;
+    int j = 0;
+    for (int o : outs) outd[j++] = o;
+    for (int k = 0; k < n; ++k) N += outd[k];
+  }
+};
+
+// Forward of one group on the fp16 path:
+//   hs = s x16 [A stacked]^T over 64 columns (fp32 `hs`, fp16 `hs16`);
+//   out (+ res) = x16 W~^T + hs16 bx16^T, fused (NF4 decoded in the GEMM).
+int nf4_fwd16(const qblk_nf4_block_params& p, const Nf4Scratch& w, int T, int in, const f16* x16,
+              const Group& g, float* hs, f16* hs16, const float* res, float* out, hipStream_t st) {
+  const float sc = p.alpha / (float)p.rank;
+  QBLK_TRY(lora_pack16(p, g.id3, g.outd, g.n, in, 0, w.a16x, st));
+  {
+    GemmDesc d = base(Layout::NT, T, 64, in);
+    d.a = x16; d.lda = in; d.a_src = Src::F16;
+    d.b = seg1(w.a16x, 64); d.ldb = in; d.b_src = Src::F16;
+    d.c = seg1(hs, T); d.ldc = 64;
+    d.alpha = sc;
+    d.c16 = hs16; d.ldc16 = 64;
+    QBLK_TRY(gemm(d, st));
+  }
+  QBLK_TRY(lora_pack16(p, g.id3, g.outd, g.n, in, 1, w.bx16, st));
+  GemmDesc d = base(Layout::NT, T, g.N, in);
+  d.a = x16; d.lda = in; d.a_src = Src::F16;
+  d.b = rows3(g.outd[0], g.outd[1], g.outd[2]); d.ldb = in;
+  d.b_src = Src::NF4;
+  d.nf4 = nf4seg(p, g.id3[0], g.id3[1], g.id3[2]);
+  d.c = seg1(out, T); d.ldc = g.N;
+  d.r = res; d.ldr = g.N;
+  d.ext16_a = hs16; d.ext16_lda = 64;
+  d.ext16_b = w.bx16; d.ext16_ldb = 64;
+  if (gemm_nf4_fused(d)) return gemm(d, st);
+  // dense fallback: decoded copy, then the LoRA tile as an accumulating product
+  QBLK_TRY(dequant_group(p, g.id3, g.outd, g.n, in, w.w16, st));
+  GemmDesc e = base(Layout::NT, T, g.N, in);
+  e.a = x16; e.lda = in; e.a_src = Src::F16;
+  e.b = seg1(w.w16, g.N); e.ldb = in; e.b_src = Src::F16;
+  e.c = seg1(out, T); e.ldc = g.N;
+  e.r = res; e.ldr = g.N;
+  QBLK_TRY(gemm(e, st));
+  GemmDesc u = base(Layout::NT, T, g.N, 64);
+  u.a = hs16; u.lda = 64; u.a_src = Src::F16;
+  u.b = seg1(w.bx16, g.N); u.ldb = 64; u.b_src = Src::F16;
+  u.c = seg1(out, T); u.ldc = g.N;
+  u.accumulate = 1;
+  return gemm(u, st);
+}
+
+// Backward of one group on the fp16 path, dY given as its fp16 copy dy16
+// [T, N] (written by its producer):
+//   dh = s dY16 B (over 64 columns; fp32 dh and its fp16 copy);
+//   dX = dY16 W~ + dh16 [A stacked], fused (fp16 copy into dx16 if set);
+//   dB_k = dY16_k^T hs16_k (diagonal blocks); dA_k = dh16_k^T X16.
 int nf4_bwd16(const qblk_nf4_block_params& p, const qblk_lora_grads& gr, const Nf4Scratch& w, int T, int in,
-              const float* dy, const f16* x16, const float* x, const float* h, std::initializer_list<int> ids,
-              std::initializer_list<int> outs, float* dh, float* dx, hipStream_t st) {
-  const int r = p.rank, n = (int)ids.size();
-  const float sc = p.alpha / (float)r;
-  int outd[3] = {0, 0, 0}, id3[3] = {-1, -1, -1}, j = 0;
-  for (int o : outs) outd[j++] = o;
-  j = 0;
-  for (int id : ids) id3[j++] = id;
-  int Nout = 0;
-  for (int k = 0; k < n; ++k) Nout += outd[k];
-  (void)x16;
-  int col = 0;
-  for (int k = 0; k < n; ++k) {  // dh[:, k r:(k+1) r] = s dY_k B_k
-    GemmDesc g = base(Layout::NN, T, r, outd[k]);
-    g.a = dy + col; g.lda = Nout;
-    g.b = seg1(p.lora_b[id3[k]], outd[k]); g.ldb = r;
-    g.c = seg1(dh + k * r, T); g.ldc = n * r;
-    g.alpha = sc;
-    QBLK_TRY(gemm(g, st));
-    col += outd[k];
+              const f16* dy16, const f16* x16, const f16* hs16, const Group& g, float* dh, float* dx, f16* dx16,
+              hipStream_t st) {
+  const float sc = p.alpha / (float)p.rank;
+  const int r = p.rank, n = g.n;
+  QBLK_TRY(lora_pack16(p, g.id3, g.outd, n, in, 2, w.bt16, st));
+  {
+    GemmDesc d = base(Layout::NT, T, 64, g.N);
+    d.a = dy16; d.lda = g.N; d.a_src = Src::F16;
+    d.b = seg1(w.bt16, 64); d.ldb = g.N; d.b_src = Src::F16;
+    d.c = seg1(dh, T); d.ldc = 64;
+    d.alpha = sc;
+    d.c16 = w.dh16; d.ldc16 = 64;
+    QBLK_TRY(gemm(d, st));
   }
-  QBLK_TRY(cast_f16(T, Nout, dy, Nout, w.dy16, Nout, nullptr, 0, st));
-  QBLK_TRY(dequant_group(p, id3, outd, n, in, w.w16, st));
-  {  // dX = dY W~
-    GemmDesc g = base(Layout::NN, T, in, Nout);
-    g.a = w.dy16; g.lda = Nout; g.a_src = Src::F16;
-    g.b = seg1(w.w16, Nout); g.ldb = in; g.b_src = Src::F16;
-    g.c = seg1(dx, T); g.ldc = in;
-    QBLK_TRY(gemm(g, st));
+  QBLK_TRY(lora_pack16(p, g.id3, g.outd, n, in, 0, w.a16x, st));
+  {
+    GemmDesc d = base(Layout::NN, T, in, g.N);
+    d.a = dy16; d.lda = g.N; d.a_src = Src::F16;
+    d.b = rows3(g.outd[0], g.outd[1], g.outd[2]); d.ldb = in;
+    d.b_src = Src::NF4;
+    d.nf4 = nf4seg(p, g.id3[0], g.id3[1], g.id3[2]);
+    d.c = seg1(dx, T); d.ldc = in;
+    d.c16 = dx16; d.ldc16 = in;
+    d.ext16_a = w.dh16; d.ext16_lda = 64;
+    d.ext16_b = w.a16x; d.ext16_ldb = in;
+    if (gemm_nf4_fused(d)) {
+      QBLK_TRY(gemm(d, st));
+    } else {
+      QBLK_TRY(dequant_group(p, g.id3, g.outd, n, in, w.w16, st));
+      GemmDesc e = base(Layout::NN, T, in, g.N);
+      e.a = dy16; e.lda = g.N; e.a_src = Src::F16;
+      e.b = seg1(w.w16, g.N); e.ldb = in; e.b_src = Src::F16;
+      e.c = seg1(dx, T); e.ldc = in;
+      QBLK_TRY(gemm(e, st));
+      GemmDesc u = base(Layout::NN, T, in, 64);
+      u.a = w.dh16; u.lda = 64; u.a_src = Src::F16;
+      u.b = seg1(w.a16x, 64); u.ldb = in; u.b_src = Src::F16;
+      u.c = seg1(dx, T); u.ldc = in;
+      u.c16 = dx16; u.ldc16 = in;
+      u.accumulate = 1;
+      QBLK_TRY(gemm(u, st));
+    }
   }
-  {  // dX += dh [A_0; A_1; A_2]
-    GemmDesc g = base(Layout::NN, T, in, n * r);
-    g.a = dh; g.lda = n * r;
-    g.b = rows3(r, n > 1 ? r : 0, n > 2 ? r : 0);
-    for (int k = 0; k < n; ++k) g.b.p[k] = p.lora_a[id3[k]];
-    g.ldb = in;
-    g.c = seg1(dx, T); g.ldc = in;
-    g.accumulate = 1;
-    QBLK_TRY(gemm(g, st));
+  {  // dB_k = dY16_k^T hs16_k (s is in hs16)
+    GemmDesc d = base(Layout::TN, g.N, 64, T);
+    d.a = dy16; d.lda = g.N; d.a_src = Src::F16;
+    d.b = seg1(hs16, T); d.ldb = 64; d.b_src = Src::F16;
+    d.c = rows3(g.outd[0], g.outd[1], g.outd[2]);
+    for (int k = 0; k < n; ++k) d.c.p[k] = gr.lora_b[g.id3[k]];
+    d.ldc = r;
+    d.c_cols_blockdiag = r;
+    QBLK_TRY(gemm(d, st));
   }
-  {  // dB_k = s dY_k^T h_k
-    GemmDesc g = base(Layout::TN, Nout, n * r, T);
-    g.a = dy; g.lda = Nout;
-    g.b = seg1(h, T); g.ldb = n * r;
-    g.c = rows3(outd[0], outd[1], outd[2]);
-    for (int k = 0; k < n; ++k) g.c.p[k] = gr.lora_b[id3[k]];
-    g.ldc = r;
-    g.c_cols_blockdiag = r;
-    g.alpha = sc;
-    QBLK_TRY(gemm(g, st));
-  }
-  {  // dA_k = dh_k^T X
-    GemmDesc g = base(Layout::TN, n * r, in, T);
-    g.a = dh; g.lda = n * r;
-    g.b = seg1(x, T); g.ldb = in;
-    g.c = rows3(r, n > 1 ? r : 0, n > 2 ? r : 0);
-    for (int k = 0; k < n; ++k) g.c.p[k] = gr.lora_a[id3[k]];
-    g.ldc = in;
-    QBLK_TRY(gemm(g, st));
+  {  // dA_k = dh16_k^T X16
+    GemmDesc d = base(Layout::TN, n * r, in, T);
+    d.a = w.dh16; d.lda = 64; d.a_src = Src::F16;
+    d.b = seg1(x16, T); d.ldb = in; d.b_src = Src::F16;
+    d.c = rows3(r, n > 1 ? r : 0, n > 2 ? r : 0);
+    for (int k = 0; k < n; ++k) d.c.p[k] = gr.lora_a[g.id3[k]];
+    d.ldc = in;
+    QBLK_TRY(gemm(d, st));
   }
   return QBLK_OK;
 }
@@ -391,27 +483,32 @@ extern "C" int32_t qblk_block_forward_nf4_lora(const qblk_config* cfg, const qbl
   t_ws = &w.base;
   ProjFwd proj;
   const bool f16p = w.w16 != nullptr;
+  const Group gq({PQ, PK, PV}, {qd, kvd, kvd}), go({PO}, {h}), ggu({PG, PU}, {I, I}), gd({PD}, {h});
   proj.qkv = [&](const float* n1, float* qkv, hipStream_t s_) {
+    if (f16p) return nf4_fwd16(P, w, T, h, s.base.n1_16, gq, s.h_qkv, s.hs16_qkv, nullptr, qkv, s_);
     QBLK_TRY(lora_down(P, T, h, n1, {PQ, PK, PV}, s.h_qkv, s_));
-    if (f16p) return nf4_fwd16(P, w, T, h, s.base.n1_16, {PQ, PK, PV}, {qd, kvd, kvd}, s.h_qkv, nullptr, qkv, s_);
     return nf4_fwd(P, T, h, n1, {PQ, PK, PV}, {qd, kvd, kvd}, s.h_qkv, nullptr, qkv, s_);
   };
   proj.o = [&](const float* o, const float* res, float* out, hipStream_t s_) {
+    if (f16p) return nf4_fwd16(P, w, T, qd, s.base.o16, go, s.h_o, s.hs16_o, res, out, s_);
     QBLK_TRY(lora_down(P, T, qd, o, {PO}, s.h_o, s_));
-    if (f16p) return nf4_fwd16(P, w, T, qd, s.base.o16, {PO}, {h}, s.h_o, res, out, s_);
     return nf4_fwd(P, T, qd, o, {PO}, {h}, s.h_o, res, out, s_);
   };
   proj.gate_up = [&](const float* n2, float* gu, hipStream_t s_) {
+    if (f16p) return nf4_fwd16(P, w, T, h, s.base.n2_16, ggu, s.h_gu, s.hs16_gu, nullptr, gu, s_);
     QBLK_TRY(lora_down(P, T, h, n2, {PG, PU}, s.h_gu, s_));
-    if (f16p) return nf4_fwd16(P, w, T, h, s.base.n2_16, {PG, PU}, {I, I}, s.h_gu, nullptr, gu, s_);
     return nf4_fwd(P, T, h, n2, {PG, PU}, {I, I}, s.h_gu, nullptr, gu, s_);
   };
   proj.down = [&](const float* sv, const float* res, float* out, hipStream_t s_) {
+    if (f16p) return nf4_fwd16(P, w, T, I, s.base.s16, gd, s.h_d, s.hs16_d, res, out, s_);
     QBLK_TRY(lora_down(P, T, I, sv, {PD}, s.h_d, s_));
-    if (f16p) return nf4_fwd16(P, w, T, I, s.base.s16, {PD}, {h}, s.h_d, res, out, s_);
     return nf4_fwd(P, T, I, sv, {PD}, {h}, s.h_d, res, out, s_);
   };
-  const int rc = block_forward_impl(c, proj, P.g_in, P.g_post, P.g_q, P.g_k, x, y, s.base, st);
+  // on the fp16 path every product reads the fp16 copies of n1, n2 and s:
+  // their fp32 forms are not written
+  Saved sv = s.base;
+  if (f16p) sv.n1 = sv.n2 = sv.s = nullptr;
+  const int rc = block_forward_impl(c, proj, P.g_in, P.g_post, P.g_q, P.g_k, x, y, sv, st);
   t_ws = nullptr;
   return rc;
 }
@@ -439,26 +536,49 @@ extern "C" int32_t qblk_block_backward_nf4_lora(const qblk_config* cfg, const qb
   t_ws = &w.base;
   ProjBwd proj;
   const bool f16p = w.w16 != nullptr;
+  const Group gq({PQ, PK, PV}, {qd, kvd, kvd}), go({PO}, {h}), ggu({PG, PU}, {I, I}), gd({PD}, {h});
+  // fp16 path: each output gradient's fp16 copy comes from its producer
+  // (into a16) and the hooks get a null fp32 pointer, as in the dense block
+  f16* const dy16 = w.base.a16;
+  // the upstream gradient of the block (and any output gradient that came
+  // as fp32) is cast once into the fp16 slot
+  auto as16 = [&](const float* g, int n, hipStream_t s_) -> int {
+    return g ? cast_f16(T, n, g, n, dy16, n, nullptr, 0, s_) : QBLK_OK;
+  };
   proj.down = [&](const float* dyv, const float* sv, float* ds, hipStream_t s_) {
-    if (f16p) return nf4_bwd16(P, G, w, T, I, dyv, s.base.s16, sv, s.h_d, {PD}, {h}, w.dh_d, ds, s_);
+    if (f16p) {
+      QBLK_TRY(as16(dyv, h, s_));
+      return nf4_bwd16(P, G, w, T, I, dy16, s.base.s16, s.hs16_d, gd, w.dh_d, ds, nullptr, s_);
+    }
     return nf4_bwd(P, G, T, I, dyv, sv, s.h_d, {PD}, {h}, w.dh_d, ds, s_);
   };
   proj.gate_up = [&](const float* dgu, const float* n2, float* dn2, hipStream_t s_) {
-    if (f16p) return nf4_bwd16(P, G, w, T, h, dgu, s.base.n2_16, n2, s.h_gu, {PG, PU}, {I, I}, w.dh_gu, dn2, s_);
+    if (f16p) {
+      QBLK_TRY(as16(dgu, 2 * I, s_));
+      return nf4_bwd16(P, G, w, T, h, dy16, s.base.n2_16, s.hs16_gu, ggu, w.dh_gu, dn2, nullptr, s_);
+    }
     return nf4_bwd(P, G, T, h, dgu, n2, s.h_gu, {PG, PU}, {I, I}, w.dh_gu, dn2, s_);
   };
   proj.o = [&](const float* dr1, const float* o, float* d_o, hipStream_t s_) {
-    if (f16p) return nf4_bwd16(P, G, w, T, qd, dr1, s.base.o16, o, s.h_o, {PO}, {h}, w.dh_o, d_o, s_);
+    // the attention backward reads dO's fp16 copy
+    if (f16p) {
+      QBLK_TRY(as16(dr1, h, s_));
+      return nf4_bwd16(P, G, w, T, qd, dy16, s.base.o16, s.hs16_o, go, w.dh_o, d_o,
+                       s.base.q16 ? w.base.do16 : nullptr, s_);
+    }
     return nf4_bwd(P, G, T, qd, dr1, o, s.h_o, {PO}, {h}, w.dh_o, d_o, s_);
   };
   proj.qkv = [&](const float* dqkv, const float* n1, float* dn1, hipStream_t s_) {
-    if (f16p)
-      return nf4_bwd16(P, G, w, T, h, dqkv, s.base.n1_16, n1, s.h_qkv, {PQ, PK, PV}, {qd, kvd, kvd}, w.dh_qkv,
-                       dn1, s_);
+    if (f16p) {
+      QBLK_TRY(as16(dqkv, qd + 2 * kvd, s_));
+      return nf4_bwd16(P, G, w, T, h, dy16, s.base.n1_16, s.hs16_qkv, gq, w.dh_qkv, dn1, nullptr, s_);
+    }
     return nf4_bwd(P, G, T, h, dqkv, n1, s.h_qkv, {PQ, PK, PV}, {qd, kvd, kvd}, w.dh_qkv, dn1, s_);
   };
+  Scratch wb16 = w.base;
+  wb16.prod16 = f16p;
   const int rc = block_backward_impl(c, proj, P.g_in, P.g_post, P.g_q, P.g_k, x, dy, s.base, dx, w.sink_h,
-                                     w.sink_h + h, w.sink_d, w.sink_d + c.head_dim, w.base, st);
+                                     w.sink_h + h, w.sink_d, w.sink_d + c.head_dim, wb16, st);
   t_ws = nullptr;
   return rc;
 }
