@@ -136,7 +136,14 @@ class Nf4Block:
                                     self.rank, self.alpha, self.x, self.y, self.saved, self.scratch)
         return self.y
 
-    def backward(self):
+    def backward(self, recompute=False):
+        """recompute=True: the forward's activations are not taken from an
+        earlier forward call; the forward is re-run first (into the same
+        `saved` workspace), as [block] CudaNf4TransformerBlock::backward
+        re-runs the forward before its backward, so one workspace can serve
+        many blocks. The results are the same bit for bit."""
+        if recompute:
+            self.forward()
         qblk.block_backward_nf4_lora(self.c, self.codes, self.absmax, self.lora_a, self.lora_b, self.gammas,
                                      self.rank, self.alpha, self.x, self.dy, self.saved, self.dx, self.grad_a,
                                      self.grad_b, self.scratch)

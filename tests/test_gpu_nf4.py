@@ -57,3 +57,26 @@ def test_nf4_lora_block(name, c, rank, b_std):
             check("dA_" + n, blk.grad_a[n], da_ref[n], FP16_TOL, rep)
         check("dB_" + n, blk.grad_b[n], db_ref[n], FP16_TOL, rep)
     announce("  " + " ".join(f"{k}={v:.1e}" for k, v in rep.items()))
+
+
+def test_nf4_backward_recompute_bitwise():
+    """backward(recompute=True) re-runs the forward into the workspace first:
+    with the workspace overwritten after the forward, dx and the LoRA
+    gradients equal those of the plain forward + backward bit for bit."""
+    need_gpu()
+    c = SMALL.with_tokens(seq=64, batch=2)
+    announce(f"nf4 lora block recompute T={c.tokens}")
+    inp = synth.nf4_lora_inputs(c, rank=8, b_std=1e-3)
+    blk = Nf4Block(c, 8, 16.0)
+    blk.load(inp)
+    blk.forward()
+    dx0 = blk.backward().clone()
+    ga0 = {n: t.clone() for n, t in blk.grad_a.items()}
+    gb0 = {n: t.clone() for n, t in blk.grad_b.items()}
+    blk.saved.fill_(0x7F)  # the saved activations are gone
+    dx1 = blk.backward(recompute=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dx0, dx1)
+    for n in synth.PROJ_NAMES:
+        assert torch.equal(ga0[n], blk.grad_a[n]), n
+        assert torch.equal(gb0[n], blk.grad_b[n]), n

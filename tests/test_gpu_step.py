@@ -226,3 +226,40 @@ def test_stack_micro_batches():
         assert abs(loss - loss0) <= 1e-5 * abs(loss0), (k, loss, loss0)
         assert abs(norm - norm0) <= FP32_TOL * norm0, (k, norm, norm0)
         check(f"grads k={k} vs k=1", g, g0.cpu().numpy().astype(np.float64), FP32_TOL)
+
+
+@pytest.mark.parametrize("segments", [1, 2, 4])
+def test_stack_checkpoint_segments(segments):
+    """Activation checkpointing: a 4-layer stack with its layers in 1, 2 or
+    4 segments, recomputed from their checkpoints in the backward (all but
+    the last segment). Loss, norm, every gradient and
+    the updated weights equal those of the step that keeps every layer's
+    activations bit for bit, and match oracle.stack_step; the kept
+    activations shrink with the segment length."""
+    need_gpu()
+    from bwd_rmsnorm_qkv_amd.stack import StackStep
+    c = synth.STACK36_SMALL.with_tokens(seq=128, batch=2)
+    layers, vocab = 4, 2048
+    inp = synth.stack_inputs(c, layers=layers, vocab=vocab, seed=5)
+    announce(f"stack checkpoint segments={segments}")
+    runs = []
+    for seg in (None, segments):
+        st = StackStep(c, layers, vocab, checkpoint_segments=seg)
+        st.load(inp)
+        st.step()
+        torch.cuda.synchronize()
+        runs.append((st, st.loss(), st.norm.clone(), st.g.buf.clone(), st.w.buf.clone(), st.dx.clone()))
+    (s0, l0, n0, g0, w0, dx0), (s1, l1, n1, g1, w1, dx1) = runs
+    assert l0 == l1 and torch.equal(n0, n1)
+    assert torch.equal(g0, g1) and torch.equal(w0, w1) and torch.equal(dx0, dx1)
+    announce(f"  kept activations: {s0.workspace_bytes() / 2**20:.1f} MiB without, "
+             f"{s1.workspace_bytes() / 2**20:.1f} MiB with {segments} segment(s)")
+    if segments > 1:
+        assert s1.workspace_bytes() < s0.workspace_bytes()
+    ref = oracle.stack_step(c, inp["layers"], inp["x"], inp["g_final"], inp["w_lm"], inp["targets"],
+                            synth.CLIP_MAX_NORM, synth.ADAMW)
+    assert abs(l1 - ref["loss"]) <= 1e-5 * abs(ref["loss"])
+    names = [f"{l}.{n}" for l in range(layers) for n in qblk.PARAMS] + ["g_final", "w_lm"]
+    for i, n in enumerate(names):
+        check("g_" + n, s1.g[n], ref["grads"][i], FP32_TOL)
+    check("dx", dx1, ref["dx"], FP32_TOL)
