@@ -17,10 +17,12 @@ Also reported in the same JSON line:
   cpu_baseline  the CPU oracle (numpy float64) on a bounded sample of the
                 same workload, on this host's cores;
   extra         the 36-layer stack training step (fused CE, global clip,
-                AdamW), the frozen-NF4 + LoRA block at seq 2048, and the
-                block step with clip + AdamW.
+                AdamW), also with activation checkpointing (6 segments),
+                the frozen-NF4 + LoRA block at seq 2048 (each with its
+                roofline fraction), and the Qwen3-4B block's whole training
+                step (fwd + bwd + clip + AdamW writing the fp16 weights).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu] [--only NAME]
 """
 import argparse
 import json
@@ -50,7 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["stack36_train_step", "nf4_lora_block"],
+    ap.add_argument("--only", choices=["stack36_train_step", "stack36_train_step_checkpointed", "nf4_lora_block",
+                                       "qwen3_4b_block_train_step"],
                     help="time only this workload (for kernel traces) and print its JSON object")
     return ap.parse_args()
 
@@ -187,6 +190,9 @@ def gemm_roofline(c, torch, qblk, reps):
     return {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK, "unit": "TFLOP/s",
         "frac": round(achieved / MFMA_F16_PEAK, 4), "traffic": gemm_traffic(),
+        "traffic_source": "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of the same 12 launches, scaled by a 256 MiB "
+                          "copy (profiles/block_gemm_hbm_traffic_qwen3_4b_s512.md; null when the GEMM sources "
+                          "changed since)",
         "kernel": "gemm_dma_kernel (the 12 GEMM launches of one block fwd+bwd, split-K reduce included)",
         "flops_per_step": flops, "gemm_ms_per_step": round(step_ms, 4),
         "avg_launch_us": round(1e3 * step_ms / len(bufs), 2),
@@ -202,13 +208,13 @@ def stack_param_count(synth):
 
 
 def hbm_kernels(torch, qblk, synth, reps=10):
-    """The memory-bound steps the library exports as calls, each timed
-    alone with HIP events on the current stream (reps calls after two
-    warm-ups): algorithmic bytes / time against the HBM peak. AdamW and the
-    squared sum run over the 36-layer stack's parameter count (working sets
-    of GBs, far beyond the 256 MB last-level cache); the norms run at the
-    Qwen3-4B block shape, whose working set (tens of MB) the last-level cache
-    can hold, so their rate can exceed what HBM alone delivers."""
+    """The memory-bound steps the library exports as calls, each timed alone
+    with HIP events on the current stream (reps calls after two warm-ups):
+    algorithmic bytes / time against the HBM peak. Working sets are sized
+    well beyond the 256 MB last-level cache (the `shape` of each row), so
+    the rate is HBM's; the norms are also timed at the Qwen3-4B block shape
+    the block step runs (512 rows: 10-16 MB, cache-resident and
+    launch-latency bound)."""
     out = []
 
     def add(name, workload, nbytes, fn):
@@ -224,26 +230,65 @@ def hbm_kernels(torch, qblk, synth, reps=10):
     v = torch.zeros(n, device="cuda")
     add("adamw_step", f"{n} fp32 parameters (36-layer stack): w, g, m, v read; w, m, v written", 28 * n,
         lambda: qblk.adamw_step([w], [g], [m], [v], 1e-3, 0.9, 0.999, 1e-8, 0.01, 1))
+    w16 = torch.empty(n, dtype=torch.float16, device="cuda")
+    add("adamw_step_pack16", f"{n} fp32 parameters: as adamw_step plus the fp16 copy of w written", 30 * n,
+        lambda: qblk.adamw_step_pack16([w], [g], [m], [v], [w16], 1e-3, 0.9, 0.999, 1e-8, 0.01, 1))
+    del w16
     norm = torch.zeros(1, device="cuda")
     scale = torch.zeros(1, device="cuda")
     cs = torch.empty(max(qblk.clip_workspace_size([g]), 16), dtype=torch.uint8, device="cuda")
     add("clip_grad_norm (squared sum)", f"{n} fp32 gradients read once", 4 * n,
         lambda: qblk.clip_grad_norm([g], 1.0, 0, norm, scale, cs))
-    del w, m, v, cs
+    del w, m, v, cs, g
     c = synth.QWEN3_4B_BLOCK
-    T, h = c.tokens, c.hidden
-    x = torch.randn(T, h, device="cuda")
-    dy = torch.randn(T, h, device="cuda")
-    gam = torch.ones(h, device="cuda")
-    y = torch.empty_like(x)
-    rho = torch.empty(T, device="cuda")
-    add("rmsnorm_forward", f"[{T}, {h}] fp32: x read, y written", 2 * 4 * T * h,
-        lambda: qblk.rmsnorm_forward(T, h, 1e-6, x, None, gam, y, None, rho))
-    dx = torch.empty_like(x)
-    dgam = torch.empty(h, device="cuda")
-    rs = torch.empty(max(qblk.rmsnorm_workspace_size(T, h), 16), dtype=torch.uint8, device="cuda")
-    add("rmsnorm_backward", f"[{T}, {h}] fp32: x, dy read, dx written", 3 * 4 * T * h,
-        lambda: qblk.rmsnorm_backward(T, h, 1e-6, x, gam, dy, None, dx, dgam, rs))
+    h = c.hidden
+    for T, tag in ((c.tokens, "block shape"), (16384, "HBM-resident")):
+        x = torch.randn(T, h, device="cuda")
+        dy = torch.randn(T, h, device="cuda")
+        gam = torch.ones(h, device="cuda")
+        y = torch.empty_like(x)
+        rho = torch.empty(T, device="cuda")
+        add("rmsnorm_forward", f"[{T}, {h}] fp32 ({tag}): x read, y written", 2 * 4 * T * h,
+            lambda: qblk.rmsnorm_forward(T, h, 1e-6, x, None, gam, y, None, rho))
+        dx = torch.empty_like(x)
+        dgam = torch.empty(h, device="cuda")
+        rs = torch.empty(max(qblk.rmsnorm_workspace_size(T, h), 16), dtype=torch.uint8, device="cuda")
+        add("rmsnorm_backward", f"[{T}, {h}] fp32 ({tag}): x, dy read, dx written", 3 * 4 * T * h,
+            lambda: qblk.rmsnorm_backward(T, h, 1e-6, x, gam, dy, None, dx, dgam, rs))
+        del x, dy, y, dx, rs
+    T, I = 4096, c.intermediate
+    gu = torch.randn(T, 2 * I, device="cuda")
+    sw = torch.empty(T, I, device="cuda")
+    add("swiglu_forward", f"gu [{T}, {2 * I}] read, s [{T}, {I}] written (fp32)", 3 * 4 * T * I,
+        lambda: qblk.swiglu_forward(T, I, gu, sw))
+    dgu = torch.empty_like(gu)
+    add("swiglu_backward", f"gu [{T}, {2 * I}], ds [{T}, {I}] read, dgu written (fp32)", 5 * 4 * T * I,
+        lambda: qblk.swiglu_backward(T, I, gu, sw, dgu))
+    del gu, sw, dgu
+    T, S, H, KV, d = 8192, 512, c.heads, c.kv_heads, c.head_dim
+    ld = (H + 2 * KV) * d
+    qkv = torch.randn(T, ld, device="cuda")
+    gq, gk = torch.ones(d, device="cuda"), torch.ones(d, device="cuda")
+    qr, kr = torch.empty(T, H * d, device="cuda"), torch.empty(T, KV * d, device="cuda")
+    rq, rk = torch.empty(T, H, device="cuda"), torch.empty(T, KV, device="cuda")
+    qs = torch.empty(max(qblk.qk_norm_rope_workspace_size(T, S, H, KV, d), 16), dtype=torch.uint8, device="cuda")
+    add("qk_norm_rope_forward", f"q, k of qkv [{T}, {ld}] read, qr, kr written (fp32, 32/8 heads, d128)",
+        2 * 4 * T * (H + KV) * d,
+        lambda: qblk.qk_norm_rope_forward(T, S, H, KV, d, 1, 1e-6, 1e6, qkv, ld, gq, gk, qr, kr, rq, rk, qs))
+    dqkv = torch.empty_like(qkv)
+    dg1, dg2 = torch.empty(d, device="cuda"), torch.empty(d, device="cuda")
+    add("qk_norm_rope_backward", f"q, k of qkv, dqr, dkr read; dq, dk written (fp32, [{T}] tokens)",
+        3 * 4 * T * (H + KV) * d,
+        lambda: qblk.qk_norm_rope_backward(T, S, H, KV, d, 1, 1e-6, 1e6, qkv, ld, gq, gk, qr, kr, dqkv, dg1, dg2,
+                                           qs))
+    del qkv, qr, kr, dqkv, qs
+    T, V = synth.STACK36_SMALL.tokens, synth.STACK_VOCAB
+    z = torch.randn(T, V, device="cuda")
+    tgt = torch.randint(0, V, (T,), dtype=torch.int32, device="cuda")
+    lp, am = torch.empty(T, device="cuda"), torch.empty(T, dtype=torch.int32, device="cuda")
+    add("cross_entropy_rows", f"logits [{T}, {V}] fp32 read and overwritten by their gradient", 2 * 4 * T * V,
+        lambda: qblk.cross_entropy_rows(T, V, z, tgt, 1.0 / T, lp, am))
+    del z
     numel = 2 * c.intermediate * h
     codes = torch.randint(0, 256, (numel // 2,), dtype=torch.uint8, device="cuda")
     absmax = torch.rand(numel // 64, device="cuda")
@@ -253,13 +298,29 @@ def hbm_kernels(torch, qblk, synth, reps=10):
     return out
 
 
-def cpu_baseline(c, inp, budget_s=12.0):
-    import oracle
+def host_cores():
+    """(threads the BLAS pool runs, cores in this process's affinity mask,
+    CPU model)."""
+    aff = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [aff])
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        blas = aff
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return blas, aff, model
+
+
+def cpu_baseline(c, inp, budget_s=10.0):
+    import oracle
+    blas, aff, model = host_cores()
     n, t0 = 0, time.perf_counter()
     while True:
         y, cache = oracle.block_forward(c, inp["params"], inp["x"])
@@ -268,19 +329,135 @@ def cpu_baseline(c, inp, budget_s=12.0):
         if time.perf_counter() - t0 > budget_s or n >= 5:
             break
     dt = (time.perf_counter() - t0) / n
-    return {"value": round(c.tokens / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": round(c.tokens / dt, 2), "unit": "tokens/s", "cores": blas, "kind": "oracle",
             "sample": f"{n} x full Qwen3-4B-shaped block fwd+bwd (512 tokens), numpy float64, "
-                      f"{dt:.2f} s each"}
+                      f"{dt:.2f} s each", "affinity_cores": aff, "cpu_model": model}
 
 
-def extra_stack(torch, qblk, synth, steps, warmup):
+def cpu_baselines_other(synth):
+    """The oracle on the other workloads, each on a bounded sample scaled to
+    the workload's unit (tokens/s of a block or of a stack step)."""
+    import oracle
+    blas, aff, model = host_cores()
+    out = []
+
+    def tm(fn, reps=1):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        return (time.perf_counter() - t0) / reps
+
+    def block_fb(c, inp):
+        _, cache = oracle.block_forward(c, inp["params"], inp["x"])
+        return oracle.block_backward(c, inp["params"], cache, inp["dy"])
+
+    c = synth.TINY_BLOCK
+    inp = synth.block_inputs(c)
+    dt = tm(lambda: block_fb(c, inp), 20)
+    out.append({"workload": "tiny block fwd+bwd (32 tokens, fp32)", "value": round(c.tokens / dt, 1),
+                "unit": "tokens/s", "sample": f"20 runs, {dt * 1e3:.1f} ms each"})
+    c = synth.SMALL_BLOCK
+    inp = synth.block_inputs(c)
+
+    def small_step():
+        _, g = block_fb(c, inp)
+        names = list(g)
+        _, _, cl = oracle.global_clip([g[k] for k in names], synth.CLIP_MAX_NORM)
+        for k, gg in zip(names, cl):
+            z = np.zeros(np.shape(gg))
+            oracle.adamw_update(inp["params"][k], gg, z, z, step=1, **synth.ADAMW)
+    dt = tm(small_step, 2)
+    out.append({"workload": "small block fwd+bwd + clip + AdamW (1024 tokens, fp32)",
+                "value": round(c.tokens / dt, 1), "unit": "tokens/s", "sample": f"2 runs, {dt:.2f} s each"})
+    # 36-layer stack step: one layer fwd+bwd, the LM head + CE and AdamW over
+    # 1/16 of the parameters, each timed once and scaled to the whole step
+    c = synth.STACK36_SMALL
+    inp = synth.block_inputs(c)
+    t_layer = tm(lambda: block_fb(c, inp))
+    rng = np.random.default_rng(0)
+    V = synth.STACK_VOCAB
+    w_lm = (rng.standard_normal((V, c.hidden)) * 0.02).astype(np.float32)
+    tgt = rng.integers(0, V, c.tokens)
+    t_lm = tm(lambda: oracle.lm_head_cross_entropy(inp["x"], np.ones(c.hidden, np.float32), w_lm, tgt, c.eps))
+    del w_lm
+    n_par = stack_param_count(synth)
+    part = n_par // 16
+    wp, gp = rng.standard_normal(part) * 0.02, rng.standard_normal(part) * 1e-3
+    t_adam = 16 * tm(lambda: oracle.adamw_update(wp, gp, np.zeros(part), np.zeros(part), step=1, **synth.ADAMW))
+    step_s = synth.STACK_LAYERS * t_layer + t_lm + t_adam
+    out.append({"workload": "36-layer stack training step (1024 tokens, vocab 151936, fp32)",
+                "value": round(c.tokens / step_s, 2), "unit": "tokens/s",
+                "sample": f"1 layer fwd+bwd {t_layer:.2f} s x 36 + LM head/CE {t_lm:.2f} s + AdamW "
+                          f"{t_adam:.2f} s (1/16 of the parameters, x 16) = {step_s:.1f} s per step"})
+    # NF4 + LoRA block at seq 2048: one forward + backward
+    c = synth.NF4_LORA_QWEN3_4B
+    inp = synth.nf4_lora_inputs(c, b_std=1e-3)
+    deq = {}
+    for k in synth.PROJ_NAMES:
+        packed, scales, _ = oracle.nf4_quantize(inp["params"][k])
+        deq[k] = oracle.nf4_dequantize(packed, scales, inp["params"][k].shape)
+    gam = {k: inp["params"][k] for k in ("g_in", "g_post", "g_q", "g_k")}
+    sc = synth.LORA_ALPHA / synth.LORA_RANK
+
+    def nf4_fb():
+        _, cache = oracle.nf4_block_forward(c, gam, deq, inp["lora_a"], inp["lora_b"], inp["x"], sc)
+        oracle.nf4_block_backward(c, gam, deq, inp["lora_a"], inp["lora_b"], cache, inp["dy"], sc)
+    dt = tm(nf4_fb)
+    out.append({"workload": "NF4 + LoRA Qwen3-4B-shaped block fwd+bwd (2048 tokens)",
+                "value": round(c.tokens / dt, 1), "unit": "tokens/s", "sample": f"1 run, {dt:.2f} s"})
+    for o in out:
+        o.update({"cores": blas, "kind": "oracle", "affinity_cores": aff, "cpu_model": model})
+    return out
+
+
+def stack_flops(synth):
+    """Algorithmic FLOPs of one 36-layer stack step: per layer 6 T P of the
+    projections (fwd, dX, dW) plus the causal attention (fwd 2 2 S^2/2 d
+    per head, backward twice that), and the LM head's 6 T V h."""
+    c, L, V = synth.STACK36_SMALL, synth.STACK_LAYERS, synth.STACK_VOCAB
+    T, h, qd, kvd, I, d = c.tokens, c.hidden, c.q_dim, c.kv_dim, c.intermediate, c.head_dim
+    P = h * (qd + 2 * kvd) + qd * h + 3 * h * I
+    attn = 3 * 2 * 2 * (c.seq * c.seq / 2) * d * c.heads * c.batch
+    return L * (6 * T * P + attn) + 6 * T * V * h
+
+
+def nf4_flops(synth):
+    """fwd + dX of the 7 projections (4 T P; no base dW), causal attention
+    fwd + bwd, and the rank-r LoRA products (h, dh, dA, dB and their share
+    of the fused products: 2 T r (in + out) per projection, x 4)."""
+    c, r = synth.NF4_LORA_QWEN3_4B, synth.LORA_RANK
+    T, h, qd, kvd, I, d = c.tokens, c.hidden, c.q_dim, c.kv_dim, c.intermediate, c.head_dim
+    P = h * (qd + 2 * kvd) + qd * h + 3 * h * I
+    attn = 3 * 2 * 2 * (c.seq * c.seq / 2) * d * c.heads * c.batch
+    io = [(h, qd), (h, kvd), (h, kvd), (qd, h), (h, I), (h, I), (I, h)]
+    lora = sum(4 * 2 * T * r * (i + o) for i, o in io)
+    return 4 * T * P + attn + lora
+
+
+def extra_stack(torch, qblk, synth, steps, warmup, checkpoint_segments=None):
     from bwd_rmsnorm_qkv_amd.stack import StackStep
-    st = StackStep(synth.STACK36_SMALL, synth.STACK_LAYERS, synth.STACK_VOCAB)
+    st = StackStep(synth.STACK36_SMALL, synth.STACK_LAYERS, synth.STACK_VOCAB,
+                   checkpoint_segments=checkpoint_segments)
     st.load(synth.stack_inputs())
     ms = timed(st.step, steps, warmup, torch)
-    return {"workload": "36-layer stack (h512, 8 heads, 2 kv, d64, I1408), seq 1024, vocab 151936, fp32: "
-                        "fwd + fused CE + bwd + global clip + AdamW, loss partials to host",
-            "ms_per_step": round(ms, 3), "tokens_per_s": round(synth.STACK36_SMALL.tokens / ms * 1e3, 1)}
+    flops = stack_flops(synth)
+    adam_bytes = 28 * stack_param_count(synth)
+    ideal_ms = (flops / (MFMA_F32_PEAK * 1e12) + adam_bytes / (HBM_PEAK * 1e9)) * 1e3
+    out = {"workload": "36-layer stack (h512, 8 heads, 2 kv, d64, I1408), seq 1024, vocab 151936, fp32: "
+                       "fwd + fused CE + bwd + global clip + AdamW, loss partials to host",
+           "ms_per_step": round(ms, 3), "tokens_per_s": round(synth.STACK36_SMALL.tokens / ms * 1e3, 1),
+           "activation_bytes": st.workspace_bytes(),
+           "roofline": {"bound": "mfma fp32 + hbm", "gflop": round(flops / 1e9, 1),
+                        "adamw_gb": round(adam_bytes / 1e9, 3), "ideal_ms": round(ideal_ms, 3),
+                        "peak": f"{MFMA_F32_PEAK} TFLOP/s fp32, {HBM_PEAK} GB/s",
+                        "frac": round(ideal_ms / ms, 4)}}
+    if checkpoint_segments:
+        out["checkpoint_segments"] = checkpoint_segments
+    return out
+
+
+def extra_stack_ckpt(torch, qblk, synth, steps, warmup):
+    return extra_stack(torch, qblk, synth, steps, warmup, checkpoint_segments=6)
 
 
 def extra_nf4(torch, qblk, synth, steps, warmup):
@@ -289,8 +466,33 @@ def extra_nf4(torch, qblk, synth, steps, warmup):
     blk = Nf4Block(c, synth.LORA_RANK, synth.LORA_ALPHA)
     blk.load(synth.nf4_lora_inputs(c, b_std=1e-3))
     ms = timed(blk.fwd_bwd, steps, warmup, torch)
-    return {"workload": "frozen NF4 + LoRA r16 Qwen3-4B block, seq 2048, fp16 operands: fwd + bwd (dx, LoRA grads)",
-            "ms_per_step": round(ms, 3), "tokens_per_s": round(c.tokens / ms * 1e3, 1)}
+    flops = nf4_flops(synth)
+    ideal_ms = flops / (MFMA_F16_PEAK * 1e12) * 1e3
+    return {"workload": "frozen NF4 + LoRA r16 Qwen3-4B block, seq 2048, fp16 operands, NF4 decoded inside the "
+                        "GEMMs: fwd + bwd (dx, LoRA grads)",
+            "ms_per_step": round(ms, 3), "tokens_per_s": round(c.tokens / ms * 1e3, 1),
+            "roofline": {"bound": "mfma fp16", "gflop": round(flops / 1e9, 1), "ideal_ms": round(ideal_ms, 4),
+                         "peak": f"{MFMA_F16_PEAK} TFLOP/s", "frac": round(ideal_ms / ms, 4)}}
+
+
+def extra_block_train(torch, qblk, synth, steps, warmup):
+    """One Qwen3-4B-shaped block's whole training step: fwd + bwd + global
+    clip + AdamW, AdamW writing the fp16 weight copies the next step's GEMMs
+    read (no separate cast)."""
+    from bwd_rmsnorm_qkv_amd.runtime import BlockTrainStep, dev
+    c = synth.QWEN3_4B_BLOCK
+    inp = synth.block_inputs(c)
+    st = BlockTrainStep(c)
+    st.load(inp["params"])
+    X, DY = dev(inp["x"]), dev(inp["dy"])
+    ms = timed(lambda: st.step(X, DY), steps, warmup, torch)
+    return {"workload": "Qwen3-4B-shaped block training step (seq 512): fwd + bwd + global clip + AdamW with the "
+                        "fp16 weight copies written by AdamW", "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(c.tokens / ms * 1e3, 1)}
+
+
+EXTRAS = {"stack36_train_step": extra_stack, "stack36_train_step_checkpointed": extra_stack_ckpt,
+          "nf4_lora_block": extra_nf4, "qwen3_4b_block_train_step": extra_block_train}
 
 
 def main():
@@ -306,7 +508,7 @@ def main():
     torch.cuda.set_device(0)
     qblk.lib()
     if args.only:
-        fn = {"stack36_train_step": extra_stack, "nf4_lora_block": extra_nf4}[args.only]
+        fn = EXTRAS[args.only]
         print(json.dumps({"only": args.only, "steps": args.steps, **fn(torch, qblk, synth, args.steps, args.warmup)}),
               flush=True)
         return
@@ -317,11 +519,10 @@ def main():
     X, DY = dev(inp["x"]), dev(inp["dy"])
     G = {k: empty(v.shape) for k, v in inp["params"].items()}
     blk = Block(c)
-    # fp16 weight copies cast once at load (refreshed only when the fp32
-    # weights change, i.e. after an optimizer step); timed on its own
-    Pk = blk.pack_f16(P)
-    pack_ms = timed(lambda: blk.pack_f16(P), 5, 1, torch)
-    P = Pk
+    # the fp16 weight copies the GEMMs read: packed once at load here; in a
+    # training step AdamW writes them as it updates the fp32 masters
+    # (qblk_adamw_step_pack16, timed in the qwen3_4b_block_train_step extra)
+    P = blk.pack_f16(P)
 
     def step():
         blk.forward(P, X)
@@ -344,13 +545,14 @@ def main():
                    "seq": c.seq, "batch": c.batch, "global_batch": c.batch, "seq_len": c.seq,
                    "parallelism": "single GPU"},
         "roofline": roof,
-        "fp16_weight_pack_ms": round(pack_ms, 4),
+        "fp16_weights": "packed once at load; a training step refreshes them inside AdamW "
+                        "(qblk_adamw_step_pack16), see extra.qwen3_4b_block_train_step",
     }
     log("memory-bound kernels")
     out["hbm"] = hbm_kernels(torch, qblk, synth)
     if not args.no_extra:
         extra = {}
-        for name, fn in (("stack36_train_step", extra_stack), ("nf4_lora_block", extra_nf4)):
+        for name, fn in EXTRAS.items():
             try:
                 log(f"extra: {name}")
                 extra[name] = fn(torch, qblk, synth, max(3, args.steps // 10), 2)
@@ -360,6 +562,7 @@ def main():
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(c, inp)
+        out["cpu_baseline_other_workloads"] = cpu_baselines_other(synth)
     print(json.dumps(out), flush=True)
 
 

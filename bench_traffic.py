@@ -6,8 +6,12 @@ rocprofv3 hardware counters, for bench.py's roofline entry.
       runtime's plain copy: 256 MiB read, 256 MiB written), then the 12 GEMM
       launches of one Qwen3-4B-shaped block
       forward + backward (same kernels, shapes and operand types as
-      bench.py's replay), each once. Meant to run under
-      `rocprofv3 --pmc <counter>`, one counter set per run.
+      bench.py's replay), each once; then, each after a marker (a short
+      spin kernel), one forward + backward of the Qwen3-4B-shaped block
+      (seq 512), of the NF4 + LoRA block (seq 2048) and of one layer of the
+      36-layer stack's block (fp32, seq 1024), whose attention kernels the
+      summary reports. Meant to run under `rocprofv3 --pmc <counter>`, one
+      counter set per run.
 
   python bench_traffic.py summarize FETCH_DIR WRITE_DIR MFMA_DIR OUT.md
       Reads the three counter runs (FETCH_SIZE; WRITE_SIZE; GRBM_GUI_ACTIVE
@@ -27,6 +31,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 COPY_BYTES = 256 << 20
+
+
+def _attn_workloads():
+    from bwd_rmsnorm_qkv_amd import synth
+    return [("qwen3_4b block, seq 512 (fp16)", synth.QWEN3_4B_BLOCK),
+            ("nf4 + LoRA qwen3_4b block, seq 2048 (fp16)", synth.NF4_LORA_QWEN3_4B),
+            ("36-layer stack block, seq 1024 (fp32)", synth.STACK36_SMALL)]
+
 GEMM_SOURCES = ["bwd_rmsnorm_qkv_amd/csrc/gemm.hip", "bwd_rmsnorm_qkv_amd/csrc/gemm.h",
                 "bwd_rmsnorm_qkv_amd/csrc/common.h"]
 
@@ -66,6 +78,23 @@ def run():
     for (lay, M, N, K, acc, A, lda, B, ldb, C) in bufs:
         qblk.gemm(lay, 1, M, N, K, A, lda, B, ldb, C, N, acc, scratch=scratch)
         torch.cuda.synchronize()
+    del bufs, scratch, src, dst
+    from bwd_rmsnorm_qkv_amd.runtime import Block, Nf4Block, dev, empty
+    for name, cfg in _attn_workloads():
+        torch.cuda._sleep(1)  # marker
+        torch.cuda.synchronize()
+        if name.startswith("nf4"):
+            blk = Nf4Block(cfg, synth.LORA_RANK, synth.LORA_ALPHA)
+            blk.load(synth.nf4_lora_inputs(cfg, b_std=1e-3))
+            blk.fwd_bwd()
+        else:
+            inp = synth.block_inputs(cfg)
+            P = {k: dev(v) for k, v in inp["params"].items()}
+            blk = Block(cfg)
+            blk.forward(P, dev(inp["x"]))
+            blk.backward(P, dev(inp["x"]), dev(inp["dy"]), {k: empty(v.shape) for k, v in inp["params"].items()})
+        torch.cuda.synchronize()
+        del blk
     print("done", flush=True)
 
 
@@ -86,9 +115,22 @@ def _per_dispatch(rows, counter):
     return [out[k] for k in sorted(out)]
 
 
+def _groups(disp):
+    """Dispatches split at the marker spins: [before the first marker, then
+    one group per attention workload]."""
+    out = [[]]
+    for n, v in disp:
+        if "spin_kernel" in n:
+            out.append([])
+        else:
+            out[-1].append((n, v))
+    return out
+
+
 def _split(disp):
     """(copy, launches): the calibration copy and the 12 GEMM launches, each a
     list of dispatches (the product, then its split-K reduce if any)."""
+    disp = _groups(disp)[0]
     copy = [v for (n, v) in disp if "copyBuffer" in n]  # the runtime's plain copy kernel
     gemm = [(n, v) for (n, v) in disp if "gemm" in n or "splitk_reduce" in n]
     launches = []
@@ -152,7 +194,23 @@ def summarize(fetch_dir, write_dir, mfma_dir, out_path):
         f"traffic_bytes_per_launch: {per:.0f}",
         f"gemm_source_sha1: {source_digest()}",
         "",
+        "## Attention kernels (MFMA busy and HBM traffic per dispatch)",
+        "",
+        "| workload | kernel | read MB | written MB | MFMA busy |",
+        "|---|---|---:|---:|---:|",
     ]
+    fg = _groups(_per_dispatch(_rows(fetch_dir), "FETCH_SIZE"))[1:]
+    wg = _groups(_per_dispatch(_rows(write_dir), "WRITE_SIZE"))[1:]
+    bg = _groups(_per_dispatch(mrows, "SQ_VALU_MFMA_BUSY_CYCLES"))[1:]
+    gg = _groups(_per_dispatch(mrows, "GRBM_GUI_ACTIVE"))[1:]
+    for (wname, _), f_, w_, b_, g_ in zip(_attn_workloads(), fg, wg, bg, gg):
+        for (n, fv), (_, wv), (_, bv), (_, gv) in zip(f_, w_, b_, g_):
+            if "attn_" not in n:
+                continue
+            short = n.split("attn_", 1)[1].split("(")[0].split("Ev")[0][:40]
+            lines.append(f"| {wname} | attn_{short} | {fv * f_fac / 1e3 * 1.024:.1f} | {wv * w_fac / 1e3 * 1.024:.1f} | "
+                         f"{bv / max(gv * 128.0, 1.0):.3f} |")
+    lines.append("")
     with open(out_path, "w") as f:
         f.write("\n".join(lines))
     print(f"wrote {out_path}: {per / 1e6:.1f} MB per launch")

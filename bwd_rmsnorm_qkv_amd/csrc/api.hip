@@ -296,6 +296,41 @@ int32_t qblk_adamw_step(int32_t n, float* const* w, const float* const* g, float
   return adamw(n, w, g, m, v, numel, lr, beta1, beta2, eps, weight_decay, step, grad_scale_dev, S(stream));
 }
 
+int32_t qblk_adamw_step_pack16(int32_t n, float* const* w, const float* const* g, float* const* m,
+                               float* const* v, const int64_t* numel, void* const* w16, float lr, float beta1,
+                               float beta2, float eps, float weight_decay, int32_t step,
+                               const float* grad_scale_dev, qblk_stream_t stream) {
+  if (n <= 0 || !w || !g || !m || !v || !numel || !w16)
+    return fail(QBLK_EINVAL, "adamw_pack16: null argument or n <= 0");
+  if (step < 1) return fail(QBLK_EINVAL, "adamw_pack16: step must be >= 1");
+  for (int i = 0; i < n; ++i) {
+    if (!w[i] || !g[i] || !m[i] || !v[i] || numel[i] < 0) return fail(QBLK_EINVAL, "adamw_pack16: tensor %d", i);
+    if ((uintptr_t)w16[i] % 2) return fail(QBLK_EINVAL, "adamw_pack16: fp16 copy %d misaligned", i);
+  }
+  return adamw(n, w, g, m, v, numel, lr, beta1, beta2, eps, weight_decay, step, grad_scale_dev, S(stream),
+               (f16* const*)w16);
+}
+
+int32_t qblk_block_pack_f16_offsets(const qblk_config* cfg, int64_t* offsets) {
+  QBLK_TRY(check_config(cfg));
+  if (!offsets) return fail(QBLK_EINVAL, "block_pack_f16_offsets: offsets is NULL");
+  Packed16 pk;
+  size_t bytes = 0;
+  char* const base = (char*)(uintptr_t)4096;  // any 256-aligned address: only differences are used
+  carve_pack16(*cfg, base, pk, bytes);
+  const int64_t h = cfg->hidden, qd = (int64_t)cfg->heads * cfg->head_dim, kvd = (int64_t)cfg->kv_heads * cfg->head_dim;
+  const int64_t I = cfg->intermediate;
+  const f16* b16 = (const f16*)base;
+  offsets[0] = pk.qkv - b16;
+  offsets[1] = offsets[0] + qd * h;
+  offsets[2] = offsets[1] + kvd * h;
+  offsets[3] = pk.o - b16;
+  offsets[4] = pk.gu - b16;
+  offsets[5] = offsets[4] + I * h;
+  offsets[6] = pk.d - b16;
+  return QBLK_OK;
+}
+
 // ---------------------------------------------------------------- NF4
 
 int32_t qblk_nf4_quantize(const float* w, int64_t numel, uint8_t* codes, float* absmax, qblk_stream_t stream) {
@@ -385,6 +420,75 @@ int32_t qblk_rmsnorm_backward(int32_t rows, int32_t n, float eps, const float* x
   QBLK_TRY(rmsnorm_check(rows, n));
   if (scratch_bytes < rmsnorm_bwd_scratch(rows, n)) return fail(QBLK_EINVAL, "rmsnorm_backward: scratch too small");
   return rmsnorm_backward(rows, n, eps, x, gamma, dy, dres, dx, nullptr, dgamma, (float*)scratch, S(stream));
+}
+
+int32_t qblk_swiglu_forward(int32_t tokens, int32_t inter, const float* gu, float* s, qblk_stream_t stream) {
+  if (tokens <= 0 || inter <= 0 || inter % 4) return fail(QBLK_EINVAL, "swiglu_forward: bad sizes");
+  if (!gu || !s || !aligned16(gu) || !aligned16(s)) return fail(QBLK_EINVAL, "swiglu_forward: null or misaligned");
+  return swiglu_forward(tokens, inter, gu, s, nullptr, S(stream));
+}
+
+int32_t qblk_swiglu_backward(int32_t tokens, int32_t inter, const float* gu, const float* ds, float* dgu,
+                             qblk_stream_t stream) {
+  if (tokens <= 0 || inter <= 0 || inter % 4) return fail(QBLK_EINVAL, "swiglu_backward: bad sizes");
+  if (!gu || !ds || !dgu || !aligned16(gu) || !aligned16(ds) || !aligned16(dgu))
+    return fail(QBLK_EINVAL, "swiglu_backward: null or misaligned");
+  return swiglu_backward(tokens, inter, gu, ds, dgu, nullptr, S(stream));
+}
+
+static size_t qk_tab_bytes(int32_t seq, int32_t head_dim) {
+  return ((size_t)seq * (head_dim / 2) * sizeof(float2) + 255) & ~(size_t)255;
+}
+
+static int check_qk(int32_t tokens, int32_t seq, int32_t heads, int32_t kv_heads, int32_t head_dim, int64_t ld_qkv) {
+  if (tokens <= 0 || seq <= 0 || tokens % seq || heads <= 0 || kv_heads <= 0 || heads % kv_heads)
+    return fail(QBLK_EINVAL, "qk_norm_rope: bad sizes");
+  if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(QBLK_EUNSUPPORTED, "qk_norm_rope: head_dim %d", head_dim);
+  if (ld_qkv < (int64_t)(heads + 2 * kv_heads) * head_dim || ld_qkv % 4)
+    return fail(QBLK_EINVAL, "qk_norm_rope: ld_qkv");
+  return QBLK_OK;
+}
+
+int32_t qblk_qk_norm_rope_workspace_size(int32_t tokens, int32_t seq, int32_t heads, int32_t kv_heads,
+                                         int32_t head_dim, size_t* scratch_bytes) {
+  QBLK_TRY(check_qk(tokens, seq, heads, kv_heads, head_dim, (int64_t)(heads + 2 * kv_heads) * head_dim));
+  if (!scratch_bytes) return fail(QBLK_EINVAL, "qk_norm_rope_workspace_size: null");
+  *scratch_bytes = qk_tab_bytes(seq, head_dim) + qk_norm_rope_bwd_scratch(tokens, heads, kv_heads, head_dim) + 256;
+  return QBLK_OK;
+}
+
+int32_t qblk_qk_norm_rope_forward(int32_t tokens, int32_t seq, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                  int32_t qk_norm, float eps, float rope_theta, const float* qkv, int64_t ld_qkv,
+                                  const float* g_q, const float* g_k, float* qr, float* kr, float* rho_q,
+                                  float* rho_k, void* scratch, size_t scratch_bytes, qblk_stream_t stream) {
+  QBLK_TRY(check_qk(tokens, seq, heads, kv_heads, head_dim, ld_qkv));
+  if (!qkv || !qr || !kr || !scratch || (qk_norm && (!g_q || !g_k || !rho_q || !rho_k)))
+    return fail(QBLK_EINVAL, "qk_norm_rope_forward: null pointer");
+  if (scratch_bytes < qk_tab_bytes(seq, head_dim) || !aligned16(scratch))
+    return fail(QBLK_EINVAL, "qk_norm_rope_forward: scratch");
+  float2* tab = (float2*)scratch;
+  QBLK_TRY(rope_table(seq, head_dim, rope_theta, tab, S(stream)));
+  QkRopeArgs a{tokens, seq, heads, kv_heads, head_dim, qk_norm, eps, qkv, ld_qkv, g_q, g_k, tab, qr, kr, rho_q, rho_k};
+  return qk_norm_rope_forward(a, S(stream));
+}
+
+int32_t qblk_qk_norm_rope_backward(int32_t tokens, int32_t seq, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                   int32_t qk_norm, float eps, float rope_theta, const float* qkv, int64_t ld_qkv,
+                                   const float* g_q, const float* g_k, const float* dqr, const float* dkr,
+                                   float* dqkv, float* dg_q, float* dg_k, void* scratch, size_t scratch_bytes,
+                                   qblk_stream_t stream) {
+  QBLK_TRY(check_qk(tokens, seq, heads, kv_heads, head_dim, ld_qkv));
+  if (!qkv || !dqr || !dkr || !dqkv || !dg_q || !dg_k || !scratch || (qk_norm && (!g_q || !g_k)))
+    return fail(QBLK_EINVAL, "qk_norm_rope_backward: null pointer");
+  size_t need = 0;
+  QBLK_TRY(qblk_qk_norm_rope_workspace_size(tokens, seq, heads, kv_heads, head_dim, &need));
+  if (scratch_bytes < need || !aligned16(scratch)) return fail(QBLK_EINVAL, "qk_norm_rope_backward: scratch");
+  float2* tab = (float2*)scratch;
+  QBLK_TRY(rope_table(seq, head_dim, rope_theta, tab, S(stream)));
+  QkRopeBwdArgs b{tokens, seq, heads, kv_heads, head_dim, qk_norm, eps, qkv, ld_qkv, g_q, g_k, tab,
+                  dqr, dkr, dqkv, dg_q, dg_k};
+  return qk_norm_rope_backward(b, (float*)((char*)scratch + qk_tab_bytes(seq, head_dim)), S(stream));
 }
 
 static int check_attn_ld(int32_t heads_or_kv, int32_t d, int64_t ld) {

@@ -127,6 +127,7 @@ __global__ __launch_bounds__(256) void scale_kernel(const ScaleChunk c, const fl
 
 struct AdamChunk {
   float* w[kChunk];
+  f16* w16[kChunk];  // optional fp16 copy of the updated weight (NULL: none)
   const float* g[kChunk];
   float* m[kChunk];
   float* v[kChunk];
@@ -139,11 +140,16 @@ struct AdamHp {
   float lr, b1, b2, eps, wd, bc1, bc2;
 };
 
+// Every rounding step spelled out (explicit fma, no contraction left to the
+// compiler), so the vector and scalar paths give the same bits whatever
+// tile or tensor split an element falls in.
 __device__ __forceinline__ void adam1(float& w, float g, float& m, float& v, const AdamHp& h) {
-  m = h.b1 * m + (1.f - h.b1) * g;
-  v = h.b2 * v + (1.f - h.b2) * g * g;
+#pragma clang fp contract(off)
+  m = __builtin_fmaf(h.b1, m, (1.f - h.b1) * g);
+  v = __builtin_fmaf(h.b2, v, (1.f - h.b2) * (g * g));
   const float mh = m / h.bc1, vh = v / h.bc2;
-  w = w - h.lr * (mh / (sqrtf(vh) + h.eps) + h.wd * w);
+  const float upd = __builtin_fmaf(h.wd, w, mh / (sqrtf(vh) + h.eps));
+  w = __builtin_fmaf(-h.lr, upd, w);
 }
 
 __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk c, const AdamHp h,
@@ -153,10 +159,12 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk c, const Ada
   const int64_t base = (tile - (j ? c.tile_end[j - 1] : 0)) * kTile;
   const float sc = scale_dev ? scale_dev[0] : 1.f;
   float *w = c.w[j], *m = c.m[j], *v = c.v[j];
+  f16* const w16 = c.w16[j];
   const float* g = c.g[j];
   const int64_t n = c.n[j];
   const bool vec = base + kTile <= n &&
-                   (((uintptr_t)w | (uintptr_t)g | (uintptr_t)m | (uintptr_t)v) & 15) == 0;
+                   (((uintptr_t)w | (uintptr_t)g | (uintptr_t)m | (uintptr_t)v) & 15) == 0 &&
+                   ((uintptr_t)w16 & 7) == 0;
   if (vec) {
     // every load of the tile is issued before any store (the stores could
     // alias later loads as far as the compiler knows, which would otherwise
@@ -180,6 +188,7 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk c, const Ada
       store_stream(w + e, W[u]);
       store_stream(m + e, M[u]);
       store_stream(v + e, V[u]);
+      if (w16) *(half4*)(w16 + e) = to_half4(W[u]);
     }
   } else {
     const int64_t end = min(base + (int64_t)kTile, n);
@@ -189,6 +198,7 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk c, const Ada
       w[e] = W;
       m[e] = M;
       v[e] = V;
+      if (w16) w16[e] = to_f16(W);
     }
   }
 }
@@ -277,7 +287,7 @@ size_t static_clip_scratch_bytes() { return sizeof(double) * kStaticClipChunks *
 
 int adamw(int n, float* const* w, const float* const* g, float* const* m, float* const* v,
           const int64_t* numel, float lr, float b1, float b2, float eps, float wd, int step,
-          const float* scale_dev, hipStream_t st) {
+          const float* scale_dev, hipStream_t st, f16* const* w16) {
   AdamHp h;
   h.lr = lr;
   h.b1 = b1;
@@ -291,6 +301,7 @@ int adamw(int n, float* const* w, const float* const* g, float* const* m, float*
     int64_t acc = 0;
     for (int j = ci * kChunk; j < std::min(n, (ci + 1) * kChunk); ++j) {
       c.w[c.count] = w[j];
+      c.w16[c.count] = w16 ? w16[j] : nullptr;
       c.g[c.count] = g[j];
       c.m[c.count] = m[j];
       c.v[c.count] = v[j];

@@ -88,6 +88,9 @@ _SIGS = {
     "qblk_adamw_step": ([C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                          C.c_float, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, C.c_void_p,
                          C.c_void_p], C.c_int32),
+    "qblk_adamw_step_pack16": ([C.c_int32] + [C.c_void_p] * 6 + [C.c_float] * 5 + [C.c_int32, C.c_void_p,
+                                                                                    C.c_void_p], C.c_int32),
+    "qblk_block_pack_f16_offsets": ([C.c_void_p, C.c_void_p], C.c_int32),
     "qblk_nf4_codebook": ([C.c_void_p], C.c_int32),
     "qblk_nf4_quantize": ([C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int32),
     "qblk_nf4_dequantize": ([C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p], C.c_int32),
@@ -106,6 +109,13 @@ _SIGS = {
     "qblk_gemm_ex": ([C.c_int32] * 5 + [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_int64, C.c_int32,
                                         C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p],
                      C.c_int32),
+    "qblk_swiglu_forward": ([C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int32),
+    "qblk_swiglu_backward": ([C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int32),
+    "qblk_qk_norm_rope_workspace_size": ([C.c_int32] * 5 + [C.POINTER(C.c_size_t)], C.c_int32),
+    "qblk_qk_norm_rope_forward": ([C.c_int32] * 6 + [C.c_float, C.c_float, C.c_void_p, C.c_int64]
+                                  + [C.c_void_p] * 7 + [C.c_size_t, C.c_void_p], C.c_int32),
+    "qblk_qk_norm_rope_backward": ([C.c_int32] * 6 + [C.c_float, C.c_float, C.c_void_p, C.c_int64]
+                                   + [C.c_void_p] * 8 + [C.c_size_t, C.c_void_p], C.c_int32),
     "qblk_rmsnorm_workspace_size": ([C.c_int32, C.c_int32, C.POINTER(C.c_size_t)], C.c_int32),
     "qblk_rmsnorm_forward": ([C.c_int32, C.c_int32, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p],
@@ -277,6 +287,54 @@ def adamw_step(w, g, m, v, lr, beta1, beta2, eps, weight_decay, step, grad_scale
     _check(lib().qblk_adamw_step(len(w), _ptr_array(w), _ptr_array(g), _ptr_array(m), _ptr_array(v),
                                  _numel_array(w), lr, beta1, beta2, eps, weight_decay, int(step),
                                  _p(grad_scale_dev), _stream(stream)))
+
+
+def swiglu_forward(tokens, inter, gu, s, stream=None):
+    _check(lib().qblk_swiglu_forward(tokens, inter, _p(gu), _p(s), _stream(stream)))
+
+
+def swiglu_backward(tokens, inter, gu, ds, dgu, stream=None):
+    _check(lib().qblk_swiglu_backward(tokens, inter, _p(gu), _p(ds), _p(dgu), _stream(stream)))
+
+
+def qk_norm_rope_workspace_size(tokens, seq, heads, kv_heads, head_dim):
+    n = C.c_size_t()
+    _check(lib().qblk_qk_norm_rope_workspace_size(tokens, seq, heads, kv_heads, head_dim, C.byref(n)))
+    return n.value
+
+
+def qk_norm_rope_forward(tokens, seq, heads, kv_heads, head_dim, qk_norm, eps, theta, qkv, ld_qkv, g_q, g_k,
+                         qr, kr, rho_q, rho_k, scratch, stream=None):
+    _check(lib().qblk_qk_norm_rope_forward(tokens, seq, heads, kv_heads, head_dim, int(qk_norm), eps, theta,
+                                           _p(qkv), ld_qkv, _p(g_q), _p(g_k), _p(qr), _p(kr), _p(rho_q),
+                                           _p(rho_k), _p(scratch), scratch.numel() * scratch.element_size(),
+                                           _stream(stream)))
+
+
+def qk_norm_rope_backward(tokens, seq, heads, kv_heads, head_dim, qk_norm, eps, theta, qkv, ld_qkv, g_q, g_k,
+                          dqr, dkr, dqkv, dg_q, dg_k, scratch, stream=None):
+    _check(lib().qblk_qk_norm_rope_backward(tokens, seq, heads, kv_heads, head_dim, int(qk_norm), eps, theta,
+                                            _p(qkv), ld_qkv, _p(g_q), _p(g_k), _p(dqr), _p(dkr), _p(dqkv),
+                                            _p(dg_q), _p(dg_k), _p(scratch),
+                                            scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def adamw_step_pack16(w, g, m, v, w16, lr, beta1, beta2, eps, weight_decay, step, grad_scale_dev=None,
+                      stream=None):
+    """w16: per tensor an fp16 device address (int) or tensor for the copy, or None."""
+    assert len(w) == len(g) == len(m) == len(v) == len(w16)
+    ptrs = (C.c_void_p * len(w16))(*[(x if isinstance(x, int) else _p(x)) if x is not None else None
+                                     for x in w16])
+    _check(lib().qblk_adamw_step_pack16(len(w), _ptr_array(w), _ptr_array(g), _ptr_array(m), _ptr_array(v),
+                                        _numel_array(w), ptrs, lr, beta1, beta2, eps, weight_decay, int(step),
+                                        _p(grad_scale_dev), _stream(stream)))
+
+
+def block_pack_f16_offsets(cfg):
+    c = cfg if isinstance(cfg, Config) else make_config(cfg)
+    off = (C.c_int64 * 7)()
+    _check(lib().qblk_block_pack_f16_offsets(C.byref(c), off))
+    return dict(zip(PROJ, list(off)))
 
 
 # ------------------------------------------------------------------- NF4

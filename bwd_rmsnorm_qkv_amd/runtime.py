@@ -96,6 +96,56 @@ class Block:
         return self.dx if dx is None else dx
 
 
+class BlockTrainStep:
+    """One training step of a single block: forward, backward, the global
+    clip and AdamW over its 11 tensors (flat fp32 buffers). With fp16
+    operands (gemm_precision 1) the packed fp16 weight set the GEMMs read is
+    written by AdamW itself (qblk_adamw_step_pack16) as it updates the
+    fp32 masters, so no separate cast runs between steps; it is packed once
+    at load."""
+
+    def __init__(self, cfg, adamw=None, max_norm=1.0):
+        from .synth import ADAMW
+        self.cfg, self.blk = cfg, Block(cfg)
+        self.hp = dict(ADAMW if adamw is None else adamw)
+        self.max_norm = max_norm
+        shapes = block_shapes(cfg)
+        self.w, self.g, self.m, self.v = (FlatParams(shapes) for _ in range(4))
+        self.fp16 = cfg.gemm_precision == 1
+        self.params = self.w.views
+        if self.fp16:
+            self.packed = byte_buffer(qblk.block_pack_f16_size(self.blk.c))
+            off = qblk.block_pack_f16_offsets(self.blk.c)
+            base = self.packed.data_ptr()
+            self.w16 = [base + 2 * off[n] if n in off else None for n in PARAMS]
+            self.params = {**self.w.views, "w16": self.packed}
+        self.norm, self.scale = empty(1), empty(1)
+        self.clip_scratch = byte_buffer(qblk.clip_workspace_size([self.g.buf]))
+        self.t = 0
+
+    def load(self, params: dict):
+        self.w.load(params)
+        self.m.buf.zero_()
+        self.v.buf.zero_()
+        if self.fp16:
+            qblk.block_pack_f16(self.blk.c, self.w.views, self.packed)
+        self.t = 0
+
+    def step(self, x, dy):
+        self.blk.forward(self.params, x)
+        self.blk.backward(self.params, x, dy, self.g.views)
+        qblk.clip_grad_norm([self.g.buf], self.max_norm, 0, self.norm, self.scale, self.clip_scratch)
+        self.t += 1
+        hp = self.hp
+        if self.fp16:
+            qblk.adamw_step_pack16(self.w.tensors(), self.g.tensors(), self.m.tensors(), self.v.tensors(), self.w16,
+                                   hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], self.t,
+                                   grad_scale_dev=self.scale)
+        else:
+            qblk.adamw_step([self.w.buf], [self.g.buf], [self.m.buf], [self.v.buf], hp["lr"], hp["beta1"],
+                            hp["beta2"], hp["eps"], hp["weight_decay"], self.t, grad_scale_dev=self.scale)
+
+
 class Nf4Block:
     """A frozen-NF4 + LoRA block: base weights encoded on the device by
     qblk_nf4_quantize, LoRA A/B and their gradients, and workspaces."""

@@ -215,6 +215,24 @@ int32_t qblk_adamw_step(int32_t n, float* const* w, const float* const* g, float
                         float eps, float weight_decay, int32_t step, const float* grad_scale_dev,
                         qblk_stream_t stream);
 
+/* AdamW that also writes the fp16 copy of every updated weight in the same
+ * pass (round to nearest even), so a training step with fp16 GEMM operands
+ * needs no separate cast of the fp32 masters ([block] set_fp16_weights
+ * refreshes such copies after each update). Same arguments and errors as
+ * qblk_adamw_step, plus w16: host array of n device pointers to fp16
+ * buffers of numel[i] elements (2-byte aligned; an entry may be NULL: no
+ * copy for that tensor). For the packed set of qblk_block_pack_f16 the
+ * pointers are packed + 2 * offset, offsets from qblk_block_pack_f16_offsets. */
+int32_t qblk_adamw_step_pack16(int32_t n, float* const* w, const float* const* g, float* const* m,
+                               float* const* v, const int64_t* numel, void* const* w16, float lr, float beta1,
+                               float beta2, float eps, float weight_decay, int32_t step,
+                               const float* grad_scale_dev, qblk_stream_t stream);
+
+/* Element offsets (fp16 elements from the start of the packed set) of the
+ * seven projection weights w_q, w_k, w_v, w_o, w_gate, w_up, w_down in the
+ * packed fp16 weight set of qblk_block_pack_f16 (host array of 7). */
+int32_t qblk_block_pack_f16_offsets(const qblk_config* cfg, int64_t* offsets);
+
 /* ---------------------------------------------------------------- NF4 --- */
 
 /* The 16 NormalFloat4 levels used by the NF4 kernels, ascending, written to

@@ -61,6 +61,44 @@ int32_t qblk_rmsnorm_backward(int32_t rows, int32_t n, float eps, const float* x
 /* Scratch bytes for the RMSNorm entry points above. */
 int32_t qblk_rmsnorm_workspace_size(int32_t rows, int32_t n, size_t* scratch_bytes);
 
+/* SwiGLU ([block] fused_swiglu_forward): s [T, I] = silu(g) * u with
+ * g = gu[:, :I], u = gu[:, I:] of gu [T, 2I] (fp32, dense). I a multiple
+ * of 4; buffers 16-byte aligned. */
+int32_t qblk_swiglu_forward(int32_t tokens, int32_t inter, const float* gu, float* s, qblk_stream_t stream);
+
+/* Its backward ([block] SwiGLU backward; [wgpu] ffn_backward):
+ * dgu = [ds * u * silu'(g) | ds * silu(g)], silu'(g) = sigmoid(g) (1 + g
+ * (1 - sigmoid(g))). dgu [T, 2I] overwritten. */
+int32_t qblk_swiglu_backward(int32_t tokens, int32_t inter, const float* gu, const float* ds, float* dgu,
+                             qblk_stream_t stream);
+
+/* Scratch bytes of the two QK-norm + RoPE entry points below (the RoPE
+ * table and the gamma-gradient partial sums). */
+int32_t qblk_qk_norm_rope_workspace_size(int32_t tokens, int32_t seq, int32_t heads, int32_t kv_heads,
+                                         int32_t head_dim, size_t* scratch_bytes);
+
+/* Per-head RMSNorm of q and k (when qk_norm; gammas g_q, g_k [head_dim]
+ * shared by the heads) then NeoX RoPE at position s = t % seq with angle
+ * s * theta^(-2i/head_dim) ([block] compute_attention_cuda). qkv [T,
+ * ld_qkv] holds q | k | v (heads, kv_heads, kv_heads heads of head_dim);
+ * writes qr [T, heads*d], kr [T, kv_heads*d] (dense), rho_q [T, heads],
+ * rho_k [T, kv_heads] (the inverse RMS, when qk_norm). */
+int32_t qblk_qk_norm_rope_forward(int32_t tokens, int32_t seq, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                  int32_t qk_norm, float eps, float rope_theta, const float* qkv, int64_t ld_qkv,
+                                  const float* g_q, const float* g_k, float* qr, float* kr, float* rho_q,
+                                  float* rho_k, void* scratch, size_t scratch_bytes, qblk_stream_t stream);
+
+/* Its backward: from dqr, dkr (gradients at the attention inputs) the
+ * gradients at the projection outputs, written into the q and k columns of
+ * dqkv [T, ld_qkv] (v columns untouched), and dg_q, dg_k [head_dim]
+ * (overwritten; zero without qk_norm). The QK-norm backward is the true
+ * derivative (absent on the page). */
+int32_t qblk_qk_norm_rope_backward(int32_t tokens, int32_t seq, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                   int32_t qk_norm, float eps, float rope_theta, const float* qkv, int64_t ld_qkv,
+                                   const float* g_q, const float* g_k, const float* dqr, const float* dkr,
+                                   float* dqkv, float* dg_q, float* dg_k, void* scratch, size_t scratch_bytes,
+                                   qblk_stream_t stream);
+
 /* GQA causal softmax attention forward over q [T, heads*d], k, v
  * [T, kv_heads*d] (rows strided by ldq/ldk/ldv elements) for `batch`
  * independent sequences of length seq: o [T, heads*d] (ldo) and the

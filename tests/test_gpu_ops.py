@@ -271,3 +271,82 @@ def test_nf4_quantize_bit_exact():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(deq.cpu().numpy().reshape(w.shape),
                                   oracle.nf4_dequantize(packed, scales, w.shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("T,I", [(37, 176), (256, 1408), (512, 9728)])
+def test_swiglu(T, I):
+    need_gpu()
+    announce(f"swiglu T={T} I={I}")
+    rng = np.random.default_rng(T + I)
+    gu = (rng.standard_normal((T, 2 * I)) * 2).astype(np.float32)
+    ds = rng.standard_normal((T, I)).astype(np.float32)
+    GU, DS = dev(gu), dev(ds)
+    s, dgu = empty((T, I)), empty((T, 2 * I))
+    qblk.swiglu_forward(T, I, GU, s)
+    qblk.swiglu_backward(T, I, GU, DS, dgu)
+    torch.cuda.synchronize()
+    g, u = gu[:, :I].astype(np.float64), gu[:, I:].astype(np.float64)
+    check("s", s, ops.swiglu_fwd(g, u), FP32_TOL)
+    dg, du = ops.swiglu_bwd(g, u, ds.astype(np.float64))
+    check("dg", dgu[:, :I], dg, FP32_TOL)
+    check("du", dgu[:, I:], du, FP32_TOL)
+
+
+# (batch, seq, heads, kv_heads, head_dim, qk_norm, theta)
+QK_CASES = [(1, 32, 4, 2, 16, 1, 1e4), (3, 13, 4, 2, 16, 1, 1e4), (2, 48, 8, 2, 64, 1, 1e4),
+            (2, 48, 8, 2, 64, 0, 1e4), (1, 37, 8, 2, 32, 1, 1e4), (1, 512, 32, 8, 128, 1, 1e6)]
+
+
+@pytest.mark.parametrize("case", QK_CASES)
+def test_qk_norm_rope(case):
+    """QK-norm + RoPE forward and backward (the true QK-norm derivative)
+    against the oracle's per-head RMSNorm and RoPE, with non-unit gammas and
+    the v columns of the packed projection output left alone."""
+    need_gpu()
+    B, S, H, KV, d, qk, theta = case
+    T = B * S
+    announce(f"qk_norm_rope T={T} H={H} KV={KV} d={d} qk_norm={qk}")
+    rng = np.random.default_rng(T * d + H)
+    ld = (H + 2 * KV) * d
+    qkv = rng.standard_normal((T, ld)).astype(np.float32)
+    gq = (1 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    gk = (1 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    dqr = rng.standard_normal((T, H * d)).astype(np.float32)
+    dkr = rng.standard_normal((T, KV * d)).astype(np.float32)
+    eps = 1e-6
+    QKV, GQ, GK = dev(qkv), dev(gq), dev(gk)
+    qr, kr = empty((T, H * d)), empty((T, KV * d))
+    rq, rk = empty((T, H)), empty((T, KV))
+    scratch = byte_buffer(qblk.qk_norm_rope_workspace_size(T, S, H, KV, d))
+    qblk.qk_norm_rope_forward(T, S, H, KV, d, qk, eps, theta, QKV, ld, GQ, GK, qr, kr, rq, rk, scratch)
+    dqkv = torch.full((T, ld), 5.0, device="cuda")
+    dgq, dgk = empty(d), empty(d)
+    qblk.qk_norm_rope_backward(T, S, H, KV, d, qk, eps, theta, QKV, ld, GQ, GK, dev(dqr), dev(dkr), dqkv, dgq,
+                               dgk, scratch)
+    torch.cuda.synchronize()
+    pos = np.tile(np.arange(S), B)
+    q = qkv[:, :H * d].astype(np.float64)
+    k = qkv[:, H * d:(H + KV) * d].astype(np.float64)
+    if qk:
+        qn, rho_q = ops.head_rmsnorm_fwd(q, gq, H, eps)
+        kn, rho_k = ops.head_rmsnorm_fwd(k, gk, KV, eps)
+        check("rho_q", rq, rho_q, FP32_TOL)
+        check("rho_k", rk, rho_k, FP32_TOL)
+    else:
+        qn, kn = q, k
+    check("qr", qr, ops.rope_fwd(qn, pos, H, theta), FP32_TOL)
+    check("kr", kr, ops.rope_fwd(kn, pos, KV, theta), FP32_TOL)
+    dqn = ops.rope_bwd(dqr.astype(np.float64), pos, H, theta)
+    dkn = ops.rope_bwd(dkr.astype(np.float64), pos, KV, theta)
+    if qk:
+        dq, dg_q = ops.head_rmsnorm_bwd(q, gq, dqn, H, eps)
+        dk, dg_k = ops.head_rmsnorm_bwd(k, gk, dkn, KV, eps)
+        check("dg_q", dgq, dg_q, FP32_TOL)
+        check("dg_k", dgk, dg_k, FP32_TOL)
+    else:
+        dq, dk = dqn, dkn
+        assert torch.count_nonzero(dgq).item() == 0 and torch.count_nonzero(dgk).item() == 0
+    out = dqkv.cpu().numpy()
+    check("dq", out[:, :H * d], dq, FP32_TOL)
+    check("dk", out[:, H * d:(H + KV) * d], dk, FP32_TOL)
+    assert np.all(out[:, (H + KV) * d:] == 5.0), "v columns must be left alone"

@@ -8,7 +8,7 @@ import torch
 import oracle
 from bwd_rmsnorm_qkv_amd import qblk, synth
 from bwd_rmsnorm_qkv_amd.runtime import Block, FlatParams, block_shapes, byte_buffer, dev, empty
-from gpu_util import FP32_TOL, announce, check, need_gpu, rel_err
+from gpu_util import FP16_TOL, FP32_TOL, announce, check, need_gpu, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -263,3 +263,43 @@ def test_stack_checkpoint_segments(segments):
     for i, n in enumerate(names):
         check("g_" + n, s1.g[n], ref["grads"][i], FP32_TOL)
     check("dx", dx1, ref["dx"], FP32_TOL)
+
+
+@pytest.mark.parametrize("shape", ["small_fp16", "qwen3_4b"])
+def test_block_train_step_fp16_pack_in_adamw(shape):
+    """Two training steps of one fp16-operand block in which AdamW writes the
+    packed fp16 weight set (qblk_adamw_step_pack16): after each step the
+    packed set equals, bit for bit, qblk_block_pack_f16 of the updated fp32
+    masters, and the masters and moments equal those of qblk_adamw_step on
+    the same gradients; step 1's loss-free quantities (gradient norm, clip
+    scale) match the oracle."""
+    need_gpu()
+    from bwd_rmsnorm_qkv_amd.runtime import BlockTrainStep
+    c = (synth.QWEN3_4B_BLOCK if shape == "qwen3_4b" else
+         synth.BlockShape(hidden=512, heads=8, kv_heads=2, head_dim=64, intermediate=1408, seq=96, batch=2,
+                          rope_theta=1e4, gemm_precision=1))
+    announce(f"block train step with fp16 pack in AdamW ({shape}, T={c.tokens})")
+    inp = synth.block_inputs(c)
+    st = BlockTrainStep(c)
+    st.load(inp["params"])
+    X, DY = dev(inp["x"]), dev(inp["dy"])
+    ref_pack = byte_buffer(st.packed.numel())
+    for step in (1, 2):
+        w0, m0, v0 = st.w.buf.clone(), st.m.buf.clone(), st.v.buf.clone()
+        st.step(X, DY)
+        torch.cuda.synchronize()
+        # the same update by the plain AdamW from the same state and gradients
+        w1, m1, v1 = w0.clone(), m0.clone(), v0.clone()
+        hp = synth.ADAMW
+        qblk.adamw_step([w1], [st.g.buf], [m1], [v1], hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                        hp["weight_decay"], step, grad_scale_dev=st.scale)
+        qblk.block_pack_f16(st.blk.c, st.w.views, ref_pack)
+        torch.cuda.synchronize()
+        assert torch.equal(w1, st.w.buf) and torch.equal(m1, st.m.buf) and torch.equal(v1, st.v.buf)
+        assert torch.equal(ref_pack, st.packed), f"packed fp16 set differs after step {step}"
+        if step == 1:
+            _, cache = oracle.block_forward(c, inp["params"], inp["x"])
+            _, g_ref = oracle.block_backward(c, inp["params"], cache, inp["dy"])
+            n_ref, s_ref, _ = oracle.global_clip([g_ref[n] for n in qblk.PARAMS], synth.CLIP_MAX_NORM)
+            assert abs(st.norm.item() - n_ref) <= FP16_TOL * n_ref
+            assert abs(st.scale.item() - s_ref) <= FP16_TOL * s_ref
