@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["stack36_train_step", "stack36_train_step_checkpointed", "nf4_lora_block",
-                                       "qwen3_4b_block_train_step"],
+                                       "qwen3_4b_block_train_step", "qwen3_4b_block_bf16"],
                     help="time only this workload (for kernel traces) and print its JSON object")
     return ap.parse_args()
 
@@ -491,8 +491,28 @@ def extra_block_train(torch, qblk, synth, steps, warmup):
             "tokens_per_s": round(c.tokens / ms * 1e3, 1)}
 
 
+def extra_block_bf16(torch, qblk, synth, steps, warmup):
+    """The headline block with bfloat16 GEMM and attention operands."""
+    from dataclasses import replace
+    from bwd_rmsnorm_qkv_amd.runtime import Block, dev, empty
+    c = replace(synth.QWEN3_4B_BLOCK, gemm_precision=2)
+    inp = synth.block_inputs(c)
+    blk = Block(c)
+    P = blk.pack_f16({k: dev(v) for k, v in inp["params"].items()})
+    X, DY = dev(inp["x"]), dev(inp["dy"])
+    G = {k: empty(v.shape) for k, v in inp["params"].items()}
+
+    def step():
+        blk.forward(P, X)
+        blk.backward(P, X, DY, G)
+    ms = timed(step, steps, warmup, torch)
+    return {"workload": "Qwen3-4B-shaped block fwd+bwd (seq 512) with bfloat16 operands, fp32 accumulate",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(c.tokens / ms * 1e3, 1)}
+
+
 EXTRAS = {"stack36_train_step": extra_stack, "stack36_train_step_checkpointed": extra_stack_ckpt,
-          "nf4_lora_block": extra_nf4, "qwen3_4b_block_train_step": extra_block_train}
+          "nf4_lora_block": extra_nf4, "qwen3_4b_block_train_step": extra_block_train,
+          "qwen3_4b_block_bf16": extra_block_bf16}
 
 
 def main():

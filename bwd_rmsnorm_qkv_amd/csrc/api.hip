@@ -297,18 +297,19 @@ int32_t qblk_adamw_step(int32_t n, float* const* w, const float* const* g, float
 }
 
 int32_t qblk_adamw_step_pack16(int32_t n, float* const* w, const float* const* g, float* const* m,
-                               float* const* v, const int64_t* numel, void* const* w16, float lr, float beta1,
-                               float beta2, float eps, float weight_decay, int32_t step,
+                               float* const* v, const int64_t* numel, void* const* w16, int32_t w16_bf16, float lr,
+                               float beta1, float beta2, float eps, float weight_decay, int32_t step,
                                const float* grad_scale_dev, qblk_stream_t stream) {
   if (n <= 0 || !w || !g || !m || !v || !numel || !w16)
     return fail(QBLK_EINVAL, "adamw_pack16: null argument or n <= 0");
+  if (w16_bf16 != 0 && w16_bf16 != 1) return fail(QBLK_EINVAL, "adamw_pack16: w16_bf16 must be 0 or 1");
   if (step < 1) return fail(QBLK_EINVAL, "adamw_pack16: step must be >= 1");
   for (int i = 0; i < n; ++i) {
     if (!w[i] || !g[i] || !m[i] || !v[i] || numel[i] < 0) return fail(QBLK_EINVAL, "adamw_pack16: tensor %d", i);
     if ((uintptr_t)w16[i] % 2) return fail(QBLK_EINVAL, "adamw_pack16: fp16 copy %d misaligned", i);
   }
   return adamw(n, w, g, m, v, numel, lr, beta1, beta2, eps, weight_decay, step, grad_scale_dev, S(stream),
-               (f16* const*)w16);
+               (f16* const*)w16, w16_bf16 == 1);
 }
 
 int32_t qblk_block_pack_f16_offsets(const qblk_config* cfg, int64_t* offsets) {
@@ -349,7 +350,7 @@ int32_t qblk_nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t n
 
 int32_t qblk_gemm_workspace_size(int32_t layout, int32_t precision, int32_t M, int32_t N, int32_t K,
                                  size_t* scratch_bytes) {
-  if (layout < 0 || layout > 2 || precision < 0 || precision > 1) return fail(QBLK_EINVAL, "gemm: layout/precision");
+  if (layout < 0 || layout > 2 || precision < 0 || precision > 2) return fail(QBLK_EINVAL, "gemm: layout/precision");
   if (M <= 0 || N <= 0 || K <= 0) return fail(QBLK_EINVAL, "gemm: bad shape");
   // enough for either operand storage (fp16 storage plans its own splits)
   size_t need = 0;
@@ -375,8 +376,11 @@ int32_t qblk_gemm(int32_t layout, int32_t precision, int32_t M, int32_t N, int32
 int32_t qblk_gemm_ex(int32_t layout, int32_t precision, int32_t M, int32_t N, int32_t K, const void* A, int64_t lda,
                      int32_t a_dtype, const void* B, int64_t ldb, int32_t b_dtype, float* C, int64_t ldc,
                      int32_t accumulate, void* scratch, size_t scratch_bytes, qblk_stream_t stream) {
-  if (layout < 0 || layout > 2 || precision < 0 || precision > 1) return fail(QBLK_EINVAL, "gemm: layout/precision");
-  if (a_dtype < 0 || a_dtype > 1 || b_dtype < 0 || b_dtype > 1) return fail(QBLK_EINVAL, "gemm: operand dtype");
+  if (layout < 0 || layout > 2 || precision < 0 || precision > 2) return fail(QBLK_EINVAL, "gemm: layout/precision");
+  if (a_dtype < 0 || a_dtype > 2 || b_dtype < 0 || b_dtype > 2) return fail(QBLK_EINVAL, "gemm: operand dtype");
+  // bfloat16 storage goes with bfloat16 operands only, and back
+  if ((precision == 2) != (a_dtype == 2) || (precision == 2) != (b_dtype == 2))
+    return fail(QBLK_EINVAL, "gemm: bfloat16 operands (precision 2) need bfloat16 storage (dtype 2) of both");
   if (lda % 4 || ldb % 4) return fail(QBLK_EINVAL, "gemm: lda and ldb must be multiples of 4");
   if (!A || !B || !C || !aligned16(A) || !aligned16(B)) return fail(QBLK_EINVAL, "gemm: null or misaligned operand");
   GemmDesc d;
@@ -384,7 +388,7 @@ int32_t qblk_gemm_ex(int32_t layout, int32_t precision, int32_t M, int32_t N, in
   d.prec = (Prec)precision;
   d.M = M; d.N = N; d.K = K;
   d.a = A; d.lda = lda;
-  d.a_src = a_dtype ? Src::F16 : Src::F32;
+  d.a_src = a_dtype ? Src::F16 : Src::F32;  // Src::F16: 16-bit storage (fp16, or bfloat16 with precision 2)
   d.b_src = b_dtype ? Src::F16 : Src::F32;
   const int brows = d.layout == Layout::NT ? N : K;
   d.b = seg1(B, brows); d.ldb = ldb;

@@ -50,6 +50,7 @@ struct AttnDmaArgs {
   float* dk; int64_t lddk;
   float* dv; int64_t lddv;
   f16* dv16 = nullptr; int64_t lddv16 = 0;  // optional fp16 copy of dv
+  int bf16 = 0;  // 16-bit operands and copies are bfloat16 (else fp16)
 };
 
 bool attention_dma_supported(int batch, int seq, int heads, int kv_heads, int head_dim);

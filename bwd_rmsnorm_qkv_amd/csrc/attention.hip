@@ -463,7 +463,7 @@ __global__ __launch_bounds__(64) void attn_dkv_kernel(const AttnArgs a, const fl
   }
 }
 
-__global__ void attn_gqa_reduce_kernel(int64_t T, int heads, int kv_heads, int D,
+__global__ void attn_gqa_reduce_kernel(int64_t T, int heads, int kv_heads, int D, int bf16,
                                        const float* dk_part, const float* dv_part, float* dk,
                                        int64_t lddk, float* dv, int64_t lddv, f16* dv16, int64_t lddv16) {
   const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -481,7 +481,7 @@ __global__ void attn_gqa_reduce_kernel(int64_t T, int heads, int kv_heads, int D
   }
   dk[t * lddk + g * D + j] = sk;
   dv[t * lddv + g * D + j] = sv;
-  if (dv16) dv16[t * lddv16 + g * D + j] = (f16)sv;
+  if (dv16) dv16[t * lddv16 + g * D + j] = to_16(sv, bf16);
 }
 
 template <Prec P, int DP>
@@ -508,7 +508,7 @@ int bwd_launch(const AttnArgs& a, float* delta, float* dk_part, float* dv_part, 
   QBLK_TRY(check_launch("attn_dkv_kernel"));
   const int64_t n = T * a.kv_heads * a.head_dim;
   hipLaunchKernelGGL(attn_gqa_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, T,
-                     a.heads, a.kv_heads, a.head_dim, (const float*)dk_part, (const float*)dv_part, a.dk,
+                     a.heads, a.kv_heads, a.head_dim, 0, (const float*)dk_part, (const float*)dv_part, a.dk,
                      a.lddk, a.dv, a.lddv, (f16*)nullptr, (int64_t)0);
   return check_launch("attn_gqa_reduce_kernel");
 }
@@ -545,6 +545,12 @@ struct AttnElem<f16> {
   static __device__ __forceinline__ floatx16 mma(Chunk a, Chunk b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
+};
+template <>
+struct AttnElem<bf16> {  // bfloat16 bit patterns in the same 16-byte chunks
+  using Chunk = half8;
+  static constexpr int EPC = 8;
+  static __device__ __forceinline__ floatx16 mma(Chunk a, Chunk b, floatx16 c) { return mfma16<true>(a, b, c); }
 };
 template <>
 struct AttnElem<float> {
@@ -633,7 +639,7 @@ struct TrReads {
         v[db][rr] = (uint32_t)((slot + row * D + (((col >> 3) ^ RT::sw(row)) << 3) + (col & 7)) * 2);
       }
   }
-  __device__ __forceinline__ half8 frag(const f16* X, int db, int s2) const {
+  __device__ __forceinline__ half8 frag(const void* X, int db, int s2) const {
     typedef short short4v __attribute__((ext_vector_type(4)));
     half8 out;
 #pragma unroll
@@ -742,19 +748,21 @@ __device__ __forceinline__ void load_row_frags(const T* row, int kh, typename At
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef unsigned uint4v __attribute__((ext_vector_type(4)));
 
+template <bool BF>
 __device__ __forceinline__ unsigned pack2(float a, float b) {
   half2v h;
-  h[0] = (f16)a;
-  h[1] = (f16)b;
+  h[0] = to_16(a, BF);
+  h[1] = to_16(b, BF);
   return __builtin_bit_cast(unsigned, h);
 }
 
 // fp16: accumulator values 8 s2 .. 8 s2 + 7 as the B operand of a product
 // contracting over rows 16 s2 .. 16 s2 + 15: after the swap, lane half kh
 // holds rows 16 s2 + 8 kh + j, j = 0..7, in order.
+template <bool BF>
 __device__ __forceinline__ half8 acc_rows_operand(const floatx16& p, int s2) {
-  unsigned r0a = pack2(p[8 * s2 + 0], p[8 * s2 + 1]), r0b = pack2(p[8 * s2 + 2], p[8 * s2 + 3]);
-  unsigned r1a = pack2(p[8 * s2 + 4], p[8 * s2 + 5]), r1b = pack2(p[8 * s2 + 6], p[8 * s2 + 7]);
+  unsigned r0a = pack2<BF>(p[8 * s2 + 0], p[8 * s2 + 1]), r0b = pack2<BF>(p[8 * s2 + 2], p[8 * s2 + 3]);
+  unsigned r1a = pack2<BF>(p[8 * s2 + 4], p[8 * s2 + 5]), r1b = pack2<BF>(p[8 * s2 + 6], p[8 * s2 + 7]);
   const auto x = __builtin_amdgcn_permlane32_swap(r0a, r1a, false, false);
   const auto y = __builtin_amdgcn_permlane32_swap(r0b, r1b, false, false);
   uint4v u;
@@ -767,15 +775,14 @@ __device__ __forceinline__ half8 acc_rows_operand(const floatx16& p, int s2) {
 
 // fp16: out[db] += X^T-block times the 32 x 32 accumulator p, contracting
 // over the accumulator's rows; X is a row tile [32][D] read transposed.
-template <int D>
-__device__ __forceinline__ void acc_rows_product_tr(const f16* X, const TrReads<D>& rd, const floatx16& p,
+template <int D, bool BF>
+__device__ __forceinline__ void acc_rows_product_tr(const void* X, const TrReads<D>& rd, const floatx16& p,
                                                     floatx16 (&out)[D / 32]) {
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
-    const half8 bp = acc_rows_operand(p, s2);
+    const half8 bp = acc_rows_operand<BF>(p, s2);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-      out[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rd.frag(X, db, s2), bp, out[db], 0, 0, 0);
+    for (int db = 0; db < D / 32; ++db) out[db] = mfma16<BF>(rd.frag(X, db, s2), bp, out[db]);
   }
 }
 
@@ -811,7 +818,7 @@ __device__ __forceinline__ XtReads<T, D> make_xt_reads(int lane, int slot_rows, 
 template <typename T, int D>
 __device__ __forceinline__ void acc_rows_product_any(const T* X, const XtReads<T, D>& rd, const floatx16& p,
                                                      floatx16 (&out)[D / 32]) {
-  if constexpr (sizeof(T) == 2) acc_rows_product_tr<D>(X, rd, p, out);
+  if constexpr (sizeof(T) == 2) acc_rows_product_tr<D, std::is_same_v<T, bf16>>(X, rd, p, out);
   else acc_rows_product_tt<D>(X, rd, p, out);
 }
 
@@ -1097,7 +1104,7 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
             const float4 vv =
                 make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
             *(float4*)(a.o + ooff + db * 32 + 8 * g) = vv;
-            if (a.o16) *(half4*)(a.o16 + ooff + db * 32 + 8 * g) = to_half4(vv);
+            if (a.o16) *(half4*)(a.o16 + ooff + db * 32 + 8 * g) = to_16x4(vv, std::is_same_v<T, bf16>);
           }
         }
       if (w == 0 && kh == 0) a.lse[((int64_t)b * a.heads + h) * S + qi] = (M + log2f(L)) * kLn2;
@@ -1459,7 +1466,7 @@ int bwd_dma_launch(const AttnDmaArgs& a, float* delta, float* dk_part, float* dv
   QBLK_TRY(check_launch("attn_dma_dkv_kernel"));
   const int64_t n = T_ * a.kv_heads * D;
   hipLaunchKernelGGL(attn_gqa_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, T_, a.heads,
-                     a.kv_heads, D, (const float*)dk_part, (const float*)dv_part, a.dk, a.lddk, a.dv, a.lddv,
+                     a.kv_heads, D, a.bf16, (const float*)dk_part, (const float*)dv_part, a.dk, a.lddk, a.dv, a.lddv,
                      a.dv16, a.lddv16);
   return check_launch("attn_gqa_reduce_kernel");
 }
@@ -1535,6 +1542,7 @@ int attention_dma_forward(const AttnDmaArgs& a, hipStream_t st) {
     if (a.head_dim != 64) return fail(QBLK_EUNSUPPORTED, "attention (tiled copies): fp32 needs head_dim 64");
     return fwd_dma_launch<float, 64>(a, st);
   }
+  if (a.bf16) return a.head_dim == 64 ? fwd_dma_launch<bf16, 64>(a, st) : fwd_dma_launch<bf16, 128>(a, st);
   return a.head_dim == 64 ? fwd_dma_launch<f16, 64>(a, st) : fwd_dma_launch<f16, 128>(a, st);
 }
 
@@ -1555,6 +1563,9 @@ int attention_dma_backward(const AttnDmaArgs& a, void* scratch, hipStream_t st) 
     if (a.head_dim != 64) return fail(QBLK_EUNSUPPORTED, "attention backward (tiled copies): fp32 needs head_dim 64");
     return bwd_dma_launch<float, 64>(a, delta, dk_part, dv_part, st);
   }
+  if (a.bf16)
+    return a.head_dim == 64 ? bwd_dma_launch<bf16, 64>(a, delta, dk_part, dv_part, st)
+                            : bwd_dma_launch<bf16, 128>(a, delta, dk_part, dv_part, st);
   return a.head_dim == 64 ? bwd_dma_launch<f16, 64>(a, delta, dk_part, dv_part, st)
                           : bwd_dma_launch<f16, 128>(a, delta, dk_part, dv_part, st);
 }

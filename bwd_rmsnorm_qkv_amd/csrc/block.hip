@@ -57,7 +57,7 @@ void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes) {
   s.gu = cv.take<float>(T * 2 * I);
   s.s = cv.take<float>(T * I);
   s.n1_16 = s.o16 = s.n2_16 = s.s16 = nullptr;
-  if (c.gemm_precision == 1 && T % 8 == 0) {
+  if (c.gemm_precision != 0 && T % 8 == 0) {
     s.n1_16 = cv.take<f16>(T * h);
     s.o16 = cv.take<f16>(T * qd);
     s.n2_16 = cv.take<f16>(T * h);
@@ -65,7 +65,7 @@ void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes) {
   }
   s.q16 = s.k16 = s.v16 = nullptr;
   s.qT32 = s.kT32 = s.vT32 = nullptr;
-  if (use_attention_dma(c) && c.gemm_precision == 1) {
+  if (use_attention_dma(c) && c.gemm_precision != 0) {
     s.q16 = cv.take<f16>(T * qd);
     s.k16 = cv.take<f16>(T * kvd);
     s.v16 = cv.take<f16>(T * kvd);
@@ -79,10 +79,15 @@ void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes) {
 
 bool use_attention_dma(const qblk_config& c) {
   return attention_dma_supported(c.batch, c.seq, c.heads, c.kv_heads, c.head_dim) &&
-         (c.gemm_precision == 1 || c.head_dim == 64);
+         (c.gemm_precision != 0 || c.head_dim == 64);
 }
 
-Prec prec_of(const qblk_config& c) { return c.gemm_precision ? Prec::F16 : Prec::F32; }
+Prec prec_of(const qblk_config& c) {
+  return c.gemm_precision == 2 ? Prec::BF16 : c.gemm_precision == 1 ? Prec::F16 : Prec::F32;
+}
+
+// The block's 16-bit operand copies hold bfloat16 (gemm_precision 2).
+static bool bf(const qblk_config& c) { return c.gemm_precision == 2; }
 
 // Largest split-K workspace any GEMM of the block asks for.
 static size_t block_gemm_ws(const qblk_config& c, int r) {
@@ -150,14 +155,14 @@ void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes, 
   s.pack = Packed16{};
   s.do16 = nullptr;
   s.doT32 = nullptr;
-  if (use_attention_dma(c) && c.gemm_precision == 1) {
+  if (use_attention_dma(c) && c.gemm_precision != 0) {
     s.do16 = cv.take<f16>(T * qd);
   } else if (use_attention_dma(c)) {
     s.doT32 = cv.take<float>(T * qd);
   }
-  if (c.gemm_precision == 1 && (lora_rank == 0 || T % 8 == 0))
+  if (c.gemm_precision != 0 && (lora_rank == 0 || T % 8 == 0))
     s.a16 = cv.take<f16>(T * std::max({qd + 2 * kvd, 2 * I, h, qd}));
-  if (c.gemm_precision == 1 && lora_rank == 0) {
+  if (c.gemm_precision != 0 && lora_rank == 0) {
     size_t pb = 0;
     carve_pack16(c, nullptr, s.pack, pb);
     char* pbase = cv.take<char>(pb);
@@ -182,7 +187,7 @@ int pack16(const qblk_config& c, const qblk_block_params& p, const Packed16& o, 
   const int h = c.hidden, d = c.head_dim;
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
   auto one = [&](int rows, int cols, const float* w, f16* out) {
-    return cast_f16(rows, cols, w, cols, out, cols, nullptr, 0, st);
+    return cast_f16(rows, cols, w, cols, out, cols, nullptr, 0, st, bf(c));
   };
   QBLK_TRY(one(qd, h, p.w_q, o.qkv));
   QBLK_TRY(one(kvd, h, p.w_k, o.qkv + (size_t)qd * h));
@@ -204,8 +209,16 @@ int check_config(const qblk_config* c) {
     return fail(QBLK_EINVAL, "config: hidden, intermediate and heads*head_dim must be multiples of 8");
   if (c->head_dim != 16 && c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
     return fail(QBLK_EUNSUPPORTED, "config: head_dim %d not in {16, 32, 64, 128}", c->head_dim);
-  if (c->gemm_precision != 0 && c->gemm_precision != 1)
-    return fail(QBLK_EINVAL, "config: gemm_precision must be 0 or 1");
+  if (c->gemm_precision < 0 || c->gemm_precision > 2)
+    return fail(QBLK_EINVAL, "config: gemm_precision must be 0, 1 or 2");
+  if (c->gemm_precision == 2) {
+    const int64_t T = (int64_t)c->seq * c->batch;
+    const int qkv = (c->heads + 2 * c->kv_heads) * c->head_dim;
+    if (T % 64 || c->hidden % 64 || c->intermediate % 64 || (c->heads * c->head_dim) % 64 || qkv % 64 ||
+        (c->head_dim != 64 && c->head_dim != 128) || c->seq % 8)
+      return fail(QBLK_EUNSUPPORTED, "config: bfloat16 operands need seq*batch, hidden, intermediate and the "
+                                     "projection widths multiples of 64, head_dim 64 or 128, seq a multiple of 8");
+  }
   if (c->gemm_precision == 0 && c->head_dim == 128)
     return fail(QBLK_EUNSUPPORTED, "config: fp32 attention backward supports head_dim <= 64");
   if (!(c->eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(QBLK_EINVAL, "config: eps/rope_theta");
@@ -235,6 +248,7 @@ AttnDmaArgs attn_dma_args(const qblk_config& c, const Saved& s) {
     a.qT = s.qT32; a.kT = s.kT32; a.vT = s.vT32;
   }
   a.ldt = T;
+  a.bf16 = bf(c);
   a.o = s.o; a.ldo = qd;
   a.lse = s.lse;
   return a;
@@ -253,10 +267,11 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
 
   // the input norm's launch also writes the RoPE table (independent work)
   const RopeTabJob tj = rope_table_job(c.seq, d, c.rope_theta, s.tab);
-  QBLK_TRY(rmsnorm_forward(T, h, c.eps, x, nullptr, g_in, s.n1, s.n1_16, nullptr, s.rho1, st, &tj));
+  QBLK_TRY(rmsnorm_forward(T, h, c.eps, x, nullptr, g_in, s.n1, s.n1_16, nullptr, s.rho1, st, &tj, bf(c)));
   QBLK_TRY(proj.qkv(s.n1, s.qkv, st));
   QkRopeArgs qa{T, c.seq, c.heads, c.kv_heads, d, c.qk_norm, c.eps, s.qkv, ldqkv, g_q, g_k, s.tab,
                 s.qr, s.kr, s.rho_q, s.rho_k};
+  qa.bf16 = bf(c);
   if (s.q16) {  // attention reads only the fp16 operand copies, written here
     qa.q16 = s.q16;
     qa.k16 = s.k16;
@@ -282,12 +297,12 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
     aa.o = s.o; aa.ldo = qd;
     aa.lse = s.lse;
     QBLK_TRY(attention_forward(aa, prec_of(c), st));
-    if (s.o16) QBLK_TRY(cast_f16(T, qd, s.o, qd, s.o16, qd, nullptr, 0, st));
+    if (s.o16) QBLK_TRY(cast_f16(T, qd, s.o, qd, s.o16, qd, nullptr, 0, st, bf(c)));
   }
   QBLK_TRY(proj.o(s.o, x, s.r1, st));  // r1 = x + o Wo^T
-  QBLK_TRY(rmsnorm_forward(T, h, c.eps, s.r1, nullptr, g_post, s.n2, s.n2_16, nullptr, s.rho2, st));
+  QBLK_TRY(rmsnorm_forward(T, h, c.eps, s.r1, nullptr, g_post, s.n2, s.n2_16, nullptr, s.rho2, st, nullptr, bf(c)));
   QBLK_TRY(proj.gate_up(s.n2, s.gu, st));
-  QBLK_TRY(swiglu_forward(T, I, s.gu, s.s, s.s16, st));
+  QBLK_TRY(swiglu_forward(T, I, s.gu, s.s, s.s16, st, bf(c)));
   QBLK_TRY(proj.down(s.s, s.r1, y, st));  // y = r1 + s Wd^T
   return QBLK_OK;
 }
@@ -306,14 +321,14 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
   const bool p16 = w.prod16, qkv16 = p16 && s.q16 != nullptr;
   // FFN: ds = dy Wd; dWd = dy^T s; SwiGLU backward; dn2 = dg Wg + du Wu; dWg, dWu.
   QBLK_TRY(proj.down(dy, s.s, w.ds, st));
-  QBLK_TRY(swiglu_backward(T, I, s.gu, w.ds, p16 ? nullptr : w.dgu, p16 ? w.a16 : nullptr, st));
+  QBLK_TRY(swiglu_backward(T, I, s.gu, w.ds, p16 ? nullptr : w.dgu, p16 ? w.a16 : nullptr, st, bf(c)));
   QBLK_TRY(proj.gate_up(p16 ? nullptr : w.dgu, s.n2, w.dn2, st));
   // post-attention norm backward, plus the second residual's gradient dy
   // the gamma gradients are finished by one column-sum launch at the end
   ColsumJob jobs[kMaxColsumJobs];
   int nj = 0;
   QBLK_TRY(rmsnorm_backward_partials(T, h, c.eps, s.r1, g_post, w.dn2, dy, w.dr1, p16 ? w.a16 : nullptr, w.red,
-                                     st));
+                                     st, bf(c)));
   jobs[nj++] = ColsumJob{rmsnorm_bwd_parts(T, h), h, w.red, dg_post, accumulate};
   // O projection
   QBLK_TRY(proj.o(p16 ? nullptr : w.dr1, s.o, w.d_o, st));
@@ -321,7 +336,7 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
   if (s.q16 || s.qT32) {
     AttnDmaArgs ab = attn_dma_args(c, s);
     if (s.q16) {
-      if (!p16) QBLK_TRY(cast_f16(T, qd, w.d_o, qd, w.do16, qd, nullptr, 0, st));
+      if (!p16) QBLK_TRY(cast_f16(T, qd, w.d_o, qd, w.do16, qd, nullptr, 0, st, bf(c)));
       ab.d_o = w.do16;
     } else {
       QBLK_TRY(transpose_f32(T, qd, w.d_o, qd, w.doT32, T, st));
@@ -358,6 +373,7 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
     qb.dqkv16 = w.a16;
   }
   qb.accumulate_dg = accumulate;
+  qb.bf16 = bf(c);
   QBLK_TRY(qk_norm_rope_backward_partials(qb, w.red_qk, jobs, nj, st));
   QBLK_TRY(proj.qkv(qkv16 ? nullptr : w.dqkv, s.n1, w.dn1, st));
   // input norm backward, plus the first residual's gradient dr1
@@ -392,14 +408,15 @@ Seg seg3(const void* a, int na, const void* b, int nb, const void* cc, int nc) {
   return s;
 }
 
-// Both operands fp16 (the direct-to-LDS GEMM kernel's operands).
-GemmDesc g16(const Scratch& w, Layout l, int M, int N, int K, const f16* a, int64_t lda, const f16* b,
-             int64_t ldb, Seg c, int64_t ldc) {
+// Both operands 16-bit (the direct-to-LDS GEMM kernel's operands), fp16 or
+// bfloat16 as the block's precision says.
+GemmDesc g16(const qblk_config& cfg, const Scratch& w, Layout l, int M, int N, int K, const f16* a, int64_t lda,
+             const f16* b, int64_t ldb, Seg c, int64_t ldc) {
   GemmDesc g;
   g.ws = w.gemm_ws;
   g.ws_bytes = w.gemm_ws_bytes;
   g.layout = l;
-  g.prec = Prec::F16;
+  g.prec = prec_of(cfg);
   g.M = M; g.N = N; g.K = K;
   g.a = a; g.lda = lda; g.a_src = Src::F16;
   g.b = seg1(b, l == Layout::NT ? N : K); g.ldb = ldb; g.b_src = Src::F16;
@@ -410,7 +427,7 @@ GemmDesc g16(const Scratch& w, Layout l, int M, int N, int K, const f16* a, int6
 // The fp16 copies path needs fp16 row strides (T for the transposed
 // attention copies) that are multiples of 8.
 bool use_f16_copies(const qblk_config& c) {
-  return c.gemm_precision == 1 && (c.seq * c.batch) % 8 == 0;
+  return c.gemm_precision != 0 && (c.seq * c.batch) % 8 == 0;
 }
 
 // The weights' fp16 copies: the caller's packed set, or cast into scratch.
@@ -434,7 +451,7 @@ int dense16_forward(const qblk_config& c, const qblk_block_params& p, const floa
   QBLK_TRY(weights16(c, p, w, W, st));
   auto proj = [&](const f16* act, int n_in, const f16* wt, int n_out, const float* res, float* out,
                   hipStream_t s_) -> int {
-    GemmDesc g = g16(w, Layout::NT, T, n_out, n_in, act, n_in, wt, n_in, seg1(out, T), n_out);
+    GemmDesc g = g16(c, w, Layout::NT, T, n_out, n_in, act, n_in, wt, n_in, seg1(out, T), n_out);
     g.r = res; g.ldr = n_out;
     return gemm(g, s_);
   };
@@ -471,12 +488,12 @@ int dense16_backward(const qblk_config& c, const qblk_block_params& p, const qbl
   // dx16 (optional) receives an fp16 copy of dX.
   auto dxdw = [&](const float* dyv, int n_out, const f16* x16, int n_in, const f16* wt, Seg cseg, float* dxo,
                   f16* dx16, hipStream_t s_) -> int {
-    if (dyv) QBLK_TRY(cast_f16(T, n_out, dyv, n_out, w.a16, n_out, nullptr, 0, s_));
-    GemmDesc gx = g16(w, Layout::NN, T, n_in, n_out, w.a16, n_out, wt, n_in, seg1(dxo, T), n_in);
+    if (dyv) QBLK_TRY(cast_f16(T, n_out, dyv, n_out, w.a16, n_out, nullptr, 0, s_, bf(c)));
+    GemmDesc gx = g16(c, w, Layout::NN, T, n_in, n_out, w.a16, n_out, wt, n_in, seg1(dxo, T), n_in);
     gx.c16 = dx16;
     gx.ldc16 = n_in;
     QBLK_TRY(gemm(gx, s_));
-    GemmDesc gw = g16(w, Layout::TN, n_out, n_in, T, w.a16, n_out, x16, n_in, cseg, n_in);
+    GemmDesc gw = g16(c, w, Layout::TN, n_out, n_in, T, w.a16, n_out, x16, n_in, cseg, n_in);
     gw.accumulate = accumulate;
     return gemm(gw, s_);
   };

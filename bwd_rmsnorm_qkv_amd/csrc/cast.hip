@@ -1,6 +1,6 @@
-// fp32 -> fp16 (round to nearest even) copies of a row-major matrix, plain
-// and/or transposed, for the fp16-operand contractions: every product of
-// the block then reads both operands K-contiguous in fp16.
+// fp32 -> fp16 or bfloat16 (round to nearest even) copies of a row-major
+// matrix, plain and/or transposed, for the 16-bit-operand contractions:
+// every product of the block then reads both operands K-contiguous.
 //
 // One workgroup converts a 64 x 64 tile: 16-byte loads along the rows, the
 // plain copy stored straight from registers, the transposed one through an
@@ -14,7 +14,7 @@ namespace {
 
 __global__ __launch_bounds__(256) void cast_f16_kernel(int R, int C, const float* __restrict__ in, int64_t ldi,
                                                        f16* __restrict__ out, int64_t ldo,
-                                                       f16* __restrict__ outT, int64_t ldt) {
+                                                       f16* __restrict__ outT, int64_t ldt, int bf16) {
   __shared__ float tile[64][65];
   const int t = threadIdx.x;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void cast_f16_kernel(int R, int C, const float
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (row < R && col < C) v = *(const float4*)(in + (int64_t)row * ldi + col);
     if (out && row < R && col < C) {
-      *(half4*)(out + (int64_t)row * ldo + col) = to_half4(v);
+      *(half4*)(out + (int64_t)row * ldo + col) = to_16x4(v, bf16);
     }
     tile[lr][lc] = v.x;
     tile[lr][lc + 1] = v.y;
@@ -46,9 +46,10 @@ __global__ __launch_bounds__(256) void cast_f16_kernel(int R, int C, const float
     if (c >= C) continue;
     f16* dst = outT + (int64_t)c * ldt + row;
     if (row + 3 < R) {
-      *(half4*)dst = to_half4(make_float4(tile[lr][lcc], tile[lr + 1][lcc], tile[lr + 2][lcc], tile[lr + 3][lcc]));
+      *(half4*)dst = to_16x4(make_float4(tile[lr][lcc], tile[lr + 1][lcc], tile[lr + 2][lcc], tile[lr + 3][lcc]),
+                             bf16);
     } else {
-      for (int j = 0; j < 4 && row + j < R; ++j) dst[j] = (f16)tile[lr + j][lcc];
+      for (int j = 0; j < 4 && row + j < R; ++j) dst[j] = to_16(tile[lr + j][lcc], bf16);
     }
   }
 }
@@ -56,11 +57,11 @@ __global__ __launch_bounds__(256) void cast_f16_kernel(int R, int C, const float
 // The copy alone (no transpose): float4 column j of row blockIdx.y (+
 // k gridDim.y) per thread, no LDS.
 __global__ __launch_bounds__(256) void cast_f16_rows_kernel(int R, int C, const float* __restrict__ in, int64_t ldi,
-                                                            f16* __restrict__ out, int64_t ldo) {
+                                                            f16* __restrict__ out, int64_t ldo, int bf16) {
   const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (j >= C) return;
   for (int r = blockIdx.y; r < R; r += gridDim.y)
-    *(half4*)(out + (int64_t)r * ldo + j) = to_half4(*(const float4*)(in + (int64_t)r * ldi + j));
+    *(half4*)(out + (int64_t)r * ldo + j) = to_16x4(*(const float4*)(in + (int64_t)r * ldi + j), bf16);
 }
 
 // fp32 transpose through the same 64 x 64 LDS tile.
@@ -111,18 +112,18 @@ int transpose_f32(int R, int C, const float* in, int64_t ldi, float* outT, int64
 }
 
 int cast_f16(int R, int C, const float* in, int64_t ldi, f16* out, int64_t ldo, f16* outT, int64_t ldt,
-             hipStream_t st) {
+             hipStream_t st, bool bf16) {
   if (R <= 0 || C <= 0) return fail(QBLK_EINVAL, "cast_f16: bad shape %d x %d", R, C);
   if (C % 4 || ldi % 4 || (out && ldo % 4) || (outT && ldt % 4))
     return fail(QBLK_EINVAL, "cast_f16: columns and leading dimensions must be multiples of 4");
   if (!in || (!out && !outT)) return fail(QBLK_EINVAL, "cast_f16: null pointer");
   if (!outT) {
     const dim3 g((unsigned)ceil_div(C, 1024), (unsigned)std::min(R, 65535));
-    hipLaunchKernelGGL(cast_f16_rows_kernel, g, dim3(256), 0, st, R, C, in, ldi, out, ldo);
+    hipLaunchKernelGGL(cast_f16_rows_kernel, g, dim3(256), 0, st, R, C, in, ldi, out, ldo, (int)bf16);
     return check_launch("cast_f16_rows_kernel");
   }
   const dim3 grid((unsigned)ceil_div(C, 64), (unsigned)ceil_div(R, 64));
-  hipLaunchKernelGGL(cast_f16_kernel, grid, dim3(256), 0, st, R, C, in, ldi, out, ldo, outT, ldt);
+  hipLaunchKernelGGL(cast_f16_kernel, grid, dim3(256), 0, st, R, C, in, ldi, out, ldo, outT, ldt, (int)bf16);
   return check_launch("cast_f16_kernel");
 }
 

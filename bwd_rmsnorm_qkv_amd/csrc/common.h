@@ -93,12 +93,42 @@ __device__ __forceinline__ float wave_max(float v) {
 // rounding mode; the packed round-toward-zero conversion is never used).
 __device__ __forceinline__ f16 to_f16(float x) { return (f16)x; }
 
+// bfloat16 operands (gemm_precision 2) travel in the same 16-bit buffers as
+// fp16 ones: the buffers are typed f16 as plain 16-bit containers and hold
+// bfloat16 bit patterns when `bf` is set. fp32 -> bf16 rounds to nearest
+// even (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16 to_16(float x, bool bf) {
+  return bf ? __builtin_bit_cast(f16, (bf16)x) : (f16)x;
+}
+
 __device__ __forceinline__ half4 to_half4(float4 v) {
   half4 h;
   h[0] = (f16)v.x;
   h[1] = (f16)v.y;
   h[2] = (f16)v.z;
   h[3] = (f16)v.w;
+  return h;
+}
+
+// v_mfma_f32_32x32x16_f16, or its bfloat16 twin on the same 16-bit lanes.
+template <bool BF>
+__device__ __forceinline__ floatx16 mfma16(half8 a, half8 b, floatx16 c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                    0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half4 to_16x4(float4 v, bool bf) {
+  if (!bf) return to_half4(v);
+  half4 h;
+  h[0] = __builtin_bit_cast(f16, (bf16)v.x);
+  h[1] = __builtin_bit_cast(f16, (bf16)v.y);
+  h[2] = __builtin_bit_cast(f16, (bf16)v.z);
+  h[3] = __builtin_bit_cast(f16, (bf16)v.w);
   return h;
 }
 

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void qk_rope_fwd_kernel(QkRopeArgs a) {
     const int hh = head - nqk;
     const float* src = a.qkv + (int64_t)t * a.ld_qkv + (int64_t)nqk * d + hh * d;
     f16* dst = a.v16 + ((int64_t)t * a.kv_heads + hh) * d;
-    for (int c = lane; c < d; c += 64) dst[c] = (f16)src[c];
+    for (int c = lane; c < d; c += 64) dst[c] = to_16(src[c], a.bf16);
     return;
   }
   const bool is_q = head < a.heads;
@@ -66,8 +66,8 @@ __global__ __launch_bounds__(256) void qk_rope_fwd_kernel(QkRopeArgs a) {
       dst[orow + lane + half] = o1;
     }
     if (dst16) {
-      dst16[orow + lane] = (f16)o0;
-      dst16[orow + lane + half] = (f16)o1;
+      dst16[orow + lane] = to_16(o0, a.bf16);
+      dst16[orow + lane + half] = to_16(o1, a.bf16);
     }
   }
 }
@@ -142,8 +142,8 @@ __global__ __launch_bounds__(256) void qk_rope_bwd_kernel(QkRopeBwdArgs a, int n
         a.dqkv[o + half] = o1;
       }
       if (a.dqkv16) {
-        a.dqkv16[o] = (f16)o0;
-        a.dqkv16[o + half] = (f16)o1;
+        a.dqkv16[o] = to_16(o0, a.bf16);
+        a.dqkv16[o + half] = to_16(o1, a.bf16);
       }
     }
   }
@@ -167,10 +167,10 @@ __global__ __launch_bounds__(256) void qk_rope_bwd_kernel(QkRopeBwdArgs a, int n
 // skipped). Heads past the last of a group's range are computed on head 0
 // and not stored.
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ h2v to_h2(float a, float b) {
+__device__ __forceinline__ h2v to_h2(float a, float b, bool bf) {
   h2v h;
-  h[0] = (f16)a;
-  h[1] = (f16)b;
+  h[0] = to_16(a, bf);
+  h[1] = to_16(b, bf);
   return h;
 }
 
@@ -222,8 +222,8 @@ __global__ __launch_bounds__(256) void qk_rope_fwd_pair_kernel(QkRopeArgs a) {
     if (!valid) continue;
     if (is_v) {
       f16* dst = a.v16 + ((int64_t)t * a.kv_heads + hh) * D + 2 * j;
-      *(h2v*)dst = to_h2(p.x, p.y);
-      *(h2v*)(dst + HALF) = to_h2(q.x, q.y);
+      *(h2v*)dst = to_h2(p.x, p.y, a.bf16);
+      *(h2v*)(dst + HALF) = to_h2(q.x, q.y, a.bf16);
       continue;
     }
     // NeoX rotation of the pairs (2j, HALF + 2j) and (2j + 1, HALF + 2j + 1)
@@ -237,8 +237,8 @@ __global__ __launch_bounds__(256) void qk_rope_fwd_pair_kernel(QkRopeArgs a) {
       *(float2*)(dst + orow + HALF) = o1;
     }
     if (dst16) {
-      *(h2v*)(dst16 + orow) = to_h2(o0.x, o0.y);
-      *(h2v*)(dst16 + orow + HALF) = to_h2(o1.x, o1.y);
+      *(h2v*)(dst16 + orow) = to_h2(o0.x, o0.y, a.bf16);
+      *(h2v*)(dst16 + orow + HALF) = to_h2(o1.x, o1.y, a.bf16);
     }
   }
 }
@@ -315,8 +315,8 @@ __global__ __launch_bounds__(64 * kQkBwdWaves) void qk_rope_bwd_pair_kernel(QkRo
       *(float2*)(a.dqkv + o + HALF) = o1;
     }
     if (a.dqkv16) {
-      *(h2v*)(a.dqkv16 + o) = to_h2(o0.x, o0.y);
-      *(h2v*)(a.dqkv16 + o + HALF) = to_h2(o1.x, o1.y);
+      *(h2v*)(a.dqkv16 + o) = to_h2(o0.x, o0.y, a.bf16);
+      *(h2v*)(a.dqkv16 + o + HALF) = to_h2(o1.x, o1.y, a.bf16);
     }
   }
   if (!a.qk_norm) return;
@@ -380,7 +380,7 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf
 // One row of gu per blockIdx.y step, float4 column j per thread (a 2-D
 // grid: no index division per element).
 __global__ __launch_bounds__(256) void swiglu_fwd_kernel(int T, int I, const float* __restrict__ gu,
-                                                         float* __restrict__ s, f16* __restrict__ s16) {
+                                                         float* __restrict__ s, f16* __restrict__ s16, int bf16) {
   const int i4 = I / 4, j = blockIdx.x * 256 + threadIdx.x;
   if (j >= i4) return;
   for (int t = blockIdx.y; t < T; t += gridDim.y) {
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256) void swiglu_fwd_kernel(int T, int I, const flo
     o.w = g.w * sigmoidf_(g.w) * u.w;
     const int64_t e = (int64_t)t * i4 + j;
     if (s) ((float4*)s)[e] = o;
-    if (s16) ((half4*)s16)[e] = to_half4(o);
+    if (s16) ((half4*)s16)[e] = to_16x4(o, bf16);
   }
 }
 
@@ -406,7 +406,7 @@ __device__ __forceinline__ void swiglu_grad(float g, float u, float ds, float& d
 
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(int T, int I, const float* __restrict__ gu,
                                                          const float* __restrict__ ds, float* __restrict__ dgu,
-                                                         f16* __restrict__ dgu16) {
+                                                         f16* __restrict__ dgu16, int bf16) {
   const int i4 = I / 4, j = blockIdx.x * 256 + threadIdx.x;
   if (j >= i4) return;
   for (int t = blockIdx.y; t < T; t += gridDim.y) {
@@ -423,8 +423,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(int T, int I, const flo
       ((float4*)(dgu + (int64_t)t * 2 * I + I))[j] = du;
     }
     if (dgu16) {
-      ((half4*)(dgu16 + (int64_t)t * 2 * I))[j] = to_half4(dg);
-      ((half4*)(dgu16 + (int64_t)t * 2 * I + I))[j] = to_half4(du);
+      ((half4*)(dgu16 + (int64_t)t * 2 * I))[j] = to_16x4(dg, bf16);
+      ((half4*)(dgu16 + (int64_t)t * 2 * I + I))[j] = to_16x4(du, bf16);
     }
   }
 }
@@ -522,13 +522,14 @@ int qk_norm_rope_backward_partials(const QkRopeBwdArgs& a, float* scratch, Colsu
   return 0;
 }
 
-int swiglu_forward(int T, int I, const float* gu, float* s, f16* s16, hipStream_t st) {
-  hipLaunchKernelGGL(swiglu_fwd_kernel, swiglu_grid(T, I), dim3(256), 0, st, T, I, gu, s, s16);
+int swiglu_forward(int T, int I, const float* gu, float* s, f16* s16, hipStream_t st, bool bf16) {
+  hipLaunchKernelGGL(swiglu_fwd_kernel, swiglu_grid(T, I), dim3(256), 0, st, T, I, gu, s, s16, (int)bf16);
   return check_launch("swiglu_fwd_kernel");
 }
 
-int swiglu_backward(int T, int I, const float* gu, const float* ds, float* dgu, f16* dgu16, hipStream_t st) {
-  hipLaunchKernelGGL(swiglu_bwd_kernel, swiglu_grid(T, I), dim3(256), 0, st, T, I, gu, ds, dgu, dgu16);
+int swiglu_backward(int T, int I, const float* gu, const float* ds, float* dgu, f16* dgu16, hipStream_t st,
+                    bool bf16) {
+  hipLaunchKernelGGL(swiglu_bwd_kernel, swiglu_grid(T, I), dim3(256), 0, st, T, I, gu, ds, dgu, dgu16, (int)bf16);
   return check_launch("swiglu_bwd_kernel");
 }
 

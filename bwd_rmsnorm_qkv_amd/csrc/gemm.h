@@ -15,7 +15,11 @@
 
 namespace qblk {
 
-enum class Prec : int { F32 = 0, F16 = 1 };
+// F16 / BF16: operands rounded to fp16 / bfloat16 (nearest even), fp32
+// accumulate. With BF16, 16-bit operand storage (Src::F16) holds bfloat16
+// bit patterns, and only the direct-to-LDS kernels run (16-bit storage of
+// both operands, K a multiple of 64).
+enum class Prec : int { F32 = 0, F16 = 1, BF16 = 2 };
 enum class Layout : int { NT = 0, NN = 1, TN = 2 };
 enum class Src : int { F32 = 0, F16 = 1, NF4 = 2 };
 

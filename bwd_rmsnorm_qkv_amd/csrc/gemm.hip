@@ -565,7 +565,7 @@ __device__ __forceinline__ bool epi_pass_fast(const GemmDesc& d, bool vec, float
       o.w += cv.w;
     }
     store_c4((float4*)(cp + q * cs), o);
-    if (hp) *(half4*)(hp + q * hs) = to_half4(o);
+    if (hp) *(half4*)(hp + q * hs) = to_16x4(o, d.prec == Prec::BF16);
   }
   return true;
 }
@@ -910,7 +910,7 @@ struct DmaOperand {
   }
 };
 
-template <int BM, int BN, int WM, int WN, int NS, int NB, bool AK, bool BK_>
+template <int BM, int BN, int WM, int WN, int NS, int NB, bool AK, bool BK_, bool BF>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d, const Grid gd) {
   constexpr int BK = 64;
   constexpr int NW = WM * WN;
@@ -979,7 +979,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, TM * TN>([&](auto Jx) __attribute__((always_inline)) {
         constexpr int j = decltype(Jx)::value, tm = j / TN, tn = j % TN, i = s * TM * TN + j;
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[s & 1][tm], bv[s & 1][tn], acc[tm][tn], 0, 0, 0);
+        acc[tm][tn] = mfma16<BF>(av[s & 1][tm], bv[s & 1][tn], acc[tm][tn]);
         static_for<(i * NC) / NM, ((i + 1) * NC) / NM>([&](auto Cx) __attribute__((always_inline)) {
           constexpr int c = decltype(Cx)::value;
           if constexpr (c < OA::J) {
@@ -1132,12 +1132,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
           o.w += cv.w;
         }
         store_c4(cp, o);
-        if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + col) = to_half4(o);
+        if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + col) = to_16x4(o, BF);
       } else {
         for (int j = 0; j < 4 && col + j < d.N; ++j) {
           if (bd > 0 && (col + j < lo || col + j >= lo + bd)) continue;
           put_out(d, rp + (col + j - lo), row, col + j, vv[j]);
-          if (d.c16) d.c16[(int64_t)row * d.ldc16 + col + j] = (f16)rp[col + j - lo];
+          if (d.c16) d.c16[(int64_t)row * d.ldc16 + col + j] = to_16(rp[col + j - lo], BF);
         }
       }
     }
@@ -1443,7 +1443,7 @@ __global__ __launch_bounds__(256) void gemm_nf4_kernel(const GemmDesc d, const G
 // (the weights of a forward product, streamed from HBM while A stays in L2)
 // has a third stage and its copies run two K tiles ahead: B(kt+3) goes into
 // the stage tile kt just freed.
-template <int BN, bool AK, bool BK_, int NB>
+template <int BN, bool AK, bool BK_, int NB, bool BF>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Grid gd) {
   constexpr int BM = 256, WM = 4, WN = 2, BK = 64;
   static_assert(BN == 256 || (BN == 192 && BK_), "192-wide tiles need a K-major B");
@@ -1507,7 +1507,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[ks][tm], bv[ks][tn], acc[tm][tn], 0, 0, 0);
+          acc[tm][tn] = mfma16<BF>(av[ks][tm], bv[ks][tn], acc[tm][tn]);
     __builtin_amdgcn_s_setprio(0);
   };
   // The wave's copies of a refill (Mode bit 0: A of tile ka into sa if ca;
@@ -1533,7 +1533,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
     __builtin_amdgcn_s_setprio(1);
     static_for<0, NM>([&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value, ks = i / (TM * TN), tm = (i / TN) % TM, tn = i % TN;
-      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[ks][tm], bv[ks][tn], acc[tm][tn], 0, 0, 0);
+      acc[tm][tn] = mfma16<BF>(av[ks][tm], bv[ks][tn], acc[tm][tn]);
       copies_after(I, std::integral_constant<int, NM>{}, Mode, ca, ka, sa, cb, kb2, sb);
     });
     __builtin_amdgcn_s_setprio(0);
@@ -1715,12 +1715,12 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmDesc d, const Gr
             o.w += cv.w;
           }
           store_c4(cp, o);
-          if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + col) = to_half4(o);
+          if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + col) = to_16x4(o, BF);
         } else {
           for (int j = 0; j < 4 && col + j < d.N; ++j) {
             if (bd > 0 && (col + j < lo || col + j >= lo + bd)) continue;
             put_out(d, rp + (col + j - lo), row, col + j, vv[j]);
-            if (d.c16) d.c16[(int64_t)row * d.ldc16 + col + j] = (f16)rp[col + j - lo];
+            if (d.c16) d.c16[(int64_t)row * d.ldc16 + col + j] = to_16(rp[col + j - lo], BF);
           }
         }
       }
@@ -1766,7 +1766,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmDesc d, in
           o.w += cv.w;
         }
         store_c4(cp, o);
-        if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + c0) = to_half4(o);
+        if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + c0) = to_16x4(o, d.prec == Prec::BF16);
       } else {
         const float vv[4] = {v.x, v.y, v.z, v.w};
         for (int j = 0; j < 4; ++j)
@@ -1779,7 +1779,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmDesc d, in
         const int col = c0 + j;
         if (bd > 0 && (col < lo || col >= lo + bd)) continue;
         put_out(d, rp + (col - lo), row, col, sj);
-        if (d.c16) d.c16[(int64_t)row * d.ldc16 + col] = (f16)rp[col - lo];
+        if (d.c16) d.c16[(int64_t)row * d.ldc16 + col] = to_16(rp[col - lo], d.prec == Prec::BF16);
       }
     }
   }
@@ -1824,7 +1824,10 @@ struct PpCfg {
   template <int BN, bool AK, bool BKM, int NB>
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
-    hipLaunchKernelGGL((gemm_pp_kernel<BN, AK, BKM, NB>), dim3(nwg), dim3(threads), 0, st, d, g);
+    if (d.prec == Prec::BF16)
+      hipLaunchKernelGGL((gemm_pp_kernel<BN, AK, BKM, NB, true>), dim3(nwg), dim3(threads), 0, st, d, g);
+    else
+      hipLaunchKernelGGL((gemm_pp_kernel<BN, AK, BKM, NB, false>), dim3(nwg), dim3(threads), 0, st, d, g);
   }
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     switch (d.layout) {
@@ -1845,7 +1848,12 @@ struct DmaCfg {
   template <bool AK, bool BKM>
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, AK, BKM>), dim3(nwg), dim3(threads), 0, st, d, g);
+    if (d.prec == Prec::BF16)
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, AK, BKM, true>), dim3(nwg), dim3(threads), 0, st,
+                         d, g);
+    else
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, AK, BKM, false>), dim3(nwg), dim3(threads), 0, st,
+                         d, g);
   }
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     switch (d.layout) {
@@ -1882,7 +1890,7 @@ bool nt16_big(const GemmDesc& d) {
 // extends the contraction, an MN-major operand has M (or N) a multiple of 8
 // and is a single segment.
 bool nt16_ok(const GemmDesc& d) {
-  if (d.prec != Prec::F16) return false;
+  if (d.prec != Prec::F16 && d.prec != Prec::BF16) return false;
   if (d.a_src != Src::F16 || d.b_src != Src::F16 || d.ext.kext > 0 || d.b_src == Src::NF4) return false;
   if (d.K % 64 != 0 || d.lda % 8 != 0 || d.ldb % 8 != 0) return false;
   if ((uintptr_t)d.a % 16 != 0) return false;
@@ -2076,11 +2084,11 @@ int elems16(Src s) { return s == Src::F32 ? 4 : 8; }
 
 namespace {
 __global__ void c16_copy_kernel(int M, int N, const float* __restrict__ c, int64_t ldc, f16* __restrict__ c16,
-                                int64_t ldc16) {
+                                int64_t ldc16, int bf16) {
   const int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (e >= (int64_t)M * N) return;
   const int64_t r = e / N, col = e % N;
-  c16[r * ldc16 + col] = (f16)c[r * ldc + col];
+  c16[r * ldc16 + col] = to_16(c[r * ldc + col], bf16);
 }
 }  // namespace
 
@@ -2094,7 +2102,7 @@ int gemm(const GemmDesc& d, hipStream_t st) {
       QBLK_TRY(gemm(e, st));
       const int64_t mn = (int64_t)d.M * d.N;
       hipLaunchKernelGGL(c16_copy_kernel, dim3((unsigned)ceil_div(mn, 256)), dim3(256), 0, st, d.M, d.N,
-                         (const float*)d.c.p[0], d.ldc, d.c16, d.ldc16);
+                         (const float*)d.c.p[0], d.ldc, d.c16, d.ldc16, (int)(d.prec == Prec::BF16));
       return check_launch("c16_copy_kernel");
     }
   }
@@ -2110,6 +2118,12 @@ int gemm(const GemmDesc& d, hipStream_t st) {
   if (d.ext.kext % 4 != 0) return fail(QBLK_EINVAL, "gemm: K extension must be a multiple of 4");
   if (d.ext.kext > (d.prec == Prec::F16 ? 64 : 32))
     return fail(QBLK_EUNSUPPORTED, "gemm: K extension wider than one K tile");
+  if (d.prec == Prec::BF16) {
+    if (!nt16_ok(d))
+      return fail(QBLK_EUNSUPPORTED, "gemm: bfloat16 operands need 16-bit storage of both operands, K a multiple "
+                                     "of 64 and 16-byte aligned rows");
+    return launch_nt16(d, st);
+  }
   if (d.prec == Prec::F32) {
     switch (d.layout) {
       case Layout::NT: return dispatch_src<Prec::F32, Layout::NT>(d, st);

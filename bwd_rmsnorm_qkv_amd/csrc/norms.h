@@ -13,17 +13,20 @@ size_t rmsnorm_bwd_scratch(int rows, int n);
 // y (fp32) and/or y16 (fp16) = RMSNorm(x [+ res]) * gamma; sum_out = x + res.
 // With `tab` the same launch also writes that RoPE table.
 struct RopeTabJob;
+// bf16: the 16-bit copies (y16, dx16, s16, ...) of every producer below hold
+// bfloat16 instead of fp16.
 int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res,
                     const float* gamma, float* y, f16* y16, float* sum_out, float* rho,
-                    hipStream_t st, const RopeTabJob* tab = nullptr);
+                    hipStream_t st, const RopeTabJob* tab = nullptr, bool bf16 = false);
 // dx = RMSNorm backward (+ dres); dgamma overwritten; scratch: rmsnorm_bwd_scratch.
 int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* gamma,
                      const float* dy, const float* dres, float* dx, f16* dx16, float* dgamma, float* scratch,
-                     hipStream_t st);
+                     hipStream_t st, bool bf16 = false);
 // The same, leaving dgamma's per-block partial sums ([rmsnorm_bwd_parts,
 // n]) in `partial` for a later column sum.
 int rmsnorm_backward_partials(int rows, int n, float eps, const float* x, const float* gamma, const float* dy,
-                              const float* dres, float* dx, f16* dx16, float* partial, hipStream_t st);
+                              const float* dres, float* dx, f16* dx16, float* partial, hipStream_t st,
+                              bool bf16 = false);
 // out[c] = sum_p partial[p][c], fixed order.
 int colsum(int parts, int n, const float* partial, float* out, hipStream_t st);
 // Up to four such sums in one launch.
@@ -68,6 +71,7 @@ struct QkRopeArgs {
   // optional fp16 copies of the attention operands [T, heads d] and
   // [T, kv_heads d] (v16 copies V from qkv unchanged)
   f16 *q16 = nullptr, *k16 = nullptr, *v16 = nullptr;
+  int bf16 = 0;  // the 16-bit copies hold bfloat16
 };
 int qk_norm_rope_forward(const QkRopeArgs& a, hipStream_t st);
 
@@ -86,6 +90,7 @@ struct QkRopeBwdArgs {
   float *dg_q, *dg_k;
   f16* dqkv16 = nullptr;   // optional fp16 copy of the q and k columns of dqkv
   int accumulate_dg = 0;   // 1: dg_q, dg_k receive += (and stay as they are without QK-norm)
+  int bf16 = 0;            // dqkv16 holds bfloat16
 };
 size_t qk_norm_rope_bwd_scratch(int T, int heads, int kv_heads, int head_dim);
 int qk_norm_rope_backward(const QkRopeBwdArgs& a, float* scratch, hipStream_t st);
@@ -96,15 +101,16 @@ int qk_norm_rope_backward_partials(const QkRopeBwdArgs& a, float* scratch, Colsu
                                    hipStream_t st);
 
 // s = silu(g) * u with g, u the two halves of gu [T, 2I]; s fp32 and/or fp16.
-int swiglu_forward(int T, int I, const float* gu, float* s, f16* s16, hipStream_t st);
+int swiglu_forward(int T, int I, const float* gu, float* s, f16* s16, hipStream_t st, bool bf16 = false);
 // dgu = [ds * u * silu'(g) | ds * silu(g)].
-int swiglu_backward(int T, int I, const float* gu, const float* ds, float* dgu, f16* dgu16, hipStream_t st);
+int swiglu_backward(int T, int I, const float* gu, const float* ds, float* dgu, f16* dgu16, hipStream_t st,
+                    bool bf16 = false);
 
 // fp16 copies of an fp32 matrix in [R, C] (row stride ldi): out [R, C]
 // (stride ldo) and/or outT [C, R] (stride ldt); either may be NULL.
 // C and every stride must be multiples of 4.
 int cast_f16(int R, int C, const float* in, int64_t ldi, f16* out, int64_t ldo, f16* outT, int64_t ldt,
-             hipStream_t st);
+             hipStream_t st, bool bf16 = false);
 // outT [C, R] (stride ldt) = transpose of in [R, C] (stride ldi), fp32.
 int transpose_f32(int R, int C, const float* in, int64_t ldi, float* outT, int64_t ldt, hipStream_t st);
 

@@ -127,7 +127,8 @@ __global__ __launch_bounds__(256) void scale_kernel(const ScaleChunk c, const fl
 
 struct AdamChunk {
   float* w[kChunk];
-  f16* w16[kChunk];  // optional fp16 copy of the updated weight (NULL: none)
+  f16* w16[kChunk];  // optional 16-bit copy of the updated weight (NULL: none)
+  int bf16;          // the copies are bfloat16 (else fp16)
   const float* g[kChunk];
   float* m[kChunk];
   float* v[kChunk];
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk c, const Ada
       store_stream(w + e, W[u]);
       store_stream(m + e, M[u]);
       store_stream(v + e, V[u]);
-      if (w16) *(half4*)(w16 + e) = to_half4(W[u]);
+      if (w16) *(half4*)(w16 + e) = to_16x4(W[u], c.bf16);
     }
   } else {
     const int64_t end = min(base + (int64_t)kTile, n);
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk c, const Ada
       w[e] = W;
       m[e] = M;
       v[e] = V;
-      if (w16) w16[e] = to_f16(W);
+      if (w16) w16[e] = to_16(W, c.bf16);
     }
   }
 }
@@ -287,7 +288,7 @@ size_t static_clip_scratch_bytes() { return sizeof(double) * kStaticClipChunks *
 
 int adamw(int n, float* const* w, const float* const* g, float* const* m, float* const* v,
           const int64_t* numel, float lr, float b1, float b2, float eps, float wd, int step,
-          const float* scale_dev, hipStream_t st, f16* const* w16) {
+          const float* scale_dev, hipStream_t st, f16* const* w16, bool bf16) {
   AdamHp h;
   h.lr = lr;
   h.b1 = b1;
@@ -298,6 +299,7 @@ int adamw(int n, float* const* w, const float* const* g, float* const* m, float*
   h.bc2 = (float)(1.0 - pow((double)b2, (double)step));
   for (int ci = 0; ci < nchunks(n); ++ci) {
     AdamChunk c{};
+    c.bf16 = bf16;
     int64_t acc = 0;
     for (int j = ci * kChunk; j < std::min(n, (ci + 1) * kChunk); ++j) {
       c.w[c.count] = w[j];

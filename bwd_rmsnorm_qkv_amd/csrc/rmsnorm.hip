@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(int rows, int n, float
                                                           const float* __restrict__ res,
                                                           const float* __restrict__ gamma,
                                                           float* __restrict__ y,
-                                                          f16* __restrict__ y16,
+                                                          f16* __restrict__ y16, int bf16,
                                                           float* __restrict__ sum_out,
                                                           float* __restrict__ rho_out,
                                                           const RopeTabJob tj) {
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(int rows, int n, float
       o.z = v[j].z * rho * g.z;
       o.w = v[j].w * rho * g.w;
       if (y) ((float4*)(y + (int64_t)row * n))[c] = o;
-      if (y16) ((half4*)(y16 + (int64_t)row * n))[c] = to_half4(o);
+      if (y16) ((half4*)(y16 + (int64_t)row * n))[c] = to_16x4(o, bf16);
     }
   }
 }
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int rows, int n, float
                                                           const float* __restrict__ dy,
                                                           const float* __restrict__ dres,
                                                           float* __restrict__ dx,
-                                                          f16* __restrict__ dx16,
+                                                          f16* __restrict__ dx16, int bf16,
                                                           float* __restrict__ partial) {
   __shared__ float4 red[kWavesPerBlock][VPL * 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(int rows, int n, float
         o.w = rho * (e[j].w - xv[j].w * dot);
         o.x += rv[j].x; o.y += rv[j].y; o.z += rv[j].z; o.w += rv[j].w;
         ((float4*)(dx + (int64_t)row * n))[c] = o;
-        if (dx16) ((half4*)(dx16 + (int64_t)row * n))[c] = to_half4(o);
+        if (dx16) ((half4*)(dx16 + (int64_t)row * n))[c] = to_16x4(o, bf16);
         dg[j].x += dv[j].x * xv[j].x;
         dg[j].y += dv[j].y * xv[j].y;
         dg[j].z += dv[j].z * xv[j].z;
@@ -186,7 +186,8 @@ template <int VPT>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_row_kernel(int rows, int n, float eps, const float* __restrict__ x,
                                                               const float* __restrict__ res,
                                                               const float* __restrict__ gamma, float* __restrict__ y,
-                                                              f16* __restrict__ y16, float* __restrict__ sum_out,
+                                                              f16* __restrict__ y16, int bf16,
+                                                              float* __restrict__ sum_out,
                                                               float* __restrict__ rho_out, const RopeTabJob tj) {
   __shared__ float red[4];
   if ((int)blockIdx.x >= rows) {  // the RoPE table's workgroups
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_row_kernel(int rows, int n, f
       const float4 o = make_float4(v[j].x * rho * gv[j].x, v[j].y * rho * gv[j].y, v[j].z * rho * gv[j].z,
                                    v[j].w * rho * gv[j].w);
       if (y) ((float4*)(y + (int64_t)row * n))[c] = o;
-      if (y16) ((half4*)(y16 + (int64_t)row * n))[c] = to_half4(o);
+      if (y16) ((half4*)(y16 + (int64_t)row * n))[c] = to_16x4(o, bf16);
     }
   }
 }
@@ -243,8 +244,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_row_kernel(int rows, int n, f
                                                               const float* __restrict__ gamma,
                                                               const float* __restrict__ dy,
                                                               const float* __restrict__ dres, float* __restrict__ dx,
-                                                              f16* __restrict__ dx16, float* __restrict__ partial,
-                                                              int rpb) {
+                                                              f16* __restrict__ dx16, int bf16,
+                                                              float* __restrict__ partial, int rpb) {
   __shared__ float red[2][2][4];  // [row of the pair][row sum, dot][wave]
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int n4 = n >> 2;
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_row_kernel(int rows, int n, f
         o.z = rho[k] * (gv[j].z * d.z - xh.z * dm) + r.z;
         o.w = rho[k] * (gv[j].w * d.w - xh.w * dm) + r.w;
         ((float4*)(dx + (int64_t)row * n))[c] = o;
-        if (dx16) ((half4*)(dx16 + (int64_t)row * n))[c] = to_half4(o);
+        if (dx16) ((half4*)(dx16 + (int64_t)row * n))[c] = to_16x4(o, bf16);
         dg[j] = make_float4(dg[j].x + d.x * xh.x, dg[j].y + d.y * xh.y, dg[j].z + d.z * xh.z, dg[j].w + d.w * xh.w);
       }
     }
@@ -402,7 +403,7 @@ int rmsnorm_check(int rows, int n) {
 
 int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res,
                     const float* gamma, float* y, f16* y16, float* sum_out, float* rho,
-                    hipStream_t st, const RopeTabJob* tab) {
+                    hipStream_t st, const RopeTabJob* tab, bool bf16) {
   QBLK_TRY(rmsnorm_check(rows, n));
   const RopeTabJob tj = tab ? *tab : RopeTabJob{};
   const int64_t tab_blocks = ceil_div((int64_t)tj.seq * tj.half, 256);
@@ -412,7 +413,7 @@ int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res
 #define QBLK_CASE(V)                                                                                       \
   case V:                                                                                                  \
     hipLaunchKernelGGL(rmsnorm_fwd_row_kernel<V>, g, dim3(256), 0, st, rows, n, eps, x, res, gamma, y, y16, \
-                       sum_out, rho, tj);                                                                  \
+                       (int)bf16, sum_out, rho, tj);                                                                  \
     break;
       QBLK_CASE(1) QBLK_CASE(2) QBLK_CASE(3) QBLK_CASE(4)
 #undef QBLK_CASE
@@ -424,7 +425,7 @@ int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res
 #define QBLK_CASE(V)                                                                          \
   case V:                                                                                     \
     hipLaunchKernelGGL(rmsnorm_fwd_kernel<V>, grid, block, 0, st, rows, n, eps, x, res, gamma, \
-                       y, y16, sum_out, rho, tj);                                             \
+                       y, y16, (int)bf16, sum_out, rho, tj);                                  \
     break;
     QBLK_CASE(1) QBLK_CASE(2) QBLK_CASE(4) QBLK_CASE(8) QBLK_CASE(12) QBLK_CASE(16)
 #undef QBLK_CASE
@@ -434,13 +435,13 @@ int rmsnorm_forward(int rows, int n, float eps, const float* x, const float* res
 
 int rmsnorm_backward(int rows, int n, float eps, const float* x, const float* gamma,
                      const float* dy, const float* dres, float* dx, f16* dx16, float* dgamma, float* scratch,
-                     hipStream_t st) {
-  QBLK_TRY(rmsnorm_backward_partials(rows, n, eps, x, gamma, dy, dres, dx, dx16, scratch, st));
+                     hipStream_t st, bool bf16) {
+  QBLK_TRY(rmsnorm_backward_partials(rows, n, eps, x, gamma, dy, dres, dx, dx16, scratch, st, bf16));
   return colsum(rmsnorm_bwd_parts(rows, n), n, scratch, dgamma, st);
 }
 
 int rmsnorm_backward_partials(int rows, int n, float eps, const float* x, const float* gamma, const float* dy,
-                              const float* dres, float* dx, f16* dx16, float* scratch, hipStream_t st) {
+                              const float* dres, float* dx, f16* dx16, float* scratch, hipStream_t st, bool bf16) {
   QBLK_TRY(rmsnorm_check(rows, n));
   const int parts = rmsnorm_bwd_parts(rows, n);
   if (rms_rowwg(rows, n)) {
@@ -449,7 +450,7 @@ int rmsnorm_backward_partials(int rows, int n, float eps, const float* x, const 
 #define QBLK_CASE(V)                                                                                         \
   case V:                                                                                                    \
     hipLaunchKernelGGL(rmsnorm_bwd_row_kernel<V>, dim3((unsigned)parts), dim3(256), 0, st, rows, n, eps, x, \
-                       gamma, dy, dres, dx, dx16, scratch, rpb);                                             \
+                       gamma, dy, dres, dx, dx16, (int)bf16, scratch, rpb);                                  \
     break;
       QBLK_CASE(1) QBLK_CASE(2) QBLK_CASE(3) QBLK_CASE(4)
 #undef QBLK_CASE
@@ -461,7 +462,7 @@ int rmsnorm_backward_partials(int rows, int n, float eps, const float* x, const 
 #define QBLK_CASE(V)                                                                             \
   case V:                                                                                        \
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<V>, grid, block, 0, st, rows, n, eps, x, gamma, dy,     \
-                       dres, dx, dx16, scratch);                                                 \
+                       dres, dx, dx16, (int)bf16, scratch);                                      \
     break;
     QBLK_CASE(1) QBLK_CASE(2) QBLK_CASE(4) QBLK_CASE(8) QBLK_CASE(12) QBLK_CASE(16)
 #undef QBLK_CASE

@@ -18,11 +18,12 @@ int clip_grad_norm(int n, float* const* g, const int64_t* numel, float max_norm,
 // up on the current device) and its size in bytes.
 int static_clip_scratch(void** out);
 size_t static_clip_scratch_bytes();
-// w16 (optional host array, entries may be NULL): an fp16 copy (round to
-// nearest even) of each updated weight written in the same pass.
+// w16 (optional host array, entries may be NULL): a 16-bit copy (fp16, or
+// bfloat16 with bf16; round to nearest even) of each updated weight written
+// in the same pass.
 int adamw(int n, float* const* w, const float* const* g, float* const* m, float* const* v,
           const int64_t* numel, float lr, float b1, float b2, float eps, float wd, int step,
-          const float* scale_dev, hipStream_t st, f16* const* w16 = nullptr);
+          const float* scale_dev, hipStream_t st, f16* const* w16 = nullptr, bool bf16 = false);
 
 int nf4_quantize(const float* w, int64_t numel, uint8_t* codes, float* absmax, hipStream_t st);
 // fp16 decode (L[c] * a in fp32, rounded to nearest even) for the GEMMs.

@@ -88,8 +88,8 @@ _SIGS = {
     "qblk_adamw_step": ([C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                          C.c_float, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, C.c_void_p,
                          C.c_void_p], C.c_int32),
-    "qblk_adamw_step_pack16": ([C.c_int32] + [C.c_void_p] * 6 + [C.c_float] * 5 + [C.c_int32, C.c_void_p,
-                                                                                    C.c_void_p], C.c_int32),
+    "qblk_adamw_step_pack16": ([C.c_int32] + [C.c_void_p] * 6 + [C.c_int32] + [C.c_float] * 5
+                               + [C.c_int32, C.c_void_p, C.c_void_p], C.c_int32),
     "qblk_block_pack_f16_offsets": ([C.c_void_p, C.c_void_p], C.c_int32),
     "qblk_nf4_codebook": ([C.c_void_p], C.c_int32),
     "qblk_nf4_quantize": ([C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int32),
@@ -320,14 +320,15 @@ def qk_norm_rope_backward(tokens, seq, heads, kv_heads, head_dim, qk_norm, eps, 
 
 
 def adamw_step_pack16(w, g, m, v, w16, lr, beta1, beta2, eps, weight_decay, step, grad_scale_dev=None,
-                      stream=None):
-    """w16: per tensor an fp16 device address (int) or tensor for the copy, or None."""
+                      stream=None, bf16=False):
+    """w16: per tensor a 16-bit device address (int) or tensor for the copy,
+    or None; bf16: the copies are bfloat16 (else fp16)."""
     assert len(w) == len(g) == len(m) == len(v) == len(w16)
     ptrs = (C.c_void_p * len(w16))(*[(x if isinstance(x, int) else _p(x)) if x is not None else None
                                      for x in w16])
     _check(lib().qblk_adamw_step_pack16(len(w), _ptr_array(w), _ptr_array(g), _ptr_array(m), _ptr_array(v),
-                                        _numel_array(w), ptrs, lr, beta1, beta2, eps, weight_decay, int(step),
-                                        _p(grad_scale_dev), _stream(stream)))
+                                        _numel_array(w), ptrs, int(bool(bf16)), lr, beta1, beta2, eps, weight_decay,
+                                        int(step), _p(grad_scale_dev), _stream(stream)))
 
 
 def block_pack_f16_offsets(cfg):
@@ -396,9 +397,9 @@ def gemm_workspace_size(layout, precision, M, N, K):
 
 
 def gemm(layout, precision, M, N, K, A, lda, B, ldb, Cm, ldc, accumulate=0, scratch=None, stream=None):
-    """fp32 or fp16 operand tensors (the storage type is taken from the tensors)."""
+    """fp32, fp16 or bfloat16 operand tensors (the storage type is taken from the tensors)."""
     nbytes = 0 if scratch is None else scratch.numel() * scratch.element_size()
-    code = lambda t: {torch.float32: 0, torch.float16: 1}[t.dtype]
+    code = lambda t: {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[t.dtype]
     _check(lib().qblk_gemm_ex(layout, precision, M, N, K, _p(A), lda, code(A), _p(B), ldb, code(B), _p(Cm), ldc,
                               accumulate, _p(scratch), nbytes, _stream(stream)))
 

@@ -111,7 +111,7 @@ class BlockTrainStep:
         self.max_norm = max_norm
         shapes = block_shapes(cfg)
         self.w, self.g, self.m, self.v = (FlatParams(shapes) for _ in range(4))
-        self.fp16 = cfg.gemm_precision == 1
+        self.fp16 = cfg.gemm_precision in (1, 2)  # 16-bit operands: fp16 (1) or bfloat16 (2)
         self.params = self.w.views
         if self.fp16:
             self.packed = byte_buffer(qblk.block_pack_f16_size(self.blk.c))
@@ -140,7 +140,7 @@ class BlockTrainStep:
         if self.fp16:
             qblk.adamw_step_pack16(self.w.tensors(), self.g.tensors(), self.m.tensors(), self.v.tensors(), self.w16,
                                    hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], self.t,
-                                   grad_scale_dev=self.scale)
+                                   grad_scale_dev=self.scale, bf16=self.cfg.gemm_precision == 2)
         else:
             qblk.adamw_step([self.w.buf], [self.g.buf], [self.m.buf], [self.v.buf], hp["lr"], hp["beta1"],
                             hp["beta2"], hp["eps"], hp["weight_decay"], self.t, grad_scale_dev=self.scale)

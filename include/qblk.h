@@ -62,7 +62,11 @@ typedef struct {
   int32_t qk_norm;      /* 1: per-head RMSNorm on Q and K before RoPE */
   int32_t gemm_precision; /* 0: fp32 contractions; 1: fp16 operands (round to
                              nearest even), fp32 accumulate, for every
-                             projection and the attention products */
+                             projection and the attention products;
+                             2: the same with bfloat16 operands (needs
+                             seq*batch, hidden, intermediate and the
+                             projection widths multiples of 64, head_dim
+                             64 or 128; else QBLK_EUNSUPPORTED) */
 } qblk_config;
 
 /* The 11 trainable tensors of a block: w_q [H*d, h], w_k [KV*d, h],
@@ -96,7 +100,8 @@ int32_t qblk_block_workspace_size(const qblk_config* cfg, size_t* saved_bytes,
 int32_t qblk_block_pack_f16_size(const qblk_config* cfg, size_t* bytes);
 
 /* Writes the packed fp16 weight set ([block] set_fp16_weights, cast_f32_to_f16
- * with round to nearest even) of p's fp32 projection weights into `packed`
+ * with round to nearest even; bfloat16 when cfg->gemm_precision is 2) of
+ * p's fp32 projection weights into `packed`
  * (device, 16-byte aligned, at least qblk_block_pack_f16_size bytes): each
  * weight as stored and transposed, for the forward and the dX products. */
 int32_t qblk_block_pack_f16(const qblk_config* cfg, const qblk_block_params* p, void* packed,
@@ -215,17 +220,19 @@ int32_t qblk_adamw_step(int32_t n, float* const* w, const float* const* g, float
                         float eps, float weight_decay, int32_t step, const float* grad_scale_dev,
                         qblk_stream_t stream);
 
-/* AdamW that also writes the fp16 copy of every updated weight in the same
- * pass (round to nearest even), so a training step with fp16 GEMM operands
- * needs no separate cast of the fp32 masters ([block] set_fp16_weights
- * refreshes such copies after each update). Same arguments and errors as
- * qblk_adamw_step, plus w16: host array of n device pointers to fp16
- * buffers of numel[i] elements (2-byte aligned; an entry may be NULL: no
- * copy for that tensor). For the packed set of qblk_block_pack_f16 the
- * pointers are packed + 2 * offset, offsets from qblk_block_pack_f16_offsets. */
+/* AdamW that also writes the 16-bit copy of every updated weight in the same
+ * pass (round to nearest even), so a training step with 16-bit GEMM
+ * operands needs no separate cast of the fp32 masters ([block]
+ * set_fp16_weights refreshes such copies after each update). Same arguments
+ * and errors as qblk_adamw_step, plus w16: host array of n device pointers
+ * to 16-bit buffers of numel[i] elements (2-byte aligned; an entry may be
+ * NULL: no copy for that tensor), and w16_bf16: 0 fp16 copies, 1 bfloat16
+ * (match the block's gemm_precision 1 or 2). For the packed set of
+ * qblk_block_pack_f16 the pointers are packed + 2 * offset, offsets from
+ * qblk_block_pack_f16_offsets. */
 int32_t qblk_adamw_step_pack16(int32_t n, float* const* w, const float* const* g, float* const* m,
-                               float* const* v, const int64_t* numel, void* const* w16, float lr, float beta1,
-                               float beta2, float eps, float weight_decay, int32_t step,
+                               float* const* v, const int64_t* numel, void* const* w16, int32_t w16_bf16, float lr,
+                               float beta1, float beta2, float eps, float weight_decay, int32_t step,
                                const float* grad_scale_dev, qblk_stream_t stream);
 
 /* Element offsets (fp16 elements from the start of the packed set) of the

@@ -34,8 +34,11 @@ int32_t qblk_gemm_workspace_size(int32_t layout, int32_t precision, int32_t M, i
                                  size_t* scratch_bytes);
 
 /* qblk_gemm with the storage type of each operand given: a_dtype/b_dtype
- * 0 = fp32, 1 = fp16 (IEEE binary16). fp16 storage is how the block keeps
- * activations that only feed contractions. */
+ * 0 = fp32, 1 = fp16 (IEEE binary16), 2 = bfloat16. 16-bit storage is how
+ * the block keeps activations that only feed contractions. precision 2
+ * (bfloat16 operands, fp32 accumulate) takes bfloat16 storage of both
+ * operands, K a multiple of 64 and 16-byte aligned rows (the direct-to-LDS
+ * kernels), else QBLK_EUNSUPPORTED. */
 int32_t qblk_gemm_ex(int32_t layout, int32_t precision, int32_t M, int32_t N, int32_t K, const void* A,
                      int64_t lda, int32_t a_dtype, const void* B, int64_t ldb, int32_t b_dtype, float* C,
                      int64_t ldc, int32_t accumulate, void* scratch, size_t scratch_bytes,

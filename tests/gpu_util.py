@@ -5,6 +5,12 @@ import torch
 
 FP32_TOL = 2e-4   # max|err| / max|ref| for fp32 paths
 FP16_TOL = 2e-2   # for fp16-operand contraction paths
+# bfloat16-operand paths: the error of a rounded-operand contraction scales
+# with the operands' unit roundoff, 8x larger for bfloat16 (2^-8) than for
+# fp16 (2^-11); the fp16 paths measure <= 1.3e-3 against the oracle at the
+# full Qwen3-4B shape, so bfloat16 is expected near 1e-2, and 5e-2 bounds it
+# with margin.
+BF16_TOL = 5e-2
 
 
 def need_gpu():

@@ -68,3 +68,23 @@ def test_invalid_arguments_fail_before_device_work():
                                None) == qblk.QBLK_EINVAL
     cfg = qblk.make_config(synth.TINY_BLOCK)
     assert lib.qblk_block_forward(C.byref(cfg), None, None, None, None, 0, None, 0, None) == qblk.QBLK_EINVAL
+
+
+def test_bf16_config_needs_direct_to_lds_shapes():
+    """bfloat16 operands run only on the direct-to-LDS kernels: a token
+    count that is not a multiple of 64 is refused on the host (no device
+    work); the Qwen3-4B shape is accepted."""
+    c = synth.BlockShape(hidden=512, heads=8, kv_heads=2, head_dim=64, intermediate=1408, seq=100, batch=2,
+                         rope_theta=1e4, gemm_precision=2)
+    with pytest.raises(qblk.QblkError) as e:
+        qblk.block_workspace_size(qblk.make_config(c))
+    assert e.value.code == qblk.QBLK_EUNSUPPORTED
+    ok = synth.BlockShape(hidden=2560, heads=32, kv_heads=8, head_dim=128, intermediate=9728, seq=512, batch=1,
+                          rope_theta=1e6, gemm_precision=2)
+    saved, scratch = qblk.block_workspace_size(qblk.make_config(ok))
+    assert saved > 0 and scratch > 0
+    bad = qblk.make_config(ok)
+    bad.gemm_precision = 3
+    with pytest.raises(qblk.QblkError) as e:
+        qblk.block_workspace_size(bad)
+    assert e.value.code == qblk.QBLK_EINVAL

@@ -8,7 +8,7 @@ import torch
 import oracle
 from bwd_rmsnorm_qkv_amd import qblk, synth
 from bwd_rmsnorm_qkv_amd.runtime import Block, dev, empty
-from gpu_util import FP16_TOL, FP32_TOL, announce, check, need_gpu
+from gpu_util import BF16_TOL, FP16_TOL, FP32_TOL, announce, check, need_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,16 @@ CASES = {
     "small_fp16_no_qk_norm": synth.BlockShape(hidden=512, heads=8, kv_heads=2, head_dim=64, intermediate=1408,
                                               seq=96, batch=2, rope_theta=1e4, qk_norm=0, gemm_precision=1),
     "qwen3_4b": synth.QWEN3_4B_BLOCK,
+    # bfloat16 operands (gemm_precision 2)
+    "small_bf16_t192": synth.BlockShape(hidden=512, heads=8, kv_heads=2, head_dim=64, intermediate=1408,
+                                        seq=96, batch=2, rope_theta=1e4, gemm_precision=2),
+    "qwen3_4b_bf16": synth.BlockShape(hidden=2560, heads=32, kv_heads=8, head_dim=128, intermediate=9728,
+                                      seq=512, batch=1, rope_theta=1e6, gemm_precision=2),
 }
+
+
+def _tol(c):
+    return {0: FP32_TOL, 1: FP16_TOL, 2: BF16_TOL}[c.gemm_precision]
 
 
 def _gammas_perturbed(p, seed):
@@ -53,7 +62,7 @@ def _gammas_perturbed(p, seed):
 def test_block_forward_backward(name, unit_gammas):
     need_gpu()
     c = CASES[name]
-    if name == "qwen3_4b" and not unit_gammas:
+    if name.startswith("qwen3_4b") and not unit_gammas:
         pytest.skip("one gamma variant at full Qwen3-4B size")
     announce(f"block {name} T={c.tokens} unit_gammas={unit_gammas}")
     inp = synth.block_inputs(c)
@@ -61,7 +70,7 @@ def test_block_forward_backward(name, unit_gammas):
     P = {k: dev(v) for k, v in params.items()}
     X, DY = dev(inp["x"]), dev(inp["dy"])
     blk = Block(c)
-    if name == "qwen3_4b":
+    if name.startswith("qwen3_4b"):
         P = blk.pack_f16(P)  # weights cast once, as the benchmark runs it
     y = blk.forward(P, X)
     grads = {k: empty(v.shape) for k, v in params.items()}
@@ -69,7 +78,7 @@ def test_block_forward_backward(name, unit_gammas):
     torch.cuda.synchronize()
     y_ref, cache = oracle.block_forward(c, params, inp["x"])
     dx_ref, g_ref = oracle.block_backward(c, params, cache, inp["dy"])
-    tol = FP16_TOL if c.gemm_precision else FP32_TOL
+    tol = _tol(c)
     rep = {}
     check("y", y, y_ref, tol, rep)
     check("dx", dx, dx_ref, tol, rep)
@@ -78,7 +87,7 @@ def test_block_forward_backward(name, unit_gammas):
     announce("  " + " ".join(f"{k}={v:.1e}" for k, v in rep.items()))
 
 
-@pytest.mark.parametrize("name", ["small_fp16_t192", "small_fp16_t200"])
+@pytest.mark.parametrize("name", ["small_fp16_t192", "small_fp16_t200", "small_bf16_t192"])
 def test_block_packed_weights_match(name):
     """Caller-packed fp16 weights and the per-call cast into scratch are the
     same numbers, so the results are bitwise equal."""
@@ -123,7 +132,7 @@ def test_block_backward_deterministic():
 
 
 @pytest.mark.parametrize("name", ["small", "small_fp16_t192", "fp16_wide_split", "small_d32_ragged",
-                                  "small_fp16_no_qk_norm"])
+                                  "small_fp16_no_qk_norm", "small_bf16_t192"])
 def test_block_backward_accumulate(name):
     """Two micro-batches through qblk_block_backward_accumulate: every
     parameter gradient matches the sum of the oracle's gradients of the two
@@ -138,7 +147,7 @@ def test_block_backward_accumulate(name):
     params = _gammas_perturbed(inp1["params"], 5)
     P = {k: dev(v) for k, v in params.items()}
     blk = Block(c)
-    if c.gemm_precision == 1:
+    if c.gemm_precision:
         P = blk.pack_f16(P)
     mb = [(dev(i["x"]), dev(i["dy"])) for i in (inp1, inp2)]
     single = []
@@ -160,7 +169,7 @@ def test_block_backward_accumulate(name):
         _, cache = oracle.block_forward(c, params, i["x"])
         dx_ref, g = oracle.block_backward(c, params, cache, i["dy"])
         ref = g if ref is None else {k: ref[k] + g[k] for k in ref}
-    tol = FP16_TOL if c.gemm_precision else FP32_TOL
+    tol = _tol(c)
     rep = {}
     check("dx", dx, dx_ref, tol, rep)
     for k in qblk.PARAMS:

@@ -8,7 +8,7 @@ import oracle
 from oracle import ops
 from bwd_rmsnorm_qkv_amd import qblk
 from bwd_rmsnorm_qkv_amd.runtime import dev, empty, byte_buffer
-from gpu_util import FP16_TOL, FP32_TOL, announce, check, need_gpu
+from gpu_util import BF16_TOL, FP16_TOL, FP32_TOL, announce, check, need_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -350,3 +350,48 @@ def test_qk_norm_rope(case):
     check("dq", out[:, :H * d], dq, FP32_TOL)
     check("dk", out[:, H * d:(H + KV) * d], dk, FP32_TOL)
     assert np.all(out[:, (H + KV) * d:] == 5.0), "v columns must be left alone"
+
+
+# bfloat16 operands (precision 2): shapes the direct-to-LDS kernels take
+# (K a multiple of 64), small and big tiles, split K, ragged M and N
+GEMM_BF16_SHAPES = [(200, 136, 128), (300, 392, 256), (64, 96, 4096), (512, 2560, 4096), (512, 19456, 2560),
+                    (2560, 9728, 512)]
+
+
+@pytest.mark.parametrize("layout", [0, 1, 2])
+@pytest.mark.parametrize("shape", GEMM_BF16_SHAPES)
+def test_gemm_bf16(layout, shape):
+    """The operands are rounded to bfloat16 on the host (torch, nearest
+    even) and handed over as bfloat16 storage: the reference is the exact
+    fp64 product of those same values, so the only difference is the fp32
+    accumulation order (the fp32 tolerance applies). The fp32 originals
+    against the same product stay within the bfloat16 tolerance."""
+    need_gpu()
+    M, N, K = shape
+    if layout == 2 and M % 8:
+        pytest.skip("TN needs M % 8 == 0")
+    announce(f"gemm bf16 layout={layout} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + 3 * N + 7 * K + layout)
+    a_shape = (M, K) if layout in (0, 1) else (K, M)
+    b_shape = (N, K) if layout == 0 else (K, N)
+    A32 = torch.from_numpy(rng.standard_normal(a_shape).astype(np.float32))
+    B32 = torch.from_numpy(rng.standard_normal(b_shape).astype(np.float32))
+    A16, B16 = A32.to(torch.bfloat16), B32.to(torch.bfloat16)
+    Ar, Br = A16.double().numpy(), B16.double().numpy()
+    ref = (Ar if layout != 2 else Ar.T) @ (Br.T if layout == 0 else Br)
+    ref32 = (A32.double().numpy() if layout != 2 else A32.double().numpy().T) @ \
+            (B32.double().numpy().T if layout == 0 else B32.double().numpy())
+    C = torch.full((M, N), 3.0, device="cuda")
+    ws = qblk.gemm_workspace_size(layout, 2, M, N, K)
+    scratch = byte_buffer(ws) if ws else None
+    qblk.gemm(layout, 2, M, N, K, A16.cuda(), a_shape[1], B16.cuda(), b_shape[1], C, N, scratch=scratch)
+    torch.cuda.synchronize()
+    check("C (same bfloat16 inputs)", C, ref, FP32_TOL)
+    check("C (fp32 originals)", C, ref32, BF16_TOL)
+
+
+def test_gemm_bf16_needs_bf16_storage():
+    need_gpu()
+    A = torch.zeros((64, 64), device="cuda")
+    with pytest.raises(qblk.QblkError):
+        qblk.gemm(0, 2, 64, 64, 64, A, 64, A, 64, torch.empty((64, 64), device="cuda"), 64)
