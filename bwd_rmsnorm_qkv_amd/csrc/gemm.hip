@@ -1789,10 +1789,20 @@ constexpr int kTargetWgs = 256;  // one 4-wave workgroup per CU (LDS-limited)
 constexpr int kMinKtPerSplit = 8;
 constexpr int kMaxSplits = 32;
 
-// Register-staged kernel tile: 128 x 128 (2 x 2 waves of 2 x 2 blocks of
-// 32 x 32, two waves per SIMD), the K tile 64 fp16 / 32 fp32 elements.
-// Other tile shapes measured slower on every product of the block.
-constexpr int kRegBM = 128, kRegBN = 128;
+// Register-staged kernel tiles: 128 x 128 (2 x 2 waves of 2 x 2 blocks of
+// 32 x 32) or 64 x 64 (2 x 2 waves of one 32 x 32 block each), the K tile
+// 64 fp16 / 32 fp32 elements. Products with short K (<= 1408) whose
+// 128-wide tiles number fewer than 256 take the 64-wide ones: 4x the
+// tiles fill the CUs without splitting K as far, which measured faster on
+// every such product of the 36-layer stack's block (fp32: e.g. 1024 x 512
+// x 512 in 15 instead of 29 us); long-K products keep the 128-wide tiles,
+// whose operand reuse wins there (1024 x 512 x 2816: 50 against 70 us).
+constexpr int kRegSmallK = 1408;
+constexpr int kRegTargetBig = 512, kRegTargetSmall = 512;
+
+bool reg_small_tiles(const GemmDesc& d) {
+  return d.K <= kRegSmallK && ceil_div(d.M, 128) * ceil_div(d.N, 128) < 256;
+}
 
 // target_wgs > 0: split K so that tiles x splits reaches it (rounding up);
 // target_wgs < 0: so that it stays within -target_wgs (rounding down, one
@@ -1941,7 +1951,8 @@ Grid plan(const GemmDesc& d, size_t ws_bytes) {
     return g;
   }
   const int bk = d.prec == Prec::F16 ? PT<Prec::F16>::BK : PT<Prec::F32>::BK;
-  return plan_tiles(d, ws_bytes, kRegBM, kRegBN, bk);
+  if (reg_small_tiles(d)) return plan_tiles(d, ws_bytes, 64, 64, bk, kRegTargetSmall);
+  return plan_tiles(d, ws_bytes, 128, 128, bk, kRegTargetBig);
 }
 
 // The fused NF4 kernel applies to fp16 A (K-major, 16-byte aligned rows),
@@ -2039,7 +2050,10 @@ template <Prec P, Layout L, Src AS, Src BS, bool EXT>
 int launch(const GemmDesc& d, hipStream_t st) {
   const Grid g = plan(d, d.ws ? d.ws_bytes : 0);
   const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
-  hipLaunchKernelGGL((gemm_kernel<P, L, AS, BS, EXT, 2, 2, 2, 2, PT<P>::BK>), dim3(nwg), dim3(256), 0, st, d, g);
+  if (reg_small_tiles(d))
+    hipLaunchKernelGGL((gemm_kernel<P, L, AS, BS, EXT, 2, 2, 1, 1, PT<P>::BK>), dim3(nwg), dim3(256), 0, st, d, g);
+  else
+    hipLaunchKernelGGL((gemm_kernel<P, L, AS, BS, EXT, 2, 2, 2, 2, PT<P>::BK>), dim3(nwg), dim3(256), 0, st, d, g);
   QBLK_TRY(check_launch("gemm_kernel"));
   return finish_splits(d, g, st);
 }
