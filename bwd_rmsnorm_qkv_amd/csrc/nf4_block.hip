@@ -44,9 +44,10 @@ struct Nf4Scratch {
   Scratch base;
   float *dh_qkv, *dh_o, *dh_gu, *dh_d;  // s dY B ([T, n r]; fp16 path: [T, 64])
   f16* dh16;                            // fp16 path: fp16 copy of the current group's dh [T, 64]
-  f16* a16x;                            // fp16 path: [A_0; A_1; A_2; 0] [64, in]
-  f16* bx16;                            // fp16 path: block-diagonal B [out, 64]
-  f16* bt16;                            // fp16 path: block-diagonal B^T [64, out]
+  // fp16 path, per projection group (q|k|v, o, gate|up, down), packed once
+  // per call: [A_0; A_1; A_2; 0] [64, in], block-diagonal B [out, 64] and
+  // its transpose [64, out]
+  f16 *a16x[4], *bx16[4], *bt16[4];
   float *sink_h, *sink_d;               // gamma gradients are not outputs
   f16* w16;                             // fp16 W~ of the current group (dense fallback)
 };
@@ -70,7 +71,8 @@ size_t carve_nf4(const qblk_config& c, int r, void* saved, void* scratch, Nf4Sav
   s->h_gu = take(saved, sb, T * hw);
   s->h_d = take(saved, sb, T * hw);
   s->hs16_qkv = s->hs16_o = s->hs16_gu = s->hs16_d = nullptr;
-  w->dh16 = w->a16x = w->bx16 = w->bt16 = w->w16 = nullptr;
+  w->dh16 = w->w16 = nullptr;
+  for (int g = 0; g < 4; ++g) w->a16x[g] = w->bx16[g] = w->bt16[g] = nullptr;
   if (f16p) {
     s->hs16_qkv = (f16*)take(saved, sb, T * 32);
     s->hs16_o = (f16*)take(saved, sb, T * 32);
@@ -87,11 +89,13 @@ size_t carve_nf4(const qblk_config& c, int r, void* saved, void* scratch, Nf4Sav
     const size_t h = c.hidden, qd = (size_t)c.heads * c.head_dim, kvd = (size_t)c.kv_heads * c.head_dim;
     const size_t I = c.intermediate, qkv = qd + 2 * kvd;
     const size_t wmax = std::max({qkv * h, h * qd, 2 * I * h, h * I});
-    const size_t omax = std::max({qkv, h, 2 * I}), imax = std::max({h, qd, I});
+    const size_t ins[4] = {h, qd, h, I}, outs[4] = {qkv, h, 2 * I, h};
     w->dh16 = (f16*)take(scratch, wb, T * 32);
-    w->a16x = (f16*)take(scratch, wb, 32 * imax);
-    w->bx16 = (f16*)take(scratch, wb, 32 * omax);
-    w->bt16 = (f16*)take(scratch, wb, 32 * omax);
+    for (int g = 0; g < 4; ++g) {
+      w->a16x[g] = (f16*)take(scratch, wb, 32 * ins[g]);
+      w->bx16[g] = (f16*)take(scratch, wb, 32 * outs[g]);
+      w->bt16[g] = (f16*)take(scratch, wb, 32 * outs[g]);
+    }
     w->w16 = (f16*)take(scratch, wb, wmax / 2 + 64);
   }
   *scratch_bytes = wb;
@@ -287,26 +291,39 @@ struct LoraPack {
   int n, r, in, out, mode;
 };
 
-__global__ __launch_bounds__(256) void lora_pack16_kernel(const LoraPack a, f16* __restrict__ dst) {
-  const int64_t e = blockIdx.x * (int64_t)256 + threadIdx.x;
-  const int64_t total = a.mode == 0 ? 64 * (int64_t)a.in : 64 * (int64_t)a.out;
-  if (e >= total) return;
+// Several packs in one launch: job j fills dst[j], elements [end[j-1], end[j])
+// of the launch's index space.
+constexpr int kMaxPackJobs = 8;
+struct LoraPackJobs {
+  LoraPack job[kMaxPackJobs];
+  f16* dst[kMaxPackJobs];
+  int64_t end[kMaxPackJobs];
+  int count;
+};
+
+__global__ __launch_bounds__(256) void lora_pack16_kernel(const LoraPackJobs J) {
+  // every index fits 32 bits (64 x the widest projection side per job)
+  const int ge = blockIdx.x * 256 + threadIdx.x;
+  if (ge >= (int)J.end[J.count - 1]) return;
+  int j = 0;
+  while (j + 1 < J.count && ge >= (int)J.end[j]) ++j;
+  const LoraPack& a = J.job[j];
+  const int e = ge - (j ? (int)J.end[j - 1] : 0);
   float v = 0.f;
   if (a.mode == 0) {
-    const int row = (int)(e / a.in), col = (int)(e % a.in);
+    const int row = e / a.in, col = e - row * a.in;
     if (row < a.n * a.r) v = a.m[row / a.r][(int64_t)(row % a.r) * a.in + col];
   } else {
-    const int o = a.mode == 1 ? (int)(e / 64) : (int)(e % a.out);
-    const int c = a.mode == 1 ? (int)(e % 64) : (int)(e / a.out);
+    const int o = a.mode == 1 ? e >> 6 : e % a.out;
+    const int c = a.mode == 1 ? e & 63 : e / a.out;
     int k = 0;
     while (k + 1 < a.n && o >= a.start[k + 1]) ++k;
     if (c >= k * a.r && c < (k + 1) * a.r) v = a.m[k][(int64_t)(o - a.start[k]) * a.r + (c - k * a.r)];
   }
-  dst[e] = (f16)v;
+  J.dst[j][e] = (f16)v;
 }
 
-int lora_pack16(const qblk_nf4_block_params& p, const int* id3, const int* outd, int n, int in, int mode,
-                f16* dst, hipStream_t st) {
+LoraPack lora_pack_job(const qblk_nf4_block_params& p, const int* id3, const int* outd, int n, int in, int mode) {
   LoraPack a{};
   a.n = n; a.r = p.rank; a.in = in; a.mode = mode;
   int o = 0;
@@ -317,9 +334,7 @@ int lora_pack16(const qblk_nf4_block_params& p, const int* id3, const int* outd,
   }
   a.start[n] = o;
   a.out = o;
-  const int64_t total = mode == 0 ? 64 * (int64_t)in : 64 * (int64_t)o;
-  hipLaunchKernelGGL(lora_pack16_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, st, a, dst);
-  return check_launch("lora_pack16_kernel");
+  return a;
 }
 
 struct Group {
@@ -332,23 +347,43 @@ struct Group {
   }
 };
 
+// The 4 groups' packs of the given two modes into their buffers, one launch.
+int lora_pack16_groups(const qblk_nf4_block_params& p, const Group* gs, const int* ins, int mode_a, f16* const* dst_a,
+                       int mode_b, f16* const* dst_b, hipStream_t st) {
+  LoraPackJobs J{};
+  int64_t acc = 0;
+  for (int gi = 0; gi < 4; ++gi)
+    for (int t = 0; t < 2; ++t) {
+      const int mode = t ? mode_b : mode_a;
+      const LoraPack a = lora_pack_job(p, gs[gi].id3, gs[gi].outd, gs[gi].n, ins[gi], mode);
+      J.job[J.count] = a;
+      J.dst[J.count] = (t ? dst_b : dst_a)[gi];
+      acc += mode == 0 ? 64 * (int64_t)a.in : 64 * (int64_t)a.out;
+      J.end[J.count] = acc;
+      ++J.count;
+    }
+  if (acc >= (int64_t)1 << 31) return fail(QBLK_EUNSUPPORTED, "nf4 block: LoRA operands too large to pack");
+  hipLaunchKernelGGL(lora_pack16_kernel, dim3((unsigned)ceil_div(acc, 256)), dim3(256), 0, st, J);
+  return check_launch("lora_pack16_kernel");
+}
+
 // Forward of one group on the fp16 path:
 //   hs = s x16 [A stacked]^T over 64 columns (fp32 `hs`, fp16 `hs16`);
 //   out (+ res) = x16 W~^T + hs16 bx16^T, fused (NF4 decoded in the GEMM).
-int nf4_fwd16(const qblk_nf4_block_params& p, const Nf4Scratch& w, int T, int in, const f16* x16,
+int nf4_fwd16(const qblk_nf4_block_params& p, const Nf4Scratch& w, int gi, int T, int in, const f16* x16,
               const Group& g, float* hs, f16* hs16, const float* res, float* out, hipStream_t st) {
   const float sc = p.alpha / (float)p.rank;
-  QBLK_TRY(lora_pack16(p, g.id3, g.outd, g.n, in, 0, w.a16x, st));
+  const f16* a16x = w.a16x[gi];
+  const f16* bx16 = w.bx16[gi];
   {
     GemmDesc d = base(Layout::NT, T, 64, in);
     d.a = x16; d.lda = in; d.a_src = Src::F16;
-    d.b = seg1(w.a16x, 64); d.ldb = in; d.b_src = Src::F16;
+    d.b = seg1(a16x, 64); d.ldb = in; d.b_src = Src::F16;
     d.c = seg1(hs, T); d.ldc = 64;
     d.alpha = sc;
     d.c16 = hs16; d.ldc16 = 64;
     QBLK_TRY(gemm(d, st));
   }
-  QBLK_TRY(lora_pack16(p, g.id3, g.outd, g.n, in, 1, w.bx16, st));
   GemmDesc d = base(Layout::NT, T, g.N, in);
   d.a = x16; d.lda = in; d.a_src = Src::F16;
   d.b = rows3(g.outd[0], g.outd[1], g.outd[2]); d.ldb = in;
@@ -357,7 +392,7 @@ int nf4_fwd16(const qblk_nf4_block_params& p, const Nf4Scratch& w, int T, int in
   d.c = seg1(out, T); d.ldc = g.N;
   d.r = res; d.ldr = g.N;
   d.ext16_a = hs16; d.ext16_lda = 64;
-  d.ext16_b = w.bx16; d.ext16_ldb = 64;
+  d.ext16_b = bx16; d.ext16_ldb = 64;
   if (gemm_nf4_fused(d)) return gemm(d, st);
   // dense fallback: decoded copy, then the LoRA tile as an accumulating product
   QBLK_TRY(dequant_group(p, g.id3, g.outd, g.n, in, w.w16, st));
@@ -369,7 +404,7 @@ int nf4_fwd16(const qblk_nf4_block_params& p, const Nf4Scratch& w, int T, int in
   QBLK_TRY(gemm(e, st));
   GemmDesc u = base(Layout::NT, T, g.N, 64);
   u.a = hs16; u.lda = 64; u.a_src = Src::F16;
-  u.b = seg1(w.bx16, g.N); u.ldb = 64; u.b_src = Src::F16;
+  u.b = seg1(bx16, g.N); u.ldb = 64; u.b_src = Src::F16;
   u.c = seg1(out, T); u.ldc = g.N;
   u.accumulate = 1;
   return gemm(u, st);
@@ -380,22 +415,22 @@ int nf4_fwd16(const qblk_nf4_block_params& p, const Nf4Scratch& w, int T, int in
 //   dh = s dY16 B (over 64 columns; fp32 dh and its fp16 copy);
 //   dX = dY16 W~ + dh16 [A stacked], fused (fp16 copy into dx16 if set);
 //   dB_k = dY16_k^T hs16_k (diagonal blocks); dA_k = dh16_k^T X16.
-int nf4_bwd16(const qblk_nf4_block_params& p, const qblk_lora_grads& gr, const Nf4Scratch& w, int T, int in,
-              const f16* dy16, const f16* x16, const f16* hs16, const Group& g, float* dh, float* dx, f16* dx16,
-              hipStream_t st) {
+int nf4_bwd16(const qblk_nf4_block_params& p, const qblk_lora_grads& gr, const Nf4Scratch& w, int gi, int T,
+              int in, const f16* dy16, const f16* x16, const f16* hs16, const Group& g, float* dh, float* dx,
+              f16* dx16, hipStream_t st) {
   const float sc = p.alpha / (float)p.rank;
   const int r = p.rank, n = g.n;
-  QBLK_TRY(lora_pack16(p, g.id3, g.outd, n, in, 2, w.bt16, st));
+  const f16* a16x = w.a16x[gi];
+  const f16* bt16 = w.bt16[gi];
   {
     GemmDesc d = base(Layout::NT, T, 64, g.N);
     d.a = dy16; d.lda = g.N; d.a_src = Src::F16;
-    d.b = seg1(w.bt16, 64); d.ldb = g.N; d.b_src = Src::F16;
+    d.b = seg1(bt16, 64); d.ldb = g.N; d.b_src = Src::F16;
     d.c = seg1(dh, T); d.ldc = 64;
     d.alpha = sc;
     d.c16 = w.dh16; d.ldc16 = 64;
     QBLK_TRY(gemm(d, st));
   }
-  QBLK_TRY(lora_pack16(p, g.id3, g.outd, n, in, 0, w.a16x, st));
   {
     GemmDesc d = base(Layout::NN, T, in, g.N);
     d.a = dy16; d.lda = g.N; d.a_src = Src::F16;
@@ -405,7 +440,7 @@ int nf4_bwd16(const qblk_nf4_block_params& p, const qblk_lora_grads& gr, const N
     d.c = seg1(dx, T); d.ldc = in;
     d.c16 = dx16; d.ldc16 = in;
     d.ext16_a = w.dh16; d.ext16_lda = 64;
-    d.ext16_b = w.a16x; d.ext16_ldb = in;
+    d.ext16_b = a16x; d.ext16_ldb = in;
     if (gemm_nf4_fused(d)) {
       QBLK_TRY(gemm(d, st));
     } else {
@@ -417,7 +452,7 @@ int nf4_bwd16(const qblk_nf4_block_params& p, const qblk_lora_grads& gr, const N
       QBLK_TRY(gemm(e, st));
       GemmDesc u = base(Layout::NN, T, in, 64);
       u.a = w.dh16; u.lda = 64; u.a_src = Src::F16;
-      u.b = seg1(w.a16x, 64); u.ldb = in; u.b_src = Src::F16;
+      u.b = seg1(a16x, 64); u.ldb = in; u.b_src = Src::F16;
       u.c = seg1(dx, T); u.ldc = in;
       u.c16 = dx16; u.ldc16 = in;
       u.accumulate = 1;
@@ -485,29 +520,38 @@ extern "C" int32_t qblk_block_forward_nf4_lora(const qblk_config* cfg, const qbl
   const bool f16p = w.w16 != nullptr;
   const Group gq({PQ, PK, PV}, {qd, kvd, kvd}), go({PO}, {h}), ggu({PG, PU}, {I, I}), gd({PD}, {h});
   proj.qkv = [&](const float* n1, float* qkv, hipStream_t s_) {
-    if (f16p) return nf4_fwd16(P, w, T, h, s.base.n1_16, gq, s.h_qkv, s.hs16_qkv, nullptr, qkv, s_);
+    if (f16p) return nf4_fwd16(P, w, 0, T, h, s.base.n1_16, gq, s.h_qkv, s.hs16_qkv, nullptr, qkv, s_);
     QBLK_TRY(lora_down(P, T, h, n1, {PQ, PK, PV}, s.h_qkv, s_));
     return nf4_fwd(P, T, h, n1, {PQ, PK, PV}, {qd, kvd, kvd}, s.h_qkv, nullptr, qkv, s_);
   };
   proj.o = [&](const float* o, const float* res, float* out, hipStream_t s_) {
-    if (f16p) return nf4_fwd16(P, w, T, qd, s.base.o16, go, s.h_o, s.hs16_o, res, out, s_);
+    if (f16p) return nf4_fwd16(P, w, 1, T, qd, s.base.o16, go, s.h_o, s.hs16_o, res, out, s_);
     QBLK_TRY(lora_down(P, T, qd, o, {PO}, s.h_o, s_));
     return nf4_fwd(P, T, qd, o, {PO}, {h}, s.h_o, res, out, s_);
   };
   proj.gate_up = [&](const float* n2, float* gu, hipStream_t s_) {
-    if (f16p) return nf4_fwd16(P, w, T, h, s.base.n2_16, ggu, s.h_gu, s.hs16_gu, nullptr, gu, s_);
+    if (f16p) return nf4_fwd16(P, w, 2, T, h, s.base.n2_16, ggu, s.h_gu, s.hs16_gu, nullptr, gu, s_);
     QBLK_TRY(lora_down(P, T, h, n2, {PG, PU}, s.h_gu, s_));
     return nf4_fwd(P, T, h, n2, {PG, PU}, {I, I}, s.h_gu, nullptr, gu, s_);
   };
   proj.down = [&](const float* sv, const float* res, float* out, hipStream_t s_) {
-    if (f16p) return nf4_fwd16(P, w, T, I, s.base.s16, gd, s.h_d, s.hs16_d, res, out, s_);
+    if (f16p) return nf4_fwd16(P, w, 3, T, I, s.base.s16, gd, s.h_d, s.hs16_d, res, out, s_);
     QBLK_TRY(lora_down(P, T, I, sv, {PD}, s.h_d, s_));
     return nf4_fwd(P, T, I, sv, {PD}, {h}, s.h_d, res, out, s_);
   };
   // on the fp16 path every product reads the fp16 copies of n1, n2 and s:
   // their fp32 forms are not written
   Saved sv = s.base;
-  if (f16p) sv.n1 = sv.n2 = sv.s = nullptr;
+  if (f16p) {
+    sv.n1 = sv.n2 = sv.s = nullptr;
+    const Group gs[4] = {gq, go, ggu, gd};
+    const int ins[4] = {h, qd, h, I};
+    const int rc = lora_pack16_groups(P, gs, ins, 0, w.a16x, 1, w.bx16, st);
+    if (rc) {
+      t_ws = nullptr;
+      return rc;
+    }
+  }
   const int rc = block_forward_impl(c, proj, P.g_in, P.g_post, P.g_q, P.g_k, x, y, sv, st);
   t_ws = nullptr;
   return rc;
@@ -548,14 +592,14 @@ extern "C" int32_t qblk_block_backward_nf4_lora(const qblk_config* cfg, const qb
   proj.down = [&](const float* dyv, const float* sv, float* ds, hipStream_t s_) {
     if (f16p) {
       QBLK_TRY(as16(dyv, h, s_));
-      return nf4_bwd16(P, G, w, T, I, dy16, s.base.s16, s.hs16_d, gd, w.dh_d, ds, nullptr, s_);
+      return nf4_bwd16(P, G, w, 3, T, I, dy16, s.base.s16, s.hs16_d, gd, w.dh_d, ds, nullptr, s_);
     }
     return nf4_bwd(P, G, T, I, dyv, sv, s.h_d, {PD}, {h}, w.dh_d, ds, s_);
   };
   proj.gate_up = [&](const float* dgu, const float* n2, float* dn2, hipStream_t s_) {
     if (f16p) {
       QBLK_TRY(as16(dgu, 2 * I, s_));
-      return nf4_bwd16(P, G, w, T, h, dy16, s.base.n2_16, s.hs16_gu, ggu, w.dh_gu, dn2, nullptr, s_);
+      return nf4_bwd16(P, G, w, 2, T, h, dy16, s.base.n2_16, s.hs16_gu, ggu, w.dh_gu, dn2, nullptr, s_);
     }
     return nf4_bwd(P, G, T, h, dgu, n2, s.h_gu, {PG, PU}, {I, I}, w.dh_gu, dn2, s_);
   };
@@ -563,7 +607,7 @@ extern "C" int32_t qblk_block_backward_nf4_lora(const qblk_config* cfg, const qb
     // the attention backward reads dO's fp16 copy
     if (f16p) {
       QBLK_TRY(as16(dr1, h, s_));
-      return nf4_bwd16(P, G, w, T, qd, dy16, s.base.o16, s.hs16_o, go, w.dh_o, d_o,
+      return nf4_bwd16(P, G, w, 1, T, qd, dy16, s.base.o16, s.hs16_o, go, w.dh_o, d_o,
                        s.base.q16 ? w.base.do16 : nullptr, s_);
     }
     return nf4_bwd(P, G, T, qd, dr1, o, s.h_o, {PO}, {h}, w.dh_o, d_o, s_);
@@ -571,12 +615,21 @@ extern "C" int32_t qblk_block_backward_nf4_lora(const qblk_config* cfg, const qb
   proj.qkv = [&](const float* dqkv, const float* n1, float* dn1, hipStream_t s_) {
     if (f16p) {
       QBLK_TRY(as16(dqkv, qd + 2 * kvd, s_));
-      return nf4_bwd16(P, G, w, T, h, dy16, s.base.n1_16, s.hs16_qkv, gq, w.dh_qkv, dn1, nullptr, s_);
+      return nf4_bwd16(P, G, w, 0, T, h, dy16, s.base.n1_16, s.hs16_qkv, gq, w.dh_qkv, dn1, nullptr, s_);
     }
     return nf4_bwd(P, G, T, h, dqkv, n1, s.h_qkv, {PQ, PK, PV}, {qd, kvd, kvd}, w.dh_qkv, dn1, s_);
   };
   Scratch wb16 = w.base;
   wb16.prod16 = f16p;
+  if (f16p) {
+    const Group gs[4] = {gq, go, ggu, gd};
+    const int ins[4] = {h, qd, h, I};
+    const int rc = lora_pack16_groups(P, gs, ins, 2, w.bt16, 0, w.a16x, st);
+    if (rc) {
+      t_ws = nullptr;
+      return rc;
+    }
+  }
   const int rc = block_backward_impl(c, proj, P.g_in, P.g_post, P.g_q, P.g_k, x, dy, s.base, dx, w.sink_h,
                                      w.sink_h + h, w.sink_d, w.sink_d + c.head_dim, wb16, st);
   t_ws = nullptr;
