@@ -102,7 +102,11 @@ __global__ __launch_bounds__(256) void clip_finalize_kernel(int nparts, const do
   }
   if (tid == 0) {
     const double norm = sqrt(red[0]);
-    const double scale = norm > (double)max_norm ? (double)max_norm / norm : 1.0;
+    // a non-finite norm (some gradient is NaN or infinite) gives a NaN scale:
+    // AdamW then skips the step
+    const double scale = !isfinite(norm)          ? (double)NAN
+                         : norm > (double)max_norm ? (double)max_norm / norm
+                                                   : 1.0;
     norm_dev[0] = (float)norm;
     scale_dev[0] = (float)scale;
   }
@@ -159,6 +163,9 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk c, const Ada
   const int j = find_tensor(c.tile_end, c.count, tile);
   const int64_t base = (tile - (j ? c.tile_end[j - 1] : 0)) * kTile;
   const float sc = scale_dev ? scale_dev[0] : 1.f;
+  // the trainer's guard: a step with non-finite gradients (the clip's NaN
+  // scale) leaves weights, moments and 16-bit copies as they are
+  if (!isfinite(sc)) return;
   float *w = c.w[j], *m = c.m[j], *v = c.v[j];
   f16* const w16 = c.w16[j];
   const float* g = c.g[j];

@@ -183,7 +183,9 @@ int32_t qblk_clip_workspace_size(int32_t n, const int64_t* numel, size_t* scratc
 
 /* Global L2 gradient clip ([trainer] squared-sum clip and fused clip state):
  * norm = sqrt(sum over all n tensors of sum g^2) (fp64 final reduction);
- * scale = max_norm / norm if norm > max_norm, else 1. Writes norm_dev[0]
+ * scale = max_norm / norm if norm > max_norm, else 1; a non-finite norm
+ * (some gradient NaN or infinite) gives scale = NaN, which makes
+ * qblk_adamw_step skip the update. Writes norm_dev[0]
  * and scale_dev[0] (device fp32). With apply = 1 every gradient is
  * multiplied by scale in place; with apply = 0 they are left untouched
  * (pass scale_dev to qblk_adamw_step instead).
@@ -214,7 +216,11 @@ int32_t qblk_clip_grad_norm_noalloc(int32_t n, float* const* grads, const int64_
  *   m = beta1 m + (1-beta1) g';  v = beta2 v + (1-beta2) g'^2
  *   w = w - lr * (m/(1-beta1^step) / (sqrt(v/(1-beta2^step)) + eps) + weight_decay * w)
  * step >= 1. w, m, v updated in place; g is read only. Pointer arrays and
- * numel are host arrays of device pointers. */
+ * numel are host arrays of device pointers. When grad_scale_dev[0] is not
+ * finite (the clip's mark of non-finite gradients) nothing is written: the
+ * device-side form of the trainer's guard that skips the optimizer step on
+ * a non-finite loss or gradient ([trainer] train_step_inner NaN guard and
+ * the accumulated-gradient check before the optimizer). */
 int32_t qblk_adamw_step(int32_t n, float* const* w, const float* const* g, float* const* m,
                         float* const* v, const int64_t* numel, float lr, float beta1, float beta2,
                         float eps, float weight_decay, int32_t step, const float* grad_scale_dev,

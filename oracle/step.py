@@ -102,7 +102,8 @@ def stack_step(c, layers, x, g_final, w_lm, targets, max_norm, adamw, step=1):
     (all block tensors, the final-norm gamma and the LM head) before any
     AdamW, then AdamW on every tensor with zero initial moments.
     Returns a dict with the loss, per-token partials, the norm, the clip
-    scale, and the updated parameters and moments.
+    scale, the updated parameters and moments, and whether the guard
+    against non-finite values skipped the update.
     """
     eps = c["eps"] if isinstance(c, dict) else c.eps
     h = np.asarray(x, np.float64)
@@ -124,13 +125,21 @@ def stack_step(c, layers, x, g_final, w_lm, targets, max_norm, adamw, step=1):
     for p in layers:
         params += [p[n] for n in PARAM_NAMES]
     params += [g_final, w_lm]
+    # The trainer's guard (same page, train_step_inner): a non-finite loss
+    # ends the step before the optimizer, and its accumulated-gradient path
+    # skips the optimizer when any gradient is NaN or infinite; either way
+    # the parameters and moments stay as they were.
+    skipped = not (np.isfinite(ce["loss"]) and all(np.all(np.isfinite(g)) for g in flat))
     new_w, new_m, new_v = [], [], []
     for w, g in zip(params, clipped):
         z = np.zeros(np.shape(w))
-        w2, m2, v2 = adamw_update(w, g, z, z, step=step, **adamw)
+        if skipped:
+            w2, m2, v2 = np.array(w, np.float64), z, z
+        else:
+            w2, m2, v2 = adamw_update(w, g, z, z, step=step, **adamw)
         new_w.append(w2)
         new_m.append(m2)
         new_v.append(v2)
     return dict(loss=ce["loss"], loss_partials=ce["loss_partials"], argmax=ce["argmax"],
                 norm=norm, scale=scale, grads=flat, new_w=new_w, new_m=new_m, new_v=new_v,
-                dx=dh)
+                dx=dh, skipped=skipped)

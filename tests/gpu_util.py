@@ -1,4 +1,6 @@
 """Shared helpers of the GPU parity tests."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -32,10 +34,17 @@ def rel_err(gpu, ref):
     return float(np.max(np.abs(g - r)) / denom)
 
 
+# Every comparison made through check(): (test id, tensor name, error, tolerance).
+# The test session prints the worst ratio per test at its end (conftest.py).
+PARITY_LOG = []
+
+
 def check(name, gpu, ref, tol, report=None):
     e = rel_err(gpu, ref)
     if report is not None:
         report[name] = e
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    PARITY_LOG.append((test, name, e, tol))
     assert e <= tol, f"{name}: max|err|/max|ref| = {e:.3e} > {tol:.1e}"
     return e
 

@@ -679,6 +679,42 @@ def test_stack_step_matches_torch():
                                    err_msg=str(i))
 
 
+def test_stack_step_non_finite_input_skips_the_update():
+    """A NaN in the last token of the first sequence reaches that token's
+    cross-entropy partial (NaN in the oracle and in torch float64; the
+    sequence's earlier tokens may turn NaN too, as 0 * NaN in a dense masked
+    product, so they are not constrained), while the second sequence never
+    mixes with the first: its partials equal the finite input's and torch's.
+    The oracle's loss is NaN and, per the trainer's guard (cuda_trainer.rs
+    page, train_step_inner), no parameter or moment moves; the finite step
+    is not skipped."""
+    c, inp = _tiny_stack()
+    ref_ok = oracle.stack_step(c, inp["layers"], inp["x"], inp["g_final"], inp["w_lm"], inp["targets"],
+                               1.0, synth.ADAMW)
+    assert not ref_ok["skipped"]
+    x = inp["x"].copy()
+    x[c.seq - 1, 3] = np.nan
+    ref = oracle.stack_step(c, inp["layers"], x, inp["g_final"], inp["w_lm"], inp["targets"], 1.0, synth.ADAMW)
+    tl = [{n: torch.tensor(p[n], dtype=torch.float64) for n in PARAM_NAMES} for p in inp["layers"]]
+    h = torch.tensor(x, dtype=torch.float64)
+    with torch.no_grad():
+        for tp in tl:
+            h = _torch_block(c, tp, h)
+        z = F.linear(F.rms_norm(h, (c.hidden,), torch.tensor(inp["g_final"], dtype=torch.float64), eps=c.eps),
+                     torch.tensor(inp["w_lm"], dtype=torch.float64))
+        tpart = F.cross_entropy(z, torch.tensor(inp["targets"], dtype=torch.int64), reduction="none").numpy()
+    last, second = c.seq - 1, slice(c.seq, 2 * c.seq)
+    assert np.isnan(tpart[last]) and np.isnan(ref["loss_partials"][last])
+    assert np.isfinite(ref["loss_partials"][second]).all()
+    np.testing.assert_allclose(ref["loss_partials"][second], tpart[second], rtol=1e-12)
+    np.testing.assert_allclose(ref["loss_partials"][second], ref_ok["loss_partials"][second], rtol=1e-12)
+    assert np.isnan(ref["loss"]) and ref["skipped"]
+    params = [p[n] for p in inp["layers"] for n in PARAM_NAMES] + [inp["g_final"], inp["w_lm"]]
+    for w, w2, m2, v2 in zip(params, ref["new_w"], ref["new_m"], ref["new_v"]):
+        assert np.array_equal(w2, np.asarray(w, np.float64))
+        assert not np.any(m2) and not np.any(v2)
+
+
 def test_stack_step_finite_differences():
     """Central differences of the stack's mean cross-entropy (forward only:
     the blocks, final norm, LM head and log-sum-exp) along a random direction
