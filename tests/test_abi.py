@@ -88,3 +88,24 @@ def test_bf16_config_needs_direct_to_lds_shapes():
     with pytest.raises(qblk.QblkError) as e:
         qblk.block_workspace_size(bad)
     assert e.value.code == qblk.QBLK_EINVAL
+
+
+def test_size_limits_are_refused_on_the_host():
+    """The limits of the row kernels and of the LoRA tile, refused before
+    any device work: hidden above 4096 (one RMSNorm row per wave's
+    registers) is unsupported; LoRA ranks must be multiples of 4 up to 20
+    (three ranks of a projection group in one 64-wide tile); 4096 and 20
+    themselves are accepted."""
+    import dataclasses
+    big = dataclasses.replace(synth.QWEN3_4B_BLOCK, hidden=4160)
+    with pytest.raises(qblk.QblkError) as e:
+        qblk.block_workspace_size(qblk.make_config(big))
+    assert e.value.code == qblk.QBLK_EUNSUPPORTED
+    assert b"4096" in qblk.lib().qblk_last_error()
+    edge = dataclasses.replace(synth.QWEN3_4B_BLOCK, hidden=4096)
+    assert min(qblk.block_workspace_size(qblk.make_config(edge))) > 0
+    for rank in (0, 24, 6):
+        with pytest.raises(qblk.QblkError) as e:
+            qblk.nf4_block_workspace_size(synth.NF4_LORA_QWEN3_4B, rank)
+        assert e.value.code == qblk.QBLK_EINVAL, rank
+    assert min(qblk.nf4_block_workspace_size(synth.NF4_LORA_QWEN3_4B, 20)) > 0
