@@ -16,6 +16,9 @@ Pages cited (docs.rs source pages of the Rust crate aprender-train, module
   (0.38.0): CPU/WGPU restatements of RMSNorm, cross-entropy, the FFN backward
   and the LoRA forward/backward.
 
+``fp8`` follows the OCP 8-bit floating point specification (the 8-bit
+operand variant; the pages name no 8-bit format).
+
 Inputs are float32 arrays widened exactly to float64; every step runs in
 float64 with numpy matmul as the only library primitive. Where the pages leave
 a step open, the reading taken is named in the function's docstring.
@@ -31,3 +34,4 @@ from .block import block_forward, block_backward, PARAM_NAMES
 from .step import (lm_head_cross_entropy, global_clip, adamw_update, stack_step)
 from .nf4 import (nf4_codebook, nf4_quantize, nf4_dequantize, lora_linear_fwd,
                   lora_linear_bwd, nf4_block_forward, nf4_block_backward)
+from . import fp8

@@ -774,3 +774,77 @@ def test_gradient_of_whole_batch_is_sum_over_micro_batches():
         acc = flat if acc is None else [a + b for a, b in zip(acc, flat)]
     for i, (a, b) in enumerate(zip(acc, whole["grads"])):
         np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-15, err_msg=str(i))
+
+
+# ------------------------------------------------------------------ fp8
+
+@pytest.mark.parametrize("fmt,tdt", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_fp8_rounding_matches_torch(fmt, tdt):
+    """oracle.fp8 rounding against torch's own float8 casts (an independent
+    implementation of the OCP formats, round to nearest even) on values
+    spread over every binade of the format, subnormals and exact ties
+    included; and every finite bit pattern decodes to torch's value and
+    encodes back to itself."""
+    from oracle import fp8
+    rng = np.random.default_rng(81)
+    fmax = fp8.FORMATS[fmt][3]
+    emin = 1 - fp8.FORMATS[fmt][2]
+    mag = np.exp2(rng.uniform(emin - fp8.FORMATS[fmt][1] - 2, np.log2(fmax), 20000))
+    v = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(np.float32).astype(np.float64)
+    v = np.clip(v, -fmax, fmax)
+    codes = np.arange(256, dtype=np.uint8)
+    tvals = torch.from_numpy(codes).view(tdt).float().double().numpy()
+    finite = np.isfinite(tvals)
+    # midpoints between neighbouring representable values: exact ties
+    reps = np.unique(tvals[finite])
+    mids = (reps[:-1] + reps[1:]) / 2
+    v = np.concatenate([v, mids, reps])
+    ours = fp8.round_to_format(v, fmt)
+    theirs = torch.from_numpy(v).to(tdt).double().numpy()
+    assert np.array_equal(ours, theirs)
+    dec = fp8.decode(codes, fmt)
+    assert np.array_equal(np.isnan(dec), np.isnan(tvals))
+    assert np.array_equal(dec[finite], tvals[finite])
+    back = fp8.encode(dec[finite], fmt)
+    # -0 and +0 keep their patterns
+    assert np.array_equal(back, codes[finite])
+    assert fp8.round_to_format(np.array([fmax]), fmt)[0] == fmax
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_quantize_and_product_bounds(fmt):
+    """Per-tensor quantization: the largest magnitude lands on the format's
+    largest finite value, zeros stay zero with scale 1; the scaled-back
+    operand is within the format's relative step (2^-m, half of it for
+    round to nearest) of the original away from the subnormals, and the
+    product of two quantized operands within the closed-form bound
+    sum_k |a_k||b_k| (2 u + u^2) + the subnormal absolute terms of the
+    exact product."""
+    from oracle import fp8
+    _, m, bias, fmax = fp8.FORMATS[fmt]
+    u = 2.0 ** -(m + 1)
+    rng = np.random.default_rng(82)
+    a = rng.standard_normal((40, 256)).astype(np.float32)
+    b = (0.02 * rng.standard_normal((24, 256))).astype(np.float32)
+    qa, ia = fp8.quantize(a, fmt)
+    qb, ib = fp8.quantize(b, fmt)
+    da, db = fp8.decode(qa, fmt), fp8.decode(qb, fmt)
+    assert np.max(np.abs(da)) == fmax and np.max(np.abs(db)) == fmax
+    sa = np.float32(fmax) / np.float32(np.max(np.abs(a)))
+    norm_a = np.abs(a.astype(np.float64) * sa) >= 2.0 ** (1 - bias)
+    rel = np.abs(da * float(ia) - a) / np.abs(a)
+    assert np.all(rel[norm_a] <= u * (1 + 1e-6))
+    c = fp8.gemm_nt(qa, fmt, ia, qb, fmt, ib)
+    exact = a.astype(np.float64) @ b.astype(np.float64).T
+    sub_a = 2.0 ** (1 - bias - m) / 2 * float(ia)  # absolute error of a subnormal code, unscaled
+    sub_b = 2.0 ** (1 - bias - m) / 2 * float(ib)
+    bound = (np.abs(a) @ np.abs(b).T) * (2 * u + u * u) * 1.001 \
+        + sub_a * np.abs(b).sum(1)[None, :] * (1 + u) + sub_b * np.abs(a).sum(1)[:, None] * (1 + u) \
+        + 256 * sub_a * sub_b
+    assert np.all(np.abs(c - exact) <= bound)
+    z, iz = fp8.quantize(np.zeros((3, 16), np.float32), fmt)
+    assert not z.any() and iz == 1.0
+    # exact on integer operands the format holds: the product is the integer product
+    ai = rng.integers(-8, 9, (5, 32)).astype(np.float64)
+    bi = rng.integers(-8, 9, (7, 32)).astype(np.float64)
+    assert np.array_equal(fp8.gemm_nt(fp8.encode(ai, fmt), fmt, 1.0, fp8.encode(bi, fmt), fmt, 1.0), ai @ bi.T)
