@@ -19,9 +19,13 @@ namespace qblk {
 // accumulate. With BF16, 16-bit operand storage (Src::F16) holds bfloat16
 // bit patterns, and only the direct-to-LDS kernels run (16-bit storage of
 // both operands, K a multiple of 64).
-enum class Prec : int { F32 = 0, F16 = 1, BF16 = 2 };
+// FP8: 8-bit operands (OCP E4M3 or E5M2 per operand, see f8_a_e5m2 /
+// f8_b_e5m2) in 8-bit storage (Src::F8), NT only, K a multiple of 128,
+// on v_mfma_f32_32x32x64_f8f6f4; the product is multiplied by the device
+// scalars scale_a_dev[0] * scale_b_dev[0] (the operands' inverse scales).
+enum class Prec : int { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
 enum class Layout : int { NT = 0, NN = 1, TN = 2 };
-enum class Src : int { F32 = 0, F16 = 1, NF4 = 2 };
+enum class Src : int { F32 = 0, F16 = 1, NF4 = 2, F8 = 3 };
 
 // Up to three row segments stored at different addresses that together act
 // as one matrix: storage row r lives in segment s with start[s] <= r <
@@ -108,6 +112,11 @@ struct GemmDesc {
   int64_t ext16_lda = 0;
   const f16* ext16_b = nullptr;
   int64_t ext16_ldb = 0;
+  // FP8 only: operand formats (0 E4M3, 1 E5M2) and the device scalars
+  // the accumulated product is multiplied by (NULL: 1).
+  int32_t f8_a_e5m2 = 0, f8_b_e5m2 = 0;
+  const float* scale_a_dev = nullptr;
+  const float* scale_b_dev = nullptr;
 };
 
 int gemm(const GemmDesc& d, hipStream_t stream);

@@ -910,8 +910,33 @@ struct DmaOperand {
   }
 };
 
-template <int BM, int BN, int WM, int WN, int NS, int NB, bool AK, bool BK_, bool BF>
+// fp8 MFMA over 64 K: a and b are 32 bytes of 8-bit operands per lane.
+// FA / FB pick each operand's format (0 E4M3, 1 E5M2). The lane's 32 bytes
+// hold K values in the same arrangement for A and B, so the block product
+// is the dot product over those 64 K whatever order the unit takes them in.
+typedef int int8v __attribute__((ext_vector_type(8)));
+template <int FA, int FB>
+__device__ __forceinline__ floatx16 mfma8(half8 a0, half8 a1, half8 b0, half8 b1, floatx16 c) {
+  const int4 x0 = __builtin_bit_cast(int4, a0), x1 = __builtin_bit_cast(int4, a1);
+  const int4 y0 = __builtin_bit_cast(int4, b0), y1 = __builtin_bit_cast(int4, b1);
+  const int8v a = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  const int8v b = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+  // scale operands 0: the unscaled v_mfma_f32_32x32x64_f8f6f4
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
+}
+
+// EK: operand kind. 0 fp16, 1 bfloat16 (16-bit elements, K tiles of 64);
+// 2 + fa + 2 fb: fp8 with A format fa and B format fb (0 E4M3, 1 E5M2).
+// The fp8 kernels take the descriptor in 16-bit units (K, lda, ldb and
+// the split-K chunk halved: two fp8 values per unit), so staging, copies
+// and fragment reads are those of the 16-bit kernel; a K tile then holds
+// 128 fp8 values and feeds two fp8 MFMAs per 32 x 32 block, each taking
+// the fragments of two 16-bit K steps.
+template <int BM, int BN, int WM, int WN, int NS, int NB, bool AK, bool BK_, int EK>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d, const Grid gd) {
+  constexpr bool BF = EK == 1, F8 = EK >= 2;
+  constexpr int FA = F8 ? (EK - 2) & 1 : 0, FB = F8 ? (EK - 2) >> 1 : 0;
+  static_assert(!F8 || (AK && BK_), "fp8 operands: both K-major (NT)");
   constexpr int BK = 64;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
@@ -962,8 +987,48 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   // kb2 into db if cb) are interleaved with the MFMAs: copy c goes after
   // MFMA floor(c NM / NC), so its issue overlaps the MFMA before it instead
   // of holding up the whole tile.
+  auto compute8 = [&](const f16* sa, const f16* sb, bool ca, int ka, f16* da, bool cb, int kb2, f16* db)
+      __attribute__((always_inline)) {
+    // fp8: MFMA p (of 2) takes the fragments of 16-bit steps 2p and 2p + 1;
+    // the second pair's fragments are read before the first pair's MFMAs
+    half8 av[2][2][TM], bv[2][2][TN];
+    auto frag = [&](int s, half8* a, half8* b) __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < TM; ++t) a[t] = OA::frag(sa, wm * TM * 32 + t * 32, s, lane, ko[s]);
+#pragma unroll
+      for (int t = 0; t < TN; ++t) b[t] = OB::frag(sb, wn * TN * 32 + t * 32, s, lane, ko[s]);
+    };
+    constexpr int NM = 2 * TM * TN, NC = OA::J + OB::J;
+    frag(0, av[0][0], bv[0][0]);
+    frag(1, av[0][1], bv[0][1]);
+    static_for<0, 2>([&](auto Px) __attribute__((always_inline)) {
+      constexpr int p = decltype(Px)::value;
+      if constexpr (p == 0) {
+        frag(2, av[1][0], bv[1][0]);
+        frag(3, av[1][1], bv[1][1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, TM * TN>([&](auto Jx) __attribute__((always_inline)) {
+        constexpr int j = decltype(Jx)::value, tm = j / TN, tn = j % TN, i = p * TM * TN + j;
+        acc[tm][tn] = mfma8<FA, FB>(av[p][0][tm], av[p][1][tm], bv[p][0][tn], bv[p][1][tn], acc[tm][tn]);
+        static_for<(i * NC) / NM, ((i + 1) * NC) / NM>([&](auto Cx) __attribute__((always_inline)) {
+          constexpr int c = decltype(Cx)::value;
+          if constexpr (c < OA::J) {
+            if (ca) oa.issue_one(ka, da, d.lda, w, c);
+          } else {
+            if (cb) ob.issue_one(kb2, db, d.ldb, w, c - OA::J);
+          }
+        });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
   auto compute = [&](const f16* sa, const f16* sb, bool ca, int ka, f16* da, bool cb, int kb2, f16* db)
       __attribute__((always_inline)) {
+    if constexpr (F8) {
+      compute8(sa, sb, ca, ka, da, cb, kb2, db);
+      return;
+    }
     half8 av[2][TM], bv[2][TN];
     auto frag = [&](int s, half8* a, half8* b) __attribute__((always_inline)) {
 #pragma unroll
@@ -1058,6 +1123,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   if (left > 0) step(I0{}, nfull);
   if constexpr (NS > 2) if (left > 1) step(I1{}, nfull + 1);
   if constexpr (NS > 3) if (left > 2) step(I2{}, nfull + 2);
+  if constexpr (F8) {
+    // the operands' inverse scales (split-K partials carry them too)
+    const float sc = (d.scale_a_dev ? d.scale_a_dev[0] : 1.f) * (d.scale_b_dev ? d.scale_b_dev[0] : 1.f);
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[a][b][e] *= sc;
+  }
 
   // Epilogue through LDS: the wave parks one 32-row block (tm) of its tile
   // at a time in its own slice of the (now idle) stage buffers and reads it
@@ -1859,11 +1934,26 @@ struct DmaCfg {
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
     if (d.prec == Prec::BF16)
-      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, AK, BKM, true>), dim3(nwg), dim3(threads), 0, st,
-                         d, g);
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, AK, BKM, 1>), dim3(nwg), dim3(threads), 0, st, d,
+                         g);
     else
-      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, AK, BKM, false>), dim3(nwg), dim3(threads), 0, st,
-                         d, g);
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, AK, BKM, 0>), dim3(nwg), dim3(threads), 0, st, d,
+                         g);
+  }
+  // fp8 operands (NT), the descriptor in 16-bit units
+  template <int EK>
+  static void launch8(const GemmDesc& d, const Grid& g, hipStream_t st) {
+    const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, true, true, EK>), dim3(nwg), dim3(threads), 0, st, d,
+                       g);
+  }
+  static void launch8(const GemmDesc& d, const Grid& g, hipStream_t st) {
+    switch (d.f8_a_e5m2 + 2 * d.f8_b_e5m2) {
+      case 0: launch8<2>(d, g, st); break;
+      case 1: launch8<3>(d, g, st); break;
+      case 2: launch8<4>(d, g, st); break;
+      default: launch8<5>(d, g, st); break;
+    }
   }
   static void launch(const GemmDesc& d, const Grid& g, hipStream_t st) {
     switch (d.layout) {
@@ -2038,6 +2128,37 @@ int finish_splits(const GemmDesc& d, const Grid& g, hipStream_t st) {
   return 0;
 }
 
+// fp8 operands: NT, 8-bit storage of both, K a multiple of 128 (one
+// 128-byte K tile), lda and ldb multiples of 16 and 16-byte aligned rows,
+// a single B segment and no K extension.
+bool f8_ok(const GemmDesc& d) {
+  if (d.prec != Prec::FP8 || d.a_src != Src::F8 || d.b_src != Src::F8 || d.layout != Layout::NT) return false;
+  if (d.K % 128 != 0 || d.K == 0 || d.lda % 16 != 0 || d.ldb % 16 != 0 || d.b.nseg != 1) return false;
+  if ((uintptr_t)d.a % 16 != 0 || (uintptr_t)d.b.p[0] % 16 != 0 || d.ext.kext > 0) return false;
+  return (unsigned)d.f8_a_e5m2 <= 1 && (unsigned)d.f8_b_e5m2 <= 1;
+}
+
+// The fp8 product runs on the 128 x 128 direct-to-LDS kernel with the
+// descriptor in 16-bit units; planning (tiles, split-K) is that of a
+// 16-bit product of half the K.
+GemmDesc f8_units(const GemmDesc& d) {
+  GemmDesc u = d;
+  u.K = d.K / 2;
+  u.lda = d.lda / 2;
+  u.ldb = d.ldb / 2;
+  return u;
+}
+
+int launch_f8(const GemmDesc& d, hipStream_t st) {
+  const GemmDesc u = f8_units(d);
+  Grid g = plan_tiles(u, u.ws ? u.ws_bytes : 0, Nt16Small::bm, Nt16Small::bn, 64, -2 * kTargetWgs);
+  g.bn = Nt16Small::bn;
+  g.vec = out_vec4(u, g);
+  Nt16Small::launch8(u, g, st);
+  QBLK_TRY(check_launch("gemm_dma_kernel (fp8)"));
+  return finish_splits(u, g, st);
+}
+
 int launch_nt16(const GemmDesc& d, hipStream_t st) {
   const Grid g = plan(d, d.ws ? d.ws_bytes : 0);
   if (nt16_big(d)) Nt16Big::launch(d, g, st);
@@ -2092,7 +2213,7 @@ int dispatch_src(const GemmDesc& d, hipStream_t st) {
   return fail(QBLK_EUNSUPPORTED, "gemm: operand storage combination (fp16 storage needs fp16 contraction)");
 }
 
-int elems16(Src s) { return s == Src::F32 ? 4 : 8; }
+int elems16(Src s) { return s == Src::F32 ? 4 : s == Src::F8 ? 16 : 8; }
 
 }  // namespace
 
@@ -2132,6 +2253,14 @@ int gemm(const GemmDesc& d, hipStream_t st) {
   if (d.ext.kext % 4 != 0) return fail(QBLK_EINVAL, "gemm: K extension must be a multiple of 4");
   if (d.ext.kext > (d.prec == Prec::F16 ? 64 : 32))
     return fail(QBLK_EUNSUPPORTED, "gemm: K extension wider than one K tile");
+  if (d.prec == Prec::FP8) {
+    if (!f8_ok(d))
+      return fail(QBLK_EUNSUPPORTED, "gemm: fp8 operands need NT layout, 8-bit storage of both, K a multiple of "
+                                     "128, lda and ldb multiples of 16 and 16-byte aligned rows");
+    return launch_f8(d, st);
+  }
+  if (d.a_src == Src::F8 || d.b_src == Src::F8)
+    return fail(QBLK_EINVAL, "gemm: 8-bit storage goes with fp8 operands only");
   if (d.prec == Prec::BF16) {
     if (!nt16_ok(d))
       return fail(QBLK_EUNSUPPORTED, "gemm: bfloat16 operands need 16-bit storage of both operands, K a multiple "
@@ -2164,6 +2293,10 @@ size_t gemm_nf4_workspace(int M, int N, int k_total) {
 }
 
 size_t gemm_workspace(const GemmDesc& d) {
+  if (d.prec == Prec::FP8) {
+    const Grid g = plan_tiles(f8_units(d), (size_t)-1, Nt16Small::bm, Nt16Small::bn, 64, -2 * kTargetWgs);
+    return g.splits > 1 ? (size_t)g.splits * d.M * d.N * sizeof(float) : 0;
+  }
   const Grid g = nf4_fused_ok(d) ? plan_nf4(d, (size_t)-1) : plan(d, (size_t)-1);
   return g.splits > 1 ? (size_t)g.splits * d.M * d.N * sizeof(float) : 0;
 }

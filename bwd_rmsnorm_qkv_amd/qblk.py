@@ -109,6 +109,13 @@ _SIGS = {
     "qblk_gemm_ex": ([C.c_int32] * 5 + [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_int64, C.c_int32,
                                         C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p],
                      C.c_int32),
+    "qblk_fp8_quantize_workspace_size": ([C.c_int32, C.c_int32, C.POINTER(C.c_size_t)], C.c_int32),
+    "qblk_fp8_quantize": ([C.c_int32, C.c_int32, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_int64,
+                           C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int32),
+    "qblk_gemm_fp8_workspace_size": ([C.c_int32] * 3 + [C.POINTER(C.c_size_t)], C.c_int32),
+    "qblk_gemm_fp8": ([C.c_int32] * 3 + [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_int64, C.c_int32,
+                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p,
+                                         C.c_size_t, C.c_void_p], C.c_int32),
     "qblk_swiglu_forward": ([C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int32),
     "qblk_swiglu_backward": ([C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int32),
     "qblk_qk_norm_rope_workspace_size": ([C.c_int32] * 5 + [C.POINTER(C.c_size_t)], C.c_int32),
@@ -402,6 +409,33 @@ def gemm(layout, precision, M, N, K, A, lda, B, ldb, Cm, ldc, accumulate=0, scra
     code = lambda t: {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[t.dtype]
     _check(lib().qblk_gemm_ex(layout, precision, M, N, K, _p(A), lda, code(A), _p(B), ldb, code(B), _p(Cm), ldc,
                               accumulate, _p(scratch), nbytes, _stream(stream)))
+
+
+def fp8_quantize_workspace_size(rows, cols):
+    n = C.c_size_t()
+    _check(lib().qblk_fp8_quantize_workspace_size(rows, cols, C.byref(n)))
+    return n.value
+
+
+def fp8_quantize(rows, cols, x, ldx, e5m2, q, ldq, inv_scale, scratch, stream=None):
+    """x fp32 [rows, ldx] -> q uint8 [rows, ldq] (E4M3, or E5M2 with
+    e5m2 = 1) and inv_scale (device fp32 [1]) = 1 / the per-tensor scale."""
+    _check(lib().qblk_fp8_quantize(rows, cols, _p(x), ldx, int(e5m2), _p(q), ldq, _p(inv_scale), _p(scratch),
+                                   scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def gemm_fp8_workspace_size(M, N, K):
+    n = C.c_size_t()
+    _check(lib().qblk_gemm_fp8_workspace_size(M, N, K, C.byref(n)))
+    return n.value
+
+
+def gemm_fp8(M, N, K, A, lda, a_e5m2, B, ldb, b_e5m2, a_inv_scale, b_inv_scale, Cm, ldc, accumulate=0,
+             scratch=None, stream=None):
+    """C[M, N] (+)= (A8 [M, K] B8 [N, K]^T) * a_inv_scale[0] * b_inv_scale[0]."""
+    nbytes = 0 if scratch is None else scratch.numel() * scratch.element_size()
+    _check(lib().qblk_gemm_fp8(M, N, K, _p(A), lda, int(a_e5m2), _p(B), ldb, int(b_e5m2), _p(a_inv_scale),
+                               _p(b_inv_scale), _p(Cm), ldc, accumulate, _p(scratch), nbytes, _stream(stream)))
 
 
 def rmsnorm_workspace_size(rows, n):

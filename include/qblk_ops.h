@@ -44,6 +44,39 @@ int32_t qblk_gemm_ex(int32_t layout, int32_t precision, int32_t M, int32_t N, in
                      int64_t ldc, int32_t accumulate, void* scratch, size_t scratch_bytes,
                      qblk_stream_t stream);
 
+/* 8-bit floating-point operands (the 8-bit counterpart of [block]'s
+ * fp16 GEMM tier and set_fp16_weights copies; the formats are those of the
+ * OCP 8-bit floating point specification: E4M3 with largest finite 448,
+ * no infinities; E5M2 with largest finite 57344).
+ *
+ * qblk_fp8_quantize: per-tensor scaled conversion of an fp32 matrix x
+ * [rows, cols] (row stride ldx elements) into q [rows, cols] bytes (row
+ * stride ldq), E4M3 (e5m2 = 0) or E5M2 (e5m2 = 1):
+ *   s = FMAX / max|x| (fp32, correctly rounded; 1 if x is all zero),
+ *   q = round_to_nearest_even(clamp(fp32(x * s), -FMAX, FMAX)),
+ * and inv_scale_dev[0] = 1 / s (device fp32). A NaN element stays NaN;
+ * infinite inputs are outside the contract. scratch: device memory of
+ * qblk_fp8_quantize_workspace_size bytes (the partial maxima). Two
+ * launches on `stream`, no host synchronisation. */
+int32_t qblk_fp8_quantize_workspace_size(int32_t rows, int32_t cols, size_t* scratch_bytes);
+int32_t qblk_fp8_quantize(int32_t rows, int32_t cols, const float* x, int64_t ldx, int32_t e5m2, uint8_t* q,
+                          int64_t ldq, float* inv_scale_dev, void* scratch, size_t scratch_bytes,
+                          qblk_stream_t stream);
+
+/* fp8 contraction on v_mfma_f32_32x32x64_f8f6f4, fp32 accumulate:
+ *   C[M, N] (+)= (A8[M, K] B8[N, K]^T) * a_inv_scale[0] * b_inv_scale[0]
+ * A8, B8 row-major bytes (K contiguous, strides lda / ldb >= K, multiples
+ * of 16, 16-byte aligned), each E4M3 or E5M2 (a_e5m2 / b_e5m2); the two
+ * scales are device fp32 scalars (NULL: 1), as qblk_fp8_quantize leaves
+ * them. K a multiple of 128 (else QBLK_EINVAL). C fp32 [M, ldc]; with
+ * accumulate = 1, C += result. `scratch` (optional) enables split K; its
+ * useful size comes from qblk_gemm_fp8_workspace_size. */
+int32_t qblk_gemm_fp8_workspace_size(int32_t M, int32_t N, int32_t K, size_t* scratch_bytes);
+int32_t qblk_gemm_fp8(int32_t M, int32_t N, int32_t K, const uint8_t* A, int64_t lda, int32_t a_e5m2,
+                      const uint8_t* B, int64_t ldb, int32_t b_e5m2, const float* a_inv_scale,
+                      const float* b_inv_scale, float* C, int64_t ldc, int32_t accumulate, void* scratch,
+                      size_t scratch_bytes, qblk_stream_t stream);
+
 /* RMSNorm forward over rows of x [rows, n] ([block] rms_norm_forward):
  * y = x * rho * gamma with rho[r] = (mean x^2 + eps)^(-1/2) written to rho.
  * When `res` is not NULL, x is first replaced by x + res and that sum is
