@@ -36,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_F16_PEAK = 2516.6   # TFLOP/s, dense
+MFMA_F8_PEAK = 5033.2    # TFLOP/s, dense
 MFMA_F32_PEAK = 157.3    # TFLOP/s
 HBM_PEAK = 8000.0        # GB/s
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "block_gemm_hbm_traffic_qwen3_4b_s512.md")
@@ -53,7 +54,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["stack36_train_step", "stack36_train_step_checkpointed", "nf4_lora_block",
-                                       "qwen3_4b_block_train_step", "qwen3_4b_block_bf16"],
+                                       "qwen3_4b_block_train_step", "qwen3_4b_block_bf16", "qwen3_4b_gemm_fp8"],
                     help="time only this workload (for kernel traces) and print its JSON object")
     return ap.parse_args()
 
@@ -289,6 +290,14 @@ def hbm_kernels(torch, qblk, synth, reps=10):
     add("cross_entropy_rows", f"logits [{T}, {V}] fp32 read and overwritten by their gradient", 2 * 4 * T * V,
         lambda: qblk.cross_entropy_rows(T, V, z, tgt, 1.0 / T, lp, am))
     del z
+    T = 16384
+    x = torch.randn(T, h, device="cuda")
+    q8 = torch.empty(T, h, dtype=torch.uint8, device="cuda")
+    inv = torch.empty(1, device="cuda")
+    fs = torch.empty(qblk.fp8_quantize_workspace_size(T, h), dtype=torch.uint8, device="cuda")
+    add("fp8_quantize", f"[{T}, {h}] fp32 -> E4M3 codes: x read twice (max, then convert), codes written",
+        9 * T * h, lambda: qblk.fp8_quantize(T, h, x, h, 0, q8, h, inv, fs))
+    del x, q8
     numel = 2 * c.intermediate * h
     codes = torch.randint(0, 256, (numel // 2,), dtype=torch.uint8, device="cuda")
     absmax = torch.rand(numel // 64, device="cuda")
@@ -510,9 +519,48 @@ def extra_block_bf16(torch, qblk, synth, steps, warmup):
             "ms_per_step": round(ms, 4), "tokens_per_s": round(c.tokens / ms * 1e3, 1)}
 
 
+def extra_gemm_fp8(torch, qblk, synth, steps, warmup):
+    """The 12 products of one Qwen3-4B block step (seq 512) as fp8 NT
+    products (qblk_gemm_fp8): activations and weights E4M3, gradients E5M2,
+    every operand already quantized with K contiguous (the backward's dX and
+    dW take transposed copies), against the fp8 MFMA peak; beside it the
+    quantizer at the block's activation shapes, the work an fp8 step adds
+    per product."""
+    c = synth.QWEN3_4B_BLOCK
+    bufs, flops = [], 0.0
+    for i, (_, M, N, K, acc) in enumerate(block_gemms(c)):
+        A = torch.randint(0, 0x70, (M, K), dtype=torch.uint8, device="cuda")
+        B = torch.randint(0, 0x70, (N, K), dtype=torch.uint8, device="cuda")
+        Cm = torch.empty(M, N, device="cuda")
+        ws = qblk.gemm_fp8_workspace_size(M, N, K)
+        sc = torch.empty(ws, dtype=torch.uint8, device="cuda") if ws else None
+        bufs.append((M, N, K, A, int(i >= 4), B, Cm, acc, sc))
+        flops += 2.0 * M * N * K
+    one = torch.ones(1, device="cuda")
+
+    def seq():
+        for M, N, K, A, a5, B, Cm, acc, sc in bufs:
+            qblk.gemm_fp8(M, N, K, A, K, a5, B, K, 0, one, one, Cm, N, accumulate=acc, scratch=sc)
+    ms = timed(seq, steps, warmup, torch)
+    tf = flops / (ms * 1e-3) / 1e12
+    quant = []
+    for rows, cols in ((c.tokens, c.hidden), (c.tokens, c.intermediate), (c.tokens, 2 * c.intermediate)):
+        x = torch.randn(rows, cols, device="cuda")
+        q8 = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+        inv = torch.empty(1, device="cuda")
+        fs = torch.empty(qblk.fp8_quantize_workspace_size(rows, cols), dtype=torch.uint8, device="cuda")
+        qms = timed(lambda: qblk.fp8_quantize(rows, cols, x, cols, 1, q8, cols, inv, fs), steps, warmup, torch)
+        quant.append({"shape": [rows, cols], "us": round(qms * 1e3, 2)})
+    return {"workload": "the 12 GEMM products of one Qwen3-4B block fwd+bwd (seq 512) as fp8 NT products, "
+                        "operands pre-quantized", "ms_per_step": round(ms, 4), "gflop": round(flops / 1e9, 2),
+            "roofline": {"bound": "mfma fp8", "achieved": round(tf, 1), "peak": MFMA_F8_PEAK, "unit": "TFLOP/s",
+                         "frac": round(tf / MFMA_F8_PEAK, 4)},
+            "fp8_quantize": quant}
+
+
 EXTRAS = {"stack36_train_step": extra_stack, "stack36_train_step_checkpointed": extra_stack_ckpt,
           "nf4_lora_block": extra_nf4, "qwen3_4b_block_train_step": extra_block_train,
-          "qwen3_4b_block_bf16": extra_block_bf16}
+          "qwen3_4b_block_bf16": extra_block_bf16, "qwen3_4b_gemm_fp8": extra_gemm_fp8}
 
 
 def main():
