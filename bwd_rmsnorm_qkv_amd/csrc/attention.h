@@ -22,6 +22,7 @@ struct AttnArgs {
 
 int attention_check(int batch, int seq, int heads, int kv_heads, int head_dim);
 size_t attention_bwd_scratch(int batch, int seq, int heads, int head_dim);
+int attention_kv_split(int batch, int seq, int heads);
 int attention_forward(const AttnArgs& a, Prec p, hipStream_t st);
 int attention_backward(const AttnArgs& a, Prec p, void* scratch, hipStream_t st);
 
@@ -51,6 +52,9 @@ struct AttnDmaArgs {
   float* dv; int64_t lddv;
   f16* dv16 = nullptr; int64_t lddv16 = 0;  // optional fp16 copy of dv
   int bf16 = 0;  // 16-bit operands and copies are bfloat16 (else fp16)
+  // set by the backward's launch: key-range splits and the partial dQ
+  int split = 1;
+  float* dq_part = nullptr;
 };
 
 bool attention_dma_supported(int batch, int seq, int heads, int kv_heads, int head_dim);

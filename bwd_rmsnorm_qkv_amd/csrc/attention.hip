@@ -463,22 +463,38 @@ __global__ __launch_bounds__(64) void attn_dkv_kernel(const AttnArgs a, const fl
   }
 }
 
+// Index space: T kv_heads D sums of dK and dV over the group's heads and
+// the Z key-range splits (split-major, then head, in that fixed order);
+// with Z > 1 also T heads D sums of dQ over its Z splits (dq_part [Z, T,
+// heads, D]) written to dq.
 __global__ void attn_gqa_reduce_kernel(int64_t T, int heads, int kv_heads, int D, int bf16,
                                        const float* dk_part, const float* dv_part, float* dk,
-                                       int64_t lddk, float* dv, int64_t lddv, f16* dv16, int64_t lddv16) {
+                                       int64_t lddk, float* dv, int64_t lddv, f16* dv16, int64_t lddv16, int Z,
+                                       const float* dq_part, float* dq, int64_t lddq) {
   const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   const int64_t n = T * kv_heads * D;
-  if (idx >= n) return;
+  const int64_t part = T * heads * D;  // elements of one split's partial buffer
+  if (idx >= n) {
+    const int64_t e = idx - n;
+    if (Z <= 1 || e >= part) return;
+    const int64_t t = e / ((int64_t)heads * D);
+    const int c = (int)(e % ((int64_t)heads * D));
+    float s = 0.f;
+    for (int z = 0; z < Z; ++z) s += dq_part[z * part + e];
+    dq[t * lddq + c] = s;
+    return;
+  }
   const int64_t t = idx / ((int64_t)kv_heads * D);
   const int rem = (int)(idx % ((int64_t)kv_heads * D));
   const int g = rem / D, j = rem % D;
   const int G = heads / kv_heads;
   float sk = 0.f, sv = 0.f;
-  for (int w = 0; w < G; ++w) {
-    const int64_t o = (t * heads + g * G + w) * (int64_t)D + j;
-    sk += dk_part[o];
-    sv += dv_part[o];
-  }
+  for (int z = 0; z < Z; ++z)
+    for (int w = 0; w < G; ++w) {
+      const int64_t o = z * part + (t * heads + g * G + w) * (int64_t)D + j;
+      sk += dk_part[o];
+      sv += dv_part[o];
+    }
   dk[t * lddk + g * D + j] = sk;
   dv[t * lddv + g * D + j] = sv;
   if (dv16) dv16[t * lddv16 + g * D + j] = to_16(sv, bf16);
@@ -509,7 +525,8 @@ int bwd_launch(const AttnArgs& a, float* delta, float* dk_part, float* dv_part, 
   const int64_t n = T * a.kv_heads * a.head_dim;
   hipLaunchKernelGGL(attn_gqa_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, T,
                      a.heads, a.kv_heads, a.head_dim, 0, (const float*)dk_part, (const float*)dv_part, a.dk,
-                     a.lddk, a.dv, a.lddv, (f16*)nullptr, (int64_t)0);
+                     a.lddk, a.dv, a.lddv, (f16*)nullptr, (int64_t)0, 1, (const float*)nullptr, (float*)nullptr,
+                     (int64_t)0);
   return check_launch("attn_gqa_reduce_kernel");
 }
 
@@ -1136,9 +1153,13 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
   const T* d_o = (const T*)a.d_o;
   const int G = a.heads / a.kv_heads, h = blockIdx.y, grp = h / G, b = blockIdx.z;
   const int S = a.seq;
+  // Z workgroups share a tile pair, split z taking the key tiles
+  // z W + w + t Z W (all W Z waves interleaved); with Z > 1 each writes its
+  // partial dQ to dq_part[z], summed in split order afterwards
+  const int Z = a.split, z = blockIdx.x % Z;
   // tiles t and ntl-1-t share a workgroup (pass 0 the later tile): every
   // workgroup then has the same causal work, and half as many fit one wave
-  const int ntl = (S + 31) / 32, pr = blockIdx.x;
+  const int ntl = (S + 31) / 32, pr = blockIdx.x / Z;
   const int npass = 2 * pr + 1 == ntl ? 1 : 2;
   for (int pass = 0; pass < npass; ++pass) {
     if (pass) __syncthreads();  // the previous tile's combine is done with the stages
@@ -1186,17 +1207,18 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
 #pragma unroll
       for (int ww = 1; ww < W; ++ww) dl += x[ww * 64 + lane];
       __syncthreads();  // the stage is refilled from here on
-      if (w == 0 && kh == 0 && qi < S) delta[rowi] = dl;
+      if (z == 0 && w == 0 && kh == 0 && qi < S) delta[rowi] = dl;
     }
     floatx16 dq[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) dq[db][e] = 0.f;
-    const int n = w <= qt ? (qt - w) / W + 1 : 0;
+    const int w0 = z * W + w, WZ = W * Z;  // first key tile and stride of this wave
+    const int n = w0 <= qt ? (qt - w0) / WZ + 1 : 0;
 
     auto issue = [&](int t, T* sk, T* sv, T* skt) __attribute__((always_inline)) {
-      const int kv0 = (w + W * t) * 32;
+      const int kv0 = (w0 + WZ * t) * 32;
       copy_row_tile<T, D>(sk + w * RT::ELEMS, k, a.ldk, tok0, kv0, S, grp * D, ck, lane);
       copy_row_tile<T, D>(sv + w * RT::ELEMS, v, a.ldv, tok0, kv0, S, grp * D, cv, lane);
       if constexpr (!TR) {
@@ -1205,7 +1227,7 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
       }
     };
     auto compute = [&](const T* sk, const T* sv, const T* skt, int t) __attribute__((always_inline)) {
-      const int kv0 = (w + W * t) * 32;
+      const int kv0 = (w0 + WZ * t) * 32;
       floatx16 s, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -1252,7 +1274,8 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
     sum_owned<W, NB, false>(dq, w, lane, slot, NoScale{});
     if (qi < S) {
       const float inv = 1.0f / sqrtf((float)D);
-      float* row = a.dq + (tok0 + qi) * a.lddq + (int64_t)h * D + 4 * kh;
+      float* row = Z == 1 ? a.dq + (tok0 + qi) * a.lddq + (int64_t)h * D + 4 * kh
+                          : a.dq_part + ((z * (int64_t)a.batch * S + tok0 + qi) * a.heads + h) * D + 4 * kh;
 #pragma unroll
       for (int db = 0; db < NB; ++db)
         if (db % W == w) {
@@ -1296,10 +1319,15 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
   const int h = blockIdx.y, b = blockIdx.z;
   const int G = a.heads / a.kv_heads, grp = h / G;
   const int S = a.seq;
+  // Z workgroups share a tile pair, split z taking the query tiles
+  // kt + z W + w + t Z W; each writes its partials to dk_part[z], dv_part[z]
+  const int Z = a.split, z = blockIdx.x % Z;
   // tiles t and ntl-1-t share a workgroup (pass 0 the later tile): every
   // workgroup then has the same causal work, and half as many fit one wave
-  const int ntl = (S + 31) / 32, pr = blockIdx.x;
+  const int ntl = (S + 31) / 32, pr = blockIdx.x / Z;
   const int npass = 2 * pr + 1 == ntl ? 1 : 2;
+  dk_part += z * (int64_t)a.batch * S * a.heads * D;
+  dv_part += z * (int64_t)a.batch * S * a.heads * D;
   for (int pass = 0; pass < npass; ++pass) {
     if (pass) __syncthreads();  // the previous tile's combine is done with the stages
     const int kt = pass == 0 ? ntl - 1 - pr : pr, kv0 = kt * 32;
@@ -1329,8 +1357,9 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
     const int nqt = (S + 31) / 32;
     const float* lse_h = a.lse + ((int64_t)b * a.heads + h) * S;
     const float* dl_h = delta + ((int64_t)b * a.heads + h) * S;
-    const int n = kt + w < nqt ? (nqt - 1 - kt - w) / W + 1 : 0;  // query tiles kt+w, kt+w+W, ..
-    auto qtile = [&](int t) { return kt + w + W * t; };
+    const int w0 = z * W + w, WZ = W * Z;
+    const int n = kt + w0 < nqt ? (nqt - 1 - kt - w0) / WZ + 1 : 0;  // query tiles kt+w0, kt+w0+WZ, ..
+    auto qtile = [&](int t) { return kt + w0 + WZ * t; };
 
     auto issue = [&](int t, T* sq, T* so, T* sqt, T* sot) __attribute__((always_inline)) {
       const int q0 = qtile(t) * 32;
@@ -1455,19 +1484,23 @@ int fwd_dma_launch(const AttnDmaArgs& a, hipStream_t st) {
 }
 
 template <typename T, int D>
-int bwd_dma_launch(const AttnDmaArgs& a, float* delta, float* dk_part, float* dv_part, hipStream_t st) {
+int bwd_dma_launch(const AttnDmaArgs& a0, float* delta, float* dk_part, float* dv_part, float* dq_part,
+                   hipStream_t st) {
+  AttnDmaArgs a = a0;
+  a.split = attention_kv_split(a.batch, a.seq, a.heads);
+  a.dq_part = dq_part;
   const int64_t T_ = (int64_t)a.batch * a.seq;
-  // tiles are processed in pairs (one workgroup per pair)
-  dim3 grid((unsigned)ceil_div(ceil_div(a.seq, 32), 2), (unsigned)a.heads, (unsigned)a.batch);
+  // tiles are processed in pairs (Z workgroups per pair)
+  dim3 grid((unsigned)(ceil_div(ceil_div(a.seq, 32), 2) * a.split), (unsigned)a.heads, (unsigned)a.batch);
   hipLaunchKernelGGL((attn_dma_dq_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DQ_W), 0, st, a, delta);
   QBLK_TRY(check_launch("attn_dma_dq_kernel"));
   hipLaunchKernelGGL((attn_dma_dkv_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DKV_W), 0, st, a,
                      (const float*)delta, dk_part, dv_part);
   QBLK_TRY(check_launch("attn_dma_dkv_kernel"));
-  const int64_t n = T_ * a.kv_heads * D;
+  const int64_t n = T_ * a.kv_heads * D + (a.split > 1 ? T_ * a.heads * D : 0);
   hipLaunchKernelGGL(attn_gqa_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, T_, a.heads,
                      a.kv_heads, D, a.bf16, (const float*)dk_part, (const float*)dv_part, a.dk, a.lddk, a.dv, a.lddv,
-                     a.dv16, a.lddv16);
+                     a.dv16, a.lddv16, a.split, (const float*)dq_part, a.dq, a.lddq);
   return check_launch("attn_gqa_reduce_kernel");
 }
 
@@ -1483,9 +1516,21 @@ int attention_check(int batch, int seq, int heads, int kv_heads, int head_dim) {
   return 0;
 }
 
+// Key-range splits of the tiled backward: a pair of 32-row tiles per
+// workgroup and one workgroup per CU (their LDS) leave CUs idle when
+// pairs x heads x batch is at most half the 256 CUs; two workgroups then
+// share each pair (each half the key or query tiles), their partial sums
+// added in split order by the GQA reduction.
+int attention_kv_split(int batch, int seq, int heads) {
+  const int64_t wgs = ceil_div(ceil_div(seq, 32), 2) * (int64_t)heads * batch;
+  return 2 * wgs <= 256 ? 2 : 1;
+}
+
 size_t attention_bwd_scratch(int batch, int seq, int heads, int head_dim) {
   const size_t T = (size_t)batch * seq;
-  return (T * heads + 2 * T * heads * head_dim) * sizeof(float);
+  const size_t Z = (size_t)attention_kv_split(batch, seq, heads);
+  // delta, Z dK and Z dV partial buffers, and with Z > 1 Z dQ partials
+  return (T * heads + (2 * Z + (Z > 1 ? Z : 0)) * T * heads * head_dim) * sizeof(float);
 }
 
 int attention_forward(const AttnArgs& a, Prec p, hipStream_t st) {
@@ -1556,18 +1601,21 @@ int attention_dma_backward(const AttnDmaArgs& a, void* scratch, hipStream_t st) 
   if (a.lddo % 8 || a.lddo32 % 4 || a.lddq % 4 || a.lddk % 4 || a.lddv % 4)
     return fail(QBLK_EINVAL, "attention backward (tiled copies): row strides");
   const int64_t T = (int64_t)a.batch * a.seq;
+  const int64_t part = T * a.heads * a.head_dim;
+  const int Z = attention_kv_split(a.batch, a.seq, a.heads);
   float* delta = (float*)scratch;
   float* dk_part = delta + T * a.heads;
-  float* dv_part = dk_part + T * a.heads * a.head_dim;
+  float* dv_part = dk_part + Z * part;
+  float* dq_part = dv_part + Z * part;  // used when Z > 1
   if (a.fp32) {
     if (a.head_dim != 64) return fail(QBLK_EUNSUPPORTED, "attention backward (tiled copies): fp32 needs head_dim 64");
-    return bwd_dma_launch<float, 64>(a, delta, dk_part, dv_part, st);
+    return bwd_dma_launch<float, 64>(a, delta, dk_part, dv_part, dq_part, st);
   }
   if (a.bf16)
-    return a.head_dim == 64 ? bwd_dma_launch<bf16, 64>(a, delta, dk_part, dv_part, st)
-                            : bwd_dma_launch<bf16, 128>(a, delta, dk_part, dv_part, st);
-  return a.head_dim == 64 ? bwd_dma_launch<f16, 64>(a, delta, dk_part, dv_part, st)
-                          : bwd_dma_launch<f16, 128>(a, delta, dk_part, dv_part, st);
+    return a.head_dim == 64 ? bwd_dma_launch<bf16, 64>(a, delta, dk_part, dv_part, dq_part, st)
+                            : bwd_dma_launch<bf16, 128>(a, delta, dk_part, dv_part, dq_part, st);
+  return a.head_dim == 64 ? bwd_dma_launch<f16, 64>(a, delta, dk_part, dv_part, dq_part, st)
+                          : bwd_dma_launch<f16, 128>(a, delta, dk_part, dv_part, dq_part, st);
 }
 
 }  // namespace qblk
