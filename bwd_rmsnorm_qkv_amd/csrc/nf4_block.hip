@@ -291,34 +291,59 @@ struct LoraPack {
   int n, r, in, out, mode;
 };
 
-// Several packs in one launch: job j fills dst[j], elements [end[j-1], end[j])
-// of the launch's index space.
+// Several packs in one launch: job j fills dst[j] with its count[j]
+// elements, taken by the workgroups from begin[j] / 256 on (every job
+// starts on a workgroup boundary, so a workgroup's job is uniform and its
+// fields are scalar loads).
 constexpr int kMaxPackJobs = 8;
 struct LoraPackJobs {
   LoraPack job[kMaxPackJobs];
   f16* dst[kMaxPackJobs];
-  int64_t end[kMaxPackJobs];
-  int count;
+  int begin[kMaxPackJobs + 1];  // in elements, multiples of 256
+  int count[kMaxPackJobs];
+  int njobs;
 };
 
 __global__ __launch_bounds__(256) void lora_pack16_kernel(const LoraPackJobs J) {
   // every index fits 32 bits (64 x the widest projection side per job)
-  const int ge = blockIdx.x * 256 + threadIdx.x;
-  if (ge >= (int)J.end[J.count - 1]) return;
+  const int g0 = blockIdx.x * 256;
   int j = 0;
-  while (j + 1 < J.count && ge >= (int)J.end[j]) ++j;
+  while (j + 1 < J.njobs && g0 >= J.begin[j + 1]) ++j;
+  j = __builtin_amdgcn_readfirstlane(j);
   const LoraPack& a = J.job[j];
-  const int e = ge - (j ? (int)J.end[j - 1] : 0);
+  const int e = g0 - J.begin[j] + threadIdx.x;
+  if (e >= J.count[j]) return;
   float v = 0.f;
   if (a.mode == 0) {
     const int row = e / a.in, col = e - row * a.in;
-    if (row < a.n * a.r) v = a.m[row / a.r][(int64_t)(row % a.r) * a.in + col];
+    if (row < a.n * a.r) {
+      const int k = row / a.r;
+      const float* m = k == 0 ? a.m[0] : k == 1 ? a.m[1] : a.m[2];
+      v = m[(int64_t)(row - k * a.r) * a.in + col];
+    }
+  } else if (a.mode == 1) {
+    const int o = e >> 6, c = e & 63;
+    const int k = (a.n > 1 && o >= a.start[1]) + (a.n > 2 && o >= a.start[2]);
+    const float* m = k == 0 ? a.m[0] : k == 1 ? a.m[1] : a.m[2];
+    const int o0 = k == 0 ? a.start[0] : k == 1 ? a.start[1] : a.start[2];
+    if (c >= k * a.r && c < (k + 1) * a.r) v = m[(int64_t)(o - o0) * a.r + (c - k * a.r)];
   } else {
-    const int o = a.mode == 1 ? e >> 6 : e % a.out;
-    const int c = a.mode == 1 ? e & 63 : e / a.out;
-    int k = 0;
-    while (k + 1 < a.n && o >= a.start[k + 1]) ++k;
-    if (c >= k * a.r && c < (k + 1) * a.r) v = a.m[k][(int64_t)(o - a.start[k]) * a.r + (c - k * a.r)];
+    // the transpose: a thread takes columns 4 c4 .. 4 c4 + 3 of one row o
+    // of B (one contiguous read; r is a multiple of 4, so they lie in one
+    // block) and writes them down four rows of the [64, out] operand
+    const int o = e % a.out, c4 = e / a.out;
+    const int k = (a.n > 1 && o >= a.start[1]) + (a.n > 2 && o >= a.start[2]);
+    const float* m = k == 0 ? a.m[0] : k == 1 ? a.m[1] : a.m[2];
+    const int o0 = k == 0 ? a.start[0] : k == 1 ? a.start[1] : a.start[2];
+    float q[4] = {0.f, 0.f, 0.f, 0.f};
+    if (4 * c4 >= k * a.r && 4 * c4 < (k + 1) * a.r) {
+      const float* src = m + (int64_t)(o - o0) * a.r + (4 * c4 - k * a.r);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = src[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) J.dst[j][(int64_t)(4 * c4 + i) * a.out + o] = (f16)q[i];
+    return;
   }
   J.dst[j][e] = (f16)v;
 }
@@ -356,14 +381,18 @@ int lora_pack16_groups(const qblk_nf4_block_params& p, const Group* gs, const in
     for (int t = 0; t < 2; ++t) {
       const int mode = t ? mode_b : mode_a;
       const LoraPack a = lora_pack_job(p, gs[gi].id3, gs[gi].outd, gs[gi].n, ins[gi], mode);
-      J.job[J.count] = a;
-      J.dst[J.count] = (t ? dst_b : dst_a)[gi];
-      acc += mode == 0 ? 64 * (int64_t)a.in : 64 * (int64_t)a.out;
-      J.end[J.count] = acc;
-      ++J.count;
+      J.job[J.njobs] = a;
+      // mode 2 threads each write four elements
+      const int64_t cnt = mode == 0 ? 64 * (int64_t)a.in : (mode == 1 ? 64 : 16) * (int64_t)a.out;
+      J.dst[J.njobs] = (t ? dst_b : dst_a)[gi];
+      J.begin[J.njobs] = (int)acc;
+      J.count[J.njobs] = (int)cnt;
+      acc += ceil_div(cnt, 256) * 256;
+      ++J.njobs;
+      if (acc >= (int64_t)1 << 31) return fail(QBLK_EUNSUPPORTED, "nf4 block: LoRA operands too large to pack");
     }
-  if (acc >= (int64_t)1 << 31) return fail(QBLK_EUNSUPPORTED, "nf4 block: LoRA operands too large to pack");
-  hipLaunchKernelGGL(lora_pack16_kernel, dim3((unsigned)ceil_div(acc, 256)), dim3(256), 0, st, J);
+  J.begin[J.njobs] = (int)acc;
+  hipLaunchKernelGGL(lora_pack16_kernel, dim3((unsigned)(acc / 256)), dim3(256), 0, st, J);
   return check_launch("lora_pack16_kernel");
 }
 
