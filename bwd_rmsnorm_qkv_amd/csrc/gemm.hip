@@ -2029,9 +2029,13 @@ Grid plan(const GemmDesc& d, size_t ws_bytes) {
     const bool big = nt16_big(d);
     const int bn = big ? big_bn(d) : Nt16Small::bn;
     // split K only as far as the workgroups still fit one wave: the big
-    // tiles run one workgroup per CU (kTargetWgs), the small ones two
+    // tiles run one workgroup per CU (kTargetWgs), the small ones two, or
+    // one for K <= 4096 (measured at the seq-512 Qwen3-4B products: there
+    // the second split's partial sums cost more than the second workgroup
+    // per CU gains)
     Grid g = big ? plan_tiles(d, ws_bytes, Nt16Big::bm, bn, 64, -kTargetWgs)
-                 : plan_tiles(d, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64, -2 * kTargetWgs);
+                 : plan_tiles(d, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64,
+                              d.K <= 4096 ? -kTargetWgs : -2 * kTargetWgs);
     g.bn = bn;
     g.vec = out_vec4(d, g);
     // weight gradients (TN): the N tiles of one A tile on neighbouring
