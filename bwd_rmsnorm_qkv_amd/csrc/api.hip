@@ -532,7 +532,7 @@ int32_t qblk_attention_forward_f16(int32_t batch, int32_t seq, int32_t heads, in
   AttnDmaArgs a = attn16_dense(batch, seq, heads, kv_heads, head_dim);
   a.q = q16; a.k = k16; a.v = v16;
   a.o = o; a.lse = lse;
-  return attention_dma_forward(a, S(stream));
+  return attention_dma_forward(a, nullptr, S(stream));
 }
 
 int32_t qblk_attention_backward_f16(int32_t batch, int32_t seq, int32_t heads, int32_t kv_heads,

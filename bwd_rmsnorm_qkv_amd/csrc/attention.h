@@ -52,13 +52,18 @@ struct AttnDmaArgs {
   float* dv; int64_t lddv;
   f16* dv16 = nullptr; int64_t lddv16 = 0;  // optional fp16 copy of dv
   int bf16 = 0;  // 16-bit operands and copies are bfloat16 (else fp16)
-  // set by the backward's launch: key-range splits and the partial dQ
+  // set by the launches: key-range splits, the backward's partial dQ and
+  // the forward's partial outputs with their (max, sum) pairs
   int split = 1;
   float* dq_part = nullptr;
+  float* o_part = nullptr;
+  float* ml_part = nullptr;
 };
 
 bool attention_dma_supported(int batch, int seq, int heads, int kv_heads, int head_dim);
-int attention_dma_forward(const AttnDmaArgs& a, hipStream_t st);
+// scratch: attention_bwd_scratch bytes (the forward's key-range splits
+// keep their partial outputs there), or NULL for no split.
+int attention_dma_forward(const AttnDmaArgs& a, void* scratch, hipStream_t st);
 // scratch: attention_bwd_scratch bytes.
 int attention_dma_backward(const AttnDmaArgs& a, void* scratch, hipStream_t st);
 

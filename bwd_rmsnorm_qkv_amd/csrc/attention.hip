@@ -1006,9 +1006,14 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
   const T* vT = (const T*)a.vT;
   const int G = a.heads / a.kv_heads, h = blockIdx.y, grp = h / G, b = blockIdx.z;
   const int S = a.seq;
+  // Z workgroups share a tile pair, split z taking the key tiles
+  // z W + w + t Z W; with Z > 1 each writes its partial output (relative to
+  // its own maximum) with that maximum and sum, merged by
+  // attn_fwd_combine_kernel
+  const int Z = a.split, z = blockIdx.x % Z;
   // tiles t and ntl-1-t share a workgroup (pass 0 the later tile): every
   // workgroup then has the same causal work, and half as many fit one wave
-  const int ntl = (S + 31) / 32, pr = blockIdx.x;
+  const int ntl = (S + 31) / 32, pr = blockIdx.x / Z;
   const int npass = 2 * pr + 1 == ntl ? 1 : 2;
   for (int pass = 0; pass < npass; ++pass) {
     if (pass) __syncthreads();  // the previous tile's combine is done with the stages
@@ -1032,16 +1037,17 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
     float m = -INFINITY, l = 0.f;
-    const int n = w <= qt ? (qt - w) / W + 1 : 0;  // key tiles w, w+W, .. <= qt
+    const int w0 = z * W + w, WZ = W * Z;
+    const int n = w0 <= qt ? (qt - w0) / WZ + 1 : 0;  // key tiles w0, w0+WZ, .. <= qt
 
     auto issue = [&](int t, T* sk, T* sv) __attribute__((always_inline)) {
-      const int kv0 = (w + W * t) * 32;
+      const int kv0 = (w0 + WZ * t) * 32;
       copy_row_tile<T, D>(sk + w * RT::ELEMS, k, a.ldk, tok0, kv0, S, grp * D, ck, lane);
       if constexpr (TR) copy_row_tile<T, D>(sv + w * VE, v, a.ldv, tok0, kv0, S, grp * D, cv, lane);
       else copy_tr_tile<D>(sv + w * VE, vT, a.ldt, tok0, kv0, S, grp * D, cv, lane);
     };
     auto compute = [&](const T* sk, const T* sv, int t) __attribute__((always_inline)) {
-      const int kv0 = (w + W * t) * 32;
+      const int kv0 = (w0 + WZ * t) * 32;
       floatx16 s;
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -1110,6 +1116,23 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
       L = ww == 0 ? lw : L + lw;
     }
     sum_owned<W, NB, true>(o, w, lane, slot, [&](int ww) __attribute__((always_inline)) { return fw[ww]; });
+    if (Z > 1) {
+      // this split's output relative to its maximum M, and M, L
+      if (qi < S) {
+        const int64_t row = (z * (int64_t)a.batch * S + tok0 + qi) * a.heads + h;
+        float* op = a.o_part + row * D + 4 * kh;
+#pragma unroll
+        for (int db = 0; db < NB; ++db)
+          if (db % W == w) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *(float4*)(op + db * 32 + 8 * g) =
+                  make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+          }
+        if (w == 0 && kh == 0) *(float2*)(a.ml_part + 2 * row) = make_float2(M, L);
+      }
+      continue;
+    }
     if (qi < S) {
       const float inv = 1.0f / L;
       const int64_t ooff = (tok0 + qi) * a.ldo + (int64_t)h * D + 4 * kh;
@@ -1475,12 +1498,61 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
   }
 }
 
+// Merge of the forward's Z key-range splits per (token, head): with
+// M = max M_z and f_z = 2^(M_z - M), o = sum f_z O_z / sum f_z L_z (split
+// order), lse = (M + log2 sum f_z L_z) ln 2. One thread per 4 columns.
+__global__ __launch_bounds__(256) void attn_fwd_combine_kernel(const AttnDmaArgs a, int D) {
+  const int64_t T = (int64_t)a.batch * a.seq;
+  const int64_t e = blockIdx.x * (int64_t)256 + threadIdx.x;
+  const int c4 = D / 4;
+  if (e >= T * a.heads * c4) return;
+  const int64_t row = e / c4;  // token * heads + head
+  const int col = 4 * (int)(e % c4);
+  const int Z = a.split;
+  float M = -INFINITY;
+  for (int z = 0; z < Z; ++z) M = fmaxf(M, a.ml_part[2 * (z * T * a.heads + row)]);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int z = 0; z < Z; ++z) {
+    const float2 ml = *(const float2*)(a.ml_part + 2 * (z * T * a.heads + row));
+    const float f = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+    L += ml.y * f;
+    const float4 v = *(const float4*)(a.o_part + (z * T * a.heads + row) * D + col);
+    acc.x += f * v.x;
+    acc.y += f * v.y;
+    acc.z += f * v.z;
+    acc.w += f * v.w;
+  }
+  const float inv = 1.0f / L;
+  const int64_t tok = row / a.heads;
+  const int h = (int)(row % a.heads);
+  const float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  const int64_t off = tok * a.ldo + (int64_t)h * D + col;
+  *(float4*)(a.o + off) = o;
+  if (a.o16) *(half4*)(a.o16 + off) = to_16x4(o, a.bf16 != 0);
+  if (col == 0) {
+    const int b = (int)(tok / a.seq), sq = (int)(tok % a.seq);
+    a.lse[((int64_t)b * a.heads + h) * a.seq + sq] = (M + log2f(L)) * kLn2;
+  }
+}
+
 template <typename T, int D>
-int fwd_dma_launch(const AttnDmaArgs& a, hipStream_t st) {
-  // tiles are processed in pairs (one workgroup per pair)
-  dim3 grid((unsigned)ceil_div(ceil_div(a.seq, 32), 2), (unsigned)a.heads, (unsigned)a.batch);
+int fwd_dma_launch(const AttnDmaArgs& a0, void* scratch, hipStream_t st) {
+  AttnDmaArgs a = a0;
+  a.split = scratch ? attention_kv_split(a.batch, a.seq, a.heads) : 1;
+  const int64_t ntok = (int64_t)a.batch * a.seq;
+  if (a.split > 1) {
+    a.o_part = (float*)scratch;
+    a.ml_part = a.o_part + a.split * ntok * a.heads * D;
+  }
+  // tiles are processed in pairs (Z workgroups per pair)
+  dim3 grid((unsigned)(ceil_div(ceil_div(a.seq, 32), 2) * a.split), (unsigned)a.heads, (unsigned)a.batch);
   hipLaunchKernelGGL((attn_dma_fwd_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::FWD_W), 0, st, a);
-  return check_launch("attn_dma_fwd_kernel");
+  QBLK_TRY(check_launch("attn_dma_fwd_kernel"));
+  if (a.split == 1) return 0;
+  const int64_t n = ntok * a.heads * (D / 4);
+  hipLaunchKernelGGL(attn_fwd_combine_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, a, D);
+  return check_launch("attn_fwd_combine_kernel");
 }
 
 template <typename T, int D>
@@ -1581,14 +1653,17 @@ static int check_dma(const AttnDmaArgs& a) {
   return 0;
 }
 
-int attention_dma_forward(const AttnDmaArgs& a, hipStream_t st) {
+int attention_dma_forward(const AttnDmaArgs& a, void* scratch, hipStream_t st) {
   QBLK_TRY(check_dma(a));
+  if (scratch && ((uintptr_t)scratch & 15))
+    return fail(QBLK_EINVAL, "attention (tiled copies): misaligned scratch");
   if (a.fp32) {
     if (a.head_dim != 64) return fail(QBLK_EUNSUPPORTED, "attention (tiled copies): fp32 needs head_dim 64");
-    return fwd_dma_launch<float, 64>(a, st);
+    return fwd_dma_launch<float, 64>(a, scratch, st);
   }
-  if (a.bf16) return a.head_dim == 64 ? fwd_dma_launch<bf16, 64>(a, st) : fwd_dma_launch<bf16, 128>(a, st);
-  return a.head_dim == 64 ? fwd_dma_launch<f16, 64>(a, st) : fwd_dma_launch<f16, 128>(a, st);
+  if (a.bf16)
+    return a.head_dim == 64 ? fwd_dma_launch<bf16, 64>(a, scratch, st) : fwd_dma_launch<bf16, 128>(a, scratch, st);
+  return a.head_dim == 64 ? fwd_dma_launch<f16, 64>(a, scratch, st) : fwd_dma_launch<f16, 128>(a, scratch, st);
 }
 
 int attention_dma_backward(const AttnDmaArgs& a, void* scratch, hipStream_t st) {

@@ -90,9 +90,11 @@ struct ProjBwd {
   std::function<int(const float*, const float*, float*, hipStream_t)> qkv, o, gate_up, down;
 };
 
+// attn_ws: the scratch's attention region (the forward's key-range
+// splits keep partial outputs there), or NULL.
 int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g_in, const float* g_post,
                        const float* g_q, const float* g_k, const float* x, float* y, const Saved& s,
-                       hipStream_t st);
+                       void* attn_ws, hipStream_t st);
 int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* g_in, const float* g_post,
                         const float* g_q, const float* g_k, const float* x, const float* dy, const Saved& s,
                         float* dx, float* dg_in, float* dg_post, float* dg_q, float* dg_k, const Scratch& w,

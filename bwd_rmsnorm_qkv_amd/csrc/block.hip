@@ -260,7 +260,7 @@ AttnDmaArgs attn_dma_args(const qblk_config& c, const Saved& s) {
 // NF4 block substitutes dequant + LoRA GEMMs (nf4_block.hip).
 int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g_in, const float* g_post,
                        const float* g_q, const float* g_k, const float* x, float* y, const Saved& s,
-                       hipStream_t st) {
+                       void* attn_ws, hipStream_t st) {
   const int T = c.seq * c.batch, h = c.hidden, d = c.head_dim;
   const int qd = c.heads * d, kvd = c.kv_heads * d, I = c.intermediate;
   const int ldqkv = qd + 2 * kvd;
@@ -287,7 +287,7 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
     }
     AttnDmaArgs af = attn_dma_args(c, s);
     af.o16 = s.o16;
-    QBLK_TRY(attention_dma_forward(af, st));
+    QBLK_TRY(attention_dma_forward(af, attn_ws, st));
   } else {
     AttnArgs aa{};
     aa.batch = c.batch; aa.seq = c.seq; aa.heads = c.heads; aa.kv_heads = c.kv_heads; aa.head_dim = d;
@@ -471,7 +471,7 @@ int dense16_forward(const qblk_config& c, const qblk_block_params& p, const floa
   // saved rho): their fp32 forms are not written
   Saved s16 = s;
   s16.n1 = s16.n2 = s16.s = nullptr;
-  return block_forward_impl(c, pf, p.g_in, p.g_post, p.g_q, p.g_k, x, y, s16, st);
+  return block_forward_impl(c, pf, p.g_in, p.g_post, p.g_q, p.g_k, x, y, s16, w.attn, st);
 }
 
 // dX = dY W (NN: dY16 [T, n_out] K-major, W16 [n_out, n_in] read out-major)
@@ -543,7 +543,7 @@ int dense_block_forward(const qblk_config& c, const qblk_block_params& p, const 
     g.r = res; g.ldr = h;
     return gemm(g, s_);
   };
-  return block_forward_impl(c, proj, p.g_in, p.g_post, p.g_q, p.g_k, x, y, s, st);
+  return block_forward_impl(c, proj, p.g_in, p.g_post, p.g_q, p.g_k, x, y, s, w.attn, st);
 }
 
 int dense_block_backward(const qblk_config& c, const qblk_block_params& p, const qblk_block_grads& gr,

@@ -581,7 +581,7 @@ extern "C" int32_t qblk_block_forward_nf4_lora(const qblk_config* cfg, const qbl
       return rc;
     }
   }
-  const int rc = block_forward_impl(c, proj, P.g_in, P.g_post, P.g_q, P.g_k, x, y, sv, st);
+  const int rc = block_forward_impl(c, proj, P.g_in, P.g_post, P.g_q, P.g_k, x, y, sv, w.base.attn, st);
   t_ws = nullptr;
   return rc;
 }
