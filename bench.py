@@ -95,6 +95,23 @@ def timed(fn, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps  # ms per step
 
 
+def step_percentiles(fn, steps, torch):
+    """p10 / p50 / p90 of per-step times: one event pair around each step,
+    all queued behind one spin (the pairs' own packets add a few us)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    fn()
+    torch.cuda.synchronize()
+    front_run(torch, min(20.0, 1.0 + 0.05 * steps))
+    for e0, e1 in evs:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    t = np.sort([e0.elapsed_time(e1) for e0, e1 in evs])
+    pick = lambda q: round(float(t[min(len(t) - 1, int(q * (len(t) - 1) + 0.5))]), 4)
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "steps": steps}
+
+
 def block_gemms(c):
     """(layout, M, N, K, accumulate) of every GEMM launch of one block
     forward + backward as the block entry points issue them on the fp16
@@ -600,12 +617,14 @@ def main():
     ms = timed(step, args.steps, args.warmup, torch)
     value = c.tokens / (ms * 1e-3)
     log(f"block fwd+bwd {ms:.4f} ms/step, {value:.0f} tokens/s")
+    pct = step_percentiles(step, max(10, args.steps), torch)
     roof = gemm_roofline(c, torch, qblk, reps=max(5, args.steps // 2))
     log(f"GEMM roofline {roof['achieved']} TFLOP/s ({roof['frac']*100:.1f}% of peak)")
     out = {
         "metric": "train tokens/s per block fwd+bwd (Qwen3-4B shape); % MFMA peak, % HBM BW",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "step_ms_percentiles": pct,
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16 GEMM operands, fp32 accumulate/master",
         "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights)",
         "config": {"workload": "Qwen3-4B-shaped decoder block fwd+bwd", "hidden": c.hidden, "heads": c.heads,
