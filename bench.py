@@ -150,6 +150,35 @@ def gemm_traffic():
     return float(vals["traffic_bytes_per_launch"])
 
 
+def mfma_counters():
+    """MFMA busy fractions (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x
+    SIMDs) of the block's GEMM launches and of the attention kernels, from
+    the same committed counter summary as `traffic` (a rocprofv3 --pmc run
+    of bench_traffic.py); each part is None when its kernels' sources
+    changed since the counters were taken."""
+    import bench_traffic
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    gemm, attn, sha, asha = [], [], None, None
+    for line in lines:
+        if line.startswith("gemm_source_sha1: "):
+            sha = line.split(": ", 1)[1].strip()
+        if line.startswith("attention_source_sha1: "):
+            asha = line.split(": ", 1)[1].strip()
+        cells = [x.strip() for x in line.strip().strip("|").split("|")]
+        if len(cells) == 6 and cells[0].isdigit():
+            gemm.append({"launch": int(cells[0]), "shape": cells[1], "mfma_busy": float(cells[5])})
+        elif len(cells) == 5 and "attn" in cells[1]:
+            attn.append({"workload": cells[0], "kernel": cells[1].strip("`"), "mfma_busy": float(cells[4])})
+    fresh_attn = asha == bench_traffic.source_digest(bench_traffic.ATTENTION_SOURCES)
+    return {"source": TRAFFIC_SUMMARY.replace(ROOT + os.sep, ""),
+            "gemm": gemm if sha == bench_traffic.source_digest() else None,
+            "attention": attn if fresh_attn else None}
+
+
 def gemm_roofline(c, torch, qblk, reps):
     """Replay the step's GEMMs (same kernels, shapes, layouts and operand
     types as the block), timed with HIP events on the current stream, the
@@ -632,6 +661,7 @@ def main():
                    "seq": c.seq, "batch": c.batch, "global_batch": c.batch, "seq_len": c.seq,
                    "parallelism": "single GPU"},
         "roofline": roof,
+        "mfma_busy_counters": mfma_counters(),
         "fp16_weights": "packed once at load; a training step refreshes them inside AdamW "
                         "(qblk_adamw_step_pack16), see extra.qwen3_4b_block_train_step",
     }

@@ -43,9 +43,13 @@ GEMM_SOURCES = ["bwd_rmsnorm_qkv_amd/csrc/gemm.hip", "bwd_rmsnorm_qkv_amd/csrc/g
                 "bwd_rmsnorm_qkv_amd/csrc/common.h"]
 
 
-def source_digest():
+ATTENTION_SOURCES = ["bwd_rmsnorm_qkv_amd/csrc/attention.hip", "bwd_rmsnorm_qkv_amd/csrc/attention.h",
+                     "bwd_rmsnorm_qkv_amd/csrc/common.h"]
+
+
+def source_digest(files=None):
     h = hashlib.sha1()
-    for rel in GEMM_SOURCES:
+    for rel in files or GEMM_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -193,6 +197,7 @@ def summarize(fetch_dir, write_dir, mfma_dir, out_path):
         "",
         f"traffic_bytes_per_launch: {per:.0f}",
         f"gemm_source_sha1: {source_digest()}",
+        f"attention_source_sha1: {source_digest(ATTENTION_SOURCES)}",
         "",
         "## Attention kernels (MFMA busy and HBM traffic per dispatch)",
         "",
