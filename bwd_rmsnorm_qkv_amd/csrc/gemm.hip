@@ -1252,8 +1252,11 @@ __device__ __forceinline__ uint32_t pk_scale(uint32_t pair, half2v s) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Two workgroups per CU need at most 256 registers per lane (the
+// second launch-bounds argument): without it the accumulators went to AGPRs
+// beside 212 VGPRs and only one workgroup fit.
 template <bool NN>
-__global__ __launch_bounds__(256) void gemm_nf4_kernel(const GemmDesc d, const Grid gd) {
+__global__ __launch_bounds__(256, 2) void gemm_nf4_kernel(const GemmDesc d, const Grid gd) {
   constexpr int BM = 128, BN = 128, BK = 64, WM = 2, WN = 2, NW = 4, TM = 2, TN = 2;
   using OA = DmaOperand<BM, true, NW>;
   using OB = DmaOperand<BN, !NN, NW>;  // fragment reads of the decoded stage
