@@ -28,6 +28,11 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
+
+def _rel(path):
+    """A path as given on the command line, relative to the repository root."""
+    return os.path.relpath(os.path.abspath(path), ROOT)
+
 def _csv(d, suffix):
     f = glob.glob(os.path.join(d, f"*{suffix}"))
     if not f:
@@ -97,10 +102,9 @@ def summarize(trace_dir, bench_json, out_path):
         "Commands (repository root, one MI355X):",
         "",
         "```",
-        "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o bench "
-        "-- python bench.py --no-cpu --no-extra > gpurun_out/trace/bench.json",
-        "python bench_trace.py summarize gpurun_out/trace gpurun_out/trace/bench.json "
-        + os.path.relpath(out_path, ROOT),
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d {_rel(trace_dir)} -o bench "
+        f"-- python bench.py --no-cpu --no-extra > {_rel(bench_json)}",
+        f"python bench_trace.py summarize {_rel(trace_dir)} {_rel(bench_json)} " + os.path.relpath(out_path, ROOT),
         "```",
         "",
         "## GEMM replay (the roofline entry)",
@@ -170,9 +174,9 @@ def summarize_steps(trace_dir, bench_json, out_path, title, command):
         agg[n] = (c + 1, t + ns)
     busy = sum(t for _, t in agg.values()) / steps / 1e3
     lines = [f"# Kernel durations: {title}", "", "Commands (repository root, one MI355X):", "", "```",
-             "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o bench -- " + command
-             + " > gpurun_out/trace/bench.json",
-             f"python bench_trace.py steps gpurun_out/trace gpurun_out/trace/bench.json "
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d {_rel(trace_dir)} -o bench -- " + command
+             + f" > {_rel(bench_json)}",
+             f"python bench_trace.py steps {_rel(trace_dir)} {_rel(bench_json)} "
              f"{os.path.relpath(out_path, ROOT)} \"{title}\" \"{command}\"", "```", "",
              "## Timed loop, per step", "",
              f"{steps} steps; kernel busy time {busy:.1f} us per step; bench: {bench['ms_per_step'] * 1e3:.1f} us "

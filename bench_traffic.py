@@ -47,6 +47,11 @@ ATTENTION_SOURCES = ["bwd_rmsnorm_qkv_amd/csrc/attention.hip", "bwd_rmsnorm_qkv_
                      "bwd_rmsnorm_qkv_amd/csrc/common.h"]
 
 
+def _rel(path):
+    """A path as given on the command line, relative to the repository root."""
+    return os.path.relpath(os.path.abspath(path), ROOT)
+
+
 def source_digest(files=None):
     h = hashlib.sha1()
     for rel in files or GEMM_SOURCES:
@@ -166,11 +171,11 @@ def summarize(fetch_dir, write_dir, mfma_dir, out_path):
         "Commands (repository root; one counter set per run):",
         "",
         "```",
-        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic/fetch -o f -- python bench_traffic.py run",
-        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic/write -o w -- python bench_traffic.py run",
-        "rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES --output-format csv -d gpurun_out/traffic/mfma -o m "
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {_rel(fetch_dir)} -o f -- python bench_traffic.py run",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {_rel(write_dir)} -o w -- python bench_traffic.py run",
+        f"rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES --output-format csv -d {_rel(mfma_dir)} -o m "
         "-- python bench_traffic.py run",
-        "python bench_traffic.py summarize gpurun_out/traffic/fetch gpurun_out/traffic/write gpurun_out/traffic/mfma "
+        f"python bench_traffic.py summarize {_rel(fetch_dir)} {_rel(write_dir)} {_rel(mfma_dir)} "
         + os.path.relpath(out_path, ROOT),
         "```",
         "",
