@@ -470,6 +470,7 @@ struct Grid {
   int vec = 0;    // 1: output rows (and partials, residual) take 16-byte stores
   int bn = 0;     // tile width (ping-pong kernel: 256 or 192)
   int nfast = 0;  // ping-pong kernel: N tiles fastest (consecutive workgroups share an A tile)
+  int deep = 0;   // 128 x 128 tiles, one workgroup per CU: three A and three B stages
 };
 
 // Final value of C[row, col]: the row pointer `cp` already routed through
@@ -1967,9 +1968,13 @@ struct DmaCfg {
   }
 };
 // 128 x 128 tiles, 4 waves, two workgroups per CU (80 KB LDS each: two A
-// stages, three B stages); and 256 x 256 tiles, 8 waves of 64 x 128, one
-// workgroup per CU (the ping-pong kernel).
+// stages, three B stages), or, when the grid leaves one workgroup per CU,
+// three stages of each (96 KB: one wave per SIMD has no other wave to hide
+// the copies' latency behind, so they run a tile further ahead); and
+// 256 x 256 tiles, 8 waves of 64 x 128, one workgroup per CU (the
+// ping-pong kernel).
 using Nt16Small = DmaCfg<128, 128, 2, 2, 2, 3>;
+using Nt16Deep = DmaCfg<128, 128, 2, 2, 3, 3>;
 using Nt16Big = PpCfg;
 
 // Big tiles pay off once they alone give at least half the CUs a tile.
@@ -2031,15 +2036,15 @@ Grid plan(const GemmDesc& d, size_t ws_bytes) {
   if (nt16_ok(d)) {
     const bool big = nt16_big(d);
     const int bn = big ? big_bn(d) : Nt16Small::bn;
-    // split K only as far as the workgroups still fit one wave: the big
-    // tiles run one workgroup per CU (kTargetWgs), the small ones two, or
-    // one for K <= 4096 (measured at the seq-512 Qwen3-4B products: there
-    // the second split's partial sums cost more than the second workgroup
-    // per CU gains)
+    // split K only as far as one workgroup per CU (kTargetWgs): at the
+    // seq-512 Qwen3-4B products a second split's partial sums cost more
+    // than a second workgroup per CU gains, once the lone workgroup keeps
+    // three tiles of copies in flight (e.g. 512 x 2560 x 9728: 3 splits
+    // with three stages 36 us, 6 splits with two 40 us)
     Grid g = big ? plan_tiles(d, ws_bytes, Nt16Big::bm, bn, 64, -kTargetWgs)
-                 : plan_tiles(d, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64,
-                              d.K <= 4096 ? -kTargetWgs : -2 * kTargetWgs);
+                 : plan_tiles(d, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64, -kTargetWgs);
     g.bn = bn;
+    g.deep = !big && g.tiles_m * g.tiles_n * g.splits <= kTargetWgs;
     g.vec = out_vec4(d, g);
     // weight gradients (TN): the N tiles of one A tile on neighbouring
     // workgroups, so that the long A operand is read about once while the
@@ -2169,6 +2174,7 @@ int launch_f8(const GemmDesc& d, hipStream_t st) {
 int launch_nt16(const GemmDesc& d, hipStream_t st) {
   const Grid g = plan(d, d.ws ? d.ws_bytes : 0);
   if (nt16_big(d)) Nt16Big::launch(d, g, st);
+  else if (g.deep) Nt16Deep::launch(d, g, st);
   else Nt16Small::launch(d, g, st);
   QBLK_TRY(check_launch("gemm_dma_kernel"));
   return finish_splits(d, g, st);
