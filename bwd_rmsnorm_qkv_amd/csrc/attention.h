@@ -23,6 +23,7 @@ struct AttnArgs {
 int attention_check(int batch, int seq, int heads, int kv_heads, int head_dim);
 size_t attention_bwd_scratch(int batch, int seq, int heads, int head_dim);
 int attention_kv_split(int batch, int seq, int heads);
+int attention_group_waves(int batch, int seq, int heads, int kv_heads);
 int attention_forward(const AttnArgs& a, Prec p, hipStream_t st);
 int attention_backward(const AttnArgs& a, Prec p, void* scratch, hipStream_t st);
 

@@ -1498,6 +1498,253 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
   }
 }
 
+// Copies of one row tile split over the G waves of a KV group: wave w
+// issues the 1 KB copies j = w, w + G, ... (its n of them), with the
+// source offsets of those copies precomputed.
+template <typename T, int D, int G>
+struct GrpCopy {
+  using RT = RowTile<T, D>;
+  static constexpr int CPW = (RT::NI + G - 1) / G;
+  uint32_t v[CPW];
+  int n;
+  __device__ __forceinline__ GrpCopy(int lane, int w, int64_t ld) {
+    n = 0;
+#pragma unroll
+    for (int jj = 0; jj < CPW; ++jj) {
+      const int j = jj * G + w;
+      if (j < RT::NI) n = jj + 1;
+      const int row = j * RT::RPI + lane / RT::NCH;
+      const int lc = (lane % RT::NCH) ^ RT::sw(row);
+      v[jj] = (uint32_t)((row * ld + lc * AttnElem<T>::EPC) * (int64_t)sizeof(T));
+    }
+  }
+  // rows r0 .. r0+31 of a [T, *] matrix, columns col0 .. col0+D-1; a tile
+  // running past the sequence clamps its rows to S-1 (they are masked)
+  __device__ __forceinline__ void copy(T* tile, const T* base, int64_t ld, int64_t tok0, int r0, int S, int col0,
+                                       int lane, int w) const {
+    if (r0 + 32 <= S) {
+      const char* slab = (const char*)(base + (tok0 + r0) * ld + col0);
+#pragma unroll
+      for (int jj = 0; jj < CPW; ++jj)
+        if (jj < n) dma16_asm(slab + v[jj], tile + (jj * G + w) * (1024 / sizeof(T)));
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < CPW; ++jj)
+        if (jj < n) {
+          const int j = jj * G + w;
+          const int row = j * RT::RPI + lane / RT::NCH;
+          const int lc = (lane % RT::NCH) ^ RT::sw(row);
+          dma16_asm(base + (tok0 + min(r0 + row, S - 1)) * ld + col0 + lc * AttnElem<T>::EPC,
+                    tile + j * (1024 / sizeof(T)));
+        }
+    }
+  }
+};
+
+// Forward with the key and value tiles shared by a KV group (16-bit
+// operands): grid (pairs of q tiles, KV heads, batch); wave w = hw + G hf
+// computes query head grp G + hw (lane owns a query, as in
+// attn_dma_fwd_kernel) over the key tiles hf, hf + NH, ... of its q tile.
+// Each half hf streams its key and value tiles through a ring of NS stages
+// shared by its G waves (each wave issues its share of the copies), so the
+// LDS fill per tile is one K and one V tile for G heads instead of one per
+// head; with NH = 2 halves two waves share each SIMD, one's softmax beside
+// the other's MFMAs. Step j: each wave waits for its own copies of its
+// half's tile j, a barrier (every copy of step j landed, every wave is done
+// with step j-1), the copies of step j+2 into the stages of step j-1, then
+// the tile. The two halves of a head then merge their (max, sum, output)
+// through LDS, each wave writing half of the head's columns. Tiles t and
+// ntl-1-t share a workgroup as in the other kernels.
+template <typename T, int D, int G, int NH>
+__global__ __launch_bounds__(G* NH * 64) void attn_grp_fwd_kernel(const AttnDmaArgs a) {
+  using RT = RowTile<T, D>;
+  using E = AttnElem<T>;
+  static_assert(sizeof(T) == 2, "16-bit operands");
+  static_assert(NH == 1 || NH == 2, "key halves");
+  // merge space: a wave parks NB/2 blocks of 4 KB in one stage buffer, and
+  // the 8 waves' (max, sum) pairs fill 4 KB of another
+  static_assert(NH == 1 || (G * NH <= 8 && (D / 64) * 4096 <= RT::ELEMS * (int)sizeof(T) &&
+                            4096 <= RT::ELEMS * (int)sizeof(T)), "merge space");
+  constexpr int NS = 3, NB = D / 32;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hw = w % G, hf = w / G;
+  // stage buffers: index 2 (NS hf' + s) + (0 K, 1 V)
+  auto buf = [](int idx) __attribute__((always_inline)) -> T* {
+    switch (idx) {
+      case 0: return att_lds<T, 60, RT::ELEMS>();
+      case 1: return att_lds<T, 61, RT::ELEMS>();
+      case 2: return att_lds<T, 62, RT::ELEMS>();
+      case 3: return att_lds<T, 63, RT::ELEMS>();
+      case 4: return att_lds<T, 64, RT::ELEMS>();
+      case 5: return att_lds<T, 65, RT::ELEMS>();
+    }
+    if constexpr (NH == 2) {
+      switch (idx) {
+        case 6: return att_lds<T, 66, RT::ELEMS>();
+        case 7: return att_lds<T, 67, RT::ELEMS>();
+        case 8: return att_lds<T, 68, RT::ELEMS>();
+        case 9: return att_lds<T, 69, RT::ELEMS>();
+        case 10: return att_lds<T, 70, RT::ELEMS>();
+      }
+      return att_lds<T, 71, RT::ELEMS>();
+    }
+    return nullptr;
+  };
+  T* const sK0 = buf(2 * NS * hf), *const sV0 = buf(2 * NS * hf + 1);
+  T* const sK1 = buf(2 * NS * hf + 2), *const sV1 = buf(2 * NS * hf + 3);
+  T* const sK2 = buf(2 * NS * hf + 4), *const sV2 = buf(2 * NS * hf + 5);
+  const T* q = (const T*)a.q;
+  const T* k = (const T*)a.k;
+  const T* v = (const T*)a.v;
+  const int grp = blockIdx.y, h = grp * G + hw, b = blockIdx.z;
+  const int S = a.seq;
+  const int ntl = (S + 31) / 32, pr = blockIdx.x;
+  const int npass = 2 * pr + 1 == ntl ? 1 : 2;
+  const int i = lane & 31, kh = lane >> 5;
+  const float sc = kLog2e / sqrtf((float)D);
+  const int64_t tok0 = (int64_t)b * S;
+  const RowReads<T, D> rk(i, kh, 0);
+  const TrReads<D> rv(lane, 0);
+  const GrpCopy<T, D, G> ck(lane, hw, a.ldk), cv(lane, hw, a.ldv);
+  const int per_tile = ck.n + cv.n;  // this wave's copies per tile
+  for (int pass = 0; pass < npass; ++pass) {
+    if (pass) __syncthreads();  // every wave is done with the previous pass's stages
+    const int qt = pass == 0 ? ntl - 1 - pr : pr, q0 = qt * 32;
+    const int qi = q0 + i;
+    typename E::Chunk qc[RT::STEPS];
+    load_row_frags<T, D>(q + (tok0 + min(qi, S - 1)) * a.ldq + (int64_t)h * D, kh, qc);
+    floatx16 o[NB];
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    const int nt = qt + 1;                 // key tiles 0 .. qt
+    const int nh = (nt - hf + NH - 1) / NH;  // this half's: hf, hf + NH, ...
+    const int nsteps = (nt + NH - 1) / NH;
+
+    auto issue = [&](int j, T* sk, T* sv) __attribute__((always_inline)) {
+      const int kv0 = (j * NH + hf) * 32;
+      ck.copy(sk, k, a.ldk, tok0, kv0, S, grp * D, lane, hw);
+      cv.copy(sv, v, a.ldv, tok0, kv0, S, grp * D, lane, hw);
+    };
+    auto compute = [&](const T* sk, const T* sv, int j) __attribute__((always_inline)) {
+      const int kv0 = (j * NH + hf) * 32;
+      floatx16 s;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+      for (int c = 0; c < RT::STEPS; ++c) s = E::mma(lds_at<typename E::Chunk>(sk, rk.v[c]), qc[c], s);
+      if (kv0 == q0) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kv0 + 8 * g + 4 * kh + r > qi) s[4 * g + r] = -INFINITY;
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+      mx = half_max(mx) * sc;
+      if (__any(mx > m + kRescaleSlack)) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = exp2_hw(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < NB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        m = mn;
+      }
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = exp2_hw(fmaf(s[e], sc, -m));
+        s[e] = p;
+        ps += p;
+      }
+      l += half_sum(ps);
+      acc_rows_product_tr<D, std::is_same_v<T, bf16>>(sv, rv, s, o);
+    };
+    if (0 < nh) issue(0, sK0, sV0);
+    if (1 < nh) issue(1, sK1, sV1);
+    auto step = [&](T* sk, T* sv, T* rk2, T* rv2, int j) __attribute__((always_inline)) {
+      if (j + 1 < nh) wait_vmcnt_le(per_tile);
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (j + 2 < nh) issue(j + 2, rk2, rv2);
+      if (j < nh) compute(sk, sv, j);
+    };
+    const int nfull = nsteps / NS * NS;
+    for (int j = 0; j < nfull; j += NS) {
+      step(sK0, sV0, sK2, sV2, j);
+      step(sK1, sV1, sK0, sV0, j + 1);
+      step(sK2, sV2, sK1, sV1, j + 2);
+    }
+    if (nsteps - nfull > 0) step(sK0, sV0, sK2, sV2, nfull);
+    if (nsteps - nfull > 1) step(sK1, sV1, sK0, sV0, nfull + 1);
+
+    float M = m, L = l;
+    if constexpr (NH == 2) {
+      // the two halves of head hw merge: wave (hw, hf) parks its max, sum
+      // and the blocks its partner writes (db / (NB/2) != hf), reads the
+      // partner's and adds them, half 0's term first
+      constexpr int OWN = NB / 2;
+      __syncthreads();  // every wave is done with the stages
+      float* park = (float*)buf(w);
+      float* ml = (float*)buf(2 * NS * NH - 1) + 128 * w;  // [m, l] x 64 lanes per wave, last buffer's tail
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+        if (db / OWN != hf) {
+          float4* p = (float4*)(park + (db % OWN) * 1024);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) p[g * 64 + lane] = make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+        }
+      ml[lane] = m;
+      ml[64 + lane] = l;
+      __syncthreads();
+      const int pw = hw + G * (1 - hf);  // partner wave
+      const float* pml = (const float*)buf(2 * NS * NH - 1) + 128 * pw;
+      const float mp = pml[lane], lp = pml[64 + lane];
+      M = fmaxf(m, mp);
+      const float f = m == -INFINITY ? 0.f : exp2f(m - M), fp = mp == -INFINITY ? 0.f : exp2f(mp - M);
+      L = hf == 0 ? l * f + lp * fp : lp * fp + l * f;
+      const float* ppark = (const float*)buf(pw);
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+        if (db / OWN == hf) {
+          const float4* p = (const float4*)(ppark + (db % OWN) * 1024);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 x = p[g * 64 + lane];
+            const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float own = o[db][4 * g + r] * f, oth = xv[r] * fp;
+              o[db][4 * g + r] = hf == 0 ? own + oth : oth + own;
+            }
+          }
+        }
+    }
+    if (qi < S) {
+      const float inv = 1.0f / L;
+      const int64_t ooff = (tok0 + qi) * a.ldo + (int64_t)h * D + 4 * kh;
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+        if (NH == 1 || db / (NB / 2) == hf) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 vv = make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+                                          o[db][4 * g + 3] * inv);
+            *(float4*)(a.o + ooff + db * 32 + 8 * g) = vv;
+            if (a.o16) *(half4*)(a.o16 + ooff + db * 32 + 8 * g) = to_16x4(vv, std::is_same_v<T, bf16>);
+          }
+        }
+      if (kh == 0 && hf == 0) a.lse[((int64_t)b * a.heads + h) * S + qi] = (M + log2f(L)) * kLn2;
+    }
+  }
+}
+
 // Merge of the forward's Z key-range splits per (token, head): with
 // M = max M_z and f_z = 2^(M_z - M), o = sum f_z O_z / sum f_z L_z (split
 // order), lse = (M + log2 sum f_z L_z) ln 2. One thread per 4 columns.
@@ -1539,6 +1786,16 @@ __global__ __launch_bounds__(256) void attn_fwd_combine_kernel(const AttnDmaArgs
 template <typename T, int D>
 int fwd_dma_launch(const AttnDmaArgs& a0, void* scratch, hipStream_t st) {
   AttnDmaArgs a = a0;
+  if constexpr (sizeof(T) == 2) {
+    const int G = attention_group_waves(a.batch, a.seq, a.heads, a.kv_heads);
+    if (G) {
+      dim3 grid((unsigned)ceil_div(ceil_div(a.seq, 32), 2), (unsigned)a.kv_heads, (unsigned)a.batch);
+      if (G == 2) hipLaunchKernelGGL((attn_grp_fwd_kernel<T, D, 2, 2>), grid, dim3(256), 0, st, a);
+      else if (G == 4) hipLaunchKernelGGL((attn_grp_fwd_kernel<T, D, 4, 2>), grid, dim3(512), 0, st, a);
+      else hipLaunchKernelGGL((attn_grp_fwd_kernel<T, D, 8, 1>), grid, dim3(512), 0, st, a);
+      return check_launch("attn_grp_fwd_kernel");
+    }
+  }
   a.split = scratch ? attention_kv_split(a.batch, a.seq, a.heads) : 1;
   const int64_t ntok = (int64_t)a.batch * a.seq;
   if (a.split > 1) {
@@ -1596,6 +1853,18 @@ int attention_check(int batch, int seq, int heads, int kv_heads, int head_dim) {
 int attention_kv_split(int batch, int seq, int heads) {
   const int64_t wgs = ceil_div(ceil_div(seq, 32), 2) * (int64_t)heads * batch;
   return 2 * wgs <= 256 ? 2 : 1;
+}
+
+// The group-shared forward (16-bit operands): G = heads / kv_heads waves
+// per workgroup, one per query head of a KV group, when G is 2, 4 or 8 and
+// its grid (tile pairs x KV heads x batch) gives at least half the 256 CUs
+// a workgroup; 0 otherwise (the per-head kernel with its key-range split
+// then fills the CUs better).
+int attention_group_waves(int batch, int seq, int heads, int kv_heads) {
+  const int G = heads / kv_heads;
+  if (G != 2 && G != 4 && G != 8) return 0;
+  const int64_t wgs = ceil_div(ceil_div(seq, 32), 2) * (int64_t)kv_heads * batch;
+  return wgs >= 128 ? G : 0;
 }
 
 size_t attention_bwd_scratch(int batch, int seq, int heads, int head_dim) {
