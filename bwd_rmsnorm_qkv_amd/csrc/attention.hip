@@ -1745,6 +1745,211 @@ __global__ __launch_bounds__(G* NH * 64) void attn_grp_fwd_kernel(const AttnDmaA
   }
 }
 
+// dQ with the key and value tiles shared by a KV group (16-bit operands),
+// the layout of attn_grp_fwd_kernel: wave w = hw + G hf takes query head
+// grp G + hw over the key tiles hf, hf + NH, ... of its q tile (K and V
+// through the half's shared ring), recomputes P from the LSE, forms dS and
+// accumulates dQ = dS K; delta = rowsum(dO o) is summed by the two halves
+// over half the columns each and stored for the dK/dV kernel. The halves'
+// dQ blocks are added in LDS (half 0 first), each wave writing half of the
+// head's columns.
+template <typename T, int D, int G, int NH>
+__global__ __launch_bounds__(G* NH * 64) void attn_grp_dq_kernel(const AttnDmaArgs a, float* delta) {
+  using RT = RowTile<T, D>;
+  using E = AttnElem<T>;
+  static_assert(sizeof(T) == 2, "16-bit operands");
+  static_assert(NH == 1 || NH == 2, "key halves");
+  static_assert(NH == 1 || (G * NH <= 8 && (D / 64) * 4096 <= RT::ELEMS * (int)sizeof(T) &&
+                            4096 <= RT::ELEMS * (int)sizeof(T)), "merge space");
+  constexpr int NS = 3, NB = D / 32;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hw = w % G, hf = w / G;
+  auto buf = [](int idx) __attribute__((always_inline)) -> T* {
+    switch (idx) {
+      case 0: return att_lds<T, 72, RT::ELEMS>();
+      case 1: return att_lds<T, 73, RT::ELEMS>();
+      case 2: return att_lds<T, 74, RT::ELEMS>();
+      case 3: return att_lds<T, 75, RT::ELEMS>();
+      case 4: return att_lds<T, 76, RT::ELEMS>();
+      case 5: return att_lds<T, 77, RT::ELEMS>();
+    }
+    if constexpr (NH == 2) {
+      switch (idx) {
+        case 6: return att_lds<T, 78, RT::ELEMS>();
+        case 7: return att_lds<T, 79, RT::ELEMS>();
+        case 8: return att_lds<T, 80, RT::ELEMS>();
+        case 9: return att_lds<T, 81, RT::ELEMS>();
+        case 10: return att_lds<T, 82, RT::ELEMS>();
+      }
+      return att_lds<T, 83, RT::ELEMS>();
+    }
+    return nullptr;
+  };
+  T* const sK0 = buf(2 * NS * hf), *const sV0 = buf(2 * NS * hf + 1);
+  T* const sK1 = buf(2 * NS * hf + 2), *const sV1 = buf(2 * NS * hf + 3);
+  T* const sK2 = buf(2 * NS * hf + 4), *const sV2 = buf(2 * NS * hf + 5);
+  // the last stage buffer (stage 2 of the last half) is free until step 0
+  // refills it: the delta exchange and, after the loop, the merge's sums
+  float* const xchg = (float*)buf(2 * NS * NH - 1);
+  const T* q = (const T*)a.q;
+  const T* k = (const T*)a.k;
+  const T* v = (const T*)a.v;
+  const T* d_o = (const T*)a.d_o;
+  const int grp = blockIdx.y, h = grp * G + hw, b = blockIdx.z;
+  const int S = a.seq;
+  const int ntl = (S + 31) / 32, pr = blockIdx.x;
+  const int npass = 2 * pr + 1 == ntl ? 1 : 2;
+  const int i = lane & 31, kh = lane >> 5;
+  const float sc = kLog2e / sqrtf((float)D);
+  const int64_t tok0 = (int64_t)b * S;
+  const RowReads<T, D> rr(i, kh, 0);
+  const TrReads<D> rkt(lane, 0);
+  const GrpCopy<T, D, G> ck(lane, hw, a.ldk), cv(lane, hw, a.ldv);
+  const int per_tile = ck.n + cv.n;
+  for (int pass = 0; pass < npass; ++pass) {
+    if (pass) __syncthreads();  // every wave is done with the previous pass's stages
+    const int qt = pass == 0 ? ntl - 1 - pr : pr, q0 = qt * 32;
+    const int qi = q0 + i, qc_i = min(qi, S - 1);
+    typename E::Chunk qc[RT::STEPS], dc[RT::STEPS];
+    load_row_frags<T, D>(q + (tok0 + qc_i) * a.ldq + (int64_t)h * D, kh, qc);
+    load_row_frags<T, D>(d_o + (tok0 + qc_i) * a.lddo + (int64_t)h * D, kh, dc);
+    const int64_t rowi = ((int64_t)b * a.heads + h) * S + qc_i;
+    const float lse2 = a.lse[rowi] * kLog2e;
+    float dl;
+    {
+      // delta over columns hf D/NH .. (hf+1) D/NH - 1 of the head, the lane
+      // halves (kh) half of those each
+      constexpr int CW = D / NH / 2;
+      const int64_t c0 = (int64_t)h * D + hf * (D / NH) + kh * CW;
+      const float* orow = a.o + (tok0 + qc_i) * a.ldo + c0;
+      const float* drow = a.do32 + (tok0 + qc_i) * a.lddo32 + c0;
+      float4 o4[CW / 4], d4[CW / 4];
+#pragma unroll
+      for (int j = 0; j < CW / 4; ++j) {
+        o4[j] = *(const float4*)(orow + 4 * j);
+        d4[j] = *(const float4*)(drow + 4 * j);
+      }
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < CW / 4; ++j)
+        part += o4[j].x * d4[j].x + o4[j].y * d4[j].y + o4[j].z * d4[j].z + o4[j].w * d4[j].w;
+      part = cross_half_sum(part);
+      if constexpr (NH == 2) {
+        xchg[w * 64 + lane] = part;
+        __syncthreads();
+        const float p0 = xchg[hw * 64 + lane], p1 = xchg[(hw + G) * 64 + lane];
+        dl = p0 + p1;
+      } else {
+        dl = part;
+      }
+      if (hf == 0 && kh == 0 && qi < S) delta[rowi] = dl;
+    }
+    floatx16 dq[NB];
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dq[db][e] = 0.f;
+    const int nt = qt + 1;
+    const int nh = (nt - hf + NH - 1) / NH;
+    const int nsteps = (nt + NH - 1) / NH;
+
+    auto issue = [&](int j, T* sk, T* sv) __attribute__((always_inline)) {
+      const int kv0 = (j * NH + hf) * 32;
+      ck.copy(sk, k, a.ldk, tok0, kv0, S, grp * D, lane, hw);
+      cv.copy(sv, v, a.ldv, tok0, kv0, S, grp * D, lane, hw);
+    };
+    auto compute = [&](const T* sk, const T* sv, int j) __attribute__((always_inline)) {
+      const int kv0 = (j * NH + hf) * 32;
+      floatx16 s, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s[e] = 0.f;
+        dp[e] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < RT::STEPS; ++c) {
+        s = E::mma(lds_at<typename E::Chunk>(sk, rr.v[c]), qc[c], s);
+        dp = E::mma(lds_at<typename E::Chunk>(sv, rr.v[c]), dc[c], dp);
+      }
+      if (kv0 == q0) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * g + r;
+            const int kj = kv0 + 8 * g + 4 * kh + r;
+            const float p = (kj > qi || kj >= S) ? 0.f : exp2_hw(fmaf(s[e], sc, -lse2));
+            s[e] = p * (dp[e] - dl);  // dS^T, unscaled
+          }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = exp2_hw(fmaf(s[e], sc, -lse2)) * (dp[e] - dl);
+      }
+      acc_rows_product_tr<D, std::is_same_v<T, bf16>>(sk, rkt, s, dq);
+    };
+    if (0 < nh) issue(0, sK0, sV0);
+    if (1 < nh) issue(1, sK1, sV1);
+    auto step = [&](T* sk, T* sv, T* rk2, T* rv2, int j) __attribute__((always_inline)) {
+      if (j + 1 < nh) wait_vmcnt_le(per_tile);
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (j + 2 < nh) issue(j + 2, rk2, rv2);
+      if (j < nh) compute(sk, sv, j);
+    };
+    const int nfull = nsteps / NS * NS;
+    for (int j = 0; j < nfull; j += NS) {
+      step(sK0, sV0, sK2, sV2, j);
+      step(sK1, sV1, sK0, sV0, j + 1);
+      step(sK2, sV2, sK1, sV1, j + 2);
+    }
+    if (nsteps - nfull > 0) step(sK0, sV0, sK2, sV2, nfull);
+    if (nsteps - nfull > 1) step(sK1, sV1, sK0, sV0, nfull + 1);
+
+    if constexpr (NH == 2) {
+      // wave (hw, hf) parks the blocks its partner writes and adds the
+      // partner's parked ones to its own, half 0's term first
+      constexpr int OWN = NB / 2;
+      __syncthreads();  // every wave is done with the stages
+      float* park = (float*)buf(w);
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+        if (db / OWN != hf) {
+          float4* p = (float4*)(park + (db % OWN) * 1024);
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            p[g * 64 + lane] = make_float4(dq[db][4 * g], dq[db][4 * g + 1], dq[db][4 * g + 2], dq[db][4 * g + 3]);
+        }
+      __syncthreads();
+      const float* ppark = (const float*)buf(hw + G * (1 - hf));
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+        if (db / OWN == hf) {
+          const float4* p = (const float4*)(ppark + (db % OWN) * 1024);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 x = p[g * 64 + lane];
+            const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              dq[db][4 * g + r] = hf == 0 ? dq[db][4 * g + r] + xv[r] : xv[r] + dq[db][4 * g + r];
+          }
+        }
+    }
+    if (qi < S) {
+      const float inv = 1.0f / sqrtf((float)D);
+      float* row = a.dq + (tok0 + qi) * a.lddq + (int64_t)h * D + 4 * kh;
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+        if (NH == 1 || db / (NB / 2) == hf) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *(float4*)(row + db * 32 + 8 * g) = make_float4(dq[db][4 * g] * inv, dq[db][4 * g + 1] * inv,
+                                                            dq[db][4 * g + 2] * inv, dq[db][4 * g + 3] * inv);
+        }
+    }
+  }
+}
+
 // Merge of the forward's Z key-range splits per (token, head): with
 // M = max M_z and f_z = 2^(M_z - M), o = sum f_z O_z / sum f_z L_z (split
 // order), lse = (M + log2 sum f_z L_z) ln 2. One thread per 4 columns.
@@ -1821,8 +2026,21 @@ int bwd_dma_launch(const AttnDmaArgs& a0, float* delta, float* dk_part, float* d
   const int64_t T_ = (int64_t)a.batch * a.seq;
   // tiles are processed in pairs (Z workgroups per pair)
   dim3 grid((unsigned)(ceil_div(ceil_div(a.seq, 32), 2) * a.split), (unsigned)a.heads, (unsigned)a.batch);
-  hipLaunchKernelGGL((attn_dma_dq_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DQ_W), 0, st, a, delta);
-  QBLK_TRY(check_launch("attn_dma_dq_kernel"));
+  int G = 0;
+  if constexpr (sizeof(T) == 2) G = attention_group_waves(a.batch, a.seq, a.heads, a.kv_heads);
+  if (G) {
+    // (the group kernels run only where the key-range split is 1)
+    dim3 ggrid((unsigned)ceil_div(ceil_div(a.seq, 32), 2), (unsigned)a.kv_heads, (unsigned)a.batch);
+    if constexpr (sizeof(T) == 2) {
+      if (G == 2) hipLaunchKernelGGL((attn_grp_dq_kernel<T, D, 2, 2>), ggrid, dim3(256), 0, st, a, delta);
+      else if (G == 4) hipLaunchKernelGGL((attn_grp_dq_kernel<T, D, 4, 2>), ggrid, dim3(512), 0, st, a, delta);
+      else hipLaunchKernelGGL((attn_grp_dq_kernel<T, D, 8, 1>), ggrid, dim3(512), 0, st, a, delta);
+    }
+    QBLK_TRY(check_launch("attn_grp_dq_kernel"));
+  } else {
+    hipLaunchKernelGGL((attn_dma_dq_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DQ_W), 0, st, a, delta);
+    QBLK_TRY(check_launch("attn_dma_dq_kernel"));
+  }
   hipLaunchKernelGGL((attn_dma_dkv_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DKV_W), 0, st, a,
                      (const float*)delta, dk_part, dv_part);
   QBLK_TRY(check_launch("attn_dma_dkv_kernel"));
