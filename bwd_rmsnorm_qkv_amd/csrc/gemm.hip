@@ -1253,19 +1253,27 @@ __device__ __forceinline__ uint32_t pk_scale(uint32_t pair, half2v s) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Two workgroups per CU need at most 256 registers per lane (the
-// second launch-bounds argument): without it the accumulators went to AGPRs
-// beside 212 VGPRs and only one workgroup fit.
-template <bool NN>
-__global__ __launch_bounds__(256, 2) void gemm_nf4_kernel(const GemmDesc d, const Grid gd) {
-  constexpr int BM = 128, BN = 128, BK = 64, WM = 2, WN = 2, NW = 4, TM = 2, TN = 2;
+// Tiles: 128 x 128 with 4 waves of 64 x 64, two workgroups per CU, or
+// 256 x 256 with 8 waves of 64 x 128, one workgroup per CU (two waves per
+// SIMD): each decoded B tile then serves 256 rows of A, half the decode
+// work per product, and each A tile 256 columns. Two workgroups per CU need
+// at most 256 registers per lane (the second launch-bounds argument):
+// without it the 128 x 128 kernel's accumulators went to AGPRs beside 212
+// VGPRs and only one workgroup fit.
+template <bool NN, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM* WN * 64, WM * WN == 4 ? 2 : 1) void gemm_nf4_kernel(const GemmDesc d,
+                                                                                     const Grid gd) {
+  constexpr int BK = 64, NW = WM * WN, TM = BM / WM / 32, TN = BN / WN / 32;
+  static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "tile");
+  // B's decode shares: NT two threads per tile row, NN NW threads per K-row
+  static_assert(BN == 32 * NW, "B tile width");
   using OA = DmaOperand<BM, true, NW>;
   using OB = DmaOperand<BN, !NN, NW>;  // fragment reads of the decoded stage
 
   __shared__ Nf4Lut lut;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w % WM, wn = w / WM;
-  {
+  if (tid < 256) {
     const f16 lo = (f16)d.nf4.levels[tid & 15], hi = (f16)d.nf4.levels[tid >> 4];
     lut.v[tid] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
   }
@@ -1292,10 +1300,10 @@ __global__ __launch_bounds__(256, 2) void gemm_nf4_kernel(const GemmDesc d, cons
   };
 
   // This thread's share of a B tile: NT, storage row n0 + (tid >> 1),
-  // K elements 32 (tid & 1) .. + 31 of the tile; NN, K-row tid >> 2 of the
-  // tile, columns n0 + 32 (tid & 3) .. + 31.
-  const int brow = NN ? tid >> 2 : tid >> 1;
-  const int bpart = NN ? tid & 3 : tid & 1;
+  // K elements 32 (tid & 1) .. + 31 of the tile; NN, K-row tid / NW of the
+  // tile, columns n0 + 32 (tid % NW) .. + 31.
+  const int brow = NN ? tid / NW : tid >> 1;
+  const int bpart = NN ? tid % NW : tid & 1;
   const uint8_t* ncodes = nullptr;  // NT: codes of this row at K = 32 bpart
   const float* nscale = nullptr;    // NT: scales of this row
   int bcol = 0;                     // NN: first column
@@ -1308,38 +1316,42 @@ __global__ __launch_bounds__(256, 2) void gemm_nf4_kernel(const GemmDesc d, cons
   } else {
     bcol = min(n0 + 32 * bpart, d.N - 32);
   }
+  // codes (16 bytes: 32 weights) and scale of an NF4 tile, loaded a tile
+  // ahead; the LoRA tile's fp16 share is read chunk by chunk at decode time
   struct BReg {
-    u32x4 q[4];
+    u32x4 q;
     float sc;
   };
   auto loadB = [&](int kt, BReg& r) __attribute__((always_inline)) {
     if (kt < nkt_main) {
       if constexpr (!NN) {
-        r.q[0] = *(const u32x4*)(ncodes + (int64_t)kt * (BK / 2));
+        r.q = *(const u32x4*)(ncodes + (int64_t)kt * (BK / 2));
         r.sc = nscale[kt];
       } else {
         const int k0 = kt * BK;  // the tile's K-rows lie in one segment
         const int sg = seg_of(d.b, k0);
         const int64_t e = (int64_t)(k0 + brow - d.b.start[sg]) * d.ldb + bcol;
-        r.q[0] = *(const u32x4*)(d.nf4.codes[sg] + e / 2);
+        r.q = *(const u32x4*)(d.nf4.codes[sg] + e / 2);
         r.sc = d.nf4.scales[sg][e / 64];
       }
-    } else {
-      const f16* src = NN ? d.ext16_b + (int64_t)brow * d.ext16_ldb + bcol
-                          : d.ext16_b + (int64_t)min(n0 + brow, d.N - 1) * d.ext16_ldb + 32 * bpart;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r.q[i] = *(const u32x4*)(src + 8 * i);
     }
   };
   // Decode (or copy, for the LoRA tile) 8-element chunk i of the thread's
   // share into stage sb at the position the fragment reads expect. The
-  // table reads (lut_read) and the scaling + store (lut_store) are split so
-  // that the MFMAs of a K step run while the reads are in flight.
+  // table reads (lut_read; the LoRA chunk's global read) and the scaling +
+  // store (lut_store) are split so that the MFMAs of a K step run while
+  // the reads are in flight.
   auto lut_read = [&](int kt, const BReg& r, int i, uint32_t (&lv)[4]) __attribute__((always_inline)) {
     if (kt < nkt_main) {
-      const uint32_t c = r.q[0][i];
+      const uint32_t c = r.q[i];
 #pragma unroll
       for (int b = 0; b < 4; ++b) lv[b] = lut.v[(c >> (8 * b)) & 255];
+    } else {
+      const f16* src = NN ? d.ext16_b + (int64_t)brow * d.ext16_ldb + bcol
+                          : d.ext16_b + (int64_t)min(n0 + brow, d.N - 1) * d.ext16_ldb + 32 * bpart;
+      const u32x4 x = *(const u32x4*)(src + 8 * i);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) lv[b] = x[b];
     }
   };
   auto lut_store = [&](int kt, const BReg& r, int i, const uint32_t (&lv)[4], f16* sb) __attribute__((always_inline)) {
@@ -1350,7 +1362,8 @@ __global__ __launch_bounds__(256, 2) void gemm_nf4_kernel(const GemmDesc d, cons
 #pragma unroll
       for (int b = 0; b < 4; ++b) out[b] = pk_scale(lv[b], s2);
     } else {
-      out = r.q[i];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) out[b] = lv[b];
     }
     const int c = 4 * bpart + i;  // 8-element chunk within the tile row
     int pos;
@@ -1456,15 +1469,19 @@ __global__ __launch_bounds__(256, 2) void gemm_nf4_kernel(const GemmDesc d, cons
   }
   if (kt < kt1) step(std::integral_constant<int, 0>{}, kt);
 
-  // Epilogue: as gemm_dma_kernel's (staged through the idle stages).
+  // Epilogue: as gemm_dma_kernel's (staged through the idle stages, two
+  // waves' 32-row slices per stage buffer).
   constexpr int WC = TN * 32;
   constexpr int CPR = WC / 4;
+  static_assert(2 * 32 * WC * 4 <= BM * BK * 2 && 2 * 32 * WC * 4 <= BN * BK * 2 && NW <= 8, "epilogue staging");
   const int ii = lane & 31, kh = lane >> 5;
   __syncthreads();
   float* ep;
   switch (w >> 1) {
     case 0: ep = (float*)sA0; break;
-    default: ep = (float*)sB0; break;
+    case 1: ep = (float*)sB0; break;
+    case 2: ep = (float*)sA1; break;
+    default: ep = (float*)sB1; break;
   }
   ep += (w & 1) * 32 * WC;
   auto eslot = [](int r, int c) { return r * WC + ((c ^ (((r >> 2) & 1) << 3)) << 2); };
@@ -2106,12 +2123,20 @@ int nf4_splits(int tiles, int nkt, int64_t mn) {
   return best;
 }
 
+// 256 x 256 tiles once M spans at least two of them (an NN product's N is
+// a multiple of 32 only, so its B shares may clamp at the edge as the
+// 128-wide tiles do).
+bool nf4_big(const GemmDesc& d) { return d.M >= 512; }
+
 Grid plan_nf4(const GemmDesc& d, size_t ws_bytes) {
   Grid g;
-  g.tiles_m = (int)ceil_div(d.M, 128);
-  g.tiles_n = (int)ceil_div(d.N, 128);
+  const bool big = nf4_big(d);
+  const int t = big ? 256 : 128;
+  g.tiles_m = (int)ceil_div(d.M, t);
+  g.tiles_n = (int)ceil_div(d.N, t);
   const int nkt = d.K / 64 + (d.ext16_a ? 1 : 0);
-  int splits = nf4_splits(g.tiles_m * g.tiles_n, nkt, (int64_t)d.M * d.N);
+  int splits = big ? std::max(1, std::min(kTargetWgs / (g.tiles_m * g.tiles_n), nkt / kMinKtPerSplit))
+                   : nf4_splits(g.tiles_m * g.tiles_n, nkt, (int64_t)d.M * d.N);
   if (splits > 1 && (size_t)splits * d.M * d.N * sizeof(float) > ws_bytes) splits = 1;
   const int kt_per = (int)ceil_div(nkt, splits);
   g.splits = std::max(1, (int)ceil_div(nkt, kt_per));
@@ -2125,8 +2150,17 @@ int finish_splits(const GemmDesc& d, const Grid& g, hipStream_t st);
 int launch_nf4(const GemmDesc& d, hipStream_t st) {
   const Grid g = plan_nf4(d, d.ws ? d.ws_bytes : 0);
   const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
-  if (d.layout == Layout::NT) hipLaunchKernelGGL(gemm_nf4_kernel<false>, dim3(nwg), dim3(256), 0, st, d, g);
-  else hipLaunchKernelGGL(gemm_nf4_kernel<true>, dim3(nwg), dim3(256), 0, st, d, g);
+  if (nf4_big(d)) {
+    if (d.layout == Layout::NT)
+      hipLaunchKernelGGL((gemm_nf4_kernel<false, 256, 256, 4, 2>), dim3(nwg), dim3(512), 0, st, d, g);
+    else
+      hipLaunchKernelGGL((gemm_nf4_kernel<true, 256, 256, 4, 2>), dim3(nwg), dim3(512), 0, st, d, g);
+  } else {
+    if (d.layout == Layout::NT)
+      hipLaunchKernelGGL((gemm_nf4_kernel<false, 128, 128, 2, 2>), dim3(nwg), dim3(256), 0, st, d, g);
+    else
+      hipLaunchKernelGGL((gemm_nf4_kernel<true, 128, 128, 2, 2>), dim3(nwg), dim3(256), 0, st, d, g);
+  }
   QBLK_TRY(check_launch("gemm_nf4_kernel"));
   return finish_splits(d, g, st);
 }

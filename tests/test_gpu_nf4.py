@@ -20,7 +20,10 @@ SMALL = synth.BlockShape(hidden=256, heads=4, kv_heads=2, head_dim=64, intermedi
 # not a multiple of 64 (general GEMM kernel); T = 140: the fused-decode path
 SMALL_T72 = synth.BlockShape(hidden=256, heads=4, kv_heads=2, head_dim=64, intermediate=480, seq=36, batch=2,
                              rope_theta=1e6, gemm_precision=1)
-CASES = [("small_ragged", SMALL, 8), ("small_t72", SMALL_T72, 8),
+# T = 600: the fused kernel's 256 x 256 tiles (M >= 512), ragged in M and N
+MID_T600 = synth.BlockShape(hidden=256, heads=4, kv_heads=2, head_dim=64, intermediate=576, seq=300, batch=2,
+                            rope_theta=1e6, gemm_precision=1)
+CASES = [("small_ragged", SMALL, 8), ("small_t72", SMALL_T72, 8), ("mid_t600", MID_T600, 8),
          ("qwen3_4b_seq2048", synth.NF4_LORA_QWEN3_4B, synth.LORA_RANK)]
 
 
