@@ -1810,9 +1810,6 @@ __global__ __launch_bounds__(G* NH * 64) void attn_grp_dq_kernel(const AttnDmaAr
     if (pass) __syncthreads();  // every wave is done with the previous pass's stages
     const int qt = pass == 0 ? ntl - 1 - pr : pr, q0 = qt * 32;
     const int qi = q0 + i, qc_i = min(qi, S - 1);
-    typename E::Chunk qc[RT::STEPS], dc[RT::STEPS];
-    load_row_frags<T, D>(q + (tok0 + qc_i) * a.ldq + (int64_t)h * D, kh, qc);
-    load_row_frags<T, D>(d_o + (tok0 + qc_i) * a.lddo + (int64_t)h * D, kh, dc);
     const int64_t rowi = ((int64_t)b * a.heads + h) * S + qc_i;
     const float lse2 = a.lse[rowi] * kLog2e;
     float dl;
@@ -1844,6 +1841,10 @@ __global__ __launch_bounds__(G* NH * 64) void attn_grp_dq_kernel(const AttnDmaAr
       }
       if (hf == 0 && kh == 0 && qi < S) delta[rowi] = dl;
     }
+    // the operand fragments after the delta sums (fewer live registers)
+    typename E::Chunk qc[RT::STEPS], dc[RT::STEPS];
+    load_row_frags<T, D>(q + (tok0 + qc_i) * a.ldq + (int64_t)h * D, kh, qc);
+    load_row_frags<T, D>(d_o + (tok0 + qc_i) * a.lddo + (int64_t)h * D, kh, dc);
     floatx16 dq[NB];
 #pragma unroll
     for (int db = 0; db < NB; ++db)
@@ -1866,11 +1867,13 @@ __global__ __launch_bounds__(G* NH * 64) void attn_grp_dq_kernel(const AttnDmaAr
         s[e] = 0.f;
         dp[e] = 0.f;
       }
+      // S^T, then dP^T: a scheduling fence between them keeps the V
+      // fragments' reads from being hoisted beside the K ones (registers)
 #pragma unroll
-      for (int c = 0; c < RT::STEPS; ++c) {
-        s = E::mma(lds_at<typename E::Chunk>(sk, rr.v[c]), qc[c], s);
-        dp = E::mma(lds_at<typename E::Chunk>(sv, rr.v[c]), dc[c], dp);
-      }
+      for (int c = 0; c < RT::STEPS; ++c) s = E::mma(lds_at<typename E::Chunk>(sk, rr.v[c]), qc[c], s);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < RT::STEPS; ++c) dp = E::mma(lds_at<typename E::Chunk>(sv, rr.v[c]), dc[c], dp);
       if (kv0 == q0) {
 #pragma unroll
         for (int g = 0; g < 4; ++g)
@@ -1945,6 +1948,162 @@ __global__ __launch_bounds__(G* NH * 64) void attn_grp_dq_kernel(const AttnDmaAr
           for (int g = 0; g < 4; ++g)
             *(float4*)(row + db * 32 + 8 * g) = make_float4(dq[db][4 * g] * inv, dq[db][4 * g + 1] * inv,
                                                             dq[db][4 * g + 2] * inv, dq[db][4 * g + 3] * inv);
+        }
+    }
+  }
+}
+
+// dK, dV per query head with the query-side tiles shared by KB key tiles
+// (16-bit operands): grid (pairs of blocks of KB key tiles, heads, batch);
+// wave w owns key tile KB b + w of block b (lane owns a key, as in
+// attn_dma_dkv_kernel) and the workgroup streams the block's query tiles
+// (Q and dO, each copied once for the KB key tiles, the waves issuing
+// their shares) through a ring of NS stages; a wave skips the query tiles
+// below its key tile. Step t: the wave waits for its own copies of tile t,
+// a barrier, the copies of tile t+2 into the stage of tile t-1, then the
+// tile. The per-head partials go to dk_part / dv_part as in the per-tile
+// kernel. Blocks b and nkb-1-b share a workgroup (the first has the most
+// query tiles).
+template <typename T, int D, int KB>
+__global__ __launch_bounds__(KB * 64) void attn_grp_dkv_kernel(const AttnDmaArgs a, const float* delta,
+                                                               float* dk_part, float* dv_part) {
+  using RT = RowTile<T, D>;
+  using E = AttnElem<T>;
+  static_assert(sizeof(T) == 2, "16-bit operands");
+  constexpr int NS = 3, NB = D / 32;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  auto sQ = [](auto S) { return att_lds<T, 84 + 2 * decltype(S)::value, RT::ELEMS>(); };
+  auto sO = [](auto S) { return att_lds<T, 85 + 2 * decltype(S)::value, RT::ELEMS>(); };
+  const T* q = (const T*)a.q;
+  const T* k = (const T*)a.k;
+  const T* v = (const T*)a.v;
+  const T* d_o = (const T*)a.d_o;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int G = a.heads / a.kv_heads, grp = h / G;
+  const int S = a.seq;
+  const int ntl = (S + 31) / 32, nkb = (ntl + KB - 1) / KB, pr = blockIdx.x;
+  const int npass = 2 * pr + 1 == nkb ? 1 : 2;
+  const int i = lane & 31, kh = lane >> 5;
+  const float sc = kLog2e / sqrtf((float)D);
+  const int64_t tok0 = (int64_t)b * S;
+  const RowReads<T, D> rr(i, kh, 0);
+  const TrReads<D> rxt(lane, 0);
+  const GrpCopy<T, D, KB> cq(lane, w, a.ldq), co(lane, w, a.lddo);
+  const int per_tile = cq.n + co.n;
+  const float* lse_h = a.lse + ((int64_t)b * a.heads + h) * S;
+  const float* dl_h = delta + ((int64_t)b * a.heads + h) * S;
+  for (int pass = 0; pass < npass; ++pass) {
+    if (pass) __syncthreads();  // every wave is done with the previous pass's stages
+    const int bi = pass == 0 ? pr : nkb - 1 - pr;
+    const int qs = bi * KB;           // first query tile of the stream
+    const int kt = qs + w, kv0 = kt * 32;
+    const int kj = kv0 + i;           // this lane's key (column of every accumulator)
+    typename E::Chunk kc[RT::STEPS], vc[RT::STEPS];
+    {
+      const int kr = min(kj, S - 1);
+      load_row_frags<T, D>(k + (tok0 + kr) * a.ldk + (int64_t)grp * D, kh, kc);
+      load_row_frags<T, D>(v + (tok0 + kr) * a.ldv + (int64_t)grp * D, kh, vc);
+    }
+    floatx16 dk[NB], dv[NB];
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        dk[db][e] = 0.f;
+        dv[db][e] = 0.f;
+      }
+    const int n = ntl - qs;  // query tiles qs .. ntl-1
+
+    auto issue = [&](int t, T* sq, T* so) __attribute__((always_inline)) {
+      const int q0 = (qs + t) * 32;
+      cq.copy(sq, q, a.ldq, tok0, q0, S, h * D, lane, w);
+      co.copy(so, d_o, a.lddo, tok0, q0, S, h * D, lane, w);
+    };
+    // log-sum-exp (in powers of two) and delta of this lane's 16 query rows
+    // q0 + 8g + 4kh + r of the next tile, loaded a step ahead before that
+    // step's copies are issued
+    float4 lq[4], dq4[4], lq_n[4], dq4_n[4];
+    auto load_ld = [&](int t, float4 (&L)[4], float4 (&Dl)[4]) __attribute__((always_inline)) {
+      const int q0 = (qs + t) * 32;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qr = q0 + 8 * g + 4 * kh;
+        L[g] = qr < S ? *(const float4*)(lse_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
+        Dl[g] = qr < S ? *(const float4*)(dl_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    auto compute = [&](const T* sq, const T* so, int t) __attribute__((always_inline)) {
+      const int q0 = (qs + t) * 32;
+      floatx16 s, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s[e] = 0.f;
+        dp[e] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < RT::STEPS; ++c) {
+        s = E::mma(lds_at<typename E::Chunk>(sq, rr.v[c]), kc[c], s);
+        dp = E::mma(lds_at<typename E::Chunk>(so, rr.v[c]), vc[c], dp);
+      }
+      auto sm = [&](auto Masked) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * g + r;
+            const float L = r == 0 ? lq[g].x : r == 1 ? lq[g].y : r == 2 ? lq[g].z : lq[g].w;
+            const float Dl = r == 0 ? dq4[g].x : r == 1 ? dq4[g].y : r == 2 ? dq4[g].z : dq4[g].w;
+            float p = exp2_hw(fmaf(s[e], sc, -L * kLog2e));
+            if constexpr (decltype(Masked)::value) {
+              const int qq = q0 + 8 * g + 4 * kh + r;
+              if (kj > qq || qq >= S || kj >= S) p = 0.f;
+            }
+            s[e] = p;
+            dp[e] = p * (dp[e] - Dl);
+          }
+      };
+      if (q0 == kv0 || q0 + 32 > S) sm(std::true_type{});
+      else sm(std::false_type{});
+      acc_rows_product_tr<D, std::is_same_v<T, bf16>>(so, rxt, s, dv);   // dV^T += dO^T P
+      acc_rows_product_tr<D, std::is_same_v<T, bf16>>(sq, rxt, dp, dk);  // dK^T += Q^T dS
+    };
+    load_ld(0, lq_n, dq4_n);
+    issue(0, sQ(I0{}), sO(I0{}));
+    if (1 < n) issue(1, sQ(I1{}), sO(I1{}));
+    auto step = [&](auto St, int t) __attribute__((always_inline)) {
+      constexpr int st = decltype(St)::value;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        lq[g] = lq_n[g];
+        dq4[g] = dq4_n[g];
+      }
+      if (t + 1 < n) load_ld(t + 1, lq_n, dq4_n);
+      if (t + 1 < n) wait_vmcnt_le(per_tile + 8);
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (t + 2 < n) issue(t + 2, sQ(IC<(st + 2) % NS>{}), sO(IC<(st + 2) % NS>{}));
+      if (qs + t >= kt && kt < ntl) compute(sQ(St), sO(St), t);
+    };
+    const int nfull = n / NS * NS;
+    for (int t = 0; t < nfull; t += NS) {
+      step(IC<0>{}, t);
+      step(IC<1>{}, t + 1);
+      step(IC<2>{}, t + 2);
+    }
+    if (n - nfull > 0) step(IC<0>{}, nfull);
+    if (n - nfull > 1) step(IC<1>{}, nfull + 1);
+    if (kt < ntl && kj < S) {
+      const float inv = 1.0f / sqrtf((float)D);
+      float* krow = dk_part + ((tok0 + kj) * a.heads + h) * (int64_t)D + 4 * kh;
+      float* vrow = dv_part + ((tok0 + kj) * a.heads + h) * (int64_t)D + 4 * kh;
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          *(float4*)(krow + db * 32 + 8 * g) =
+              make_float4(dk[db][4 * g] * inv, dk[db][4 * g + 1] * inv, dk[db][4 * g + 2] * inv, dk[db][4 * g + 3] * inv);
+          *(float4*)(vrow + db * 32 + 8 * g) =
+              make_float4(dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
         }
     }
   }
@@ -2041,9 +2200,19 @@ int bwd_dma_launch(const AttnDmaArgs& a0, float* delta, float* dk_part, float* d
     hipLaunchKernelGGL((attn_dma_dq_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DQ_W), 0, st, a, delta);
     QBLK_TRY(check_launch("attn_dma_dq_kernel"));
   }
-  hipLaunchKernelGGL((attn_dma_dkv_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DKV_W), 0, st, a,
-                     (const float*)delta, dk_part, dv_part);
-  QBLK_TRY(check_launch("attn_dma_dkv_kernel"));
+  if (G) {
+    // blocks of 4 key tiles share the query-side stream; pairs of blocks
+    const int64_t nkb = ceil_div(ceil_div(a.seq, 32), 4);
+    dim3 kgrid((unsigned)ceil_div(nkb, 2), (unsigned)a.heads, (unsigned)a.batch);
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL((attn_grp_dkv_kernel<T, D, 4>), kgrid, dim3(256), 0, st, a, (const float*)delta, dk_part,
+                         dv_part);
+    QBLK_TRY(check_launch("attn_grp_dkv_kernel"));
+  } else {
+    hipLaunchKernelGGL((attn_dma_dkv_kernel<T, D>), grid, dim3(64 * AttnSplit<T>::DKV_W), 0, st, a,
+                       (const float*)delta, dk_part, dv_part);
+    QBLK_TRY(check_launch("attn_dma_dkv_kernel"));
+  }
   const int64_t n = T_ * a.kv_heads * D + (a.split > 1 ? T_ * a.heads * D : 0);
   hipLaunchKernelGGL(attn_gqa_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, T_, a.heads,
                      a.kv_heads, D, a.bf16, (const float*)dk_part, (const float*)dv_part, a.dk, a.lddk, a.dv, a.lddv,
