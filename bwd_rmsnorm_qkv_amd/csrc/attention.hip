@@ -1974,6 +1974,8 @@ __global__ __launch_bounds__(KB * 64) void attn_grp_dkv_kernel(const AttnDmaArgs
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   auto sQ = [](auto S) { return att_lds<T, 84 + 2 * decltype(S)::value, RT::ELEMS>(); };
   auto sO = [](auto S) { return att_lds<T, 85 + 2 * decltype(S)::value, RT::ELEMS>(); };
+  // per stage: the tile's 32 log-sum-exps then its 32 deltas
+  auto sL = [](auto S) { return att_lds<float, 90 + decltype(S)::value, 64>(); };
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
   const T* v = (const T*)a.v;
@@ -1989,7 +1991,8 @@ __global__ __launch_bounds__(KB * 64) void attn_grp_dkv_kernel(const AttnDmaArgs
   const RowReads<T, D> rr(i, kh, 0);
   const TrReads<D> rxt(lane, 0);
   const GrpCopy<T, D, KB> cq(lane, w, a.ldq), co(lane, w, a.lddo);
-  const int per_tile = cq.n + co.n;
+  // wave 0 also copies the tile's log-sum-exps and deltas (16 lanes)
+  const int per_tile = cq.n + co.n + (w == 0 ? 1 : 0);
   const float* lse_h = a.lse + ((int64_t)b * a.heads + h) * S;
   const float* dl_h = delta + ((int64_t)b * a.heads + h) * S;
   for (int pass = 0; pass < npass; ++pass) {
@@ -2014,26 +2017,26 @@ __global__ __launch_bounds__(KB * 64) void attn_grp_dkv_kernel(const AttnDmaArgs
       }
     const int n = ntl - qs;  // query tiles qs .. ntl-1
 
-    auto issue = [&](int t, T* sq, T* so) __attribute__((always_inline)) {
+    // Q and dO tiles, and in wave 0 the tile's log-sum-exps and deltas
+    // (lanes 0-7 and 8-15, 16 bytes each; rows past S are not read: S is a
+    // multiple of 8)
+    auto issue = [&](int t, T* sq, T* so, float* sl) __attribute__((always_inline)) {
       const int q0 = (qs + t) * 32;
       cq.copy(sq, q, a.ldq, tok0, q0, S, h * D, lane, w);
       co.copy(so, d_o, a.lddo, tok0, q0, S, h * D, lane, w);
-    };
-    // log-sum-exp (in powers of two) and delta of this lane's 16 query rows
-    // q0 + 8g + 4kh + r of the next tile, loaded a step ahead before that
-    // step's copies are issued
-    float4 lq[4], dq4[4], lq_n[4], dq4_n[4];
-    auto load_ld = [&](int t, float4 (&L)[4], float4 (&Dl)[4]) __attribute__((always_inline)) {
-      const int q0 = (qs + t) * 32;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qr = q0 + 8 * g + 4 * kh;
-        L[g] = qr < S ? *(const float4*)(lse_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
-        Dl[g] = qr < S ? *(const float4*)(dl_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (w == 0) {
+        const int r = q0 + 4 * (lane & 7);
+        if (lane < 16 && r < S) dma16_asm((lane < 8 ? lse_h : dl_h) + r, sl);
       }
     };
-    auto compute = [&](const T* sq, const T* so, int t) __attribute__((always_inline)) {
+    auto compute = [&](const T* sq, const T* so, const float* sl, int t) __attribute__((always_inline)) {
       const int q0 = (qs + t) * 32;
+      float4 lq[4], dq4[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        lq[g] = *(const float4*)(sl + 8 * g + 4 * kh);
+        dq4[g] = *(const float4*)(sl + 32 + 8 * g + 4 * kh);
+      }
       floatx16 s, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -2051,13 +2054,16 @@ __global__ __launch_bounds__(KB * 64) void attn_grp_dkv_kernel(const AttnDmaArgs
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int e = 4 * g + r;
-            const float L = r == 0 ? lq[g].x : r == 1 ? lq[g].y : r == 2 ? lq[g].z : lq[g].w;
-            const float Dl = r == 0 ? dq4[g].x : r == 1 ? dq4[g].y : r == 2 ? dq4[g].z : dq4[g].w;
-            float p = exp2_hw(fmaf(s[e], sc, -L * kLog2e));
+            float L = r == 0 ? lq[g].x : r == 1 ? lq[g].y : r == 2 ? lq[g].z : lq[g].w;
+            float Dl = r == 0 ? dq4[g].x : r == 1 ? dq4[g].y : r == 2 ? dq4[g].z : dq4[g].w;
+            bool off = false;
             if constexpr (decltype(Masked)::value) {
               const int qq = q0 + 8 * g + 4 * kh + r;
-              if (kj > qq || qq >= S || kj >= S) p = 0.f;
+              off = kj > qq || qq >= S || kj >= S;
+              if (qq >= S) L = Dl = 0.f;  // rows past S were not copied
             }
+            float p = exp2_hw(fmaf(s[e], sc, -L * kLog2e));
+            if (off) p = 0.f;
             s[e] = p;
             dp[e] = p * (dp[e] - Dl);
           }
@@ -2067,22 +2073,15 @@ __global__ __launch_bounds__(KB * 64) void attn_grp_dkv_kernel(const AttnDmaArgs
       acc_rows_product_tr<D, std::is_same_v<T, bf16>>(so, rxt, s, dv);   // dV^T += dO^T P
       acc_rows_product_tr<D, std::is_same_v<T, bf16>>(sq, rxt, dp, dk);  // dK^T += Q^T dS
     };
-    load_ld(0, lq_n, dq4_n);
-    issue(0, sQ(I0{}), sO(I0{}));
-    if (1 < n) issue(1, sQ(I1{}), sO(I1{}));
+    issue(0, sQ(I0{}), sO(I0{}), sL(I0{}));
+    if (1 < n) issue(1, sQ(I1{}), sO(I1{}), sL(I1{}));
     auto step = [&](auto St, int t) __attribute__((always_inline)) {
       constexpr int st = decltype(St)::value;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        lq[g] = lq_n[g];
-        dq4[g] = dq4_n[g];
-      }
-      if (t + 1 < n) load_ld(t + 1, lq_n, dq4_n);
-      if (t + 1 < n) wait_vmcnt_le(per_tile + 8);
+      if (t + 1 < n) wait_vmcnt_le(per_tile);
       else wait_vmcnt<0>();
       __syncthreads();
-      if (t + 2 < n) issue(t + 2, sQ(IC<(st + 2) % NS>{}), sO(IC<(st + 2) % NS>{}));
-      if (qs + t >= kt && kt < ntl) compute(sQ(St), sO(St), t);
+      if (t + 2 < n) issue(t + 2, sQ(IC<(st + 2) % NS>{}), sO(IC<(st + 2) % NS>{}), sL(IC<(st + 2) % NS>{}));
+      if (qs + t >= kt && kt < ntl) compute(sQ(St), sO(St), sL(St), t);
     };
     const int nfull = n / NS * NS;
     for (int t = 0; t < nfull; t += NS) {
