@@ -1881,6 +1881,59 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmDesc d, in
   }
 }
 
+// Split-K finish for 16-byte rows without diagonal blocks: each thread takes
+// 4 columns of R consecutive rows and issues every partial load of those
+// rows before any epilogue (R x splits loads in flight per thread instead of
+// splits). The partials are added in split order, as in
+// splitk_reduce_kernel.
+template <int R>
+__global__ __launch_bounds__(256) void splitk_reduce_rows_kernel(const GemmDesc d, int splits) {
+  const int64_t mn = (int64_t)d.M * d.N;
+  const int c0 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c0 >= d.N) return;
+  const int r0 = blockIdx.y * R;
+  float4 v[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) v[j] = *(const float4*)(d.ws + (int64_t)min(r0 + j, d.M - 1) * d.N + c0);
+  for (int p = 1; p < splits; ++p) {
+    float4 u[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) u[j] = *(const float4*)(d.ws + p * mn + (int64_t)min(r0 + j, d.M - 1) * d.N + c0);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      v[j].x += u[j].x;
+      v[j].y += u[j].y;
+      v[j].z += u[j].z;
+      v[j].w += u[j].w;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int row = r0 + j;
+    if (row >= d.M) break;
+    int lo = 0;
+    float* rp = out_row(d, row, lo);
+    float4 o = make_float4(d.alpha * v[j].x, d.alpha * v[j].y, d.alpha * v[j].z, d.alpha * v[j].w);
+    if (d.r) {
+      const float4 rv = *(const float4*)(d.r + (int64_t)row * d.ldr + c0);
+      o.x += rv.x;
+      o.y += rv.y;
+      o.z += rv.z;
+      o.w += rv.w;
+    }
+    float4* cp = (float4*)(rp + c0);
+    if (d.accumulate) {
+      const float4 cv = *cp;
+      o.x += cv.x;
+      o.y += cv.y;
+      o.z += cv.z;
+      o.w += cv.w;
+    }
+    store_c4(cp, o);
+    if (d.c16) *(half4*)(d.c16 + (int64_t)row * d.ldc16 + c0) = to_16x4(o, d.prec == Prec::BF16);
+  }
+}
+
 constexpr int kTargetWgs = 256;  // one 4-wave workgroup per CU (LDS-limited)
 constexpr int kMinKtPerSplit = 8;
 constexpr int kMaxSplits = 32;
@@ -2168,7 +2221,12 @@ int launch_nf4(const GemmDesc& d, hipStream_t st) {
 int finish_splits(const GemmDesc& d, const Grid& g, hipStream_t st) {
   if (g.splits > 1) {
     const dim3 grid((unsigned)ceil_div(d.N, 1024), (unsigned)std::min(d.M, 65535));
-    hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, st, d, g.splits, (int)out_vec4(d, g));
+    if (out_vec4(d, g) && d.c_cols_blockdiag == 0 && ceil_div(d.M, 4) <= 65535) {
+      const dim3 rgrid((unsigned)ceil_div(d.N, 1024), (unsigned)ceil_div(d.M, 4));
+      hipLaunchKernelGGL(splitk_reduce_rows_kernel<4>, rgrid, dim3(256), 0, st, d, g.splits);
+    } else {
+      hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, st, d, g.splits, (int)out_vec4(d, g));
+    }
     QBLK_TRY(check_launch("splitk_reduce_kernel"));
   }
   return 0;
