@@ -1884,12 +1884,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmDesc d, in
 // Split-K finish for 16-byte rows without diagonal blocks: each thread takes
 // 4 columns of R consecutive rows and issues every partial load of those
 // rows before any epilogue (R x splits loads in flight per thread instead of
-// splits). The partials are added in split order, as in
+// splits); a workgroup spans up to 1024 columns (fewer threads for narrow
+// outputs). The partials are added in split order, as in
 // splitk_reduce_kernel.
 template <int R>
 __global__ __launch_bounds__(256) void splitk_reduce_rows_kernel(const GemmDesc d, int splits) {
   const int64_t mn = (int64_t)d.M * d.N;
-  const int c0 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int c0 = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (c0 >= d.N) return;
   const int r0 = blockIdx.y * R;
   float4 v[R];
@@ -2222,8 +2223,9 @@ int finish_splits(const GemmDesc& d, const Grid& g, hipStream_t st) {
   if (g.splits > 1) {
     const dim3 grid((unsigned)ceil_div(d.N, 1024), (unsigned)std::min(d.M, 65535));
     if (out_vec4(d, g) && d.c_cols_blockdiag == 0 && ceil_div(d.M, 4) <= 65535) {
-      const dim3 rgrid((unsigned)ceil_div(d.N, 1024), (unsigned)ceil_div(d.M, 4));
-      hipLaunchKernelGGL(splitk_reduce_rows_kernel<4>, rgrid, dim3(256), 0, st, d, g.splits);
+      const int threads = (int)std::min<int64_t>(256, ceil_div(ceil_div(d.N, 4), 64) * 64);
+      const dim3 rgrid((unsigned)ceil_div(d.N, 4 * threads), (unsigned)ceil_div(d.M, 4));
+      hipLaunchKernelGGL(splitk_reduce_rows_kernel<4>, rgrid, dim3(threads), 0, st, d, g.splits);
     } else {
       hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, st, d, g.splits, (int)out_vec4(d, g));
     }
