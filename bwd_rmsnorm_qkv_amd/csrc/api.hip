@@ -520,7 +520,6 @@ static AttnDmaArgs attn16_dense(int32_t batch, int32_t seq, int32_t heads, int32
   a.batch = batch; a.seq = seq; a.heads = heads; a.kv_heads = kv_heads; a.head_dim = head_dim;
   a.ldq = (int64_t)heads * head_dim;
   a.ldk = a.ldv = (int64_t)kv_heads * head_dim;
-  a.ldt = (int64_t)batch * seq;
   a.ldo = a.lddo = a.lddo32 = a.lddq = (int64_t)heads * head_dim;
   a.lddk = a.lddv = (int64_t)kv_heads * head_dim;
   return a;

@@ -32,21 +32,19 @@ int attention_backward(const AttnArgs& a, Prec p, void* scratch, hipStream_t st)
 namespace qblk {
 
 // Attention on tiled copies (head_dim 64 or 128, seq a multiple of 8): the
-// operands are fp16 copies (fp32 = 0) or fp32 tensors (fp32 = 1): q, k, v
-// row-major [T, heads*d] / [T, kv_heads*d] and the transposed copies
-// qT [heads*d, T], kT, vT [kv_heads*d, T], d_o [T, heads*d], doT
-// [heads*d, T] (row stride ldt = T for the transposed ones). Every tile
-// reaches LDS by direct global -> LDS copies.
+// operands are 16-bit copies (fp32 = 0) or fp32 tensors (fp32 = 1, head_dim
+// 64): q, k, v row-major [T, heads*d] / [T, kv_heads*d] and d_o
+// [T, heads*d]. Every tile reaches LDS by direct global -> LDS copies; the
+// transposed operands (V^T, K^T, Q^T, dO^T) are read out of the row tiles.
 struct AttnDmaArgs {
   int batch, seq, heads, kv_heads, head_dim;
   int fp32;
   const void *q, *k, *v;    int64_t ldq, ldk, ldv;
-  const void *qT, *kT, *vT; int64_t ldt;
   float* o; int64_t ldo;   // fp32 [T, heads*d]
   f16* o16;                // optional fp16 copy of o (same stride), may be NULL
   float* lse;              // [batch, heads, seq], natural log
   // backward only
-  const void *d_o, *doT; int64_t lddo;
+  const void* d_o; int64_t lddo;
   const float* do32; int64_t lddo32;  // fp32 dO (for delta = rowsum(dO o))
   float* dq; int64_t lddq;
   float* dk; int64_t lddk;

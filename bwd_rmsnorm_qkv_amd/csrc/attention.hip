@@ -605,17 +605,6 @@ struct RowTile {
   }
 };
 
-// Transposed tile (fp32 only): D rows x 32 floats (128 bytes per row).
-template <typename T, int D>
-struct TrTile {
-  static constexpr int NCH = 32 * (int)sizeof(T) / 16;
-  static_assert(NCH == 8, "transposed tiles are fp32");
-  static constexpr int RPI = 64 / NCH;  // 8 rows per wave copy
-  static constexpr int NI = D / RPI;
-  static constexpr int ELEMS = D * 32;
-  static __device__ __forceinline__ int sw(int row) { return (row >> 1) & 7; }
-};
-
 template <typename C>
 __device__ __forceinline__ C lds_at(const void* base, uint32_t off) {
   return *(const C*)((const char*)base + off);
@@ -671,20 +660,20 @@ struct TrReads {
   }
 };
 
-// Per-lane byte offsets of the fp32 transposed-tile reads: block db, group
-// g reads the chunk 2g + kh of row db*32 + i.
-template <int D>
-struct TtReads {
-  using TT = TrTile<float, D>;
-  uint32_t v[D / 32][4];
-  __device__ __forceinline__ TtReads(int i, int kh, int slot) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int row = db * 32 + i;
-        v[db][g] = (uint32_t)((slot + row * 32 + (((2 * g + kh) ^ TT::sw(row)) * 4)) * 4);
-      }
+// fp32 transposed reads straight out of a row tile X [32][D] (D = 64): the
+// A operand of the r-th MFMA of group g (32x32x2) is X[key][d] with
+// key = 8g + 4kh + r and d = 32 db + i, one float per lane. With the row
+// tile's swizzle (16 chunks of 4 floats; row bits 0-1 -> chunk bits 2-3,
+// row bits 2-3 -> chunk bits 0-1) that float sits in chunk
+// ((db ^ (r >> 1)) << 3) | ((i >> 2) ^ kh ^ 4 (r & 1) ^ (2g & 3)) of row
+// key. Holds the lane's parts of that address (slot: the wave's tile
+// within the stage, in floats).
+struct Rt32Reads {
+  int lx, lb;  // (i >> 2) ^ kh; slot + 4 kh rows + the float within the chunk
+  __device__ __forceinline__ Rt32Reads(int lane, int slot) {
+    const int i = lane & 31, kh = lane >> 5;
+    lx = (i >> 2) ^ kh;
+    lb = slot + kh * 4 * 64 + (i & 3);
   }
 };
 
@@ -706,8 +695,6 @@ struct CopyOffsets {
 };
 template <typename T, int D>
 using RowCopy = CopyOffsets<T, RowTile<T, D>::NCH, RowTile<T, D>::NI, RowTile<T, D>>;
-template <int D>
-using TrCopy = CopyOffsets<float, TrTile<float, D>::NCH, TrTile<float, D>::NI, TrTile<float, D>>;
 
 // Row tile: rows r0 .. r0+31 of a [T, *] matrix, columns col0 .. col0+D-1.
 // Whole tiles use the precomputed offsets; a tile running past the end of
@@ -727,29 +714,6 @@ __device__ __forceinline__ void copy_row_tile(T* tile, const T* base, int64_t ld
       const int lc = (lane % RT::NCH) ^ RT::sw(row);
       dma16_asm(base + (tok0 + min(r0 + row, S - 1)) * ld + col0 + lc * AttnElem<T>::EPC,
             tile + j * (1024 / sizeof(T)));
-    }
-  }
-}
-
-// Transposed tile (fp32): rows row0 .. row0+D-1 of a [*, T] matrix, columns
-// tok0 + c0 .. +31; chunks past S read chunk 0 of the sequence (masked).
-template <int D>
-__device__ __forceinline__ void copy_tr_tile(float* tile, const float* base, int64_t ldt, int64_t tok0, int c0,
-                                             int S, int row0, const TrCopy<D>& off, int lane) {
-  using T = float;
-  using TT = TrTile<T, D>;
-  if (c0 + 32 <= S) {
-    const char* slab = (const char*)(base + (int64_t)row0 * ldt + tok0 + c0);
-#pragma unroll
-    for (int j = 0; j < TT::NI; ++j) dma16_asm(slab + off.v[j], tile + j * (1024 / sizeof(T)));
-  } else {
-#pragma unroll
-    for (int j = 0; j < TT::NI; ++j) {
-      const int row = j * TT::RPI + lane / TT::NCH;
-      const int lc = (lane % TT::NCH) ^ TT::sw(row);
-      int c = c0 + lc * AttnElem<T>::EPC;
-      if (c >= S) c = 0;
-      dma16_asm(base + (int64_t)(row0 + row) * ldt + tok0 + c, tile + j * (1024 / sizeof(T)));
     }
   }
 }
@@ -803,40 +767,42 @@ __device__ __forceinline__ void acc_rows_product_tr(const void* X, const TrReads
   }
 }
 
-// fp32: the same product with X^T staged as a transposed tile [D][32]: the
-// accumulator value 4g + r is directly the B operand pairing key 8g + r
+// fp32: the same product with X^T read out of the row tile X (Rt32Reads):
+// group g's accumulator value 4g + r is the B operand pairing key 8g + r
 // (lanes 0-31) with key 8g + 4 + r (lanes 32-63).
 template <int D>
-__device__ __forceinline__ void acc_rows_product_tt(const float* Xt, const TtReads<D>& rd, const floatx16& p,
-                                                    floatx16 (&out)[D / 32]) {
+__device__ __forceinline__ void acc_rows_product_rt32(const float* X, const Rt32Reads& rd, const floatx16& p,
+                                                      floatx16 (&out)[D / 32]) {
+  static_assert(D == 64, "fp32 row tiles of 64 columns");
 #pragma unroll
   for (int g = 0; g < 4; ++g)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const float4 a = lds_at<float4>(Xt, rd.v[db][g]);
-      out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, p[4 * g + 0], out[db], 0, 0, 0);
-      out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, p[4 * g + 1], out[db], 0, 0, 0);
-      out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, p[4 * g + 2], out[db], 0, 0, 0);
-      out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, p[4 * g + 3], out[db], 0, 0, 0);
+    for (int r = 0; r < 4; ++r) {
+      const int lc = rd.lx ^ (((r & 1) << 2) ^ ((2 * g) & 3));
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const float a = X[(8 * g + r) * D + rd.lb + ((((db ^ (r >> 1)) << 3) | lc) << 2)];
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[4 * g + r], out[db], 0, 0, 0);
+      }
     }
 }
 
-// Transposed-operand reads of the kernels: fp16 reads row tiles through
-// the transposing LDS instruction, fp32 reads staged transposed tiles.
+// Transposed-operand reads of the kernels, out of the row tiles: fp16
+// through the transposing LDS instruction, fp32 one float per lane.
 template <typename T, int D>
-using XtReads = std::conditional_t<sizeof(T) == 2, TrReads<D>, TtReads<D>>;
+using XtReads = std::conditional_t<sizeof(T) == 2, TrReads<D>, Rt32Reads>;
 
 template <typename T, int D>
-__device__ __forceinline__ XtReads<T, D> make_xt_reads(int lane, int slot_rows, int slot_tt) {
+__device__ __forceinline__ XtReads<T, D> make_xt_reads(int lane, int slot_rows) {
   if constexpr (sizeof(T) == 2) return TrReads<D>(lane, slot_rows);
-  else return TtReads<D>(lane & 31, lane >> 5, slot_tt);
+  else return Rt32Reads(lane, slot_rows);
 }
 
 template <typename T, int D>
 __device__ __forceinline__ void acc_rows_product_any(const T* X, const XtReads<T, D>& rd, const floatx16& p,
                                                      floatx16 (&out)[D / 32]) {
   if constexpr (sizeof(T) == 2) acc_rows_product_tr<D, std::is_same_v<T, bf16>>(X, rd, p, out);
-  else acc_rows_product_tt<D>(X, rd, p, out);
+  else acc_rows_product_rt32<D>(X, rd, p, out);
 }
 
 using I0 = std::integral_constant<int, 0>;
@@ -990,20 +956,16 @@ constexpr float kRescaleSlack = 8.f;
 template <typename T, int D>
 __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(const AttnDmaArgs a) {
   using RT = RowTile<T, D>;
-  using TT = TrTile<float, (sizeof(T) == 4 ? D : 64)>;
   using E = AttnElem<T>;
   constexpr int W = AttnSplit<T>::FWD_W, NS = AttnSplit<T>::FWD_NS;
-  // fp16 stages V as a row tile and reads V^T out of it; fp32 stages V^T
-  constexpr bool TR = sizeof(T) == 2;
-  constexpr int VE = TR ? RT::ELEMS : TT::ELEMS;
-  constexpr int VNI = TR ? RT::NI : TT::NI;
+  // V is staged as a row tile and V^T read out of it
+  constexpr int VE = RT::ELEMS, VNI = RT::NI;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   auto sK = [](auto S) { return att_lds<T, 2 * decltype(S)::value, W * RT::ELEMS>(); };
   auto sV = [](auto S) { return att_lds<T, 2 * decltype(S)::value + 1, W * VE>(); };
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
   const T* v = (const T*)a.v;
-  const T* vT = (const T*)a.vT;
   const int G = a.heads / a.kv_heads, h = blockIdx.y, grp = h / G, b = blockIdx.z;
   const int S = a.seq;
   // Z workgroups share a tile pair, split z taking the key tiles
@@ -1024,10 +986,8 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
     const int qi = q0 + i;
 
     const RowReads<T, D> rk(i, kh, w * RT::ELEMS);
-    const XtReads<T, D> rv = make_xt_reads<T, D>(lane, w * RT::ELEMS, w * VE);
-    const RowCopy<T, D> ck(lane, a.ldk);
-    using VCopy = std::conditional_t<TR, RowCopy<T, D>, TrCopy<(TR ? 64 : D)>>;
-    const VCopy cv(lane, TR ? a.ldv : a.ldt);
+    const XtReads<T, D> rv = make_xt_reads<T, D>(lane, w * VE);
+    const RowCopy<T, D> ck(lane, a.ldk), cv(lane, a.ldv);
 
     typename E::Chunk qc[RT::STEPS];
     load_row_frags<T, D>(q + (tok0 + min(qi, S - 1)) * a.ldq + (int64_t)h * D, kh, qc);
@@ -1043,8 +1003,7 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
     auto issue = [&](int t, T* sk, T* sv) __attribute__((always_inline)) {
       const int kv0 = (w0 + WZ * t) * 32;
       copy_row_tile<T, D>(sk + w * RT::ELEMS, k, a.ldk, tok0, kv0, S, grp * D, ck, lane);
-      if constexpr (TR) copy_row_tile<T, D>(sv + w * VE, v, a.ldv, tok0, kv0, S, grp * D, cv, lane);
-      else copy_tr_tile<D>(sv + w * VE, vT, a.ldt, tok0, kv0, S, grp * D, cv, lane);
+      copy_row_tile<T, D>(sv + w * VE, v, a.ldv, tok0, kv0, S, grp * D, cv, lane);
     };
     auto compute = [&](const T* sk, const T* sv, int t) __attribute__((always_inline)) {
       const int kv0 = (w0 + WZ * t) * 32;
@@ -1153,26 +1112,21 @@ __global__ __launch_bounds__(AttnSplit<T>::FWD_W * 64) void attn_dma_fwd_kernel(
 }
 
 // dQ: grid (pairs of q tiles, heads, batch); the W waves take key tiles w, w+W, ...
-// (K, V and, in fp32, K^T through private LDS stages); wave 0 sums the
-// partial dQ in wave order and writes it. Only the diagonal tile is masked.
+// (K and V through private LDS stages, K^T read out of the K row tile); the
+// waves' partial dQ blocks are summed in wave order and written. Only the
+// diagonal tile is masked.
 template <typename T, int D>
 __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(const AttnDmaArgs a,
                                                                              float* delta) {
   using RT = RowTile<T, D>;
-  using TT = TrTile<float, (sizeof(T) == 4 ? D : 64)>;
   using E = AttnElem<T>;
   constexpr int W = AttnSplit<T>::DQ_W, NS = AttnSplit<T>::DQ_NS;
-  // fp16 reads K^T out of the K row tile; fp32 stages K^T too
-  constexpr bool TR = sizeof(T) == 2;
-  constexpr int KTE = TR ? 16 : TT::ELEMS;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   auto sK = [](auto S) { return att_lds<T, 3 * decltype(S)::value, W * RT::ELEMS>(); };
   auto sV = [](auto S) { return att_lds<T, 3 * decltype(S)::value + 1, W * RT::ELEMS>(); };
-  auto sKt = [](auto S) { return att_lds<T, 3 * decltype(S)::value + 2, W * KTE>(); };
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
   const T* v = (const T*)a.v;
-  const T* kT = (const T*)a.kT;
   const T* d_o = (const T*)a.d_o;
   const int G = a.heads / a.kv_heads, h = blockIdx.y, grp = h / G, b = blockIdx.z;
   const int S = a.seq;
@@ -1193,7 +1147,7 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
     const int qi = q0 + i, qc_i = min(qi, S - 1);
 
     const RowReads<T, D> rr(i, kh, w * RT::ELEMS);
-    const XtReads<T, D> rkt = make_xt_reads<T, D>(lane, w * RT::ELEMS, w * KTE);
+    const XtReads<T, D> rkt = make_xt_reads<T, D>(lane, w * RT::ELEMS);
     const RowCopy<T, D> ck(lane, a.ldk), cv(lane, a.ldv);
 
     typename E::Chunk qc[RT::STEPS], dc[RT::STEPS];
@@ -1240,16 +1194,12 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
     const int w0 = z * W + w, WZ = W * Z;  // first key tile and stride of this wave
     const int n = w0 <= qt ? (qt - w0) / WZ + 1 : 0;
 
-    auto issue = [&](int t, T* sk, T* sv, T* skt) __attribute__((always_inline)) {
+    auto issue = [&](int t, T* sk, T* sv) __attribute__((always_inline)) {
       const int kv0 = (w0 + WZ * t) * 32;
       copy_row_tile<T, D>(sk + w * RT::ELEMS, k, a.ldk, tok0, kv0, S, grp * D, ck, lane);
       copy_row_tile<T, D>(sv + w * RT::ELEMS, v, a.ldv, tok0, kv0, S, grp * D, cv, lane);
-      if constexpr (!TR) {
-        const TrCopy<D> ckt(lane, a.ldt);
-        copy_tr_tile<D>(skt + w * KTE, kT, a.ldt, tok0, kv0, S, grp * D, ckt, lane);
-      }
     };
-    auto compute = [&](const T* sk, const T* sv, const T* skt, int t) __attribute__((always_inline)) {
+    auto compute = [&](const T* sk, const T* sv, int t) __attribute__((always_inline)) {
       const int kv0 = (w0 + WZ * t) * 32;
       floatx16 s, dp;
 #pragma unroll
@@ -1276,13 +1226,11 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] = exp2_hw(fmaf(s[e], sc, -lse2)) * (dp[e] - dl);
       }
-      if constexpr (TR) acc_rows_product_any<T, D>(sk, rkt, s, dq);
-      else acc_rows_product_any<T, D>(skt, rkt, s, dq);
+      acc_rows_product_any<T, D>(sk, rkt, s, dq);
     };
     wave_ring<NS>(
-        n, 2 * RT::NI + (TR ? 0 : TT::NI),
-        [&](int t, auto St) __attribute__((always_inline)) { issue(t, sK(St), sV(St), sKt(St)); }, [](int) {},
-        [&](int t, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), sKt(St), t); });
+        n, 2 * RT::NI, [&](int t, auto St) __attribute__((always_inline)) { issue(t, sK(St), sV(St)); },
+        [](int) {}, [&](int t, auto St) __attribute__((always_inline)) { compute(sK(St), sV(St), t); });
 
     // one exchange: each wave adds the blocks it owns in wave order and
     // writes them
@@ -1312,8 +1260,8 @@ __global__ __launch_bounds__(AttnSplit<T>::DQ_W * 64) void attn_dma_dq_kernel(co
 }
 
 // dK, dV per query head: grid (pairs of kv tiles, heads, batch); the W waves take
-// query tiles kt+w, kt+w+W, ... (Q, dO and, in fp32, their transposes
-// through private LDS stages); wave 0 sums the partials in wave order into
+// query tiles kt+w, kt+w+W, ... (Q and dO through private LDS stages, Q^T
+// and dO^T read out of those row tiles); the partials are summed in wave order into
 // per-head buffers [T, heads, D], summed over each group afterwards. Masks
 // apply only on the diagonal tile and on a query tile that runs past the
 // end of the sequence.
@@ -1322,23 +1270,15 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
                                                                                const float* delta,
                                                                                float* dk_part, float* dv_part) {
   using RT = RowTile<T, D>;
-  using TT = TrTile<float, (sizeof(T) == 4 ? D : 64)>;
   using E = AttnElem<T>;
   constexpr int W = AttnSplit<T>::DKV_W, NS = AttnSplit<T>::DKV_NS;
-  // fp16 reads Q^T and dO^T out of the row tiles; fp32 stages them too
-  constexpr bool TR = sizeof(T) == 2;
-  constexpr int XTE = TR ? 16 : TT::ELEMS;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   auto sQ = [](auto S) { return att_lds<T, 4 * decltype(S)::value, W * RT::ELEMS>(); };
   auto sO = [](auto S) { return att_lds<T, 4 * decltype(S)::value + 1, W * RT::ELEMS>(); };
-  auto sQt = [](auto S) { return att_lds<T, 4 * decltype(S)::value + 2, W * XTE>(); };
-  auto sOt = [](auto S) { return att_lds<T, 4 * decltype(S)::value + 3, W * XTE>(); };
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
   const T* v = (const T*)a.v;
-  const T* qT = (const T*)a.qT;
   const T* d_o = (const T*)a.d_o;
-  const T* doT = (const T*)a.doT;
   const int h = blockIdx.y, b = blockIdx.z;
   const int G = a.heads / a.kv_heads, grp = h / G;
   const int S = a.seq;
@@ -1360,7 +1300,7 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
     const int kj = kv0 + i;  // this lane's key (column of every accumulator)
 
     const RowReads<T, D> rr(i, kh, w * RT::ELEMS);
-    const XtReads<T, D> rxt = make_xt_reads<T, D>(lane, w * RT::ELEMS, w * XTE);
+    const XtReads<T, D> rxt = make_xt_reads<T, D>(lane, w * RT::ELEMS);
     const RowCopy<T, D> cq(lane, a.ldq), co(lane, a.lddo);
 
     typename E::Chunk kc[RT::STEPS], vc[RT::STEPS];
@@ -1384,15 +1324,10 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
     const int n = kt + w0 < nqt ? (nqt - 1 - kt - w0) / WZ + 1 : 0;  // query tiles kt+w0, kt+w0+WZ, ..
     auto qtile = [&](int t) { return kt + w0 + WZ * t; };
 
-    auto issue = [&](int t, T* sq, T* so, T* sqt, T* sot) __attribute__((always_inline)) {
+    auto issue = [&](int t, T* sq, T* so) __attribute__((always_inline)) {
       const int q0 = qtile(t) * 32;
       copy_row_tile<T, D>(sq + w * RT::ELEMS, q, a.ldq, tok0, q0, S, h * D, cq, lane);
       copy_row_tile<T, D>(so + w * RT::ELEMS, d_o, a.lddo, tok0, q0, S, h * D, co, lane);
-      if constexpr (!TR) {
-        const TrCopy<D> ct(lane, a.ldt);
-        copy_tr_tile<D>(sqt + w * XTE, qT, a.ldt, tok0, q0, S, h * D, ct, lane);
-        copy_tr_tile<D>(sot + w * XTE, doT, a.ldt, tok0, q0, S, h * D, ct, lane);
-      }
     };
     // log-sum-exp (in powers of two) and delta of this lane's 16 query rows
     // q0 + 8g + 4kh + r of the next query tile, loaded one step ahead and
@@ -1408,7 +1343,7 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
         Dl[g] = qr < S ? *(const float4*)(dl_h + qr) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     };
-    auto compute = [&](const T* sq, const T* so, const T* sqt, const T* sot, int t) __attribute__((always_inline)) {
+    auto compute = [&](const T* sq, const T* so, int t) __attribute__((always_inline)) {
       const int q0 = qtile(t) * 32;
       floatx16 s, dp;
 #pragma unroll
@@ -1440,18 +1375,12 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
       };
       if (q0 == kv0 || q0 + 32 > S) sm(std::true_type{});
       else sm(std::false_type{});
-      if constexpr (TR) {
-        acc_rows_product_any<T, D>(so, rxt, s, dv);   // dV^T += dO^T P
-        acc_rows_product_any<T, D>(sq, rxt, dp, dk);  // dK^T += Q^T dS
-      } else {
-        acc_rows_product_any<T, D>(sot, rxt, s, dv);
-        acc_rows_product_any<T, D>(sqt, rxt, dp, dk);
-      }
+      acc_rows_product_any<T, D>(so, rxt, s, dv);   // dV^T += dO^T P
+      acc_rows_product_any<T, D>(sq, rxt, dp, dk);  // dK^T += Q^T dS
     };
     if (n > 0) load_ld(0, lq_n, dq4_n);
     wave_ring<NS>(
-        n, 2 * RT::NI + (TR ? 0 : 2 * TT::NI),
-        [&](int t, auto St) __attribute__((always_inline)) { issue(t, sQ(St), sO(St), sQt(St), sOt(St)); },
+        n, 2 * RT::NI, [&](int t, auto St) __attribute__((always_inline)) { issue(t, sQ(St), sO(St)); },
         [&](int t) __attribute__((always_inline)) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -1460,7 +1389,7 @@ __global__ __launch_bounds__(AttnSplit<T>::DKV_W * 64) void attn_dma_dkv_kernel(
           }
           if (t + 1 < n) load_ld(t + 1, lq_n, dq4_n);
         },
-        [&](int t, auto St) __attribute__((always_inline)) { compute(sQ(St), sO(St), sQt(St), sOt(St), t); });
+        [&](int t, auto St) __attribute__((always_inline)) { compute(sQ(St), sO(St), t); });
 
     // one exchange over the 2 NB blocks (dK's, then dV's): each wave adds
     // the blocks it owns in wave order and writes them
@@ -2299,10 +2228,9 @@ static int check_dma(const AttnDmaArgs& a) {
   QBLK_TRY(attention_check(a.batch, a.seq, a.heads, a.kv_heads, a.head_dim));
   if (!attention_dma_supported(a.batch, a.seq, a.heads, a.kv_heads, a.head_dim))
     return fail(QBLK_EUNSUPPORTED, "attention (tiled copies): head_dim must be 64 or 128 and seq a multiple of 8");
-  const int64_t T = (int64_t)a.batch * a.seq;
-  if (a.ldt != T || a.ldq % 8 || a.ldk % 8 || a.ldv % 8 || a.ldo % 4)
-    return fail(QBLK_EINVAL, "attention (tiled copies): strides (ldt must be T; row strides multiples of 8)");
-  const void* ptrs[] = {a.q, a.k, a.fp32 ? a.vT : a.v, a.o, a.lse};
+  if (a.ldq % 8 || a.ldk % 8 || a.ldv % 8 || a.ldo % 4)
+    return fail(QBLK_EINVAL, "attention (tiled copies): row strides must be multiples of 8 (o: 4)");
+  const void* ptrs[] = {a.q, a.k, a.v, a.o, a.lse};
   for (const void* p : ptrs)
     if (!p || ((uintptr_t)p & 15)) return fail(QBLK_EINVAL, "attention (tiled copies): null or misaligned pointer");
   return 0;
@@ -2326,8 +2254,6 @@ int attention_dma_backward(const AttnDmaArgs& a, void* scratch, hipStream_t st) 
   const void* ptrs[] = {a.v, a.d_o, a.do32, a.dq, a.dk, a.dv, scratch};
   for (const void* p : ptrs)
     if (!p || ((uintptr_t)p & 15)) return fail(QBLK_EINVAL, "attention backward (tiled copies): null or misaligned pointer");
-  if (a.fp32 && (!a.qT || !a.kT || !a.doT))
-    return fail(QBLK_EINVAL, "attention backward (tiled copies): fp32 needs the transposed copies");
   if (a.lddo % 8 || a.lddo32 % 4 || a.lddq % 4 || a.lddk % 4 || a.lddv % 4)
     return fail(QBLK_EINVAL, "attention backward (tiled copies): row strides");
   const int64_t T = (int64_t)a.batch * a.seq;

@@ -25,11 +25,10 @@ struct Saved {
   float* n2;       // [T, h]
   float* gu;       // [T, 2I] gate | up
   float* s;        // [T, I] SwiGLU output
-  // Attention on tiled copies (when use_attention_dma): fp16 copies of the
-  // attention inputs (fp16-operand configs), or fp32 transposed copies
-  // (fp32 configs); NULL otherwise.
+  // Attention on tiled copies (when use_attention_dma) with 16-bit
+  // operands: 16-bit copies of the attention inputs; NULL otherwise (fp32
+  // configs read the fp32 tensors themselves).
   f16 *q16, *k16, *v16;
-  float *qT32, *kT32, *vT32;
   // fp16 copies of the projection inputs n1, o, n2, s (fp16-operand configs
   // with T a multiple of 8), written by their producers; NULL otherwise.
   f16 *n1_16, *o16, *n2_16, *s16;
@@ -62,7 +61,6 @@ struct Scratch {
   f16* a16;  // fp16 copy of the current output gradient
   Packed16 pack;
   f16* do16;          // attention on tiled copies: dO copy (fp16 configs)
-  float* doT32;       // attention on tiled copies: dO transposed (fp32 configs)
   // Set by the fp16-copies backward: producers write each output gradient's
   // fp16 copy straight into a16 and the projection hooks are then passed a
   // null fp32 gradient (the copy is already in a16).

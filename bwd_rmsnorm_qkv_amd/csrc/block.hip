@@ -64,15 +64,10 @@ void carve_saved(const qblk_config& c, void* base, Saved& s, size_t& bytes) {
     s.s16 = cv.take<f16>(T * I);
   }
   s.q16 = s.k16 = s.v16 = nullptr;
-  s.qT32 = s.kT32 = s.vT32 = nullptr;
   if (use_attention_dma(c) && c.gemm_precision != 0) {
     s.q16 = cv.take<f16>(T * qd);
     s.k16 = cv.take<f16>(T * kvd);
     s.v16 = cv.take<f16>(T * kvd);
-  } else if (use_attention_dma(c)) {
-    s.qT32 = cv.take<float>(T * qd);
-    s.kT32 = cv.take<float>(T * kvd);
-    s.vT32 = cv.take<float>(T * kvd);
   }
   bytes = cv.off;
 }
@@ -154,12 +149,7 @@ void carve_scratch(const qblk_config& c, void* base, Scratch& s, size_t& bytes, 
   s.a16 = nullptr;
   s.pack = Packed16{};
   s.do16 = nullptr;
-  s.doT32 = nullptr;
-  if (use_attention_dma(c) && c.gemm_precision != 0) {
-    s.do16 = cv.take<f16>(T * qd);
-  } else if (use_attention_dma(c)) {
-    s.doT32 = cv.take<float>(T * qd);
-  }
+  if (use_attention_dma(c) && c.gemm_precision != 0) s.do16 = cv.take<f16>(T * qd);
   if (c.gemm_precision != 0 && (lora_rank == 0 || T % 8 == 0))
     s.a16 = cv.take<f16>(T * std::max({qd + 2 * kvd, 2 * I, h, qd}));
   if (c.gemm_precision != 0 && lora_rank == 0) {
@@ -240,14 +230,12 @@ AttnDmaArgs attn_dma_args(const qblk_config& c, const Saved& s) {
     a.q = s.q16; a.ldq = qd;
     a.k = s.k16; a.ldk = kvd;
     a.v = s.v16; a.ldv = kvd;
-  } else {  // fp32: the tensors themselves plus transposed copies
+  } else {  // fp32: the tensors themselves
     a.fp32 = 1;
     a.q = s.qr; a.ldq = qd;
     a.k = s.kr; a.ldk = kvd;
     a.v = s.qkv + qd + kvd; a.ldv = qd + 2 * kvd;
-    a.qT = s.qT32; a.kT = s.kT32; a.vT = s.vT32;
   }
-  a.ldt = T;
   a.bf16 = bf(c);
   a.o = s.o; a.ldo = qd;
   a.lse = s.lse;
@@ -279,12 +267,7 @@ int block_forward_impl(const qblk_config& c, const ProjFwd& proj, const float* g
     qa.qr = qa.kr = nullptr;
   }
   QBLK_TRY(qk_norm_rope_forward(qa, st));
-  if (s.q16 || s.qT32) {
-    if (!s.q16) {
-      QBLK_TRY(transpose_f32(T, qd, s.qr, qd, s.qT32, T, st));
-      QBLK_TRY(transpose_f32(T, kvd, s.kr, kvd, s.kT32, T, st));
-      QBLK_TRY(transpose_f32(T, kvd, s.qkv + qd + kvd, ldqkv, s.vT32, T, st));
-    }
+  if (use_attention_dma(c)) {
     AttnDmaArgs af = attn_dma_args(c, s);
     af.o16 = s.o16;
     QBLK_TRY(attention_dma_forward(af, attn_ws, st));
@@ -333,14 +316,13 @@ int block_backward_impl(const qblk_config& c, const ProjBwd& proj, const float* 
   // O projection
   QBLK_TRY(proj.o(p16 ? nullptr : w.dr1, s.o, w.d_o, st));
   // attention backward: dq, dk at the attention inputs; dv straight into dqkv
-  if (s.q16 || s.qT32) {
+  if (use_attention_dma(c)) {
     AttnDmaArgs ab = attn_dma_args(c, s);
     if (s.q16) {
       if (!p16) QBLK_TRY(cast_f16(T, qd, w.d_o, qd, w.do16, qd, nullptr, 0, st, bf(c)));
       ab.d_o = w.do16;
     } else {
-      QBLK_TRY(transpose_f32(T, qd, w.d_o, qd, w.doT32, T, st));
-      ab.d_o = w.d_o; ab.doT = w.doT32;
+      ab.d_o = w.d_o;
     }
     ab.lddo = qd;
     ab.do32 = w.d_o; ab.lddo32 = qd;

@@ -64,52 +64,8 @@ __global__ __launch_bounds__(256) void cast_f16_rows_kernel(int R, int C, const 
     *(half4*)(out + (int64_t)r * ldo + j) = to_16x4(*(const float4*)(in + (int64_t)r * ldi + j), bf16);
 }
 
-// fp32 transpose through the same 64 x 64 LDS tile.
-__global__ __launch_bounds__(256) void transpose_f32_kernel(int R, int C, const float* __restrict__ in, int64_t ldi,
-                                                            float* __restrict__ outT, int64_t ldt) {
-  __shared__ float tile[64][65];
-  const int t = threadIdx.x;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int lc = (t & 15) * 4;
-  const int col = c0 + lc;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int lr = p * 16 + (t >> 4);
-    const int row = r0 + lr;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row < R && col < C) v = *(const float4*)(in + (int64_t)row * ldi + col);
-    tile[lr][lc] = v.x;
-    tile[lr][lc + 1] = v.y;
-    tile[lr][lc + 2] = v.z;
-    tile[lr][lc + 3] = v.w;
-  }
-  __syncthreads();
-  const int lr = (t & 15) * 4;
-  const int row = r0 + lr;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int lcc = p * 16 + (t >> 4);
-    const int c = c0 + lcc;
-    if (c >= C) continue;
-    float* dst = outT + (int64_t)c * ldt + row;
-    if (row + 3 < R) {
-      *(float4*)dst = make_float4(tile[lr][lcc], tile[lr + 1][lcc], tile[lr + 2][lcc], tile[lr + 3][lcc]);
-    } else {
-      for (int j = 0; j < 4 && row + j < R; ++j) dst[j] = tile[lr + j][lcc];
-    }
-  }
-}
-
 }  // namespace
 
-int transpose_f32(int R, int C, const float* in, int64_t ldi, float* outT, int64_t ldt, hipStream_t st) {
-  if (R <= 0 || C <= 0) return fail(QBLK_EINVAL, "transpose_f32: bad shape %d x %d", R, C);
-  if (C % 4 || ldi % 4 || ldt % 4) return fail(QBLK_EINVAL, "transpose_f32: columns and strides must be multiples of 4");
-  if (!in || !outT) return fail(QBLK_EINVAL, "transpose_f32: null pointer");
-  const dim3 grid((unsigned)ceil_div(C, 64), (unsigned)ceil_div(R, 64));
-  hipLaunchKernelGGL(transpose_f32_kernel, grid, dim3(256), 0, st, R, C, in, ldi, outT, ldt);
-  return check_launch("transpose_f32_kernel");
-}
 
 int cast_f16(int R, int C, const float* in, int64_t ldi, f16* out, int64_t ldo, f16* outT, int64_t ldt,
              hipStream_t st, bool bf16) {

@@ -111,7 +111,5 @@ int swiglu_backward(int T, int I, const float* gu, const float* ds, float* dgu, 
 // C and every stride must be multiples of 4.
 int cast_f16(int R, int C, const float* in, int64_t ldi, f16* out, int64_t ldo, f16* outT, int64_t ldt,
              hipStream_t st, bool bf16 = false);
-// outT [C, R] (stride ldt) = transpose of in [R, C] (stride ldi), fp32.
-int transpose_f32(int R, int C, const float* in, int64_t ldi, float* outT, int64_t ldt, hipStream_t st);
 
 }  // namespace qblk
