@@ -870,8 +870,7 @@ __device__ __forceinline__ void wave_ring(int n, int per_tile, Issue&& issue, Pr
 // between them, each with private stages, and combine at the end.
 template <typename T>
 struct AttnSplit {
-  static constexpr bool F16 = sizeof(T) == 2;
-  static constexpr int FWD_W = 4, DQ_W = F16 ? 4 : 2, DKV_W = F16 ? 4 : 2;
+  static constexpr int FWD_W = 4, DQ_W = 4, DKV_W = 4;
   static constexpr int FWD_NS = 2, DQ_NS = 2, DKV_NS = 2;
 };
 
