@@ -23,6 +23,10 @@ struct AttnArgs {
 int attention_check(int batch, int seq, int heads, int kv_heads, int head_dim);
 size_t attention_bwd_scratch(int batch, int seq, int heads, int head_dim);
 int attention_kv_split(int batch, int seq, int heads);
+// Whether the per-head kernels take one tile per 2-wave workgroup instead of
+// causal tile pairs (16-bit operands, no key-range split, at least two
+// (tile, head) units per CU).
+bool attention_unpaired(int batch, int seq, int heads, bool sixteen_bit);
 int attention_group_waves(int batch, int seq, int heads, int kv_heads);
 int attention_forward(const AttnArgs& a, Prec p, hipStream_t st);
 int attention_backward(const AttnArgs& a, Prec p, void* scratch, hipStream_t st);

@@ -217,12 +217,18 @@ ATTN16_SHAPES = [  # batch, seq, heads, kv_heads, head_dim: fp16 copies, direct-
     (3, 40, 8, 8, 128),     # G = 1, ragged, batch > 1
     (1, 512, 32, 8, 128),   # the Qwen3-4B-shaped attention
     (1, 64, 8, 1, 64),      # G = 8: two dQ workgroups per group
+    (1, 640, 24, 24, 64),   # tile pairs without a key-range split
     (2, 48, 12, 2, 64),     # G = 6: dQ workgroups of 3 waves
     # tile pairs x KV heads x batch >= 128: the forward shares each K/V tile
     # among the G query heads of its group (one wave per head)
     (1, 1024, 32, 8, 128),  # G = 4
     (2, 1024, 16, 8, 64),   # G = 2, batch > 1
     (1, 1000, 64, 8, 64),   # G = 8, ragged last tile
+    # (tile, head) units >= 512, one key-range split, no group kernel: one
+    # tile per 2-wave workgroup instead of causal tile pairs
+    (1, 504, 32, 8, 64),    # G = 4, ragged last tile
+    (2, 328, 24, 24, 128),  # G = 1, ragged, batch > 1
+    (1, 1024, 16, 2, 64),   # G = 8
 ]
 
 
