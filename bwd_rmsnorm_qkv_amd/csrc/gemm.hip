@@ -1235,9 +1235,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
 // table maps a code byte to its two levels as an fp16 pair, which one
 // packed fp16 multiply scales by the block's scale (rounded to fp16): one
 // table read and one multiply per two weights. The codes are 4x smaller
-// than an fp16 copy, so B's traffic drops by 4x; A and the MFMA loop are
-// those of gemm_dma_kernel (128 x 128 tiles, 4 waves, two workgroups per
-// CU, two stages per operand).
+// than an fp16 copy, so B's traffic drops by 4x; A and the MFMA loop follow
+// gemm_dma_kernel's (here 128 x 128 tiles of 4 waves, two workgroups per
+// CU, two stages per operand, or the 256 x 256 tiles below).
 //
 // LoRA rides as one more K tile after the NF4 ones: A from ext16_a
 // ([M, 64] fp16, DMA), B from ext16_b (fp16, copied to LDS as it is).
@@ -2042,14 +2042,20 @@ struct DmaCfg {
     }
   }
 };
-// 128 x 128 tiles, 4 waves, two workgroups per CU (80 KB LDS each: two A
-// stages, three B stages), or, when the grid leaves one workgroup per CU,
-// three stages of each (96 KB: one wave per SIMD has no other wave to hide
-// the copies' latency behind, so they run a tile further ahead); and
-// 256 x 256 tiles, 8 waves of 64 x 128, one workgroup per CU (the
-// ping-pong kernel).
-using Nt16Small = DmaCfg<128, 128, 2, 2, 2, 3>;
-using Nt16Deep = DmaCfg<128, 128, 2, 2, 3, 3>;
+// 128 x 128 tiles, 8 waves of 32 x 64, two workgroups per CU (80 KB LDS
+// each: two A stages, three B stages), or, when the grid leaves one
+// workgroup per CU, three stages of each (96 KB: the copies run a tile
+// further ahead); and 256 x 256 tiles, 8 waves of 64 x 128, one workgroup
+// per CU (the ping-pong kernel). A wave streams its share of a tile's
+// copies at a bounded rate (global->LDS probes: about 10 B/clk per CU with
+// 4 copying waves, 21 B/clk with 8 or more), so 8 waves of 32 x 64 fill
+// the 128 x 128 tiles faster than 4 of 64 x 64, which their twice as many
+// fragment reads per MFMA do not cost back (the Qwen3-4B block step at seq
+// 512 ≈ 1 % faster, the NF4 block ≈ 1.7 %). The fp8 products keep 4 waves
+// of 64 x 64 (F8Cfg), as measured.
+using Nt16Small = DmaCfg<128, 128, 4, 2, 2, 3>;
+using Nt16Deep = DmaCfg<128, 128, 4, 2, 3, 3>;
+using F8Cfg = DmaCfg<128, 128, 2, 2, 2, 3>;
 using Nt16Big = PpCfg;
 
 // Big tiles pay off once they alone give at least half the CUs a tile.
@@ -2265,10 +2271,10 @@ GemmDesc f8_units(const GemmDesc& d) {
 
 int launch_f8(const GemmDesc& d, hipStream_t st) {
   const GemmDesc u = f8_units(d);
-  Grid g = plan_tiles(u, u.ws ? u.ws_bytes : 0, Nt16Small::bm, Nt16Small::bn, 64, -2 * kTargetWgs);
-  g.bn = Nt16Small::bn;
+  Grid g = plan_tiles(u, u.ws ? u.ws_bytes : 0, F8Cfg::bm, F8Cfg::bn, 64, -2 * kTargetWgs);
+  g.bn = F8Cfg::bn;
   g.vec = out_vec4(u, g);
-  Nt16Small::launch8(u, g, st);
+  F8Cfg::launch8(u, g, st);
   QBLK_TRY(check_launch("gemm_dma_kernel (fp8)"));
   return finish_splits(u, g, st);
 }
@@ -2409,7 +2415,7 @@ size_t gemm_nf4_workspace(int M, int N, int k_total) {
 
 size_t gemm_workspace(const GemmDesc& d) {
   if (d.prec == Prec::FP8) {
-    const Grid g = plan_tiles(f8_units(d), (size_t)-1, Nt16Small::bm, Nt16Small::bn, 64, -2 * kTargetWgs);
+    const Grid g = plan_tiles(f8_units(d), (size_t)-1, F8Cfg::bm, F8Cfg::bn, 64, -2 * kTargetWgs);
     return g.splits > 1 ? (size_t)g.splits * d.M * d.N * sizeof(float) : 0;
   }
   const Grid g = nf4_fused_ok(d) ? plan_nf4(d, (size_t)-1) : plan(d, (size_t)-1);
