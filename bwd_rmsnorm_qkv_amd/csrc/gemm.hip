@@ -926,8 +926,23 @@ __device__ __forceinline__ floatx16 mfma8(half8 a0, half8 a1, half8 b0, half8 b1
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
+// fp32 operands over 8 K (in the 16-bit staging: one K step of 16 units):
+// the lane's 16 bytes of A and of B hold 4 fp32 K values each, in the same
+// arrangement for both (lane half kh: K 4 kh .. 4 kh + 3 of the step), so
+// four v_mfma_f32_32x32x2_f32 with the j-th value of each lane (K pairs
+// (j, 4 + j) across the two halves) give the block product over those 8 K.
+__device__ __forceinline__ floatx16 mfma32x4(half8 a, half8 b, floatx16 c) {
+  const float4 x = __builtin_bit_cast(float4, a), y = __builtin_bit_cast(float4, b);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y.z, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y.w, c, 0, 0, 0);
+}
+
 // EK: operand kind. 0 fp16, 1 bfloat16 (16-bit elements, K tiles of 64);
-// 2 + fa + 2 fb: fp8 with A format fa and B format fb (0 E4M3, 1 E5M2).
+// 2 + fa + 2 fb: fp8 with A format fa and B format fb (0 E4M3, 1 E5M2);
+// 6: fp32 (NT; the descriptor in 16-bit units like fp8's: K, lda, ldb and
+// the split-K chunk doubled, a K tile then 32 fp32 values).
 // The fp8 kernels take the descriptor in 16-bit units (K, lda, ldb and
 // the split-K chunk halved: two fp8 values per unit), so staging, copies
 // and fragment reads are those of the 16-bit kernel; a K tile then holds
@@ -935,9 +950,10 @@ __device__ __forceinline__ floatx16 mfma8(half8 a0, half8 a1, half8 b0, half8 b1
 // the fragments of two 16-bit K steps.
 template <int BM, int BN, int WM, int WN, int NS, int NB, bool AK, bool BK_, int EK>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d, const Grid gd) {
-  constexpr bool BF = EK == 1, F8 = EK >= 2;
+  constexpr bool BF = EK == 1, F8 = EK >= 2 && EK <= 5, F32 = EK == 6;
   constexpr int FA = F8 ? (EK - 2) & 1 : 0, FB = F8 ? (EK - 2) >> 1 : 0;
   static_assert(!F8 || (AK && BK_), "fp8 operands: both K-major (NT)");
+  static_assert(!F32 || (AK && BK_), "fp32 operands: both K-major (NT)");
   constexpr int BK = 64;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
@@ -1045,7 +1061,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, TM * TN>([&](auto Jx) __attribute__((always_inline)) {
         constexpr int j = decltype(Jx)::value, tm = j / TN, tn = j % TN, i = s * TM * TN + j;
-        acc[tm][tn] = mfma16<BF>(av[s & 1][tm], bv[s & 1][tn], acc[tm][tn]);
+        if constexpr (F32)
+          acc[tm][tn] = mfma32x4(av[s & 1][tm], bv[s & 1][tn], acc[tm][tn]);
+        else
+          acc[tm][tn] = mfma16<BF>(av[s & 1][tm], bv[s & 1][tn], acc[tm][tn]);
         static_for<(i * NC) / NM, ((i + 1) * NC) / NM>([&](auto Cx) __attribute__((always_inline)) {
           constexpr int c = decltype(Cx)::value;
           if constexpr (c < OA::J) {
@@ -2026,6 +2045,12 @@ struct DmaCfg {
     hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, true, true, EK>), dim3(nwg), dim3(threads), 0, st, d,
                        g);
   }
+  // fp32 operands (NT), the descriptor in 16-bit units
+  static void launch32(const GemmDesc& d, const Grid& g, hipStream_t st) {
+    const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, true, true, 6>), dim3(nwg), dim3(threads), 0, st, d,
+                       g);
+  }
   static void launch8(const GemmDesc& d, const Grid& g, hipStream_t st) {
     switch (d.f8_a_e5m2 + 2 * d.f8_b_e5m2) {
       case 0: launch8<2>(d, g, st); break;
@@ -2279,6 +2304,49 @@ int launch_f8(const GemmDesc& d, hipStream_t st) {
   return finish_splits(u, g, st);
 }
 
+// fp32 NT products on the direct-to-LDS kernel: K a multiple of 32, lda and
+// ldb multiples of 4, 16-byte aligned rows, no K extension, and at least
+// 128 output tiles of 128 x 128 (half the CUs busy without splitting K).
+// The descriptor goes over in 16-bit units (K, lda, ldb doubled), so tiles,
+// copies and fragment reads are the 16-bit kernel's; each 16-byte fragment
+// holds 4 fp32 K values. Measured against the register-staged kernel: the
+// vocabulary-151936 LM head (1024 x 151936 x 512) 1.47 -> 1.28 ms, 1024 x
+// 2816 x 512 37-40 -> 35 us; products with fewer tiles (1024 x 768 x 512:
+// 48 tiles, 19 -> 25 us) stay on the register kernel's 64-wide tiles.
+bool f32nt_ok(const GemmDesc& d) {
+  if (d.prec != Prec::F32 || d.layout != Layout::NT || d.a_src != Src::F32 || d.b_src != Src::F32) return false;
+  if (d.ext.kext > 0 || d.K % 32 != 0 || d.K == 0 || d.lda % 4 != 0 || d.ldb % 4 != 0) return false;
+  if ((uintptr_t)d.a % 16 != 0) return false;
+  for (int s = 0; s < d.b.nseg; ++s)
+    if ((uintptr_t)d.b.p[s] % 16 != 0) return false;
+  return ceil_div(d.M, Nt16Small::bm) * ceil_div(d.N, Nt16Small::bn) >= 128;
+}
+
+GemmDesc f32_units(const GemmDesc& d) {
+  GemmDesc u = d;
+  u.K = 2 * d.K;
+  u.lda = 2 * d.lda;
+  u.ldb = 2 * d.ldb;
+  return u;
+}
+
+Grid plan_f32nt(const GemmDesc& u, size_t ws_bytes) {
+  Grid g = plan_tiles(u, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64, -kTargetWgs);
+  g.bn = Nt16Small::bn;
+  g.deep = g.tiles_m * g.tiles_n * g.splits <= kTargetWgs;
+  g.vec = out_vec4(u, g);
+  return g;
+}
+
+int launch_f32nt(const GemmDesc& d, hipStream_t st) {
+  const GemmDesc u = f32_units(d);
+  const Grid g = plan_f32nt(u, u.ws ? u.ws_bytes : 0);
+  if (g.deep) Nt16Deep::launch32(u, g, st);
+  else Nt16Small::launch32(u, g, st);
+  QBLK_TRY(check_launch("gemm_dma_kernel (fp32)"));
+  return finish_splits(u, g, st);
+}
+
 int launch_nt16(const GemmDesc& d, hipStream_t st) {
   const Grid g = plan(d, d.ws ? d.ws_bytes : 0);
   if (nt16_big(d)) Nt16Big::launch(d, g, st);
@@ -2388,6 +2456,7 @@ int gemm(const GemmDesc& d, hipStream_t st) {
                                      "of 64 and 16-byte aligned rows");
     return launch_nt16(d, st);
   }
+  if (f32nt_ok(d)) return launch_f32nt(d, st);
   if (d.prec == Prec::F32) {
     switch (d.layout) {
       case Layout::NT: return dispatch_src<Prec::F32, Layout::NT>(d, st);
@@ -2418,7 +2487,9 @@ size_t gemm_workspace(const GemmDesc& d) {
     const Grid g = plan_tiles(f8_units(d), (size_t)-1, F8Cfg::bm, F8Cfg::bn, 64, -2 * kTargetWgs);
     return g.splits > 1 ? (size_t)g.splits * d.M * d.N * sizeof(float) : 0;
   }
-  const Grid g = nf4_fused_ok(d) ? plan_nf4(d, (size_t)-1) : plan(d, (size_t)-1);
+  const Grid g = nf4_fused_ok(d) ? plan_nf4(d, (size_t)-1)
+                 : f32nt_ok(d)    ? plan_f32nt(f32_units(d), (size_t)-1)
+                                  : plan(d, (size_t)-1);
   return g.splits > 1 ? (size_t)g.splits * d.M * d.N * sizeof(float) : 0;
 }
 

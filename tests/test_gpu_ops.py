@@ -52,6 +52,37 @@ def test_gemm(layout, precision, shape):
         check("C unsplit", C1, Cref, FP16_TOL if precision else FP32_TOL)
 
 
+# fp32 NT products with at least 128 output tiles of 128 x 128 (K a multiple
+# of 32) run on the direct-to-LDS kernel: ragged M and N, and one split over K
+GEMM32_DMA_SHAPES = [(1000, 2104, 96), (1024, 2048, 4096), (1032, 2056, 1408)]
+
+
+@pytest.mark.parametrize("shape", GEMM32_DMA_SHAPES)
+def test_gemm_fp32_nt_direct(shape):
+    need_gpu()
+    M, N, K = shape
+    announce(f"gemm fp32 NT direct-to-LDS M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + 5 * N + 11 * K)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = rng.standard_normal((N, K)).astype(np.float32)
+    Cref = A.astype(np.float64) @ B.astype(np.float64).T
+    dA, dB = dev(A), dev(B)
+    Cg = torch.full((M, N), 7.0, device="cuda")
+    ws = qblk.gemm_workspace_size(0, 0, M, N, K)
+    scratch = byte_buffer(ws) if ws else None
+    qblk.gemm(0, 0, M, N, K, dA, K, dB, K, Cg, N, scratch=scratch)
+    torch.cuda.synchronize()
+    check("C", Cg, Cref, FP32_TOL)
+    qblk.gemm(0, 0, M, N, K, dA, K, dB, K, Cg, N, accumulate=1, scratch=scratch)
+    torch.cuda.synchronize()
+    check("C+C", Cg, 2 * Cref, FP32_TOL)
+    if ws:
+        C1 = torch.empty((M, N), device="cuda")
+        qblk.gemm(0, 0, M, N, K, dA, K, dB, K, C1, N)
+        torch.cuda.synchronize()
+        check("C unsplit", C1, Cref, FP32_TOL)
+
+
 # fp16-stored operands: K a multiple of 64 takes the NT direct-to-LDS kernel,
 # the others the general one
 GEMM16_SHAPES = [(200, 136, 128), (37, 24, 64), (300, 392, 256), (130, 130, 192),
