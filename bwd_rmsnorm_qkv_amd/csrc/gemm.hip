@@ -911,6 +911,40 @@ struct DmaOperand {
   }
 };
 
+// An M/N-contiguous fp32 operand of the fp32 direct-to-LDS path: R fp32
+// columns (2R 16-bit units) by 32 K-rows per stage, copied like a 16-bit
+// MN-major tile of 2R columns (chunks swizzled by (krow & 3) << 2). The
+// fragment of K step s (8 K) for lane (i, kh) is the 4 values at K-rows
+// 8s + 4kh + j, column rb + i, read one float each (K-row 8s + 4kh + j has
+// swizzle j): the arrangement of the K-major fp32 fragments, so the two
+// kinds pair in one MFMA. The kernel hands over units (ld doubled, K and
+// its split offsets doubled); columns and rows convert here.
+template <int R, int NW>
+struct DmaOperandF32MN {
+  using Base = DmaOperand<2 * R, false, NW, 32>;
+  static constexpr int J = Base::J;
+  Base b;
+  __device__ __forceinline__ void init(const f16* base, int64_t ld, int r0, int rmax, int64_t kb, int lane, int w,
+                                       const Seg*) {
+    b.init(base, ld, 2 * r0, 2 * rmax, kb / 2, lane, w, nullptr);
+  }
+  __device__ __forceinline__ void issue_one(int kt, f16* tile, int64_t ld, int w, int j) const {
+    b.issue_one(kt, tile, ld, w, j);
+  }
+  __device__ __forceinline__ void issue(int kt, f16* tile, int64_t ld, int w) const { b.issue(kt, tile, ld, w); }
+  static __device__ __forceinline__ int koff(int, int) { return 0; }
+  static __device__ __forceinline__ half8 frag(const f16* tile, int rb, int s, int lane, int) {
+    const int i = lane & 31, kh = lane >> 5, m = rb + i;
+    const f16* col = tile + (8 * s + 4 * kh) * (2 * R) + (m & 3) * 2;
+    float4 v;
+    v.x = *(const float*)(col + (((m >> 2) ^ 0) << 3));
+    v.y = *(const float*)(col + 1 * (2 * R) + (((m >> 2) ^ 4) << 3));
+    v.z = *(const float*)(col + 2 * (2 * R) + (((m >> 2) ^ 8) << 3));
+    v.w = *(const float*)(col + 3 * (2 * R) + (((m >> 2) ^ 12) << 3));
+    return __builtin_bit_cast(half8, v);
+  }
+};
+
 // fp8 MFMA over 64 K: a and b are 32 bytes of 8-bit operands per lane.
 // FA / FB pick each operand's format (0 E4M3, 1 E5M2). The lane's 32 bytes
 // hold K values in the same arrangement for A and B, so the block product
@@ -953,13 +987,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   constexpr bool BF = EK == 1, F8 = EK >= 2 && EK <= 5, F32 = EK == 6;
   constexpr int FA = F8 ? (EK - 2) & 1 : 0, FB = F8 ? (EK - 2) >> 1 : 0;
   static_assert(!F8 || (AK && BK_), "fp8 operands: both K-major (NT)");
-  static_assert(!F32 || (AK && BK_), "fp32 operands: both K-major (NT)");
+
   constexpr int BK = 64;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "tile");
-  using OA = DmaOperand<BM, AK, NW>;
-  using OB = DmaOperand<BN, BK_, NW>;
+  using OA = std::conditional_t<F32 && !AK, DmaOperandF32MN<BM, NW>, DmaOperand<BM, AK, NW>>;
+  using OB = std::conditional_t<F32 && !BK_, DmaOperandF32MN<BN, NW>, DmaOperand<BN, BK_, NW>>;
   constexpr int JS = OA::J + OB::J;
 
   // the wave index as a scalar: the copies' LDS addresses (M0) then need
@@ -2045,11 +2079,19 @@ struct DmaCfg {
     hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, true, true, EK>), dim3(nwg), dim3(threads), 0, st, d,
                        g);
   }
-  // fp32 operands (NT), the descriptor in 16-bit units
+  // fp32 operands, the descriptor in 16-bit units
+  template <bool AK, bool BKM>
   static void launch32(const GemmDesc& d, const Grid& g, hipStream_t st) {
     const unsigned nwg = (unsigned)(g.tiles_m * g.tiles_n * g.splits);
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, true, true, 6>), dim3(nwg), dim3(threads), 0, st, d,
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, NS, NB, AK, BKM, 6>), dim3(nwg), dim3(threads), 0, st, d,
                        g);
+  }
+  static void launch32(const GemmDesc& d, const Grid& g, hipStream_t st) {
+    switch (d.layout) {
+      case Layout::NT: launch32<true, true>(d, g, st); break;
+      case Layout::NN: launch32<true, false>(d, g, st); break;
+      case Layout::TN: launch32<false, false>(d, g, st); break;
+    }
   }
   static void launch8(const GemmDesc& d, const Grid& g, hipStream_t st) {
     switch (d.f8_a_e5m2 + 2 * d.f8_b_e5m2) {
@@ -2304,22 +2346,22 @@ int launch_f8(const GemmDesc& d, hipStream_t st) {
   return finish_splits(u, g, st);
 }
 
-// fp32 NT products on the direct-to-LDS kernel: K a multiple of 32, lda and
-// ldb multiples of 4, 16-byte aligned rows, no K extension, and at least
-// 128 output tiles of 128 x 128 (half the CUs busy without splitting K).
-// The descriptor goes over in 16-bit units (K, lda, ldb doubled), so tiles,
-// copies and fragment reads are the 16-bit kernel's; each 16-byte fragment
-// holds 4 fp32 K values. Measured against the register-staged kernel: the
-// vocabulary-151936 LM head (1024 x 151936 x 512) 1.47 -> 1.28 ms, 1024 x
-// 2816 x 512 37-40 -> 35 us; products with fewer tiles (1024 x 768 x 512:
-// 48 tiles, 19 -> 25 us) stay on the register kernel's 64-wide tiles.
-bool f32nt_ok(const GemmDesc& d) {
-  if (d.prec != Prec::F32 || d.layout != Layout::NT || d.a_src != Src::F32 || d.b_src != Src::F32) return false;
+// fp32 products on the direct-to-LDS kernel: K a multiple of 32, lda and
+// ldb multiples of 4, 16-byte aligned rows, no K extension; for NN and TN
+// the M/N-contiguous operands' widths multiples of 4 and a single B
+// segment. The descriptor goes over in 16-bit units (K, lda, ldb doubled),
+// so tiles, copies and the K-major fragment reads are the 16-bit kernel's
+// (each 16-byte fragment holds 4 fp32 K values); M/N-contiguous operands
+// take DmaOperandF32MN.
+bool f32dma_fits(const GemmDesc& d) {
+  if (d.prec != Prec::F32 || d.a_src != Src::F32 || d.b_src != Src::F32) return false;
   if (d.ext.kext > 0 || d.K % 32 != 0 || d.K == 0 || d.lda % 4 != 0 || d.ldb % 4 != 0) return false;
   if ((uintptr_t)d.a % 16 != 0) return false;
   for (int s = 0; s < d.b.nseg; ++s)
     if ((uintptr_t)d.b.p[s] % 16 != 0) return false;
-  return ceil_div(d.M, Nt16Small::bm) * ceil_div(d.N, Nt16Small::bn) >= 128;
+  if (d.layout == Layout::TN && (d.M % 4 != 0 || d.M < 4)) return false;
+  if (d.layout != Layout::NT && (d.N % 4 != 0 || d.N < 4 || d.b.nseg != 1)) return false;
+  return true;
 }
 
 GemmDesc f32_units(const GemmDesc& d) {
@@ -2330,7 +2372,7 @@ GemmDesc f32_units(const GemmDesc& d) {
   return u;
 }
 
-Grid plan_f32nt(const GemmDesc& u, size_t ws_bytes) {
+Grid plan_f32dma(const GemmDesc& u, size_t ws_bytes) {
   Grid g = plan_tiles(u, ws_bytes, Nt16Small::bm, Nt16Small::bn, 64, -kTargetWgs);
   g.bn = Nt16Small::bn;
   g.deep = g.tiles_m * g.tiles_n * g.splits <= kTargetWgs;
@@ -2338,9 +2380,24 @@ Grid plan_f32nt(const GemmDesc& u, size_t ws_bytes) {
   return g;
 }
 
-int launch_f32nt(const GemmDesc& d, hipStream_t st) {
+// The direct-to-LDS kernel takes an fp32 product when its 128 x 128 tiles
+// and K splits give at least two thirds of the CUs a workgroup; with fewer
+// the register-staged kernel's 64-wide tiles were faster. Measured (one
+// MI355X, ms or us per product): the vocabulary-151936 LM head 1.47 ->
+// 1.28 ms (logits, NT), 1.55-1.60 -> 1.23-1.26 ms (dX, NN, 32 tiles in 8
+// splits), 1.69 -> 1.31 ms (dW, TN); the seq-1024 layer products NN 1024 x
+// 512 x 2816 51.6 -> 38 us (256 workgroups), TN 512 x 1408 x 1024 37.8 ->
+// 29.5 us (176); but NT 1024 x 512 x 1408 (160 workgroups) 25 -> 28.8 us
+// and NT 1024 x 768 x 512 (96) 18.9 -> 24.8 us.
+bool f32dma_use(const GemmDesc& d, size_t ws_bytes) {
+  if (!f32dma_fits(d)) return false;
+  const Grid g = plan_f32dma(f32_units(d), ws_bytes);
+  return 3 * g.tiles_m * g.tiles_n * g.splits >= 2 * kTargetWgs;
+}
+
+int launch_f32dma(const GemmDesc& d, hipStream_t st) {
   const GemmDesc u = f32_units(d);
-  const Grid g = plan_f32nt(u, u.ws ? u.ws_bytes : 0);
+  const Grid g = plan_f32dma(u, u.ws ? u.ws_bytes : 0);
   if (g.deep) Nt16Deep::launch32(u, g, st);
   else Nt16Small::launch32(u, g, st);
   QBLK_TRY(check_launch("gemm_dma_kernel (fp32)"));
@@ -2456,7 +2513,7 @@ int gemm(const GemmDesc& d, hipStream_t st) {
                                      "of 64 and 16-byte aligned rows");
     return launch_nt16(d, st);
   }
-  if (f32nt_ok(d)) return launch_f32nt(d, st);
+  if (f32dma_use(d, d.ws ? d.ws_bytes : 0)) return launch_f32dma(d, st);
   if (d.prec == Prec::F32) {
     switch (d.layout) {
       case Layout::NT: return dispatch_src<Prec::F32, Layout::NT>(d, st);
@@ -2488,7 +2545,7 @@ size_t gemm_workspace(const GemmDesc& d) {
     return g.splits > 1 ? (size_t)g.splits * d.M * d.N * sizeof(float) : 0;
   }
   const Grid g = nf4_fused_ok(d) ? plan_nf4(d, (size_t)-1)
-                 : f32nt_ok(d)    ? plan_f32nt(f32_units(d), (size_t)-1)
+                 : f32dma_use(d, (size_t)-1) ? plan_f32dma(f32_units(d), (size_t)-1)
                                   : plan(d, (size_t)-1);
   return g.splits > 1 ? (size_t)g.splits * d.M * d.N * sizeof(float) : 0;
 }

@@ -52,33 +52,40 @@ def test_gemm(layout, precision, shape):
         check("C unsplit", C1, Cref, FP16_TOL if precision else FP32_TOL)
 
 
-# fp32 NT products with at least 128 output tiles of 128 x 128 (K a multiple
-# of 32) run on the direct-to-LDS kernel: ragged M and N, and one split over K
-GEMM32_DMA_SHAPES = [(1000, 2104, 96), (1024, 2048, 4096), (1032, 2056, 1408)]
+# fp32 products whose 128 x 128 tiles and K splits give at least 171
+# workgroups (K a multiple of 32) run on the direct-to-LDS kernel: ragged M
+# and N, K splits, all three layouts (NN and TN read M/N-contiguous fp32
+# tiles); layout, M, N, K
+GEMM32_DMA_SHAPES = [(0, 1000, 2952, 96), (0, 1024, 2048, 4096), (0, 1288, 2056, 1408),
+                     (1, 1000, 2952, 96), (1, 1024, 512, 2816), (1, 264, 520, 30016),
+                     (2, 1000, 2952, 96), (2, 2816, 512, 1024), (2, 520, 1400, 1024)]
 
 
-@pytest.mark.parametrize("shape", GEMM32_DMA_SHAPES)
-def test_gemm_fp32_nt_direct(shape):
+@pytest.mark.parametrize("layout,M,N,K", GEMM32_DMA_SHAPES)
+def test_gemm_fp32_direct(layout, M, N, K):
     need_gpu()
-    M, N, K = shape
-    announce(f"gemm fp32 NT direct-to-LDS M={M} N={N} K={K}")
-    rng = np.random.default_rng(M + 5 * N + 11 * K)
-    A = rng.standard_normal((M, K)).astype(np.float32)
-    B = rng.standard_normal((N, K)).astype(np.float32)
-    Cref = A.astype(np.float64) @ B.astype(np.float64).T
+    announce(f"gemm fp32 direct-to-LDS layout={layout} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + 5 * N + 11 * K + layout)
+    a_shape = (M, K) if layout in (0, 1) else (K, M)
+    b_shape = (N, K) if layout == 0 else (K, N)
+    A = rng.standard_normal(a_shape).astype(np.float32)
+    B = rng.standard_normal(b_shape).astype(np.float32)
+    Cref = (A.astype(np.float64) if layout != 2 else A.astype(np.float64).T) @ \
+           (B.astype(np.float64).T if layout == 0 else B.astype(np.float64))
     dA, dB = dev(A), dev(B)
     Cg = torch.full((M, N), 7.0, device="cuda")
-    ws = qblk.gemm_workspace_size(0, 0, M, N, K)
+    ws = qblk.gemm_workspace_size(layout, 0, M, N, K)
     scratch = byte_buffer(ws) if ws else None
-    qblk.gemm(0, 0, M, N, K, dA, K, dB, K, Cg, N, scratch=scratch)
+    qblk.gemm(layout, 0, M, N, K, dA, a_shape[1], dB, b_shape[1], Cg, N, scratch=scratch)
     torch.cuda.synchronize()
     check("C", Cg, Cref, FP32_TOL)
-    qblk.gemm(0, 0, M, N, K, dA, K, dB, K, Cg, N, accumulate=1, scratch=scratch)
+    qblk.gemm(layout, 0, M, N, K, dA, a_shape[1], dB, b_shape[1], Cg, N, accumulate=1, scratch=scratch)
     torch.cuda.synchronize()
     check("C+C", Cg, 2 * Cref, FP32_TOL)
     if ws:
+        # without the workspace: unsplit, on whichever kernel then applies
         C1 = torch.empty((M, N), device="cuda")
-        qblk.gemm(0, 0, M, N, K, dA, K, dB, K, C1, N)
+        qblk.gemm(layout, 0, M, N, K, dA, a_shape[1], dB, b_shape[1], C1, N)
         torch.cuda.synchronize()
         check("C unsplit", C1, Cref, FP32_TOL)
 
