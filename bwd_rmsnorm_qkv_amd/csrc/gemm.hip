@@ -1188,6 +1188,37 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
         for (int e = 0; e < 16; ++e) acc[a][b][e] *= sc;
   }
 
+  constexpr int WC = TN * 32;  // wave tile width
+  if constexpr (WC < 64) {
+    // Narrow wave tiles (64 x 64 workgroup tiles of 32 x 32 per wave): each
+    // lane stores its accumulators directly, one column per lane and 32
+    // consecutive columns per row (128-byte row pieces per wave store).
+    const int ii = lane & 31, kh = lane >> 5;
+    float* part = gd.splits > 1 ? d.ws + (int64_t)sp * d.M * d.N : nullptr;
+    const int bd = d.c_cols_blockdiag;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * TM * 32 + tm * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
+        if (row >= d.M) continue;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int col = n0 + wn * WC + tn * 32 + ii;
+          if (col >= d.N) continue;
+          if (part) {
+            part[(int64_t)row * d.N + col] = acc[tm][tn][e];
+            continue;
+          }
+          int lo = 0;
+          float* rp = out_row(d, row, lo);
+          if (bd > 0 && (col < lo || col >= lo + bd)) continue;
+          put_out(d, rp + (col - lo), row, col, acc[tm][tn][e]);
+          if (d.c16) d.c16[(int64_t)row * d.ldc16 + col] = to_16(rp[col - lo], BF);
+        }
+      }
+    return;
+  }
   // Epilogue through LDS: the wave parks one 32-row block (tm) of its tile
   // at a time in its own slice of the (now idle) stage buffers and reads it
   // back so that every lane writes 16 contiguous bytes and each wave
@@ -1195,10 +1226,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   // instructions of element-wise stores. The float4 slots of a row are
   // XOR-swizzled by row bit 2, so the two half-waves, which park rows r and
   // r + 4, write different banks.
-  constexpr int WC = TN * 32;  // wave tile width
   constexpr int CPR = WC / 4;  // float4 slots per row
-  static_assert(CPR >= 16 && (32 * CPR) % 64 == 0, "epilogue row width");
-  static_assert(BM == BN && 2 * 32 * WC * 4 <= BM * BK * 2 && NW <= 8, "epilogue staging space");
+  static_assert(WC < 64 || (CPR >= 16 && (32 * CPR) % 64 == 0), "epilogue row width");
+  static_assert(WC < 64 || (BM == BN && 2 * 32 * WC * 4 <= BM * BK * 2 && NW <= 8), "epilogue staging space");
   const int ii = lane & 31, kh = lane >> 5;
   __syncthreads();  // every wave is done reading the stages
   float* ep;
@@ -2123,6 +2153,7 @@ struct DmaCfg {
 using Nt16Small = DmaCfg<128, 128, 4, 2, 2, 3>;
 using Nt16Deep = DmaCfg<128, 128, 4, 2, 3, 3>;
 using F8Cfg = DmaCfg<128, 128, 2, 2, 2, 3>;
+using F32Small = DmaCfg<64, 64, 2, 2, 3, 3>;
 using Nt16Big = PpCfg;
 
 // Big tiles pay off once they alone give at least half the CUs a tile.
@@ -2380,19 +2411,42 @@ Grid plan_f32dma(const GemmDesc& u, size_t ws_bytes) {
   return g;
 }
 
-// The direct-to-LDS kernel takes an fp32 product when its 128 x 128 tiles
-// and K splits give at least two thirds of the CUs a workgroup; with fewer
-// the register-staged kernel's 64-wide tiles were faster. Measured (one
-// MI355X, ms or us per product): the vocabulary-151936 LM head 1.47 ->
-// 1.28 ms (logits, NT), 1.55-1.60 -> 1.23-1.26 ms (dX, NN, 32 tiles in 8
-// splits), 1.69 -> 1.31 ms (dW, TN); the seq-1024 layer products NN 1024 x
-// 512 x 2816 51.6 -> 38 us (256 workgroups), TN 512 x 1408 x 1024 37.8 ->
-// 29.5 us (176); but NT 1024 x 512 x 1408 (160 workgroups) 25 -> 28.8 us
-// and NT 1024 x 768 x 512 (96) 18.9 -> 24.8 us.
-bool f32dma_use(const GemmDesc& d, size_t ws_bytes) {
-  if (!f32dma_fits(d)) return false;
+// fp32 products that fit the direct-to-LDS kernel run on it, with 128 x 128
+// tiles when they give at least two rounds of workgroups or at least 4096
+// K per workgroup (the LM head: the fill per FLOP halves), else with 64 x 64
+// tiles of 4 waves split over K up to one workgroup per CU. Measured (one
+// MI355X) against the register-staged kernel's 64-wide tiles: the
+// vocabulary-151936 LM head 1.47 -> 1.28 ms (logits, NT), 1.55-1.60 ->
+// 1.23 ms (dX, NN, 32 tiles in 8 splits), 1.69 -> 1.31 ms (dW, TN), where
+// 64 x 64 tiles took 1.43, 1.32-1.49 and 1.43 ms; every product of a
+// seq-1024 layer of the 36-layer stack faster on 64 x 64 tiles (NN 1024 x
+// 512 x 768 23.3 -> 16.1 us, TN 768 x 512 x 1024 25.4 -> 18.3 us, NN 1024
+// x 512 x 2816 51.6 -> 34 us; the twelve 321 -> 294 us), which also beat
+// 128 x 128 tiles on them (NT 1024 x 2816 x 512 35.6-38.9 -> 33.8 us).
+Grid plan_f32dma64(const GemmDesc& u, size_t ws_bytes) {
+  Grid g = plan_tiles(u, ws_bytes, F32Small::bm, F32Small::bn, 64, -kTargetWgs);
+  g.bn = F32Small::bn;
+  g.deep = 0;
+  g.vec = out_vec4(u, g);
+  return g;
+}
+
+// 0: register-staged kernel; 1: 64 x 64 direct-to-LDS tiles; 2: 128 x 128
+// (decided on the unlimited-workspace plan, so that gemm_workspace and the
+// launch agree whatever workspace the caller then passes).
+int f32dma_kind(const GemmDesc& d, size_t ws_bytes) {
+  if (!f32dma_fits(d)) return 0;
   const Grid g = plan_f32dma(f32_units(d), ws_bytes);
-  return 3 * g.tiles_m * g.tiles_n * g.splits >= 2 * kTargetWgs;
+  const bool rounds2 = g.tiles_m * g.tiles_n * g.splits >= 2 * kTargetWgs;
+  return rounds2 || g.kchunk / 2 >= 4096 ? 2 : 1;
+}
+
+int launch_f32dma64(const GemmDesc& d, hipStream_t st) {
+  const GemmDesc u = f32_units(d);
+  const Grid g = plan_f32dma64(u, u.ws ? u.ws_bytes : 0);
+  F32Small::launch32(u, g, st);
+  QBLK_TRY(check_launch("gemm_dma_kernel (fp32, 64 x 64)"));
+  return finish_splits(u, g, st);
 }
 
 int launch_f32dma(const GemmDesc& d, hipStream_t st) {
@@ -2513,7 +2567,11 @@ int gemm(const GemmDesc& d, hipStream_t st) {
                                      "of 64 and 16-byte aligned rows");
     return launch_nt16(d, st);
   }
-  if (f32dma_use(d, d.ws ? d.ws_bytes : 0)) return launch_f32dma(d, st);
+  switch (f32dma_kind(d, (size_t)-1)) {  // by shape alone, as gemm_workspace decides
+    case 2: return launch_f32dma(d, st);
+    case 1: return launch_f32dma64(d, st);
+    default: break;
+  }
   if (d.prec == Prec::F32) {
     switch (d.layout) {
       case Layout::NT: return dispatch_src<Prec::F32, Layout::NT>(d, st);
@@ -2545,7 +2603,8 @@ size_t gemm_workspace(const GemmDesc& d) {
     return g.splits > 1 ? (size_t)g.splits * d.M * d.N * sizeof(float) : 0;
   }
   const Grid g = nf4_fused_ok(d) ? plan_nf4(d, (size_t)-1)
-                 : f32dma_use(d, (size_t)-1) ? plan_f32dma(f32_units(d), (size_t)-1)
+                 : f32dma_kind(d, (size_t)-1) == 2 ? plan_f32dma(f32_units(d), (size_t)-1)
+                 : f32dma_kind(d, (size_t)-1) == 1 ? plan_f32dma64(f32_units(d), (size_t)-1)
                                   : plan(d, (size_t)-1);
   return g.splits > 1 ? (size_t)g.splits * d.M * d.N * sizeof(float) : 0;
 }

@@ -52,13 +52,14 @@ def test_gemm(layout, precision, shape):
         check("C unsplit", C1, Cref, FP16_TOL if precision else FP32_TOL)
 
 
-# fp32 products whose 128 x 128 tiles and K splits give at least 171
-# workgroups (K a multiple of 32) run on the direct-to-LDS kernel: ragged M
-# and N, K splits, all three layouts (NN and TN read M/N-contiguous fp32
-# tiles); layout, M, N, K
-GEMM32_DMA_SHAPES = [(0, 1000, 2952, 96), (0, 1024, 2048, 4096), (0, 1288, 2056, 1408),
-                     (1, 1000, 2952, 96), (1, 1024, 512, 2816), (1, 264, 520, 30016),
-                     (2, 1000, 2952, 96), (2, 2816, 512, 1024), (2, 520, 1400, 1024)]
+# fp32 products with K a multiple of 32 and 16-byte rows run on the
+# direct-to-LDS kernel: 128 x 128 tiles with two rounds of workgroups or
+# >= 4096 K per workgroup, 64 x 64 tiles otherwise; ragged M and N, K
+# splits, all three layouts (NN and TN read M/N-contiguous fp32 tiles);
+# layout, M, N, K
+GEMM32_DMA_SHAPES = [(0, 2048, 4096, 96), (2, 2048, 4096, 96), (1, 264, 520, 73728),  # 128 x 128
+                     (0, 1000, 2952, 96), (0, 1288, 2056, 1408), (1, 1000, 2952, 96), (1, 1024, 512, 2816),
+                     (2, 1000, 2952, 96), (2, 2816, 512, 1024), (2, 520, 1400, 1024), (0, 72, 40, 64)]
 
 
 @pytest.mark.parametrize("layout,M,N,K", GEMM32_DMA_SHAPES)
