@@ -918,29 +918,63 @@ struct DmaOperand {
 // 8s + 4kh + j, column rb + i, read one float each (K-row 8s + 4kh + j has
 // swizzle j): the arrangement of the K-major fp32 fragments, so the two
 // kinds pair in one MFMA. The kernel hands over units (ld doubled, K and
-// its split offsets doubled); columns and rows convert here.
+// its split offsets doubled); columns and rows convert here. Storage rows
+// may lie in up to three segments whose boundaries fall on 32-row K tiles:
+// each copy then takes its tile's segment (the same for every lane).
 template <int R, int NW>
 struct DmaOperandF32MN {
-  using Base = DmaOperand<2 * R, false, NW, 32>;
-  static constexpr int J = Base::J;
-  Base b;
-  __device__ __forceinline__ void init(const f16* base, int64_t ld, int r0, int rmax, int64_t kb, int lane, int w,
-                                       const Seg*) {
-    b.init(base, ld, 2 * r0, 2 * rmax, kb / 2, lane, w, nullptr);
+  static constexpr int RU = 2 * R;      // 16-bit units per K-row
+  static constexpr int CPR = RU / 8;    // 16-byte chunks per K-row
+  static constexpr int RPI = 64 / CPR;  // K-rows per 1 KB wave copy
+  static constexpr int J = RU * 32 / 512 / NW;
+  static_assert(J * 512 * NW == RU * 32 && RPI >= 1, "DMA split");
+  int64_t off[J];  // this lane's offset (units) of copy j inside a K tile
+  const f16* p0;    // segment 0's base (the operand's without segments)
+  int64_t d1, d2;   // segments 1 and 2: their bases' offsets from p0 (units)
+  int s1, s2, kb_rows;  // segment starts (past the end when absent)
+  __device__ __forceinline__ void init(const f16* base_, int64_t ld, int r0, int rmax, int64_t kb, int lane, int w,
+                                       const Seg* seg_) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int blk = NW * j + w;
+      const int krow = blk * RPI + lane / CPR;
+      const int lc = (lane % CPR) ^ ((krow & 3) << 2);
+      const int col = min(2 * r0 + lc * 8, 2 * rmax - 8);
+      off[j] = (int64_t)krow * ld + col;
+    }
+    // the segment table is copied into scalars: indexing the kernel
+    // argument's table at run time would put the whole descriptor in
+    // private memory
+    // (arithmetic on the offsets, as in out_row: a selected pointer was
+    // compiled to an indexed load from a private copy of the operand)
+    const int ns = seg_ ? seg_->nseg : 1;
+    p0 = ns > 1 ? (const f16*)seg_->p[0] : base_;
+    d1 = ns > 1 ? (const f16*)seg_->p[1] - p0 : 0;
+    d2 = ns > 2 ? (const f16*)seg_->p[2] - p0 : 0;
+    s1 = ns > 1 ? seg_->start[1] : 0x7fffffff;
+    s2 = ns > 2 ? seg_->start[2] : 0x7fffffff;
+    kb_rows = (int)(kb / 2);
   }
   __device__ __forceinline__ void issue_one(int kt, f16* tile, int64_t ld, int w, int j) const {
-    b.issue_one(kt, tile, ld, w, j);
+    const int r = kb_rows + kt * 32;  // the tile's first storage row
+    const int in1 = r >= s1, in2 = r >= s2;
+    const int64_t so = in2 * d2 + (in1 - in2) * d1;
+    const int st = in1 * s1 + in2 * (s2 - s1);
+    dma16_asm(p0 + so + (int64_t)(r - st) * ld + off[j], tile + 512 * (NW * j + w));
   }
-  __device__ __forceinline__ void issue(int kt, f16* tile, int64_t ld, int w) const { b.issue(kt, tile, ld, w); }
+  __device__ __forceinline__ void issue(int kt, f16* tile, int64_t ld, int w) const {
+#pragma unroll
+    for (int j = 0; j < J; ++j) issue_one(kt, tile, ld, w, j);
+  }
   static __device__ __forceinline__ int koff(int, int) { return 0; }
   static __device__ __forceinline__ half8 frag(const f16* tile, int rb, int s, int lane, int) {
     const int i = lane & 31, kh = lane >> 5, m = rb + i;
-    const f16* col = tile + (8 * s + 4 * kh) * (2 * R) + (m & 3) * 2;
+    const f16* col = tile + (8 * s + 4 * kh) * RU + (m & 3) * 2;
     float4 v;
     v.x = *(const float*)(col + (((m >> 2) ^ 0) << 3));
-    v.y = *(const float*)(col + 1 * (2 * R) + (((m >> 2) ^ 4) << 3));
-    v.z = *(const float*)(col + 2 * (2 * R) + (((m >> 2) ^ 8) << 3));
-    v.w = *(const float*)(col + 3 * (2 * R) + (((m >> 2) ^ 12) << 3));
+    v.y = *(const float*)(col + 1 * RU + (((m >> 2) ^ 4) << 3));
+    v.z = *(const float*)(col + 2 * RU + (((m >> 2) ^ 8) << 3));
+    v.w = *(const float*)(col + 3 * RU + (((m >> 2) ^ 12) << 3));
     return __builtin_bit_cast(half8, v);
   }
 };
@@ -1016,7 +1050,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(const GemmDesc d,
   OA oa;
   OB ob;
   oa.init((const f16*)d.a, d.lda, m0, d.M, kb, lane, w, nullptr);
-  ob.init((const f16*)d.b.p[0], d.ldb, n0, d.N, kb, lane, w, BK_ ? &d.b : nullptr);
+  ob.init((const f16*)d.b.p[0], d.ldb, n0, d.N, kb, lane, w, (BK_ || F32) ? &d.b : nullptr);
 
   floatx16 acc[TM][TN];
 #pragma unroll
@@ -2391,7 +2425,12 @@ bool f32dma_fits(const GemmDesc& d) {
   for (int s = 0; s < d.b.nseg; ++s)
     if ((uintptr_t)d.b.p[s] % 16 != 0) return false;
   if (d.layout == Layout::TN && (d.M % 4 != 0 || d.M < 4)) return false;
-  if (d.layout != Layout::NT && (d.N % 4 != 0 || d.N < 4 || d.b.nseg != 1)) return false;
+  if (d.layout != Layout::NT) {
+    // M/N-contiguous B: its segments (along K) start on 32-row K tiles
+    if (d.N % 4 != 0 || d.N < 4) return false;
+    for (int s = 1; s < d.b.nseg; ++s)
+      if (d.b.start[s] % 32 != 0) return false;
+  }
   return true;
 }
 
